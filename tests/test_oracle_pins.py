@@ -1,0 +1,496 @@
+"""Pins of the fp64 CPU oracle to things other than itself.
+
+Each test ties one oracle function to what the pages and mathematics fix:
+closed forms, invariants, exact special cases, an independent library
+routine (numpy/torch), or a high-precision brute force written in a
+different formulation (mpmath, Sinkhorn as diagonal scaling vectors).
+The aim is that a plausible slip anywhere in the oracle (a dropped eps, a
+wrong axis, a transposed comb, an off-by-one iteration count, a wrong
+stride) fails at least one of them.
+
+Sources: "Mix projection" page (mix formula; Block.hc_pre / hc_post listing),
+"Reading weights" page (learned-pre formula; hc_split_sinkhorn listing),
+attention page (config.json).
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import mpmath as mp
+import numpy as np
+import pytest
+import torch
+
+from hyper_connection_residual_02_amd import inputs as hin
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "page_constants.json")
+EPS = 1e-6
+NEPS = 1e-20
+
+
+def _gold():
+    with open(GOLD) as f:
+        return json.load(f)
+
+
+def _rand_bits(rng, shape, scale=1.0):
+    v = torch.from_numpy((rng.standard_normal(shape) * scale).astype(np.float32))
+    return hin.bits(v.to(torch.bfloat16))
+
+
+def _bf16_bits_of(vals):
+    return hin.bits(torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16))
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding
+
+
+def test_round_bf16_matches_torch_on_fp32_values(orc):
+    # For values that are exactly floats, a single rounding from double is
+    # the same as torch's float32 -> bfloat16 round-to-nearest-even.
+    rng = np.random.default_rng(1)
+    f = rng.standard_normal(20000).astype(np.float32) * np.float32(3.0)
+    # force exact ties: low 16 bits = 0x8000 with both parities of bit 16
+    ties = (rng.integers(0x3F000000, 0x40800000, 2000, dtype=np.uint32)
+            & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    f = np.concatenate([f, ties.view(np.float32), -ties.view(np.float32)])
+    ref = hin.bits(torch.from_numpy(f).to(torch.bfloat16))
+    got = np.array([orc.round_bf16(float(v)) for v in f], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_round_bf16_definition_cases(orc):
+    one = 0x3F80
+    assert orc.round_bf16(1.0) == one
+    assert orc.round_bf16(1.0 + 2.0**-8) == one            # tie -> even (down)
+    assert orc.round_bf16(1.0 + 3 * 2.0**-8) == one + 2    # tie -> even (up)
+    # single rounding from double: just above a tie goes up (a detour through
+    # float32 would land on the tie and go down)
+    assert orc.round_bf16(1.0 + 2.0**-8 + 2.0**-40) == one + 1
+    assert orc.round_bf16(-(1.0 + 2.0**-8 + 2.0**-40)) == 0x8000 | (one + 1)
+    big = (2 - 2.0**-7) * 2.0**127                          # largest bf16
+    assert orc.round_bf16(big) == 0x7F7F
+    assert orc.round_bf16((2 - 2.0**-8) * 2.0**127) == 0x7F80   # tie -> inf
+    assert orc.round_bf16((2 - 2.0**-8 - 2.0**-20) * 2.0**127) == 0x7F7F
+    assert orc.round_bf16(-1e300) == 0xFF80
+    assert orc.round_bf16(0.0) == 0 and orc.round_bf16(-0.0) == 0x8000
+    assert orc.round_bf16(2.0**-133) == 0x0001              # smallest subnormal
+    assert orc.round_bf16(2.0**-134) == 0                   # tie -> even (0)
+    assert orc.round_bf16(float("nan")) == 0x7FC0
+    # bf16 -> double is exact: a round trip of every finite pattern is identity
+    pats = np.arange(0, 0x7F80, 7, dtype=np.uint16)
+    back = np.array([orc.round_bf16(v) for v in orc.bf16_to_f64(pats)])
+    assert np.array_equal(back, pats)
+
+
+# --------------------------------------------------------------------------
+# mix projection (Mix projection page, formula)
+
+
+def test_mixes_matches_numpy_fp64(orc):
+    rng = np.random.default_rng(2)
+    n, hc, d = 5, 4, 64
+    R = _rand_bits(rng, (n, hc, d))
+    W = (rng.standard_normal((24, hc * d)) * 0.02).astype(np.float32)
+    got = orc.mixes(R, W)
+    X = orc.bf16_to_f64(R).reshape(n, hc * d)
+    ref = (X @ W.astype(np.float64).T) / np.sqrt((X * X).mean(1, keepdims=True) + NEPS)
+    assert np.allclose(got, ref, rtol=1e-13, atol=1e-15)
+
+
+def test_mixes_flatten_order_is_stream_major(orc):
+    # The stream is flattened as x.flatten(2): element (k, c) sits at k*d + c.
+    # A W row that picks one (k, c) must return that element (divided by RMS).
+    rng = np.random.default_rng(3)
+    n, hc, d = 3, 4, 64
+    R = _rand_bits(rng, (n, hc, d))
+    X = orc.bf16_to_f64(R)
+    W = np.zeros((24, hc * d), np.float32)
+    picks = [(j % hc, (7 * j + 3) % d) for j in range(24)]
+    for j, (k, c) in enumerate(picks):
+        W[j, k * d + c] = 1.0
+    got = orc.mixes(R, W)
+    rms = np.sqrt((X.reshape(n, -1) ** 2).mean(1) + NEPS)
+    for j, (k, c) in enumerate(picks):
+        assert np.allclose(got[:, j], X[:, k, c] / rms, rtol=1e-15, atol=0)
+
+
+def test_mixes_exact_integers(orc):
+    # Small-integer residual and dyadic weights: every product and sum is
+    # exact, and mean(x^2) = 4 so that 1/sqrt(4 + 1e-20) = 1/2 in double.
+    hc, d = 4, 64
+    K = hc * d
+    x = np.array([2 if (i % 3) else -2 for i in range(K)], dtype=np.float32)  # x^2 = 4
+    R = _bf16_bits_of(x.reshape(1, hc, d))
+    rng = np.random.default_rng(4)
+    Wi = rng.integers(-64, 65, size=(24, K))
+    W = (Wi / 128.0).astype(np.float32)
+    got = orc.mixes(R, W)[0]
+    for j in range(24):
+        exact = Fraction(int(np.dot(Wi[j], x.astype(np.int64))), 128) / 2
+        assert got[j] == float(exact)
+
+
+def test_mixes_scale_invariance_and_zero_token(orc):
+    rng = np.random.default_rng(5)
+    n, hc, d = 4, 4, 64
+    R = _rand_bits(rng, (n, hc, d))
+    W = (rng.standard_normal((24, hc * d)) * 0.02).astype(np.float32)
+    X = orc.bf16_to_f64(R)
+    R8 = _bf16_bits_of((X * 256.0).astype(np.float32))       # exact power-of-2 scale
+    a, b = orc.mixes(R, W), orc.mixes(R8, W)
+    assert np.allclose(a, b, rtol=1e-14, atol=0)
+    Z = np.zeros((2, hc, d), np.uint16)
+    mz = orc.mixes(Z, W)
+    assert np.all(mz == 0.0) and not np.any(np.isnan(mz))
+
+
+def test_projection_shape_from_page_parameter_table(orc):
+    g = _gold()
+    cfg, mp_ = g["config"], g["mix_projection"]
+    hc, d = cfg["hc_mult"], cfg["dim"]
+    assert hc * d == mp_["flattened_features"]
+    assert (2 + hc) * hc == mp_["mix_numbers"]
+    assert (2 + hc) * hc * hc * d == mp_["parameters_per_instance"]
+    w = hin.WORKLOADS["prefill"]
+    assert (w.M, w.K) == (24, 20480) and w.M * w.K == mp_["parameters_per_instance"]
+    lp = g["learned_pre"]
+    assert lp["offsets"] == hc and lp["offsets"] + lp["scales"] == lp["parameters_per_instance"]
+    assert lp["epsilon"] == cfg["hc_eps"] == EPS
+    assert cfg["norm_eps"] == NEPS and cfg["hc_sinkhorn_iters"] == 20
+
+
+# --------------------------------------------------------------------------
+# split: pre / post gates (Reading weights page, formula and listing)
+
+
+def _sig(z):
+    return 1 / (1 + mp.e ** (-z))
+
+
+def test_gates_closed_form_at_zero_mixes(orc):
+    mp.mp.dps = 40
+    rng = np.random.default_rng(6)
+    base = rng.standard_normal(24).astype(np.float32)
+    scale = np.array([1.7, 0.6, 3.0], np.float32)
+    m = np.zeros((3, 24))
+    pre, post, comb = orc.split_sinkhorn(m, scale, base)
+    for j in range(4):
+        assert abs(pre[0, j] - float(_sig(mp.mpf(float(base[j]))) + mp.mpf("1e-6"))) < 1e-15
+        assert abs(post[0, j] - float(2 * _sig(mp.mpf(float(base[4 + j]))))) < 1e-15
+    g = _gold()["closed_forms"]
+    pz, qz, _ = orc.split_sinkhorn(np.zeros((1, 24)), scale, np.zeros(24, np.float32))
+    assert np.all(pz == g["pre_at_zero_logit"]) and np.all(qz == g["post_at_zero_logit"])
+
+
+def test_gate_ranges(orc):
+    rng = np.random.default_rng(7)
+    m = rng.standard_normal((2000, 24)) * 30
+    scale = np.array([2.0, 2.0, 1.0], np.float32)
+    base = rng.standard_normal(24).astype(np.float32)
+    pre, post, _ = orc.split_sinkhorn(m, scale, base)
+    assert np.all(pre >= EPS) and np.all(pre <= 1 + EPS)
+    assert np.all(post >= 0) and np.all(post <= 2)
+    # moderate logits: strictly inside the open intervals
+    pre2, post2, _ = orc.split_sinkhorn(m / 30, scale, base)
+    assert np.all(pre2 > EPS) and np.all(pre2 < 1 + EPS)
+    assert np.all(post2 > 0) and np.all(post2 < 2)
+
+
+def test_scale_and_mix_index_roles(orc):
+    # hc_scale[0] feeds pre only, [1] post only, [2] comb only; mixes 0..3
+    # feed pre, 4..7 post, 8..23 comb (row-major j*4+k).
+    rng = np.random.default_rng(8)
+    m = rng.standard_normal((4, 24))
+    base = rng.standard_normal(24).astype(np.float32)
+    s = np.array([1.3, 0.7, 2.1], np.float32)
+    ref = orc.split_sinkhorn(m, s, base)
+    for which in range(3):
+        s2 = s.copy()
+        s2[which] *= 1.5
+        out = orc.split_sinkhorn(m, s2, base)
+        for q in range(3):
+            same = np.array_equal(out[q], ref[q])
+            assert same == (q != which), (which, q)
+    for j in range(24):
+        m2 = m.copy()
+        m2[:, j] += 0.25
+        out = orc.split_sinkhorn(m2, s, base)
+        if j < 4:
+            changed = ~np.isclose(out[0], ref[0], rtol=0, atol=0)
+            assert changed[:, j].all() and not np.delete(changed, j, 1).any()
+            assert np.array_equal(out[1], ref[1]) and np.array_equal(out[2], ref[2])
+        elif j < 8:
+            changed = out[1] != ref[1]
+            assert changed[:, j - 4].all() and not np.delete(changed, j - 4, 1).any()
+            assert np.array_equal(out[0], ref[0]) and np.array_equal(out[2], ref[2])
+        else:
+            assert np.array_equal(out[0], ref[0]) and np.array_equal(out[1], ref[1])
+            assert not np.array_equal(out[2], ref[2])
+
+
+# --------------------------------------------------------------------------
+# Sinkhorn (Reading weights page, kernel listing)
+
+
+def _logits_only(L, hc=4):
+    """mixes / scale / base such that the comb logits equal L exactly."""
+    n = L.shape[0]
+    m = np.zeros((n, (2 + hc) * hc))
+    m[:, 2 * hc:] = L.reshape(n, hc * hc)
+    return m, np.array([1.0, 1.0, 1.0], np.float32), np.zeros((2 + hc) * hc, np.float32)
+
+
+def test_uniform_logits_closed_form(orc):
+    # every logit equal: comb = (1 - eps)/4 after the 39 normalisations
+    g = _gold()["closed_forms"]
+    for val in [0.0, 3.5, -40.0]:
+        m, s, b = _logits_only(np.full((1, 4, 4), val))
+        _, _, comb = orc.split_sinkhorn(m, s, b)
+        assert np.allclose(comb, (1 - EPS) / 4, rtol=1e-15, atol=0)
+        assert abs(comb[0, 0, 0] - g["uniform_comb_eps_1e-6"]) < 1e-15
+    # W = 0 reaches the same through the projection, whatever the base of
+    # the comb slots as long as it is constant
+    _, _, comb = orc.split_sinkhorn(np.zeros((2, 24)), np.array([1, 1, 5], np.float32),
+                                    np.concatenate([np.zeros(8), np.full(16, 0.3)]).astype(np.float32))
+    assert np.allclose(comb, (1 - EPS) / 4, rtol=1e-15, atol=0)
+    # without the eps in the denominators the value would be exactly 1/4
+    _, _, c0 = orc.split_sinkhorn(m, s, b, eps=0.0)
+    assert np.all(c0 == 0.25)
+
+
+def test_rank_one_logits_give_uniform_after_one_step(orc):
+    # eps = 0, iters = 1, L_jk = a_j + c_k: the row softmax leaves identical
+    # rows and the column normalisation then gives exactly 1/4 everywhere.
+    # A column softmax would give rows proportional to exp(a_j) instead.
+    rng = np.random.default_rng(9)
+    a, c = rng.standard_normal(4) * 2, rng.standard_normal(4) * 2
+    L = (a[:, None] + c[None, :])[None]
+    m, s, b = _logits_only(L)
+    _, _, comb = orc.split_sinkhorn(m, s, b, iters=1, eps=0.0)
+    assert np.allclose(comb, 0.25, rtol=0, atol=1e-15)
+
+
+def test_eps_zero_is_a_diagonal_scaling(orc):
+    # With eps = 0 every step multiplies rows or columns by positive factors,
+    # so all cross ratios of exp(L) survive:
+    #   C_jk C_j'k' / (C_jk' C_j'k) = exp(L_jk + L_j'k' - L_jk' - L_j'k).
+    # A transposed logit layout or a dropped step breaks this.
+    rng = np.random.default_rng(10)
+    L = rng.standard_normal((3, 4, 4)) * 1.5
+    m, s, b = _logits_only(L)
+    for iters in (1, 2, 20):
+        _, _, C = orc.split_sinkhorn(m, s, b, iters=iters, eps=0.0)
+        for t in range(3):
+            for j, jj, k, kk in [(0, 1, 0, 1), (0, 3, 1, 2), (2, 3, 0, 3), (1, 2, 2, 3)]:
+                lhs = C[t, j, k] * C[t, jj, kk] / (C[t, j, kk] * C[t, jj, k])
+                rhs = math.exp(L[t, j, k] + L[t, jj, kk] - L[t, j, kk] - L[t, jj, k])
+                assert abs(lhs / rhs - 1) < 1e-12
+        # the last step is a column normalisation: columns sum to one
+        assert np.allclose(C.sum(1), 1.0, rtol=0, atol=1e-14)
+
+
+def test_column_sums_after_last_step(orc):
+    # Exactly, colsum_k = S_k / (S_k + eps) with S_k the column sum before the
+    # last normalisation; with mild logits S_k ~ 1, so 1 - colsum ~ eps.
+    rng = np.random.default_rng(11)
+    L = rng.standard_normal((200, 4, 4))
+    m, s, b = _logits_only(L)
+    _, _, C = orc.split_sinkhorn(m, s, b)
+    dev = 1 - C.sum(1)
+    assert np.all(dev > 0) and np.all(dev < 2 * EPS)
+    assert np.all(np.abs(C.sum(2) - 1) < 1e-3)       # rows close to one
+    assert np.all(C > 0)
+
+
+def _sinkhorn_scaling_vectors(L, eps, iters, dps=60):
+    """Brute force in another formulation: after the softmax-plus-eps step,
+    C = diag(u) K0 diag(v) and only the scaling vectors are updated, at 60
+    significant digits."""
+    mp.mp.dps = dps
+    hc = len(L)
+    E = [[mp.e ** mp.mpf(L[j][k]) for k in range(hc)] for j in range(hc)]
+    K0 = [[E[j][k] / mp.fsum(E[j]) + eps for k in range(hc)] for j in range(hc)]
+    u = [mp.mpf(1)] * hc
+    v = [mp.mpf(1)] * hc
+
+    def col_step():
+        for k in range(hc):
+            cs = mp.fsum(u[j] * K0[j][k] * v[k] for j in range(hc))
+            v[k] = v[k] / (cs + eps)
+
+    def row_step():
+        for j in range(hc):
+            rs = mp.fsum(u[j] * K0[j][k] * v[k] for k in range(hc))
+            u[j] = u[j] / (rs + eps)
+
+    col_step()
+    for _ in range(iters - 1):
+        row_step()
+        col_step()
+    return [[u[j] * K0[j][k] * v[k] for k in range(hc)] for j in range(hc)]
+
+
+@pytest.mark.parametrize("spread,iters", [(1.0, 20), (6.0, 20), (20.0, 20), (3.0, 1), (3.0, 2), (3.0, 21)])
+def test_sinkhorn_vs_scaling_vector_brute_force(orc, spread, iters):
+    rng = np.random.default_rng(int(spread * 10) + iters)
+    L = rng.standard_normal((4, 4, 4)) * spread
+    m, s, b = _logits_only(L)
+    _, _, C = orc.split_sinkhorn(m, s, b, iters=iters)
+    eps = mp.mpf("1e-6")
+    for t in range(4):
+        ref = _sinkhorn_scaling_vectors(L[t], eps, iters)
+        for j in range(4):
+            for k in range(4):
+                r = float(ref[j][k])
+                assert abs(C[t, j, k] - r) <= 1e-13 * max(abs(r), 1e-3), (t, j, k)
+
+
+def test_iteration_count_matters(orc):
+    # steep logits are not converged after 20 steps: 19 or 21 differ
+    rng = np.random.default_rng(12)
+    L = rng.standard_normal((8, 4, 4)) * 8
+    m, s, b = _logits_only(L)
+    c19 = orc.split_sinkhorn(m, s, b, iters=19)[2]
+    c20 = orc.split_sinkhorn(m, s, b, iters=20)[2]
+    c21 = orc.split_sinkhorn(m, s, b, iters=21)[2]
+    assert np.abs(c20 - c19).max() > 1e-9 and np.abs(c21 - c20).max() > 1e-9
+
+
+def test_split_permutation_equivariance(orc):
+    # relabelling the streams by pi permutes pre/post and conjugates comb
+    rng = np.random.default_rng(13)
+    m = rng.standard_normal((5, 24))
+    s = np.array([1.1, 0.9, 2.5], np.float32)
+    b = rng.standard_normal(24).astype(np.float32)
+    pi = np.array([2, 0, 3, 1])
+    idx = np.concatenate([pi, 4 + pi, 8 + (pi[:, None] * 4 + pi[None, :]).ravel()])
+    p1, q1, c1 = orc.split_sinkhorn(m, s, b)
+    p2, q2, c2 = orc.split_sinkhorn(m[:, idx], s, b[idx])
+    assert np.allclose(p2, p1[:, pi], rtol=1e-15, atol=0)
+    assert np.allclose(q2, q1[:, pi], rtol=1e-15, atol=0)
+    assert np.allclose(c2, c1[:, pi][:, :, pi], rtol=1e-12, atol=1e-15)
+
+
+def test_split_rejects_bad_iters(orc):
+    with pytest.raises(ValueError):
+        orc.split_sinkhorn(np.zeros((1, 24)), np.ones(3, np.float32), np.zeros(24, np.float32), iters=0)
+
+
+# --------------------------------------------------------------------------
+# hc_pre / hc_post (Mix projection page, Block listing)
+
+
+def test_pre_one_hot_and_scaling(orc):
+    rng = np.random.default_rng(14)
+    n, hc, d = 6, 4, 64
+    R = _rand_bits(rng, (n, hc, d))
+    for k in range(hc):
+        w = np.zeros((n, hc))
+        w[:, k] = 1.0
+        assert np.array_equal(orc.pre(R, w), R[:, k, :])
+    w = rng.random((n, hc))
+    h1 = orc.pre(R, w)
+    h4 = orc.pre(R, w * 4.0)
+    assert np.array_equal(orc.bf16_to_f64(h4), orc.bf16_to_f64(h1) * 4.0)
+
+
+def test_pre_closed_form_pair_average(orc):
+    # pre = (1/2, 1/2, 0, 0): h = bf16((R0 + R1)/2) where the exact half-sum
+    # of two bf16 values is rounded once
+    rng = np.random.default_rng(15)
+    n, hc, d = 3, 4, 64
+    R = _rand_bits(rng, (n, hc, d))
+    w = np.zeros((n, hc))
+    w[:, :2] = 0.5
+    X = orc.bf16_to_f64(R)
+    ref = _bf16_bits_of(np.zeros(1))  # placeholder for dtype
+    got = orc.pre(R, w)
+    exact = (X[:, 0] + X[:, 1]) / 2           # exact in double
+    ref = hin.bits(torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16))
+    # exact fits float32 (<= 9 significant bits), so torch rounds it once
+    assert np.all(exact.astype(np.float32).astype(np.float64) == exact)
+    assert np.array_equal(got, ref)
+
+
+def test_post_special_cases(orc):
+    rng = np.random.default_rng(16)
+    n, hc, d = 5, 4, 64
+    R = _rand_bits(rng, (n, hc, d))
+    x = _rand_bits(rng, (n, d))
+    zeros = np.zeros((n, hc))
+    eye = np.broadcast_to(np.eye(hc), (n, hc, hc)).copy()
+    assert np.array_equal(orc.post(x, R, zeros, eye), R)            # comb = I, post = 0
+    out = orc.post(x, R, np.ones((n, hc)), np.zeros((n, hc, hc)))   # comb = 0, post = 1
+    assert all(np.array_equal(out[:, k], x) for k in range(hc))
+    # a single one at comb[j][k] sends input stream j to output stream k
+    for j, k in [(0, 2), (3, 1), (1, 1), (2, 0)]:
+        cb = np.zeros((n, hc, hc))
+        cb[:, j, k] = 1.0
+        out = orc.post(x, R, zeros, cb)
+        assert np.array_equal(out[:, k], R[:, j])
+        for kk in range(hc):
+            if kk != k:
+                assert np.all((out[:, kk] & 0x7FFF) == 0)
+
+
+def test_post_power_of_two_scaling(orc):
+    rng = np.random.default_rng(17)
+    n, hc, d = 4, 4, 64
+    R = _rand_bits(rng, (n, hc, d))
+    x = _rand_bits(rng, (n, d))
+    q = rng.random((n, hc)) * 2
+    c = rng.random((n, hc, hc))
+    a = orc.bf16_to_f64(orc.post(x, R, q, c))
+    b = orc.bf16_to_f64(orc.post(x, R, q * 0.125, c * 0.125))
+    assert np.array_equal(a * 0.125, b)
+
+
+def test_fused_closed_form_zero_weights(orc):
+    # W = 0, base = 0: pre = 1/2 + eps, post = 1, comb = (1 - eps)/4, so
+    # h = bf16((1/2 + eps) sum_k R_k) and every output stream is
+    # bf16(x + (1 - eps)/4 sum_j R_j).
+    rng = np.random.default_rng(18)
+    n, hc, d = 4, 4, 64
+    R = _rand_bits(rng, (n, hc, d))
+    x = _rand_bits(rng, (n, d))
+    W = np.zeros((24, hc * d), np.float32)
+    h, p, q, c, m = orc.fused(R, W, np.array([1, 1, 1], np.float32), np.zeros(24, np.float32))
+    X = orc.bf16_to_f64(R)
+    S = X.sum(1)
+    mp.mp.dps = 50
+    for t in range(n):
+        for cc in range(0, d, 5):
+            exact = (mp.mpf(1) / 2 + mp.mpf("1e-6")) * mp.mpf(S[t, cc])
+            assert h[t, cc] == orc.round_bf16(float(exact))
+    out = orc.post(x, R, q, c)
+    for k in range(1, hc):
+        assert np.array_equal(out[:, k], out[:, 0])
+    xv = orc.bf16_to_f64(x)
+    for t in range(n):
+        for cc in range(0, d, 7):
+            exact = mp.mpf(xv[t, cc]) + (1 - mp.mpf("1e-6")) / 4 * mp.mpf(S[t, cc])
+            assert out[t, 0, cc] == orc.round_bf16(float(exact))
+
+
+def test_diag_scale_exact(orc):
+    rng = np.random.default_rng(19)
+    h = _rand_bits(rng, (3, 64))
+    D = _bf16_bits_of(rng.uniform(0.5, 1.5, 64).astype(np.float32))
+    got = orc.diag_scale(h, D)
+    prod = orc.bf16_to_f64(h) * orc.bf16_to_f64(D)[None]     # exact in float32
+    ref = hin.bits(torch.from_numpy(prod.astype(np.float32)).to(torch.bfloat16))
+    assert np.array_equal(got, ref)
+
+
+def test_token_independence(orc):
+    # a token's result does not depend on the other tokens in the batch
+    w = hin.WORKLOADS["tiny"]
+    t = hin.make_inputs(w)
+    R, W, s, b = hin.bits(t["R"]).reshape(w.n, w.hc, w.d), t["W"].numpy(), t["scale"].numpy(), t["base"].numpy()
+    full = orc.fused(R, W, s, b)
+    part = orc.fused(R[5:9], W, s, b)
+    for a, c in zip(full, part):
+        assert np.array_equal(a[5:9], c)
