@@ -1,1 +1,279 @@
-"""libhc: hyper-connection residual mixing on MI355X (gfx950)."""
+"""libhc: hyper-connection residual-stream mixing on MI355X (gfx950).
+
+Thin Python binding over the C-ABI in ``include/hc.h``: each function here
+has the name of the C entry point it calls, checks dtypes, shapes, devices
+and contiguity, allocates outputs with torch (device memory only), passes
+raw pointers and torch's current HIP stream, and raises ``HCError`` on a
+non-zero status.  Every step of the computation runs in the HIP kernels of
+``libhc.so``; there is no fallback of any kind -- without the built library
+or a GPU tensor every call raises.
+
+Tensor shapes follow the pages' Block methods ("Mix projection" page):
+residual ``R`` [..., hc, d] bf16, sublayer output ``x`` / input ``h``
+[..., d] bf16, ``hc_fn`` [24, hc*d] fp32, ``hc_scale`` [3], ``hc_base``
+[24] fp32, mixes [..., 24], pre/post [..., hc], comb [..., hc, hc] fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "HCError", "load", "lib_path", "hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post",
+    "hc_fused_mix_pre", "hc_diag_scale", "hc_fused_workspace_bytes", "Workspace",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libhc.so")
+_lib = None
+
+HC_MIX = 24
+
+
+class HCError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = load().hc_status_str(status).decode()
+        super().__init__("%s failed: %s (status %d)" % (fn, msg, status))
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libhc.so (built in-tree by ``hyper_connection_residual_02_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("libhc.so is not built (%s); run "
+                          "`python -m hyper_connection_residual_02_amd.build`" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, F32, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                            ctypes.c_float, ctypes.c_size_t)
+    sig = {
+        "hc_mixes": [P, P, P, I64, I32, I32, F32, P, SZ, P],
+        "hc_split_sinkhorn": [P, P, P, P, P, P, I64, I32, I32, F32, P],
+        "hc_pre": [P, P, P, I64, I32, I32, P],
+        "hc_post": [P, P, P, P, P, I64, I32, I32, P],
+        "hc_fused_mix_pre": [P, P, P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, F32, F32, P],
+        "hc_diag_scale": [P, P, P, I64, I32, P],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.hc_fused_workspace_bytes.argtypes = [I64, I32, I32]
+    lib.hc_fused_workspace_bytes.restype = SZ
+    lib.hc_status_str.argtypes = [ctypes.c_int]
+    lib.hc_status_str.restype = ctypes.c_char_p
+    lib.hc_version.argtypes = []
+    lib.hc_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------- helpers
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype, dev=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device (libhc has no CPU path)" % name)
+    if dev is not None and t.device != dev:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, dev))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _call(fn: str, *args):
+    st = getattr(load(), fn)(*args)
+    if st != 0:
+        raise HCError(fn, st)
+
+
+def hc_fused_workspace_bytes(n: int, hc: int, d: int) -> int:
+    """Workspace bytes hc_mixes / hc_fused_mix_pre need (host-only query)."""
+    return int(load().hc_fused_workspace_bytes(int(n), int(hc), int(d)))
+
+
+class Workspace:
+    """A reusable, 256-byte aligned device workspace that grows on demand."""
+
+    def __init__(self, device=None):
+        self.device = torch.device(device) if device is not None else None
+        self._buf = None
+        self._off = 0
+        self.nbytes = 0
+
+    def get(self, nbytes: int, device: torch.device):
+        if self._buf is None or nbytes > self.nbytes or self._buf.device != device:
+            self._buf = torch.empty(int(nbytes) + 256, dtype=torch.uint8, device=device)
+            self._off = (-self._buf.data_ptr()) % 256
+            self.nbytes = int(nbytes)
+        return ctypes.c_void_p(self._buf.data_ptr() + self._off), self.nbytes
+
+
+_default_ws = {}
+
+
+def _workspace(ws, nbytes, dev):
+    if ws is None:
+        ws = _default_ws.setdefault(str(dev), Workspace())
+    return ws.get(max(int(nbytes), 256), dev)
+
+
+def _lead(R: torch.Tensor, hc: int, name="R"):
+    if R.dim() < 2 or R.shape[-2] != hc:
+        raise ValueError("%s must have shape [..., %d, d], got %s" % (name, hc, tuple(R.shape)))
+    lead = tuple(R.shape[:-2])
+    n = 1
+    for s in lead:
+        n *= s
+    return lead, n, R.shape[-1]
+
+
+# ------------------------------------------------------------------- ops
+
+def hc_mixes(R: torch.Tensor, hc_fn: torch.Tensor, norm_eps: float = 1e-20,
+             out: torch.Tensor | None = None, workspace: Workspace | None = None) -> torch.Tensor:
+    """mixes = (flatten(R) @ hc_fn^T) / RMS(flatten(R)); [..., 24] fp32."""
+    dev = R.device
+    _check(R, "R", torch.bfloat16)
+    _check(hc_fn, "hc_fn", torch.float32, dev)
+    hc = 4
+    lead, n, d = _lead(R, hc)
+    if tuple(hc_fn.shape) != (HC_MIX, hc * d):
+        raise ValueError("hc_fn must be [24, %d], got %s" % (hc * d, tuple(hc_fn.shape)))
+    if out is None:
+        out = torch.empty(*lead, HC_MIX, dtype=torch.float32, device=dev)
+    _check(out, "out", torch.float32, dev)
+    wp, wb = _workspace(workspace, hc_fused_workspace_bytes(n, hc, d), dev)
+    with torch.cuda.device(dev):
+        _call("hc_mixes", _ptr(R), _ptr(hc_fn), _ptr(out), n, hc, d, float(norm_eps), wp, wb,
+              _stream(dev))
+    return out
+
+
+def hc_split_sinkhorn(mixes: torch.Tensor, hc_scale: torch.Tensor, hc_base: torch.Tensor,
+                      hc_mult: int = 4, sinkhorn_iters: int = 20, eps: float = 1e-6):
+    """(pre [...,hc], post [...,hc], comb [...,hc,hc]) from mixes [..., 24]."""
+    dev = mixes.device
+    _check(mixes, "mixes", torch.float32)
+    _check(hc_scale, "hc_scale", torch.float32, dev)
+    _check(hc_base, "hc_base", torch.float32, dev)
+    M = (2 + hc_mult) * hc_mult
+    if mixes.shape[-1] != M:
+        raise ValueError("mixes must be [..., %d]" % M)
+    lead = tuple(mixes.shape[:-1])
+    n = mixes.numel() // M
+    pre = torch.empty(*lead, hc_mult, dtype=torch.float32, device=dev)
+    post = torch.empty(*lead, hc_mult, dtype=torch.float32, device=dev)
+    comb = torch.empty(*lead, hc_mult, hc_mult, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _call("hc_split_sinkhorn", _ptr(mixes), _ptr(hc_scale), _ptr(hc_base), _ptr(pre),
+              _ptr(post), _ptr(comb), n, hc_mult, int(sinkhorn_iters), float(eps), _stream(dev))
+    return pre, post, comb
+
+
+def hc_pre(R: torch.Tensor, pre: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """h = bf16(sum_k pre[..., k] * R[..., k, :]); [..., d] bf16."""
+    dev = R.device
+    _check(R, "R", torch.bfloat16)
+    _check(pre, "pre", torch.float32, dev)
+    hc = 4
+    lead, n, d = _lead(R, hc)
+    if tuple(pre.shape) != lead + (hc,):
+        raise ValueError("pre must be %s" % (lead + (hc,),))
+    if out is None:
+        out = torch.empty(*lead, d, dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, dev)
+    with torch.cuda.device(dev):
+        _call("hc_pre", _ptr(R), _ptr(pre), _ptr(out), n, hc, d, _stream(dev))
+    return out
+
+
+def hc_post(x: torch.Tensor, R: torch.Tensor, post: torch.Tensor, comb: torch.Tensor,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """R'[..., k, :] = bf16(post[..., k] x + sum_j comb[..., j, k] R[..., j, :]).
+    ``out`` may be ``R`` itself (in place)."""
+    dev = R.device
+    _check(x, "x", torch.bfloat16, dev)
+    _check(R, "R", torch.bfloat16)
+    _check(post, "post", torch.float32, dev)
+    _check(comb, "comb", torch.float32, dev)
+    hc = 4
+    lead, n, d = _lead(R, hc)
+    if tuple(x.shape) != lead + (d,) or tuple(post.shape) != lead + (hc,) or \
+            tuple(comb.shape) != lead + (hc, hc):
+        raise ValueError("shape mismatch among x, R, post, comb")
+    if out is None:
+        out = torch.empty_like(R)
+    _check(out, "out", torch.bfloat16, dev)
+    with torch.cuda.device(dev):
+        _call("hc_post", _ptr(x), _ptr(R), _ptr(post), _ptr(comb), _ptr(out), n, hc, d,
+              _stream(dev))
+    return out
+
+
+def hc_fused_mix_pre(R: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tensor,
+                     hc_base: torch.Tensor, sinkhorn_iters: int = 20, hc_eps: float = 1e-6,
+                     norm_eps: float = 1e-20, want_pre: bool = True, want_mixes: bool = False,
+                     workspace: Workspace | None = None, out=None):
+    """hc_mixes + hc_split_sinkhorn + hc_pre in one pass over R.
+    Returns (h, pre or None, post, comb, mixes or None).  ``out`` may be a
+    dict of preallocated outputs (keys h, pre, post, comb, mixes)."""
+    dev = R.device
+    _check(R, "R", torch.bfloat16)
+    for t, nm in ((hc_fn, "hc_fn"), (hc_scale, "hc_scale"), (hc_base, "hc_base")):
+        _check(t, nm, torch.float32, dev)
+    hc = 4
+    lead, n, d = _lead(R, hc)
+    if tuple(hc_fn.shape) != (HC_MIX, hc * d):
+        raise ValueError("hc_fn must be [24, %d]" % (hc * d))
+    o = dict(out or {})
+    h = o.get("h") if o.get("h") is not None else torch.empty(*lead, d, dtype=torch.bfloat16, device=dev)
+    post = o.get("post") if o.get("post") is not None else torch.empty(*lead, hc, dtype=torch.float32, device=dev)
+    comb = o.get("comb") if o.get("comb") is not None else torch.empty(*lead, hc, hc, dtype=torch.float32, device=dev)
+    pre = o.get("pre")
+    if pre is None and want_pre:
+        pre = torch.empty(*lead, hc, dtype=torch.float32, device=dev)
+    mixes = o.get("mixes")
+    if mixes is None and want_mixes:
+        mixes = torch.empty(*lead, HC_MIX, dtype=torch.float32, device=dev)
+    wp, wb = _workspace(workspace, hc_fused_workspace_bytes(n, hc, d), dev)
+    with torch.cuda.device(dev):
+        _call("hc_fused_mix_pre", _ptr(R), _ptr(hc_fn), _ptr(hc_scale), _ptr(hc_base), _ptr(h),
+              _ptr(pre), _ptr(post), _ptr(comb), _ptr(mixes), wp, wb, n, hc, d,
+              int(sinkhorn_iters), float(hc_eps), float(norm_eps), _stream(dev))
+    return h, pre, post, comb, mixes
+
+
+def hc_diag_scale(h: torch.Tensor, D: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """x = bf16(h * D) with D [d] bf16: the chained-stack stand-in sublayer."""
+    dev = h.device
+    _check(h, "h", torch.bfloat16)
+    _check(D, "D", torch.bfloat16, dev)
+    d = h.shape[-1]
+    if tuple(D.shape) != (d,):
+        raise ValueError("D must be [%d]" % d)
+    n = h.numel() // d
+    if out is None:
+        out = torch.empty_like(h)
+    _check(out, "out", torch.bfloat16, dev)
+    with torch.cuda.device(dev):
+        _call("hc_diag_scale", _ptr(h), _ptr(D), _ptr(out), n, d, _stream(dev))
+    return out

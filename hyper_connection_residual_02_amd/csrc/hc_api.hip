@@ -1,0 +1,211 @@
+// hc_api.hip -- the C-ABI of libhc: argument checks (host only, before any
+// HIP call) and dispatch to the kernels.  See include/hc.h for the contract
+// of each entry point.
+#include <math.h>
+#include <mutex>
+
+#include "../../include/hc.h"
+#include "hc_launch.hpp"
+
+namespace hc {
+
+// ------------------------------------------------------- device properties
+static std::mutex g_mu;
+static int g_cus[64];
+
+int num_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        g_cus[dev] = v;
+    }
+    return g_cus[dev];
+}
+
+}  // namespace hc
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;   // bound on n*hc*d (sizes stay far from overflow)
+
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+struct Span {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+Span span(const void* p, uint64_t bytes) { return Span{(uintptr_t)p, (uintptr_t)p + bytes}; }
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool finite_nonneg(float v) { return isfinite(v) && v >= 0.0f; }
+
+int check_nd(int64_t n, int32_t hc, int32_t d) {
+    if (n < 0 || d <= 0 || d % 8 != 0) return HC_ERR_SHAPE;
+    if (hc != 4) return HC_ERR_UNSUPPORTED;
+    if (n > 0 && n > kMaxElems / ((int64_t)hc * d)) return HC_ERR_SHAPE;
+    return HC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hc_status_str(int s) {
+    switch (s) {
+        case HC_OK: return "HC_OK";
+        case HC_ERR_NULL: return "HC_ERR_NULL: a required pointer is NULL";
+        case HC_ERR_SHAPE: return "HC_ERR_SHAPE: bad n or d (n >= 0, d > 0, d % 8 == 0)";
+        case HC_ERR_ALIGN: return "HC_ERR_ALIGN: tensor pointers must be 16-byte aligned (scale/base 4-byte)";
+        case HC_ERR_UNSUPPORTED: return "HC_ERR_UNSUPPORTED: hc must be 4, sinkhorn_iters >= 1, d tileable";
+        case HC_ERR_WORKSPACE: return "HC_ERR_WORKSPACE: workspace missing or too small";
+        case HC_ERR_ALIAS: return "HC_ERR_ALIAS: an output overlaps an input or another output";
+        case HC_ERR_VALUE: return "HC_ERR_VALUE: epsilon must be finite and >= 0";
+        case HC_ERR_LAUNCH: return "HC_ERR_LAUNCH: the HIP runtime refused a kernel launch";
+        case HC_ERR_DEVICE: return "HC_ERR_DEVICE: device query failed";
+        default: return "HC_ERR_?: unknown status";
+    }
+}
+
+const char* hc_version(void) { return "0.1.0"; }
+
+int hc_pre(const void* R, const float* pre, void* h, int64_t n, int32_t hc_, int32_t d, void* stream) {
+    int st = check_nd(n, hc_, d);
+    if (st) return st;
+    if (n == 0) return HC_OK;
+    if (!R || !pre || !h) return HC_ERR_NULL;
+    if (!al16(R) || !al16(pre) || !al16(h)) return HC_ERR_ALIGN;
+    const uint64_t nd = (uint64_t)n * d;
+    Span sh = span(h, nd * 2);
+    if (overlap(sh, span(R, nd * 4 * 2)) || overlap(sh, span(pre, (uint64_t)n * 4 * 4))) return HC_ERR_ALIAS;
+    return hc::launch_pre(R, pre, h, n, d, (hipStream_t)stream) ? HC_ERR_LAUNCH : HC_OK;
+}
+
+int hc_post(const void* x, const void* R, const float* post, const float* comb, void* R_out, int64_t n,
+            int32_t hc_, int32_t d, void* stream) {
+    int st = check_nd(n, hc_, d);
+    if (st) return st;
+    if (n == 0) return HC_OK;
+    if (!x || !R || !post || !comb || !R_out) return HC_ERR_NULL;
+    if (!al16(x) || !al16(R) || !al16(post) || !al16(comb) || !al16(R_out)) return HC_ERR_ALIGN;
+    const uint64_t nd = (uint64_t)n * d;
+    Span so = span(R_out, nd * 4 * 2);
+    if (R_out != R && overlap(so, span(R, nd * 4 * 2))) return HC_ERR_ALIAS;
+    if (overlap(so, span(x, nd * 2)) || overlap(so, span(post, (uint64_t)n * 16)) ||
+        overlap(so, span(comb, (uint64_t)n * 64)))
+        return HC_ERR_ALIAS;
+    return hc::launch_post(x, R, post, comb, R_out, n, d, (hipStream_t)stream) ? HC_ERR_LAUNCH : HC_OK;
+}
+
+int hc_diag_scale(const void* h, const void* D, void* x, int64_t n, int32_t d, void* stream) {
+    int st = check_nd(n, 4, d);
+    if (st) return st;
+    if (n == 0) return HC_OK;
+    if (!h || !D || !x) return HC_ERR_NULL;
+    if (!al16(h) || !al16(D) || !al16(x)) return HC_ERR_ALIGN;
+    const uint64_t nd = (uint64_t)n * d;
+    Span sx = span(x, nd * 2);
+    if (overlap(sx, span(h, nd * 2)) || overlap(sx, span(D, (uint64_t)d * 2))) return HC_ERR_ALIAS;
+    return hc::launch_diag(h, D, x, n, d, (hipStream_t)stream) ? HC_ERR_LAUNCH : HC_OK;
+}
+
+int hc_split_sinkhorn(const float* mixes, const float* hc_scale, const float* hc_base, float* pre, float* post,
+                      float* comb, int64_t n, int32_t hc_, int32_t sinkhorn_iters, float hc_eps, void* stream) {
+    if (n < 0) return HC_ERR_SHAPE;
+    if (hc_ != 4 || sinkhorn_iters < 1) return HC_ERR_UNSUPPORTED;
+    if (!finite_nonneg(hc_eps)) return HC_ERR_VALUE;
+    if (n > kMaxElems / 64) return HC_ERR_SHAPE;
+    if (n == 0) return HC_OK;
+    if (!mixes || !hc_scale || !hc_base || !pre || !post || !comb) return HC_ERR_NULL;
+    if (!al16(mixes) || !al16(pre) || !al16(post) || !al16(comb) || !al4(hc_scale) || !al4(hc_base))
+        return HC_ERR_ALIGN;
+    const Span ins[] = {span(mixes, (uint64_t)n * 96), span(hc_scale, 12), span(hc_base, 96)};
+    const Span outs[] = {span(pre, (uint64_t)n * 16), span(post, (uint64_t)n * 16), span(comb, (uint64_t)n * 64)};
+    for (const Span& o : outs)
+        for (const Span& i : ins)
+            if (overlap(o, i)) return HC_ERR_ALIAS;
+    if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2])) return HC_ERR_ALIAS;
+    return hc::launch_split(mixes, hc_scale, hc_base, pre, post, comb, n, sinkhorn_iters, hc_eps,
+                            (hipStream_t)stream)
+               ? HC_ERR_LAUNCH
+               : HC_OK;
+}
+
+size_t hc_fused_workspace_bytes(int64_t n, int32_t hc_, int32_t d) {
+    if (check_nd(n, hc_, d) != HC_OK || n == 0) return 0;
+    hc::CoopPlan p;
+    if (!hc::coop_plan(n, d, p)) return 0;
+    return p.ws_bytes;
+}
+
+static int coop_common(const void* R, const float* hc_fn, void* workspace, size_t ws_bytes, int64_t n, int32_t hc_,
+                       int32_t d, float norm_eps, hc::CoopPlan& p) {
+    int st = check_nd(n, hc_, d);
+    if (st) return st;
+    if (!finite_nonneg(norm_eps)) return HC_ERR_VALUE;
+    if (n == 0) return HC_OK;
+    if (hc::coop_ks(d) == 0) return HC_ERR_UNSUPPORTED;
+    if (!R || !hc_fn) return HC_ERR_NULL;
+    if (!workspace) return HC_ERR_WORKSPACE;
+    if (!al16(R) || !al16(hc_fn) || ((uintptr_t)workspace & 255u)) return HC_ERR_ALIGN;
+    if (!hc::coop_plan(n, d, p)) return HC_ERR_UNSUPPORTED;
+    if (ws_bytes < p.ws_bytes) return HC_ERR_WORKSPACE;
+    return HC_OK;
+}
+
+int hc_mixes(const void* R, const float* hc_fn, float* mixes, int64_t n, int32_t hc_, int32_t d, float norm_eps,
+             void* workspace, size_t workspace_bytes, void* stream) {
+    hc::CoopPlan p;
+    int st = coop_common(R, hc_fn, workspace, workspace_bytes, n, hc_, d, norm_eps, p);
+    if (st || n == 0) return st;
+    if (!mixes) return HC_ERR_NULL;
+    if (!al16(mixes)) return HC_ERR_ALIGN;
+    const uint64_t K = (uint64_t)4 * d;
+    const Span sm = span(mixes, (uint64_t)n * 96);
+    if (overlap(sm, span(R, (uint64_t)n * K * 2)) || overlap(sm, span(hc_fn, 24 * K * 4)) ||
+        overlap(sm, span(workspace, p.ws_bytes)))
+        return HC_ERR_ALIAS;
+    return hc::launch_coop(p, R, hc_fn, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, mixes, workspace, n, d,
+                           1, 0.0f, norm_eps, false, (hipStream_t)stream)
+               ? HC_ERR_LAUNCH
+               : HC_OK;
+}
+
+int hc_fused_mix_pre(const void* R, const float* hc_fn, const float* hc_scale, const float* hc_base, void* h,
+                     float* pre, float* post, float* comb, float* mixes, void* workspace, size_t workspace_bytes,
+                     int64_t n, int32_t hc_, int32_t d, int32_t sinkhorn_iters, float hc_eps, float norm_eps,
+                     void* stream) {
+    if (hc_ == 4 && sinkhorn_iters < 1) return HC_ERR_UNSUPPORTED;
+    if (!finite_nonneg(hc_eps)) return HC_ERR_VALUE;
+    hc::CoopPlan p;
+    int st = coop_common(R, hc_fn, workspace, workspace_bytes, n, hc_, d, norm_eps, p);
+    if (st || n == 0) return st;
+    if (!hc_scale || !hc_base || !h || !post || !comb) return HC_ERR_NULL;
+    if (!al4(hc_scale) || !al4(hc_base) || !al16(h) || !al16(post) || !al16(comb) || (pre && !al16(pre)) ||
+        (mixes && !al16(mixes)))
+        return HC_ERR_ALIGN;
+    const uint64_t K = (uint64_t)4 * d;
+    const Span ins[] = {span(R, (uint64_t)n * K * 2), span(hc_fn, 24 * K * 4), span(hc_scale, 12),
+                        span(hc_base, 96), span(workspace, p.ws_bytes)};
+    Span outs[5];
+    int no = 0;
+    outs[no++] = span(h, (uint64_t)n * d * 2);
+    outs[no++] = span(post, (uint64_t)n * 16);
+    outs[no++] = span(comb, (uint64_t)n * 64);
+    if (pre) outs[no++] = span(pre, (uint64_t)n * 16);
+    if (mixes) outs[no++] = span(mixes, (uint64_t)n * 96);
+    for (int i = 0; i < no; ++i) {
+        for (const Span& s : ins)
+            if (overlap(outs[i], s)) return HC_ERR_ALIAS;
+        for (int j = i + 1; j < no; ++j)
+            if (overlap(outs[i], outs[j])) return HC_ERR_ALIAS;
+    }
+    return hc::launch_coop(p, R, hc_fn, hc_scale, hc_base, h, pre, post, comb, mixes, workspace, n, d,
+                           sinkhorn_iters, hc_eps, norm_eps, true, (hipStream_t)stream)
+               ? HC_ERR_LAUNCH
+               : HC_OK;
+}
+
+}  // extern "C"

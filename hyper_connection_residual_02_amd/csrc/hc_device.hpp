@@ -1,0 +1,114 @@
+// hc_device.hpp -- device helpers shared by the libhc kernels (gfx950 only).
+//
+// bf16 <-> float/double conversions, the correctly rounded double -> bf16
+// conversion used for every bf16 output, cross-lane reductions inside a
+// 16-lane row (DPP), and the per-token split + epsilon-Sinkhorn that the
+// standalone and fused kernels share so that both give bitwise the same
+// coefficients.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hc {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+constexpr int kHC = 4;                      // streams per token (hc_mult)
+constexpr int kMix = (2 + kHC) * kHC;       // 24 mix numbers per token
+
+// ---------------------------------------------------------------- bf16 bits
+// A 32-bit word holds two bf16 values: element 0 in the low half.
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t bf16_rn(float f) {
+    __bf16 b = (__bf16)f;
+    return (uint32_t)__builtin_bit_cast(uint16_t, b);
+}
+
+// double -> bf16 bits, correctly rounded (nearest even), from a single
+// conceptual rounding of y.  The fast path rounds y to float and then to
+// bf16; that double rounding can only go wrong when the float lands exactly
+// on a bf16 halfway point while y itself does not, in which case the float
+// is nudged one float ulp towards y before the second rounding.
+__device__ __forceinline__ uint32_t bf16_rn_f64(double y) {
+    float f = (float)y;
+    uint32_t u = __float_as_uint(f);
+    if (__builtin_expect((u & 0xFFFFu) == 0x8000u, 0)) {
+        double back = (double)f;
+        if (back != y) {
+            u = (__builtin_fabs(y) > __builtin_fabs(back)) ? u + 1u : u - 1u;
+            f = __uint_as_float(u);
+        }
+    }
+    return bf16_rn(f);
+}
+
+// Pack two bf16 bit patterns into one word (element 0 low).
+__device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
+
+// ------------------------------------------------ 16-lane row reductions
+// DPP controls (gfx9 encoding): quad_perm [1,0,3,2] and [2,3,0,1], row_ror 4 / 8.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum / max over the 4 lanes of a quad (lanes 4j..4j+3 of a 16-lane row).
+__device__ __forceinline__ float quad_sum(float v) {
+    v = v + dpp<0xB1>(v);
+    return v + dpp<0x4E>(v);
+}
+__device__ __forceinline__ float quad_max(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    return fmaxf(v, dpp<0x4E>(v));
+}
+// Sum over lanes e, e+4, e+8, e+12 (mod 16) of a 16-lane row.
+__device__ __forceinline__ float col4_sum(float v) {
+    v = v + dpp<0x128>(v);
+    return v + dpp<0x124>(v);
+}
+
+// Logistic function in float.
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+// ------------------------------------------------- split + epsilon-Sinkhorn
+// One token per 16-lane row; lane e = (lane & 15) holds comb entry
+// (j, k) = (e / 4, e % 4).  m points at the token's 24 mixes (any memory
+// the lane can read).  Follows the hc_split_sinkhorn listing of the
+// "Reading weights" page: pre = sigmoid(s0*m_j + b_j) + eps,
+// post = 2 sigmoid(s1*m_{4+j} + b_{4+j}), logits s2*m_{8+4j+k} + b_{8+4j+k};
+// row softmax + eps, column normalisation, then (iters - 1) x (row, column)
+// normalisations, each dividing by (sum + eps).
+// Outputs: pre_o / post_o valid in lanes e < 4 (stream e); comb_o in all.
+__device__ __forceinline__ void split_sinkhorn16(const float* m, float s0, float s1, float s2,
+                                                 const float* __restrict__ base, int iters,
+                                                 float eps, float& pre_o, float& post_o,
+                                                 float& comb_o) {
+    const int e = threadIdx.x & 15;
+    const int j4 = e & 3;
+    pre_o = sigmoidf_(m[j4] * s0 + base[j4]) + eps;
+    post_o = 2.0f * sigmoidf_(m[kHC + j4] * s1 + base[kHC + j4]);
+    float c = m[2 * kHC + e] * s2 + base[2 * kHC + e];
+    // row softmax (max subtracted for range only), then + eps
+    float mx = quad_max(c);
+    float ex = expf(c - mx);
+    float rs = quad_sum(ex);
+    c = ex / rs + eps;
+    // column normalisation
+    float cs = col4_sum(c);
+    c = c * __builtin_amdgcn_rcpf(cs + eps);
+    for (int it = 1; it < iters; ++it) {
+        rs = quad_sum(c);
+        c = c * __builtin_amdgcn_rcpf(rs + eps);
+        cs = col4_sum(c);
+        c = c * __builtin_amdgcn_rcpf(cs + eps);
+    }
+    comb_o = c;
+}
+
+}  // namespace hc

@@ -1,0 +1,46 @@
+// hc_launch.hpp -- internal launch interface between the C-ABI layer and the
+// kernel translation units.  Host code only; not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hc {
+
+// Compute units of the current device (cached per device id).
+int num_cus();
+
+// Streaming kernels (hc_stream.hip).  Return 0, or -1 if the launch failed.
+int launch_pre(const void* R, const float* pre, void* h, int64_t n, int d, hipStream_t s);
+int launch_post(const void* x, const void* R, const float* post, const float* comb, void* Rout,
+                int64_t n, int d, hipStream_t s);
+int launch_diag(const void* h, const void* D, void* x, int64_t n, int d, hipStream_t s);
+
+// Standalone split + Sinkhorn (hc_sinkhorn.hip).
+int launch_split(const float* mixes, const float* scale, const float* base, float* pre, float* post,
+                 float* comb, int64_t n, int iters, float eps, hipStream_t s);
+
+// Work split of the projection kernels (hc_coop.hip): each group of G
+// workgroups shares every token; member q owns a 32*KS-feature slice of
+// each stream and its 24-column slice of the weights.
+struct CoopPlan {
+    int KS;          // 8-feature MFMA k-steps per wave (slice = 4 waves * 8 * KS features)
+    int G;           // members per group (d / (32 * KS))
+    int TM;          // 16-token MFMA tiles per round (T = 16 * TM tokens)
+    int NG;          // groups (workgroups launched = G * NG)
+    int64_t ntiles;  // ceil(n / T)
+    size_t ws_part;  // byte offsets into the workspace
+    size_t ws_pre;
+    size_t ws_cnt;
+    size_t ws_bytes;
+};
+// K-steps per wave for d (0: d cannot be tiled).  Host only, no HIP calls.
+int coop_ks(int d);
+// Returns false if d cannot be tiled (d % 32 != 0 or no KS in 1..8 gives G <= 32).
+bool coop_plan(int64_t n, int d, CoopPlan& p);
+int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* scale, const float* base,
+                void* h, float* pre, float* post, float* comb, float* mixes, void* ws, int64_t n, int d,
+                int iters, float eps, float norm_eps, bool fused, hipStream_t s);
+
+}  // namespace hc

@@ -1,0 +1,177 @@
+// hc_stream.hip -- the streaming kernels: hc_pre, hc_post and the
+// chained-stack stand-in sublayer (diagonal scale).
+//
+// All three are HBM-bound elementwise passes.  Each thread owns one 16-byte
+// chunk (8 consecutive features) of one token and touches every stream of
+// that chunk, so every global access is a coalesced 16-byte vector access.
+// When a wave's 64 chunks all belong to one token (d a multiple of 512) the
+// token's coefficients are wave-uniform and come through scalar loads.
+//
+// Numerics: each output is the correctly rounded bf16 of its defining sum.
+// A product of an fp32 coefficient and a bf16 value has at most 32
+// significant bits, so it is exact in double; the sum of the (at most 5)
+// products is accumulated in double and rounded once (bf16_rn_f64).
+
+#include "hc_device.hpp"
+#include "hc_launch.hpp"
+
+namespace hc {
+
+// Work item = (token t, 16-byte chunk c8 of d).  A wave of 64 items covers
+// 512 features of one token when d8 % 64 == 0 ("uniform" mode); otherwise
+// items are numbered flat and each lane loads its own coefficients.
+struct ItemMap {
+    uint32_t d8;       // chunks per token row
+    uint64_t items;    // n * d8
+};
+
+__device__ __forceinline__ void item_of(uint64_t it, uint32_t d8, uint64_t& t, uint32_t& c8) {
+    if (it < 0xFFFFFFFFull) {
+        uint32_t i32 = (uint32_t)it;
+        t = i32 / d8;
+        c8 = i32 - (uint32_t)t * d8;
+    } else {
+        t = it / d8;
+        c8 = (uint32_t)(it - t * d8);
+    }
+}
+
+// ------------------------------------------------------------------ hc_pre
+// "Mix projection" page, Block.hc_pre: h_c = bf16(sum_k pre_k R_{k,c}).
+template <bool UNIFORM>
+__global__ __launch_bounds__(256) void k_pre(const u32x4* __restrict__ R, const float* __restrict__ pre,
+                                             u32x4* __restrict__ h, ItemMap map) {
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t it = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; it < map.items; it += stride) {
+        uint64_t t;
+        uint32_t c8;
+        item_of(it, map.d8, t, c8);
+        if (UNIFORM) t = __builtin_amdgcn_readfirstlane((uint32_t)t) | ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(t >> 32)) << 32);
+        const f32x4 p = *reinterpret_cast<const f32x4*>(pre + t * kHC);
+        const double p0 = p[0], p1 = p[1], p2 = p[2], p3 = p[3];
+        const uint64_t row = t * kHC * (uint64_t)map.d8 + c8;
+        const u32x4 r0 = __builtin_nontemporal_load(R + row);
+        const u32x4 r1 = __builtin_nontemporal_load(R + row + map.d8);
+        const u32x4 r2 = __builtin_nontemporal_load(R + row + 2 * (uint64_t)map.d8);
+        const u32x4 r3 = __builtin_nontemporal_load(R + row + 3 * (uint64_t)map.d8);
+        u32x4 out;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            double lo = p0 * (double)bf_lo(r0[w]);
+            lo = __builtin_fma(p1, (double)bf_lo(r1[w]), lo);
+            lo = __builtin_fma(p2, (double)bf_lo(r2[w]), lo);
+            lo = __builtin_fma(p3, (double)bf_lo(r3[w]), lo);
+            double hi = p0 * (double)bf_hi(r0[w]);
+            hi = __builtin_fma(p1, (double)bf_hi(r1[w]), hi);
+            hi = __builtin_fma(p2, (double)bf_hi(r2[w]), hi);
+            hi = __builtin_fma(p3, (double)bf_hi(r3[w]), hi);
+            out[w] = pack2(bf16_rn_f64(lo), bf16_rn_f64(hi));
+        }
+        __builtin_nontemporal_store(out, h + t * map.d8 + c8);
+    }
+}
+
+// ----------------------------------------------------------------- hc_post
+// "Mix projection" page, Block.hc_post:
+//   R'_{k,c} = bf16(post_k x_c + sum_j comb[j][k] R_{j,c}).
+template <bool UNIFORM>
+__global__ __launch_bounds__(256) void k_post(const u32x4* __restrict__ x, const u32x4* R,
+                                              const float* __restrict__ post, const float* __restrict__ comb,
+                                              u32x4* Rout, ItemMap map) {
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t it = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; it < map.items; it += stride) {
+        uint64_t t;
+        uint32_t c8;
+        item_of(it, map.d8, t, c8);
+        if (UNIFORM) t = __builtin_amdgcn_readfirstlane((uint32_t)t) | ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(t >> 32)) << 32);
+        const f32x4 q = *reinterpret_cast<const f32x4*>(post + t * kHC);
+        f32x4 cb[kHC];
+#pragma unroll
+        for (int j = 0; j < kHC; ++j) cb[j] = *reinterpret_cast<const f32x4*>(comb + (t * kHC + j) * kHC);
+        const uint64_t row = t * kHC * (uint64_t)map.d8 + c8;
+        const u32x4 xv = __builtin_nontemporal_load(x + t * map.d8 + c8);
+        u32x4 r[kHC];
+#pragma unroll
+        for (int j = 0; j < kHC; ++j) r[j] = __builtin_nontemporal_load(R + row + j * (uint64_t)map.d8);
+        u32x4 out[kHC];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const double xl = bf_lo(xv[w]), xh = bf_hi(xv[w]);
+            double rl[kHC], rh[kHC];
+#pragma unroll
+            for (int j = 0; j < kHC; ++j) {
+                rl[j] = bf_lo(r[j][w]);
+                rh[j] = bf_hi(r[j][w]);
+            }
+#pragma unroll
+            for (int k = 0; k < kHC; ++k) {
+                double yl = (double)q[k] * xl;
+                double yh = (double)q[k] * xh;
+#pragma unroll
+                for (int j = 0; j < kHC; ++j) {
+                    yl = __builtin_fma((double)cb[j][k], rl[j], yl);
+                    yh = __builtin_fma((double)cb[j][k], rh[j], yh);
+                }
+                out[k][w] = pack2(bf16_rn_f64(yl), bf16_rn_f64(yh));
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kHC; ++k) __builtin_nontemporal_store(out[k], Rout + row + k * (uint64_t)map.d8);
+    }
+}
+
+// ----------------------------------------------------------- diag_scale
+// x_c = bf16(h_c * D_c): the product of two bf16 values is exact in float.
+__global__ __launch_bounds__(256) void k_diag(const u32x4* __restrict__ h, const u32x4* __restrict__ D,
+                                              u32x4* __restrict__ x, ItemMap map) {
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t it = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; it < map.items; it += stride) {
+        uint64_t t;
+        uint32_t c8;
+        item_of(it, map.d8, t, c8);
+        const u32x4 hv = __builtin_nontemporal_load(h + t * map.d8 + c8);
+        const u32x4 dv = D[c8];
+        u32x4 out;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            out[w] = pack2(bf16_rn(bf_lo(hv[w]) * bf_lo(dv[w])), bf16_rn(bf_hi(hv[w]) * bf_hi(dv[w])));
+        __builtin_nontemporal_store(out, x + t * map.d8 + c8);
+    }
+}
+
+// ------------------------------------------------------------- launchers
+static int grid_for(uint64_t items, int per_cu_blocks) {
+    uint64_t blocks = (items + 255) / 256;
+    uint64_t cap = (uint64_t)num_cus() * per_cu_blocks;
+    if (blocks > cap) blocks = cap;
+    return (int)(blocks ? blocks : 1);
+}
+
+int launch_pre(const void* R, const float* pre, void* h, int64_t n, int d, hipStream_t s) {
+    ItemMap m{(uint32_t)(d / 8), (uint64_t)n * (uint64_t)(d / 8)};
+    const int g = grid_for(m.items, 8);
+    if (m.d8 % 64 == 0)
+        k_pre<true><<<g, 256, 0, s>>>((const u32x4*)R, pre, (u32x4*)h, m);
+    else
+        k_pre<false><<<g, 256, 0, s>>>((const u32x4*)R, pre, (u32x4*)h, m);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_post(const void* x, const void* R, const float* post, const float* comb, void* Rout,
+                int64_t n, int d, hipStream_t s) {
+    ItemMap m{(uint32_t)(d / 8), (uint64_t)n * (uint64_t)(d / 8)};
+    const int g = grid_for(m.items, 8);
+    if (m.d8 % 64 == 0)
+        k_post<true><<<g, 256, 0, s>>>((const u32x4*)x, (const u32x4*)R, post, comb, (u32x4*)Rout, m);
+    else
+        k_post<false><<<g, 256, 0, s>>>((const u32x4*)x, (const u32x4*)R, post, comb, (u32x4*)Rout, m);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_diag(const void* h, const void* D, void* x, int64_t n, int d, hipStream_t s) {
+    ItemMap m{(uint32_t)(d / 8), (uint64_t)n * (uint64_t)(d / 8)};
+    k_diag<<<grid_for(m.items, 8), 256, 0, s>>>((const u32x4*)h, (const u32x4*)D, (u32x4*)x, m);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace hc

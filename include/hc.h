@@ -1,0 +1,177 @@
+/*
+ * hc.h -- libhc: hyper-connection residual-stream mixing on MI355X (gfx950).
+ *
+ * Every token carries hc = 4 parallel copies ("streams") of a d-wide bf16
+ * residual.  For each sublayer the library
+ *   1. projects the flattened 4d stream to (2+hc)*hc = 24 mix numbers and
+ *      divides them by the stream's root mean square          (hc_mixes),
+ *   2. turns the mixes into read weights pre, write weights post and a
+ *      4x4 combination matrix comb made nearly doubly stochastic by an
+ *      epsilon-Sinkhorn iteration                            (hc_split_sinkhorn),
+ *   3. collapses the streams into the sublayer input          (hc_pre),
+ *   4. expands the sublayer output back into four streams     (hc_post),
+ * and offers steps 1-3 as one fused call (hc_fused_mix_pre).
+ *
+ * Sources (the pages' titles and the parts of them that define each call):
+ *   "DeepSeek V4.1 - Mix projection": the mix formula (RMS over all hc*d
+ *     features, eps 1e-20, float32) and the Block.hc_mixes / hc_pre /
+ *     hc_post listing;
+ *   "DeepSeek V4.1 - Reading weights": the learned-pre formula and the
+ *     hc_split_sinkhorn kernel listing and its Python wrapper;
+ *   "DeepSeek V4.1 attention": config.json (hc_mult 4, hc_sinkhorn_iters
+ *     20, hc_eps 1e-6, norm_eps 1e-20, dim 5120).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers are device pointers on the current HIP device, except where a
+ * comment says otherwise.  bf16 tensors are passed as `const void *` / `void *`
+ * holding 16-bit bf16 patterns.  All tensors are dense row-major:
+ *   R      bf16 [n][hc][d]     residual; element (k, c) of token t at
+ *                              (t*hc + k)*d + c (stream-major flattening)
+ *   x, h   bf16 [n][d]         sublayer output / sublayer input
+ *   hc_fn  fp32 [24][hc*d]     mix projection weights (row j, column k*d + c)
+ *   hc_scale fp32 [3]          scales for pre, post, comb (in that order)
+ *   hc_base  fp32 [24]         offsets, indexed like the mixes
+ *   mixes  fp32 [n][24]        [0,4) pre logits, [4,8) post, [8,24) comb
+ *                              logits row-major (j*4 + k)
+ *   pre, post fp32 [n][hc];  comb fp32 [n][hc][hc] with comb[j][k] at j*hc + k
+ * n = B*T tokens (the caller flattens batch and sequence).  hc must be 4.
+ *
+ * Ownership: the caller owns every buffer.  The library never allocates,
+ * frees or synchronises; each call enqueues its kernels on `stream` (a
+ * hipStream_t; NULL is the default stream) and returns.  Errors found by
+ * the host-side checks are returned before any HIP call is made; device
+ * faults surface at the caller's next synchronisation.  n == 0 returns
+ * HC_OK without launching anything.
+ *
+ * Alignment: every tensor pointer must be 16-byte aligned, except hc_scale
+ * and hc_base (4-byte).  Outputs must not overlap inputs or each other,
+ * except where an entry point says so.
+ *
+ * Numerics: mixes, pre, post and comb are computed in float32 (the pages'
+ * precision).  Every bf16 output (h, R') is the correctly rounded
+ * (nearest-even) value of its defining sum of products of the given fp32
+ * coefficients and bf16 inputs: the kernels accumulate in double, where
+ * those products are exact, and round once.
+ */
+#ifndef LIBHC_HC_H
+#define LIBHC_HC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hc_status {
+    HC_OK = 0,
+    HC_ERR_NULL = -1,        /* a required pointer is NULL */
+    HC_ERR_SHAPE = -2,       /* n < 0, d <= 0, d % 8 != 0, or sizes overflow */
+    HC_ERR_ALIGN = -3,       /* a pointer is not suitably aligned */
+    HC_ERR_UNSUPPORTED = -4, /* hc != 4, sinkhorn_iters < 1, or a d the
+                                projection kernels cannot tile */
+    HC_ERR_WORKSPACE = -5,   /* workspace missing or too small */
+    HC_ERR_ALIAS = -6,       /* an output overlaps an input or another output */
+    HC_ERR_VALUE = -7,       /* an epsilon is negative or not finite */
+    HC_ERR_LAUNCH = -8,      /* the HIP runtime refused a launch */
+    HC_ERR_DEVICE = -9       /* device query failed (no device, bad id) */
+} hc_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *hc_status_str(int status);
+
+/* Library version as "major.minor.patch" (static string). */
+const char *hc_version(void);
+
+/*
+ * hc_mixes -- "Mix projection" page, the mix formula and Block.hc_mixes:
+ *   r_t = 1 / sqrt( sum_i R[t][i]^2 / (hc*d) + norm_eps )
+ *   mixes[t][j] = r_t * sum_i R[t][i] * hc_fn[j][i],   i over the hc*d
+ *   flattened features, j < 24.
+ * The library's hc_mixes stops at the mixes; the pages' Block.hc_mixes
+ * also runs the split (call hc_split_sinkhorn, or hc_fused_mix_pre).
+ * Requires d % 32 == 0 and d / (32*k) <= 32 for some k in 1..8 (d = 5120:
+ * k = 5); otherwise HC_ERR_UNSUPPORTED.  `workspace` (device memory of at
+ * least hc_fused_workspace_bytes(n, hc, d) bytes, 256-byte aligned) holds
+ * cross-workgroup partial sums; its contents on entry do not matter.
+ */
+int hc_mixes(const void *R, const float *hc_fn, float *mixes, int64_t n,
+             int32_t hc, int32_t d, float norm_eps, void *workspace,
+             size_t workspace_bytes, void *stream);
+
+/*
+ * hc_split_sinkhorn -- "Reading weights" page, the hc_split_sinkhorn kernel
+ * listing (and the learned-pre formula, whose s_1 is hc_scale[0]):
+ *   pre[t][j]  = sigmoid(hc_scale[0]*mixes[t][j] + hc_base[j]) + hc_eps
+ *   post[t][j] = 2*sigmoid(hc_scale[1]*mixes[t][4+j] + hc_base[4+j])
+ *   L[j][k]    = hc_scale[2]*mixes[t][8+4j+k] + hc_base[8+4j+k]
+ *   comb = row softmax of L, + hc_eps; comb /= (column sums + hc_eps);
+ *   then (sinkhorn_iters - 1) times: comb /= (row sums + hc_eps);
+ *   comb /= (column sums + hc_eps).
+ * sinkhorn_iters >= 1 (else HC_ERR_UNSUPPORTED); hc_eps finite and >= 0.
+ * The pages' wrapper allocates its outputs; here the caller does.
+ */
+int hc_split_sinkhorn(const float *mixes, const float *hc_scale,
+                      const float *hc_base, float *pre, float *post,
+                      float *comb, int64_t n, int32_t hc,
+                      int32_t sinkhorn_iters, float hc_eps, void *stream);
+
+/*
+ * hc_pre -- "Mix projection" page, Block.hc_pre:
+ *   h[t][c] = bf16( sum_k pre[t][k] * R[t][k][c] ).
+ * d % 8 == 0.  h must not overlap R or pre.
+ */
+int hc_pre(const void *R, const float *pre, void *h, int64_t n, int32_t hc,
+           int32_t d, void *stream);
+
+/*
+ * hc_post -- "Mix projection" page, Block.hc_post:
+ *   R_out[t][k][c] = bf16( post[t][k] * x[t][c]
+ *                          + sum_j comb[t][j][k] * R[t][j][c] )
+ * (column k of comb feeds output stream k).  d % 8 == 0.  R_out == R is
+ * allowed (in place); any other overlap of R_out with an input is
+ * HC_ERR_ALIAS.
+ */
+int hc_post(const void *x, const void *R, const float *post,
+            const float *comb, void *R_out, int64_t n, int32_t hc, int32_t d,
+            void *stream);
+
+/*
+ * hc_fused_mix_pre -- hc_mixes, hc_split_sinkhorn and hc_pre in one pass
+ * over the residual (the sequence of Block.hc_mixes followed by
+ * Block.hc_pre on the "Mix projection" page).  Outputs: h (required),
+ * post and comb (required), pre and mixes (each may be NULL).  Same
+ * constraints on d as hc_mixes; the same workspace rules.  The
+ * coefficients are bitwise those of hc_mixes followed by
+ * hc_split_sinkhorn, and h is bitwise hc_pre's for those coefficients.
+ */
+int hc_fused_mix_pre(const void *R, const float *hc_fn,
+                     const float *hc_scale, const float *hc_base, void *h,
+                     float *pre, float *post, float *comb, float *mixes,
+                     void *workspace, size_t workspace_bytes, int64_t n,
+                     int32_t hc, int32_t d, int32_t sinkhorn_iters,
+                     float hc_eps, float norm_eps, void *stream);
+
+/*
+ * Bytes of device workspace hc_mixes / hc_fused_mix_pre need for these
+ * sizes on the current device (0 for n == 0; 0 with an unsupported shape,
+ * in which case the call itself reports the error).  Host-only query.
+ */
+size_t hc_fused_workspace_bytes(int64_t n, int32_t hc, int32_t d);
+
+/*
+ * hc_diag_scale -- the chained-stack workload's stand-in sublayer:
+ *   x[t][c] = bf16( h[t][c] * D[c] ),  D bf16 [d].
+ * A fixed per-layer diagonal scale between hc_pre and hc_post, so that an
+ * 80-sublayer stack can run without trained attention/FFN weights.
+ * d % 8 == 0; x must not overlap h or D.
+ */
+int hc_diag_scale(const void *h, const void *D, void *x, int64_t n,
+                  int32_t d, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBHC_HC_H */

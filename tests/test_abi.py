@@ -1,0 +1,158 @@
+"""The C-ABI library loads, exports every entry point include/hc.h declares,
+and its host-side checks return the documented status codes.  Every call
+here is an error path or n == 0, so nothing is launched: these run without
+a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hyper_connection_residual_02_amd as hcl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hc.h")
+
+OK, NULL, SHAPE, ALIGN, UNSUP, WS, ALIAS, VALUE = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return sorted(set(re.findall(r"\b(hc_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hcl.lib_path()):
+        import hyper_connection_residual_02_amd.build as b
+        b.build(verbose=False)
+    return hcl.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post", "hc_fused_mix_pre",
+            "hc_fused_workspace_bytes", "hc_status_str", "hc_diag_scale"} <= set(names)
+    for nm in names:
+        assert hasattr(lib, nm), nm
+    assert lib.hc_version().decode().count(".") == 2
+
+
+def test_status_strings(lib):
+    for code in range(-9, 1):
+        s = lib.hc_status_str(code).decode()
+        assert s.startswith("HC_")
+    assert lib.hc_status_str(-100).decode().startswith("HC_ERR_?")
+
+
+A = 0x10000          # fake, aligned addresses: never dereferenced on error paths
+B = 0x20000000
+C = 0x40000000
+D_ = 0x60000000
+E = 0x70000000
+F_ = 0x7C000000
+P = ctypes.c_void_p
+
+
+def post_call(lib, x=A, R=B, post=C, comb=D_, out=E, n=4, hc=4, d=64):
+    return lib.hc_post(P(x), P(R), P(post), P(comb), P(out), n, hc, d, None)
+
+
+def test_post_checks(lib):
+    assert post_call(lib, n=0) == OK
+    assert post_call(lib, n=-1) == SHAPE
+    assert post_call(lib, d=60) == SHAPE
+    assert post_call(lib, d=0) == SHAPE
+    assert post_call(lib, hc=3) == UNSUP
+    assert post_call(lib, x=0) == NULL
+    assert post_call(lib, comb=0) == NULL
+    assert post_call(lib, R=B + 8) == ALIGN
+    assert post_call(lib, out=E + 2) == ALIGN
+    assert post_call(lib, out=B + 16) == ALIAS           # partial overlap with R
+    assert post_call(lib, out=A) == ALIAS                # overlaps x
+    assert post_call(lib, n=1 << 40) == SHAPE            # size bound
+
+
+def test_pre_checks(lib):
+    f = lambda R=A, p=B, h=C, n=4, hc=4, d=64: lib.hc_pre(P(R), P(p), P(h), n, hc, d, None)
+    assert f(n=0) == OK
+    assert f(hc=8) == UNSUP
+    assert f(d=12) == SHAPE
+    assert f(h=0) == NULL
+    assert f(p=B + 4) == ALIGN
+    assert f(h=A + 64) == ALIAS
+
+
+def test_split_checks(lib):
+    f = lambda m=A, s=B, b=B + 64, pre=C, post=D_, comb=E, n=4, hc=4, it=20, eps=1e-6: \
+        lib.hc_split_sinkhorn(P(m), P(s), P(b), P(pre), P(post), P(comb), n, hc, it, eps, None)
+    assert f(n=0) == OK
+    assert f(n=-3) == SHAPE
+    assert f(it=0) == UNSUP
+    assert f(hc=2) == UNSUP
+    assert f(eps=-1.0) == VALUE
+    assert f(eps=float("nan")) == VALUE
+    assert f(eps=float("inf")) == VALUE
+    assert f(s=0) == NULL
+    assert f(s=B + 2) == ALIGN
+    assert f(pre=C + 4) == ALIGN
+    assert f(post=C + 32) == ALIAS
+    assert f(comb=A) == ALIAS
+
+
+def test_fused_and_mixes_checks(lib):
+    def f(R=A, W=B, s=C, b=C + 64, h=D_, pre=E, post=E + 4096, comb=E + 8192, mix=0, ws=F_,
+          wsb=1 << 30, n=4, hc=4, d=64, it=20, eps=1e-6, neps=1e-20):
+        return lib.hc_fused_mix_pre(P(R), P(W), P(s), P(b), P(h), P(pre), P(post), P(comb),
+                                    P(mix), P(ws), wsb, n, hc, d, it, eps, neps, None)
+    assert f(n=0) == OK
+    assert f(d=48) == UNSUP            # d % 32 != 0: the projection cannot be tiled
+    assert f(d=40) == SHAPE or f(d=40) == UNSUP
+    assert f(d=37 * 32) == UNSUP       # no k in 1..8 with d % (32k) == 0 and d/(32k) <= 32
+    assert f(it=0) == UNSUP
+    assert f(eps=-1e-6) == VALUE
+    assert f(neps=float("nan")) == VALUE
+    assert f(R=0) == NULL
+    assert f(h=0) == NULL
+    assert f(ws=0) == WS
+    assert f(ws=F_ + 128) == ALIGN     # workspace must be 256-byte aligned
+    assert f(W=B + 8) == ALIGN
+    assert f(wsb=16) == WS
+    assert f(h=A) == ALIAS             # h overlaps R
+    assert f(post=E) == ALIAS          # post overlaps pre
+    assert f(mix=F_) == ALIAS          # mixes overlaps the workspace
+
+    def m(R=A, W=B, out=C, ws=F_, wsb=1 << 30, n=4, hc=4, d=64, neps=1e-20):
+        return lib.hc_mixes(P(R), P(W), P(out), n, hc, d, neps, P(ws), wsb, None)
+    assert m(n=0) == OK
+    assert m(out=0) == NULL
+    assert m(out=C + 4) == ALIGN
+    assert m(out=A) == ALIAS
+    assert m(wsb=0) == WS
+    assert m(hc=5) == UNSUP
+
+
+def test_workspace_query(lib):
+    assert lib.hc_fused_workspace_bytes(0, 4, 5120) == 0
+    assert lib.hc_fused_workspace_bytes(16, 3, 5120) == 0
+    assert lib.hc_fused_workspace_bytes(16, 4, 48) == 0
+    assert lib.hc_fused_workspace_bytes(16, 4, 64) > 0
+    assert lib.hc_fused_workspace_bytes(65536, 4, 5120) > 0
+
+
+def test_diag_checks(lib):
+    f = lambda h=A, Dp=B, x=C, n=4, d=64: lib.hc_diag_scale(P(h), P(Dp), P(x), n, d, None)
+    assert f(n=0) == OK
+    assert f(d=7) == SHAPE
+    assert f(x=0) == NULL
+    assert f(x=A) == ALIAS
+    assert f(Dp=B + 2) == ALIGN
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    R = torch.zeros(2, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        hcl.hc_pre(R, torch.zeros(2, 4))
