@@ -76,6 +76,18 @@ __device__ __forceinline__ float col4_sum(float v) {
 // Logistic function in float.
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
 
+// The read and write gates of the split, shared by every kernel that forms
+// them so that all entry points agree bit for bit.
+__device__ __forceinline__ float pre_gate(float m, float s0, float b, float eps) {
+    return sigmoidf_(m * s0 + b) + eps;
+}
+__device__ __forceinline__ float post_gate(float m, float s1, float b) { return 2.0f * sigmoidf_(m * s1 + b); }
+
+// RMS normaliser of the mix formula: 1 / sqrt(sum_sq / K + norm_eps).
+__device__ __forceinline__ float rms_scale(float sum_sq, float K, float norm_eps) {
+    return 1.0f / sqrtf(sum_sq / K + norm_eps);
+}
+
 // ------------------------------------------------- split + epsilon-Sinkhorn
 // One token per 16-lane row; lane e = (lane & 15) holds comb entry
 // (j, k) = (e / 4, e % 4).  m points at the token's 24 mixes (any memory
@@ -91,8 +103,8 @@ __device__ __forceinline__ void split_sinkhorn16(const float* m, float s0, float
                                                  float& comb_o) {
     const int e = threadIdx.x & 15;
     const int j4 = e & 3;
-    pre_o = sigmoidf_(m[j4] * s0 + base[j4]) + eps;
-    post_o = 2.0f * sigmoidf_(m[kHC + j4] * s1 + base[kHC + j4]);
+    pre_o = pre_gate(m[j4], s0, base[j4], eps);
+    post_o = post_gate(m[kHC + j4], s1, base[kHC + j4]);
     float c = m[2 * kHC + e] * s2 + base[2 * kHC + e];
     // row softmax (max subtracted for range only), then + eps
     float mx = quad_max(c);

@@ -110,7 +110,7 @@ def test_fused_and_mixes_checks(lib):
     assert f(n=0) == OK
     assert f(d=48) == UNSUP            # d % 32 != 0: the projection cannot be tiled
     assert f(d=40) == SHAPE or f(d=40) == UNSUP
-    assert f(d=37 * 32) == UNSUP       # no k in 1..8 with d % (32k) == 0 and d/(32k) <= 32
+    assert f(d=67 * 32) == UNSUP       # no k in 1..5 with d % (32k) == 0 and d/(32k) <= 64
     assert f(it=0) == UNSUP
     assert f(eps=-1e-6) == VALUE
     assert f(neps=float("nan")) == VALUE
