@@ -17,7 +17,7 @@ int launch_post(const void* x, const void* R, const float* post, const float* co
                 int64_t n, int d, hipStream_t s);
 int launch_diag(const void* h, const void* D, void* x, int64_t n, int d, hipStream_t s);
 
-// Standalone split + Sinkhorn (hc_sinkhorn.hip).
+// Standalone split + Sinkhorn (hc_sinkhorn.hip); pre may be NULL (not written).
 int launch_split(const float* mixes, const float* scale, const float* base, float* pre, float* post,
                  float* comb, int64_t n, int iters, float eps, hipStream_t s);
 
@@ -30,9 +30,8 @@ struct CoopPlan {
     int TM;          // 16-token MFMA tiles per round (T = 16 * TM tokens)
     int NG;          // groups (workgroups launched = G * NG)
     int64_t ntiles;  // ceil(n / T)
-    size_t ws_part;  // byte offsets into the workspace
-    size_t ws_pre;
-    size_t ws_cnt;
+    size_t ws_part;  // byte offsets into the workspace: exchange records
+    size_t ws_mix;   // mixes of every token when the caller does not keep them
     size_t ws_bytes;
 };
 // K-steps per wave for d (0: d cannot be tiled).  Host only, no HIP calls.

@@ -9,7 +9,7 @@
 namespace hc {
 
 __global__ __launch_bounds__(256) void k_split(const float* __restrict__ mixes, const float* __restrict__ scale,
-                                               const float* __restrict__ base, float* __restrict__ pre,
+                                               const float* __restrict__ base, float* pre,
                                                float* __restrict__ post, float* __restrict__ comb, int64_t n,
                                                int iters, float eps) {
     const float s0 = scale[0], s1 = scale[1], s2 = scale[2];
@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void k_split(const float* __restrict__ mixes, 
         if (valid) {
             comb[t * (kHC * kHC) + e] = c;
             if (e < kHC) {
-                pre[t * kHC + e] = p;
+                if (pre) pre[t * kHC + e] = p;
                 post[t * kHC + e] = q;
             }
         }
