@@ -64,11 +64,14 @@ constexpr uint64_t kMagic = 0x6863776b73703031ull;   // marks an initialised wor
 constexpr uint32_t kEpochMask = 0xFFFFFu;            // 20-bit call epoch in each tag
 constexpr int kBufDword3 = 0x00020000;               // raw buffer resource, dword 3
 
-// Workspace header (first 256 bytes): magic, call epoch, error flag.
+// Workspace header (first 256 bytes): magic, call epoch, error flag, and
+// the length (16-byte records) of the record area known to hold only
+// tagged records or zeros.
 struct WsHeader {
     uint64_t magic;
     uint32_t epoch;
     uint32_t err;
+    int64_t clean;
 };
 
 struct CoopArgs {
@@ -564,9 +567,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_coop(CoopArgs a) {
     }
 }
 
-// Per-call header update.  Clears every record on the first use of a
-// workspace and when the 20-bit call epoch wraps, so a stale record never
-// carries a current tag.
+// Per-call header update.  Clears the record area on the first use of a
+// workspace, when the 20-bit call epoch wraps, and when this call's record
+// area reaches past the part known to be clean (a previous call may have
+// kept its mixes there), so a record never carries a current tag before
+// this call writes it.  Past this call's record area the workspace may
+// receive mixes, so only that area stays known clean.
 __global__ __launch_bounds__(1024) void k_init(WsHeader* hdr, u32x4* part, int64_t nchunks) {
     __shared__ int clear;
     __shared__ uint32_t next;
@@ -574,7 +580,7 @@ __global__ __launch_bounds__(1024) void k_init(WsHeader* hdr, u32x4* part, int64
         const uint32_t e = hdr->epoch;
         const bool fresh = hdr->magic != kMagic;
         uint32_t ne = fresh ? 1u : (e & kEpochMask) + 1u;
-        clear = fresh || ne > kEpochMask;
+        clear = fresh || ne > kEpochMask || hdr->clean < nchunks;
         if (ne > kEpochMask) ne = 1u;
         next = ne;
     }
@@ -586,6 +592,7 @@ __global__ __launch_bounds__(1024) void k_init(WsHeader* hdr, u32x4* part, int64
         hdr->magic = kMagic;
         hdr->epoch = next;
         hdr->err = 0u;
+        hdr->clean = nchunks;
     }
 }
 

@@ -91,10 +91,24 @@ const char *hc_version(void);
  *   flattened features, j < 24.
  * The library's hc_mixes stops at the mixes; the pages' Block.hc_mixes
  * also runs the split (call hc_split_sinkhorn, or hc_fused_mix_pre).
- * Requires d % 32 == 0 and d / (32*k) <= 32 for some k in 1..8 (d = 5120:
- * k = 5); otherwise HC_ERR_UNSUPPORTED.  `workspace` (device memory of at
- * least hc_fused_workspace_bytes(n, hc, d) bytes, 256-byte aligned) holds
- * cross-workgroup partial sums; its contents on entry do not matter.
+ * Requires d % 32 == 0 and d / (32*k) <= 64 for some k in 1..5 (d = 5120:
+ * k = 5, 32 workgroups per token group); otherwise HC_ERR_UNSUPPORTED.
+ * hc_fn is used as given, fp32, with no precision reduced: each product is
+ * formed exactly from a three-way bf16 split of the weight.
+ *
+ * Workspace: device memory of at least hc_fused_workspace_bytes(n, hc, d)
+ * bytes, 256-byte aligned.  It holds the partial sums the workgroups of a
+ * token group exchange, and a small header in its first 256 bytes that
+ * numbers the calls made with it, so that a record left by an earlier call
+ * is never taken for a current one.  Any contents are accepted on first
+ * use.  Between calls, leave it alone (or zero its first 256 bytes after
+ * using it for something else).  Calls that may run at the same time,
+ * on different streams, each need their own workspace.
+ *
+ * The launch is cooperative: every workgroup of the grid is resident at
+ * once, so each wait for a peer's partial sums ends.  As a guard, a wait
+ * that exceeds about two seconds makes the kernel stop early and flag an
+ * error word in the workspace header; outputs are then undefined.
  */
 int hc_mixes(const void *R, const float *hc_fn, float *mixes, int64_t n,
              int32_t hc, int32_t d, float norm_eps, void *workspace,
@@ -141,10 +155,12 @@ int hc_post(const void *x, const void *R, const float *post,
  * hc_fused_mix_pre -- hc_mixes, hc_split_sinkhorn and hc_pre in one pass
  * over the residual (the sequence of Block.hc_mixes followed by
  * Block.hc_pre on the "Mix projection" page).  Outputs: h (required),
- * post and comb (required), pre and mixes (each may be NULL).  Same
- * constraints on d as hc_mixes; the same workspace rules.  The
- * coefficients are bitwise those of hc_mixes followed by
- * hc_split_sinkhorn, and h is bitwise hc_pre's for those coefficients.
+ * post and comb (required), pre and mixes (each may be NULL; with mixes
+ * NULL they are kept in the workspace).  Same constraints on d as
+ * hc_mixes; the same workspace rules.  The coefficients are bitwise those
+ * of hc_mixes followed by hc_split_sinkhorn, and h is bitwise hc_pre's for
+ * those coefficients.  Launches three kernels on `stream`: a header
+ * update, the projection with pre and h, and the split of post and comb.
  */
 int hc_fused_mix_pre(const void *R, const float *hc_fn,
                      const float *hc_scale, const float *hc_base, void *h,

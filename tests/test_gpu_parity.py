@@ -220,6 +220,26 @@ def test_determinism_and_batch_invariance():
         assert torch.equal(u[:, 1000:1100], v)
 
 
+def test_workspace_reused_across_shapes():
+    # one workspace through calls of different sizes and widths, mixes kept
+    # in the workspace: every result equals that of a fresh workspace
+    w = hin.WORKLOADS["prefill"]
+    t = hin.make_inputs(w, DEV, seed=29)
+    w2 = hin.Workload("w2048", 1, 300, 4, 2048, 1.0 / np.sqrt(4 * 2048), 0.5, 2.0, 1.0)
+    t2 = hin.make_inputs(w2, DEV, seed=31)
+    shared = hcl.Workspace()
+    cases = [(t["R"], t), (t["R"][:, :100].contiguous(), t), (t2["R"], t2), (t["R"], t),
+             (t["R"][:, :5].contiguous(), t), (t["R"], t)]
+    for R, src in cases:
+        args = (R, src["W"], src["scale"], src["base"])
+        got = hcl.hc_fused_mix_pre(*args, want_pre=True, want_mixes=False, workspace=shared)
+        ref = hcl.hc_fused_mix_pre(*args, want_pre=True, want_mixes=False, workspace=hcl.Workspace())
+        torch.cuda.synchronize()
+        for u, v in zip(got, ref):
+            if u is not None:
+                assert torch.equal(u, v)
+
+
 def test_zero_and_scaled_tokens(orc):
     w = hin.WORKLOADS["decode"]
     t = hin.make_inputs(w, DEV, seed=19)
