@@ -63,6 +63,7 @@ constexpr int kOwnPairs = kChunks * kT;   // (owned token, chunk) pairs at most 
 constexpr uint64_t kMagic = 0x6863776b73703031ull;   // marks an initialised workspace
 constexpr uint32_t kEpochMask = 0xFFFFFu;            // 20-bit call epoch in each tag
 constexpr int kBufDword3 = 0x00020000;               // raw buffer resource, dword 3
+constexpr int kOOB = 0x7FFFFFF0;   // buffer offset past every resource: loads read 0, stores drop
 
 // Workspace header (first 256 bytes): magic, call epoch, error flag, and
 // the length (16-byte records) of the record area known to hold only
@@ -146,7 +147,19 @@ struct RoundCtx {
     int nown;               // tokens of a round this member owns
     uint32_t epoch;
     __amdgpu_buffer_rsrc_t rsrc;   // the record area
+    float s0, bpre;         // hc_scale[0] and hc_base[thread % 4], read once: a parameter
+                            // load inside the loop would be the youngest memory op, and
+                            // waiting for it would wait for every prefetch
 };
+
+// hc_base[thread % 4] from four uniform (scalar) loads: a per-lane vector
+// load would be waited for where it is first used inside the round loop,
+// and that wait would also wait for every store still in flight.
+__device__ __forceinline__ float base_of_lane(const float* base) {
+    const float b0 = base[0], b1 = base[1], b2 = base[2], b3 = base[3];
+    const int k = threadIdx.x & 3;
+    return k == 0 ? b0 : (k == 1 ? b1 : (k == 2 ? b2 : b3));
+}
 
 __device__ __forceinline__ uint32_t tag_of(const RoundCtx& c, int r) {
     return (c.epoch << 12) | ((uint32_t)r & 0xFFFu);
@@ -160,6 +173,9 @@ __device__ __forceinline__ int rec_off(const CoopArgs& a, const RoundCtx& c, int
 
 __device__ __forceinline__ u32x4 ld_l2(const RoundCtx& c, int off) {   // first read: served by the L2
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(c.rsrc, off, 0, 1));
+}
+__device__ __forceinline__ u32x4 ld_dev(const RoundCtx& c, int off) {  // re-read: device scope
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(c.rsrc, off, 0, 16));
 }
 __device__ __forceinline__ void st_dev(const RoundCtx& c, int off, u32x4 v) {   // device scope
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((__vector_size__(16))) int, v), c.rsrc,
@@ -179,9 +195,9 @@ struct Frags {
 // [n][per_tok] array; loads past the last token read zeros and stores past
 // it are dropped by the hardware bounds check.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int64_t per_tok_bytes, int64_t tok0,
-                                                          int64_t n) {
-    int64_t valid = n - tok0;
-    valid = valid < 0 ? 0 : (valid > 16 ? 16 : valid);
+                                                          int64_t n, int64_t ntok = 16) {
+    int64_t valid = base ? n - tok0 : 0;
+    valid = valid < 0 ? 0 : (valid > ntok ? ntok : valid);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(base)) + tok0 * per_tok_bytes,
                                              0, (int)(valid * per_tok_bytes), kBufDword3);
 }
@@ -239,26 +255,6 @@ __device__ __forceinline__ float group_sum(float v, int gp) {
     return v;
 }
 
-// Bounded wait for a record chunk carrying the expected tag (device-scope
-// reads).  On a timeout (or a flag raised elsewhere) it raises the flag and
-// returns a chunk whose tag does not match, which the caller treats as a stop.
-__device__ __noinline__ u32x4 reread(__amdgpu_buffer_rsrc_t rsrc, int off, uint32_t tag, WsHeader* hdr) {
-    u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 16));
-    if (v[3] == tag) return v;
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    for (;;) {
-        __builtin_amdgcn_s_sleep(1);
-        v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 16));
-        if (v[3] == tag) return v;
-        if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull ||
-            __hip_atomic_load(&hdr->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-            __hip_atomic_store(&hdr->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            v[3] = ~tag;
-            return v;
-        }
-    }
-}
-
 // ---------------------------------------------------- stage A: publish r
 // f holds round r in MFMA operand layout.
 template <int KS>
@@ -268,13 +264,21 @@ __device__ __forceinline__ void publish(const Frags<KS>& f, const CoopArgs& a, c
 #pragma unroll
     for (int ct = 0; ct < kTiles; ++ct) acc[ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float sq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // weight operands double-buffered from LDS: the reads for k-step s+1
+    // are in flight while the MFMAs of step s run
+    bf16x8 bw[2][kTiles];
+#pragma unroll
+    for (int ct = 0; ct < kTiles; ++ct) bw[0][ct] = L.wf[c.kg * KS][ct][c.l];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         const bf16x8 av = __builtin_bit_cast(bf16x8, f.r[s]);
-        const int kk = c.kg * KS + s;
+        if (s + 1 < KS) {
+#pragma unroll
+            for (int ct = 0; ct < kTiles; ++ct) bw[(s + 1) & 1][ct] = L.wf[c.kg * KS + s + 1][ct][c.l];
+        }
 #pragma unroll
         for (int ct = 0; ct < kTiles; ++ct)
-            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, L.wf[kk][ct][c.l], acc[ct], 0, 0, 0);
+            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw[s & 1][ct], acc[ct], 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float lo = bf_lo(f.r[s][e]), hi = bf_hi(f.r[s][e]);
@@ -302,20 +306,21 @@ __device__ __forceinline__ void publish(const Frags<KS>& f, const CoopArgs& a, c
         if (c.row < 8) L.u.red[c.kg][t][16 + c.row] = v1;
     }
     __syncthreads();
+    // 9 records per token from the first 288 threads; the other threads'
+    // stores go past the resource and are dropped (no branch around the
+    // store keeps the memory counters countable)
     const int tid = threadIdx.x;
-    if (tid < kT * kChunks) {
-        const int ch = tid / kT, t = tid - ch * kT;
-        u32x4 v;
+    const int ch = tid / kT, t = tid - ch * kT;
+    u32x4 v;
 #pragma unroll
-        for (int sl = 0; sl < 3; ++sl) {
-            const int fi = field_at(ch, sl);
-            float x = 0.0f;
-            if (fi >= 0) x = ((L.u.red[0][t][fi] + L.u.red[1][t][fi]) + L.u.red[2][t][fi]) + L.u.red[3][t][fi];
-            v[sl] = __float_as_uint(x);
-        }
-        v[3] = tag_of(c, r);
-        st_dev(c, rec_off(a, c, r, ch, t, c.q), v);
+    for (int sl = 0; sl < 3; ++sl) {
+        const int fi = field_at(ch, sl);      // -1 for ch >= kChunks
+        float x = 0.0f;
+        if (fi >= 0) x = ((L.u.red[0][t][fi] + L.u.red[1][t][fi]) + L.u.red[2][t][fi]) + L.u.red[3][t][fi];
+        v[sl] = __float_as_uint(x);
     }
+    v[3] = tag_of(c, r);
+    st_dev(c, ch < kChunks ? rec_off(a, c, r, ch, t, c.q) : kOOB, v);
 }
 
 // Exchange loads of round r issued ahead of time (held in registers).
@@ -335,7 +340,8 @@ __device__ __forceinline__ void issue_x(XLoads<PI>& X, const CoopArgs& a, const 
         for (int j = 0; j < PI; ++j) {
             const int x = j * kThreads + tid;
             const int pair = x >> a.gp_log2, m = x & (a.GP - 1);
-            if (pair < kPrePairs && m < a.G) X.pre[j] = ld_l2(c, rec_off(a, c, r, pair / kT, pair % kT, m));
+            const bool ok = pair < kPrePairs && m < a.G;
+            X.pre[j] = ld_l2(c, ok ? rec_off(a, c, r, pair / kT, pair % kT, m) : kOOB);
         }
     }
 #pragma unroll
@@ -343,49 +349,96 @@ __device__ __forceinline__ void issue_x(XLoads<PI>& X, const CoopArgs& a, const 
         const int x = j * kThreads + tid;
         const int pair = x >> a.gp_log2, m = x & (a.GP - 1);
         const int o = pair / kChunks, ch = pair - o * kChunks;
-        if (o < c.nown && m < a.G) X.own[j] = ld_l2(c, rec_off(a, c, r, ch, c.q + a.G * o, m));
+        const bool ok = o < c.nown && m < a.G;
+        X.own[j] = ld_l2(c, ok ? rec_off(a, c, r, ch, c.q + a.G * o, m) : kOOB);
     }
 }
 
-// Member sums of a loaded record chunk (3 floats): tag check (stale
-// chunks are re-read at device scope), then the group butterfly.
-__device__ __forceinline__ void chunk_sum(u32x4 v, bool have, const CoopArgs& a, const RoundCtx& c, int r, int chunk,
-                                          int t, int m, float* s3, int* bad) {
-    const uint32_t tag = tag_of(c, r);
-    float x0 = 0.0f, x1 = 0.0f, x2 = 0.0f;
-    if (have) {
-        if (v[3] != tag) {
-            v = reread(c.rsrc, rec_off(a, c, r, chunk, t, m), tag, a.hdr);
-            if (v[3] != tag) *bad = 1;
-        }
-        x0 = __uint_as_float(v[0]);
-        x1 = __uint_as_float(v[1]);
-        x2 = __uint_as_float(v[2]);
-    }
-    s3[0] = group_sum(x0, a.GP);
-    s3[1] = group_sum(x1, a.GP);
-    s3[2] = group_sum(x2, a.GP);
+// Position of pre-relevant load j / owned load j of this thread: (chunk,
+// token, member), and whether it names a real record.
+__device__ __forceinline__ bool pre_pos(const CoopArgs& a, int j, int& chunk, int& t, int& m) {
+    const int x = j * kThreads + (int)threadIdx.x;
+    const int pair = x >> a.gp_log2;
+    m = x & (a.GP - 1);
+    chunk = pair / kT;
+    t = pair - chunk * kT;
+    return pair < kPrePairs && m < a.G;
+}
+__device__ __forceinline__ bool own_pos(const CoopArgs& a, const RoundCtx& c, int j, int& chunk, int& t, int& m) {
+    const int x = j * kThreads + (int)threadIdx.x;
+    const int pair = x >> a.gp_log2;
+    m = x & (a.GP - 1);
+    const int o = pair / kChunks;
+    chunk = pair - o * kChunks;
+    t = c.q + a.G * o;
+    return o < c.nown && m < a.G;
+}
+
+// Member sums of the 3 floats of a record (zeros where there is none).
+__device__ __forceinline__ void chunk_sum(const u32x4& v, const CoopArgs& a, float* s3) {
+    s3[0] = group_sum(__uint_as_float(v[0]), a.GP);
+    s3[1] = group_sum(__uint_as_float(v[1]), a.GP);
+    s3[2] = group_sum(__uint_as_float(v[2]), a.GP);
 }
 
 // Exchange of round r: member sums of the pre-relevant records of every
 // token (into L.xsum) and of all records of the owned tokens (into
-// L.xown), in one fixed butterfly order shared by both, so pre formed here
-// is bitwise the pre of the owner's mixes.  Returns true if any thread of
-// the workgroup hit a timeout.
+// L.xown), in one fixed reduction order shared by both, so pre formed here
+// is bitwise the pre of the owner's mixes.  A wave any of whose records
+// still carries an older tag re-reads those records at device scope until
+// they are current (bounded in time).  Returns true if any thread of the
+// workgroup hit a timeout.
 template <int PI, int KS, bool FUSED>
-__device__ __forceinline__ bool exchange(const XLoads<PI>& X, const CoopArgs& a, const RoundCtx& c, Lds<KS>& L,
+__device__ __forceinline__ bool exchange(XLoads<PI>& X, const CoopArgs& a, const RoundCtx& c, Lds<KS>& L,
                                          int r) {
-    const int tid = threadIdx.x;
+    const uint32_t tag = tag_of(c, r);
+    int chunk, t, m;
+    bool stale = false;
+    if (FUSED) {
+#pragma unroll
+        for (int j = 0; j < PI; ++j) stale |= pre_pos(a, j, chunk, t, m) && X.pre[j][3] != tag;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) stale |= own_pos(a, c, j, chunk, t, m) && X.own[j][3] != tag;
     int bad = 0;
+    if (__builtin_amdgcn_ballot_w64(stale)) {           // wave-uniform, rare
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        for (;;) {
+            bool again = false;
+            if (FUSED) {
+#pragma unroll
+                for (int j = 0; j < PI; ++j)
+                    if (pre_pos(a, j, chunk, t, m) && X.pre[j][3] != tag) {
+                        X.pre[j] = ld_dev(c, rec_off(a, c, r, chunk, t, m));
+                        again |= X.pre[j][3] != tag;
+                    }
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                if (own_pos(a, c, j, chunk, t, m) && X.own[j][3] != tag) {
+                    X.own[j] = ld_dev(c, rec_off(a, c, r, chunk, t, m));
+                    again |= X.own[j][3] != tag;
+                }
+            if (!__builtin_amdgcn_ballot_w64(again)) break;
+            if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull ||
+                __hip_atomic_load(&a.hdr->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+                __hip_atomic_store(&a.hdr->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                bad = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    const int tid = threadIdx.x;
     if (FUSED) {
 #pragma unroll
         for (int j = 0; j < PI; ++j) {
             if (j * kThreads < kPrePairs * a.GP) {          // block-uniform: this load carries pairs
-                const int x = j * kThreads + tid;
-                const int pair = x >> a.gp_log2, m = x & (a.GP - 1);
+                const bool ok = pre_pos(a, j, chunk, t, m);
                 float s3[3];
-                chunk_sum(X.pre[j], pair < kPrePairs && m < a.G, a, c, r, pair / kT, pair % kT, m, s3, &bad);
-                if (m == 0 && pair < kPrePairs) {
+                chunk_sum(X.pre[j], a, s3);                 // zeros where !ok (load past the resource)
+                if (m == 0 && ok) {
+                    const int pair = chunk * kT + t;
                     L.xsum[pair][0] = s3[0];
                     L.xsum[pair][1] = s3[1];
                     L.xsum[pair][2] = s3[2];
@@ -398,11 +451,11 @@ __device__ __forceinline__ bool exchange(const XLoads<PI>& X, const CoopArgs& a,
     for (int j = 0; j < 2; ++j) {
         if (j * kThreads < npairs * a.GP) {                 // block-uniform
             const int x = j * kThreads + tid;
-            const int pair = x >> a.gp_log2, m = x & (a.GP - 1);
-            const int o = pair / kChunks, ch = pair - o * kChunks;
+            const int pair = x >> a.gp_log2;
+            const bool ok = own_pos(a, c, j, chunk, t, m);
             float s3[3];
-            chunk_sum(X.own[j], pair < npairs && m < a.G, a, c, r, ch, c.q + a.G * o, m, s3, &bad);
-            if (m == 0 && pair < npairs) {
+            chunk_sum(X.own[j], a, s3);
+            if (m == 0 && ok) {
                 L.xown[pair][0] = s3[0];
                 L.xown[pair][1] = s3[1];
                 L.xown[pair][2] = s3[2];
@@ -418,22 +471,36 @@ template <int KS, bool FUSED>
 __device__ __forceinline__ void finals(const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, int r) {
     const int tid = threadIdx.x;
     const int64_t tok0 = tile_of(c, a, r) * kT;
-    if (FUSED && tid < kT * 4) {
-        const int t = tid >> 2, j = tid & 3;
+    if (FUSED) {
+        // threads < 128: pre of (token tid/4, stream tid%4); the others
+        // compute a copy of it and their store is dropped
+        const int t = (tid >> 2) & (kT - 1), j = tid & 3;
         const float sj = j < 3 ? L.xsum[t][j] : L.xsum[kT + t][0];     // m_0..m_2: chunk 0; m_3: chunk 1 slot 0
         const float sq = L.xsum[kT + t][1];                           // sum of squares: chunk 1 slot 1
-        const float p = pre_gate(sj * rms_scale(sq, a.K, a.norm_eps), a.scale[0], a.base[j], a.eps);
-        L.preL[t][j] = p;
-        if (a.pre && t % a.G == c.q && tok0 + t < a.n) a.pre[(tok0 + t) * kHC + j] = p;
+        const float p = pre_gate(sj * rms_scale(sq, a.K, a.norm_eps), c.s0, c.bpre, a.eps);
+        if (tid < kT * 4) L.preL[t][j] = p;
+        // the owner writes pre (a null pre gives an empty resource)
+        const __amdgpu_buffer_rsrc_t rp = tile_rsrc(a.pre, kHC * 4, tok0, a.n, kT);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p), rp,
+                                              tid < kT * 4 && t % a.G == c.q ? (t * kHC + j) * 4 : kOOB, 0, 0);
     }
+    // mixes of the owned tokens; a fixed number of passes, with the stores
+    // of threads past the owned mixes dropped by the resource bound
     const int base = FUSED ? kT * 4 : 0;
-    for (int x = tid - base; x >= 0 && x < c.nown * kMix; x += kThreads - base) {
-        const int o = x / kMix, j = x - o * kMix;
+    const __amdgpu_buffer_rsrc_t rm = tile_rsrc(a.mixes, kMix * 4, tok0, a.n, kT);
+    constexpr int kPasses = (kT * kMix + (kThreads - (FUSED ? kT * 4 : 0)) - 1) / (kThreads - (FUSED ? kT * 4 : 0));
+#pragma unroll
+    for (int it = 0; it < kPasses; ++it) {
+        const int x = tid - base + it * (kThreads - base);
+        const bool ok = x >= 0 && x < c.nown * kMix;
+        const int xx = ok ? x : 0;
+        const int o = xx / kMix, j = xx - o * kMix;
         int ch, sl;
         field_pos(j, ch, sl);
         const float rs = rms_scale(L.xown[o * kChunks + 1][1], a.K, a.norm_eps);
-        const int64_t t = tok0 + c.q + (int64_t)a.G * o;
-        if (t < a.n) a.mixes[t * kMix + j] = L.xown[o * kChunks + ch][sl] * rs;
+        const float v = L.xown[o * kChunks + ch][sl] * rs;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rm, ok ? ((c.q + a.G * o) * kMix + j) * 4 : kOOB,
+                                              0, 0);
     }
     __syncthreads();        // preL is read by write_h; xsum / xown are rewritten next round
 }
@@ -490,11 +557,12 @@ __device__ __forceinline__ bool iteration(Frags<KS>& H, Frags<KS>& M, const Frag
                                           const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, int i) {
     XLoads<PI> X;
     issue_x<PI, FUSED>(X, a, c, i);
-    if (i + 3 < c.nr) load_round<KS>(P, a, c, i + 3);
-    if (i + 1 < c.nr) {
-        to_operands<KS>(M, c, L);
-        publish<KS>(M, a, c, L, i + 1);
-    }
+    // past the group's last round these load zeros (empty resource) and
+    // publish records that nobody reads; no branch keeps the memory
+    // counters countable, so waits stay partial
+    load_round<KS>(P, a, c, i + 3);
+    to_operands<KS>(M, c, L);
+    publish<KS>(M, a, c, L, i + 1);
     if (exchange<PI, KS, FUSED>(X, a, c, L, i)) return false;
     finals<KS, FUSED>(a, c, L, i);
     if (FUSED) write_h<KS>(H, a, c, L, i);
@@ -509,7 +577,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_coop(CoopArgs a) {
     RoundCtx c;
     c.g = blockIdx.x % a.NG;
     c.q = blockIdx.x / a.NG;
-    c.w = threadIdx.x >> 6;
+    c.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);     // wave-uniform: scalar
     c.l = threadIdx.x & 63;
     c.row = c.l & 15;
     c.grp = c.l >> 4;
@@ -519,6 +587,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_coop(CoopArgs a) {
     c.epoch = a.hdr->epoch;
     c.rsrc = __builtin_amdgcn_make_buffer_rsrc(a.part, 0, a.part_bytes, kBufDword3);
     if (c.g >= a.ntiles) return;
+    c.s0 = FUSED ? a.scale[0] : 0.0f;
+    c.bpre = FUSED ? base_of_lane(a.base) : 0.0f;
     c.nr = (int)((a.ntiles - c.g + a.NG - 1) / a.NG);
 
     // weight slice -> LDS as MFMA B fragments, split exactly into bf16 pieces;
@@ -556,8 +626,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_coop(CoopArgs a) {
 
     Frags<KS> H, M, A, B;
     load_round<KS>(H, a, c, 0);
-    if (1 < c.nr) load_round<KS>(M, a, c, 1);
-    if (2 < c.nr) load_round<KS>(A, a, c, 2);
+    load_round<KS>(M, a, c, 1);
+    load_round<KS>(A, a, c, 2);
     to_operands<KS>(H, c, L);
     publish<KS>(H, a, c, L, 0);
     for (int i = 0; i < c.nr; i += 2) {
@@ -566,6 +636,513 @@ __global__ __launch_bounds__(kThreads, 1) void k_coop(CoopArgs a) {
         if (!iteration<KS, PI, FUSED>(H, M, B, A, a, c, L, i + 1)) return;
     }
 }
+
+// ====================================================== wave-specialised kernel
+// Used when a group has 8..32 members.  The 8 waves of a workgroup split
+// into two roles that run one round apart, with one workgroup barrier per
+// round ("tick"):
+//
+//  * MFMA waves (0..3): wave w handles stream w of the member slice and
+//    keeps that stream's weight slice in registers (MFMA B layout), so the
+//    weights never go through LDS.  In tick t a wave issues the residual
+//    of round t+2 as direct global->LDS loads into slot (t+2) % 3, writes
+//    the records of round t-1 from the per-wave partials of the previous
+//    tick, multiplies round t out of slot t % 3 into per-wave partials, and
+//    waits until round t+1 has landed in LDS.
+//  * Exchange waves (4..7): wave x handles tokens 8x..8x+7 of a round.  In
+//    tick t it reads the records of round t-2, forms pre for its tokens
+//    (and the mixes of the token it owns), writes h of round t-2 from the
+//    residual it copied out of slot (t-2) % 3 two ticks earlier, and copies
+//    round t out of slot t % 3 for use two ticks later.
+//
+// The direct-to-LDS loads are issued with inline assembly, so the
+// compiler's memory fences at the barriers do not wait for them; the MFMA
+// waves wait for them explicitly with a vmcnt count that is exact for the
+// fixed sequence of memory instructions of a tick.
+namespace spec {
+
+constexpr int kMW = 4;                  // MFMA waves
+constexpr int kNSlot = 3;               // residual rounds held in LDS
+constexpr int kTokX = kT / 4;           // tokens per exchange wave
+constexpr int kOwnL = 5;                // owned-record loads per exchange wave: chunk pairs (0,1) .. (8,-)
+
+template <int KS>
+struct Geo {
+    static constexpr int kRowB = 4 * 64 * KS + 16;             // bytes per token in a slot (+16 pad)
+    static constexpr int kSlotB = (kT * kRowB + 4095) / 4096 * 4096;
+    static constexpr int kDma = kSlotB / 1024;                 // 1 KB load instructions per round
+    static constexpr int kDmaW = kDma / kMW;                   // per MFMA wave
+    static constexpr int kBlk = 4 * KS;                        // 8-feature blocks per token and stream
+    static constexpr int kItems = kTokX * kBlk;                // h items (token, block) per exchange wave
+    static constexpr int kPass = (kItems + 63) / 64;
+};
+
+template <int KS>
+struct Lds {
+    uint8_t slot[kNSlot][Geo<KS>::kSlotB];
+    float red[2][kMW][kT][kRed];           // per-MFMA-wave partials, double-buffered by round parity
+    float xpre[4][kTokX][4];               // pre of each exchange wave's tokens
+    float xown[4][10][4];                  // member sums of the owned token's records
+    int stop;                              // set when a wait timed out
+};
+
+typedef __attribute__((ext_vector_type(4))) uint32_t v4u;
+
+// Raw buffer resource words over [base, base + bytes); made wave-uniform.
+__device__ __forceinline__ v4u rsrc_words(uintptr_t base, uint32_t bytes) {
+    v4u r;
+    r.x = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    r.y = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32) & 0xFFFFu);
+    r.z = __builtin_amdgcn_readfirstlane(bytes);
+    r.w = (uint32_t)kBufDword3;
+    return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
+}
+
+// One 16-byte-per-lane load from the buffer straight into LDS at
+// lds + 16 * lane (M0 holds the LDS address; saved and restored).
+__device__ __forceinline__ void dma16(v4u rs, uint32_t lds, uint32_t voff) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(rs), "s"(lds)
+        : "memory");
+}
+
+template <int KS>
+struct MState {
+    bf16x8 w[KS][kTiles];                  // weight slice of stream w, MFMA B layout
+    uint32_t dvoff[Geo<KS>::kDmaW];        // lane byte offsets of this wave's loads within a round
+};
+
+template <int KS>
+struct XState {
+    u32x4 rb[2][Geo<KS>::kPass][kHC];      // residual for h, two rounds (by parity)
+    u32x4 P[kTokX];                        // records of the next exchange (issued a tick early)
+    u32x4 O[kOwnL];
+};
+
+// Sum over the 32 lanes of each half-wave (all lanes of a half get the
+// same value): DPP within rows of 16, then a permlane16 swap.
+__device__ __forceinline__ float gsum32(float v) {
+    v = quad_sum(v);
+    v = col4_sum(v);
+    auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(x[0]) + __uint_as_float(x[1]);
+}
+// The value of the lower half-wave (lanes 0..31) and of the upper half
+// (lanes 32..63) of a value that is uniform within each half, in every lane.
+__device__ __forceinline__ void halves(float v, float& lo, float& hi) {
+    auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    lo = __uint_as_float(x[0]);
+    hi = __uint_as_float(x[1]);
+}
+
+template <int KS>
+__device__ __forceinline__ void m_setup(MState<KS>& S, const CoopArgs& a, const RoundCtx& c) {
+    // weight slice of stream w: k-step st, lane (column i, k-block grp) holds
+    // features 32*st + 8*grp .. +7 of stream w of the member slice
+    const int64_t K = (int64_t)kHC * a.d;
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+#pragma unroll
+        for (int ct = 0; ct < kTiles; ++ct) {
+            int piece, j;
+            if (ct < 3) { piece = ct; j = c.row; }
+            else if (ct == 3) { piece = c.row < 8 ? 0 : 1; j = 16 + (c.row & 7); }
+            else { piece = c.row < 8 ? 2 : -1; j = 16 + c.row; }
+            const int jj = piece < 0 ? 0 : j;
+            const f32x4* src = reinterpret_cast<const f32x4*>(a.W + jj * K + (int64_t)c.w * a.d +
+                                                              c.q * (32 * KS) + 32 * st + 8 * c.grp);
+            const f32x4 w0 = src[0], w1 = src[1];
+            bf16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = e < 4 ? w0[e] : w1[e - 4];
+                const __bf16 hi = (__bf16)x;
+                const float r1 = x - (float)hi;
+                const __bf16 mid = (__bf16)r1;
+                const __bf16 lo = (__bf16)(r1 - (float)mid);
+                v[e] = piece == 0 ? hi : (piece == 1 ? mid : (piece == 2 ? lo : (__bf16)0.0f));
+            }
+            // pinned in registers: keeps the compiler from re-forming the
+            // pieces inside the round loop
+            u32x4 pinned = __builtin_bit_cast(u32x4, v);
+            asm volatile("" : "+v"(pinned));
+            S.w[st][ct] = __builtin_bit_cast(bf16x8, pinned);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < Geo<KS>::kDmaW; ++i) {
+        const int I = c.w * Geo<KS>::kDmaW + i;
+        const int pos = I * 1024 + 16 * c.l;
+        const int tk = pos / Geo<KS>::kRowB, wb = pos - tk * Geo<KS>::kRowB;
+        const int k = wb / (64 * KS), off = wb - k * (64 * KS);
+        S.dvoff[i] = (tk < kT && k < kHC) ? (uint32_t)(tk * 8 * a.d + k * 2 * a.d + c.q * (64 * KS) + off)
+                                          : (uint32_t)kOOB;
+    }
+}
+
+// Round r of this group into slot r % 3 (rounds past the end: zeros).
+template <int KS>
+__device__ __forceinline__ void m_dma(const MState<KS>& S, const CoopArgs& a, const RoundCtx& c, Lds<KS>& L,
+                                      int r) {
+    const int64_t tok0 = tile_of(c, a, r) * kT;
+    int64_t valid = a.n - tok0;
+    valid = valid < 0 ? 0 : (valid > kT ? kT : valid);
+    const v4u rs = rsrc_words(reinterpret_cast<uintptr_t>(a.R) + (uintptr_t)(valid > 0 ? tok0 : 0) * 8 * a.d,
+                              (uint32_t)(valid * 8 * a.d));
+    const uint32_t base = lds_addr(&L.slot[r % kNSlot][0]) + c.w * Geo<KS>::kDmaW * 1024;
+#pragma unroll
+    for (int i = 0; i < Geo<KS>::kDmaW; ++i) dma16(rs, base + i * 1024, S.dvoff[i]);
+}
+
+// Records of round r from the partials of the four MFMA waves (two store
+// instructions per wave, always; past the group's rounds they are dropped).
+template <int KS>
+__device__ __forceinline__ void m_publish(const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, int r) {
+    const int tid = threadIdx.x;
+    const int b = r & 1;
+    const bool live = r >= 0 && r < c.nr;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int idx = p * (kMW * 64) + tid;
+        const int ch = idx / kT, tk = idx - ch * kT;
+        u32x4 v;
+#pragma unroll
+        for (int sl = 0; sl < 3; ++sl) {
+            const int fi = field_at(ch, sl);
+            float x = 0.0f;
+            if (fi >= 0)
+                x = ((L.red[b][0][tk][fi] + L.red[b][1][tk][fi]) + L.red[b][2][tk][fi]) + L.red[b][3][tk][fi];
+            v[sl] = __float_as_uint(x);
+        }
+        v[3] = tag_of(c, r);
+        st_dev(c, live && ch < kChunks ? rec_off(a, c, r, ch, tk, c.q) : kOOB, v);
+    }
+}
+
+// Partial mixes and sum of squares of stream w for round r (slot r % 3).
+template <int KS>
+__device__ __forceinline__ void m_mfma(const MState<KS>& S, const RoundCtx& c, Lds<KS>& L, int r) {
+    const uint8_t* slot = &L.slot[r % kNSlot][0];
+    const int b = r & 1;
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt) {
+        f32x4 acc[kTiles];
+#pragma unroll
+        for (int ct = 0; ct < kTiles; ++ct) acc[ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        float sq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+            const u32x4 av = *reinterpret_cast<const u32x4*>(
+                slot + (16 * tt + c.row) * Geo<KS>::kRowB + c.w * (64 * KS) + 64 * st + 16 * c.grp);
+            const bf16x8 ab = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+            for (int ct = 0; ct < kTiles; ++ct)
+                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, S.w[st][ct], acc[ct], 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lo = bf_lo(av[e]), hi = bf_hi(av[e]);
+                sq[e] = __builtin_fmaf(hi, hi, __builtin_fmaf(lo, lo, sq[e]));
+            }
+        }
+        float ss = (sq[0] + sq[1]) + (sq[2] + sq[3]);
+        {
+            auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+            ss = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+            auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+            ss = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+        }
+        if (c.grp == 0) L.red[b][c.w][16 * tt + c.row][24] = ss;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int t = 16 * tt + 4 * c.grp + rr;
+            const float v0 = (acc[2][rr] + acc[1][rr]) + acc[0][rr];
+            const float t3 = acc[3][rr];
+            const float t3x = dpp<0x128>(t3);
+            const float v1 = (acc[4][rr] + t3x) + t3;
+            L.red[b][c.w][t][c.row] = v0;
+            if (c.row < 8) L.red[b][c.w][t][16 + c.row] = v1;
+        }
+    }
+}
+
+// Record loads of round r for exchange wave xw: the pre-relevant records
+// (chunks 0 and 1) of tokens 8xw..8xw+7 and all records of owned token xw.
+// Lanes 0..31 read chunk 2i (or 0) of members 0..31, lanes 32..63 chunk
+// 2i+1 (or 1).  Device scope: a record slot is rewritten every 4 rounds and
+// a copy of the old record may still sit in this CU's L1.
+template <bool FUSED>
+__device__ __forceinline__ bool pre_ok(const CoopArgs& a, const RoundCtx& c) {
+    return FUSED && (c.l & 31) < a.G;
+}
+__device__ __forceinline__ bool own_ok(const CoopArgs& a, const RoundCtx& c, int xw, int i) {
+    return xw < c.nown && (c.l & 31) < a.G && 2 * i + (c.l >> 5) < kChunks;
+}
+template <int KS, bool FUSED>
+__device__ __forceinline__ void x_issue(XState<KS>& X, const CoopArgs& a, const RoundCtx& c, int xw, int r) {
+    const int half = c.l >> 5, m = c.l & 31;
+    const int otk = c.q + a.G * xw;
+#pragma unroll
+    for (int j = 0; j < kTokX; ++j)
+        X.P[j] = ld_dev(c, pre_ok<FUSED>(a, c) ? rec_off(a, c, r, half, kTokX * xw + j, m) : kOOB);
+#pragma unroll
+    for (int i = 0; i < kOwnL; ++i)
+        X.O[i] = ld_dev(c, own_ok(a, c, xw, i) ? rec_off(a, c, r, 2 * i + half, otk, m) : kOOB);
+}
+
+// Exchange of round r for exchange wave xw, from the loads issued by
+// x_issue: pre of tokens 8xw..8xw+7 (into L.xpre, and the pre output of the
+// tokens this member owns) and the mixes of owned token xw.  A record that
+// still carries an older tag is re-read until current (bounded in time).
+// Returns true on a timeout.
+template <int KS, bool FUSED>
+__device__ __forceinline__ bool x_exchange(XState<KS>& X, const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, int xw,
+                                           int r) {
+    const uint32_t tag = tag_of(c, r);
+    const int l = c.l, half = l >> 5, m = l & 31;
+    const int otk = c.q + a.G * xw;
+    const int64_t tok0 = tile_of(c, a, r) * kT;
+    bool stale = false;
+#pragma unroll
+    for (int j = 0; j < kTokX; ++j) stale |= pre_ok<FUSED>(a, c) && X.P[j][3] != tag;
+#pragma unroll
+    for (int i = 0; i < kOwnL; ++i) stale |= own_ok(a, c, xw, i) && X.O[i][3] != tag;
+    bool bad = false;
+    if (__builtin_amdgcn_ballot_w64(stale)) {              // wave-uniform: a peer is late
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        for (;;) {
+            // re-issue every stale load at once (the others read past the
+            // resource), then wait for all of them
+            u32x4 RP[kTokX], RO[kOwnL];
+#pragma unroll
+            for (int j = 0; j < kTokX; ++j) {
+                const bool need = pre_ok<FUSED>(a, c) && X.P[j][3] != tag;
+                RP[j] = ld_dev(c, need ? rec_off(a, c, r, half, kTokX * xw + j, m) : kOOB);
+            }
+#pragma unroll
+            for (int i = 0; i < kOwnL; ++i) {
+                const bool need = own_ok(a, c, xw, i) && X.O[i][3] != tag;
+                RO[i] = ld_dev(c, need ? rec_off(a, c, r, 2 * i + half, otk, m) : kOOB);
+            }
+            bool again = false;
+#pragma unroll
+            for (int j = 0; j < kTokX; ++j)
+                if (pre_ok<FUSED>(a, c) && X.P[j][3] != tag) {
+                    X.P[j] = RP[j];
+                    again |= RP[j][3] != tag;
+                }
+#pragma unroll
+            for (int i = 0; i < kOwnL; ++i)
+                if (own_ok(a, c, xw, i) && X.O[i][3] != tag) {
+                    X.O[i] = RO[i];
+                    again |= RO[i][3] != tag;
+                }
+            if (!__builtin_amdgcn_ballot_w64(again)) break;
+            if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull ||
+                __hip_atomic_load(&a.hdr->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+                __hip_atomic_store(&a.hdr->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                bad = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    float pre_mine = 0.0f;          // lanes 0..31: pre of (token l/4, stream l%4)
+    if (FUSED) {
+        // lanes < 32 hold chunk 0 (m0 m1 m2), lanes >= 32 chunk 1 (m3 ss m4);
+        // lane 4j+k keeps m_k and the sum of squares of token j, then all
+        // 32 gates are formed at once
+        const int k = l & 3, jl = (l >> 2) & (kTokX - 1);
+        float mine_m = 0.0f, mine_ss = 1.0f;
+#pragma unroll
+        for (int j = 0; j < kTokX; ++j) {
+            const float s0 = gsum32(__uint_as_float(X.P[j][0]));
+            const float s1 = gsum32(__uint_as_float(X.P[j][1]));
+            const float s2 = gsum32(__uint_as_float(X.P[j][2]));
+            float m0, m3, m1, ss, m2, m4;
+            halves(s0, m0, m3);           // chunk 0 slot 0 = m0, chunk 1 slot 0 = m3
+            halves(s1, m1, ss);           // chunk 0 slot 1 = m1, chunk 1 slot 1 = sum of squares
+            halves(s2, m2, m4);           // chunk 0 slot 2 = m2 (m4 unused)
+            (void)m4;
+            const float mk = k == 0 ? m0 : (k == 1 ? m1 : (k == 2 ? m2 : m3));
+            mine_m = jl == j ? mk : mine_m;
+            mine_ss = jl == j ? ss : mine_ss;
+        }
+        pre_mine = pre_gate(mine_m * rms_scale(mine_ss, a.K, a.norm_eps), c.s0, c.bpre, a.eps);
+        if (l < 4 * kTokX) L.xpre[xw][jl][k] = pre_mine;
+    }
+#pragma unroll
+    for (int i = 0; i < kOwnL; ++i) {
+        const float s0 = gsum32(__uint_as_float(X.O[i][0]));
+        const float s1 = gsum32(__uint_as_float(X.O[i][1]));
+        const float s2 = gsum32(__uint_as_float(X.O[i][2]));
+        const int ch = 2 * i + half;
+        if ((l & 31) == 0 && ch < kChunks) {
+            L.xown[xw][ch][0] = s0;
+            L.xown[xw][ch][1] = s1;
+            L.xown[xw][ch][2] = s2;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");     // the wave reads back its own LDS writes
+    {
+        // mixes of the owned token: lanes 0..23
+        const int f = l < kMix ? l : 0;
+        int ch, sl;
+        field_pos(f, ch, sl);
+        const float v = L.xown[xw][ch][sl] * rms_scale(L.xown[xw][1][1], a.K, a.norm_eps);
+        const __amdgpu_buffer_rsrc_t rm = tile_rsrc(a.mixes, kMix * 4, tok0, a.n, kT);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rm,
+                                              xw < c.nown && l < kMix ? (otk * kMix + l) * 4 : kOOB, 0, 0);
+    }
+    if (FUSED) {
+        // pre output of the tokens this member owns: lanes 0..31 = (token j, stream k)
+        const int j = (l >> 2) & (kTokX - 1), k = l & 3, tk = kTokX * xw + j;
+        const __amdgpu_buffer_rsrc_t rp = tile_rsrc(a.pre, kHC * 4, tok0, a.n, kT);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pre_mine), rp,
+                                              l < 4 * kTokX && tk % a.G == c.q ? (tk * kHC + k) * 4 : kOOB, 0, 0);
+    }
+    return bad;
+}
+
+// h of round r for exchange wave xw from the residual copy rb.
+template <int KS>
+__device__ __forceinline__ void x_h(const u32x4 (&rb)[Geo<KS>::kPass][kHC], const CoopArgs& a, const RoundCtx& c,
+                                    Lds<KS>& L, int xw, int r) {
+    const int64_t tok0 = tile_of(c, a, r) * kT;
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(a.h, (int64_t)a.d * 2, tok0, a.n, kT);
+#pragma unroll
+    for (int p = 0; p < Geo<KS>::kPass; ++p) {
+        const int item = p * 64 + c.l;
+        const bool valid = item < Geo<KS>::kItems;
+        const int it = valid ? item : 0;
+        const int tk = it / Geo<KS>::kBlk, b = it - tk * Geo<KS>::kBlk;
+        const f32x4 pq = *reinterpret_cast<const f32x4*>(&L.xpre[xw][tk][0]);
+        const double p0 = pq[0], p1 = pq[1], p2 = pq[2], p3 = pq[3];
+        u32x4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            double lo = p0 * (double)bf_lo(rb[p][0][e]);
+            lo = __builtin_fma(p1, (double)bf_lo(rb[p][1][e]), lo);
+            lo = __builtin_fma(p2, (double)bf_lo(rb[p][2][e]), lo);
+            lo = __builtin_fma(p3, (double)bf_lo(rb[p][3][e]), lo);
+            double hi = p0 * (double)bf_hi(rb[p][0][e]);
+            hi = __builtin_fma(p1, (double)bf_hi(rb[p][1][e]), hi);
+            hi = __builtin_fma(p2, (double)bf_hi(rb[p][2][e]), hi);
+            hi = __builtin_fma(p3, (double)bf_hi(rb[p][3][e]), hi);
+            out[e] = pack2(bf16_rn_f64(lo), bf16_rn_f64(hi));
+        }
+        const int off = valid ? ((kTokX * xw + tk) * a.d + c.q * (32 * KS) + 8 * b) * 2 : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((__vector_size__(16))) int, out),
+                                               rs, off, 0, 2);
+    }
+}
+
+// Copy of round r's residual (slot r % 3) for this wave's h items.
+template <int KS>
+__device__ __forceinline__ void x_copy(u32x4 (&rb)[Geo<KS>::kPass][kHC], const RoundCtx& c, Lds<KS>& L, int xw,
+                                       int r) {
+    const uint8_t* slot = &L.slot[r % kNSlot][0];
+#pragma unroll
+    for (int p = 0; p < Geo<KS>::kPass; ++p) {
+        const int item = p * 64 + c.l;
+        const int it = item < Geo<KS>::kItems ? item : 0;
+        const int tk = it / Geo<KS>::kBlk, b = it - tk * Geo<KS>::kBlk;
+#pragma unroll
+        for (int k = 0; k < kHC; ++k)
+            rb[p][k] = *reinterpret_cast<const u32x4*>(slot + (kTokX * xw + tk) * Geo<KS>::kRowB + k * (64 * KS) +
+                                                      16 * b);
+    }
+}
+
+// Exchange-wave part of tick t; P is the parity of t (selects the residual
+// copy).  Returns true on a timeout.
+template <int KS, bool FUSED, int P>
+__device__ __forceinline__ bool x_tick(XState<KS>& X, const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, int t) {
+    const int xw = c.w - kMW;
+    bool bad = false;
+    if (t >= 2 && t - 2 < c.nr) {
+        bad = x_exchange<KS, FUSED>(X, a, c, L, xw, t - 2);
+        if (FUSED && !bad) x_h<KS>(X.rb[P], a, c, L, xw, t - 2);
+    }
+    if (FUSED) x_copy<KS>(X.rb[P], c, L, xw, t);
+    // records of round t-1 (published at the start of this tick) for the
+    // next tick's exchange: their latency overlaps the barrier
+    if (t >= 1 && t - 1 < c.nr) x_issue<KS, FUSED>(X, a, c, xw, t - 1);
+    return bad;
+}
+
+// The two roles run separate loops with the same barrier sequence: a
+// prologue barrier, then one barrier per tick t = 0 .. nr+1 (the exchange of
+// the last round happens in tick nr+1); after each barrier both read the
+// stop flag, so both leave after the same tick.
+template <int KS, bool FUSED>
+__global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
+    __shared__ __attribute__((aligned(16))) Lds<KS> L;
+    RoundCtx c;
+    c.g = blockIdx.x % a.NG;
+    c.q = blockIdx.x / a.NG;
+    c.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    c.l = threadIdx.x & 63;
+    c.row = c.l & 15;
+    c.grp = c.l >> 4;
+    c.tt = 0;
+    c.kg = 0;
+    c.nown = c.q < kT ? (kT - 1 - c.q) / a.G + 1 : 0;
+    c.epoch = a.hdr->epoch;
+    c.rsrc = __builtin_amdgcn_make_buffer_rsrc(a.part, 0, a.part_bytes, kBufDword3);
+    if (c.g >= a.ntiles) return;
+    c.nr = (int)((a.ntiles - c.g + a.NG - 1) / a.NG);
+    c.s0 = FUSED ? a.scale[0] : 0.0f;
+    c.bpre = FUSED ? base_of_lane(a.base) : 0.0f;
+    const int last = c.nr + 1;
+
+    if (c.w < kMW) {
+        MState<KS> S;
+        m_setup<KS>(S, a, c);
+        m_dma<KS>(S, a, c, L, 0);
+        m_dma<KS>(S, a, c, L, 1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW) : "memory");   // round 0 landed
+        __syncthreads();
+        for (int t = 0;; ++t) {
+            m_dma<KS>(S, a, c, L, t + 2);
+            m_publish<KS>(a, c, L, t - 1);
+            m_mfma<KS>(S, c, L, t);
+            // round t+1 (issued last tick) must be in LDS before the barrier:
+            // younger than its loads are only this tick's loads and the two
+            // record stores of this tick
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW + 2) : "memory");
+            __syncthreads();
+            if (L.stop || t + 1 > last) break;
+        }
+        // no load may still be writing this workgroup's LDS when it ends
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+        XState<KS> X;
+        if (threadIdx.x == kMW * 64) L.stop = 0;
+        __syncthreads();
+        for (int t = 0;; t += 2) {
+            if (x_tick<KS, FUSED, 0>(X, a, c, L, t)) L.stop = 1;
+            __syncthreads();
+            if (L.stop || t + 1 > last) break;
+            if (x_tick<KS, FUSED, 1>(X, a, c, L, t + 1)) L.stop = 1;
+            __syncthreads();
+            if (L.stop || t + 2 > last) break;
+        }
+    }
+}
+
+}  // namespace spec
 
 // Per-call header update.  Clears the record area on the first use of a
 // workspace, when the 20-bit call epoch wraps, and when this call's record
@@ -647,6 +1224,17 @@ static int launch_ks(const CoopPlan& p, CoopArgs& a, bool fused, hipStream_t s) 
     return fused ? launch_t<KS, 8, true>(p, a, s) : launch_t<KS, 8, false>(p, a, s);
 }
 
+// Wave-specialised kernel: groups of 8..32 members.
+static bool use_spec(const CoopPlan& p) { return p.G >= 8 && p.G <= 32; }
+
+template <int KS>
+static int launch_spec(const CoopPlan& p, CoopArgs& a, bool fused, hipStream_t s) {
+    void* args[] = {&a};
+    const void* f = fused ? (const void*)spec::k_spec<KS, true> : (const void*)spec::k_spec<KS, false>;
+    hipError_t e = hipLaunchCooperativeKernel(f, dim3(p.G * p.NG), dim3(kThreads), args, 0, s);
+    return e == hipSuccess ? 0 : -1;
+}
+
 int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* scale, const float* base,
                 void* h, float* pre, float* post, float* comb, float* mixes, void* ws, int64_t n, int d,
                 int iters, float eps, float norm_eps, bool fused, hipStream_t s) {
@@ -678,7 +1266,15 @@ int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* s
     k_init<<<1, 1024, 0, s>>>(a.hdr, a.part, (int64_t)(a.part_bytes / 16));
     if (hipGetLastError() != hipSuccess) return -1;
     int rc = -1;
-    switch (p.KS) {
+    if (use_spec(p)) {
+        switch (p.KS) {
+            case 1: rc = launch_spec<1>(p, a, fused, s); break;
+            case 2: rc = launch_spec<2>(p, a, fused, s); break;
+            case 3: rc = launch_spec<3>(p, a, fused, s); break;
+            case 4: rc = launch_spec<4>(p, a, fused, s); break;
+            case 5: rc = launch_spec<5>(p, a, fused, s); break;
+        }
+    } else switch (p.KS) {
         case 1: rc = launch_ks<1>(p, a, fused, s); break;
         case 2: rc = launch_ks<2>(p, a, fused, s); break;
         case 3: rc = launch_ks<3>(p, a, fused, s); break;

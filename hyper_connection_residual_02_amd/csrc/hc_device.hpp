@@ -73,8 +73,14 @@ __device__ __forceinline__ float col4_sum(float v) {
     return v + dpp<0x124>(v);
 }
 
-// Logistic function in float.
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
+// Logistic function in float: hardware exp2 and reciprocal (each within
+// about one ulp), so the gate costs a handful of instructions.  Every
+// kernel that forms a gate calls this one function, so all entry points
+// agree bit for bit.
+__device__ __forceinline__ float sigmoidf_(float z) {
+    const float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+    return __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // The read and write gates of the split, shared by every kernel that forms
 // them so that all entry points agree bit for bit.
@@ -83,9 +89,11 @@ __device__ __forceinline__ float pre_gate(float m, float s0, float b, float eps)
 }
 __device__ __forceinline__ float post_gate(float m, float s1, float b) { return 2.0f * sigmoidf_(m * s1 + b); }
 
-// RMS normaliser of the mix formula: 1 / sqrt(sum_sq / K + norm_eps).
+// RMS normaliser of the mix formula: 1 / sqrt(sum_sq / K + norm_eps), with
+// the hardware reciprocal square root (about one ulp).  One function for
+// every kernel, so the mixes and pre of all entry points agree bit for bit.
 __device__ __forceinline__ float rms_scale(float sum_sq, float K, float norm_eps) {
-    return 1.0f / sqrtf(sum_sq / K + norm_eps);
+    return __builtin_amdgcn_rsqf(sum_sq * __builtin_amdgcn_rcpf(K) + norm_eps);
 }
 
 // ------------------------------------------------- split + epsilon-Sinkhorn
