@@ -38,9 +38,10 @@
 //    issue order, so exchange loads go out before residual prefetches, and
 //    nothing waits for a store to complete: readers check tags instead.
 //  * Workgroup b belongs to group b % NG; with NG = 8 a group sits on one
-//    XCD (workgroups are dispatched round-robin over the XCDs), so the
-//    first read of a record is served by that XCD's L2.  A record with a
-//    stale tag is re-read at device scope, so placement only affects speed.
+//    XCD (workgroups are dispatched round-robin over the XCDs).  Records
+//    are written and read at device scope (loads skip the L1, whose copy
+//    of a slot's previous record a group-scope load can keep returning), so
+//    placement only affects speed.
 //  * Every wait is bounded in time; a timed-out wait raises a flag in the
 //    workspace header and the workgroup stops.
 
@@ -73,6 +74,8 @@ struct WsHeader {
     uint32_t epoch;
     uint32_t err;
     int64_t clean;
+    uint32_t xbad;      // workgroups not on the XCD their group is placed on (this call)
+    uint32_t arrive;    // workgroups past the placement check (this call)
 };
 
 struct CoopArgs {
@@ -171,8 +174,8 @@ __device__ __forceinline__ int rec_off(const CoopArgs& a, const RoundCtx& c, int
     return ((((c.g * kSlots + slot) * kChunks + chunk) * kT + t) * a.GP + member) * 16;
 }
 
-__device__ __forceinline__ u32x4 ld_l2(const RoundCtx& c, int off) {   // first read: served by the L2
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(c.rsrc, off, 0, 1));
+__device__ __forceinline__ u32x4 ld_l2(const RoundCtx& c, int off) {   // first read: device scope, skips the L1
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(c.rsrc, off, 0, 16));
 }
 __device__ __forceinline__ u32x4 ld_dev(const RoundCtx& c, int off) {  // re-read: device scope
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(c.rsrc, off, 0, 16));
@@ -664,7 +667,8 @@ namespace spec {
 constexpr int kMW = 4;                  // MFMA waves
 constexpr int kNSlot = 3;               // residual rounds held in LDS
 constexpr int kTokX = kT / 4;           // tokens per exchange wave
-constexpr int kOwnL = 5;                // owned-record loads per exchange wave: chunk pairs (0,1) .. (8,-)
+constexpr int kPreR = kTokX / 2;        // load rounds for the pre-relevant records (4 pairs each)
+constexpr int kOwnR = 3;                // load rounds for the owned token's 9 chunks (4 per round)
 
 template <int KS>
 struct Geo {
@@ -727,8 +731,8 @@ struct MState {
 template <int KS>
 struct XState {
     u32x4 rb[2][Geo<KS>::kPass][kHC];      // residual for h, two rounds (by parity)
-    u32x4 P[kTokX];                        // records of the next exchange (issued a tick early)
-    u32x4 O[kOwnL];
+    u32x4 P[kPreR][2];                     // records of the next exchange (issued a tick early)
+    u32x4 O[kOwnR][2];
 };
 
 // Sum over the 32 lanes of each half-wave (all lanes of a half get the
@@ -745,6 +749,22 @@ __device__ __forceinline__ void halves(float v, float& lo, float& hi) {
     auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     lo = __uint_as_float(x[0]);
     hi = __uint_as_float(x[1]);
+}
+
+// Record stores and loads.  Loads are device scope (sc1): they skip the
+// L1, which may hold a copy of a slot's previous record (a group-scope load
+// can keep returning that copy).  LOCAL: every member of the group runs on
+// one XCD, so plain stores, which stay in that XCD's L2, are enough (about
+// half the latency of a device-scope store); otherwise stores are device
+// scope too.
+template <bool LOCAL>
+__device__ __forceinline__ u32x4 ld_rec(const RoundCtx& c, int off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(c.rsrc, off, 0, 16));
+}
+template <bool LOCAL>
+__device__ __forceinline__ void st_rec(const RoundCtx& c, int off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((__vector_size__(16))) int, v), c.rsrc,
+                                           off, 0, LOCAL ? 0 : 16);
 }
 
 template <int KS>
@@ -808,7 +828,7 @@ __device__ __forceinline__ void m_dma(const MState<KS>& S, const CoopArgs& a, co
 
 // Records of round r from the partials of the four MFMA waves (two store
 // instructions per wave, always; past the group's rounds they are dropped).
-template <int KS>
+template <int KS, bool LOCAL>
 __device__ __forceinline__ void m_publish(const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, int r) {
     const int tid = threadIdx.x;
     const int b = r & 1;
@@ -827,7 +847,7 @@ __device__ __forceinline__ void m_publish(const CoopArgs& a, const RoundCtx& c, 
             v[sl] = __float_as_uint(x);
         }
         v[3] = tag_of(c, r);
-        st_dev(c, live && ch < kChunks ? rec_off(a, c, r, ch, tk, c.q) : kOOB, v);
+        st_rec<LOCAL>(c, live && ch < kChunks ? rec_off(a, c, r, ch, tk, c.q) : kOOB, v);
     }
 }
 
@@ -877,28 +897,47 @@ __device__ __forceinline__ void m_mfma(const MState<KS>& S, const RoundCtx& c, L
     }
 }
 
+// Lane layout of the exchange loads: a (chunk, token) pair takes one row of
+// 16 lanes; lane e of the row reads members e and e + 16, so each load
+// instruction reads 256 contiguous bytes per row.  Members past G read past
+// the resource (zeros).  Pre-relevant round q: row r holds chunk r & 1 of
+// token 8xw + 2q + (r >> 1).  Owned round q: row r holds chunk 4q + r of
+// the owned token.
+__device__ __forceinline__ int x_member(const RoundCtx& c, int i) { return (c.l & 15) + 16 * i; }
+
+// Member sum of a pair (all 16 lanes of the row get it): members e and
+// e + 16 in the lane, then the row.  Shared by the pre and owner paths, so
+// both form bitwise the same sums.
+__device__ __forceinline__ float row_member_sum(uint32_t a, uint32_t b) {
+    float v = __uint_as_float(a) + __uint_as_float(b);
+    v = quad_sum(v);
+    return col4_sum(v);
+}
+
 // Record loads of round r for exchange wave xw: the pre-relevant records
 // (chunks 0 and 1) of tokens 8xw..8xw+7 and all records of owned token xw.
 // Lanes 0..31 read chunk 2i (or 0) of members 0..31, lanes 32..63 chunk
 // 2i+1 (or 1).  Device scope: a record slot is rewritten every 4 rounds and
 // a copy of the old record may still sit in this CU's L1.
-template <bool FUSED>
-__device__ __forceinline__ bool pre_ok(const CoopArgs& a, const RoundCtx& c) {
-    return FUSED && (c.l & 31) < a.G;
-}
-__device__ __forceinline__ bool own_ok(const CoopArgs& a, const RoundCtx& c, int xw, int i) {
-    return xw < c.nown && (c.l & 31) < a.G && 2 * i + (c.l >> 5) < kChunks;
-}
-template <int KS, bool FUSED>
+template <int KS, bool FUSED, bool LOCAL>
 __device__ __forceinline__ void x_issue(XState<KS>& X, const CoopArgs& a, const RoundCtx& c, int xw, int r) {
-    const int half = c.l >> 5, m = c.l & 31;
+    const int row = c.l >> 4;
     const int otk = c.q + a.G * xw;
 #pragma unroll
-    for (int j = 0; j < kTokX; ++j)
-        X.P[j] = ld_dev(c, pre_ok<FUSED>(a, c) ? rec_off(a, c, r, half, kTokX * xw + j, m) : kOOB);
+    for (int q = 0; q < kPreR; ++q)
 #pragma unroll
-    for (int i = 0; i < kOwnL; ++i)
-        X.O[i] = ld_dev(c, own_ok(a, c, xw, i) ? rec_off(a, c, r, 2 * i + half, otk, m) : kOOB);
+        for (int i = 0; i < 2; ++i) {
+            const int m = x_member(c, i);
+            X.P[q][i] = ld_rec<LOCAL>(
+                c, FUSED && m < a.G ? rec_off(a, c, r, row & 1, kTokX * xw + 2 * q + (row >> 1), m) : kOOB);
+        }
+#pragma unroll
+    for (int q = 0; q < kOwnR; ++q)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int m = x_member(c, i), ch = 4 * q + row;
+            X.O[q][i] = ld_rec<LOCAL>(c, xw < c.nown && m < a.G && ch < kChunks ? rec_off(a, c, r, ch, otk, m) : kOOB);
+        }
 }
 
 // Exchange of round r for exchange wave xw, from the loads issued by
@@ -906,48 +945,53 @@ __device__ __forceinline__ void x_issue(XState<KS>& X, const CoopArgs& a, const 
 // tokens this member owns) and the mixes of owned token xw.  A record that
 // still carries an older tag is re-read until current (bounded in time).
 // Returns true on a timeout.
-template <int KS, bool FUSED>
+template <int KS, bool FUSED, bool LOCAL>
 __device__ __forceinline__ bool x_exchange(XState<KS>& X, const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, int xw,
                                            int r) {
     const uint32_t tag = tag_of(c, r);
-    const int l = c.l, half = l >> 5, m = l & 31;
+    const int l = c.l, row = l >> 4;
     const int otk = c.q + a.G * xw;
     const int64_t tok0 = tile_of(c, a, r) * kT;
+    // which loads name a real record
+    auto pre_live = [&](int i) { return FUSED && x_member(c, i) < a.G; };
+    auto own_live = [&](int q, int i) { return xw < c.nown && x_member(c, i) < a.G && 4 * q + row < kChunks; };
+    auto pre_off = [&](int q, int i) {
+        return rec_off(a, c, r, row & 1, kTokX * xw + 2 * q + (row >> 1), x_member(c, i));
+    };
+    auto own_off = [&](int q, int i) { return rec_off(a, c, r, 4 * q + row, otk, x_member(c, i)); };
     bool stale = false;
 #pragma unroll
-    for (int j = 0; j < kTokX; ++j) stale |= pre_ok<FUSED>(a, c) && X.P[j][3] != tag;
+    for (int q = 0; q < kPreR; ++q)
 #pragma unroll
-    for (int i = 0; i < kOwnL; ++i) stale |= own_ok(a, c, xw, i) && X.O[i][3] != tag;
+        for (int i = 0; i < 2; ++i) stale |= pre_live(i) && X.P[q][i][3] != tag;
+#pragma unroll
+    for (int q = 0; q < kOwnR; ++q)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) stale |= own_live(q, i) && X.O[q][i][3] != tag;
     bool bad = false;
     if (__builtin_amdgcn_ballot_w64(stale)) {              // wave-uniform: a peer is late
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
         for (;;) {
-            // re-issue every stale load at once (the others read past the
-            // resource), then wait for all of them
-            u32x4 RP[kTokX], RO[kOwnL];
+            // re-read every record of the exchange at once: a record that was
+            // already current comes back unchanged (its slot is not rewritten
+            // before every member has finished this round)
 #pragma unroll
-            for (int j = 0; j < kTokX; ++j) {
-                const bool need = pre_ok<FUSED>(a, c) && X.P[j][3] != tag;
-                RP[j] = ld_dev(c, need ? rec_off(a, c, r, half, kTokX * xw + j, m) : kOOB);
-            }
+            for (int q = 0; q < kPreR; ++q)
 #pragma unroll
-            for (int i = 0; i < kOwnL; ++i) {
-                const bool need = own_ok(a, c, xw, i) && X.O[i][3] != tag;
-                RO[i] = ld_dev(c, need ? rec_off(a, c, r, 2 * i + half, otk, m) : kOOB);
-            }
+                for (int i = 0; i < 2; ++i) X.P[q][i] = ld_rec<LOCAL>(c, pre_live(i) ? pre_off(q, i) : kOOB);
+#pragma unroll
+            for (int q = 0; q < kOwnR; ++q)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) X.O[q][i] = ld_rec<LOCAL>(c, own_live(q, i) ? own_off(q, i) : kOOB);
             bool again = false;
 #pragma unroll
-            for (int j = 0; j < kTokX; ++j)
-                if (pre_ok<FUSED>(a, c) && X.P[j][3] != tag) {
-                    X.P[j] = RP[j];
-                    again |= RP[j][3] != tag;
-                }
+            for (int q = 0; q < kPreR; ++q)
 #pragma unroll
-            for (int i = 0; i < kOwnL; ++i)
-                if (own_ok(a, c, xw, i) && X.O[i][3] != tag) {
-                    X.O[i] = RO[i];
-                    again |= RO[i][3] != tag;
-                }
+                for (int i = 0; i < 2; ++i) again |= pre_live(i) && X.P[q][i][3] != tag;
+#pragma unroll
+            for (int q = 0; q < kOwnR; ++q)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) again |= own_live(q, i) && X.O[q][i][3] != tag;
             if (!__builtin_amdgcn_ballot_w64(again)) break;
             if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull ||
                 __hip_atomic_load(&a.hdr->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
@@ -960,38 +1004,50 @@ __device__ __forceinline__ bool x_exchange(XState<KS>& X, const CoopArgs& a, con
     }
     float pre_mine = 0.0f;          // lanes 0..31: pre of (token l/4, stream l%4)
     if (FUSED) {
-        // lanes < 32 hold chunk 0 (m0 m1 m2), lanes >= 32 chunk 1 (m3 ss m4);
-        // lane 4j+k keeps m_k and the sum of squares of token j, then all
-        // 32 gates are formed at once
+        // round q: rows 0,1 hold chunks 0,1 of token 2q, rows 2,3 of token
+        // 2q+1; a permlane16 swap pairs the chunks, a permlane32 swap the
+        // tokens, so every lane sees both tokens' m0..m3 and sum of squares
         const int k = l & 3, jl = (l >> 2) & (kTokX - 1);
         float mine_m = 0.0f, mine_ss = 1.0f;
 #pragma unroll
-        for (int j = 0; j < kTokX; ++j) {
-            const float s0 = gsum32(__uint_as_float(X.P[j][0]));
-            const float s1 = gsum32(__uint_as_float(X.P[j][1]));
-            const float s2 = gsum32(__uint_as_float(X.P[j][2]));
-            float m0, m3, m1, ss, m2, m4;
-            halves(s0, m0, m3);           // chunk 0 slot 0 = m0, chunk 1 slot 0 = m3
-            halves(s1, m1, ss);           // chunk 0 slot 1 = m1, chunk 1 slot 1 = sum of squares
-            halves(s2, m2, m4);           // chunk 0 slot 2 = m2 (m4 unused)
-            (void)m4;
-            const float mk = k == 0 ? m0 : (k == 1 ? m1 : (k == 2 ? m2 : m3));
-            mine_m = jl == j ? mk : mine_m;
-            mine_ss = jl == j ? ss : mine_ss;
+        for (int q = 0; q < kPreR; ++q) {
+            float s3[3][2];            // [slot][token 2q + t]: chunk 0 value, then chunk 1 value below
+            float c1[3][2];
+#pragma unroll
+            for (int sl = 0; sl < 3; ++sl) {
+                const float v = row_member_sum(X.P[q][0][sl], X.P[q][1][sl]);
+                auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+                // x[0]: rows 0,2 value (chunk 0), x[1]: rows 1,3 value (chunk 1); per 32-lane half
+                float lo0, hi0, lo1, hi1;
+                halves(__uint_as_float(x[0]), lo0, hi0);
+                halves(__uint_as_float(x[1]), lo1, hi1);
+                s3[sl][0] = lo0; s3[sl][1] = hi0;      // chunk 0 of tokens 2q, 2q+1
+                c1[sl][0] = lo1; c1[sl][1] = hi1;      // chunk 1 of tokens 2q, 2q+1
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const float m0 = s3[0][t], m1 = s3[1][t], m2 = s3[2][t];
+                const float m3 = c1[0][t], ss = c1[1][t];
+                const float mk = k == 0 ? m0 : (k == 1 ? m1 : (k == 2 ? m2 : m3));
+                const bool mine = jl == 2 * q + t;
+                mine_m = mine ? mk : mine_m;
+                mine_ss = mine ? ss : mine_ss;
+            }
         }
         pre_mine = pre_gate(mine_m * rms_scale(mine_ss, a.K, a.norm_eps), c.s0, c.bpre, a.eps);
         if (l < 4 * kTokX) L.xpre[xw][jl][k] = pre_mine;
     }
+    // owned token: chunk 4q + row in row `row` of round q
 #pragma unroll
-    for (int i = 0; i < kOwnL; ++i) {
-        const float s0 = gsum32(__uint_as_float(X.O[i][0]));
-        const float s1 = gsum32(__uint_as_float(X.O[i][1]));
-        const float s2 = gsum32(__uint_as_float(X.O[i][2]));
-        const int ch = 2 * i + half;
-        if ((l & 31) == 0 && ch < kChunks) {
-            L.xown[xw][ch][0] = s0;
-            L.xown[xw][ch][1] = s1;
-            L.xown[xw][ch][2] = s2;
+    for (int q = 0; q < kOwnR; ++q) {
+        float v[3];
+#pragma unroll
+        for (int sl = 0; sl < 3; ++sl) v[sl] = row_member_sum(X.O[q][0][sl], X.O[q][1][sl]);
+        const int ch = 4 * q + row;
+        if ((l & 15) == 0 && ch < kChunks) {
+            L.xown[xw][ch][0] = v[0];
+            L.xown[xw][ch][1] = v[1];
+            L.xown[xw][ch][2] = v[2];
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");     // the wave reads back its own LDS writes
@@ -1067,18 +1123,18 @@ __device__ __forceinline__ void x_copy(u32x4 (&rb)[Geo<KS>::kPass][kHC], const R
 
 // Exchange-wave part of tick t; P is the parity of t (selects the residual
 // copy).  Returns true on a timeout.
-template <int KS, bool FUSED, int P>
+template <int KS, bool FUSED, bool LOCAL, int P>
 __device__ __forceinline__ bool x_tick(XState<KS>& X, const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, int t) {
     const int xw = c.w - kMW;
     bool bad = false;
     if (t >= 2 && t - 2 < c.nr) {
-        bad = x_exchange<KS, FUSED>(X, a, c, L, xw, t - 2);
+        bad = x_exchange<KS, FUSED, LOCAL>(X, a, c, L, xw, t - 2);
         if (FUSED && !bad) x_h<KS>(X.rb[P], a, c, L, xw, t - 2);
     }
     if (FUSED) x_copy<KS>(X.rb[P], c, L, xw, t);
     // records of round t-1 (published at the start of this tick) for the
     // next tick's exchange: their latency overlaps the barrier
-    if (t >= 1 && t - 1 < c.nr) x_issue<KS, FUSED>(X, a, c, xw, t - 1);
+    if (t >= 1 && t - 1 < c.nr) x_issue<KS, FUSED, LOCAL>(X, a, c, xw, t - 1);
     return bad;
 }
 
@@ -1086,27 +1142,9 @@ __device__ __forceinline__ bool x_tick(XState<KS>& X, const CoopArgs& a, const R
 // prologue barrier, then one barrier per tick t = 0 .. nr+1 (the exchange of
 // the last round happens in tick nr+1); after each barrier both read the
 // stop flag, so both leave after the same tick.
-template <int KS, bool FUSED>
-__global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
-    __shared__ __attribute__((aligned(16))) Lds<KS> L;
-    RoundCtx c;
-    c.g = blockIdx.x % a.NG;
-    c.q = blockIdx.x / a.NG;
-    c.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    c.l = threadIdx.x & 63;
-    c.row = c.l & 15;
-    c.grp = c.l >> 4;
-    c.tt = 0;
-    c.kg = 0;
-    c.nown = c.q < kT ? (kT - 1 - c.q) / a.G + 1 : 0;
-    c.epoch = a.hdr->epoch;
-    c.rsrc = __builtin_amdgcn_make_buffer_rsrc(a.part, 0, a.part_bytes, kBufDword3);
-    if (c.g >= a.ntiles) return;
-    c.nr = (int)((a.ntiles - c.g + a.NG - 1) / a.NG);
-    c.s0 = FUSED ? a.scale[0] : 0.0f;
-    c.bpre = FUSED ? base_of_lane(a.base) : 0.0f;
+template <int KS, bool FUSED, bool LOCAL>
+__device__ __forceinline__ void spec_body(const CoopArgs& a, const RoundCtx& c, Lds<KS>& L) {
     const int last = c.nr + 1;
-
     if (c.w < kMW) {
         MState<KS> S;
         m_setup<KS>(S, a, c);
@@ -1116,7 +1154,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
         __syncthreads();
         for (int t = 0;; ++t) {
             m_dma<KS>(S, a, c, L, t + 2);
-            m_publish<KS>(a, c, L, t - 1);
+            m_publish<KS, LOCAL>(a, c, L, t - 1);
             m_mfma<KS>(S, c, L, t);
             // round t+1 (issued last tick) must be in LDS before the barrier:
             // younger than its loads are only this tick's loads and the two
@@ -1129,17 +1167,67 @@ __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
         XState<KS> X;
-        if (threadIdx.x == kMW * 64) L.stop = 0;
         __syncthreads();
         for (int t = 0;; t += 2) {
-            if (x_tick<KS, FUSED, 0>(X, a, c, L, t)) L.stop = 1;
+            if (x_tick<KS, FUSED, LOCAL, 0>(X, a, c, L, t)) L.stop = 1;
             __syncthreads();
             if (L.stop || t + 1 > last) break;
-            if (x_tick<KS, FUSED, 1>(X, a, c, L, t + 1)) L.stop = 1;
+            if (x_tick<KS, FUSED, LOCAL, 1>(X, a, c, L, t + 1)) L.stop = 1;
             __syncthreads();
             if (L.stop || t + 2 > last) break;
         }
     }
+}
+
+template <int KS, bool FUSED>
+__global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
+    __shared__ __attribute__((aligned(16))) Lds<KS> L;
+    __shared__ int local_mode;
+    RoundCtx c;
+    c.g = blockIdx.x % a.NG;
+    c.q = blockIdx.x / a.NG;
+    c.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    c.l = threadIdx.x & 63;
+    c.row = c.l & 15;
+    c.grp = c.l >> 4;
+    c.tt = 0;
+    c.kg = 0;
+    c.nown = c.q < kT ? (kT - 1 - c.q) / a.G + 1 : 0;
+    c.epoch = a.hdr->epoch;
+    c.rsrc = __builtin_amdgcn_make_buffer_rsrc(a.part, 0, a.part_bytes, kBufDword3);
+    c.nr = (int)((a.ntiles - c.g + a.NG - 1) / a.NG);
+    c.s0 = FUSED ? a.scale[0] : 0.0f;
+    c.bpre = FUSED ? base_of_lane(a.base) : 0.0f;
+
+    // Placement: with NG a multiple of 8, the members of group g are the
+    // workgroups b = g (mod 8); if every workgroup runs on XCD b % 8 (read
+    // from the XCC id register), each group sits on one XCD and its records
+    // can stay in that XCD's L2.  All workgroups agree through one grid-wide
+    // count before the first record is written.
+    if (threadIdx.x == 0) {
+        const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11)) & 0xFu;
+        if (xcc != (blockIdx.x & 7u)) __hip_atomic_fetch_add(&a.hdr->xbad, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(&a.hdr->arrive, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        bool ok = true;
+        while (__hip_atomic_load(&a.hdr->arrive, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x) {
+            if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull) {
+                __hip_atomic_store(&a.hdr->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        const bool local =
+            a.NG % 8 == 0 && __hip_atomic_load(&a.hdr->xbad, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u;
+        local_mode = ok ? (local ? 1 : 0) : -1;
+        L.stop = 0;
+    }
+    __syncthreads();
+    const int mode = local_mode;
+    if (mode < 0 || c.g >= a.ntiles) return;
+    if (mode) spec_body<KS, FUSED, true>(a, c, L);
+    else spec_body<KS, FUSED, false>(a, c, L);
 }
 
 }  // namespace spec
@@ -1170,6 +1258,8 @@ __global__ __launch_bounds__(1024) void k_init(WsHeader* hdr, u32x4* part, int64
         hdr->epoch = next;
         hdr->err = 0u;
         hdr->clean = nchunks;
+        hdr->xbad = 0u;
+        hdr->arrive = 0u;
     }
 }
 

@@ -36,17 +36,14 @@ __device__ __forceinline__ uint32_t bf16_rn(float f) {
 // bf16; that double rounding can only go wrong when the float lands exactly
 // on a bf16 halfway point while y itself does not, in which case the float
 // is nudged one float ulp towards y before the second rounding.
+// Branch-free (selects only), so a wave computes it in a few instructions.
 __device__ __forceinline__ uint32_t bf16_rn_f64(double y) {
-    float f = (float)y;
-    uint32_t u = __float_as_uint(f);
-    if (__builtin_expect((u & 0xFFFFu) == 0x8000u, 0)) {
-        double back = (double)f;
-        if (back != y) {
-            u = (__builtin_fabs(y) > __builtin_fabs(back)) ? u + 1u : u - 1u;
-            f = __uint_as_float(u);
-        }
-    }
-    return bf16_rn(f);
+    const float f = (float)y;
+    const double back = (double)f;
+    const uint32_t u = __float_as_uint(f);
+    const bool nudge = ((u & 0xFFFFu) == 0x8000u) & (back != y);
+    const uint32_t toward = (__builtin_fabs(y) > __builtin_fabs(back)) ? 1u : 0xFFFFFFFFu;
+    return bf16_rn(__uint_as_float(u + (nudge ? toward : 0u)));
 }
 
 // Pack two bf16 bit patterns into one word (element 0 low).
