@@ -647,11 +647,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_coop(CoopArgs a) {
 //
 //  * MFMA waves (0..3): wave w handles stream w of the member slice and
 //    keeps that stream's weight slice in registers (MFMA B layout), so the
-//    weights never go through LDS.  In tick t a wave issues the residual
-//    of round t+2 as direct global->LDS loads into slot (t+2) % 3, writes
-//    the records of round t-1 from the per-wave partials of the previous
-//    tick, multiplies round t out of slot t % 3 into per-wave partials, and
-//    waits until round t+1 has landed in LDS.
+//    weights never go through LDS.  In tick t a wave writes the records of
+//    round t-1 from the per-wave partials of the previous tick, issues the
+//    residual of round t+2 as direct global->LDS loads into slot (t+2) % 3,
+//    multiplies round t out of slot t % 3 into per-wave partials, and waits
+//    until round t+1 has landed in LDS.
 //  * Exchange waves (4..7): wave x handles tokens 8x..8x+7 of a round.  In
 //    tick t it reads the records of round t-2, forms pre for its tokens
 //    (and the mixes of the token it owns), writes h of round t-2 from the
@@ -1085,18 +1085,27 @@ __device__ __forceinline__ void x_h(const u32x4 (&rb)[Geo<KS>::kPass][kHC], cons
         const int tk = it / Geo<KS>::kBlk, b = it - tk * Geo<KS>::kBlk;
         const f32x4 pq = *reinterpret_cast<const f32x4*>(&L.xpre[xw][tk][0]);
         const double p0 = pq[0], p1 = pq[1], p2 = pq[2], p3 = pq[3];
+        auto sum = [&](int w, int e) {
+            auto v = [&](uint32_t word) { return (double)(e ? bf_hi(word) : bf_lo(word)); };
+            double y = p0 * v(rb[p][0][w]);
+            y = __builtin_fma(p1, v(rb[p][1][w]), y);
+            y = __builtin_fma(p2, v(rb[p][2][w]), y);
+            return __builtin_fma(p3, v(rb[p][3][w]), y);
+        };
         u32x4 out;
+        float f[4][2];
+        bool mid = false;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            double lo = p0 * (double)bf_lo(rb[p][0][e]);
-            lo = __builtin_fma(p1, (double)bf_lo(rb[p][1][e]), lo);
-            lo = __builtin_fma(p2, (double)bf_lo(rb[p][2][e]), lo);
-            lo = __builtin_fma(p3, (double)bf_lo(rb[p][3][e]), lo);
-            double hi = p0 * (double)bf_hi(rb[p][0][e]);
-            hi = __builtin_fma(p1, (double)bf_hi(rb[p][1][e]), hi);
-            hi = __builtin_fma(p2, (double)bf_hi(rb[p][2][e]), hi);
-            hi = __builtin_fma(p3, (double)bf_hi(rb[p][3][e]), hi);
-            out[e] = pack2(bf16_rn_f64(lo), bf16_rn_f64(hi));
+        for (int w = 0; w < 4; ++w) {
+            f[w][0] = f32_mid(sum(w, 0), mid);
+            f[w][1] = f32_mid(sum(w, 1), mid);
+        }
+        if (__builtin_amdgcn_ballot_w64(mid)) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) out[w] = pack2(bf16_rn_f64(sum(w, 0)), bf16_rn_f64(sum(w, 1)));
+        } else {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) out[w] = pack2(bf16_rn(f[w][0]), bf16_rn(f[w][1]));
         }
         const int off = valid ? ((kTokX * xw + tk) * a.d + c.q * (32 * KS) + 8 * b) * 2 : kOOB;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((__vector_size__(16))) int, out),
@@ -1153,12 +1162,15 @@ __device__ __forceinline__ void spec_body(const CoopArgs& a, const RoundCtx& c, 
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW) : "memory");   // round 0 landed
         __syncthreads();
         for (int t = 0;; ++t) {
-            m_dma<KS>(S, a, c, L, t + 2);
+            // records first (peers are waiting for them), then the residual
+            // of round t+2, then the products of round t
             m_publish<KS, LOCAL>(a, c, L, t - 1);
+            m_dma<KS>(S, a, c, L, t + 2);
             m_mfma<KS>(S, c, L, t);
-            // round t+1 (issued last tick) must be in LDS before the barrier:
-            // younger than its loads are only this tick's loads and the two
-            // record stores of this tick
+            // round t+1 (issued last tick, its loads the youngest memory
+            // instructions of that tick) must be in LDS before the barrier:
+            // younger than them are only this tick's two record stores and
+            // its loads
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW + 2) : "memory");
             __syncthreads();
             if (L.stop || t + 1 > last) break;

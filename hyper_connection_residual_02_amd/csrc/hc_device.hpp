@@ -46,6 +46,17 @@ __device__ __forceinline__ uint32_t bf16_rn_f64(double y) {
     return bf16_rn(__uint_as_float(u + (nudge ? toward : 0u)));
 }
 
+// Fast path of bf16_rn_f64: the float rounding of y gives the correctly
+// rounded bf16 unless that float lands exactly on a bf16 halfway point.
+// Returns the float and raises `mid` when it does; a wave in which any lane
+// raised it redoes its item with bf16_rn_f64 (a few percent of items), so
+// results are those of bf16_rn_f64 bit for bit.
+__device__ __forceinline__ float f32_mid(double y, bool& mid) {
+    const float f = (float)y;
+    mid |= (__float_as_uint(f) & 0xFFFFu) == 0x8000u;
+    return f;
+}
+
 // Pack two bf16 bit patterns into one word (element 0 low).
 __device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
 

@@ -10,7 +10,8 @@
 // Numerics: each output is the correctly rounded bf16 of its defining sum.
 // A product of an fp32 coefficient and a bf16 value has at most 32
 // significant bits, so it is exact in double; the sum of the (at most 5)
-// products is accumulated in double and rounded once (bf16_rn_f64).
+// products is accumulated in double and rounded once (bf16_rn_f64, with its
+// float fast path taken per wave).
 
 #include "hc_device.hpp"
 #include "hc_launch.hpp"
@@ -54,18 +55,28 @@ __global__ __launch_bounds__(256) void k_pre(const u32x4* __restrict__ R, const 
         const u32x4 r1 = __builtin_nontemporal_load(R + row + map.d8);
         const u32x4 r2 = __builtin_nontemporal_load(R + row + 2 * (uint64_t)map.d8);
         const u32x4 r3 = __builtin_nontemporal_load(R + row + 3 * (uint64_t)map.d8);
+        // element e of word w (e = 0: low half): sum over the 4 streams
+        auto sum = [&](int w, int e) {
+            auto v = [&](uint32_t word) { return (double)(e ? bf_hi(word) : bf_lo(word)); };
+            double y = p0 * v(r0[w]);
+            y = __builtin_fma(p1, v(r1[w]), y);
+            y = __builtin_fma(p2, v(r2[w]), y);
+            return __builtin_fma(p3, v(r3[w]), y);
+        };
         u32x4 out;
+        float f[4][2];
+        bool mid = false;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            double lo = p0 * (double)bf_lo(r0[w]);
-            lo = __builtin_fma(p1, (double)bf_lo(r1[w]), lo);
-            lo = __builtin_fma(p2, (double)bf_lo(r2[w]), lo);
-            lo = __builtin_fma(p3, (double)bf_lo(r3[w]), lo);
-            double hi = p0 * (double)bf_hi(r0[w]);
-            hi = __builtin_fma(p1, (double)bf_hi(r1[w]), hi);
-            hi = __builtin_fma(p2, (double)bf_hi(r2[w]), hi);
-            hi = __builtin_fma(p3, (double)bf_hi(r3[w]), hi);
-            out[w] = pack2(bf16_rn_f64(lo), bf16_rn_f64(hi));
+            f[w][0] = f32_mid(sum(w, 0), mid);
+            f[w][1] = f32_mid(sum(w, 1), mid);
+        }
+        if (__builtin_amdgcn_ballot_w64(mid)) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) out[w] = pack2(bf16_rn_f64(sum(w, 0)), bf16_rn_f64(sum(w, 1)));
+        } else {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) out[w] = pack2(bf16_rn(f[w][0]), bf16_rn(f[w][1]));
         }
         __builtin_nontemporal_store(out, h + t * map.d8 + c8);
     }
@@ -79,44 +90,68 @@ __global__ __launch_bounds__(256) void k_post(const u32x4* __restrict__ x, const
                                               const float* __restrict__ post, const float* __restrict__ comb,
                                               u32x4* Rout, ItemMap map) {
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-    for (uint64_t it = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; it < map.items; it += stride) {
+    uint64_t it = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (it >= map.items) return;
+    struct Item {
         uint64_t t;
         uint32_t c8;
-        item_of(it, map.d8, t, c8);
-        if (UNIFORM) t = __builtin_amdgcn_readfirstlane((uint32_t)t) | ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(t >> 32)) << 32);
+        u32x4 xv, r[kHC];
+    };
+    // the next item's loads are in flight while this item is computed; past
+    // the end the last item is loaded again (no branch around the loads, so
+    // the wait for the current item counts only its own loads)
+    auto fetch = [&](uint64_t i, Item& I) {
+        item_of(i < map.items ? i : map.items - 1, map.d8, I.t, I.c8);
+        if (UNIFORM)
+            I.t = __builtin_amdgcn_readfirstlane((uint32_t)I.t) |
+                  ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(I.t >> 32)) << 32);
+        const uint64_t row = I.t * kHC * (uint64_t)map.d8 + I.c8;
+        I.xv = __builtin_nontemporal_load(x + I.t * map.d8 + I.c8);
+#pragma unroll
+        for (int j = 0; j < kHC; ++j) I.r[j] = __builtin_nontemporal_load(R + row + j * (uint64_t)map.d8);
+    };
+    Item cur, nxt;
+    fetch(it, cur);
+    for (; it < map.items; it += stride) {
+        fetch(it + stride, nxt);
+        const uint64_t t = cur.t;
         const f32x4 q = *reinterpret_cast<const f32x4*>(post + t * kHC);
         f32x4 cb[kHC];
 #pragma unroll
         for (int j = 0; j < kHC; ++j) cb[j] = *reinterpret_cast<const f32x4*>(comb + (t * kHC + j) * kHC);
-        const uint64_t row = t * kHC * (uint64_t)map.d8 + c8;
-        const u32x4 xv = __builtin_nontemporal_load(x + t * map.d8 + c8);
-        u32x4 r[kHC];
+        const uint64_t row = t * kHC * (uint64_t)map.d8 + cur.c8;
+        // output stream k, element e of word w: post_k x + sum_j comb[j][k] R_j
+        auto sum = [&](int k, int w, int e) {
+            auto v = [&](uint32_t word) { return (double)(e ? bf_hi(word) : bf_lo(word)); };
+            double y = (double)q[k] * v(cur.xv[w]);
 #pragma unroll
-        for (int j = 0; j < kHC; ++j) r[j] = __builtin_nontemporal_load(R + row + j * (uint64_t)map.d8);
+            for (int j = 0; j < kHC; ++j) y = __builtin_fma((double)cb[j][k], v(cur.r[j][w]), y);
+            return y;
+        };
         u32x4 out[kHC];
+        float f[kHC][4][2];
+        bool mid = false;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const double xl = bf_lo(xv[w]), xh = bf_hi(xv[w]);
-            double rl[kHC], rh[kHC];
+        for (int k = 0; k < kHC; ++k)
 #pragma unroll
-            for (int j = 0; j < kHC; ++j) {
-                rl[j] = bf_lo(r[j][w]);
-                rh[j] = bf_hi(r[j][w]);
+            for (int w = 0; w < 4; ++w) {
+                f[k][w][0] = f32_mid(sum(k, w, 0), mid);
+                f[k][w][1] = f32_mid(sum(k, w, 1), mid);
             }
+        if (__builtin_amdgcn_ballot_w64(mid)) {
 #pragma unroll
-            for (int k = 0; k < kHC; ++k) {
-                double yl = (double)q[k] * xl;
-                double yh = (double)q[k] * xh;
+            for (int k = 0; k < kHC; ++k)
 #pragma unroll
-                for (int j = 0; j < kHC; ++j) {
-                    yl = __builtin_fma((double)cb[j][k], rl[j], yl);
-                    yh = __builtin_fma((double)cb[j][k], rh[j], yh);
-                }
-                out[k][w] = pack2(bf16_rn_f64(yl), bf16_rn_f64(yh));
-            }
+                for (int w = 0; w < 4; ++w) out[k][w] = pack2(bf16_rn_f64(sum(k, w, 0)), bf16_rn_f64(sum(k, w, 1)));
+        } else {
+#pragma unroll
+            for (int k = 0; k < kHC; ++k)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) out[k][w] = pack2(bf16_rn(f[k][w][0]), bf16_rn(f[k][w][1]));
         }
 #pragma unroll
         for (int k = 0; k < kHC; ++k) __builtin_nontemporal_store(out[k], Rout + row + k * (uint64_t)map.d8);
+        cur = nxt;
     }
 }
 
