@@ -852,6 +852,9 @@ __device__ __forceinline__ void m_publish(const CoopArgs& a, const RoundCtx& c, 
 }
 
 // Partial mixes and sum of squares of stream w for round r (slot r % 3).
+// The sum of squares comes from the matrix core too: an MFMA with the A
+// operand also as B gives A A^T, whose diagonal holds each token row's sum
+// of squares over the k-step (products of bf16 values are exact in fp32).
 template <int KS>
 __device__ __forceinline__ void m_mfma(const MState<KS>& S, const RoundCtx& c, Lds<KS>& L, int r) {
     const uint8_t* slot = &L.slot[r % kNSlot][0];
@@ -861,7 +864,7 @@ __device__ __forceinline__ void m_mfma(const MState<KS>& S, const RoundCtx& c, L
         f32x4 acc[kTiles];
 #pragma unroll
         for (int ct = 0; ct < kTiles; ++ct) acc[ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        float sq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 sq = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int st = 0; st < KS; ++st) {
             const u32x4 av = *reinterpret_cast<const u32x4*>(
@@ -870,20 +873,10 @@ __device__ __forceinline__ void m_mfma(const MState<KS>& S, const RoundCtx& c, L
 #pragma unroll
             for (int ct = 0; ct < kTiles; ++ct)
                 acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, S.w[st][ct], acc[ct], 0, 0, 0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float lo = bf_lo(av[e]), hi = bf_hi(av[e]);
-                sq[e] = __builtin_fmaf(hi, hi, __builtin_fmaf(lo, lo, sq[e]));
-            }
+            sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, ab, sq, 0, 0, 0);
         }
-        float ss = (sq[0] + sq[1]) + (sq[2] + sq[3]);
-        {
-            auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
-            ss = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-            auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
-            ss = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-        }
-        if (c.grp == 0) L.red[b][c.w][16 * tt + c.row][24] = ss;
+        // diagonal element (i, i) sits in lane i + 16 * (i / 4), component i % 4
+        if ((c.row >> 2) == c.grp) L.red[b][c.w][16 * tt + c.row][24] = sq[c.row & 3];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const int t = 16 * tt + 4 * c.grp + rr;
@@ -1109,7 +1102,7 @@ __device__ __forceinline__ void x_h(const u32x4 (&rb)[Geo<KS>::kPass][kHC], cons
         }
         const int off = valid ? ((kTokX * xw + tk) * a.d + c.q * (32 * KS) + 8 * b) * 2 : kOOB;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((__vector_size__(16))) int, out),
-                                               rs, off, 0, 2);
+                                               rs, off, 0, 0);
     }
 }
 
