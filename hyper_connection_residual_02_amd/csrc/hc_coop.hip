@@ -18,16 +18,18 @@
 //    runs of the member's slice) and transposed through LDS into the MFMA
 //    operand layout.  Each of the 8 waves then takes one 16-token tile and
 //    one of 4 k-groups of the slice and runs v_mfma_f32_16x16x32_bf16 from
-//    registers, and forms the sum of squares.
-//  * The member's 25 partial sums per token are published to the workspace
+//    registers, and forms the sums of squares (plain, and of the values
+//    scaled by 2^-72 for streams whose plain sum overflows fp32) on the
+//    matrix core as the diagonal of A A^T.
+//  * The member's 26 partial sums per token are published to the workspace
 //    as tagged 16-byte records (3 floats + a round tag), stored member-
 //    fastest so that the G records of a (token, chunk) are contiguous.
-//    Every member reads the pre-relevant records (m_0..m_3 and the sum of
+//    Every member reads the pre-relevant records (m_0..m_3 and the sums of
 //    squares) of all members with contiguous loads, adds them across lanes
 //    in one fixed butterfly order, forms pre for all T tokens, and writes h
 //    for its slice from the residual still in registers (staged through
 //    LDS for coalesced stores): one HBM pass over the residual.  The owner
-//    of each token (member t mod G) adds all 25 fields the same way and
+//    of each token (member t mod G) adds all 26 fields the same way and
 //    writes the mixes (and pre); the split + Sinkhorn of post and comb then
 //    runs over those mixes in the split kernel, which shares its per-token
 //    code with hc_split_sinkhorn.
@@ -56,9 +58,9 @@ constexpr int kTT = 2;             // 16-token tiles per round
 constexpr int kKG = 4;             // k-groups of a member's slice
 constexpr int kT = 16 * kTT;       // tokens per round
 constexpr int kTiles = 5;          // 5 x 16 = 80 MFMA columns (72 used)
-constexpr int kChunks = 9;         // 16-byte chunks per partial record (25 fields + tag words)
+constexpr int kChunks = 9;         // 16-byte chunks per partial record (26 fields + tag words)
 constexpr int kSlots = 4;          // rounds of records kept per group
-constexpr int kRed = 25;           // floats per token in the per-k-group LDS partials
+constexpr int kRed = 26;           // floats per token in the per-k-group LDS partials
 constexpr int kPrePairs = 2 * kT;  // (chunk, token) pairs holding the pre-relevant fields
 constexpr int kOwnPairs = kChunks * kT;   // (owned token, chunk) pairs at most (G = 1)
 constexpr uint64_t kMagic = 0x6863776b73703031ull;   // marks an initialised workspace
@@ -105,20 +107,19 @@ struct CoopArgs {
 };
 
 // Field f of a partial record (0..23 = the 24 dot products, 24 = sum of
-// squares) by chunk and slot.  The pre-relevant fields (0..3 and 24) are
-// in chunks 0 and 1.
+// squares, 25 = sum of squares of the values times 2^-72) by chunk and
+// slot.  The pre-relevant fields (0..3, 24 and 25) are in chunks 0 and 1.
 __device__ __forceinline__ int field_at(int chunk, int slot) {
     if (chunk == 0) return slot;                                    // m0 m1 m2
-    if (chunk == 1) return slot == 0 ? 3 : (slot == 1 ? 24 : 4);    // m3 ss m4
-    const int f = 5 + 3 * (chunk - 2) + slot;                       // m5 .. m23
+    if (chunk == 1) return slot == 0 ? 3 : 23 + slot;               // m3 ss sb
+    const int f = 4 + 3 * (chunk - 2) + slot;                       // m4 .. m23
     return f <= 23 ? f : -1;
 }
 __device__ __forceinline__ void field_pos(int f, int& chunk, int& slot) {
     if (f < 3) { chunk = 0; slot = f; }
     else if (f == 3) { chunk = 1; slot = 0; }
-    else if (f == 24) { chunk = 1; slot = 1; }
-    else if (f == 4) { chunk = 1; slot = 2; }
-    else { chunk = 2 + (f - 5) / 3; slot = (f - 5) % 3; }
+    else if (f >= 24) { chunk = 1; slot = f - 23; }
+    else { chunk = 2 + (f - 4) / 3; slot = (f - 4) % 3; }
 }
 
 // Staging geometry of one 16-token tile of a member slice: per token,
@@ -258,6 +259,35 @@ __device__ __forceinline__ float group_sum(float v, int gp) {
     return v;
 }
 
+// Sums of squares of a 16-token MFMA tile.  With the A operand also as B
+// an MFMA gives A A^T, whose diagonal holds each token row's sum of squares
+// (products of bf16 values are exact in fp32); diagonal element (i, i) sits
+// in lane i + 16 * (i / 4), component i % 4.
+__device__ __forceinline__ void sq_step(const u32x4& av, f32x4& sq) {
+    const bf16x8 ab = __builtin_bit_cast(bf16x8, av);
+    sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, ab, sq, 0, 0, 0);
+}
+__device__ __forceinline__ void sq_step_scaled(const u32x4& av, f32x4& sb) {
+    u32x4 sv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sv[e] = scaled_x2(av[e]);
+    const bf16x8 ab = __builtin_bit_cast(bf16x8, sv);
+    sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, ab, sb, 0, 0, 0);
+}
+// The scaled sum of the tile (values times 2^-72) from its plain sum ss:
+// while ss is finite, ss * 2^-144 (whatever underflows is below 2^-126, far
+// under one ulp of a total that has overflowed unscaled, the only case in
+// which the scaled sum is used); where any token row of the wave overflowed,
+// `redo` recomputes the scaled sums from the operands (a wave-uniform,
+// rare branch).  Valid on the diagonal lanes.
+template <typename Redo>
+__device__ __forceinline__ float scaled_sum(int row, int grp, float ss, Redo&& redo) {
+    const bool diag = (row >> 2) == grp;
+    float sb = (ss * 0x1p-72f) * 0x1p-72f;
+    if (__builtin_amdgcn_ballot_w64(diag && !(ss <= 3.40282347e38f))) sb = redo()[row & 3];
+    return sb;
+}
+
 // ---------------------------------------------------- stage A: publish r
 // f holds round r in MFMA operand layout.
 template <int KS>
@@ -266,7 +296,7 @@ __device__ __forceinline__ void publish(const Frags<KS>& f, const CoopArgs& a, c
     f32x4 acc[kTiles];
 #pragma unroll
     for (int ct = 0; ct < kTiles; ++ct) acc[ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float sq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 sq = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     // weight operands double-buffered from LDS: the reads for k-step s+1
     // are in flight while the MFMAs of step s run
     bf16x8 bw[2][kTiles];
@@ -282,21 +312,21 @@ __device__ __forceinline__ void publish(const Frags<KS>& f, const CoopArgs& a, c
 #pragma unroll
         for (int ct = 0; ct < kTiles; ++ct)
             acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw[s & 1][ct], acc[ct], 0, 0, 0);
+        sq_step(f.r[s], sq);
+    }
+    {
+        const float ss = sq[c.row & 3];
+        const float sb = scaled_sum(c.row, c.grp, ss, [&] {
+            f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float lo = bf_lo(f.r[s][e]), hi = bf_hi(f.r[s][e]);
-            sq[e] = __builtin_fmaf(hi, hi, __builtin_fmaf(lo, lo, sq[e]));
+            for (int s = 0; s < KS; ++s) sq_step_scaled(f.r[s], v);
+            return v;
+        });
+        if ((c.row >> 2) == c.grp) {
+            L.u.red[c.kg][16 * c.tt + c.row][24] = ss;
+            L.u.red[c.kg][16 * c.tt + c.row][25] = sb;
         }
     }
-    float ss = (sq[0] + sq[1]) + (sq[2] + sq[3]);
-    // sum of squares over the 4 lane groups (rows of 16 lanes)
-    {
-        auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
-        ss = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-        auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
-        ss = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-    }
-    if (c.grp == 0) L.u.red[c.kg][16 * c.tt + c.row][24] = ss;
     // combine the three weight pieces (lo + mid first, then hi)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -479,8 +509,9 @@ __device__ __forceinline__ void finals(const CoopArgs& a, const RoundCtx& c, Lds
         // compute a copy of it and their store is dropped
         const int t = (tid >> 2) & (kT - 1), j = tid & 3;
         const float sj = j < 3 ? L.xsum[t][j] : L.xsum[kT + t][0];     // m_0..m_2: chunk 0; m_3: chunk 1 slot 0
-        const float sq = L.xsum[kT + t][1];                           // sum of squares: chunk 1 slot 1
-        const float p = pre_gate(sj * rms_scale(sq, a.K, a.norm_eps), c.s0, c.bpre, a.eps);
+        // sums of squares: chunk 1 slots 1 and 2
+        const MixScale ms = mix_scale(L.xsum[kT + t][1], L.xsum[kT + t][2], a.K, a.norm_eps);
+        const float p = pre_gate(mix_value(sj, ms), c.s0, c.bpre, a.eps);
         if (tid < kT * 4) L.preL[t][j] = p;
         // the owner writes pre (a null pre gives an empty resource)
         const __amdgpu_buffer_rsrc_t rp = tile_rsrc(a.pre, kHC * 4, tok0, a.n, kT);
@@ -500,8 +531,8 @@ __device__ __forceinline__ void finals(const CoopArgs& a, const RoundCtx& c, Lds
         const int o = xx / kMix, j = xx - o * kMix;
         int ch, sl;
         field_pos(j, ch, sl);
-        const float rs = rms_scale(L.xown[o * kChunks + 1][1], a.K, a.norm_eps);
-        const float v = L.xown[o * kChunks + ch][sl] * rs;
+        const MixScale ms = mix_scale(L.xown[o * kChunks + 1][1], L.xown[o * kChunks + 1][2], a.K, a.norm_eps);
+        const float v = mix_value(L.xown[o * kChunks + ch][sl], ms);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rm, ok ? ((c.q + a.G * o) * kMix + j) * 4 : kOOB,
                                               0, 0);
     }
@@ -851,10 +882,7 @@ __device__ __forceinline__ void m_publish(const CoopArgs& a, const RoundCtx& c, 
     }
 }
 
-// Partial mixes and sum of squares of stream w for round r (slot r % 3).
-// The sum of squares comes from the matrix core too: an MFMA with the A
-// operand also as B gives A A^T, whose diagonal holds each token row's sum
-// of squares over the k-step (products of bf16 values are exact in fp32).
+// Partial mixes and sums of squares of stream w for round r (slot r % 3).
 template <int KS>
 __device__ __forceinline__ void m_mfma(const MState<KS>& S, const RoundCtx& c, Lds<KS>& L, int r) {
     const uint8_t* slot = &L.slot[r % kNSlot][0];
@@ -865,18 +893,32 @@ __device__ __forceinline__ void m_mfma(const MState<KS>& S, const RoundCtx& c, L
 #pragma unroll
         for (int ct = 0; ct < kTiles; ++ct) acc[ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         f32x4 sq = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        auto operand = [&](int st) {
+            return *reinterpret_cast<const u32x4*>(slot + (16 * tt + c.row) * Geo<KS>::kRowB + c.w * (64 * KS) +
+                                                  64 * st + 16 * c.grp);
+        };
 #pragma unroll
         for (int st = 0; st < KS; ++st) {
-            const u32x4 av = *reinterpret_cast<const u32x4*>(
-                slot + (16 * tt + c.row) * Geo<KS>::kRowB + c.w * (64 * KS) + 64 * st + 16 * c.grp);
+            const u32x4 av = operand(st);
             const bf16x8 ab = __builtin_bit_cast(bf16x8, av);
 #pragma unroll
             for (int ct = 0; ct < kTiles; ++ct)
                 acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, S.w[st][ct], acc[ct], 0, 0, 0);
-            sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, ab, sq, 0, 0, 0);
+            sq_step(av, sq);
         }
-        // diagonal element (i, i) sits in lane i + 16 * (i / 4), component i % 4
-        if ((c.row >> 2) == c.grp) L.red[b][c.w][16 * tt + c.row][24] = sq[c.row & 3];
+        {
+            const float ss = sq[c.row & 3];
+            const float sb = scaled_sum(c.row, c.grp, ss, [&] {
+                f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int st = 0; st < KS; ++st) sq_step_scaled(operand(st), v);
+                return v;
+            });
+            if ((c.row >> 2) == c.grp) {
+                L.red[b][c.w][16 * tt + c.row][24] = ss;
+                L.red[b][c.w][16 * tt + c.row][25] = sb;
+            }
+        }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const int t = 16 * tt + 4 * c.grp + rr;
@@ -1001,7 +1043,7 @@ __device__ __forceinline__ bool x_exchange(XState<KS>& X, const CoopArgs& a, con
         // 2q+1; a permlane16 swap pairs the chunks, a permlane32 swap the
         // tokens, so every lane sees both tokens' m0..m3 and sum of squares
         const int k = l & 3, jl = (l >> 2) & (kTokX - 1);
-        float mine_m = 0.0f, mine_ss = 1.0f;
+        float mine_m = 0.0f, mine_ss = 1.0f, mine_sb = 1.0f;
 #pragma unroll
         for (int q = 0; q < kPreR; ++q) {
             float s3[3][2];            // [slot][token 2q + t]: chunk 0 value, then chunk 1 value below
@@ -1020,14 +1062,15 @@ __device__ __forceinline__ bool x_exchange(XState<KS>& X, const CoopArgs& a, con
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const float m0 = s3[0][t], m1 = s3[1][t], m2 = s3[2][t];
-                const float m3 = c1[0][t], ss = c1[1][t];
+                const float m3 = c1[0][t], ss = c1[1][t], sb = c1[2][t];
                 const float mk = k == 0 ? m0 : (k == 1 ? m1 : (k == 2 ? m2 : m3));
                 const bool mine = jl == 2 * q + t;
                 mine_m = mine ? mk : mine_m;
                 mine_ss = mine ? ss : mine_ss;
+                mine_sb = mine ? sb : mine_sb;
             }
         }
-        pre_mine = pre_gate(mine_m * rms_scale(mine_ss, a.K, a.norm_eps), c.s0, c.bpre, a.eps);
+        pre_mine = pre_gate(mix_value(mine_m, mix_scale(mine_ss, mine_sb, a.K, a.norm_eps)), c.s0, c.bpre, a.eps);
         if (l < 4 * kTokX) L.xpre[xw][jl][k] = pre_mine;
     }
     // owned token: chunk 4q + row in row `row` of round q
@@ -1049,7 +1092,7 @@ __device__ __forceinline__ bool x_exchange(XState<KS>& X, const CoopArgs& a, con
         const int f = l < kMix ? l : 0;
         int ch, sl;
         field_pos(f, ch, sl);
-        const float v = L.xown[xw][ch][sl] * rms_scale(L.xown[xw][1][1], a.K, a.norm_eps);
+        const float v = mix_value(L.xown[xw][ch][sl], mix_scale(L.xown[xw][1][1], L.xown[xw][1][2], a.K, a.norm_eps));
         const __amdgpu_buffer_rsrc_t rm = tile_rsrc(a.mixes, kMix * 4, tok0, a.n, kT);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rm,
                                               xw < c.nown && l < kMix ? (otk * kMix + l) * 4 : kOOB, 0, 0);

@@ -104,6 +104,36 @@ __device__ __forceinline__ float rms_scale(float sum_sq, float K, float norm_eps
     return __builtin_amdgcn_rsqf(sum_sq * __builtin_amdgcn_rcpf(K) + norm_eps);
 }
 
+// Overflow-safe normaliser.  A bf16 stream can hold values up to 2^128,
+// whose squares overflow fp32 long before the stream itself overflows, so
+// every kernel also forms sb, the sum of squares of the values scaled by
+// 2^-72 (scaled_x2 below).  While the plain sum ss is finite the mix is
+// dot * rms_scale(ss) exactly as before; once ss has overflowed,
+// 1/sqrt(ss/K) = 2^-72/sqrt(sb/K) (norm_eps is then far below one ulp), and
+// the 2^-72 is applied to the dot product first so that no intermediate
+// leaves the normal range.  A mix is mix_value(dot, mix_scale(ss, sb, ...)).
+struct MixScale {
+    float mul, rs;
+};
+__device__ __forceinline__ MixScale mix_scale(float ss, float sb, float K, float norm_eps) {
+    const bool big = !(ss <= 3.40282347e38f);          // overflowed (or not a number)
+    MixScale m;
+    m.mul = big ? 0x1p-72f : 1.0f;
+    m.rs = big ? __builtin_amdgcn_rsqf(sb * __builtin_amdgcn_rcpf(K)) : rms_scale(ss, K, norm_eps);
+    return m;
+}
+__device__ __forceinline__ float mix_value(float dot, MixScale s) { return (dot * s.mul) * s.rs; }
+
+// Two packed bf16 values times 2^-72, for the scaled sum of squares: the
+// magnitude bits minus 72 << 7 in each half, saturating at zero, so a value
+// below 2^-55 becomes zero or subnormal (its square is then far below one
+// ulp of a sum that has overflowed fp32 unscaled).  The sign is dropped.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t scaled_x2(uint32_t w) {
+    const u16x2 m = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(m, (u16x2){0x2400, 0x2400}));
+}
+
 // ------------------------------------------------- split + epsilon-Sinkhorn
 // One token per 16-lane row; lane e = (lane & 15) holds comb entry
 // (j, k) = (e / 4, e % 4).  m points at the token's 24 mixes (any memory

@@ -61,7 +61,7 @@ def compare_fused(orc, R, W, s, b, outs, idx=None, iters=20, eps=1e-6, neps=1e-2
     check_abs(g["pre"], op, label + " pre")
     check_abs(g["post"], oq, label + " post")
     check_abs(g["comb"], oc, label + " comb")
-    check_bf16_tol(gh, oh, pre_terms(Rb, op), label + " h end-to-end")
+    check_bf16_tol(gh, oh, lambda: pre_terms(Rb, op), label + " h end-to-end")
     # isolated: oracle split on the GPU's own mixes; oracle hc_pre on its pre
     ip, iq, ic = orc.split_sinkhorn(g["mixes"].astype(np.float64), sn, bn, hc, iters, eps)
     check_abs(g["pre"], ip, label + " pre (isolated)")
@@ -75,7 +75,7 @@ def compare_fused(orc, R, W, s, b, outs, idx=None, iters=20, eps=1e-6, neps=1e-2
         go = hin.bits(Rout.reshape(n, hc, d)[sel])
         check_bf16_exact(go, orc.post(xb, Rb, g["post"].astype(np.float64), g["comb"].astype(np.float64)),
                          label + " R' (isolated)")
-        check_bf16_tol(go, orc.post(xb, Rb, oq, oc), post_terms(xb, Rb, oq, oc), label + " R' end-to-end")
+        check_bf16_tol(go, orc.post(xb, Rb, oq, oc), lambda: post_terms(xb, Rb, oq, oc), label + " R' end-to-end")
     return om
 
 
@@ -252,7 +252,35 @@ def test_zero_and_scaled_tokens(orc):
     assert bool(torch.isfinite(mixes).all())
     check_mixes(_np(mixes[5, 0]), _np(mixes[4, 0]).astype(np.float64), tol=1e-6)
     check_mixes(_np(mixes[6, 0]), _np(mixes[4, 0]).astype(np.float64), tol=1e-6)
+    # moderate power-of-two scales leave the mixes unchanged bit for bit, so
+    # h and R' scale exactly
+    assert torch.equal(mixes[5], mixes[4])
+    assert torch.equal(h[5].float(), h[4].float() * 2.0 ** 40)
     compare_fused(orc, R, t["W"], t["scale"], t["base"], (h, pre, post, comb, mixes), x=t["x"], label="scaled")
+
+
+@pytest.mark.parametrize("d", [64, 1024, 5120])
+def test_huge_tokens_sum_of_squares_overflow(orc, d):
+    """Streams whose squares overflow fp32 (a chained stack without a norm
+    grows by about e per sublayer): at 2^56 the plain fp32 sum of squares is
+    still finite, from about 2^58 on it overflows and the scaled sum takes
+    over; up to 2^124 the bf16 values themselves stay finite."""
+    w = hin.WORKLOADS["decode"]
+    t = hin.make_inputs(w, DEV, seed=29)
+    R = t["R"][..., :d].contiguous().clone()
+    W, s, b = hin.make_params(w, DEV, seed=29)
+    W = W.view(-1, 4, w.d)[:, :, :d].contiguous().view(-1, 4 * d)
+    exps = [56, 60, 64, 80, 100, 120, 124]
+    for i, e in enumerate(exps):
+        R[8 + i] = R[i] * 2.0 ** e
+    h, pre, post, comb, mixes = run_fused(R, W, s, b)
+    assert bool(torch.isfinite(mixes).all())
+    for i, e in enumerate(exps):
+        check_mixes(_np(mixes[8 + i, 0]), _np(mixes[i, 0]).astype(np.float64), tol=1e-6)
+    x = t["x"][..., :d].contiguous()
+    compare_fused(orc, R, W, s, b, (h, pre, post, comb, mixes), x=x, label="huge d=%d" % d)
+    # the standalone projection agrees bit for bit with the fused call
+    assert torch.equal(hcl.hc_mixes(R, W), mixes)
 
 
 def test_diag_scale_bitwise(orc):
