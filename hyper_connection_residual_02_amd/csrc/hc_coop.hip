@@ -47,6 +47,8 @@
 //  * Every wait is bounded in time; a timed-out wait raises a flag in the
 //    workspace header and the workgroup stops.
 
+#include <atomic>
+
 #include "hc_device.hpp"
 #include "hc_launch.hpp"
 
@@ -78,7 +80,36 @@ struct WsHeader {
     int64_t clean;
     uint32_t xbad;      // workgroups not on the XCD their group is placed on (this call)
     uint32_t arrive;    // workgroups past the placement check (this call)
+    uint64_t ready;     // number of the call whose header update is complete
+    uint32_t clear;     // this call clears its record area before use
+    uint32_t pad;
 };
+
+static_assert(sizeof(WsHeader) <= 256, "the header occupies the first 256 bytes of the workspace");
+
+// Epoch of call number `call` (process-wide call counter): 1 .. kEpochMask.
+__host__ __device__ inline uint32_t epoch_of(uint64_t call) { return 1u + (uint32_t)(call % kEpochMask); }
+
+// Header update at the start of a call.  The record area must be cleared
+// on the first use of a workspace, when the call epoch does not increase
+// (the 20-bit epoch wrapped, or calls were numbered elsewhere), and when
+// this call's record area reaches past the part known to be clean (a
+// previous call may have kept its mixes there), so that a record never
+// carries a current tag before this call writes it.  Past this call's
+// record area the workspace may receive mixes, so only that area stays
+// known clean.  Returns whether to clear.
+__device__ inline bool header_update(WsHeader* hdr, uint64_t call, int64_t nchunks) {
+    const uint32_t ep = epoch_of(call);
+    const bool clear = hdr->magic != kMagic || ep <= hdr->epoch || hdr->clean < nchunks;
+    hdr->magic = kMagic;
+    hdr->epoch = ep;
+    hdr->err = 0u;
+    hdr->clean = nchunks;
+    hdr->xbad = 0u;
+    hdr->arrive = 0u;
+    hdr->clear = clear ? 1u : 0u;
+    return clear;
+}
 
 struct CoopArgs {
     const uint16_t* R;
@@ -104,6 +135,7 @@ struct CoopArgs {
     float norm_eps;
     float K;
     int part_bytes;
+    uint64_t call;      // process-wide number of this call (sets the record epoch)
 };
 
 // Field f of a partial record (0..23 = the 24 dot products, 24 = sum of
@@ -151,7 +183,7 @@ struct RoundCtx {
     int nown;               // tokens of a round this member owns
     uint32_t epoch;
     __amdgpu_buffer_rsrc_t rsrc;   // the record area
-    float s0, bpre;         // hc_scale[0] and hc_base[thread % 4], read once: a parameter
+    float s0, bpre;         // hc_scale[0] and hc_base of the lane's pre stream, read once: a parameter
                             // load inside the loop would be the youngest memory op, and
                             // waiting for it would wait for every prefetch
 };
@@ -159,9 +191,8 @@ struct RoundCtx {
 // hc_base[thread % 4] from four uniform (scalar) loads: a per-lane vector
 // load would be waited for where it is first used inside the round loop,
 // and that wait would also wait for every store still in flight.
-__device__ __forceinline__ float base_of_lane(const float* base) {
+__device__ __forceinline__ float base_of_lane(const float* base, int k) {
     const float b0 = base[0], b1 = base[1], b2 = base[2], b3 = base[3];
-    const int k = threadIdx.x & 3;
     return k == 0 ? b0 : (k == 1 ? b1 : (k == 2 ? b2 : b3));
 }
 
@@ -618,11 +649,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_coop(CoopArgs a) {
     c.tt = c.w & 1;
     c.kg = c.w >> 1;
     c.nown = c.q < kT ? (kT - 1 - c.q) / a.G + 1 : 0;
-    c.epoch = a.hdr->epoch;
+    c.epoch = epoch_of(a.call);
     c.rsrc = __builtin_amdgcn_make_buffer_rsrc(a.part, 0, a.part_bytes, kBufDword3);
     if (c.g >= a.ntiles) return;
     c.s0 = FUSED ? a.scale[0] : 0.0f;
-    c.bpre = FUSED ? base_of_lane(a.base) : 0.0f;
+    c.bpre = FUSED ? base_of_lane(a.base, threadIdx.x & 3) : 0.0f;
     c.nr = (int)((a.ntiles - c.g + a.NG - 1) / a.NG);
 
     // weight slice -> LDS as MFMA B fragments, split exactly into bf16 pieces;
@@ -698,8 +729,7 @@ namespace spec {
 constexpr int kMW = 4;                  // MFMA waves
 constexpr int kNSlot = 3;               // residual rounds held in LDS
 constexpr int kTokX = kT / 4;           // tokens per exchange wave
-constexpr int kPreR = kTokX / 2;        // load rounds for the pre-relevant records (4 pairs each)
-constexpr int kOwnR = 3;                // load rounds for the owned token's 9 chunks (4 per round)
+constexpr int kXL = 8;                  // exchange loads per lane and pass: 32 members / 4 lane groups
 
 template <int KS>
 struct Geo {
@@ -762,25 +792,9 @@ struct MState {
 template <int KS>
 struct XState {
     u32x4 rb[2][Geo<KS>::kPass][kHC];      // residual for h, two rounds (by parity)
-    u32x4 P[kPreR][2];                     // records of the next exchange (issued a tick early)
-    u32x4 O[kOwnR][2];
+    u32x4 P[kXL];                          // records of the next exchange (issued a tick early)
+    u32x4 O[kXL];
 };
-
-// Sum over the 32 lanes of each half-wave (all lanes of a half get the
-// same value): DPP within rows of 16, then a permlane16 swap.
-__device__ __forceinline__ float gsum32(float v) {
-    v = quad_sum(v);
-    v = col4_sum(v);
-    auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(x[0]) + __uint_as_float(x[1]);
-}
-// The value of the lower half-wave (lanes 0..31) and of the upper half
-// (lanes 32..63) of a value that is uniform within each half, in every lane.
-__device__ __forceinline__ void halves(float v, float& lo, float& hi) {
-    auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    lo = __uint_as_float(x[0]);
-    hi = __uint_as_float(x[1]);
-}
 
 // Record stores and loads.  Loads are device scope (sc1): they skip the
 // L1, which may hold a copy of a slot's previous record (a group-scope load
@@ -932,47 +946,51 @@ __device__ __forceinline__ void m_mfma(const MState<KS>& S, const RoundCtx& c, L
     }
 }
 
-// Lane layout of the exchange loads: a (chunk, token) pair takes one row of
-// 16 lanes; lane e of the row reads members e and e + 16, so each load
-// instruction reads 256 contiguous bytes per row.  Members past G read past
-// the resource (zeros).  Pre-relevant round q: row r holds chunk r & 1 of
-// token 8xw + 2q + (r >> 1).  Owned round q: row r holds chunk 4q + r of
-// the owned token.
-__device__ __forceinline__ int x_member(const RoundCtx& c, int i) { return (c.l & 15) + 16 * i; }
+// Lane layout of the exchange loads: lane l = e + 16 g reads, in load s,
+// the record of member 4s + g for entry e, so that a member sum is an
+// in-lane sum over the kXL loads followed by a sum over the 4 lane groups
+// (two swaps), with no dependent cross-lane chain.  Pre loads: entry e is
+// chunk e % 2 of token 8xw + e / 2.  Owner loads: entry e is chunk e of the
+// owned token (e < 9).  Members past G read past the resource (zeros).  The
+// pre and owner paths add in the same order, so pre formed from the pre
+// loads is bitwise the pre of the owner's mixes.
+__device__ __forceinline__ int x_member(const RoundCtx& c, int s) { return 4 * s + (c.l >> 4); }
 
-// Member sum of a pair (all 16 lanes of the row get it): members e and
-// e + 16 in the lane, then the row.  Shared by the pre and owner paths, so
-// both form bitwise the same sums.
-__device__ __forceinline__ float row_member_sum(uint32_t a, uint32_t b) {
-    float v = __uint_as_float(a) + __uint_as_float(b);
-    v = quad_sum(v);
-    return col4_sum(v);
+// Member sum of record slot sl of kXL loads (every lane of the wave with
+// the same entry gets the same total).
+__device__ __forceinline__ float member_sum(const u32x4 (&v)[kXL], int sl) {
+    float x = __uint_as_float(v[0][sl]);
+#pragma unroll
+    for (int s = 1; s < kXL; ++s) x += __uint_as_float(v[s][sl]);
+    auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+template <bool FUSED>
+__device__ __forceinline__ bool pre_live(const CoopArgs& a, const RoundCtx& c, int s) {
+    return FUSED && x_member(c, s) < a.G;
+}
+__device__ __forceinline__ bool own_live(const CoopArgs& a, const RoundCtx& c, int xw, int s) {
+    return xw < c.nown && x_member(c, s) < a.G && (c.l & 15) < kChunks;
+}
+__device__ __forceinline__ int pre_off(const CoopArgs& a, const RoundCtx& c, int r, int xw, int s) {
+    const int e = c.l & 15;
+    return rec_off(a, c, r, e & 1, kTokX * xw + (e >> 1), x_member(c, s));
+}
+__device__ __forceinline__ int own_off(const CoopArgs& a, const RoundCtx& c, int r, int xw, int s) {
+    return rec_off(a, c, r, c.l & 15, c.q + a.G * xw, x_member(c, s));
 }
 
 // Record loads of round r for exchange wave xw: the pre-relevant records
 // (chunks 0 and 1) of tokens 8xw..8xw+7 and all records of owned token xw.
-// Lanes 0..31 read chunk 2i (or 0) of members 0..31, lanes 32..63 chunk
-// 2i+1 (or 1).  Device scope: a record slot is rewritten every 4 rounds and
-// a copy of the old record may still sit in this CU's L1.
 template <int KS, bool FUSED, bool LOCAL>
 __device__ __forceinline__ void x_issue(XState<KS>& X, const CoopArgs& a, const RoundCtx& c, int xw, int r) {
-    const int row = c.l >> 4;
-    const int otk = c.q + a.G * xw;
 #pragma unroll
-    for (int q = 0; q < kPreR; ++q)
+    for (int s = 0; s < kXL; ++s) X.P[s] = ld_rec<LOCAL>(c, pre_live<FUSED>(a, c, s) ? pre_off(a, c, r, xw, s) : kOOB);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int m = x_member(c, i);
-            X.P[q][i] = ld_rec<LOCAL>(
-                c, FUSED && m < a.G ? rec_off(a, c, r, row & 1, kTokX * xw + 2 * q + (row >> 1), m) : kOOB);
-        }
-#pragma unroll
-    for (int q = 0; q < kOwnR; ++q)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int m = x_member(c, i), ch = 4 * q + row;
-            X.O[q][i] = ld_rec<LOCAL>(c, xw < c.nown && m < a.G && ch < kChunks ? rec_off(a, c, r, ch, otk, m) : kOOB);
-        }
+    for (int s = 0; s < kXL; ++s) X.O[s] = ld_rec<LOCAL>(c, own_live(a, c, xw, s) ? own_off(a, c, r, xw, s) : kOOB);
 }
 
 // Exchange of round r for exchange wave xw, from the loads issued by
@@ -984,25 +1002,14 @@ template <int KS, bool FUSED, bool LOCAL>
 __device__ __forceinline__ bool x_exchange(XState<KS>& X, const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, int xw,
                                            int r) {
     const uint32_t tag = tag_of(c, r);
-    const int l = c.l, row = l >> 4;
+    const int l = c.l, e = l & 15;
     const int otk = c.q + a.G * xw;
     const int64_t tok0 = tile_of(c, a, r) * kT;
-    // which loads name a real record
-    auto pre_live = [&](int i) { return FUSED && x_member(c, i) < a.G; };
-    auto own_live = [&](int q, int i) { return xw < c.nown && x_member(c, i) < a.G && 4 * q + row < kChunks; };
-    auto pre_off = [&](int q, int i) {
-        return rec_off(a, c, r, row & 1, kTokX * xw + 2 * q + (row >> 1), x_member(c, i));
-    };
-    auto own_off = [&](int q, int i) { return rec_off(a, c, r, 4 * q + row, otk, x_member(c, i)); };
     bool stale = false;
 #pragma unroll
-    for (int q = 0; q < kPreR; ++q)
+    for (int s = 0; s < kXL; ++s) stale |= pre_live<FUSED>(a, c, s) && X.P[s][3] != tag;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) stale |= pre_live(i) && X.P[q][i][3] != tag;
-#pragma unroll
-    for (int q = 0; q < kOwnR; ++q)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) stale |= own_live(q, i) && X.O[q][i][3] != tag;
+    for (int s = 0; s < kXL; ++s) stale |= own_live(a, c, xw, s) && X.O[s][3] != tag;
     bool bad = false;
     if (__builtin_amdgcn_ballot_w64(stale)) {              // wave-uniform: a peer is late
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -1010,23 +1017,12 @@ __device__ __forceinline__ bool x_exchange(XState<KS>& X, const CoopArgs& a, con
             // re-read every record of the exchange at once: a record that was
             // already current comes back unchanged (its slot is not rewritten
             // before every member has finished this round)
-#pragma unroll
-            for (int q = 0; q < kPreR; ++q)
-#pragma unroll
-                for (int i = 0; i < 2; ++i) X.P[q][i] = ld_rec<LOCAL>(c, pre_live(i) ? pre_off(q, i) : kOOB);
-#pragma unroll
-            for (int q = 0; q < kOwnR; ++q)
-#pragma unroll
-                for (int i = 0; i < 2; ++i) X.O[q][i] = ld_rec<LOCAL>(c, own_live(q, i) ? own_off(q, i) : kOOB);
+            x_issue<KS, FUSED, LOCAL>(X, a, c, xw, r);
             bool again = false;
 #pragma unroll
-            for (int q = 0; q < kPreR; ++q)
+            for (int s = 0; s < kXL; ++s) again |= pre_live<FUSED>(a, c, s) && X.P[s][3] != tag;
 #pragma unroll
-                for (int i = 0; i < 2; ++i) again |= pre_live(i) && X.P[q][i][3] != tag;
-#pragma unroll
-            for (int q = 0; q < kOwnR; ++q)
-#pragma unroll
-                for (int i = 0; i < 2; ++i) again |= own_live(q, i) && X.O[q][i][3] != tag;
+            for (int s = 0; s < kXL; ++s) again |= own_live(a, c, xw, s) && X.O[s][3] != tag;
             if (!__builtin_amdgcn_ballot_w64(again)) break;
             if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull ||
                 __hip_atomic_load(&a.hdr->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
@@ -1037,53 +1033,24 @@ __device__ __forceinline__ bool x_exchange(XState<KS>& X, const CoopArgs& a, con
             __builtin_amdgcn_s_sleep(1);
         }
     }
-    float pre_mine = 0.0f;          // lanes 0..31: pre of (token l/4, stream l%4)
+    // lanes with an even entry e = 2j: pre of (token 8xw + j, stream g); the
+    // odd neighbour holds the token's chunk 1 (m3 and the sums of squares)
+    float pre_mine = 0.0f;
+    const int k = l >> 4, j = e >> 1;
     if (FUSED) {
-        // round q: rows 0,1 hold chunks 0,1 of token 2q, rows 2,3 of token
-        // 2q+1; a permlane16 swap pairs the chunks, a permlane32 swap the
-        // tokens, so every lane sees both tokens' m0..m3 and sum of squares
-        const int k = l & 3, jl = (l >> 2) & (kTokX - 1);
-        float mine_m = 0.0f, mine_ss = 1.0f, mine_sb = 1.0f;
-#pragma unroll
-        for (int q = 0; q < kPreR; ++q) {
-            float s3[3][2];            // [slot][token 2q + t]: chunk 0 value, then chunk 1 value below
-            float c1[3][2];
-#pragma unroll
-            for (int sl = 0; sl < 3; ++sl) {
-                const float v = row_member_sum(X.P[q][0][sl], X.P[q][1][sl]);
-                auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-                // x[0]: rows 0,2 value (chunk 0), x[1]: rows 1,3 value (chunk 1); per 32-lane half
-                float lo0, hi0, lo1, hi1;
-                halves(__uint_as_float(x[0]), lo0, hi0);
-                halves(__uint_as_float(x[1]), lo1, hi1);
-                s3[sl][0] = lo0; s3[sl][1] = hi0;      // chunk 0 of tokens 2q, 2q+1
-                c1[sl][0] = lo1; c1[sl][1] = hi1;      // chunk 1 of tokens 2q, 2q+1
-            }
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const float m0 = s3[0][t], m1 = s3[1][t], m2 = s3[2][t];
-                const float m3 = c1[0][t], ss = c1[1][t], sb = c1[2][t];
-                const float mk = k == 0 ? m0 : (k == 1 ? m1 : (k == 2 ? m2 : m3));
-                const bool mine = jl == 2 * q + t;
-                mine_m = mine ? mk : mine_m;
-                mine_ss = mine ? ss : mine_ss;
-                mine_sb = mine ? sb : mine_sb;
-            }
-        }
-        pre_mine = pre_gate(mix_value(mine_m, mix_scale(mine_ss, mine_sb, a.K, a.norm_eps)), c.s0, c.bpre, a.eps);
-        if (l < 4 * kTokX) L.xpre[xw][jl][k] = pre_mine;
+        const float v0 = member_sum(X.P, 0), v1 = member_sum(X.P, 1), v2 = member_sum(X.P, 2);
+        const float n0 = dpp<0xF5>(v0), n1 = dpp<0xF5>(v1), n2 = dpp<0xF5>(v2);      // quad_perm [1,1,3,3]
+        const float mk = k == 0 ? v0 : (k == 1 ? v1 : (k == 2 ? v2 : n0));
+        pre_mine = pre_gate(mix_value(mk, mix_scale(n1, n2, a.K, a.norm_eps)), c.s0, c.bpre, a.eps);
+        if ((e & 1) == 0) L.xpre[xw][j][k] = pre_mine;
     }
-    // owned token: chunk 4q + row in row `row` of round q
-#pragma unroll
-    for (int q = 0; q < kOwnR; ++q) {
-        float v[3];
-#pragma unroll
-        for (int sl = 0; sl < 3; ++sl) v[sl] = row_member_sum(X.O[q][0][sl], X.O[q][1][sl]);
-        const int ch = 4 * q + row;
-        if ((l & 15) == 0 && ch < kChunks) {
-            L.xown[xw][ch][0] = v[0];
-            L.xown[xw][ch][1] = v[1];
-            L.xown[xw][ch][2] = v[2];
+    // owned token: entry e = chunk e
+    {
+        const float v0 = member_sum(X.O, 0), v1 = member_sum(X.O, 1), v2 = member_sum(X.O, 2);
+        if (l < kChunks) {
+            L.xown[xw][l][0] = v0;
+            L.xown[xw][l][1] = v1;
+            L.xown[xw][l][2] = v2;
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");     // the wave reads back its own LDS writes
@@ -1098,11 +1065,11 @@ __device__ __forceinline__ bool x_exchange(XState<KS>& X, const CoopArgs& a, con
                                               xw < c.nown && l < kMix ? (otk * kMix + l) * 4 : kOOB, 0, 0);
     }
     if (FUSED) {
-        // pre output of the tokens this member owns: lanes 0..31 = (token j, stream k)
-        const int j = (l >> 2) & (kTokX - 1), k = l & 3, tk = kTokX * xw + j;
+        // pre output of the tokens this member owns
+        const int tk = kTokX * xw + j;
         const __amdgpu_buffer_rsrc_t rp = tile_rsrc(a.pre, kHC * 4, tok0, a.n, kT);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pre_mine), rp,
-                                              l < 4 * kTokX && tk % a.G == c.q ? (tk * kHC + k) * 4 : kOOB, 0, 0);
+                                              (e & 1) == 0 && tk % a.G == c.q ? (tk * kHC + k) * 4 : kOOB, 0, 0);
     }
     return bad;
 }
@@ -1241,17 +1208,53 @@ __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
     c.tt = 0;
     c.kg = 0;
     c.nown = c.q < kT ? (kT - 1 - c.q) / a.G + 1 : 0;
-    c.epoch = a.hdr->epoch;
+    c.epoch = epoch_of(a.call);
     c.rsrc = __builtin_amdgcn_make_buffer_rsrc(a.part, 0, a.part_bytes, kBufDword3);
     c.nr = (int)((a.ntiles - c.g + a.NG - 1) / a.NG);
     c.s0 = FUSED ? a.scale[0] : 0.0f;
-    c.bpre = FUSED ? base_of_lane(a.base) : 0.0f;
+    c.bpre = FUSED ? base_of_lane(a.base, (threadIdx.x & 63) >> 4) : 0.0f;
 
+    // Start of the call.  Workgroup 0 updates the workspace header and
+    // publishes this call's number; every workgroup waits for it, clears its
+    // share of the record area if the header says so, and only then counts
+    // itself in below, so no record is written before the area is clean.
     // Placement: with NG a multiple of 8, the members of group g are the
     // workgroups b = g (mod 8); if every workgroup runs on XCD b % 8 (read
     // from the XCC id register), each group sits on one XCD and its records
     // can stay in that XCD's L2.  All workgroups agree through one grid-wide
-    // count before the first record is written.
+    // count before the first record is written.  Both waits are bounded: a
+    // workgroup that is not resident within about two seconds (the launch
+    // does not reserve the device) makes the call stop with the error flag.
+    const int64_t nchunks = a.part_bytes / 16;
+    if (threadIdx.x == 0) {
+        bool ok = true;
+        if (blockIdx.x == 0) {
+            header_update(a.hdr, a.call, nchunks);
+            __hip_atomic_store(&a.hdr->ready, a.call, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            while (__hip_atomic_load(&a.hdr->ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != a.call) {
+                if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull) {
+                    ok = false;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        local_mode = ok ? (int)__hip_atomic_load(&a.hdr->clear, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -1;
+    }
+    __syncthreads();
+    if (local_mode < 0) {
+        if (threadIdx.x == 0) __hip_atomic_store(&a.hdr->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    if (local_mode) {
+        const int64_t per = (nchunks + gridDim.x - 1) / gridDim.x;
+        const int64_t lo = per * blockIdx.x, hi = lo + per < nchunks ? lo + per : nchunks;
+        for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x) a.part[i] = u32x4{0u, 0u, 0u, 0u};
+        __threadfence();
+    }
+    __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11)) & 0xFu;
         if (xcc != (blockIdx.x & 7u)) __hip_atomic_fetch_add(&a.hdr->xbad, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1280,38 +1283,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
 
 }  // namespace spec
 
-// Per-call header update.  Clears the record area on the first use of a
-// workspace, when the 20-bit call epoch wraps, and when this call's record
-// area reaches past the part known to be clean (a previous call may have
-// kept its mixes there), so a record never carries a current tag before
-// this call writes it.  Past this call's record area the workspace may
-// receive mixes, so only that area stays known clean.
-__global__ __launch_bounds__(1024) void k_init(WsHeader* hdr, u32x4* part, int64_t nchunks) {
+// Header update and record-area clearing before a call of the cooperative
+// kernel of narrow or wide streams (the wave-specialised kernel does this
+// at its own start).
+__global__ __launch_bounds__(1024) void k_init(WsHeader* hdr, u32x4* part, int64_t nchunks, uint64_t call) {
     __shared__ int clear;
-    __shared__ uint32_t next;
-    if (threadIdx.x == 0) {
-        const uint32_t e = hdr->epoch;
-        const bool fresh = hdr->magic != kMagic;
-        uint32_t ne = fresh ? 1u : (e & kEpochMask) + 1u;
-        clear = fresh || ne > kEpochMask || hdr->clean < nchunks;
-        if (ne > kEpochMask) ne = 1u;
-        next = ne;
-    }
+    if (threadIdx.x == 0) clear = header_update(hdr, call, nchunks);
     __syncthreads();
     if (clear)
         for (int64_t i = threadIdx.x; i < nchunks; i += blockDim.x) part[i] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        hdr->magic = kMagic;
-        hdr->epoch = next;
-        hdr->err = 0u;
-        hdr->clean = nchunks;
-        hdr->xbad = 0u;
-        hdr->arrive = 0u;
-    }
 }
 
 // ------------------------------------------------------------------ host
+// Calls are numbered process-wide; the number sets the epoch in the record
+// tags, so no per-call initialisation launch is needed.
+static std::atomic<uint64_t> g_calls{0};
+
 int coop_ks(int d) {
     if (d <= 0 || d % 32 != 0) return 0;
     for (int k = 1; k <= 5; ++k)
@@ -1347,8 +1334,7 @@ bool coop_plan(int64_t n, int d, CoopPlan& p) {
 template <int KS, int PI, bool FUSED>
 static int launch_t(const CoopPlan& p, CoopArgs& a, hipStream_t s) {
     void* args[] = {&a};
-    hipError_t e = hipLaunchCooperativeKernel((const void*)k_coop<KS, PI, FUSED>, dim3(p.G * p.NG),
-                                              dim3(kThreads), args, 0, s);
+    hipError_t e = hipLaunchKernel((const void*)k_coop<KS, PI, FUSED>, dim3(p.G * p.NG), dim3(kThreads), args, 0, s);
     return e == hipSuccess ? 0 : -1;
 }
 
@@ -1369,7 +1355,7 @@ template <int KS>
 static int launch_spec(const CoopPlan& p, CoopArgs& a, bool fused, hipStream_t s) {
     void* args[] = {&a};
     const void* f = fused ? (const void*)spec::k_spec<KS, true> : (const void*)spec::k_spec<KS, false>;
-    hipError_t e = hipLaunchCooperativeKernel(f, dim3(p.G * p.NG), dim3(kThreads), args, 0, s);
+    hipError_t e = hipLaunchKernel(f, dim3(p.G * p.NG), dim3(kThreads), args, 0, s);
     return e == hipSuccess ? 0 : -1;
 }
 
@@ -1401,9 +1387,12 @@ int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* s
     a.norm_eps = norm_eps;
     a.K = (float)(kHC * d);
     a.part_bytes = (int)(p.ws_mix - p.ws_part);
-    k_init<<<1, 1024, 0, s>>>(a.hdr, a.part, (int64_t)(a.part_bytes / 16));
-    if (hipGetLastError() != hipSuccess) return -1;
+    a.call = g_calls.fetch_add(1, std::memory_order_relaxed) + 1;
     int rc = -1;
+    if (!use_spec(p)) {
+        k_init<<<1, 1024, 0, s>>>(a.hdr, a.part, (int64_t)(a.part_bytes / 16), a.call);
+        if (hipGetLastError() != hipSuccess) return -1;
+    }
     if (use_spec(p)) {
         switch (p.KS) {
             case 1: rc = launch_spec<1>(p, a, fused, s); break;

@@ -61,10 +61,13 @@ __device__ __forceinline__ float f32_mid(double y, bool& mid) {
 __device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
 
 // ------------------------------------------------ 16-lane row reductions
-// DPP controls (gfx9 encoding): quad_perm [1,0,3,2] and [2,3,0,1], row_ror 4 / 8.
+// DPP controls (gfx9 encoding): quad_perm patterns and row_ror 4 / 8, all of
+// which read a lane inside the same row, so no lane is out of bounds and
+// the bound_ctrl setting only lets the compiler fold the move into the
+// instruction that uses it.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 // Sum / max over the 4 lanes of a quad (lanes 4j..4j+3 of a 16-lane row).
 __device__ __forceinline__ float quad_sum(float v) {

@@ -98,17 +98,22 @@ const char *hc_version(void);
  *
  * Workspace: device memory of at least hc_fused_workspace_bytes(n, hc, d)
  * bytes, 256-byte aligned.  It holds the partial sums the workgroups of a
- * token group exchange, and a small header in its first 256 bytes that
- * numbers the calls made with it, so that a record left by an earlier call
- * is never taken for a current one.  Any contents are accepted on first
- * use.  Between calls, leave it alone (or zero its first 256 bytes after
- * using it for something else).  Calls that may run at the same time,
- * on different streams, each need their own workspace.
+ * token group exchange, and a small header in its first 256 bytes.  Calls
+ * are numbered by a process-wide counter in the library; the number tags
+ * every partial sum, so that a record left by an earlier call is never
+ * taken for a current one, and the header records which call last
+ * prepared the workspace.  Any contents are accepted on first use.  Between
+ * calls, leave it alone (or zero its first 256 bytes after using it for
+ * something else).  Calls that may run at the same time, on different
+ * streams, each need their own workspace.
  *
- * The launch is cooperative: every workgroup of the grid is resident at
- * once, so each wait for a peer's partial sums ends.  As a guard, a wait
- * that exceeds about two seconds makes the kernel stop early and flag an
- * error word in the workspace header; outputs are then undefined.
+ * The kernel is an ordinary launch whose grid (at most one workgroup per
+ * compute unit) fits the device at once; its workgroups wait for each
+ * other's partial sums.  Every such wait is bounded: a workgroup that is
+ * not resident within about two seconds (say, while long-running work on
+ * another stream holds compute units), or a peer that stops, makes the
+ * kernel stop early and set an error word in the workspace header; outputs
+ * are then undefined.
  */
 int hc_mixes(const void *R, const float *hc_fn, float *mixes, int64_t n,
              int32_t hc, int32_t d, float norm_eps, void *workspace,
