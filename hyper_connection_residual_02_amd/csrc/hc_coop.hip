@@ -871,8 +871,25 @@ __device__ __forceinline__ void m_dma(const MState<KS>& S, const CoopArgs& a, co
     for (int i = 0; i < Geo<KS>::kDmaW; ++i) dma16(rs, base + i * 1024, S.dvoff[i]);
 }
 
+// Record layout of this kernel, per (group, slot): member-major.  A
+// member's 288 records are chunks 0 and 1 (the pre-relevant fields) of the
+// 32 tokens, token-major (1 KB), then chunks 2..8 of the 32 tokens,
+// token-major (3.5 KB).  An exchange load then reads whole 256-byte runs of
+// one member, the owner's loads two runs per member, and a publication
+// store instruction 1 KB in one run.
+constexpr int kRecPre = 2 * kT;                 // records of the pre-relevant run
+constexpr int kRecMember = kChunks * kT;        // records per member and round
+__device__ __forceinline__ int srec_index(int chunk, int t) {
+    return chunk < 2 ? 2 * t + chunk : kRecPre + (kChunks - 2) * t + (chunk - 2);
+}
+__device__ __forceinline__ int srec_off(const CoopArgs& a, const RoundCtx& c, int r, int member, int rec) {
+    const int slot = r % kSlots;
+    return (((c.g * kSlots + slot) * a.GP + member) * kRecMember + rec) * 16;
+}
+
 // Records of round r from the partials of the four MFMA waves (two store
 // instructions per wave, always; past the group's rounds they are dropped).
+// Lane idx writes record idx of this member.
 template <int KS, bool LOCAL>
 __device__ __forceinline__ void m_publish(const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, int r) {
     const int tid = threadIdx.x;
@@ -881,7 +898,10 @@ __device__ __forceinline__ void m_publish(const CoopArgs& a, const RoundCtx& c, 
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int idx = p * (kMW * 64) + tid;
-        const int ch = idx / kT, tk = idx - ch * kT;
+        const int id = idx < kRecMember ? idx : 0;      // lanes past the records compute record 0, dropped
+        const int q = id - kRecPre;
+        const int tk = id < kRecPre ? id >> 1 : q / (kChunks - 2);
+        const int ch = id < kRecPre ? id & 1 : 2 + (q - (kChunks - 2) * (q / (kChunks - 2)));
         u32x4 v;
 #pragma unroll
         for (int sl = 0; sl < 3; ++sl) {
@@ -892,7 +912,7 @@ __device__ __forceinline__ void m_publish(const CoopArgs& a, const RoundCtx& c, 
             v[sl] = __float_as_uint(x);
         }
         v[3] = tag_of(c, r);
-        st_rec<LOCAL>(c, live && ch < kChunks ? rec_off(a, c, r, ch, tk, c.q) : kOOB, v);
+        st_rec<LOCAL>(c, live && idx < kRecMember ? srec_off(a, c, r, c.q, idx) : kOOB, v);
     }
 }
 
@@ -977,10 +997,10 @@ __device__ __forceinline__ bool own_live(const CoopArgs& a, const RoundCtx& c, i
 }
 __device__ __forceinline__ int pre_off(const CoopArgs& a, const RoundCtx& c, int r, int xw, int s) {
     const int e = c.l & 15;
-    return rec_off(a, c, r, e & 1, kTokX * xw + (e >> 1), x_member(c, s));
+    return srec_off(a, c, r, x_member(c, s), srec_index(e & 1, kTokX * xw + (e >> 1)));
 }
 __device__ __forceinline__ int own_off(const CoopArgs& a, const RoundCtx& c, int r, int xw, int s) {
-    return rec_off(a, c, r, c.l & 15, c.q + a.G * xw, x_member(c, s));
+    return srec_off(a, c, r, x_member(c, s), srec_index(c.l & 15, c.q + a.G * xw));
 }
 
 // Record loads of round r for exchange wave xw: the pre-relevant records
