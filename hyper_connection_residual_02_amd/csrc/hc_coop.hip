@@ -737,9 +737,9 @@ struct Geo {
     static constexpr int kSlotB = (kT * kRowB + 4095) / 4096 * 4096;
     static constexpr int kDma = kSlotB / 1024;                 // 1 KB load instructions per round
     static constexpr int kDmaW = kDma / kMW;                   // per MFMA wave
-    static constexpr int kBlk = 4 * KS;                        // 8-feature blocks per token and stream
+    static constexpr int kBlk = 8 * KS;                        // 4-feature blocks per token and stream
     static constexpr int kItems = kTokX * kBlk;                // h items (token, block) per exchange wave
-    static constexpr int kPass = (kItems + 63) / 64;
+    static constexpr int kPass = (kItems + 63) / 64;           // KS = 5: 320 items, 5 full passes
 };
 
 template <int KS>
@@ -791,7 +791,7 @@ struct MState {
 
 template <int KS>
 struct XState {
-    u32x4 rb[2][Geo<KS>::kPass][kHC];      // residual for h, two rounds (by parity)
+    u32x2 rb[2][Geo<KS>::kPass][kHC];      // residual for h, two rounds (by parity)
     u32x4 P[kXL];                          // records of the next exchange (issued a tick early)
     u32x4 O[kXL];
 };
@@ -1094,9 +1094,10 @@ __device__ __forceinline__ bool x_exchange(XState<KS>& X, const CoopArgs& a, con
     return bad;
 }
 
-// h of round r for exchange wave xw from the residual copy rb.
+// h of round r for exchange wave xw from the residual copy rb (items of 4
+// features: token tk, block b).
 template <int KS>
-__device__ __forceinline__ void x_h(const u32x4 (&rb)[Geo<KS>::kPass][kHC], const CoopArgs& a, const RoundCtx& c,
+__device__ __forceinline__ void x_h(const u32x2 (&rb)[Geo<KS>::kPass][kHC], const CoopArgs& a, const RoundCtx& c,
                                     Lds<KS>& L, int xw, int r) {
     const int64_t tok0 = tile_of(c, a, r) * kT;
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(a.h, (int64_t)a.d * 2, tok0, a.n, kT);
@@ -1115,30 +1116,30 @@ __device__ __forceinline__ void x_h(const u32x4 (&rb)[Geo<KS>::kPass][kHC], cons
             y = __builtin_fma(p2, v(rb[p][2][w]), y);
             return __builtin_fma(p3, v(rb[p][3][w]), y);
         };
-        u32x4 out;
-        float f[4][2];
+        u32x2 out;
+        float f[2][2];
         bool mid = false;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < 2; ++w) {
             f[w][0] = f32_mid(sum(w, 0), mid);
             f[w][1] = f32_mid(sum(w, 1), mid);
         }
         if (__builtin_amdgcn_ballot_w64(mid)) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) out[w] = pack2(bf16_rn_f64(sum(w, 0)), bf16_rn_f64(sum(w, 1)));
+            for (int w = 0; w < 2; ++w) out[w] = pack2(bf16_rn_f64(sum(w, 0)), bf16_rn_f64(sum(w, 1)));
         } else {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) out[w] = pack2(bf16_rn(f[w][0]), bf16_rn(f[w][1]));
+            for (int w = 0; w < 2; ++w) out[w] = pack2(bf16_rn(f[w][0]), bf16_rn(f[w][1]));
         }
-        const int off = valid ? ((kTokX * xw + tk) * a.d + c.q * (32 * KS) + 8 * b) * 2 : kOOB;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((__vector_size__(16))) int, out),
-                                               rs, off, 0, 0);
+        const int off = valid ? ((kTokX * xw + tk) * a.d + c.q * (32 * KS) + 4 * b) * 2 : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((__vector_size__(8))) int, out),
+                                              rs, off, 0, 0);
     }
 }
 
 // Copy of round r's residual (slot r % 3) for this wave's h items.
 template <int KS>
-__device__ __forceinline__ void x_copy(u32x4 (&rb)[Geo<KS>::kPass][kHC], const RoundCtx& c, Lds<KS>& L, int xw,
+__device__ __forceinline__ void x_copy(u32x2 (&rb)[Geo<KS>::kPass][kHC], const RoundCtx& c, Lds<KS>& L, int xw,
                                        int r) {
     const uint8_t* slot = &L.slot[r % kNSlot][0];
 #pragma unroll
@@ -1148,8 +1149,8 @@ __device__ __forceinline__ void x_copy(u32x4 (&rb)[Geo<KS>::kPass][kHC], const R
         const int tk = it / Geo<KS>::kBlk, b = it - tk * Geo<KS>::kBlk;
 #pragma unroll
         for (int k = 0; k < kHC; ++k)
-            rb[p][k] = *reinterpret_cast<const u32x4*>(slot + (kTokX * xw + tk) * Geo<KS>::kRowB + k * (64 * KS) +
-                                                      16 * b);
+            rb[p][k] = *reinterpret_cast<const u32x2*>(slot + (kTokX * xw + tk) * Geo<KS>::kRowB + k * (64 * KS) +
+                                                      8 * b);
     }
 }
 
