@@ -127,9 +127,13 @@ def summarize_counters(d: str, n: int, dd: int, command: str):
     print("\n".join(lines))
 
 
-def summarize_trace(d: str, n: int, dd: int, command: str):
+def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, steps: int = 0):
     """Per-kernel launch durations from a rocprofv3 --kernel-trace --stats
-    run (``*kernel_stats.csv`` under ``d``) of the bench command."""
+    run of the bench command under ``d``: the average over every dispatch
+    (``*kernel_stats.csv``) and, when ``steps`` is given, the average over
+    the dispatches of the timed region alone (dispatches warmup .. warmup +
+    steps - 1 of each kernel, in start order, from ``*kernel_trace.csv``) --
+    the launches the bench's own per-kernel events measure."""
     import csv
     import glob
     files = glob.glob(os.path.join(d, "*kernel_stats.csv"))
@@ -137,11 +141,25 @@ def summarize_trace(d: str, n: int, dd: int, command: str):
         raise SystemExit("no kernel_stats.csv under %s" % d)
     with open(files[0]) as fh:
         rows = list(csv.DictReader(fh))
+    timed = {}
+    if steps:
+        tfiles = glob.glob(os.path.join(d, "*kernel_trace.csv"))
+        if tfiles:
+            per = {}
+            with open(tfiles[0]) as fh:
+                for r in csv.DictReader(fh):
+                    per.setdefault(r["Kernel_Name"], []).append(
+                        (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+            for name, v in per.items():
+                v.sort()
+                sel = [dur for _, dur in v[warmup:warmup + steps]]
+                if sel:
+                    timed[name] = sum(sel) / len(sel) / 1e3
     fb, pb = algorithmic_bytes(n, dd)
     alg = {"k_spec": fb, "k_coop": fb, "k_post": pb}
     lines = ["# Kernel durations, n=%d tokens, d=%d" % (n, dd), "", "Command:", "", "    " + command, "",
-             "| kernel | calls | average us | min us | max us | algorithmic GB/s | of 8 TB/s |",
-             "|---|---|---|---|---|---|---|"]
+             "| kernel | calls | average us | min us | max us | algorithmic GB/s | of 8 TB/s | timed-region average us | of 8 TB/s |",
+             "|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"]
         if "hc::" not in name:
@@ -150,10 +168,16 @@ def summarize_trace(d: str, n: int, dd: int, command: str):
         avg = float(r["AverageNs"]) / 1e3
         key = short.split("<")[0].split("::")[-1]
         gbs = alg[key] / (avg * 1e-6) / 1e9 if key in alg else None
-        lines.append("| %s | %s | %.2f | %.2f | %.2f | %s | %s |" % (
+        t = timed.get(name)
+        tg = alg[key] / (t * 1e-6) / 1e9 if (t and key in alg) else None
+        lines.append("| %s | %s | %.2f | %.2f | %.2f | %s | %s | %s | %s |" % (
             short, r["Calls"], avg, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
-            "%.1f" % gbs if gbs else "-", "%.3f" % (gbs / HBM_PEAK_GBS) if gbs else "-"))
+            "%.1f" % gbs if gbs else "-", "%.3f" % (gbs / HBM_PEAK_GBS) if gbs else "-",
+            "%.2f" % t if t else "-", "%.3f" % (tg / HBM_PEAK_GBS) if tg else "-"))
     lines.append("")
+    if steps:
+        lines.append("Timed region: dispatches %d .. %d of each kernel (after %d warmup steps)."
+                     % (warmup, warmup + steps - 1, warmup))
     lines.append("Kernel sources hash (sha256 of csrc/, first 16 hex): %s" % kernel_source_hash())
     with open(os.path.join(PROFILE_DIR, "kernel_trace_n%d_d%d.md" % (n, dd)), "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -188,7 +212,7 @@ def main():
         if args.summarize_counters:
             summarize_counters(args.summarize_counters, w.n, w.d, args.profile_command)
         if args.summarize_trace:
-            summarize_trace(args.summarize_trace, w.n, w.d, args.profile_command)
+            summarize_trace(args.summarize_trace, w.n, w.d, args.profile_command, args.warmup, args.steps)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -235,19 +259,40 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` steps, synchronised on both sides
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # ---- timed region: exactly `steps` steps, synchronised on both sides.
+    # Each launch of a step is also bracketed by its own pair of HIP events
+    # on the launch stream: those give the per-kernel durations, taken in
+    # the timed region itself (hc_post follows the fused call, as in a step).
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+    e0, e1 = ev(), ev()
+    inner = [(ev(), ev(), ev(), ev()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     e0.record(stream)
-    for _ in range(args.steps):
-        step()
+    for fa, fz, pa, pz in inner:
+        fa.record(stream)
+        fused()
+        fz.record(stream)
+        pa.record(stream)
+        post()
+        pz.record(stream)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # ---- per-kernel launch durations (HIP events on the launch stream)
+    def stats(pairs):
+        v = np.array([a.elapsed_time(z) for a, z in pairs]) * 1e3     # us
+        return float(v.mean()), float(np.median(v)), float(v.min())
+
+    f_mean, f_med, f_min = stats([(fa, fz) for fa, fz, _, _ in inner])
+    p_mean, p_med, p_min = stats([(pa, pz) for _, _, pa, pz in inner])
+
+    # ---- the same launches timed in isolation (information): back to back
+    # (warm caches), and cold, where a 1 GiB buffer is rewritten before every
+    # launch outside its events so that no input is left in the L2 or the
+    # last-level cache
     def time_each(fn, reps):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(reps)]
@@ -259,9 +304,32 @@ def main():
         v = np.array([a.elapsed_time(z) for a, z in evs]) * 1e3     # us
         return float(v.mean()), float(np.median(v)), float(v.min())
 
-    reps = max(args.steps, 10)
-    f_mean, f_med, f_min = time_each(fused, reps)
-    p_mean, p_med, p_min = time_each(post, reps)
+    reps = min(max(args.steps, 10), 50)
+    fw_mean, fw_med, fw_min = time_each(fused, reps)
+    pw_mean, pw_med, pw_min = time_each(post, reps)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def time_cold(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, z in evs:
+            flush.fill_(1)
+            a.record(stream)
+            fn()
+            z.record(stream)
+        torch.cuda.synchronize()
+        v = np.array([a.elapsed_time(z) for a, z in evs]) * 1e3
+        return float(v.mean()), float(np.median(v)), float(v.min())
+
+    fc_mean, fc_med, fc_min = time_cold(fused, reps)
+    pc_mean, pc_med, pc_min = time_cold(post, reps)
+    del flush
+
+    def iso(bytes_, warm, cold):
+        return {"warm_avg_us": round(warm[0], 2), "warm_min_us": round(warm[2], 2),
+                "warm_frac_of_peak": round(bytes_ / (warm[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "cold_avg_us": round(cold[0], 2), "cold_min_us": round(cold[2], 2),
+                "cold_frac_of_peak": round(bytes_ / (cold[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     fb, pb = algorithmic_bytes(n, d)
     f_gbs = fb / (f_mean * 1e-6) / 1e9
     p_gbs = pb / (p_mean * 1e-6) / 1e9
@@ -324,10 +392,12 @@ def main():
             "hc_fused_mix_pre": {"avg_us": round(f_mean, 2), "median_us": round(f_med, 2),
                                  "min_us": round(f_min, 2), "GB/s": round(f_gbs, 1),
                                  "frac_of_peak": round(f_gbs / HBM_PEAK_GBS, 4),
-                                 "tokens/s": round(n / (f_mean * 1e-6), 1), "bytes": fb},
+                                 "tokens/s": round(n / (f_mean * 1e-6), 1), "bytes": fb,
+                                 "isolated": iso(fb, (fw_mean, fw_med, fw_min), (fc_mean, fc_med, fc_min))},
             "hc_post": {"avg_us": round(p_mean, 2), "median_us": round(p_med, 2), "min_us": round(p_min, 2),
                         "GB/s": round(p_gbs, 1), "frac_of_peak": round(p_gbs / HBM_PEAK_GBS, 4),
-                        "tokens/s": round(n / (p_mean * 1e-6), 1), "bytes": pb},
+                        "tokens/s": round(n / (p_mean * 1e-6), 1), "bytes": pb,
+                        "isolated": iso(pb, (pw_mean, pw_med, pw_min), (pc_mean, pc_med, pc_min))},
         },
         "wall_s_timed": round(wall, 4),
         "cpu_baseline": cpu,
