@@ -240,6 +240,31 @@ def test_workspace_reused_across_shapes():
                 assert torch.equal(u, v)
 
 
+def test_workspace_shared_by_both_projection_kernels():
+    # one workspace alternated between widths served by the wave-specialised
+    # kernel (d = 5120, 2048: it prepares the workspace header itself) and by
+    # the cooperative kernel (d = 64, 8192: a separate preparation launch),
+    # fused and standalone calls mixed: every result equals that of a fresh
+    # workspace, so no record of one call is ever taken for another's
+    shapes = []
+    for i, d in enumerate([5120, 64, 2048, 8192, 5120, 64, 8192, 2048, 5120]):
+        w = hin.Workload("d%d" % d, 1, 97 + 31 * i, 4, d, 1.0 / np.sqrt(4 * d), 0.5, 2.0, 1.0)
+        shapes.append(hin.make_inputs(w, DEV, seed=40 + i))
+    shared = hcl.Workspace()
+    for i, t in enumerate(shapes):
+        args = (t["R"], t["W"], t["scale"], t["base"])
+        if i % 3 == 2:
+            got = (hcl.hc_mixes(t["R"], t["W"], workspace=shared),)
+            ref = (hcl.hc_mixes(t["R"], t["W"], workspace=hcl.Workspace()),)
+        else:
+            got = hcl.hc_fused_mix_pre(*args, want_pre=True, want_mixes=True, workspace=shared)
+            ref = hcl.hc_fused_mix_pre(*args, want_pre=True, want_mixes=True, workspace=hcl.Workspace())
+        torch.cuda.synchronize()
+        for u, v in zip(got, ref):
+            if u is not None:
+                assert torch.equal(u, v), "call %d (d=%d)" % (i, t["R"].shape[-1])
+
+
 def test_zero_and_scaled_tokens(orc):
     w = hin.WORKLOADS["decode"]
     t = hin.make_inputs(w, DEV, seed=19)
