@@ -817,18 +817,39 @@ __device__ __forceinline__ void m_setup(MState<KS>& S, const CoopArgs& a, const 
     // weight slice of stream w: k-step st, lane (column i, k-block grp) holds
     // features 32*st + 8*grp .. +7 of stream w of the member slice
     const int64_t K = (int64_t)kHC * a.d;
-#pragma unroll
-    for (int st = 0; st < KS; ++st) {
+    // piece (0 hi, 1 mid, 2 lo, -1 none) and weight row of column tile ct
+    auto tile_piece = [&](int ct, int& piece, int& j) {
+        if (ct < 3) { piece = ct; j = c.row; }
+        else if (ct == 3) { piece = c.row < 8 ? 0 : 1; j = 16 + (c.row & 7); }
+        else { piece = c.row < 8 ? 2 : -1; j = 16 + c.row; }
+    };
+    // the fp32 weights of k-step st for every column tile
+    auto fetch = [&](int st, f32x4 (&raw)[kTiles][2]) {
 #pragma unroll
         for (int ct = 0; ct < kTiles; ++ct) {
             int piece, j;
-            if (ct < 3) { piece = ct; j = c.row; }
-            else if (ct == 3) { piece = c.row < 8 ? 0 : 1; j = 16 + (c.row & 7); }
-            else { piece = c.row < 8 ? 2 : -1; j = 16 + c.row; }
+            tile_piece(ct, piece, j);
             const int jj = piece < 0 ? 0 : j;
             const f32x4* src = reinterpret_cast<const f32x4*>(a.W + jj * K + (int64_t)c.w * a.d +
                                                               c.q * (32 * KS) + 32 * st + 8 * c.grp);
-            const f32x4 w0 = src[0], w1 = src[1];
+            raw[ct][0] = src[0];
+            raw[ct][1] = src[1];
+        }
+    };
+    // Loads of k-step st+1 are issued before the pieces of k-step st are
+    // formed (the pinning below is a scheduling barrier, so a load placed
+    // after it would wait for every earlier one): two weight round trips in
+    // flight instead of one per column tile.
+    f32x4 raw[2][kTiles][2];
+    fetch(0, raw[0]);
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+        if (st + 1 < KS) fetch(st + 1, raw[(st + 1) & 1]);
+#pragma unroll
+        for (int ct = 0; ct < kTiles; ++ct) {
+            int piece, j;
+            tile_piece(ct, piece, j);
+            const f32x4 w0 = raw[st & 1][ct][0], w1 = raw[st & 1][ct][1];
             bf16x8 v;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -1302,6 +1323,187 @@ __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
     else spec_body<KS, FUSED, false>(a, c, L);
 }
 
+
+// ============================================== two-pass path (short runs)
+// For a call of few tokens the persistent kernel's fixed costs (the start-up
+// count, filling and draining its three-round pipeline, the exchange waits)
+// dominate.  There the same arithmetic runs as two ordinary launches with no
+// waits between workgroups:
+//
+//  * k_part: the MFMA waves' loop of k_spec on its own (same weight slices
+//    and pieces, same direct-to-LDS residual ring, same products, same order
+//    of the four stream partials).  Member q of tile group g writes the 26
+//    partial sums of each token of its rounds as 9 records of 16 bytes
+//    (3 floats and a zero word) to the workspace, at
+//    [token][member][chunk].  A zero word never equals a tag of the
+//    persistent kernels (their epochs start at 1), so a workspace that both
+//    paths use stays valid for either.
+//  * k_fin: one wave per token adds the members' records in the exchange
+//    order of k_spec (lane e + 16 g holds chunk e of members 4 s + g, summed
+//    over s in order, then across the lane groups by the same two swaps),
+//    forms the mixes, pre and the split + Sinkhorn with the shared per-token
+//    code, and the block's four waves then form h from a second read of the
+//    residual (bitwise hc_pre's result for that pre).
+//
+// Mixes, pre, post, comb and h are therefore bitwise those of k_spec for the
+// same token, whichever path a call takes.
+
+constexpr int kFinTok = 4;      // tokens per k_fin block (one reducing wave each)
+
+// Records of round r from the four MFMA waves' partials, to the two-pass
+// record area (two store instructions per lane, always, as m_publish: the
+// wait count of the loop depends on it).  Rounds past the group's end store
+// nothing.
+template <int KS>
+__device__ __forceinline__ void p_publish(const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, int r) {
+    const int tid = threadIdx.x;
+    const int b = r & 1;
+    const bool live = r >= 0 && r < c.nr;
+    const int64_t tok0 = live ? tile_of(c, a, r) * kT : 0;
+    int64_t valid = live ? a.n - tok0 : 0;
+    valid = valid < 0 ? 0 : (valid > kT ? kT : valid);
+    const int64_t tok_bytes = (int64_t)a.GP * kChunks * 16;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<char*>(a.part) + tok0 * tok_bytes, 0, (int)(valid * tok_bytes), kBufDword3);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int idx = p * (kMW * 64) + tid;
+        const int id = idx < kT * kChunks ? idx : 0;
+        const int tk = id / kChunks, ch = id - tk * kChunks;
+        u32x4 v;
+#pragma unroll
+        for (int sl = 0; sl < 3; ++sl) {
+            const int fi = field_at(ch, sl);
+            float x = 0.0f;
+            if (fi >= 0)
+                x = ((L.red[b][0][tk][fi] + L.red[b][1][tk][fi]) + L.red[b][2][tk][fi]) + L.red[b][3][tk][fi];
+            v[sl] = __float_as_uint(x);
+        }
+        v[3] = 0u;
+        const int off = idx < kT * kChunks ? ((tk * a.GP + c.q) * kChunks + ch) * 16 : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((__vector_size__(16))) int, v), rs,
+                                               off, 0, 0);
+    }
+}
+
+// Pass 1: workgroup b is member b % G of tile group b / G (tiles g, g + NG,
+// ...).  Four waves, one per stream, as the MFMA waves of k_spec; tick t
+// publishes round t-1, issues round t+2 and multiplies round t.
+template <int KS>
+__global__ __launch_bounds__(kMW * 64, 1) void k_part(CoopArgs a) {
+    __shared__ __attribute__((aligned(16))) Lds<KS> L;
+    RoundCtx c;
+    c.q = blockIdx.x % a.G;
+    c.g = blockIdx.x / a.G;
+    c.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    c.l = threadIdx.x & 63;
+    c.row = c.l & 15;
+    c.grp = c.l >> 4;
+    c.tt = 0;
+    c.kg = 0;
+    c.nown = 0;
+    c.epoch = 0;
+    c.nr = (int)((a.ntiles - c.g + a.NG - 1) / a.NG);
+    c.s0 = 0.0f;
+    c.bpre = 0.0f;
+    MState<KS> S;
+    m_setup<KS>(S, a, c);
+    m_dma<KS>(S, a, c, L, 0);
+    m_dma<KS>(S, a, c, L, 1);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW) : "memory");   // round 0 landed
+    __syncthreads();
+    for (int t = 0;; ++t) {
+        p_publish<KS>(a, c, L, t - 1);
+        m_dma<KS>(S, a, c, L, t + 2);
+        m_mfma<KS>(S, c, L, t);
+        // round t+1 in LDS: younger than its loads are only this tick's two
+        // record stores and the loads of round t+2
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW + 2) : "memory");
+        __syncthreads();
+        if (t >= c.nr) break;          // tick nr published the last round
+    }
+    // no load may still be writing this workgroup's LDS when it ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Pass 2: block b covers tokens kFinTok*(b / splits) .. +3 and column part
+// b % splits of h.  Wave w reduces token kFinTok*(b / splits) + w.
+template <bool FUSED>
+__global__ __launch_bounds__(256) void k_fin(CoopArgs a, int splits) {
+    __shared__ float sums[kFinTok][kChunks][4];
+    __shared__ __attribute__((aligned(16))) float mixL[kFinTok][kMix];
+    __shared__ __attribute__((aligned(16))) float preL[kFinTok][4];
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, e = l & 15, g = l >> 4;
+    const int64_t tg = blockIdx.x / splits;
+    const int sp = blockIdx.x - (int)(tg * splits);
+    const int64_t t = tg * kFinTok + w;
+    const bool tv = t < a.n;
+    const int64_t tok_bytes = (int64_t)a.GP * kChunks * 16;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<char*>(a.part) + (tv ? t : 0) * tok_bytes, 0, tv ? (int)tok_bytes : 0, kBufDword3);
+    u32x4 v[kXL];
+#pragma unroll
+    for (int s = 0; s < kXL; ++s) {
+        const int m = 4 * s + g;
+        const int off = (e < kChunks && m < a.G) ? (m * kChunks + e) * 16 : kOOB;
+        v[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    }
+    const float x0 = member_sum(v, 0), x1 = member_sum(v, 1), x2 = member_sum(v, 2);
+    if (l < kChunks) {
+        sums[w][l][0] = x0;
+        sums[w][l][1] = x1;
+        sums[w][l][2] = x2;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");     // the wave reads back its own LDS writes
+    {
+        const int f = l < kMix ? l : 0;
+        int ch, sl;
+        field_pos(f, ch, sl);
+        const float m = mix_value(sums[w][ch][sl], mix_scale(sums[w][1][1], sums[w][1][2], a.K, a.norm_eps));
+        if (l < kMix) mixL[w][l] = m;
+        if (a.mixes && sp == 0 && tv && l < kMix) a.mixes[t * kMix + l] = m;
+    }
+    if (!FUSED) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const float s0 = a.scale[0];
+    if (l < kHC) preL[w][l] = pre_gate(mixL[w][l], s0, a.base[l], a.eps);
+    __syncthreads();
+    if (sp == 0) {
+        // the split + Sinkhorn of token t (all four 16-lane rows compute it;
+        // row 0 writes)
+        float p, q, cc;
+        split_sinkhorn16(&mixL[w][0], s0, a.scale[1], a.scale[2], a.base, a.iters, a.eps, p, q, cc);
+        if (tv && l < 16) {
+            a.comb[t * (kHC * kHC) + e] = cc;
+            if (e < kHC) {
+                a.post[t * kHC + e] = q;
+                if (a.pre) a.pre[t * kHC + e] = p;
+            }
+        }
+    }
+    // h of this block's tokens, column part sp
+    const int d8 = a.d / 8;
+    const int cs = d8 / splits;
+    const int64_t t0 = tg * kFinTok;
+    int64_t nt = a.n - t0;
+    nt = nt > kFinTok ? kFinTok : nt;
+    const int items = (int)nt * cs;
+    const u32x4* R = reinterpret_cast<const u32x4*>(a.R);
+    u32x4* h = reinterpret_cast<u32x4*>(a.h);
+    for (int i = threadIdx.x; i < items; i += 256) {
+        const int tk = i / cs;
+        const int c8 = sp * cs + (i - tk * cs);
+        const int64_t tt = t0 + tk;
+        const f32x4 p = *reinterpret_cast<const f32x4*>(&preL[tk][0]);
+        const int64_t row = tt * kHC * (int64_t)d8 + c8;
+        const u32x4 r0 = __builtin_nontemporal_load(R + row);
+        const u32x4 r1 = __builtin_nontemporal_load(R + row + d8);
+        const u32x4 r2 = __builtin_nontemporal_load(R + row + 2 * (int64_t)d8);
+        const u32x4 r3 = __builtin_nontemporal_load(R + row + 3 * (int64_t)d8);
+        __builtin_nontemporal_store(pre_chunk8(p, r0, r1, r2, r3), h + tt * d8 + c8);
+    }
+}
+
 }  // namespace spec
 
 // Header update and record-area clearing before a call of the cooperative
@@ -1335,6 +1537,16 @@ static int pow2_at_least(int x) {
     return p;
 }
 
+// Calls of at most this many tokens (at widths the wave-specialised kernel
+// serves) take the two-pass path.
+#ifndef HC_TWO_PASS_MAX_N
+#define HC_TWO_PASS_MAX_N 2048
+#endif
+constexpr int64_t kTwoPassMaxN = HC_TWO_PASS_MAX_N;
+
+// Wave-specialised kernel: groups of 8..32 members.
+static bool spec_width(int G) { return G >= 8 && G <= 32; }
+
 bool coop_plan(int64_t n, int d, CoopPlan& p) {
     const int KS = coop_ks(d);
     if (!KS) return false;
@@ -1342,11 +1554,23 @@ bool coop_plan(int64_t n, int d, CoopPlan& p) {
     p.G = d / (32 * KS);
     p.TM = kTT;
     p.ntiles = (n + kT - 1) / kT;
-    int ng = num_cus() / p.G;
+    const int cus = num_cus();
+    int ng = cus / p.G;
     if (ng < 1) ng = 1;
     if (ng > p.ntiles) ng = (int)(p.ntiles > 0 ? p.ntiles : 1);
     p.NG = ng;
     p.ws_part = 256;
+    p.two_pass = spec_width(p.G) && n <= kTwoPassMaxN;
+    p.splits = 1;
+    if (p.two_pass) {
+        // records [n][GP][9] of 16 bytes; nothing else in the workspace
+        p.ws_mix = p.ws_part + (size_t)n * pow2_at_least(p.G) * kChunks * 16;
+        p.ws_bytes = (p.ws_mix + 255) & ~(size_t)255;
+        const int64_t blocks = (n + spec::kFinTok - 1) / spec::kFinTok;
+        const int d8 = d / 8;
+        while (blocks * p.splits < 2 * cus && p.splits < 8 && d8 % (2 * p.splits) == 0) p.splits *= 2;
+        return true;
+    }
     p.ws_mix = p.ws_part + (size_t)p.NG * kSlots * kChunks * kT * pow2_at_least(p.G) * 16;
     p.ws_bytes = p.ws_mix + (((size_t)n * kMix * sizeof(float) + 255) & ~(size_t)255);
     return true;
@@ -1369,8 +1593,18 @@ static int launch_ks(const CoopPlan& p, CoopArgs& a, bool fused, hipStream_t s) 
     return fused ? launch_t<KS, 8, true>(p, a, s) : launch_t<KS, 8, false>(p, a, s);
 }
 
-// Wave-specialised kernel: groups of 8..32 members.
-static bool use_spec(const CoopPlan& p) { return p.G >= 8 && p.G <= 32; }
+static bool use_spec(const CoopPlan& p) { return spec_width(p.G); }
+
+template <int KS>
+static int launch_two_pass(const CoopPlan& p, CoopArgs& a, bool fused, hipStream_t s) {
+    spec::k_part<KS><<<p.G * p.NG, spec::kMW * 64, 0, s>>>(a);
+    if (hipGetLastError() != hipSuccess) return -1;
+    const int splits = fused ? p.splits : 1;
+    const int64_t blocks = (a.n + spec::kFinTok - 1) / spec::kFinTok * splits;
+    if (fused) spec::k_fin<true><<<(unsigned)blocks, 256, 0, s>>>(a, splits);
+    else spec::k_fin<false><<<(unsigned)blocks, 256, 0, s>>>(a, splits);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 template <int KS>
 static int launch_spec(const CoopPlan& p, CoopArgs& a, bool fused, hipStream_t s) {
@@ -1410,6 +1644,18 @@ int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* s
     a.part_bytes = (int)(p.ws_mix - p.ws_part);
     a.call = g_calls.fetch_add(1, std::memory_order_relaxed) + 1;
     int rc = -1;
+    if (p.two_pass) {
+        // mixes go only where the caller asked for them; pass 2 does the split
+        a.mixes = mixes;
+        switch (p.KS) {
+            case 1: return launch_two_pass<1>(p, a, fused, s);
+            case 2: return launch_two_pass<2>(p, a, fused, s);
+            case 3: return launch_two_pass<3>(p, a, fused, s);
+            case 4: return launch_two_pass<4>(p, a, fused, s);
+            case 5: return launch_two_pass<5>(p, a, fused, s);
+        }
+        return -1;
+    }
     if (!use_spec(p)) {
         k_init<<<1, 1024, 0, s>>>(a.hdr, a.part, (int64_t)(a.part_bytes / 16), a.call);
         if (hipGetLastError() != hipSuccess) return -1;

@@ -61,6 +61,41 @@ __device__ __forceinline__ float f32_mid(double y, bool& mid) {
 // Pack two bf16 bit patterns into one word (element 0 low).
 __device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
 
+// h of one 16-byte chunk (8 consecutive features) from the four streams'
+// chunks r0..r3 and the token's pre p ("Mix projection" page, Block.hc_pre):
+// each output is the correctly rounded bf16 of sum_k p_k R_k, accumulated in
+// double (every product is exact there) in the fixed order p0 R0 + p1 R1 +
+// p2 R2 + p3 R3.  A wave redoes its chunks with bf16_rn_f64 when any lane
+// hit a float halfway point, so the result does not depend on the path.
+__device__ __forceinline__ u32x4 pre_chunk8(const f32x4 p, const u32x4 r0, const u32x4 r1, const u32x4 r2,
+                                            const u32x4 r3) {
+    const double p0 = p[0], p1 = p[1], p2 = p[2], p3 = p[3];
+    // element e of word w (e = 0: low half): sum over the 4 streams
+    auto sum = [&](int w, int e) {
+        auto v = [&](uint32_t word) { return (double)(e ? bf_hi(word) : bf_lo(word)); };
+        double y = p0 * v(r0[w]);
+        y = __builtin_fma(p1, v(r1[w]), y);
+        y = __builtin_fma(p2, v(r2[w]), y);
+        return __builtin_fma(p3, v(r3[w]), y);
+    };
+    u32x4 out;
+    float f[4][2];
+    bool mid = false;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        f[w][0] = f32_mid(sum(w, 0), mid);
+        f[w][1] = f32_mid(sum(w, 1), mid);
+    }
+    if (__builtin_amdgcn_ballot_w64(mid)) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) out[w] = pack2(bf16_rn_f64(sum(w, 0)), bf16_rn_f64(sum(w, 1)));
+    } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) out[w] = pack2(bf16_rn(f[w][0]), bf16_rn(f[w][1]));
+    }
+    return out;
+}
+
 // ------------------------------------------------ 16-lane row reductions
 // DPP controls (gfx9 encoding): quad_perm patterns and row_ror 4 / 8, all of
 // which read a lane inside the same row, so no lane is out of bounds and

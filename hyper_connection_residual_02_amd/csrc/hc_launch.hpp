@@ -33,6 +33,8 @@ struct CoopPlan {
     size_t ws_part;  // byte offsets into the workspace: exchange records
     size_t ws_mix;   // mixes of every token when the caller does not keep them
     size_t ws_bytes;
+    bool two_pass;   // short run: k_part + k_fin instead of the persistent kernel
+    int splits;      // two-pass: column parts of h per block of 4 tokens
 };
 // K-steps per wave for d (0: d cannot be tiled).  Host only, no HIP calls.
 int coop_ks(int d);

@@ -49,35 +49,12 @@ __global__ __launch_bounds__(256) void k_pre(const u32x4* __restrict__ R, const 
         item_of(it, map.d8, t, c8);
         if (UNIFORM) t = __builtin_amdgcn_readfirstlane((uint32_t)t) | ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(t >> 32)) << 32);
         const f32x4 p = *reinterpret_cast<const f32x4*>(pre + t * kHC);
-        const double p0 = p[0], p1 = p[1], p2 = p[2], p3 = p[3];
         const uint64_t row = t * kHC * (uint64_t)map.d8 + c8;
         const u32x4 r0 = __builtin_nontemporal_load(R + row);
         const u32x4 r1 = __builtin_nontemporal_load(R + row + map.d8);
         const u32x4 r2 = __builtin_nontemporal_load(R + row + 2 * (uint64_t)map.d8);
         const u32x4 r3 = __builtin_nontemporal_load(R + row + 3 * (uint64_t)map.d8);
-        // element e of word w (e = 0: low half): sum over the 4 streams
-        auto sum = [&](int w, int e) {
-            auto v = [&](uint32_t word) { return (double)(e ? bf_hi(word) : bf_lo(word)); };
-            double y = p0 * v(r0[w]);
-            y = __builtin_fma(p1, v(r1[w]), y);
-            y = __builtin_fma(p2, v(r2[w]), y);
-            return __builtin_fma(p3, v(r3[w]), y);
-        };
-        u32x4 out;
-        float f[4][2];
-        bool mid = false;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            f[w][0] = f32_mid(sum(w, 0), mid);
-            f[w][1] = f32_mid(sum(w, 1), mid);
-        }
-        if (__builtin_amdgcn_ballot_w64(mid)) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) out[w] = pack2(bf16_rn_f64(sum(w, 0)), bf16_rn_f64(sum(w, 1)));
-        } else {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) out[w] = pack2(bf16_rn(f[w][0]), bf16_rn(f[w][1]));
-        }
+        const u32x4 out = pre_chunk8(p, r0, r1, r2, r3);
         __builtin_nontemporal_store(out, h + t * map.d8 + c8);
     }
 }

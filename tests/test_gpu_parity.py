@@ -220,6 +220,30 @@ def test_determinism_and_batch_invariance():
         assert torch.equal(u[:, 1000:1100], v)
 
 
+TWO_PASS_MAX_N = 2048   # calls of at most this many tokens take the two-pass path
+
+
+@pytest.mark.parametrize("d", [256, 1024, 2048, 3072, 4096, 5120])
+def test_two_pass_and_persistent_paths_agree_bitwise(d):
+    # A call of at most 2,048 tokens (at the widths the wave-specialised
+    # kernel serves) runs as two ordinary launches: per-member partial sums,
+    # then the reduction, split and h.  A longer call runs the persistent
+    # kernel.  A token gets bitwise the same mixes, pre, post, comb and h
+    # either way, and hc_mixes alone gives the same mixes.
+    n = TWO_PASS_MAX_N + 52
+    w = hin.Workload("w%d" % d, 1, n, 4, d, 1.0 / np.sqrt(4 * d), 0.5, 2.0, 1.0)
+    t = hin.make_inputs(w, DEV, seed=43)
+    full = run_fused(t["R"], t["W"], t["scale"], t["base"])
+    for lo, hi in [(0, 1), (7, 40), (52, n), (n - 3, n)]:
+        sub = t["R"][:, lo:hi].contiguous()
+        part = run_fused(sub, t["W"], t["scale"], t["base"])
+        for name, u, v in zip(("h", "pre", "post", "comb", "mixes"), full, part):
+            assert torch.equal(u[:, lo:hi], v), (d, lo, hi, name)
+        m = hcl.hc_mixes(sub, t["W"])
+        torch.cuda.synchronize()
+        assert torch.equal(full[4][:, lo:hi], m), (d, lo, hi, "hc_mixes")
+
+
 def test_workspace_reused_across_shapes():
     # one workspace through calls of different sizes and widths, mixes kept
     # in the workspace: every result equals that of a fresh workspace
@@ -241,14 +265,17 @@ def test_workspace_reused_across_shapes():
 
 
 def test_workspace_shared_by_both_projection_kernels():
-    # one workspace alternated between widths served by the wave-specialised
-    # kernel (d = 5120, 2048: it prepares the workspace header itself) and by
-    # the cooperative kernel (d = 64, 8192: a separate preparation launch),
-    # fused and standalone calls mixed: every result equals that of a fresh
-    # workspace, so no record of one call is ever taken for another's
+    # one workspace alternated between the wave-specialised kernel (d = 5120,
+    # 2048 with more than 2,048 tokens: it prepares the workspace header
+    # itself), the two-pass path (the same widths, fewer tokens: untagged
+    # records) and the cooperative kernel (d = 64, 8192: a separate
+    # preparation launch), fused and standalone calls mixed: every result
+    # equals that of a fresh workspace, so no record of one call is ever
+    # taken for another's
     shapes = []
-    for i, d in enumerate([5120, 64, 2048, 8192, 5120, 64, 8192, 2048, 5120]):
-        w = hin.Workload("d%d" % d, 1, 97 + 31 * i, 4, d, 1.0 / np.sqrt(4 * d), 0.5, 2.0, 1.0)
+    for i, (d, n) in enumerate([(5120, 2100), (64, 128), (2048, 97), (8192, 159), (5120, 190), (64, 221),
+                                (8192, 252), (2048, 2300), (5120, 2200), (5120, 60)]):
+        w = hin.Workload("d%d" % d, 1, n, 4, d, 1.0 / np.sqrt(4 * d), 0.5, 2.0, 1.0)
         shapes.append(hin.make_inputs(w, DEV, seed=40 + i))
     shared = hcl.Workspace()
     for i, t in enumerate(shapes):
