@@ -908,30 +908,79 @@ __device__ __forceinline__ int srec_off(const CoopArgs& a, const RoundCtx& c, in
     return (((c.g * kSlots + slot) * a.GP + member) * kRecMember + rec) * 16;
 }
 
+// Where the two records a lane publishes per round come from: for record p
+// of the lane (p = 0, 1) and slot sl, the offset of its field in one MFMA
+// wave's partials (token * kRed + field; field 0 for the empty slot), and a
+// bit per (p, sl) telling whether the slot holds a field.  Computed once
+// before the round loop, so that the publication's LDS reads carry no
+// per-lane branches and issue back to back.
+struct PubMap {
+    int off[2][3];
+    uint32_t live;
+};
+
+// rec_of(id, tk, ch): token and chunk of record id of a member's round.
+template <typename RecOf>
+__device__ __forceinline__ PubMap pub_map(RecOf rec_of) {
+    PubMap m;
+    m.live = 0u;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int idx = p * (kMW * 64) + (int)threadIdx.x;
+        const int id = idx < kRecMember ? idx : 0;      // lanes past the records compute record 0, dropped
+        int tk, ch;
+        rec_of(id, tk, ch);
+#pragma unroll
+        for (int sl = 0; sl < 3; ++sl) {
+            const int fi = field_at(ch, sl);
+            m.off[p][sl] = tk * kRed + (fi >= 0 ? fi : 0);
+            if (fi >= 0) m.live |= 1u << (3 * p + sl);
+        }
+    }
+    return m;
+}
+
+// Record p of the lane for the partials of round parity b: the four MFMA
+// waves' partials of each field added in wave order.
+template <int KS>
+__device__ __forceinline__ u32x4 pub_value(const Lds<KS>& L, int b, const PubMap& m, int p) {
+    const float* red = &L.red[b][0][0][0];
+    constexpr int kW = kT * kRed;          // floats between two waves' partials
+    float x[3];
+#pragma unroll
+    for (int sl = 0; sl < 3; ++sl) {
+        const int o = m.off[p][sl];
+        x[sl] = ((red[o] + red[o + kW]) + red[o + 2 * kW]) + red[o + 3 * kW];
+    }
+    // every lane uses all three sums here, so the compiler cannot move the
+    // reads under the per-lane selects below (it would branch around each)
+    asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]));
+    u32x4 v;
+#pragma unroll
+    for (int sl = 0; sl < 3; ++sl) v[sl] = (m.live >> (3 * p + sl)) & 1u ? __float_as_uint(x[sl]) : 0u;
+    v[3] = 0u;
+    return v;
+}
+
+// Token and chunk of record id in this kernel's member-major order.
+__device__ __forceinline__ void srec_of(int id, int& tk, int& ch) {
+    const int q = id - kRecPre;
+    tk = id < kRecPre ? id >> 1 : q / (kChunks - 2);
+    ch = id < kRecPre ? id & 1 : 2 + (q - (kChunks - 2) * (q / (kChunks - 2)));
+}
+
 // Records of round r from the partials of the four MFMA waves (two store
 // instructions per wave, always; past the group's rounds they are dropped).
 // Lane idx writes record idx of this member.
 template <int KS, bool LOCAL>
-__device__ __forceinline__ void m_publish(const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, int r) {
+__device__ __forceinline__ void m_publish(const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, const PubMap& M,
+                                          int r) {
     const int tid = threadIdx.x;
-    const int b = r & 1;
     const bool live = r >= 0 && r < c.nr;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int idx = p * (kMW * 64) + tid;
-        const int id = idx < kRecMember ? idx : 0;      // lanes past the records compute record 0, dropped
-        const int q = id - kRecPre;
-        const int tk = id < kRecPre ? id >> 1 : q / (kChunks - 2);
-        const int ch = id < kRecPre ? id & 1 : 2 + (q - (kChunks - 2) * (q / (kChunks - 2)));
-        u32x4 v;
-#pragma unroll
-        for (int sl = 0; sl < 3; ++sl) {
-            const int fi = field_at(ch, sl);
-            float x = 0.0f;
-            if (fi >= 0)
-                x = ((L.red[b][0][tk][fi] + L.red[b][1][tk][fi]) + L.red[b][2][tk][fi]) + L.red[b][3][tk][fi];
-            v[sl] = __float_as_uint(x);
-        }
+        u32x4 v = pub_value<KS>(L, r & 1, M, p);
         v[3] = tag_of(c, r);
         st_rec<LOCAL>(c, live && idx < kRecMember ? srec_off(a, c, r, c.q, idx) : kOOB, v);
     }
@@ -942,31 +991,40 @@ template <int KS>
 __device__ __forceinline__ void m_mfma(const MState<KS>& S, const RoundCtx& c, Lds<KS>& L, int r) {
     const uint8_t* slot = &L.slot[r % kNSlot][0];
     const int b = r & 1;
+    auto operand = [&](int tt, int st) {
+        return *reinterpret_cast<const u32x4*>(slot + (16 * tt + c.row) * Geo<KS>::kRowB + c.w * (64 * KS) +
+                                              64 * st + 16 * c.grp);
+    };
+    // the products of both 16-token tiles go to the matrix core before
+    // either tile's sums are read back, so that the read-back of one
+    // overlaps the other's products (each accumulator sees the k-steps in
+    // the same order as before)
+    f32x4 accs[kTT][kTiles], sqs[kTT];
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
-        f32x4 acc[kTiles];
 #pragma unroll
-        for (int ct = 0; ct < kTiles; ++ct) acc[ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        f32x4 sq = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        auto operand = [&](int st) {
-            return *reinterpret_cast<const u32x4*>(slot + (16 * tt + c.row) * Geo<KS>::kRowB + c.w * (64 * KS) +
-                                                  64 * st + 16 * c.grp);
-        };
+        for (int ct = 0; ct < kTiles; ++ct) accs[tt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        sqs[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int st = 0; st < KS; ++st) {
-            const u32x4 av = operand(st);
+            const u32x4 av = operand(tt, st);
             const bf16x8 ab = __builtin_bit_cast(bf16x8, av);
 #pragma unroll
             for (int ct = 0; ct < kTiles; ++ct)
-                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, S.w[st][ct], acc[ct], 0, 0, 0);
-            sq_step(av, sq);
+                accs[tt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, S.w[st][ct], accs[tt][ct], 0, 0, 0);
+            sq_step(av, sqs[tt]);
         }
+    }
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt) {
+        const f32x4* acc = accs[tt];
+        const f32x4 sq = sqs[tt];
         {
             const float ss = sq[c.row & 3];
             const float sb = scaled_sum(c.row, c.grp, ss, [&] {
                 f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int st = 0; st < KS; ++st) sq_step_scaled(operand(st), v);
+                for (int st = 0; st < KS; ++st) sq_step_scaled(operand(tt, st), v);
                 return v;
             });
             if ((c.row >> 2) == c.grp) {
@@ -1202,6 +1260,7 @@ __device__ __forceinline__ void spec_body(const CoopArgs& a, const RoundCtx& c, 
     if (c.w < kMW) {
         MState<KS> S;
         m_setup<KS>(S, a, c);
+        const PubMap M = pub_map(srec_of);
         m_dma<KS>(S, a, c, L, 0);
         m_dma<KS>(S, a, c, L, 1);
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW) : "memory");   // round 0 landed
@@ -1209,7 +1268,7 @@ __device__ __forceinline__ void spec_body(const CoopArgs& a, const RoundCtx& c, 
         for (int t = 0;; ++t) {
             // records first (peers are waiting for them), then the residual
             // of round t+2, then the products of round t
-            m_publish<KS, LOCAL>(a, c, L, t - 1);
+            m_publish<KS, LOCAL>(a, c, L, M, t - 1);
             m_dma<KS>(S, a, c, L, t + 2);
             m_mfma<KS>(S, c, L, t);
             // round t+1 (issued last tick, its loads the youngest memory
@@ -1355,9 +1414,9 @@ constexpr int kFinTok = 4;      // tokens per k_fin block (one reducing wave eac
 // wait count of the loop depends on it).  Rounds past the group's end store
 // nothing.
 template <int KS>
-__device__ __forceinline__ void p_publish(const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, int r) {
+__device__ __forceinline__ void p_publish(const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, const PubMap& M,
+                                          int r) {
     const int tid = threadIdx.x;
-    const int b = r & 1;
     const bool live = r >= 0 && r < c.nr;
     const int64_t tok0 = live ? tile_of(c, a, r) * kT : 0;
     int64_t valid = live ? a.n - tok0 : 0;
@@ -1368,22 +1427,19 @@ __device__ __forceinline__ void p_publish(const CoopArgs& a, const RoundCtx& c, 
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int idx = p * (kMW * 64) + tid;
-        const int id = idx < kT * kChunks ? idx : 0;
-        const int tk = id / kChunks, ch = id - tk * kChunks;
-        u32x4 v;
-#pragma unroll
-        for (int sl = 0; sl < 3; ++sl) {
-            const int fi = field_at(ch, sl);
-            float x = 0.0f;
-            if (fi >= 0)
-                x = ((L.red[b][0][tk][fi] + L.red[b][1][tk][fi]) + L.red[b][2][tk][fi]) + L.red[b][3][tk][fi];
-            v[sl] = __float_as_uint(x);
-        }
-        v[3] = 0u;
-        const int off = idx < kT * kChunks ? ((tk * a.GP + c.q) * kChunks + ch) * 16 : kOOB;
+        const int tk = idx / kChunks, ch = idx - tk * kChunks;
+        const u32x4 v = pub_value<KS>(L, r & 1, M, p);
+        const int off = idx < kRecMember ? ((tk * a.GP + c.q) * kChunks + ch) * 16 : kOOB;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((__vector_size__(16))) int, v), rs,
                                                off, 0, 0);
     }
+}
+
+// Token and chunk of record id of a member's round in the two-pass record
+// order (token-major).
+__device__ __forceinline__ void prec_of(int id, int& tk, int& ch) {
+    tk = id / kChunks;
+    ch = id - tk * kChunks;
 }
 
 // Pass 1: workgroup b is member b % G of tile group b / G (tiles g, g + NG,
@@ -1408,12 +1464,13 @@ __global__ __launch_bounds__(kMW * 64, 1) void k_part(CoopArgs a) {
     c.bpre = 0.0f;
     MState<KS> S;
     m_setup<KS>(S, a, c);
+    const PubMap M = pub_map(prec_of);
     m_dma<KS>(S, a, c, L, 0);
     m_dma<KS>(S, a, c, L, 1);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW) : "memory");   // round 0 landed
     __syncthreads();
     for (int t = 0;; ++t) {
-        p_publish<KS>(a, c, L, t - 1);
+        p_publish<KS>(a, c, L, M, t - 1);
         m_dma<KS>(S, a, c, L, t + 2);
         m_mfma<KS>(S, c, L, t);
         // round t+1 in LDS: younger than its loads are only this tick's two
@@ -1427,7 +1484,11 @@ __global__ __launch_bounds__(kMW * 64, 1) void k_part(CoopArgs a) {
 }
 
 // Pass 2: block b covers tokens kFinTok*(b / splits) .. +3 and column part
-// b % splits of h.  Wave w reduces token kFinTok*(b / splits) + w.
+// b % splits of h.  Wave w reduces token kFinTok*(b / splits) + w.  Each
+// thread issues the residual loads of its first h chunk before the
+// reduction (they do not depend on it), and the split + Sinkhorn, which
+// only blocks of column part 0 run, comes after h, so its latency overlaps
+// the h stores.
 template <bool FUSED>
 __global__ __launch_bounds__(256) void k_fin(CoopArgs a, int splits) {
     __shared__ float sums[kFinTok][kChunks][4];
@@ -1438,6 +1499,32 @@ __global__ __launch_bounds__(256) void k_fin(CoopArgs a, int splits) {
     const int sp = blockIdx.x - (int)(tg * splits);
     const int64_t t = tg * kFinTok + w;
     const bool tv = t < a.n;
+
+    // h chunks of this block: item i is token i / cs of the block, chunk
+    // sp * cs + i % cs of d / 8
+    const int d8 = a.d / 8;
+    const int cs = d8 / splits;
+    const int64_t t0 = tg * kFinTok;
+    const int64_t nt = a.n - t0 < kFinTok ? a.n - t0 : kFinTok;
+    const int items = FUSED ? (int)nt * cs : 0;
+    const u32x4* R = reinterpret_cast<const u32x4*>(a.R);
+    int i = threadIdx.x;
+    int tk = 0;
+    int64_t row = 0, hrow = 0;
+    u32x4 r0, r1, r2, r3;
+    auto fetch = [&]() {
+        tk = i / cs;
+        const int c8 = sp * cs + (i - tk * cs);
+        row = (t0 + tk) * kHC * (int64_t)d8 + c8;
+        hrow = (t0 + tk) * d8 + c8;
+        r0 = __builtin_nontemporal_load(R + row);
+        r1 = __builtin_nontemporal_load(R + row + d8);
+        r2 = __builtin_nontemporal_load(R + row + 2 * (int64_t)d8);
+        r3 = __builtin_nontemporal_load(R + row + 3 * (int64_t)d8);
+    };
+    if (i < items) fetch();
+
+    // member sums of token t's records in the exchange order of k_spec
     const int64_t tok_bytes = (int64_t)a.GP * kChunks * 16;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         reinterpret_cast<char*>(a.part) + (tv ? t : 0) * tok_bytes, 0, tv ? (int)tok_bytes : 0, kBufDword3);
@@ -1468,6 +1555,17 @@ __global__ __launch_bounds__(256) void k_fin(CoopArgs a, int splits) {
     const float s0 = a.scale[0];
     if (l < kHC) preL[w][l] = pre_gate(mixL[w][l], s0, a.base[l], a.eps);
     __syncthreads();
+
+    // h of this block's tokens, column part sp
+    u32x4* h = reinterpret_cast<u32x4*>(a.h);
+    while (i < items) {
+        const u32x4 out = pre_chunk8(*reinterpret_cast<const f32x4*>(&preL[tk][0]), r0, r1, r2, r3);
+        const int64_t hr = hrow;
+        i += 256;
+        if (i < items) fetch();
+        __builtin_nontemporal_store(out, h + hr);
+    }
+
     if (sp == 0) {
         // the split + Sinkhorn of token t (all four 16-lane rows compute it;
         // row 0 writes)
@@ -1480,27 +1578,6 @@ __global__ __launch_bounds__(256) void k_fin(CoopArgs a, int splits) {
                 if (a.pre) a.pre[t * kHC + e] = p;
             }
         }
-    }
-    // h of this block's tokens, column part sp
-    const int d8 = a.d / 8;
-    const int cs = d8 / splits;
-    const int64_t t0 = tg * kFinTok;
-    int64_t nt = a.n - t0;
-    nt = nt > kFinTok ? kFinTok : nt;
-    const int items = (int)nt * cs;
-    const u32x4* R = reinterpret_cast<const u32x4*>(a.R);
-    u32x4* h = reinterpret_cast<u32x4*>(a.h);
-    for (int i = threadIdx.x; i < items; i += 256) {
-        const int tk = i / cs;
-        const int c8 = sp * cs + (i - tk * cs);
-        const int64_t tt = t0 + tk;
-        const f32x4 p = *reinterpret_cast<const f32x4*>(&preL[tk][0]);
-        const int64_t row = tt * kHC * (int64_t)d8 + c8;
-        const u32x4 r0 = __builtin_nontemporal_load(R + row);
-        const u32x4 r1 = __builtin_nontemporal_load(R + row + d8);
-        const u32x4 r2 = __builtin_nontemporal_load(R + row + 2 * (int64_t)d8);
-        const u32x4 r3 = __builtin_nontemporal_load(R + row + 3 * (int64_t)d8);
-        __builtin_nontemporal_store(pre_chunk8(p, r0, r1, r2, r3), h + tt * d8 + c8);
     }
 }
 
