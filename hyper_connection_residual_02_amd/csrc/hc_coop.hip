@@ -1180,13 +1180,22 @@ __device__ __forceinline__ void x_h(const u32x2 (&rb)[Geo<KS>::kPass][kHC], cons
                                     Lds<KS>& L, int xw, int r) {
     const int64_t tok0 = tile_of(c, a, r) * kT;
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(a.h, (int64_t)a.d * 2, tok0, a.n, kT);
+    // pre of every pass's token, read from LDS together (one wait, not one
+    // per pass)
+    f32x4 pqs[Geo<KS>::kPass];
+#pragma unroll
+    for (int p = 0; p < Geo<KS>::kPass; ++p) {
+        const int item = p * 64 + c.l;
+        const int it = item < Geo<KS>::kItems ? item : 0;
+        pqs[p] = *reinterpret_cast<const f32x4*>(&L.xpre[xw][it / Geo<KS>::kBlk][0]);
+    }
 #pragma unroll
     for (int p = 0; p < Geo<KS>::kPass; ++p) {
         const int item = p * 64 + c.l;
         const bool valid = item < Geo<KS>::kItems;
         const int it = valid ? item : 0;
         const int tk = it / Geo<KS>::kBlk, b = it - tk * Geo<KS>::kBlk;
-        const f32x4 pq = *reinterpret_cast<const f32x4*>(&L.xpre[xw][tk][0]);
+        const f32x4 pq = pqs[p];
         const double p0 = pq[0], p1 = pq[1], p2 = pq[2], p3 = pq[3];
         auto sum = [&](int w, int e) {
             auto v = [&](uint32_t word) { return (double)(e ? bf_hi(word) : bf_lo(word)); };
