@@ -62,8 +62,9 @@ def measured_traffic(kernel: str, n: int, d: int):
     return rec.get("bytes_per_launch")
 
 
-# the projection kernel of d = 5120 (wave-specialised), that of other widths,
-# and hc_post's kernel
+# the projection kernel of d = 5120 (wave-specialised, calls of more than
+# 2,048 tokens), that of other widths, and hc_post's kernel; shorter calls
+# run the two-pass pair k_part + k_fin (summarised together)
 KERNELS = {"k_spec": "hc_fused_mix_pre", "k_coop": "hc_fused_mix_pre", "k_post": "hc_post"}
 COPY_CALIB_BYTES = 1 << 30
 
@@ -174,6 +175,18 @@ def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, step
             short, r["Calls"], avg, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
             "%.1f" % gbs if gbs else "-", "%.3f" % (gbs / HBM_PEAK_GBS) if gbs else "-",
             "%.2f" % t if t else "-", "%.3f" % (tg / HBM_PEAK_GBS) if tg else "-"))
+    # calls of up to 2,048 tokens run the fused entry point as two launches
+    part = [r for r in rows if "::k_part<" in r["Name"]]
+    fin = [r for r in rows if "::k_fin<true>" in r["Name"]]
+    if part and fin:
+        avg = (float(part[0]["AverageNs"]) + float(fin[0]["AverageNs"])) / 1e3
+        gbs = fb / (avg * 1e-6) / 1e9
+        tp, tf = timed.get(part[0]["Name"]), timed.get(fin[0]["Name"])
+        t = tp + tf if (tp and tf) else None
+        tg = fb / (t * 1e-6) / 1e9 if t else None
+        lines.append("| k_part + k_fin (hc_fused_mix_pre, two-pass) | %s | %.2f | - | - | %.1f | %.3f | %s | %s |" % (
+            part[0]["Calls"], avg, gbs, gbs / HBM_PEAK_GBS, "%.2f" % t if t else "-",
+            "%.3f" % (tg / HBM_PEAK_GBS) if tg else "-"))
     lines.append("")
     if steps:
         lines.append("Timed region: dispatches %d .. %d of each kernel (after %d warmup steps)."

@@ -107,13 +107,18 @@ const char *hc_version(void);
  * something else).  Calls that may run at the same time, on different
  * streams, each need their own workspace.
  *
- * The kernel is an ordinary launch whose grid (at most one workgroup per
- * compute unit) fits the device at once; its workgroups wait for each
- * other's partial sums.  Every such wait is bounded: a workgroup that is
- * not resident within about two seconds (say, while long-running work on
- * another stream holds compute units), or a peer that stops, makes the
- * kernel stop early and set an error word in the workspace header; outputs
- * are then undefined.
+ * Calls of more than 2,048 tokens (and every call at widths outside the
+ * d = 5120 family) run one ordinary launch whose grid (at most one
+ * workgroup per compute unit) fits the device at once; its workgroups wait
+ * for each other's partial sums.  Every such wait is bounded: a workgroup
+ * that is not resident within about two seconds (say, while long-running
+ * work on another stream holds compute units), or a peer that stops, makes
+ * the kernel stop early and set an error word in the workspace header;
+ * outputs are then undefined.  Shorter calls at widths d = 32*k*G with
+ * 8 <= G <= 32 (d = 5120 among them) run two ordinary launches with no
+ * waits between workgroups: the partial sums go through the workspace.
+ * Both give bitwise the same results for a token, so a token's mixes do not
+ * depend on how many tokens share its call.
  */
 int hc_mixes(const void *R, const float *hc_fn, float *mixes, int64_t n,
              int32_t hc, int32_t d, float norm_eps, void *workspace,
@@ -164,8 +169,11 @@ int hc_post(const void *x, const void *R, const float *post,
  * NULL they are kept in the workspace).  Same constraints on d as
  * hc_mixes; the same workspace rules.  The coefficients are bitwise those
  * of hc_mixes followed by hc_split_sinkhorn, and h is bitwise hc_pre's for
- * those coefficients.  Launches three kernels on `stream`: a header
- * update, the projection with pre and h, and the split of post and comb.
+ * those coefficients.  Launches two kernels on `stream`: the projection
+ * with pre and h, then the split of post and comb (calls of more than
+ * 2,048 tokens), or the partial sums, then their reduction with the split
+ * and h (shorter calls); widths outside the d = 5120 family add a workspace
+ * header update before the projection.
  */
 int hc_fused_mix_pre(const void *R, const float *hc_fn,
                      const float *hc_scale, const float *hc_base, void *h,
