@@ -1474,17 +1474,31 @@ __global__ __launch_bounds__(kMW * 64, 1) void k_part(CoopArgs a) {
     MState<KS> S;
     m_setup<KS>(S, a, c);
     const PubMap M = pub_map(prec_of);
+    // rounds past the group's last are neither loaded nor multiplied (a
+    // call of a few tokens has one round per group); each wait below still
+    // covers the loads of every round that is used
     m_dma<KS>(S, a, c, L, 0);
-    m_dma<KS>(S, a, c, L, 1);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW) : "memory");   // round 0 landed
+    if (1 < c.nr) {
+        m_dma<KS>(S, a, c, L, 1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW) : "memory");   // round 0 landed
+    } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
     for (int t = 0;; ++t) {
         p_publish<KS>(a, c, L, M, t - 1);
-        m_dma<KS>(S, a, c, L, t + 2);
-        m_mfma<KS>(S, c, L, t);
-        // round t+1 in LDS: younger than its loads are only this tick's two
-        // record stores and the loads of round t+2
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW + 2) : "memory");
+        if (t + 2 < c.nr) {
+            m_dma<KS>(S, a, c, L, t + 2);
+            m_mfma<KS>(S, c, L, t);
+            // round t+1 in LDS: younger than its loads are only this tick's
+            // two record stores and the loads of round t+2
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW + 2) : "memory");
+        } else {
+            if (t < c.nr) m_mfma<KS>(S, c, L, t);
+            // younger than round t+1's loads (if any) are only this tick's
+            // two record stores
+            asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        }
         __syncthreads();
         if (t >= c.nr) break;          // tick nr published the last round
     }
