@@ -104,7 +104,7 @@ def test_fused_and_post_large_sampled(orc):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("n", [1, 2, 15, 16, 17, 31, 33, 63, 100, 255, 257, 4095, 4097])
+@pytest.mark.parametrize("n", [1, 2, 15, 16, 17, 31, 33, 63, 100, 255, 257, 2048, 2049, 4095, 4097])
 def test_ragged_token_counts(orc, n):
     w = hin.WORKLOADS["prefill"]
     t = hin.make_inputs(w, DEV, seed=7, n_tokens=n)
