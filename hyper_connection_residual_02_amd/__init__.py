@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "HCError", "load", "lib_path", "hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post",
-    "hc_fused_mix_pre", "hc_diag_scale", "hc_fused_workspace_bytes", "Workspace",
+    "hc_fused_mix_pre", "hc_post_mix_pre", "hc_diag_scale", "hc_fused_workspace_bytes", "Workspace",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -60,6 +60,7 @@ def load():
         "hc_pre": [P, P, P, I64, I32, I32, P],
         "hc_post": [P, P, P, P, P, I64, I32, I32, P],
         "hc_fused_mix_pre": [P, P, P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, F32, F32, P],
+        "hc_post_mix_pre": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, F32, F32, P],
         "hc_diag_scale": [P, P, P, I64, I32, P],
     }
     for name, args in sig.items():
@@ -260,6 +261,48 @@ def hc_fused_mix_pre(R: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tenso
               _ptr(pre), _ptr(post), _ptr(comb), _ptr(mixes), wp, wb, n, hc, d,
               int(sinkhorn_iters), float(hc_eps), float(norm_eps), _stream(dev))
     return h, pre, post, comb, mixes
+
+
+def hc_post_mix_pre(x: torch.Tensor, R: torch.Tensor, post: torch.Tensor, comb: torch.Tensor,
+                    hc_fn: torch.Tensor, hc_scale: torch.Tensor, hc_base: torch.Tensor,
+                    sinkhorn_iters: int = 20, hc_eps: float = 1e-6, norm_eps: float = 1e-20,
+                    want_pre: bool = True, want_mixes: bool = False, workspace: Workspace | None = None,
+                    out_R: torch.Tensor | None = None, out=None):
+    """hc_post of one sublayer, then hc_fused_mix_pre of the next on its
+    output.  Returns (R_out, h, pre or None, post, comb, mixes or None);
+    ``out_R`` may be R itself (in place)."""
+    dev = R.device
+    _check(R, "R", torch.bfloat16)
+    _check(x, "x", torch.bfloat16, dev)
+    _check(post, "post", torch.float32, dev)
+    _check(comb, "comb", torch.float32, dev)
+    for t, nm in ((hc_fn, "hc_fn"), (hc_scale, "hc_scale"), (hc_base, "hc_base")):
+        _check(t, nm, torch.float32, dev)
+    hc = 4
+    lead, n, d = _lead(R, hc)
+    if tuple(x.shape) != tuple(lead) + (d,):
+        raise ValueError("x must be %s" % ((*lead, d),))
+    if tuple(hc_fn.shape) != (HC_MIX, hc * d):
+        raise ValueError("hc_fn must be [24, %d]" % (hc * d))
+    if out_R is None:
+        out_R = torch.empty_like(R)
+    _check(out_R, "out_R", torch.bfloat16, dev)
+    o = dict(out or {})
+    h = o.get("h") if o.get("h") is not None else torch.empty(*lead, d, dtype=torch.bfloat16, device=dev)
+    post2 = o.get("post") if o.get("post") is not None else torch.empty(*lead, hc, dtype=torch.float32, device=dev)
+    comb2 = o.get("comb") if o.get("comb") is not None else torch.empty(*lead, hc, hc, dtype=torch.float32, device=dev)
+    pre2 = o.get("pre")
+    if pre2 is None and want_pre:
+        pre2 = torch.empty(*lead, hc, dtype=torch.float32, device=dev)
+    mixes = o.get("mixes")
+    if mixes is None and want_mixes:
+        mixes = torch.empty(*lead, HC_MIX, dtype=torch.float32, device=dev)
+    wp, wb = _workspace(workspace, hc_fused_workspace_bytes(n, hc, d), dev)
+    with torch.cuda.device(dev):
+        _call("hc_post_mix_pre", _ptr(x), _ptr(R), _ptr(post), _ptr(comb), _ptr(out_R), _ptr(hc_fn),
+              _ptr(hc_scale), _ptr(hc_base), _ptr(h), _ptr(pre2), _ptr(post2), _ptr(comb2), _ptr(mixes),
+              wp, wb, n, hc, d, int(sinkhorn_iters), float(hc_eps), float(norm_eps), _stream(dev))
+    return out_R, h, pre2, post2, comb2, mixes
 
 
 def hc_diag_scale(h: torch.Tensor, D: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:

@@ -208,4 +208,49 @@ int hc_fused_mix_pre(const void* R, const float* hc_fn, const float* hc_scale, c
                : HC_OK;
 }
 
+int hc_post_mix_pre(const void* x, const void* R, const float* post, const float* comb, void* R_out,
+                    const float* hc_fn, const float* hc_scale, const float* hc_base, void* h, float* pre_next,
+                    float* post_next, float* comb_next, float* mixes_next, void* workspace, size_t workspace_bytes,
+                    int64_t n, int32_t hc_, int32_t d, int32_t sinkhorn_iters, float hc_eps, float norm_eps,
+                    void* stream) {
+    if (hc_ == 4 && sinkhorn_iters < 1) return HC_ERR_UNSUPPORTED;
+    if (!finite_nonneg(hc_eps)) return HC_ERR_VALUE;
+    hc::CoopPlan p;
+    int st = coop_common(R, hc_fn, workspace, workspace_bytes, n, hc_, d, norm_eps, p);
+    if (st || n == 0) return st;
+    if (!x || !post || !comb || !R_out || !hc_scale || !hc_base || !h || !post_next || !comb_next)
+        return HC_ERR_NULL;
+    if (!al16(x) || !al16(post) || !al16(comb) || !al16(R_out) || !al4(hc_scale) || !al4(hc_base) || !al16(h) ||
+        !al16(post_next) || !al16(comb_next) || (pre_next && !al16(pre_next)) || (mixes_next && !al16(mixes_next)))
+        return HC_ERR_ALIGN;
+    const uint64_t K = (uint64_t)4 * d;
+    const Span sR = span(R, (uint64_t)n * K * 2), sRo = span(R_out, (uint64_t)n * K * 2);
+    // R_out == R is allowed (the residual updated in place); any other
+    // overlap of R_out with R is not
+    if (R_out != R && overlap(sRo, sR)) return HC_ERR_ALIAS;
+    const Span ins[] = {span(x, (uint64_t)n * d * 2), span(post, (uint64_t)n * 16), span(comb, (uint64_t)n * 64),
+                        span(hc_fn, 24 * K * 4), span(hc_scale, 12), span(hc_base, 96),
+                        span(workspace, p.ws_bytes)};
+    Span outs[6];
+    int no = 0;
+    outs[no++] = sRo;
+    outs[no++] = span(h, (uint64_t)n * d * 2);
+    outs[no++] = span(post_next, (uint64_t)n * 16);
+    outs[no++] = span(comb_next, (uint64_t)n * 64);
+    if (pre_next) outs[no++] = span(pre_next, (uint64_t)n * 16);
+    if (mixes_next) outs[no++] = span(mixes_next, (uint64_t)n * 96);
+    for (int i = 0; i < no; ++i) {
+        for (const Span& s : ins)
+            if (overlap(outs[i], s)) return HC_ERR_ALIAS;
+        if (i > 0 && overlap(outs[i], sR)) return HC_ERR_ALIAS;
+        for (int j = i + 1; j < no; ++j)
+            if (overlap(outs[i], outs[j])) return HC_ERR_ALIAS;
+    }
+    const hc::PostIn prev{x, post, comb, R_out};
+    return hc::launch_coop(p, R, hc_fn, hc_scale, hc_base, h, pre_next, post_next, comb_next, mixes_next, workspace,
+                           n, d, sinkhorn_iters, hc_eps, norm_eps, true, (hipStream_t)stream, &prev)
+               ? HC_ERR_LAUNCH
+               : HC_OK;
+}
+
 }  // extern "C"

@@ -96,6 +96,45 @@ __device__ __forceinline__ u32x4 pre_chunk8(const f32x4 p, const u32x4 r0, const
     return out;
 }
 
+// hc_post of one 16-byte chunk (8 consecutive features) of one token
+// ("Mix projection" page, Block.hc_post): out[k] holds the chunk of output
+// stream k, each element the correctly rounded bf16 of post_k x +
+// sum_j comb[j][k] R_j, accumulated in double (every product is exact
+// there) in the fixed order post_k x, then j = 0..3.  q = post of the token,
+// cb[j] = row j of its comb, xv = the chunk of x, r[j] = the chunk of R_j.
+// Waves in which any lane hit a float halfway point redo their chunks with
+// bf16_rn_f64, so the result does not depend on the path.
+__device__ __forceinline__ void post_chunk8(const f32x4 q, const f32x4 (&cb)[kHC], const u32x4 xv,
+                                            const u32x4 (&r)[kHC], u32x4 (&out)[kHC]) {
+    auto sum = [&](int k, int w, int e) {
+        auto v = [&](uint32_t word) { return (double)(e ? bf_hi(word) : bf_lo(word)); };
+        double y = (double)q[k] * v(xv[w]);
+#pragma unroll
+        for (int j = 0; j < kHC; ++j) y = __builtin_fma((double)cb[j][k], v(r[j][w]), y);
+        return y;
+    };
+    float f[kHC][4][2];
+    bool mid = false;
+#pragma unroll
+    for (int k = 0; k < kHC; ++k)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            f[k][w][0] = f32_mid(sum(k, w, 0), mid);
+            f[k][w][1] = f32_mid(sum(k, w, 1), mid);
+        }
+    if (__builtin_amdgcn_ballot_w64(mid)) {
+#pragma unroll
+        for (int k = 0; k < kHC; ++k)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) out[k][w] = pack2(bf16_rn_f64(sum(k, w, 0)), bf16_rn_f64(sum(k, w, 1)));
+    } else {
+#pragma unroll
+        for (int k = 0; k < kHC; ++k)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) out[k][w] = pack2(bf16_rn(f[k][w][0]), bf16_rn(f[k][w][1]));
+    }
+}
+
 // ------------------------------------------------ 16-lane row reductions
 // DPP controls (gfx9 encoding): quad_perm patterns and row_ror 4 / 8, all of
 // which read a lane inside the same row, so no lane is out of bounds and

@@ -40,8 +40,17 @@ struct CoopPlan {
 int coop_ks(int d);
 // Returns false if d cannot be tiled (d % 32 != 0 or no KS in 1..8 gives G <= 32).
 bool coop_plan(int64_t n, int d, CoopPlan& p);
+// hc_post of the previous sublayer, run ahead of the projection
+// (hc_post_mix_pre): R' = hc_post(x, R, post, comb) goes to Rout, and the
+// projection, pre and h are those of R'.
+struct PostIn {
+    const void* x;
+    const float* post;
+    const float* comb;
+    void* Rout;
+};
 int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* scale, const float* base,
                 void* h, float* pre, float* post, float* comb, float* mixes, void* ws, int64_t n, int d,
-                int iters, float eps, float norm_eps, bool fused, hipStream_t s);
+                int iters, float eps, float norm_eps, bool fused, hipStream_t s, const PostIn* prev = nullptr);
 
 }  // namespace hc

@@ -97,35 +97,8 @@ __global__ __launch_bounds__(256) void k_post(const u32x4* __restrict__ x, const
 #pragma unroll
         for (int j = 0; j < kHC; ++j) cb[j] = *reinterpret_cast<const f32x4*>(comb + (t * kHC + j) * kHC);
         const uint64_t row = t * kHC * (uint64_t)map.d8 + cur.c8;
-        // output stream k, element e of word w: post_k x + sum_j comb[j][k] R_j
-        auto sum = [&](int k, int w, int e) {
-            auto v = [&](uint32_t word) { return (double)(e ? bf_hi(word) : bf_lo(word)); };
-            double y = (double)q[k] * v(cur.xv[w]);
-#pragma unroll
-            for (int j = 0; j < kHC; ++j) y = __builtin_fma((double)cb[j][k], v(cur.r[j][w]), y);
-            return y;
-        };
         u32x4 out[kHC];
-        float f[kHC][4][2];
-        bool mid = false;
-#pragma unroll
-        for (int k = 0; k < kHC; ++k)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                f[k][w][0] = f32_mid(sum(k, w, 0), mid);
-                f[k][w][1] = f32_mid(sum(k, w, 1), mid);
-            }
-        if (__builtin_amdgcn_ballot_w64(mid)) {
-#pragma unroll
-            for (int k = 0; k < kHC; ++k)
-#pragma unroll
-                for (int w = 0; w < 4; ++w) out[k][w] = pack2(bf16_rn_f64(sum(k, w, 0)), bf16_rn_f64(sum(k, w, 1)));
-        } else {
-#pragma unroll
-            for (int k = 0; k < kHC; ++k)
-#pragma unroll
-                for (int w = 0; w < 4; ++w) out[k][w] = pack2(bf16_rn(f[k][w][0]), bf16_rn(f[k][w][1]));
-        }
+        post_chunk8(q, cb, cur.xv, cur.r, out);
 #pragma unroll
         for (int k = 0; k < kHC; ++k) __builtin_nontemporal_store(out[k], Rout + row + k * (uint64_t)map.d8);
         cur = nxt;

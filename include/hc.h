@@ -183,6 +183,34 @@ int hc_fused_mix_pre(const void *R, const float *hc_fn,
                      float hc_eps, float norm_eps, void *stream);
 
 /*
+ * hc_post_mix_pre -- one sublayer boundary: hc_post of sublayer l, then
+ * hc_fused_mix_pre of sublayer l+1 on its output ("Mix projection" page,
+ * Block.hc_post followed by Block.hc_mixes and Block.hc_pre; the coefficients
+ * a sublayer computes are used by the next one, as that page's docstring
+ * puts it):
+ *   R_out = hc_post(x, R, post, comb)                       (sublayer l)
+ *   (h, pre_next, post_next, comb_next, mixes_next)
+ *         = hc_fused_mix_pre(R_out, hc_fn, hc_scale, hc_base)  (sublayer l+1)
+ * x, R, post, comb as for hc_post; hc_fn, hc_scale, hc_base and the outputs
+ * as for hc_fused_mix_pre (pre_next and mixes_next may be NULL).  Results
+ * are bitwise those of the two calls in sequence.  R_out == R is allowed
+ * (the residual updated in place); R_out must not otherwise overlap R, and
+ * no output may overlap an input or another output.  Same constraints on d
+ * and the same workspace (hc_fused_workspace_bytes) as hc_fused_mix_pre.
+ * Calls of at most 2,048 tokens at widths d = 32*k*G with 8 <= G <= 32
+ * apply hc_post while the residual is on chip for the projection (two
+ * launches, R read once); other calls run hc_post and then
+ * hc_fused_mix_pre's kernels.
+ */
+int hc_post_mix_pre(const void *x, const void *R, const float *post,
+                    const float *comb, void *R_out, const float *hc_fn,
+                    const float *hc_scale, const float *hc_base, void *h,
+                    float *pre_next, float *post_next, float *comb_next,
+                    float *mixes_next, void *workspace, size_t workspace_bytes,
+                    int64_t n, int32_t hc, int32_t d, int32_t sinkhorn_iters,
+                    float hc_eps, float norm_eps, void *stream);
+
+/*
  * Bytes of device workspace hc_mixes / hc_fused_mix_pre need for these
  * sizes on the current device (0 for n == 0; 0 with an unsupported shape,
  * in which case the call itself reports the error).  Host-only query.

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert {"hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post", "hc_fused_mix_pre",
+    assert {"hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post", "hc_fused_mix_pre", "hc_post_mix_pre",
             "hc_fused_workspace_bytes", "hc_status_str", "hc_diag_scale"} <= set(names)
     for nm in names:
         assert hasattr(lib, nm), nm
@@ -132,6 +132,29 @@ def test_fused_and_mixes_checks(lib):
     assert m(out=A) == ALIAS
     assert m(wsb=0) == WS
     assert m(hc=5) == UNSUP
+
+
+def test_post_mix_pre_checks(lib):
+    H = 0x74000000
+
+    def f(x=A, R=B, post=C, comb=C + 64, Ro=D_, W=E, s=E + 0x10000, b=E + 0x10040, h=H, pre=H + 0x1000,
+          post2=H + 0x2000, comb2=H + 0x3000, mix=0, ws=F_, wsb=1 << 30, n=4, hc=4, d=64, it=20, eps=1e-6,
+          neps=1e-20):
+        return lib.hc_post_mix_pre(P(x), P(R), P(post), P(comb), P(Ro), P(W), P(s), P(b), P(h), P(pre),
+                                   P(post2), P(comb2), P(mix), P(ws), wsb, n, hc, d, it, eps, neps, None)
+    assert f(n=0) == OK
+    assert f(hc=3) == UNSUP
+    assert f(it=0) == UNSUP
+    assert f(eps=-1.0) == VALUE
+    assert f(x=0) == NULL
+    assert f(comb=0) == NULL
+    assert f(Ro=0) == NULL
+    assert f(ws=0) == WS
+    assert f(x=A + 8) == ALIGN
+    assert f(Ro=B + 64) == ALIAS        # R_out overlaps R without being R
+    assert f(h=B) == ALIAS              # an output over the residual
+    assert f(post2=C) == ALIAS          # the next post over this sublayer's post
+    assert f(comb2=H + 0x2008 - 8) == ALIAS   # comb_next over post_next
 
 
 def test_workspace_query(lib):

@@ -244,6 +244,37 @@ def test_two_pass_and_persistent_paths_agree_bitwise(d):
         assert torch.equal(full[4][:, lo:hi], m), (d, lo, hi, "hc_mixes")
 
 
+@pytest.mark.parametrize("d,n", [(5120, 1), (5120, 64), (5120, 300), (5120, 2048), (5120, 2100),
+                                 (256, 77), (64, 40)])
+def test_post_mix_pre_matches_the_two_calls(orc, d, n):
+    # hc_post of sublayer l and then the fused call of sublayer l+1 on its
+    # output, as one entry point: bitwise the two calls in sequence, out of
+    # place and in place.  Up to 2,048 tokens at these widths hc_post is
+    # applied on chip inside the projection; beyond, and at d = 64, the two
+    # calls' kernels run in turn.
+    w = hin.Workload("pmp%d" % d, 1, n, 4, d, 1.0 / np.sqrt(4 * d), 0.5, 2.0, 1.0)
+    t = hin.make_inputs(w, DEV, seed=61)
+    nxt = hin.make_inputs(w, DEV, seed=62)          # sublayer l+1's weights, scale and base
+    _, _, post, comb, _ = run_fused(t["R"], t["W"], t["scale"], t["base"])
+    Rp = hcl.hc_post(t["x"], t["R"], post, comb)
+    ref = run_fused(Rp, nxt["W"], nxt["scale"], nxt["base"])
+    got = hcl.hc_post_mix_pre(t["x"], t["R"], post, comb, nxt["W"], nxt["scale"], nxt["base"],
+                              want_pre=True, want_mixes=True)
+    torch.cuda.synchronize()
+    assert torch.equal(got[0], Rp)
+    for name, u, v in zip(("h", "pre", "post", "comb", "mixes"), got[1:], ref):
+        assert torch.equal(u, v), name
+    R2 = t["R"].clone()
+    got2 = hcl.hc_post_mix_pre(t["x"], R2, post, comb, nxt["W"], nxt["scale"], nxt["base"],
+                               want_pre=True, want_mixes=True, out_R=R2)
+    torch.cuda.synchronize()
+    assert torch.equal(R2, Rp)
+    for name, u, v in zip(("h", "pre", "post", "comb", "mixes"), got2[1:], ref):
+        assert torch.equal(u, v), name + " (in place)"
+    if n <= 64:
+        compare_fused(orc, Rp, nxt["W"], nxt["scale"], nxt["base"], tuple(got[1:]), label="post+mix n=%d" % n)
+
+
 def test_workspace_reused_across_shapes():
     # one workspace through calls of different sizes and widths, mixes kept
     # in the workspace: every result equals that of a fresh workspace
