@@ -1708,6 +1708,11 @@ static int pow2_at_least(int x) {
 #define HC_TWO_PASS_MAX_N 2048
 #endif
 constexpr int64_t kTwoPassMaxN = HC_TWO_PASS_MAX_N;
+// hc_post_mix_pre applies hc_post inside the projection on calls of at most
+// this many tokens; beyond, the in-kernel hc_post's loads sit on every
+// round's critical path and the separate hc_post kernel is faster
+// (measured crossover between 256 and 512 tokens at d = 5120).
+constexpr int64_t kPostFuseMaxN = 256;
 
 // Wave-specialised kernel: groups of 8..32 members.
 static bool spec_width(int G) { return G >= 8 && G <= 32; }
@@ -1787,8 +1792,8 @@ int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* s
                 void* h, float* pre, float* post, float* comb, float* mixes, void* ws, int64_t n, int d,
                 int iters, float eps, float norm_eps, bool fused, hipStream_t s, const PostIn* prev) {
     char* wsb = static_cast<char*>(ws);
-    if (prev && !p.two_pass) {
-        // long calls: hc_post, then the projection of its output
+    if (prev && (!p.two_pass || n > kPostFuseMaxN)) {
+        // longer calls: hc_post, then the projection of its output
         if (launch_post(prev->x, R, prev->post, prev->comb, prev->Rout, n, d, s)) return -1;
         return launch_coop(p, prev->Rout, W, scale, base, h, pre, post, comb, mixes, ws, n, d, iters, eps,
                            norm_eps, fused, s, nullptr);

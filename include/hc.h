@@ -197,7 +197,7 @@ int hc_fused_mix_pre(const void *R, const float *hc_fn,
  * (the residual updated in place); R_out must not otherwise overlap R, and
  * no output may overlap an input or another output.  Same constraints on d
  * and the same workspace (hc_fused_workspace_bytes) as hc_fused_mix_pre.
- * Calls of at most 2,048 tokens at widths d = 32*k*G with 8 <= G <= 32
+ * Calls of at most 256 tokens at widths d = 32*k*G with 8 <= G <= 32
  * apply hc_post while the residual is on chip for the projection (two
  * launches, R read once); other calls run hc_post and then
  * hc_fused_mix_pre's kernels.
