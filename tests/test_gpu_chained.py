@@ -131,3 +131,42 @@ def test_chained_stack_stepwise(orc):
     stop = w.layers if first_nonfinite is None else first_nonfinite
     assert [l for l, _ in graded][:stop] == list(range(stop))
     assert all(c >= len(base_idx) for l, c in graded if l < stop)
+
+
+def _same_bits(a, b):
+    return torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.timeout(300)
+def test_chained_stack_with_fused_boundaries():
+    # The 80-sublayer stack on 64 decode tokens, with hc_post of sublayer l
+    # fused into sublayer l+1's projection (hc_post_mix_pre) and the
+    # residual updated in place: at every sublayer h, and at the end the
+    # residual, are bitwise those of the chain of separate calls (compared
+    # as bit patterns, since the stack overflows bf16 near its end).
+    w = hin.WORKLOADS["chained"]
+    hc, d, n = w.hc, w.d, 64
+    R0 = hin.make_inputs(w, DEV)["R"].reshape(-1, hc, d)[:n].contiguous()
+    params = [hin.make_params(w, DEV, layer=l) for l in range(w.layers)]
+    diags = [hin.make_diag(w, l, DEV) for l in range(w.layers)]
+    R = R0.clone()
+    hs = []
+    for l in range(w.layers):
+        W, s, b = params[l]
+        h, pre, post, comb, _ = hcl.hc_fused_mix_pre(R, W, s, b)
+        x = hcl.hc_diag_scale(h, diags[l])
+        R = hcl.hc_post(x, R, post, comb)
+        hs.append(h)
+    Rf = R0.clone()
+    W, s, b = params[0]
+    h, pre, post, comb, _ = hcl.hc_fused_mix_pre(Rf, W, s, b)
+    for l in range(w.layers):
+        assert _same_bits(h, hs[l]), "h of sublayer %d" % l
+        x = hcl.hc_diag_scale(h, diags[l])
+        if l + 1 < w.layers:
+            W, s, b = params[l + 1]
+            _, h, pre, post, comb, _ = hcl.hc_post_mix_pre(x, Rf, post, comb, W, s, b, out_R=Rf)
+        else:
+            hcl.hc_post(x, Rf, post, comb, out=Rf)
+    torch.cuda.synchronize()
+    assert _same_bits(Rf, R)
