@@ -197,6 +197,68 @@ def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, step
     print("\n".join(lines))
 
 
+def boundary_bytes(n: int, d: int):
+    """Minimum HBM bytes of one hc_post_mix_pre call: x, R and this
+    sublayer's post/comb read once, R' and h written once, the next
+    sublayer's pre/post/comb written once, its weights read once."""
+    hc = 4
+    return (n * (d * 2 + hc * d * 2 + (hc + hc * hc) * 4 + hc * d * 2 + d * 2 + (hc + hc + hc * hc) * 4)
+            + 24 * hc * d * 4 + 27 * 4)
+
+
+def bench_boundary(args, hcl, hin, torch, np, w, t, ws, outs, Rout, dev):
+    """--boundary: the step is one sublayer boundary, hc_post of this
+    sublayer followed by the next sublayer's fused call, as one
+    hc_post_mix_pre call.  Prints one JSON line like the default step."""
+    n, d = w.n, w.d
+    R, x, W, s, b = t["R"], t["x"], t["W"], t["scale"], t["base"]
+    nxt = hin.make_inputs(w, dev, seed=1)          # the next sublayer's weights, scale and base
+    hcl.hc_fused_mix_pre(R, W, s, b, workspace=ws, out=outs)     # this sublayer's post and comb
+    o2 = dict(h=torch.empty_like(outs["h"]), pre=torch.empty_like(outs["pre"]),
+              post=torch.empty_like(outs["post"]), comb=torch.empty_like(outs["comb"]))
+
+    def step():
+        hcl.hc_post_mix_pre(x, R, outs["post"], outs["comb"], nxt["W"], nxt["scale"], nxt["base"],
+                            sinkhorn_iters=w.iters, hc_eps=w.hc_eps, norm_eps=w.norm_eps, workspace=ws,
+                            out_R=Rout, out=o2)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for a, z in evs:
+        a.record(stream)
+        step()
+        z.record(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    v = np.array([a.elapsed_time(z) for a, z in evs]) * 1e3
+    bb = boundary_bytes(n, d)
+    gbs = bb / (v.mean() * 1e-6) / 1e9
+    line = {
+        "metric": "tokens/s + achieved HBM GB/s (% of peak), fused hc mix+pre and hc_post, d=5120",
+        "value": round(n / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) residual and sublayer output, N(0,0.007) weights)",
+        "config": {"workload": "%s: B=%d T=%d hc=4 d=%d (%d tokens), sinkhorn_iters=%d, step = one "
+                               "hc_post_mix_pre sublayer boundary" % (w.name, w.B, w.T, d, n, w.iters),
+                   "tokens": n, "d": d, "hc": 4, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "hc_post_mix_pre", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": bb, "avg_launch_us": round(float(v.mean()), 2)},
+        "kernels": {"hc_post_mix_pre": {"avg_us": round(float(v.mean()), 2), "median_us": round(float(np.median(v)), 2),
+                                        "min_us": round(float(v.min()), 2), "GB/s": round(gbs, 1),
+                                        "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": bb}},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,6 +278,9 @@ def main():
                     help="no GPU: turn a --kernel-trace --stats run under DIR into "
                          "profiles/kernel_trace_* for the chosen workload, then exit")
     ap.add_argument("--profile-command", default="", help="command recorded in the summary")
+    ap.add_argument("--boundary", action="store_true",
+                    help="time the sublayer boundary instead: one hc_post_mix_pre call (hc_post of "
+                         "this sublayer, then the next one's fused mix + Sinkhorn + hc_pre)")
     args = ap.parse_args()
 
     if args.summarize_counters or args.summarize_trace:
@@ -255,6 +320,9 @@ def main():
                 post=torch.empty(w.B, w.T, 4, device=dev),
                 comb=torch.empty(w.B, w.T, 4, 4, device=dev))
     Rout = torch.empty_like(R)
+    if args.boundary:
+        bench_boundary(args, hcl, hin, torch, np, w, t, ws, outs, Rout, dev)
+        return
 
     def fused():
         hcl.hc_fused_mix_pre(R, W, s, b, sinkhorn_iters=w.iters, hc_eps=w.hc_eps,

@@ -136,12 +136,6 @@ struct CoopArgs {
     float K;
     int part_bytes;
     uint64_t call;      // process-wide number of this call (sets the record epoch)
-    // hc_post of the previous sublayer, applied to R before the projection
-    // (two-pass path of hc_post_mix_pre only)
-    const uint16_t* X;  // sublayer output x [n][d]
-    const float* ppost; // its post [n][4]
-    const float* pcomb; // its comb [n][4][4]
-    uint16_t* Rout;     // R' [n][4][d] (may be R itself)
 };
 
 // Field f of a partial record (0..23 = the 24 dot products, 24 = sum of
@@ -1457,64 +1451,10 @@ __device__ __forceinline__ void prec_of(int id, int& tk, int& ch) {
     ch = id - tk * kChunks;
 }
 
-// hc_post of the previous sublayer on round r's residual, in place in slot
-// r % 3 and out to R': the member's slice of every token of the round.
-// Item i is token i / (4 KS), 16-byte chunk i % (4 KS) of each stream of the
-// slice; post_chunk8 is hc_post's own arithmetic, so R' is bitwise hc_post's.
-// Every lane issues the same memory instructions (items past the round or
-// past the last token load zeros and store nothing).
-template <int KS>
-__device__ __forceinline__ void p_post(const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, int r) {
-    constexpr int kPC = 4 * KS;                              // chunks per stream in the slice
-    constexpr int kItems = kT * kPC;
-    constexpr int kIter = (kItems + kMW * 64 - 1) / (kMW * 64);
-    const int64_t tok0 = tile_of(c, a, r) * kT;
-    const __amdgpu_buffer_rsrc_t rx = tile_rsrc(a.X, (int64_t)a.d * 2, tok0, a.n, kT);
-    const __amdgpu_buffer_rsrc_t rq = tile_rsrc(a.ppost, kHC * 4, tok0, a.n, kT);
-    const __amdgpu_buffer_rsrc_t rc = tile_rsrc(a.pcomb, kHC * kHC * 4, tok0, a.n, kT);
-    const __amdgpu_buffer_rsrc_t ro = tile_rsrc(a.Rout, (int64_t)kHC * a.d * 2, tok0, a.n, kT);
-    uint8_t* slot = &L.slot[r % kNSlot][0];
-    u32x4 xv[kIter];
-    f32x4 q[kIter], cb[kIter][kHC];
-#pragma unroll
-    for (int j = 0; j < kIter; ++j) {
-        const int i = (int)threadIdx.x + j * (kMW * 64);
-        const int it = i < kItems ? i : 0;
-        const int tk = it / kPC, ch = it - tk * kPC;
-        xv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rx, i < kItems ? (tk * a.d + c.q * (32 * KS) + 8 * ch) * 2 : kOOB, 0, 0));
-        q[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, tk * kHC * 4, 0, 0));
-#pragma unroll
-        for (int k = 0; k < kHC; ++k)
-            cb[j][k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     rc, (tk * kHC + k) * kHC * 4, 0, 0));
-    }
-#pragma unroll
-    for (int j = 0; j < kIter; ++j) {
-        const int i = (int)threadIdx.x + j * (kMW * 64);
-        const int it = i < kItems ? i : 0;
-        const int tk = it / kPC, ch = it - tk * kPC;
-        u32x4 rr[kHC], out[kHC];
-#pragma unroll
-        for (int k = 0; k < kHC; ++k)
-            rr[k] = *reinterpret_cast<const u32x4*>(slot + tk * Geo<KS>::kRowB + k * (64 * KS) + 16 * ch);
-        post_chunk8(q[j], cb[j], xv[j], rr, out);
-#pragma unroll
-        for (int k = 0; k < kHC; ++k) {
-            if (i < kItems) *reinterpret_cast<u32x4*>(slot + tk * Geo<KS>::kRowB + k * (64 * KS) + 16 * ch) = out[k];
-            __builtin_amdgcn_raw_buffer_store_b128(
-                __builtin_bit_cast(__attribute__((__vector_size__(16))) int, out[k]), ro,
-                i < kItems ? ((tk * kHC + k) * a.d + c.q * (32 * KS) + 8 * ch) * 2 : kOOB, 0, 0);
-        }
-    }
-}
-
 // Pass 1: workgroup b is member b % G of tile group b / G (tiles g, g + NG,
 // ...).  Four waves, one per stream, as the MFMA waves of k_spec; tick t
-// publishes round t-1, issues round t+2 and multiplies round t.  POST: the
-// residual first goes through the previous sublayer's hc_post (p_post) at
-// the start of its tick, and the projection is that of R'.
-template <int KS, bool POST>
+// publishes round t-1, issues round t+2 and multiplies round t.
+template <int KS>
 __global__ __launch_bounds__(kMW * 64, 1) void k_part(CoopArgs a) {
     __shared__ __attribute__((aligned(16))) Lds<KS> L;
     RoundCtx c;
@@ -1546,11 +1486,6 @@ __global__ __launch_bounds__(kMW * 64, 1) void k_part(CoopArgs a) {
     }
     __syncthreads();
     for (int t = 0;; ++t) {
-        if (POST && t < c.nr) {
-            // round t is in LDS (waited for at the end of the last tick)
-            p_post<KS>(a, c, L, t);
-            __syncthreads();
-        }
         p_publish<KS>(a, c, L, M, t - 1);
         if (t + 2 < c.nr) {
             m_dma<KS>(S, a, c, L, t + 2);
@@ -1708,11 +1643,6 @@ static int pow2_at_least(int x) {
 #define HC_TWO_PASS_MAX_N 2048
 #endif
 constexpr int64_t kTwoPassMaxN = HC_TWO_PASS_MAX_N;
-// hc_post_mix_pre applies hc_post inside the projection on calls of at most
-// this many tokens; beyond, the in-kernel hc_post's loads sit on every
-// round's critical path and the separate hc_post kernel is faster
-// (measured crossover between 256 and 512 tokens at d = 5120).
-constexpr int64_t kPostFuseMaxN = 256;
 
 // Wave-specialised kernel: groups of 8..32 members.
 static bool spec_width(int G) { return G >= 8 && G <= 32; }
@@ -1767,16 +1697,12 @@ static bool use_spec(const CoopPlan& p) { return spec_width(p.G); }
 
 template <int KS>
 static int launch_two_pass(const CoopPlan& p, CoopArgs& a, bool fused, hipStream_t s) {
-    const bool post = a.Rout != nullptr;
-    if (post) spec::k_part<KS, true><<<p.G * p.NG, spec::kMW * 64, 0, s>>>(a);
-    else spec::k_part<KS, false><<<p.G * p.NG, spec::kMW * 64, 0, s>>>(a);
+    spec::k_part<KS><<<p.G * p.NG, spec::kMW * 64, 0, s>>>(a);
     if (hipGetLastError() != hipSuccess) return -1;
     const int splits = fused ? p.splits : 1;
     const int64_t blocks = (a.n + spec::kFinTok - 1) / spec::kFinTok * splits;
-    CoopArgs b = a;
-    if (post) b.R = a.Rout;        // h is formed from R'
-    if (fused) spec::k_fin<true><<<(unsigned)blocks, 256, 0, s>>>(b, splits);
-    else spec::k_fin<false><<<(unsigned)blocks, 256, 0, s>>>(b, splits);
+    if (fused) spec::k_fin<true><<<(unsigned)blocks, 256, 0, s>>>(a, splits);
+    else spec::k_fin<false><<<(unsigned)blocks, 256, 0, s>>>(a, splits);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -1792,17 +1718,16 @@ int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* s
                 void* h, float* pre, float* post, float* comb, float* mixes, void* ws, int64_t n, int d,
                 int iters, float eps, float norm_eps, bool fused, hipStream_t s, const PostIn* prev) {
     char* wsb = static_cast<char*>(ws);
-    if (prev && (!p.two_pass || n > kPostFuseMaxN)) {
-        // longer calls: hc_post, then the projection of its output
+    if (prev) {
+        // hc_post, then the projection of its output.  (Applying hc_post to
+        // each round inside k_part, while the residual is in LDS, was
+        // slower: its exact-rounding work then runs on the few CUs of a
+        // short call instead of the whole chip.)
         if (launch_post(prev->x, R, prev->post, prev->comb, prev->Rout, n, d, s)) return -1;
         return launch_coop(p, prev->Rout, W, scale, base, h, pre, post, comb, mixes, ws, n, d, iters, eps,
                            norm_eps, fused, s, nullptr);
     }
     CoopArgs a;
-    a.X = prev ? static_cast<const uint16_t*>(prev->x) : nullptr;
-    a.ppost = prev ? prev->post : nullptr;
-    a.pcomb = prev ? prev->comb : nullptr;
-    a.Rout = prev ? static_cast<uint16_t*>(prev->Rout) : nullptr;
     a.R = static_cast<const uint16_t*>(R);
     a.W = W;
     a.scale = scale;

@@ -42,7 +42,8 @@ int coop_ks(int d);
 bool coop_plan(int64_t n, int d, CoopPlan& p);
 // hc_post of the previous sublayer, run ahead of the projection
 // (hc_post_mix_pre): R' = hc_post(x, R, post, comb) goes to Rout, and the
-// projection, pre and h are those of R'.
+// projection, pre and h are those of R'.  R is the argument `R` of
+// launch_coop.
 struct PostIn {
     const void* x;
     const float* post;

@@ -197,10 +197,8 @@ int hc_fused_mix_pre(const void *R, const float *hc_fn,
  * (the residual updated in place); R_out must not otherwise overlap R, and
  * no output may overlap an input or another output.  Same constraints on d
  * and the same workspace (hc_fused_workspace_bytes) as hc_fused_mix_pre.
- * Calls of at most 256 tokens at widths d = 32*k*G with 8 <= G <= 32
- * apply hc_post while the residual is on chip for the projection (two
- * launches, R read once); other calls run hc_post and then
- * hc_fused_mix_pre's kernels.
+ * The call runs hc_post's kernel and then hc_fused_mix_pre's kernels on
+ * `stream`: one call per sublayer boundary instead of two.
  */
 int hc_post_mix_pre(const void *x, const void *R, const float *post,
                     const float *comb, void *R_out, const float *hc_fn,

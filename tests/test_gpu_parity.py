@@ -249,9 +249,8 @@ def test_two_pass_and_persistent_paths_agree_bitwise(d):
 def test_post_mix_pre_matches_the_two_calls(orc, d, n):
     # hc_post of sublayer l and then the fused call of sublayer l+1 on its
     # output, as one entry point: bitwise the two calls in sequence, out of
-    # place and in place.  Up to 256 tokens at these widths hc_post is
-    # applied on chip inside the projection; beyond, and at d = 64, the two
-    # calls' kernels run in turn.
+    # place and in place (R_out == R), on the two-pass and the persistent
+    # path and at a width of the cooperative kernel.
     w = hin.Workload("pmp%d" % d, 1, n, 4, d, 1.0 / np.sqrt(4 * d), 0.5, 2.0, 1.0)
     t = hin.make_inputs(w, DEV, seed=61)
     nxt = hin.make_inputs(w, DEV, seed=62)          # sublayer l+1's weights, scale and base
