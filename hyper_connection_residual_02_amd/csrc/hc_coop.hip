@@ -1506,20 +1506,27 @@ __global__ __launch_bounds__(kMW * 64, 1) void k_part(CoopArgs a) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// Pass 2: block b covers tokens kFinTok*(b / splits) .. +3 and column part
-// b % splits of h.  Wave w reduces token kFinTok*(b / splits) + w.  Each
-// thread issues the residual loads of its first h chunk before the
-// reduction (they do not depend on it), and the split + Sinkhorn, which
-// only blocks of column part 0 run, comes after h, so its latency overlaps
-// the h stores.
+// Pass 2: a group of blocks per 4 tokens.  With splits > 1 column parts
+// (short calls, where the grid needs filling) the group has splits + 1
+// blocks: part sp < splits covers column part sp of h, and part splits runs
+// the split + Sinkhorn and writes the mixes, so the Sinkhorn's long
+// dependent chain runs beside h rather than after it.  With one column part
+// the group is one block that forms h and then runs the split + Sinkhorn
+// (a separate block would only repeat the reduction).  In every block wave
+// w reduces token 4 * group + w, and each thread issues the residual loads
+// of its first h chunk before the reduction (they do not depend on it).
 template <bool FUSED>
 __global__ __launch_bounds__(256) void k_fin(CoopArgs a, int splits) {
     __shared__ float sums[kFinTok][kChunks][4];
     __shared__ __attribute__((aligned(16))) float mixL[kFinTok][kMix];
     __shared__ __attribute__((aligned(16))) float preL[kFinTok][4];
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, e = l & 15, g = l >> 4;
-    const int64_t tg = blockIdx.x / splits;
-    const int sp = blockIdx.x - (int)(tg * splits);
+    const bool sep = FUSED && splits > 1;         // a block of its own for the split + Sinkhorn
+    const int parts = sep ? splits + 1 : 1;
+    const int64_t tg = blockIdx.x / parts;
+    const int sp = blockIdx.x - (int)(tg * parts);
+    const bool sk_only = sep && sp == splits;     // this block runs only the split + Sinkhorn
+    const bool coef = !sep || sk_only;            // this block writes the mixes and the split
     const int64_t t = tg * kFinTok + w;
     const bool tv = t < a.n;
 
@@ -1529,7 +1536,7 @@ __global__ __launch_bounds__(256) void k_fin(CoopArgs a, int splits) {
     const int cs = d8 / splits;
     const int64_t t0 = tg * kFinTok;
     const int64_t nt = a.n - t0 < kFinTok ? a.n - t0 : kFinTok;
-    const int items = FUSED ? (int)nt * cs : 0;
+    const int items = FUSED && !sk_only ? (int)nt * cs : 0;
     const u32x4* R = reinterpret_cast<const u32x4*>(a.R);
     int i = threadIdx.x;
     int tk = 0;
@@ -1571,11 +1578,28 @@ __global__ __launch_bounds__(256) void k_fin(CoopArgs a, int splits) {
         field_pos(f, ch, sl);
         const float m = mix_value(sums[w][ch][sl], mix_scale(sums[w][1][1], sums[w][1][2], a.K, a.norm_eps));
         if (l < kMix) mixL[w][l] = m;
-        if (a.mixes && sp == 0 && tv && l < kMix) a.mixes[t * kMix + l] = m;
+        if (a.mixes && coef && tv && l < kMix) a.mixes[t * kMix + l] = m;
     }
     if (!FUSED) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     const float s0 = a.scale[0];
+    // the split + Sinkhorn of token t (all four 16-lane rows compute it;
+    // row 0 writes)
+    auto split = [&]() {
+        float p, q, cc;
+        split_sinkhorn16(&mixL[w][0], s0, a.scale[1], a.scale[2], a.base, a.iters, a.eps, p, q, cc);
+        if (tv && l < 16) {
+            a.comb[t * (kHC * kHC) + e] = cc;
+            if (e < kHC) {
+                a.post[t * kHC + e] = q;
+                if (a.pre) a.pre[t * kHC + e] = p;
+            }
+        }
+    };
+    if (sk_only) {
+        split();
+        return;
+    }
     if (l < kHC) preL[w][l] = pre_gate(mixL[w][l], s0, a.base[l], a.eps);
     __syncthreads();
 
@@ -1588,20 +1612,7 @@ __global__ __launch_bounds__(256) void k_fin(CoopArgs a, int splits) {
         if (i < items) fetch();
         __builtin_nontemporal_store(out, h + hr);
     }
-
-    if (sp == 0) {
-        // the split + Sinkhorn of token t (all four 16-lane rows compute it;
-        // row 0 writes)
-        float p, q, cc;
-        split_sinkhorn16(&mixL[w][0], s0, a.scale[1], a.scale[2], a.base, a.iters, a.eps, p, q, cc);
-        if (tv && l < 16) {
-            a.comb[t * (kHC * kHC) + e] = cc;
-            if (e < kHC) {
-                a.post[t * kHC + e] = q;
-                if (a.pre) a.pre[t * kHC + e] = p;
-            }
-        }
-    }
+    if (coef) split();
 }
 
 }  // namespace spec
@@ -1700,7 +1711,7 @@ static int launch_two_pass(const CoopPlan& p, CoopArgs& a, bool fused, hipStream
     spec::k_part<KS><<<p.G * p.NG, spec::kMW * 64, 0, s>>>(a);
     if (hipGetLastError() != hipSuccess) return -1;
     const int splits = fused ? p.splits : 1;
-    const int64_t blocks = (a.n + spec::kFinTok - 1) / spec::kFinTok * splits;
+    const int64_t blocks = (a.n + spec::kFinTok - 1) / spec::kFinTok * (fused && splits > 1 ? splits + 1 : 1);
     if (fused) spec::k_fin<true><<<(unsigned)blocks, 256, 0, s>>>(a, splits);
     else spec::k_fin<false><<<(unsigned)blocks, 256, 0, s>>>(a, splits);
     return hipGetLastError() == hipSuccess ? 0 : -1;
