@@ -113,6 +113,34 @@ def test_ragged_token_counts(orc, n):
     compare_fused(orc, t["R"], t["W"], t["scale"], t["base"], outs, idx=idx, x=t["x"], label="n=%d" % n)
 
 
+@pytest.mark.parametrize("n", [100, 2100])
+@pytest.mark.parametrize("iters,eps", [(1, 1e-6), (20, 0.0), (1, 0.0), (3, 1e-3)])
+def test_fused_degenerate_parameters(orc, n, iters, eps):
+    # one Sinkhorn step (the softmax and a single column normalisation),
+    # eps = 0, and a large eps, on the two-pass (100 tokens) and the
+    # persistent path (2,100)
+    w = hin.WORKLOADS["prefill"]
+    t = hin.make_inputs(w, DEV, seed=83, n_tokens=n)
+    outs = run_fused(t["R"], t["W"], t["scale"], t["base"], iters=iters, eps=eps)
+    idx = None if n <= 300 else hin.sample_tokens(n, 64)
+    compare_fused(orc, t["R"], t["W"], t["scale"], t["base"], outs, idx=idx, iters=iters, eps=eps, x=t["x"],
+                  label="n=%d iters=%d eps=%g" % (n, iters, eps))
+
+
+@pytest.mark.timeout(300)
+def test_maximum_size_sampled(orc):
+    # 262,144 tokens (B = 32, T = 8192) at d = 5120: a 10.7 GB residual, four
+    # times the large prefill, so byte offsets into R, x, h and R' pass 2^33;
+    # sampled tokens (the first, the last and random ones) against the oracle
+    w = hin.Workload("max", 32, 8192, 4, 5120, 0.007, 0.5, 2.0, 1.0)
+    t = hin.make_inputs(w, DEV, seed=71)
+    outs = run_fused(t["R"], t["W"], t["scale"], t["base"])
+    idx = hin.sample_tokens(w.B * w.T, 96)
+    compare_fused(orc, t["R"], t["W"], t["scale"], t["base"], outs, idx=idx, x=t["x"], label="max size")
+    del t, outs
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("d", [32, 64, 256, 1024, 2048, 3072, 4096, 7168, 8192])
 def test_other_widths(orc, d):
     # every k-step count of the projection kernel (d = 32*KS*G), ragged n
