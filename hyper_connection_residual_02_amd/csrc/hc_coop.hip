@@ -1220,8 +1220,10 @@ __device__ __forceinline__ void x_h(const u32x2 (&rb)[Geo<KS>::kPass][kHC], cons
             for (int w = 0; w < 2; ++w) out[w] = pack2(bf16_rn(f[w][0]), bf16_rn(f[w][1]));
         }
         const int off = valid ? ((kTokX * xw + tk) * a.d + c.q * (32 * KS) + 4 * b) * 2 : kOOB;
+        // non-temporal (nt): h is not read again by this call, and streaming
+        // it out leaves fewer dirty lines for the next kernel to write back
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((__vector_size__(8))) int, out),
-                                              rs, off, 0, 0);
+                                              rs, off, 0, 2);
     }
 }
 
