@@ -128,7 +128,7 @@ def summarize_counters(d: str, n: int, dd: int, command: str):
     print("\n".join(lines))
 
 
-def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, steps: int = 0):
+def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, steps: int = 0, tag: str = ""):
     """Per-kernel launch durations from a rocprofv3 --kernel-trace --stats
     run of the bench command under ``d``: the average over every dispatch
     (``*kernel_stats.csv``) and, when ``steps`` is given, the average over
@@ -192,7 +192,7 @@ def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, step
         lines.append("Timed region: dispatches %d .. %d of each kernel (after %d warmup steps)."
                      % (warmup, warmup + steps - 1, warmup))
     lines.append("Kernel sources hash (sha256 of csrc/, first 16 hex): %s" % kernel_source_hash())
-    with open(os.path.join(PROFILE_DIR, "kernel_trace_n%d_d%d.md" % (n, dd)), "w") as fh:
+    with open(os.path.join(PROFILE_DIR, "kernel_trace_%sn%d_d%d.md" % (tag + "_" if tag else "", n, dd)), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -278,6 +278,10 @@ def main():
                     help="no GPU: turn a --kernel-trace --stats run under DIR into "
                          "profiles/kernel_trace_* for the chosen workload, then exit")
     ap.add_argument("--profile-command", default="", help="command recorded in the summary")
+    ap.add_argument("--summary-tag", default="", help="word added to the trace summary's file name")
+    ap.add_argument("--packed", action="store_true",
+                    help="split the weights once before timing (hc_pack_weights) and run the fused call "
+                         "on the packed form")
     ap.add_argument("--boundary", action="store_true",
                     help="time the sublayer boundary instead: one hc_post_mix_pre call (hc_post of "
                          "this sublayer, then the next one's fused mix + Sinkhorn + hc_pre)")
@@ -290,7 +294,8 @@ def main():
         if args.summarize_counters:
             summarize_counters(args.summarize_counters, w.n, w.d, args.profile_command)
         if args.summarize_trace:
-            summarize_trace(args.summarize_trace, w.n, w.d, args.profile_command, args.warmup, args.steps)
+            summarize_trace(args.summarize_trace, w.n, w.d, args.profile_command, args.warmup, args.steps,
+                            args.summary_tag)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -320,13 +325,14 @@ def main():
                 post=torch.empty(w.B, w.T, 4, device=dev),
                 comb=torch.empty(w.B, w.T, 4, 4, device=dev))
     Rout = torch.empty_like(R)
+    packed = hcl.hc_pack_weights(W) if args.packed else None
     if args.boundary:
         bench_boundary(args, hcl, hin, torch, np, w, t, ws, outs, Rout, dev)
         return
 
     def fused():
         hcl.hc_fused_mix_pre(R, W, s, b, sinkhorn_iters=w.iters, hc_eps=w.hc_eps,
-                             norm_eps=w.norm_eps, workspace=ws, out=outs)
+                             norm_eps=w.norm_eps, workspace=ws, out=outs, packed=packed)
 
     def post():
         hcl.hc_post(x, R, outs["post"], outs["comb"], out=Rout)
@@ -462,8 +468,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) residual and sublayer output, N(0,0.007) weights)",
-        "config": {"workload": "%s: B=%d T=%d hc=4 d=%d (%d tokens), sinkhorn_iters=%d"
-                               % (w.name, w.B, w.T, d, n, w.iters),
+        "config": {"workload": "%s: B=%d T=%d hc=4 d=%d (%d tokens), sinkhorn_iters=%d%s"
+                               % (w.name, w.B, w.T, d, n, w.iters,
+                                  ", weights packed once before timing" if args.packed else ""),
                    "tokens": n, "d": d, "hc": 4, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dom["name"], "achieved": round(dom["gbs"], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4),

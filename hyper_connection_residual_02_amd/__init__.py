@@ -22,7 +22,8 @@ import torch
 
 __all__ = [
     "HCError", "load", "lib_path", "hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post",
-    "hc_fused_mix_pre", "hc_post_mix_pre", "hc_diag_scale", "hc_fused_workspace_bytes", "Workspace",
+    "hc_fused_mix_pre", "hc_post_mix_pre", "hc_pack_weights", "hc_diag_scale", "hc_fused_workspace_bytes",
+    "Workspace",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +62,8 @@ def load():
         "hc_post": [P, P, P, P, P, I64, I32, I32, P],
         "hc_fused_mix_pre": [P, P, P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, F32, F32, P],
         "hc_post_mix_pre": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, F32, F32, P],
+        "hc_pack_weights": [P, P, SZ, I32, I32, P],
+        "hc_fused_mix_pre_packed": [P, P, SZ, P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, F32, F32, P],
         "hc_diag_scale": [P, P, P, I64, I32, P],
     }
     for name, args in sig.items():
@@ -69,6 +72,8 @@ def load():
         f.restype = ctypes.c_int
     lib.hc_fused_workspace_bytes.argtypes = [I64, I32, I32]
     lib.hc_fused_workspace_bytes.restype = SZ
+    lib.hc_packed_weights_bytes.argtypes = [I32, I32]
+    lib.hc_packed_weights_bytes.restype = SZ
     lib.hc_status_str.argtypes = [ctypes.c_int]
     lib.hc_status_str.restype = ctypes.c_char_p
     lib.hc_version.argtypes = []
@@ -230,13 +235,35 @@ def hc_post(x: torch.Tensor, R: torch.Tensor, post: torch.Tensor, comb: torch.Te
     return out
 
 
+def hc_pack_weights(hc_fn: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """The projection weights split once into the kernels' bf16 pieces
+    (uint8 tensor); pass it as ``packed=`` to hc_fused_mix_pre."""
+    dev = hc_fn.device
+    _check(hc_fn, "hc_fn", torch.float32)
+    hc = 4
+    if hc_fn.dim() != 2 or hc_fn.shape[0] != HC_MIX or hc_fn.shape[1] % hc:
+        raise ValueError("hc_fn must be [24, 4*d]")
+    d = hc_fn.shape[1] // hc
+    nb = int(load().hc_packed_weights_bytes(hc, d))
+    if nb == 0:
+        raise HCError("hc_pack_weights", -4)
+    if out is None:
+        out = torch.empty(nb, dtype=torch.uint8, device=dev)
+    _check(out, "out", torch.uint8, dev)
+    with torch.cuda.device(dev):
+        _call("hc_pack_weights", _ptr(hc_fn), _ptr(out), out.numel(), hc, d, _stream(dev))
+    return out
+
+
 def hc_fused_mix_pre(R: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tensor,
                      hc_base: torch.Tensor, sinkhorn_iters: int = 20, hc_eps: float = 1e-6,
                      norm_eps: float = 1e-20, want_pre: bool = True, want_mixes: bool = False,
-                     workspace: Workspace | None = None, out=None):
+                     workspace: Workspace | None = None, out=None, packed: torch.Tensor | None = None):
     """hc_mixes + hc_split_sinkhorn + hc_pre in one pass over R.
     Returns (h, pre or None, post, comb, mixes or None).  ``out`` may be a
-    dict of preallocated outputs (keys h, pre, post, comb, mixes)."""
+    dict of preallocated outputs (keys h, pre, post, comb, mixes).  With
+    ``packed`` (from hc_pack_weights(hc_fn)) the weights are not split again;
+    hc_fn is then only checked for shape."""
     dev = R.device
     _check(R, "R", torch.bfloat16)
     for t, nm in ((hc_fn, "hc_fn"), (hc_scale, "hc_scale"), (hc_base, "hc_base")):
@@ -257,9 +284,15 @@ def hc_fused_mix_pre(R: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tenso
         mixes = torch.empty(*lead, HC_MIX, dtype=torch.float32, device=dev)
     wp, wb = _workspace(workspace, hc_fused_workspace_bytes(n, hc, d), dev)
     with torch.cuda.device(dev):
-        _call("hc_fused_mix_pre", _ptr(R), _ptr(hc_fn), _ptr(hc_scale), _ptr(hc_base), _ptr(h),
-              _ptr(pre), _ptr(post), _ptr(comb), _ptr(mixes), wp, wb, n, hc, d,
-              int(sinkhorn_iters), float(hc_eps), float(norm_eps), _stream(dev))
+        if packed is not None:
+            _check(packed, "packed", torch.uint8, dev)
+            _call("hc_fused_mix_pre_packed", _ptr(R), _ptr(packed), packed.numel(), _ptr(hc_scale),
+                  _ptr(hc_base), _ptr(h), _ptr(pre), _ptr(post), _ptr(comb), _ptr(mixes), wp, wb, n, hc, d,
+                  int(sinkhorn_iters), float(hc_eps), float(norm_eps), _stream(dev))
+        else:
+            _call("hc_fused_mix_pre", _ptr(R), _ptr(hc_fn), _ptr(hc_scale), _ptr(hc_base), _ptr(h),
+                  _ptr(pre), _ptr(post), _ptr(comb), _ptr(mixes), wp, wb, n, hc, d,
+                  int(sinkhorn_iters), float(hc_eps), float(norm_eps), _stream(dev))
     return h, pre, post, comb, mixes
 
 

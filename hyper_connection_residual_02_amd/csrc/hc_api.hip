@@ -173,21 +173,32 @@ int hc_mixes(const void* R, const float* hc_fn, float* mixes, int64_t n, int32_t
                : HC_OK;
 }
 
-int hc_fused_mix_pre(const void* R, const float* hc_fn, const float* hc_scale, const float* hc_base, void* h,
-                     float* pre, float* post, float* comb, float* mixes, void* workspace, size_t workspace_bytes,
-                     int64_t n, int32_t hc_, int32_t d, int32_t sinkhorn_iters, float hc_eps, float norm_eps,
-                     void* stream) {
+}  // extern "C"
+
+// hc_fused_mix_pre with the weights as given (hc_fn) or already split
+// (packed, from hc_pack_weights).
+static int fused_impl(const void* R, const float* hc_fn, const void* packed, size_t packed_bytes,
+                      const float* hc_scale, const float* hc_base, void* h, float* pre, float* post, float* comb,
+                      float* mixes, void* workspace, size_t workspace_bytes, int64_t n, int32_t hc_, int32_t d,
+                      int32_t sinkhorn_iters, float hc_eps, float norm_eps, void* stream) {
     if (hc_ == 4 && sinkhorn_iters < 1) return HC_ERR_UNSUPPORTED;
     if (!finite_nonneg(hc_eps)) return HC_ERR_VALUE;
     hc::CoopPlan p;
-    int st = coop_common(R, hc_fn, workspace, workspace_bytes, n, hc_, d, norm_eps, p);
+    const void* wsrc = packed ? packed : (const void*)hc_fn;
+    int st = coop_common(R, static_cast<const float*>(wsrc), workspace, workspace_bytes, n, hc_, d, norm_eps, p);
     if (st || n == 0) return st;
+    const uint64_t K = (uint64_t)4 * d;
+    uint64_t wbytes = 24 * K * 4;
+    if (packed) {
+        wbytes = hc::packed_weights_bytes(d);
+        if (wbytes == 0) return HC_ERR_UNSUPPORTED;
+        if (packed_bytes < wbytes) return HC_ERR_WORKSPACE;
+    }
     if (!hc_scale || !hc_base || !h || !post || !comb) return HC_ERR_NULL;
     if (!al4(hc_scale) || !al4(hc_base) || !al16(h) || !al16(post) || !al16(comb) || (pre && !al16(pre)) ||
         (mixes && !al16(mixes)))
         return HC_ERR_ALIGN;
-    const uint64_t K = (uint64_t)4 * d;
-    const Span ins[] = {span(R, (uint64_t)n * K * 2), span(hc_fn, 24 * K * 4), span(hc_scale, 12),
+    const Span ins[] = {span(R, (uint64_t)n * K * 2), span(wsrc, wbytes), span(hc_scale, 12),
                         span(hc_base, 96), span(workspace, p.ws_bytes)};
     Span outs[5];
     int no = 0;
@@ -203,9 +214,45 @@ int hc_fused_mix_pre(const void* R, const float* hc_fn, const float* hc_scale, c
             if (overlap(outs[i], outs[j])) return HC_ERR_ALIAS;
     }
     return hc::launch_coop(p, R, hc_fn, hc_scale, hc_base, h, pre, post, comb, mixes, workspace, n, d,
-                           sinkhorn_iters, hc_eps, norm_eps, true, (hipStream_t)stream)
+                           sinkhorn_iters, hc_eps, norm_eps, true, (hipStream_t)stream, nullptr, packed)
                ? HC_ERR_LAUNCH
                : HC_OK;
+}
+
+extern "C" {
+
+int hc_fused_mix_pre(const void* R, const float* hc_fn, const float* hc_scale, const float* hc_base, void* h,
+                     float* pre, float* post, float* comb, float* mixes, void* workspace, size_t workspace_bytes,
+                     int64_t n, int32_t hc_, int32_t d, int32_t sinkhorn_iters, float hc_eps, float norm_eps,
+                     void* stream) {
+    return fused_impl(R, hc_fn, nullptr, 0, hc_scale, hc_base, h, pre, post, comb, mixes, workspace,
+                      workspace_bytes, n, hc_, d, sinkhorn_iters, hc_eps, norm_eps, stream);
+}
+
+size_t hc_packed_weights_bytes(int32_t hc_, int32_t d) {
+    if (hc_ != 4 || d <= 0) return 0;
+    return hc::packed_weights_bytes(d);
+}
+
+int hc_pack_weights(const float* hc_fn, void* packed, size_t packed_bytes, int32_t hc_, int32_t d, void* stream) {
+    if (d <= 0 || d % 8 != 0) return HC_ERR_SHAPE;
+    if (hc_ != 4) return HC_ERR_UNSUPPORTED;
+    const size_t pb = hc::packed_weights_bytes(d);
+    if (pb == 0) return HC_ERR_UNSUPPORTED;
+    if (!hc_fn || !packed) return HC_ERR_NULL;
+    if (!al16(hc_fn) || !al16(packed)) return HC_ERR_ALIGN;
+    if (packed_bytes < pb) return HC_ERR_WORKSPACE;
+    if (overlap(span(packed, pb), span(hc_fn, (uint64_t)24 * 4 * d * 4))) return HC_ERR_ALIAS;
+    return hc::launch_pack(hc_fn, packed, d, (hipStream_t)stream) ? HC_ERR_LAUNCH : HC_OK;
+}
+
+int hc_fused_mix_pre_packed(const void* R, const void* packed, size_t packed_bytes, const float* hc_scale,
+                            const float* hc_base, void* h, float* pre, float* post, float* comb, float* mixes,
+                            void* workspace, size_t workspace_bytes, int64_t n, int32_t hc_, int32_t d,
+                            int32_t sinkhorn_iters, float hc_eps, float norm_eps, void* stream) {
+    if (!packed && n > 0) return HC_ERR_NULL;
+    return fused_impl(R, nullptr, packed, packed_bytes, hc_scale, hc_base, h, pre, post, comb, mixes, workspace,
+                      workspace_bytes, n, hc_, d, sinkhorn_iters, hc_eps, norm_eps, stream);
 }
 
 int hc_post_mix_pre(const void* x, const void* R, const float* post, const float* comb, void* R_out,

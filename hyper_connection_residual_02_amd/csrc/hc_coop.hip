@@ -136,6 +136,7 @@ struct CoopArgs {
     float K;
     int part_bytes;
     uint64_t call;      // process-wide number of this call (sets the record epoch)
+    const u32x4* Wp;    // weights already split into MFMA pieces (hc_pack_weights), or null
 };
 
 // Field f of a partial record (0..23 = the 24 dot products, 24 = sum of
@@ -783,6 +784,13 @@ __device__ __forceinline__ void dma16(v4u rs, uint32_t lds, uint32_t voff) {
         : "memory");
 }
 
+// Index (16-byte units) of lane l's piece vector for member q, stream w,
+// k-step st, column tile ct in the packed weights: [q][w][st][ct][lane].
+template <int KS>
+__device__ __forceinline__ int64_t packed_index(int q, int w, int st, int ct, int l) {
+    return ((((int64_t)q * kHC + w) * KS + st) * kTiles + ct) * 64 + l;
+}
+
 template <int KS>
 struct MState {
     bf16x8 w[KS][kTiles];                  // weight slice of stream w, MFMA B layout
@@ -836,6 +844,23 @@ __device__ __forceinline__ void m_setup(MState<KS>& S, const CoopArgs& a, const 
             raw[ct][1] = src[1];
         }
     };
+    if (a.Wp) {
+        // pieces split once by k_pack, in this very register layout: every
+        // load is issued before the first pin
+        u32x4 pk[KS][kTiles];
+#pragma unroll
+        for (int st = 0; st < KS; ++st)
+#pragma unroll
+            for (int ct = 0; ct < kTiles; ++ct) pk[st][ct] = a.Wp[packed_index<KS>(c.q, c.w, st, ct, c.l)];
+#pragma unroll
+        for (int st = 0; st < KS; ++st)
+#pragma unroll
+            for (int ct = 0; ct < kTiles; ++ct) {
+                u32x4 pinned = pk[st][ct];
+                asm volatile("" : "+v"(pinned));
+                S.w[st][ct] = __builtin_bit_cast(bf16x8, pinned);
+            }
+    } else {
     // Loads of k-step st+1 are issued before the pieces of k-step st are
     // formed (the pinning below is a scheduling barrier, so a load placed
     // after it would wait for every earlier one): two weight round trips in
@@ -866,6 +891,7 @@ __device__ __forceinline__ void m_setup(MState<KS>& S, const CoopArgs& a, const 
             asm volatile("" : "+v"(pinned));
             S.w[st][ct] = __builtin_bit_cast(bf16x8, pinned);
         }
+    }
     }
 #pragma unroll
     for (int i = 0; i < Geo<KS>::kDmaW; ++i) {
@@ -1508,6 +1534,27 @@ __global__ __launch_bounds__(kMW * 64, 1) void k_part(CoopArgs a) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Weight packing (hc_pack_weights): block q, wave w forms member q's
+// pieces of stream w with m_setup's own conversion and stores the registers
+// as they are, so a packed call's weights are bitwise an unpacked call's.
+template <int KS>
+__global__ __launch_bounds__(kMW * 64) void k_pack(CoopArgs a, u32x4* out) {
+    RoundCtx c;
+    c.q = blockIdx.x;
+    c.g = 0;
+    c.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    c.l = threadIdx.x & 63;
+    c.row = c.l & 15;
+    c.grp = c.l >> 4;
+    MState<KS> S;
+    m_setup<KS>(S, a, c);
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+#pragma unroll
+        for (int ct = 0; ct < kTiles; ++ct)
+            out[packed_index<KS>(c.q, c.w, st, ct, c.l)] = __builtin_bit_cast(u32x4, S.w[st][ct]);
+}
+
 // Pass 2: a group of blocks per 4 tokens.  With splits > 1 column parts
 // (short calls, where the grid needs filling) the group has splits + 1
 // blocks: part sp < splits covers column part sp of h, and part splits runs
@@ -1708,6 +1755,31 @@ static int launch_ks(const CoopPlan& p, CoopArgs& a, bool fused, hipStream_t s) 
 
 static bool use_spec(const CoopPlan& p) { return spec_width(p.G); }
 
+size_t packed_weights_bytes(int d) {
+    const int KS = coop_ks(d);
+    if (!KS || !spec_width(d / (32 * KS))) return 0;
+    return (size_t)(d / (32 * KS)) * kHC * KS * kTiles * 64 * 16;
+}
+
+int launch_pack(const float* W, void* out, int d, hipStream_t s) {
+    const int KS = coop_ks(d);
+    CoopArgs a{};
+    a.W = W;
+    a.d = d;
+    a.Wp = nullptr;
+    const int G = d / (32 * KS);
+    u32x4* o = static_cast<u32x4*>(out);
+    switch (KS) {
+        case 1: spec::k_pack<1><<<G, spec::kMW * 64, 0, s>>>(a, o); break;
+        case 2: spec::k_pack<2><<<G, spec::kMW * 64, 0, s>>>(a, o); break;
+        case 3: spec::k_pack<3><<<G, spec::kMW * 64, 0, s>>>(a, o); break;
+        case 4: spec::k_pack<4><<<G, spec::kMW * 64, 0, s>>>(a, o); break;
+        case 5: spec::k_pack<5><<<G, spec::kMW * 64, 0, s>>>(a, o); break;
+        default: return -1;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 template <int KS>
 static int launch_two_pass(const CoopPlan& p, CoopArgs& a, bool fused, hipStream_t s) {
     spec::k_part<KS><<<p.G * p.NG, spec::kMW * 64, 0, s>>>(a);
@@ -1729,7 +1801,8 @@ static int launch_spec(const CoopPlan& p, CoopArgs& a, bool fused, hipStream_t s
 
 int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* scale, const float* base,
                 void* h, float* pre, float* post, float* comb, float* mixes, void* ws, int64_t n, int d,
-                int iters, float eps, float norm_eps, bool fused, hipStream_t s, const PostIn* prev) {
+                int iters, float eps, float norm_eps, bool fused, hipStream_t s, const PostIn* prev,
+                const void* Wp) {
     char* wsb = static_cast<char*>(ws);
     if (prev) {
         // hc_post, then the projection of its output.  (Applying hc_post to
@@ -1738,9 +1811,10 @@ int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* s
         // short call instead of the whole chip.)
         if (launch_post(prev->x, R, prev->post, prev->comb, prev->Rout, n, d, s)) return -1;
         return launch_coop(p, prev->Rout, W, scale, base, h, pre, post, comb, mixes, ws, n, d, iters, eps,
-                           norm_eps, fused, s, nullptr);
+                           norm_eps, fused, s, nullptr, Wp);
     }
     CoopArgs a;
+    a.Wp = static_cast<const u32x4*>(Wp);
     a.R = static_cast<const uint16_t*>(R);
     a.W = W;
     a.scale = scale;

@@ -50,8 +50,15 @@ struct PostIn {
     const float* comb;
     void* Rout;
 };
+// Wp: the weights already split by launch_pack (widths the wave-specialised
+// kernel serves only), or null to split W in each call.
 int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* scale, const float* base,
                 void* h, float* pre, float* post, float* comb, float* mixes, void* ws, int64_t n, int d,
-                int iters, float eps, float norm_eps, bool fused, hipStream_t s, const PostIn* prev = nullptr);
+                int iters, float eps, float norm_eps, bool fused, hipStream_t s, const PostIn* prev = nullptr,
+                const void* Wp = nullptr);
+// Bytes of packed weights for width d (0: d is not served by the
+// wave-specialised kernels), and the packing launch.
+size_t packed_weights_bytes(int d);
+int launch_pack(const float* W, void* out, int d, hipStream_t s);
 
 }  // namespace hc

@@ -209,6 +209,39 @@ int hc_post_mix_pre(const void *x, const void *R, const float *post,
                     float hc_eps, float norm_eps, void *stream);
 
 /*
+ * Weight packing, for callers that run one weight set many times (a model's
+ * layers at inference).  The projection uses each fp32 weight as three
+ * bf16 pieces (hi + mid + lo, exactly); hc_pack_weights forms those pieces
+ * once, in the register layout of the projection kernels, and
+ * hc_fused_mix_pre_packed then loads them instead of forming them in every
+ * call.  Results are bitwise those of hc_fused_mix_pre with the same hc_fn.
+ * Only widths d = 32*k*G with 8 <= G <= 32 (d = 5120 among them) have a
+ * packed form; other widths return HC_ERR_UNSUPPORTED.  The packed buffer
+ * is owned by the caller, device memory, 16-byte aligned, and must be
+ * packed again whenever hc_fn changes.
+ *
+ * hc_packed_weights_bytes: bytes of the packed form for d (0 if none;
+ *   3,276,800 at d = 5120).  Host-only query.
+ * hc_pack_weights: packed <- pieces of hc_fn (fp32 [24][hc*d]); enqueued on
+ *   `stream`.  HC_ERR_WORKSPACE if packed_bytes is too small.
+ * hc_fused_mix_pre_packed: hc_fused_mix_pre with `packed` in place of
+ *   hc_fn; all other arguments and rules as there.  HC_ERR_WORKSPACE if
+ *   packed_bytes is smaller than hc_packed_weights_bytes(hc, d).
+ */
+size_t hc_packed_weights_bytes(int32_t hc, int32_t d);
+
+int hc_pack_weights(const float *hc_fn, void *packed, size_t packed_bytes,
+                    int32_t hc, int32_t d, void *stream);
+
+int hc_fused_mix_pre_packed(const void *R, const void *packed,
+                            size_t packed_bytes, const float *hc_scale,
+                            const float *hc_base, void *h, float *pre,
+                            float *post, float *comb, float *mixes,
+                            void *workspace, size_t workspace_bytes, int64_t n,
+                            int32_t hc, int32_t d, int32_t sinkhorn_iters,
+                            float hc_eps, float norm_eps, void *stream);
+
+/*
  * Bytes of device workspace hc_mixes / hc_fused_mix_pre need for these
  * sizes on the current device (0 for n == 0; 0 with an unsupported shape,
  * in which case the call itself reports the error).  Host-only query.

@@ -157,6 +157,34 @@ def test_post_mix_pre_checks(lib):
     assert f(comb2=H + 0x2008 - 8) == ALIAS   # comb_next over post_next
 
 
+def test_packed_weights_checks(lib):
+    assert lib.hc_packed_weights_bytes(4, 5120) == 32 * 4 * 5 * 5 * 64 * 16
+    assert lib.hc_packed_weights_bytes(4, 64) == 0          # served by the cooperative kernel: no packed form
+    assert lib.hc_packed_weights_bytes(3, 5120) == 0
+    nb = lib.hc_packed_weights_bytes(4, 256)
+    assert nb > 0
+
+    def pk(W=A, out=B, nbytes=nb, hc=4, d=256):
+        return lib.hc_pack_weights(P(W), P(out), nbytes, hc, d, None)
+    assert pk(d=64) == UNSUP
+    assert pk(hc=5) == UNSUP
+    assert pk(d=40) == UNSUP or pk(d=40) == SHAPE
+    assert pk(W=0) == NULL
+    assert pk(out=B + 8) == ALIGN
+    assert pk(nbytes=nb - 16) == WS
+    assert pk(out=A + 1024) == ALIAS     # the packed form over the weights
+
+    def f(R=A, pkd=B, nbytes=nb, s=C, b=C + 64, h=D_, pre=E, post=E + 4096, comb=E + 8192, mix=0, ws=F_,
+          wsb=1 << 30, n=4, hc=4, d=256, it=20, eps=1e-6, neps=1e-20):
+        return lib.hc_fused_mix_pre_packed(P(R), P(pkd), nbytes, P(s), P(b), P(h), P(pre), P(post), P(comb),
+                                           P(mix), P(ws), wsb, n, hc, d, it, eps, neps, None)
+    assert f(n=0) == OK
+    assert f(pkd=0) == NULL
+    assert f(nbytes=16) == WS
+    assert f(d=64) == UNSUP
+    assert f(h=B) == ALIAS               # h over the packed weights
+
+
 def test_workspace_query(lib):
     assert lib.hc_fused_workspace_bytes(0, 4, 5120) == 0
     assert lib.hc_fused_workspace_bytes(16, 3, 5120) == 0

@@ -302,6 +302,21 @@ def test_post_mix_pre_matches_the_two_calls(orc, d, n):
         compare_fused(orc, Rp, nxt["W"], nxt["scale"], nxt["base"], tuple(got[1:]), label="post+mix n=%d" % n)
 
 
+@pytest.mark.parametrize("d,n", [(5120, 1), (5120, 64), (5120, 2048), (5120, 2100), (1024, 77), (256, 300)])
+def test_packed_weights_match_unpacked_bitwise(d, n):
+    # weights split once by hc_pack_weights give bitwise the results of the
+    # call that splits them itself, on the two-pass and the persistent path
+    w = hin.Workload("pk%d" % d, 1, n, 4, d, 1.0 / np.sqrt(4 * d), 0.5, 2.0, 1.0)
+    t = hin.make_inputs(w, DEV, seed=91)
+    packed = hcl.hc_pack_weights(t["W"])
+    ref = run_fused(t["R"], t["W"], t["scale"], t["base"])
+    got = hcl.hc_fused_mix_pre(t["R"], t["W"], t["scale"], t["base"], want_pre=True, want_mixes=True,
+                               packed=packed)
+    torch.cuda.synchronize()
+    for name, u, v in zip(("h", "pre", "post", "comb", "mixes"), got, ref):
+        assert torch.equal(u, v), (d, n, name)
+
+
 def test_workspace_reused_across_shapes():
     # one workspace through calls of different sizes and widths, mixes kept
     # in the workspace: every result equals that of a fresh workspace
