@@ -820,10 +820,13 @@ __device__ __forceinline__ void st_rec(const RoundCtx& c, int off, u32x4 v) {
                                            off, 0, LOCAL ? 0 : 16);
 }
 
+// Weight slice of stream w split into MFMA B fragments: k-step st, lane
+// (column i, k-block grp) holds features 32*st + 8*grp .. +7 of stream w of
+// the member slice, as the bf16 piece (hi, mid or lo) of column tile ct.
+// Each fragment is pinned in registers, which keeps the compiler from
+// re-forming the pieces inside the round loop.
 template <int KS>
-__device__ __forceinline__ void m_setup(MState<KS>& S, const CoopArgs& a, const RoundCtx& c) {
-    // weight slice of stream w: k-step st, lane (column i, k-block grp) holds
-    // features 32*st + 8*grp .. +7 of stream w of the member slice
+__device__ __forceinline__ void m_split_weights(MState<KS>& S, const CoopArgs& a, const RoundCtx& c) {
     const int64_t K = (int64_t)kHC * a.d;
     // piece (0 hi, 1 mid, 2 lo, -1 none) and weight row of column tile ct
     auto tile_piece = [&](int ct, int& piece, int& j) {
@@ -844,27 +847,10 @@ __device__ __forceinline__ void m_setup(MState<KS>& S, const CoopArgs& a, const 
             raw[ct][1] = src[1];
         }
     };
-    if (a.Wp) {
-        // pieces split once by k_pack, in this very register layout: every
-        // load is issued before the first pin
-        u32x4 pk[KS][kTiles];
-#pragma unroll
-        for (int st = 0; st < KS; ++st)
-#pragma unroll
-            for (int ct = 0; ct < kTiles; ++ct) pk[st][ct] = a.Wp[packed_index<KS>(c.q, c.w, st, ct, c.l)];
-#pragma unroll
-        for (int st = 0; st < KS; ++st)
-#pragma unroll
-            for (int ct = 0; ct < kTiles; ++ct) {
-                u32x4 pinned = pk[st][ct];
-                asm volatile("" : "+v"(pinned));
-                S.w[st][ct] = __builtin_bit_cast(bf16x8, pinned);
-            }
-    } else {
     // Loads of k-step st+1 are issued before the pieces of k-step st are
-    // formed (the pinning below is a scheduling barrier, so a load placed
-    // after it would wait for every earlier one): two weight round trips in
-    // flight instead of one per column tile.
+    // formed (the pin is a scheduling barrier, so a load placed after it
+    // would wait for every earlier one): two weight round trips in flight
+    // instead of one per column tile.
     f32x4 raw[2][kTiles][2];
     fetch(0, raw[0]);
 #pragma unroll
@@ -885,14 +871,36 @@ __device__ __forceinline__ void m_setup(MState<KS>& S, const CoopArgs& a, const 
                 const __bf16 lo = (__bf16)(r1 - (float)mid);
                 v[e] = piece == 0 ? hi : (piece == 1 ? mid : (piece == 2 ? lo : (__bf16)0.0f));
             }
-            // pinned in registers: keeps the compiler from re-forming the
-            // pieces inside the round loop
             u32x4 pinned = __builtin_bit_cast(u32x4, v);
             asm volatile("" : "+v"(pinned));
             S.w[st][ct] = __builtin_bit_cast(bf16x8, pinned);
         }
     }
-    }
+}
+
+// The same fragments from weights split once by k_pack, stored in this
+// register layout: every load is issued before the first pin.
+template <int KS>
+__device__ __forceinline__ void m_load_packed(MState<KS>& S, const CoopArgs& a, const RoundCtx& c) {
+    u32x4 pk[KS][kTiles];
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+#pragma unroll
+        for (int ct = 0; ct < kTiles; ++ct) pk[st][ct] = a.Wp[packed_index<KS>(c.q, c.w, st, ct, c.l)];
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+#pragma unroll
+        for (int ct = 0; ct < kTiles; ++ct) {
+            u32x4 pinned = pk[st][ct];
+            asm volatile("" : "+v"(pinned));
+            S.w[st][ct] = __builtin_bit_cast(bf16x8, pinned);
+        }
+}
+
+template <int KS>
+__device__ __forceinline__ void m_setup(MState<KS>& S, const CoopArgs& a, const RoundCtx& c) {
+    if (a.Wp) m_load_packed<KS>(S, a, c);
+    else m_split_weights<KS>(S, a, c);
 #pragma unroll
     for (int i = 0; i < Geo<KS>::kDmaW; ++i) {
         const int I = c.w * Geo<KS>::kDmaW + i;
@@ -1535,7 +1543,7 @@ __global__ __launch_bounds__(kMW * 64, 1) void k_part(CoopArgs a) {
 }
 
 // Weight packing (hc_pack_weights): block q, wave w forms member q's
-// pieces of stream w with m_setup's own conversion and stores the registers
+// pieces of stream w with the projection's own conversion and stores the registers
 // as they are, so a packed call's weights are bitwise an unpacked call's.
 template <int KS>
 __global__ __launch_bounds__(kMW * 64) void k_pack(CoopArgs a, u32x4* out) {
@@ -1547,7 +1555,7 @@ __global__ __launch_bounds__(kMW * 64) void k_pack(CoopArgs a, u32x4* out) {
     c.row = c.l & 15;
     c.grp = c.l >> 4;
     MState<KS> S;
-    m_setup<KS>(S, a, c);
+    m_split_weights<KS>(S, a, c);
 #pragma unroll
     for (int st = 0; st < KS; ++st)
 #pragma unroll

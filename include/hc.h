@@ -210,7 +210,9 @@ int hc_post_mix_pre(const void *x, const void *R, const float *post,
 
 /*
  * Weight packing, for callers that run one weight set many times (a model's
- * layers at inference).  The projection uses each fp32 weight as three
+ * layers at inference).  It computes nothing of the method: it re-arranges
+ * hc_fn, the projection weights of the "Mix projection" page's mix formula
+ * (float32), for the kernels.  The projection uses each fp32 weight as three
  * bf16 pieces (hi + mid + lo, exactly); hc_pack_weights forms those pieces
  * once, in the register layout of the projection kernels, and
  * hc_fused_mix_pre_packed then loads them instead of forming them in every
