@@ -137,6 +137,7 @@ struct CoopArgs {
     int part_bytes;
     uint64_t call;      // process-wide number of this call (sets the record epoch)
     const u32x4* Wp;    // weights already split into MFMA pieces (hc_pack_weights), or null
+    int ext_init;       // k_spec: the header was updated by a launch just before (k_hdr)
 };
 
 // Field f of a partial record (0..23 = the 24 dot products, 24 = sum of
@@ -1372,7 +1373,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
     // workgroup that is not resident within about two seconds (the launch
     // does not reserve the device) makes the call stop with the error flag.
     const int64_t nchunks = a.part_bytes / 16;
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == 0 && a.ext_init) {
+        // the header was updated by k_hdr, launched just before this kernel
+        local_mode = (int)__hip_atomic_load(&a.hdr->clear, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (threadIdx.x == 0) {
         bool ok = true;
         if (blockIdx.x == 0) {
             header_update(a.hdr, a.call, nchunks);
@@ -1674,6 +1678,17 @@ __global__ __launch_bounds__(256) void k_fin(CoopArgs a, int splits) {
 
 }  // namespace spec
 
+// Header update alone, before a call of the wave-specialised kernel that is
+// being captured into a graph.  k_spec's own start-up waits for the host's
+// number of this call to appear in the header; a replayed graph repeats the
+// number, so that wait would let workgroups run ahead of workgroup 0's
+// update.  With the update in a launch of its own, kernel order does it on
+// every replay (and since a replay repeats the epoch, the update orders the
+// record area cleared, which k_spec's workgroups then do in parallel).
+__global__ void k_hdr(WsHeader* hdr, int64_t nchunks, uint64_t call) {
+    if (threadIdx.x == 0) header_update(hdr, call, nchunks);
+}
+
 // Header update and record-area clearing before a call of the cooperative
 // kernel of narrow or wide streams (the wave-specialised kernel does this
 // at its own start).
@@ -1821,7 +1836,7 @@ int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* s
         return launch_coop(p, prev->Rout, W, scale, base, h, pre, post, comb, mixes, ws, n, d, iters, eps,
                            norm_eps, fused, s, nullptr, Wp);
     }
-    CoopArgs a;
+    CoopArgs a{};
     a.Wp = static_cast<const u32x4*>(Wp);
     a.R = static_cast<const uint16_t*>(R);
     a.W = W;
@@ -1864,7 +1879,14 @@ int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* s
         k_init<<<1, 1024, 0, s>>>(a.hdr, a.part, (int64_t)(a.part_bytes / 16), a.call);
         if (hipGetLastError() != hipSuccess) return -1;
     }
+    a.ext_init = 0;
     if (use_spec(p)) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+            a.ext_init = 1;
+            k_hdr<<<1, 64, 0, s>>>(a.hdr, (int64_t)(a.part_bytes / 16), a.call);
+            if (hipGetLastError() != hipSuccess) return -1;
+        }
         switch (p.KS) {
             case 1: rc = launch_spec<1>(p, a, fused, s); break;
             case 2: rc = launch_spec<2>(p, a, fused, s); break;

@@ -317,6 +317,49 @@ def test_packed_weights_match_unpacked_bitwise(d, n):
         assert torch.equal(u, v), (d, n, name)
 
 
+@pytest.mark.parametrize("d,n", [(5120, 64), (5120, 4096), (64, 77)])
+def test_graph_capture_replays_bitwise(d, n):
+    # the fused call and hc_post captured into one HIP graph, on the
+    # two-pass (64 tokens), persistent (4,096) and cooperative (d = 64)
+    # paths: every replay, with eager calls of the library in between,
+    # gives bitwise the eager results
+    w = hin.Workload("g%d" % d, 1, n, 4, d, 1.0 / np.sqrt(4 * d), 0.5, 2.0, 1.0)
+    t = hin.make_inputs(w, DEV, seed=97)
+    R, x, W, s, b = t["R"], t["x"], t["W"], t["scale"], t["base"]
+    ws = hcl.Workspace()
+    outs = dict(h=torch.empty(1, n, d, dtype=torch.bfloat16, device=DEV), pre=torch.empty(1, n, 4, device=DEV),
+                post=torch.empty(1, n, 4, device=DEV), comb=torch.empty(1, n, 4, 4, device=DEV),
+                mixes=torch.empty(1, n, 24, device=DEV))
+    Rout = torch.empty_like(R)
+
+    def step():
+        hcl.hc_fused_mix_pre(R, W, s, b, want_pre=True, want_mixes=True, workspace=ws, out=outs)
+        hcl.hc_post(x, R, outs["post"], outs["comb"], out=Rout)
+
+    step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in outs.items()}
+    ref["Rout"] = Rout.clone()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for v in list(outs.values()) + [Rout]:
+            v.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in list(outs.items()) + [("Rout", Rout)]:
+            assert torch.equal(v, ref[k]), (d, n, rep, k)
+        hcl.hc_fused_mix_pre(R, W, s, b, workspace=ws)      # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_workspace_reused_across_shapes():
     # one workspace through calls of different sizes and widths, mixes kept
     # in the workspace: every result equals that of a fresh workspace
