@@ -282,6 +282,9 @@ def main():
     ap.add_argument("--packed", action="store_true",
                     help="split the weights once before timing (hc_pack_weights) and run the fused call "
                          "on the packed form")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a HIP graph (captured once before timing); "
+                         "value is then the replay rate")
     ap.add_argument("--boundary", action="store_true",
                     help="time the sublayer boundary instead: one hc_post_mix_pre call (hc_post of "
                          "this sublayer, then the next one's fused mix + Sinkhorn + hc_pre)")
@@ -374,6 +377,28 @@ def main():
         return float(v.mean()), float(np.median(v)), float(v.min())
 
     f_mean, f_med, f_min = stats([(fa, fz) for fa, fz, _, _ in inner])
+
+    # ---- the same step replayed from a HIP graph: launch overheads gone
+    graph_ms = None
+    if args.graph:
+        side = torch.cuda.Stream(dev)
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step()
+        for _ in range(args.warmup):
+            gr.replay()
+        torch.cuda.synchronize()
+        g0, g1 = ev(), ev()
+        g0.record(stream)
+        for _ in range(args.steps):
+            gr.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+        del gr
     p_mean, p_med, p_min = stats([(pa, pz) for _, _, pa, pz in inner])
 
     # ---- the same launches timed in isolation (information): back to back
@@ -454,6 +479,9 @@ def main():
                "sample": "%d pass(es) over the first %d of %d tokens of the same inputs (fused "
                          "mix+Sinkhorn+pre, then hc_post), %.1f s" % (passes, k, n, csec)}
 
+    eager_ms = ms_step
+    if graph_ms is not None:
+        ms_step = graph_ms
     tok_s = n / (ms_step * 1e-3)
     line = {
         "metric": "tokens/s + achieved HBM GB/s (% of peak), fused hc mix+pre and hc_post, d=5120",
@@ -468,9 +496,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) residual and sublayer output, N(0,0.007) weights)",
-        "config": {"workload": "%s: B=%d T=%d hc=4 d=%d (%d tokens), sinkhorn_iters=%d%s"
+        "config": {"workload": "%s: B=%d T=%d hc=4 d=%d (%d tokens), sinkhorn_iters=%d%s%s"
                                % (w.name, w.B, w.T, d, n, w.iters,
-                                  ", weights packed once before timing" if args.packed else ""),
+                                  ", weights packed once before timing" if args.packed else "",
+                                  ", step replayed from a HIP graph (eager step %.4f ms)" % eager_ms
+                                  if graph_ms is not None else ""),
                    "tokens": n, "d": d, "hc": 4, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dom["name"], "achieved": round(dom["gbs"], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4),
