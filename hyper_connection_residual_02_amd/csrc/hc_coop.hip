@@ -803,6 +803,8 @@ struct XState {
     u32x2 rb[2][Geo<KS>::kPass][kHC];      // residual for h, two rounds (by parity)
     u32x4 P[kXL];                          // records of the next exchange (issued a tick early)
     u32x4 O[kXL];
+    int pb, ob;                            // lane offsets of the pre and owner loads of load s = 0 in a
+                                           // round's slot (load s adds s * kLoadStride)
 };
 
 // Record stores and loads.  Loads are device scope (sc1): they skip the
@@ -1109,22 +1111,27 @@ __device__ __forceinline__ bool pre_live(const CoopArgs& a, const RoundCtx& c, i
 __device__ __forceinline__ bool own_live(const CoopArgs& a, const RoundCtx& c, int xw, int s) {
     return xw < c.nown && x_member(c, s) < a.G && (c.l & 15) < kChunks;
 }
-__device__ __forceinline__ int pre_off(const CoopArgs& a, const RoundCtx& c, int r, int xw, int s) {
-    const int e = c.l & 15;
-    return srec_off(a, c, r, x_member(c, s), srec_index(e & 1, kTokX * xw + (e >> 1)));
-}
-__device__ __forceinline__ int own_off(const CoopArgs& a, const RoundCtx& c, int r, int xw, int s) {
-    return srec_off(a, c, r, x_member(c, s), srec_index(c.l & 15, c.q + a.G * xw));
-}
-
 // Record loads of round r for exchange wave xw: the pre-relevant records
 // (chunks 0 and 1) of tokens 8xw..8xw+7 and all records of owned token xw.
+// Offsets: load s reads member 4s + lane / 16, so its offset within a
+// round's slot is that of load 0 plus s * kLoadStride; the lane part is
+// computed once (x_offsets) and each load costs one add.
+constexpr int kLoadStride = 4 * kRecMember * 16;
+template <int KS>
+__device__ __forceinline__ void x_offsets(XState<KS>& X, const CoopArgs& a, const RoundCtx& c, int xw) {
+    const int e = c.l & 15, mem0 = c.l >> 4;
+    X.pb = (mem0 * kRecMember + srec_index(e & 1, kTokX * xw + (e >> 1))) * 16;
+    X.ob = (mem0 * kRecMember + srec_index(e, c.q + a.G * xw)) * 16;
+}
 template <int KS, bool FUSED, bool LOCAL>
 __device__ __forceinline__ void x_issue(XState<KS>& X, const CoopArgs& a, const RoundCtx& c, int xw, int r) {
+    const int slot = ((c.g * kSlots + r % kSlots) * a.GP) * kRecMember * 16;    // srec_off of member 0, record 0
 #pragma unroll
-    for (int s = 0; s < kXL; ++s) X.P[s] = ld_rec<LOCAL>(c, pre_live<FUSED>(a, c, s) ? pre_off(a, c, r, xw, s) : kOOB);
+    for (int s = 0; s < kXL; ++s)
+        X.P[s] = ld_rec<LOCAL>(c, pre_live<FUSED>(a, c, s) ? slot + X.pb + s * kLoadStride : kOOB);
 #pragma unroll
-    for (int s = 0; s < kXL; ++s) X.O[s] = ld_rec<LOCAL>(c, own_live(a, c, xw, s) ? own_off(a, c, r, xw, s) : kOOB);
+    for (int s = 0; s < kXL; ++s)
+        X.O[s] = ld_rec<LOCAL>(c, own_live(a, c, xw, s) ? slot + X.ob + s * kLoadStride : kOOB);
 }
 
 // Exchange of round r for exchange wave xw, from the loads issued by
@@ -1329,6 +1336,7 @@ __device__ __forceinline__ void spec_body(const CoopArgs& a, const RoundCtx& c, 
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
         XState<KS> X;
+        x_offsets<KS>(X, a, c, c.w - kMW);
         __syncthreads();
         for (int t = 0;; t += 2) {
             if (x_tick<KS, FUSED, LOCAL, 0>(X, a, c, L, t)) L.stop = 1;
