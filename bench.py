@@ -29,12 +29,12 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E peak, GB/s
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
-def algorithmic_bytes(n: int, d: int):
+def algorithmic_bytes(n: int, d: int, hc: int = 4):
     """Minimum HBM bytes per launch: every input read once, every output
-    written once.  fused: R + h + pre/post/comb (+ the weights, once per
-    launch); hc_post: R + x + post/comb + R'."""
-    hc = 4
-    fused = n * (hc * d * 2 + d * 2 + (hc + hc + hc * hc) * 4) + 24 * hc * d * 4 + 27 * 4
+    written once.  fused: R + h + pre/post/comb (+ the weights, scale and
+    base, once per launch); hc_post: R + x + post/comb + R'."""
+    M = (2 + hc) * hc
+    fused = n * (hc * d * 2 + d * 2 + (hc + hc + hc * hc) * 4) + M * hc * d * 4 + (3 + M) * 4
     post = n * (hc * d * 2 + d * 2 + (hc + hc * hc) * 4 + hc * d * 2)
     return fused, post
 
@@ -265,6 +265,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="large", choices=["large", "prefill", "decode"])
+    ap.add_argument("--hc", type=int, default=4,
+                    help="streams per token (1..8); other than 4 runs the plain kernels of hc_general.hip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=65536, help="tokens per oracle pass")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -319,14 +321,20 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = hin.WORKLOADS[args.workload]
+    if args.hc != w.hc:
+        if args.packed or args.boundary:
+            print("--hc other than 4 runs the plain step only (no --packed, no --boundary)", file=sys.stderr)
+            sys.exit(2)
+        import dataclasses
+        w = dataclasses.replace(w, hc=args.hc)
     n, d = w.n, w.d
     t = hin.make_inputs(w, dev)
     R, x, W, s, b = t["R"], t["x"], t["W"], t["scale"], t["base"]
     ws = hcl.Workspace()
     outs = dict(h=torch.empty(w.B, w.T, d, dtype=torch.bfloat16, device=dev),
-                pre=torch.empty(w.B, w.T, 4, device=dev),
-                post=torch.empty(w.B, w.T, 4, device=dev),
-                comb=torch.empty(w.B, w.T, 4, 4, device=dev))
+                pre=torch.empty(w.B, w.T, w.hc, device=dev),
+                post=torch.empty(w.B, w.T, w.hc, device=dev),
+                comb=torch.empty(w.B, w.T, w.hc, w.hc, device=dev))
     Rout = torch.empty_like(R)
     packed = hcl.hc_pack_weights(W) if args.packed else None
     if args.boundary:
@@ -442,7 +450,7 @@ def main():
                 "warm_frac_of_peak": round(bytes_ / (warm[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "cold_avg_us": round(cold[0], 2), "cold_min_us": round(cold[2], 2),
                 "cold_frac_of_peak": round(bytes_ / (cold[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-    fb, pb = algorithmic_bytes(n, d)
+    fb, pb = algorithmic_bytes(n, d, w.hc)
     f_gbs = fb / (f_mean * 1e-6) / 1e9
     p_gbs = pb / (p_mean * 1e-6) / 1e9
 
@@ -457,7 +465,9 @@ def main():
         dom = dict(name="hc_post", kernel="k_post", us=p_mean, bytes=pb, gbs=p_gbs)
     else:
         dom = dict(name="hc_fused_mix_pre", kernel="k_spec", us=f_mean, bytes=fb, gbs=f_gbs)
-    traffic = measured_traffic(dom["kernel"], n, d)
+    if w.hc != 4:
+        dom["kernel"] = "k_gpost" if dom["name"] == "hc_post" else "k_gmix + k_gsplit + k_gpre"
+    traffic = measured_traffic(dom["kernel"], n, d) if w.hc == 4 else None
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample of the same workload
     cpu = None
@@ -465,7 +475,7 @@ def main():
         import oracle
         oracle.build(force=False)
         k = min(args.cpu_sample, n)
-        Rb = hin.bits(R.reshape(n, 4, d)[:k])
+        Rb = hin.bits(R.reshape(n, w.hc, d)[:k])
         xb = hin.bits(x.reshape(n, d)[:k])
         Wn, sn, bn = W.cpu().numpy(), s.cpu().numpy(), b.cpu().numpy()
         passes = 0
@@ -496,12 +506,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) residual and sublayer output, N(0,0.007) weights)",
-        "config": {"workload": "%s: B=%d T=%d hc=4 d=%d (%d tokens), sinkhorn_iters=%d%s%s"
-                               % (w.name, w.B, w.T, d, n, w.iters,
+        "config": {"workload": "%s: B=%d T=%d hc=%d d=%d (%d tokens), sinkhorn_iters=%d%s%s"
+                               % (w.name, w.B, w.T, w.hc, d, n, w.iters,
                                   ", weights packed once before timing" if args.packed else "",
                                   ", step replayed from a HIP graph (eager step %.4f ms)" % eager_ms
                                   if graph_ms is not None else ""),
-                   "tokens": n, "d": d, "hc": 4, "parallelism": "single GPU"},
+                   "tokens": n, "d": d, "hc": w.hc, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dom["name"], "achieved": round(dom["gbs"], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": dom["bytes"],

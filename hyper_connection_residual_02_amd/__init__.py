@@ -142,6 +142,13 @@ def _workspace(ws, nbytes, dev):
     return ws.get(max(int(nbytes), 256), dev)
 
 
+def _streams(R: torch.Tensor) -> int:
+    """Stream count hc of a residual [..., hc, d] (libhc serves 1..8)."""
+    if R.dim() < 2:
+        raise ValueError("R must have shape [..., hc, d], got %s" % (tuple(R.shape),))
+    return int(R.shape[-2])
+
+
 def _lead(R: torch.Tensor, hc: int, name="R"):
     if R.dim() < 2 or R.shape[-2] != hc:
         raise ValueError("%s must have shape [..., %d, d], got %s" % (name, hc, tuple(R.shape)))
@@ -156,16 +163,18 @@ def _lead(R: torch.Tensor, hc: int, name="R"):
 
 def hc_mixes(R: torch.Tensor, hc_fn: torch.Tensor, norm_eps: float = 1e-20,
              out: torch.Tensor | None = None, workspace: Workspace | None = None) -> torch.Tensor:
-    """mixes = (flatten(R) @ hc_fn^T) / RMS(flatten(R)); [..., 24] fp32."""
+    """mixes = (flatten(R) @ hc_fn^T) / RMS(flatten(R)); [..., (2+hc)*hc] fp32,
+    hc = R.shape[-2] (1..8)."""
     dev = R.device
     _check(R, "R", torch.bfloat16)
     _check(hc_fn, "hc_fn", torch.float32, dev)
-    hc = 4
+    hc = _streams(R)
+    M = (2 + hc) * hc
     lead, n, d = _lead(R, hc)
-    if tuple(hc_fn.shape) != (HC_MIX, hc * d):
-        raise ValueError("hc_fn must be [24, %d], got %s" % (hc * d, tuple(hc_fn.shape)))
+    if tuple(hc_fn.shape) != (M, hc * d):
+        raise ValueError("hc_fn must be [%d, %d], got %s" % (M, hc * d, tuple(hc_fn.shape)))
     if out is None:
-        out = torch.empty(*lead, HC_MIX, dtype=torch.float32, device=dev)
+        out = torch.empty(*lead, M, dtype=torch.float32, device=dev)
     _check(out, "out", torch.float32, dev)
     wp, wb = _workspace(workspace, hc_fused_workspace_bytes(n, hc, d), dev)
     with torch.cuda.device(dev):
@@ -176,7 +185,7 @@ def hc_mixes(R: torch.Tensor, hc_fn: torch.Tensor, norm_eps: float = 1e-20,
 
 def hc_split_sinkhorn(mixes: torch.Tensor, hc_scale: torch.Tensor, hc_base: torch.Tensor,
                       hc_mult: int = 4, sinkhorn_iters: int = 20, eps: float = 1e-6):
-    """(pre [...,hc], post [...,hc], comb [...,hc,hc]) from mixes [..., 24]."""
+    """(pre [...,hc], post [...,hc], comb [...,hc,hc]) from mixes [..., (2+hc)*hc]."""
     dev = mixes.device
     _check(mixes, "mixes", torch.float32)
     _check(hc_scale, "hc_scale", torch.float32, dev)
@@ -200,7 +209,8 @@ def hc_pre(R: torch.Tensor, pre: torch.Tensor, out: torch.Tensor | None = None) 
     dev = R.device
     _check(R, "R", torch.bfloat16)
     _check(pre, "pre", torch.float32, dev)
-    hc = 4
+    hc = _streams(R)
+    M = (2 + hc) * hc
     lead, n, d = _lead(R, hc)
     if tuple(pre.shape) != lead + (hc,):
         raise ValueError("pre must be %s" % (lead + (hc,),))
@@ -221,7 +231,8 @@ def hc_post(x: torch.Tensor, R: torch.Tensor, post: torch.Tensor, comb: torch.Te
     _check(R, "R", torch.bfloat16)
     _check(post, "post", torch.float32, dev)
     _check(comb, "comb", torch.float32, dev)
-    hc = 4
+    hc = _streams(R)
+    M = (2 + hc) * hc
     lead, n, d = _lead(R, hc)
     if tuple(x.shape) != lead + (d,) or tuple(post.shape) != lead + (hc,) or \
             tuple(comb.shape) != lead + (hc, hc):
@@ -268,10 +279,11 @@ def hc_fused_mix_pre(R: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tenso
     _check(R, "R", torch.bfloat16)
     for t, nm in ((hc_fn, "hc_fn"), (hc_scale, "hc_scale"), (hc_base, "hc_base")):
         _check(t, nm, torch.float32, dev)
-    hc = 4
+    hc = _streams(R)
+    M = (2 + hc) * hc
     lead, n, d = _lead(R, hc)
-    if tuple(hc_fn.shape) != (HC_MIX, hc * d):
-        raise ValueError("hc_fn must be [24, %d]" % (hc * d))
+    if tuple(hc_fn.shape) != (M, hc * d):
+        raise ValueError("hc_fn must be [%d, %d]" % (M, hc * d))
     o = dict(out or {})
     h = o.get("h") if o.get("h") is not None else torch.empty(*lead, d, dtype=torch.bfloat16, device=dev)
     post = o.get("post") if o.get("post") is not None else torch.empty(*lead, hc, dtype=torch.float32, device=dev)
@@ -281,7 +293,7 @@ def hc_fused_mix_pre(R: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tenso
         pre = torch.empty(*lead, hc, dtype=torch.float32, device=dev)
     mixes = o.get("mixes")
     if mixes is None and want_mixes:
-        mixes = torch.empty(*lead, HC_MIX, dtype=torch.float32, device=dev)
+        mixes = torch.empty(*lead, M, dtype=torch.float32, device=dev)
     wp, wb = _workspace(workspace, hc_fused_workspace_bytes(n, hc, d), dev)
     with torch.cuda.device(dev):
         if packed is not None:
@@ -311,12 +323,13 @@ def hc_post_mix_pre(x: torch.Tensor, R: torch.Tensor, post: torch.Tensor, comb: 
     _check(comb, "comb", torch.float32, dev)
     for t, nm in ((hc_fn, "hc_fn"), (hc_scale, "hc_scale"), (hc_base, "hc_base")):
         _check(t, nm, torch.float32, dev)
-    hc = 4
+    hc = _streams(R)
+    M = (2 + hc) * hc
     lead, n, d = _lead(R, hc)
     if tuple(x.shape) != tuple(lead) + (d,):
         raise ValueError("x must be %s" % ((*lead, d),))
-    if tuple(hc_fn.shape) != (HC_MIX, hc * d):
-        raise ValueError("hc_fn must be [24, %d]" % (hc * d))
+    if tuple(hc_fn.shape) != (M, hc * d):
+        raise ValueError("hc_fn must be [%d, %d]" % (M, hc * d))
     if out_R is None:
         out_R = torch.empty_like(R)
     _check(out_R, "out_R", torch.bfloat16, dev)
@@ -329,7 +342,7 @@ def hc_post_mix_pre(x: torch.Tensor, R: torch.Tensor, post: torch.Tensor, comb: 
         pre2 = torch.empty(*lead, hc, dtype=torch.float32, device=dev)
     mixes = o.get("mixes")
     if mixes is None and want_mixes:
-        mixes = torch.empty(*lead, HC_MIX, dtype=torch.float32, device=dev)
+        mixes = torch.empty(*lead, M, dtype=torch.float32, device=dev)
     wp, wb = _workspace(workspace, hc_fused_workspace_bytes(n, hc, d), dev)
     with torch.cuda.device(dev):
         _call("hc_post_mix_pre", _ptr(x), _ptr(R), _ptr(post), _ptr(comb), _ptr(out_R), _ptr(hc_fn),

@@ -44,7 +44,7 @@ bool finite_nonneg(float v) { return isfinite(v) && v >= 0.0f; }
 
 int check_nd(int64_t n, int32_t hc, int32_t d) {
     if (n < 0 || d <= 0 || d % 8 != 0) return HC_ERR_SHAPE;
-    if (hc != 4) return HC_ERR_UNSUPPORTED;
+    if (hc != 4 && !hc::gen_hc(hc)) return HC_ERR_UNSUPPORTED;
     if (n > 0 && n > kMaxElems / ((int64_t)hc * d)) return HC_ERR_SHAPE;
     return HC_OK;
 }
@@ -59,7 +59,7 @@ const char* hc_status_str(int s) {
         case HC_ERR_NULL: return "HC_ERR_NULL: a required pointer is NULL";
         case HC_ERR_SHAPE: return "HC_ERR_SHAPE: bad n or d (n >= 0, d > 0, d % 8 == 0)";
         case HC_ERR_ALIGN: return "HC_ERR_ALIGN: tensor pointers must be 16-byte aligned (scale/base 4-byte)";
-        case HC_ERR_UNSUPPORTED: return "HC_ERR_UNSUPPORTED: hc must be 4, sinkhorn_iters >= 1, d tileable";
+        case HC_ERR_UNSUPPORTED: return "HC_ERR_UNSUPPORTED: hc must be 1..8 (4 for packed weights), sinkhorn_iters >= 1, d tileable";
         case HC_ERR_WORKSPACE: return "HC_ERR_WORKSPACE: workspace missing or too small";
         case HC_ERR_ALIAS: return "HC_ERR_ALIAS: an output overlaps an input or another output";
         case HC_ERR_VALUE: return "HC_ERR_VALUE: epsilon must be finite and >= 0";
@@ -79,8 +79,10 @@ int hc_pre(const void* R, const float* pre, void* h, int64_t n, int32_t hc_, int
     if (!al16(R) || !al16(pre) || !al16(h)) return HC_ERR_ALIGN;
     const uint64_t nd = (uint64_t)n * d;
     Span sh = span(h, nd * 2);
-    if (overlap(sh, span(R, nd * 4 * 2)) || overlap(sh, span(pre, (uint64_t)n * 4 * 4))) return HC_ERR_ALIAS;
-    return hc::launch_pre(R, pre, h, n, d, (hipStream_t)stream) ? HC_ERR_LAUNCH : HC_OK;
+    if (overlap(sh, span(R, nd * hc_ * 2)) || overlap(sh, span(pre, (uint64_t)n * hc_ * 4))) return HC_ERR_ALIAS;
+    const int e = hc_ == 4 ? hc::launch_pre(R, pre, h, n, d, (hipStream_t)stream)
+                           : hc::launch_gen_pre(R, pre, h, n, hc_, d, (hipStream_t)stream);
+    return e ? HC_ERR_LAUNCH : HC_OK;
 }
 
 int hc_post(const void* x, const void* R, const float* post, const float* comb, void* R_out, int64_t n,
@@ -91,12 +93,14 @@ int hc_post(const void* x, const void* R, const float* post, const float* comb, 
     if (!x || !R || !post || !comb || !R_out) return HC_ERR_NULL;
     if (!al16(x) || !al16(R) || !al16(post) || !al16(comb) || !al16(R_out)) return HC_ERR_ALIGN;
     const uint64_t nd = (uint64_t)n * d;
-    Span so = span(R_out, nd * 4 * 2);
-    if (R_out != R && overlap(so, span(R, nd * 4 * 2))) return HC_ERR_ALIAS;
-    if (overlap(so, span(x, nd * 2)) || overlap(so, span(post, (uint64_t)n * 16)) ||
-        overlap(so, span(comb, (uint64_t)n * 64)))
+    Span so = span(R_out, nd * hc_ * 2);
+    if (R_out != R && overlap(so, span(R, nd * hc_ * 2))) return HC_ERR_ALIAS;
+    if (overlap(so, span(x, nd * 2)) || overlap(so, span(post, (uint64_t)n * hc_ * 4)) ||
+        overlap(so, span(comb, (uint64_t)n * hc_ * hc_ * 4)))
         return HC_ERR_ALIAS;
-    return hc::launch_post(x, R, post, comb, R_out, n, d, (hipStream_t)stream) ? HC_ERR_LAUNCH : HC_OK;
+    const int e = hc_ == 4 ? hc::launch_post(x, R, post, comb, R_out, n, d, (hipStream_t)stream)
+                           : hc::launch_gen_post(x, R, post, comb, R_out, n, hc_, d, (hipStream_t)stream);
+    return e ? HC_ERR_LAUNCH : HC_OK;
 }
 
 int hc_diag_scale(const void* h, const void* D, void* x, int64_t n, int32_t d, void* stream) {
@@ -114,27 +118,31 @@ int hc_diag_scale(const void* h, const void* D, void* x, int64_t n, int32_t d, v
 int hc_split_sinkhorn(const float* mixes, const float* hc_scale, const float* hc_base, float* pre, float* post,
                       float* comb, int64_t n, int32_t hc_, int32_t sinkhorn_iters, float hc_eps, void* stream) {
     if (n < 0) return HC_ERR_SHAPE;
-    if (hc_ != 4 || sinkhorn_iters < 1) return HC_ERR_UNSUPPORTED;
+    if ((hc_ != 4 && !hc::gen_hc(hc_)) || sinkhorn_iters < 1) return HC_ERR_UNSUPPORTED;
     if (!finite_nonneg(hc_eps)) return HC_ERR_VALUE;
-    if (n > kMaxElems / 64) return HC_ERR_SHAPE;
+    const uint64_t M = (uint64_t)(2 + hc_) * hc_;
+    if (n > kMaxElems / (int64_t)M) return HC_ERR_SHAPE;
     if (n == 0) return HC_OK;
     if (!mixes || !hc_scale || !hc_base || !pre || !post || !comb) return HC_ERR_NULL;
     if (!al16(mixes) || !al16(pre) || !al16(post) || !al16(comb) || !al4(hc_scale) || !al4(hc_base))
         return HC_ERR_ALIGN;
-    const Span ins[] = {span(mixes, (uint64_t)n * 96), span(hc_scale, 12), span(hc_base, 96)};
-    const Span outs[] = {span(pre, (uint64_t)n * 16), span(post, (uint64_t)n * 16), span(comb, (uint64_t)n * 64)};
+    const Span ins[] = {span(mixes, (uint64_t)n * M * 4), span(hc_scale, 12), span(hc_base, M * 4)};
+    const Span outs[] = {span(pre, (uint64_t)n * hc_ * 4), span(post, (uint64_t)n * hc_ * 4),
+                         span(comb, (uint64_t)n * hc_ * hc_ * 4)};
     for (const Span& o : outs)
         for (const Span& i : ins)
             if (overlap(o, i)) return HC_ERR_ALIAS;
     if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2])) return HC_ERR_ALIAS;
-    return hc::launch_split(mixes, hc_scale, hc_base, pre, post, comb, n, sinkhorn_iters, hc_eps,
-                            (hipStream_t)stream)
-               ? HC_ERR_LAUNCH
-               : HC_OK;
+    const int e = hc_ == 4 ? hc::launch_split(mixes, hc_scale, hc_base, pre, post, comb, n, sinkhorn_iters, hc_eps,
+                                              (hipStream_t)stream)
+                           : hc::launch_gen_split(mixes, hc_scale, hc_base, pre, post, comb, n, hc_, sinkhorn_iters,
+                                                  hc_eps, (hipStream_t)stream);
+    return e ? HC_ERR_LAUNCH : HC_OK;
 }
 
 size_t hc_fused_workspace_bytes(int64_t n, int32_t hc_, int32_t d) {
     if (check_nd(n, hc_, d) != HC_OK || n == 0) return 0;
+    if (hc_ != 4) return hc::gen_ws_bytes(n, hc_);
     hc::CoopPlan p;
     if (!hc::coop_plan(n, d, p)) return 0;
     return p.ws_bytes;
@@ -157,6 +165,20 @@ static int coop_common(const void* R, const float* hc_fn, void* workspace, size_
 
 int hc_mixes(const void* R, const float* hc_fn, float* mixes, int64_t n, int32_t hc_, int32_t d, float norm_eps,
              void* workspace, size_t workspace_bytes, void* stream) {
+    if (hc_ != 4) {
+        // other stream counts: one plain kernel, no workspace
+        int st = check_nd(n, hc_, d);
+        if (st) return st;
+        if (!finite_nonneg(norm_eps)) return HC_ERR_VALUE;
+        if (n == 0) return HC_OK;
+        if (!R || !hc_fn || !mixes) return HC_ERR_NULL;
+        if (!al16(R) || !al16(hc_fn) || !al16(mixes)) return HC_ERR_ALIGN;
+        const uint64_t K = (uint64_t)hc_ * d, M = (uint64_t)(2 + hc_) * hc_;
+        const Span sm = span(mixes, (uint64_t)n * M * 4);
+        if (overlap(sm, span(R, (uint64_t)n * K * 2)) || overlap(sm, span(hc_fn, M * K * 4))) return HC_ERR_ALIAS;
+        return hc::launch_gen_mixes(R, hc_fn, mixes, n, hc_, d, norm_eps, (hipStream_t)stream) ? HC_ERR_LAUNCH
+                                                                                              : HC_OK;
+    }
     hc::CoopPlan p;
     int st = coop_common(R, hc_fn, workspace, workspace_bytes, n, hc_, d, norm_eps, p);
     if (st || n == 0) return st;
@@ -175,13 +197,79 @@ int hc_mixes(const void* R, const float* hc_fn, float* mixes, int64_t n, int32_t
 
 }  // extern "C"
 
+// hc_fused_mix_pre (and, with prev, hc_post_mix_pre) for stream counts other
+// than four: the checks of the four-stream call with hc-sized buffers, then
+// the plain kernels in sequence.
+static int gen_fused(const hc::PostIn* prev, const void* R, const float* hc_fn, const float* hc_scale,
+                     const float* hc_base, void* h, float* pre, float* post, float* comb, float* mixes,
+                     void* workspace, size_t workspace_bytes, int64_t n, int32_t hc_, int32_t d,
+                     int32_t sinkhorn_iters, float hc_eps, float norm_eps, void* stream) {
+    int st = check_nd(n, hc_, d);
+    if (st) return st;
+    if (sinkhorn_iters < 1) return HC_ERR_UNSUPPORTED;
+    if (!finite_nonneg(hc_eps) || !finite_nonneg(norm_eps)) return HC_ERR_VALUE;
+    if (n == 0) return HC_OK;
+    if (!R || !hc_fn || !hc_scale || !hc_base || !h || !post || !comb) return HC_ERR_NULL;
+    if (prev && (!prev->x || !prev->post || !prev->comb || !prev->Rout)) return HC_ERR_NULL;
+    if (!workspace) return HC_ERR_WORKSPACE;
+    const size_t wsb = hc::gen_ws_bytes(n, hc_);
+    if (workspace_bytes < wsb) return HC_ERR_WORKSPACE;
+    if (!al16(R) || !al16(hc_fn) || ((uintptr_t)workspace & 255u) || !al4(hc_scale) || !al4(hc_base) || !al16(h) ||
+        !al16(post) || !al16(comb) || (pre && !al16(pre)) || (mixes && !al16(mixes)))
+        return HC_ERR_ALIGN;
+    if (prev && (!al16(prev->x) || !al16(prev->post) || !al16(prev->comb))) return HC_ERR_ALIGN;
+    const uint64_t K = (uint64_t)hc_ * d, M = (uint64_t)(2 + hc_) * hc_;
+    const void* Rin = prev ? prev->Rout : R;   // the stream the projection reads
+    const Span sR = span(R, (uint64_t)n * K * 2), sRin = span(Rin, (uint64_t)n * K * 2);
+    if (prev && Rin != R && overlap(sRin, sR)) return HC_ERR_ALIAS;
+    Span ins[8];
+    int ni = 0;
+    ins[ni++] = sR;
+    ins[ni++] = span(hc_fn, M * K * 4);
+    ins[ni++] = span(hc_scale, 12);
+    ins[ni++] = span(hc_base, M * 4);
+    ins[ni++] = span(workspace, wsb);
+    if (prev) {
+        ins[ni++] = span(prev->x, (uint64_t)n * d * 2);
+        ins[ni++] = span(prev->post, (uint64_t)n * hc_ * 4);
+        ins[ni++] = span(prev->comb, (uint64_t)n * hc_ * hc_ * 4);
+    }
+    Span outs[6];
+    int no = 0;
+    if (prev) outs[no++] = sRin;
+    outs[no++] = span(h, (uint64_t)n * d * 2);
+    outs[no++] = span(post, (uint64_t)n * hc_ * 4);
+    outs[no++] = span(comb, (uint64_t)n * hc_ * hc_ * 4);
+    if (pre) outs[no++] = span(pre, (uint64_t)n * hc_ * 4);
+    if (mixes) outs[no++] = span(mixes, (uint64_t)n * M * 4);
+    for (int i = 0; i < no; ++i) {
+        // R_out (the first output of hc_post_mix_pre) may be R itself
+        for (int k = 0; k < ni; ++k)
+            if (!(prev && i == 0 && k == 0 && Rin == R) && overlap(outs[i], ins[k])) return HC_ERR_ALIAS;
+        for (int j = i + 1; j < no; ++j)
+            if (overlap(outs[i], outs[j])) return HC_ERR_ALIAS;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (prev && hc::launch_gen_post(prev->x, R, prev->post, prev->comb, prev->Rout, n, hc_, d, s))
+        return HC_ERR_LAUNCH;
+    return hc::launch_gen_fused(Rin, hc_fn, hc_scale, hc_base, h, pre, post, comb, mixes, workspace, n, hc_, d,
+                                sinkhorn_iters, hc_eps, norm_eps, s)
+               ? HC_ERR_LAUNCH
+               : HC_OK;
+}
+
 // hc_fused_mix_pre with the weights as given (hc_fn) or already split
 // (packed, from hc_pack_weights).
 static int fused_impl(const void* R, const float* hc_fn, const void* packed, size_t packed_bytes,
                       const float* hc_scale, const float* hc_base, void* h, float* pre, float* post, float* comb,
                       float* mixes, void* workspace, size_t workspace_bytes, int64_t n, int32_t hc_, int32_t d,
                       int32_t sinkhorn_iters, float hc_eps, float norm_eps, void* stream) {
-    if (hc_ == 4 && sinkhorn_iters < 1) return HC_ERR_UNSUPPORTED;
+    if (hc_ != 4) {
+        if (packed) return HC_ERR_UNSUPPORTED;
+        return gen_fused(nullptr, R, hc_fn, hc_scale, hc_base, h, pre, post, comb, mixes, workspace,
+                         workspace_bytes, n, hc_, d, sinkhorn_iters, hc_eps, norm_eps, stream);
+    }
+    if (sinkhorn_iters < 1) return HC_ERR_UNSUPPORTED;
     if (!finite_nonneg(hc_eps)) return HC_ERR_VALUE;
     hc::CoopPlan p;
     const void* wsrc = packed ? packed : (const void*)hc_fn;
@@ -260,7 +348,12 @@ int hc_post_mix_pre(const void* x, const void* R, const float* post, const float
                     float* post_next, float* comb_next, float* mixes_next, void* workspace, size_t workspace_bytes,
                     int64_t n, int32_t hc_, int32_t d, int32_t sinkhorn_iters, float hc_eps, float norm_eps,
                     void* stream) {
-    if (hc_ == 4 && sinkhorn_iters < 1) return HC_ERR_UNSUPPORTED;
+    if (hc_ != 4) {
+        const hc::PostIn prev{x, post, comb, R_out};
+        return gen_fused(&prev, R, hc_fn, hc_scale, hc_base, h, pre_next, post_next, comb_next, mixes_next,
+                         workspace, workspace_bytes, n, hc_, d, sinkhorn_iters, hc_eps, norm_eps, stream);
+    }
+    if (sinkhorn_iters < 1) return HC_ERR_UNSUPPORTED;
     if (!finite_nonneg(hc_eps)) return HC_ERR_VALUE;
     hc::CoopPlan p;
     int st = coop_common(R, hc_fn, workspace, workspace_bytes, n, hc_, d, norm_eps, p);

@@ -1,0 +1,357 @@
+// hc_general.hip -- the hyper-connection mixing for stream counts other than
+// four (hc = 1..8, hc != 4).  The "Reading weights" page writes its split +
+// Sinkhorn kernel for any hc_mult, and the mix formula of the "Mix
+// projection" page projects the flattened hc*d stream to (2 + hc) * hc
+// numbers for any hc; four streams take the tuned kernels of the other
+// files.  Here every step is a plain kernel, one template instance per hc:
+//
+//  * k_gmix  -- projection and RMS: a 32-token tile per workgroup, the
+//               reduction axis staged 64 elements at a time through LDS
+//               (tokens as float, weights as float), every (token, output)
+//               pair accumulated in double by one thread in feature order.
+//               Products of a bf16 and an fp32 value are exact in double,
+//               so the sums are those of a plain in-order fp64 loop.
+//  * k_gsplit -- split + epsilon-Sinkhorn, one token per thread, with the
+//               gate, softmax and normalisation arithmetic of the four-stream
+//               kernel (same functions, same order).
+//  * k_gpre, k_gpost -- hc_pre and hc_post over 16-byte chunks (8 features
+//               of one token), summed in double in the order of the formula
+//               and rounded once to bf16 (nearest even).
+#include "hc_device.hpp"
+#include "hc_launch.hpp"
+
+namespace hc {
+
+bool gen_hc(int hc_) { return hc_ >= 1 && hc_ <= kGenMaxHC && hc_ != kHC; }
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t gen_ws_bytes(int64_t n, int hc_) {
+    const size_t M = (size_t)(2 + hc_) * hc_;
+    return align256((size_t)n * M * 4) + align256((size_t)n * hc_ * 4);
+}
+
+namespace {
+
+constexpr int kGThreads = 256;
+constexpr int kGT = 32;      // tokens per projection tile (kGT * 8 == kGThreads)
+constexpr int kGKC = 64;     // reduction elements per staged step
+static_assert(kGT * 8 == kGThreads, "one 16-byte chunk of the token tile per thread");
+
+// Mix formula of the "Mix projection" page: m_j = r * sum_i x_i W[j, i] with
+// r = 1 / sqrt(sum_i x_i^2 / K + norm_eps), K = hc * d.  Output j == M of
+// each token is its sum of squares.
+template <int HC>
+__global__ __launch_bounds__(kGThreads) void k_gmix(const uint16_t* __restrict__ R, const float* __restrict__ W,
+                                                    float* __restrict__ mixes, int64_t n, int d, float norm_eps) {
+    constexpr int M = (2 + HC) * HC;
+    constexpr int NP = kGT * (M + 1);
+    constexpr int PPT = (NP + kGThreads - 1) / kGThreads;
+    __shared__ float xs[kGT][kGKC + 1];    // odd row stride: the pairs of a wave read distinct banks
+    __shared__ float ws[M][kGKC + 1];
+    __shared__ double ssq[kGT];
+    const int64_t K = (int64_t)HC * d;
+    const int64_t ntiles = (n + kGT - 1) / kGT;
+    const int tid = threadIdx.x;
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t t0 = tile * kGT;
+    double acc[PPT];
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) acc[p] = 0.0;
+
+    for (int64_t k0 = 0; k0 < K; k0 += kGKC) {
+        {
+            // K is a multiple of 8, so a chunk is either wholly inside the row or past its end
+            const int t = tid >> 3, q = tid & 7;
+            const int64_t k = k0 + q * 8;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (t0 + t < n && k < K) v = *reinterpret_cast<const uint4*>(R + (t0 + t) * K + k);
+            float* xr = &xs[t][q * 8];
+            xr[0] = bf_lo(v.x); xr[1] = bf_hi(v.x);
+            xr[2] = bf_lo(v.y); xr[3] = bf_hi(v.y);
+            xr[4] = bf_lo(v.z); xr[5] = bf_hi(v.z);
+            xr[6] = bf_lo(v.w); xr[7] = bf_hi(v.w);
+        }
+        for (int i = tid; i < M * (kGKC / 4); i += kGThreads) {
+            const int j = i / (kGKC / 4), q = i - j * (kGKC / 4);
+            const int64_t k = k0 + q * 4;
+            float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (k < K) w = *reinterpret_cast<const float4*>(W + (int64_t)j * K + k);
+            float* wr = &ws[j][q * 4];
+            wr[0] = w.x; wr[1] = w.y; wr[2] = w.z; wr[3] = w.w;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) {
+            const int pair = tid + p * kGThreads;
+            if (pair < NP) {
+                const int t = pair / (M + 1), j = pair - t * (M + 1);
+                const float* xr = xs[t];
+                const float* wr = j < M ? ws[j] : xs[t];
+                double a = acc[p];
+#pragma unroll 16
+                for (int k = 0; k < kGKC; ++k) a = __builtin_fma((double)xr[k], (double)wr[k], a);
+                acc[p] = a;
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+        const int pair = tid + p * kGThreads;
+        const int t = pair / (M + 1), j = pair - t * (M + 1);
+        if (pair < NP && j == M) ssq[t] = acc[p];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+        const int pair = tid + p * kGThreads;
+        const int t = pair / (M + 1), j = pair - t * (M + 1);
+        if (pair < NP && j < M && t0 + t < n) {
+            const double r = 1.0 / __builtin_sqrt(ssq[t] / (double)K + (double)norm_eps);
+            mixes[(t0 + t) * M + j] = (float)(acc[p] * r);
+        }
+    }
+    __syncthreads();        // ssq and the tiles are rewritten by the next tile
+    }
+}
+
+// Split + epsilon-Sinkhorn of the "Reading weights" page for hc streams:
+// pre_j = sigmoid(s0 m_j + b_j) + eps, post_j = 2 sigmoid(s1 m_{hc+j} +
+// b_{hc+j}), logits s2 m_{2hc + j hc + k} + b_{2hc + j hc + k}; a row softmax
+// plus eps, a column normalisation, then (iters - 1) row and column
+// normalisations, each dividing by (sum + eps).
+template <int HC>
+__global__ __launch_bounds__(kGThreads) void k_gsplit(const float* __restrict__ mixes, const float* __restrict__ scale,
+                                                      const float* __restrict__ base, float* __restrict__ pre,
+                                                      float* __restrict__ post, float* __restrict__ comb, int64_t n,
+                                                      int iters, float eps) {
+    constexpr int M = (2 + HC) * HC;
+    const float s0 = scale[0], s1 = scale[1], s2 = scale[2];
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += stride) {
+        const float* m = mixes + t * M;
+#pragma unroll
+        for (int j = 0; j < HC; ++j) {
+            if (pre) pre[t * HC + j] = pre_gate(m[j], s0, base[j], eps);
+            post[t * HC + j] = post_gate(m[HC + j], s1, base[HC + j]);
+        }
+        float c[HC][HC];
+#pragma unroll
+        for (int j = 0; j < HC; ++j)
+#pragma unroll
+            for (int k = 0; k < HC; ++k) c[j][k] = m[2 * HC + j * HC + k] * s2 + base[2 * HC + j * HC + k];
+        // row softmax (the maximum is subtracted for range only), then + eps
+#pragma unroll
+        for (int j = 0; j < HC; ++j) {
+            float mx = c[j][0];
+#pragma unroll
+            for (int k = 1; k < HC; ++k) mx = fmaxf(mx, c[j][k]);
+            float s = 0.0f;
+#pragma unroll
+            for (int k = 0; k < HC; ++k) {
+                c[j][k] = expf(c[j][k] - mx);
+                s += c[j][k];
+            }
+#pragma unroll
+            for (int k = 0; k < HC; ++k) c[j][k] = c[j][k] / s + eps;
+        }
+        auto col = [&]() {
+#pragma unroll
+            for (int k = 0; k < HC; ++k) {
+                float s = 0.0f;
+#pragma unroll
+                for (int j = 0; j < HC; ++j) s += c[j][k];
+                const float r = __builtin_amdgcn_rcpf(s + eps);
+#pragma unroll
+                for (int j = 0; j < HC; ++j) c[j][k] *= r;
+            }
+        };
+        col();
+        for (int it = 1; it < iters; ++it) {
+#pragma unroll
+            for (int j = 0; j < HC; ++j) {
+                float s = 0.0f;
+#pragma unroll
+                for (int k = 0; k < HC; ++k) s += c[j][k];
+                const float r = __builtin_amdgcn_rcpf(s + eps);
+#pragma unroll
+                for (int k = 0; k < HC; ++k) c[j][k] *= r;
+            }
+            col();
+        }
+#pragma unroll
+        for (int j = 0; j < HC; ++j)
+#pragma unroll
+            for (int k = 0; k < HC; ++k) comb[(t * HC + j) * HC + k] = c[j][k];
+    }
+}
+
+// 8 features of one stream chunk as doubles (element e of the 16 bytes).
+__device__ __forceinline__ double bf_at(const uint4& v, int e) {
+    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+    return (double)((e & 1) ? bf_hi(w) : bf_lo(w));
+}
+
+__device__ __forceinline__ uint4 pack8(const uint32_t (&o)[8]) {
+    return make_uint4(pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7]));
+}
+
+// hc_pre of the "Mix projection" page: h_c = bf16(sum_k pre_k R_{k,c}).
+template <int HC>
+__global__ __launch_bounds__(kGThreads) void k_gpre(const uint16_t* __restrict__ R, const float* __restrict__ pre,
+                                                    uint16_t* __restrict__ h, int64_t n, int d) {
+    const int cpt = d / 8;
+    const int64_t items = n * cpt;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items; it += stride) {
+        const int64_t t = it / cpt;
+        const int c0 = (int)(it - t * cpt) * 8;
+        uint4 r[HC];
+        double p[HC];
+#pragma unroll
+        for (int k = 0; k < HC; ++k) {
+            r[k] = *reinterpret_cast<const uint4*>(R + (t * HC + k) * d + c0);
+            p[k] = pre[t * HC + k];
+        }
+        uint32_t o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            double y = p[0] * bf_at(r[0], e);
+#pragma unroll
+            for (int k = 1; k < HC; ++k) y = __builtin_fma(p[k], bf_at(r[k], e), y);
+            o[e] = bf16_rn_f64(y);
+        }
+        *reinterpret_cast<uint4*>(h + t * d + c0) = pack8(o);
+    }
+}
+
+// hc_post of the "Mix projection" page: output stream k is
+// bf16(post_k x_c + sum_j comb[j][k] R_{j,c}).  An item reads every stream
+// of its chunk before writing any, so R_out may be R.
+template <int HC>
+__global__ __launch_bounds__(kGThreads) void k_gpost(const uint16_t* __restrict__ x, const uint16_t* R,
+                                                     const float* __restrict__ post, const float* __restrict__ comb,
+                                                     uint16_t* Rout, int64_t n, int d) {
+    const int cpt = d / 8;
+    const int64_t items = n * cpt;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items; it += stride) {
+        const int64_t t = it / cpt;
+        const int c0 = (int)(it - t * cpt) * 8;
+        const uint4 xv = *reinterpret_cast<const uint4*>(x + t * d + c0);
+        uint4 r[HC];
+#pragma unroll
+        for (int j = 0; j < HC; ++j) r[j] = *reinterpret_cast<const uint4*>(R + (t * HC + j) * d + c0);
+#pragma unroll
+        for (int k = 0; k < HC; ++k) {
+            const double pk = post[t * HC + k];
+            double cj[HC];
+#pragma unroll
+            for (int j = 0; j < HC; ++j) cj[j] = comb[(t * HC + j) * HC + k];
+            uint32_t o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                double y = pk * bf_at(xv, e);
+#pragma unroll
+                for (int j = 0; j < HC; ++j) y = __builtin_fma(cj[j], bf_at(r[j], e), y);
+                o[e] = bf16_rn_f64(y);
+            }
+            *reinterpret_cast<uint4*>(Rout + (t * HC + k) * d + c0) = pack8(o);
+        }
+    }
+}
+
+int grid_for(int64_t items) {
+    const int64_t cap = (int64_t)num_cus() * 8;
+    const int64_t need = (items + kGThreads - 1) / kGThreads;
+    return (int)(need < cap ? (need > 0 ? need : 1) : cap);
+}
+
+template <template <int> class Op, typename... A>
+int dispatch_hc(int hc_, A... args) {
+    switch (hc_) {
+        case 1: return Op<1>::run(args...);
+        case 2: return Op<2>::run(args...);
+        case 3: return Op<3>::run(args...);
+        case 5: return Op<5>::run(args...);
+        case 6: return Op<6>::run(args...);
+        case 7: return Op<7>::run(args...);
+        case 8: return Op<8>::run(args...);
+        default: return -1;
+    }
+}
+
+template <int HC>
+struct MixOp {
+    static int run(const void* R, const float* W, float* mixes, int64_t n, int d, float norm_eps, hipStream_t s) {
+        const int64_t tiles = (n + kGT - 1) / kGT, cap = (int64_t)num_cus() * 16;
+        hipLaunchKernelGGL(k_gmix<HC>, dim3((unsigned)(tiles < cap ? tiles : cap)), dim3(kGThreads), 0, s,
+                           static_cast<const uint16_t*>(R), W, mixes, n, d, norm_eps);
+        return hipGetLastError() == hipSuccess ? 0 : -1;
+    }
+};
+
+template <int HC>
+struct SplitOp {
+    static int run(const float* mixes, const float* scale, const float* base, float* pre, float* post, float* comb,
+                   int64_t n, int iters, float eps, hipStream_t s) {
+        hipLaunchKernelGGL(k_gsplit<HC>, dim3(grid_for(n)), dim3(kGThreads), 0, s, mixes, scale, base, pre, post,
+                           comb, n, iters, eps);
+        return hipGetLastError() == hipSuccess ? 0 : -1;
+    }
+};
+
+template <int HC>
+struct PreOp {
+    static int run(const void* R, const float* pre, void* h, int64_t n, int d, hipStream_t s) {
+        hipLaunchKernelGGL(k_gpre<HC>, dim3(grid_for(n * (d / 8))), dim3(kGThreads), 0, s,
+                           static_cast<const uint16_t*>(R), pre, static_cast<uint16_t*>(h), n, d);
+        return hipGetLastError() == hipSuccess ? 0 : -1;
+    }
+};
+
+template <int HC>
+struct PostOp {
+    static int run(const void* x, const void* R, const float* post, const float* comb, void* Rout, int64_t n, int d,
+                   hipStream_t s) {
+        hipLaunchKernelGGL(k_gpost<HC>, dim3(grid_for(n * (d / 8))), dim3(kGThreads), 0, s,
+                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(R), post, comb,
+                           static_cast<uint16_t*>(Rout), n, d);
+        return hipGetLastError() == hipSuccess ? 0 : -1;
+    }
+};
+
+}  // namespace
+
+int launch_gen_mixes(const void* R, const float* W, float* mixes, int64_t n, int hc_, int d, float norm_eps,
+                     hipStream_t s) {
+    return dispatch_hc<MixOp>(hc_, R, W, mixes, n, d, norm_eps, s);
+}
+
+int launch_gen_split(const float* mixes, const float* scale, const float* base, float* pre, float* post,
+                     float* comb, int64_t n, int hc_, int iters, float eps, hipStream_t s) {
+    return dispatch_hc<SplitOp>(hc_, mixes, scale, base, pre, post, comb, n, iters, eps, s);
+}
+
+int launch_gen_pre(const void* R, const float* pre, void* h, int64_t n, int hc_, int d, hipStream_t s) {
+    return dispatch_hc<PreOp>(hc_, R, pre, h, n, d, s);
+}
+
+int launch_gen_post(const void* x, const void* R, const float* post, const float* comb, void* Rout, int64_t n,
+                    int hc_, int d, hipStream_t s) {
+    return dispatch_hc<PostOp>(hc_, x, R, post, comb, Rout, n, d, s);
+}
+
+int launch_gen_fused(const void* R, const float* W, const float* scale, const float* base, void* h, float* pre,
+                     float* post, float* comb, float* mixes, void* ws, int64_t n, int hc_, int d, int iters,
+                     float eps, float norm_eps, hipStream_t s) {
+    const size_t M = (size_t)(2 + hc_) * hc_;
+    float* mx = mixes ? mixes : static_cast<float*>(ws);
+    float* pr = pre ? pre : reinterpret_cast<float*>(static_cast<char*>(ws) + align256((size_t)n * M * 4));
+    if (launch_gen_mixes(R, W, mx, n, hc_, d, norm_eps, s)) return -1;
+    if (launch_gen_split(mx, scale, base, pr, post, comb, n, hc_, iters, eps, s)) return -1;
+    return launch_gen_pre(R, pr, h, n, hc_, d, s);
+}
+
+}  // namespace hc

@@ -21,6 +21,24 @@ int launch_diag(const void* h, const void* D, void* x, int64_t n, int d, hipStre
 int launch_split(const float* mixes, const float* scale, const float* base, float* pre, float* post,
                  float* comb, int64_t n, int iters, float eps, hipStream_t s);
 
+// Stream counts other than four (hc_general.hip): 1 <= hc <= kGenMaxHC.
+constexpr int kGenMaxHC = 8;
+bool gen_hc(int hc);
+// Workspace of the fused call: the mixes, then pre (each 256-byte aligned).
+size_t gen_ws_bytes(int64_t n, int hc);
+int launch_gen_mixes(const void* R, const float* W, float* mixes, int64_t n, int hc, int d, float norm_eps,
+                     hipStream_t s);
+int launch_gen_split(const float* mixes, const float* scale, const float* base, float* pre, float* post,
+                     float* comb, int64_t n, int hc, int iters, float eps, hipStream_t s);
+int launch_gen_pre(const void* R, const float* pre, void* h, int64_t n, int hc, int d, hipStream_t s);
+int launch_gen_post(const void* x, const void* R, const float* post, const float* comb, void* Rout, int64_t n,
+                    int hc, int d, hipStream_t s);
+// mixes, split + Sinkhorn and hc_pre in sequence; mixes and pre may be NULL
+// (kept in ws, of gen_ws_bytes).
+int launch_gen_fused(const void* R, const float* W, const float* scale, const float* base, void* h, float* pre,
+                     float* post, float* comb, float* mixes, void* ws, int64_t n, int hc, int d, int iters,
+                     float eps, float norm_eps, hipStream_t s);
+
 // Work split of the projection kernels (hc_coop.hip): each group of G
 // workgroups shares every token; member q owns a 32*KS-feature slice of
 // each stream and its 24-column slice of the weights.

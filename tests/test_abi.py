@@ -65,7 +65,10 @@ def test_post_checks(lib):
     assert post_call(lib, n=-1) == SHAPE
     assert post_call(lib, d=60) == SHAPE
     assert post_call(lib, d=0) == SHAPE
-    assert post_call(lib, hc=3) == UNSUP
+    assert post_call(lib, hc=9) == UNSUP
+    assert post_call(lib, hc=0) == UNSUP
+    assert post_call(lib, hc=3, x=0) == NULL
+    assert post_call(lib, hc=3, out=B + 16) == ALIAS
     assert post_call(lib, x=0) == NULL
     assert post_call(lib, comb=0) == NULL
     assert post_call(lib, R=B + 8) == ALIGN
@@ -78,7 +81,9 @@ def test_post_checks(lib):
 def test_pre_checks(lib):
     f = lambda R=A, p=B, h=C, n=4, hc=4, d=64: lib.hc_pre(P(R), P(p), P(h), n, hc, d, None)
     assert f(n=0) == OK
-    assert f(hc=8) == UNSUP
+    assert f(hc=9) == UNSUP
+    assert f(hc=8, h=0) == NULL
+    assert f(hc=8, h=A + 4032) == ALIAS    # R spans 4 * 8 * 64 * 2 bytes at hc = 8
     assert f(d=12) == SHAPE
     assert f(h=0) == NULL
     assert f(p=B + 4) == ALIGN
@@ -91,7 +96,10 @@ def test_split_checks(lib):
     assert f(n=0) == OK
     assert f(n=-3) == SHAPE
     assert f(it=0) == UNSUP
-    assert f(hc=2) == UNSUP
+    assert f(hc=9) == UNSUP
+    assert f(hc=0) == UNSUP
+    assert f(hc=2, s=0) == NULL
+    assert f(hc=2, comb=A + 96) == ALIAS   # mixes span 4 * 8 * 4 bytes at hc = 2
     assert f(eps=-1.0) == VALUE
     assert f(eps=float("nan")) == VALUE
     assert f(eps=float("inf")) == VALUE
@@ -123,6 +131,13 @@ def test_fused_and_mixes_checks(lib):
     assert f(h=A) == ALIAS             # h overlaps R
     assert f(post=E) == ALIAS          # post overlaps pre
     assert f(mix=F_) == ALIAS          # mixes overlaps the workspace
+    # other stream counts: the same checks on hc-sized buffers
+    assert f(hc=9) == UNSUP
+    assert f(hc=2, it=0) == UNSUP
+    assert f(hc=2, ws=0) == WS
+    assert f(hc=2, wsb=16) == WS
+    assert f(hc=2, h=A) == ALIAS
+    assert f(hc=2, d=60) == SHAPE
 
     def m(R=A, W=B, out=C, ws=F_, wsb=1 << 30, n=4, hc=4, d=64, neps=1e-20):
         return lib.hc_mixes(P(R), P(W), P(out), n, hc, d, neps, P(ws), wsb, None)
@@ -131,7 +146,10 @@ def test_fused_and_mixes_checks(lib):
     assert m(out=C + 4) == ALIGN
     assert m(out=A) == ALIAS
     assert m(wsb=0) == WS
-    assert m(hc=5) == UNSUP
+    assert m(hc=9) == UNSUP
+    assert m(hc=5, n=0) == OK
+    assert m(hc=5, out=0) == NULL
+    assert m(hc=5, out=A) == ALIAS
 
 
 def test_post_mix_pre_checks(lib):
@@ -143,7 +161,10 @@ def test_post_mix_pre_checks(lib):
         return lib.hc_post_mix_pre(P(x), P(R), P(post), P(comb), P(Ro), P(W), P(s), P(b), P(h), P(pre),
                                    P(post2), P(comb2), P(mix), P(ws), wsb, n, hc, d, it, eps, neps, None)
     assert f(n=0) == OK
-    assert f(hc=3) == UNSUP
+    assert f(hc=9) == UNSUP
+    assert f(hc=3, Ro=B + 64) == ALIAS
+    assert f(hc=3, ws=0) == WS
+    assert f(hc=3, x=0) == NULL
     assert f(it=0) == UNSUP
     assert f(eps=-1.0) == VALUE
     assert f(x=0) == NULL
@@ -182,12 +203,14 @@ def test_packed_weights_checks(lib):
     assert f(pkd=0) == NULL
     assert f(nbytes=16) == WS
     assert f(d=64) == UNSUP
+    assert f(hc=3) == UNSUP              # packed weights: four streams only
     assert f(h=B) == ALIAS               # h over the packed weights
 
 
 def test_workspace_query(lib):
     assert lib.hc_fused_workspace_bytes(0, 4, 5120) == 0
-    assert lib.hc_fused_workspace_bytes(16, 3, 5120) == 0
+    assert lib.hc_fused_workspace_bytes(16, 9, 5120) == 0
+    assert lib.hc_fused_workspace_bytes(16, 3, 5120) == 1024 + 256    # mixes, then pre, 256-byte aligned
     assert lib.hc_fused_workspace_bytes(16, 4, 48) == 0
     assert lib.hc_fused_workspace_bytes(16, 4, 64) > 0
     assert lib.hc_fused_workspace_bytes(65536, 4, 5120) > 0

@@ -6,6 +6,8 @@ checked on every token when the oracle finishes in seconds (tiny, decode,
 prefill) and on sampled tokens otherwise (large prefill: 65,536 tokens),
 in the launch configuration the benchmark uses.  Tolerances: tests/hc_check.py.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -480,3 +482,62 @@ def test_errors_are_raised_on_gpu():
         hcl.hc_split_sinkhorn(torch.zeros(4, 24, device=DEV), t["scale"], t["base"], sinkhorn_iters=0)
     with pytest.raises(ValueError):
         hcl.hc_pre(t["R"].cpu(), torch.zeros(1, 16, 4))
+
+
+# ------------------------------------------------- stream counts other than 4
+# The split + Sinkhorn listing and the mix formula are written for any hc;
+# hc = 1..8 other than 4 run the plain kernels of hc_general.hip.
+
+def _hc_workload(hc, d):
+    return dataclasses.replace(hin.WORKLOADS["prefill"], hc=hc, d=d)
+
+
+@pytest.mark.parametrize("hc,d,n", [(1, 64, 37), (2, 256, 100), (3, 5120, 33), (5, 128, 65), (6, 512, 40),
+                                    (7, 64, 17), (8, 5120, 70)])
+def test_other_stream_counts(orc, hc, d, n):
+    w = _hc_workload(hc, d)
+    t = hin.make_inputs(w, DEV, seed=11, n_tokens=n)
+    R = t["R"]
+    R[0, 0].zero_()                                   # an all-zero token: mixes exactly 0
+    if n > 1:
+        R[0, 1].mul_(2.0 ** 100)                      # squares far beyond the float range
+    outs = run_fused(R, t["W"], t["scale"], t["base"])
+    assert bool((outs[4][0, 0] == 0).all())
+    compare_fused(orc, R, t["W"], t["scale"], t["base"], outs, x=t["x"], label="hc=%d d=%d" % (hc, d))
+    # the standalone entry points give the fused call's results bit for bit
+    h, pre, post, comb, mixes = outs
+    m2 = hcl.hc_mixes(R, t["W"])
+    p2, q2, c2 = hcl.hc_split_sinkhorn(m2, t["scale"], t["base"], hc_mult=hc)
+    h2 = hcl.hc_pre(R, p2)
+    torch.cuda.synchronize()
+    for a, b in ((m2, mixes), (p2, pre), (q2, post), (c2, comb)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(h2.view(torch.int16), h.view(torch.int16))
+
+
+@pytest.mark.parametrize("hc", [2, 8])
+def test_post_mix_pre_other_stream_counts(hc):
+    w = _hc_workload(hc, 256)
+    t = hin.make_inputs(w, DEV, seed=12, n_tokens=50)
+    _, _, post, comb, _ = run_fused(t["R"], t["W"], t["scale"], t["base"])
+    W2, s2, b2 = hin.make_params(w, DEV, seed=13)
+    R1 = hcl.hc_post(t["x"], t["R"], post, comb)
+    a = hcl.hc_fused_mix_pre(R1, W2, s2, b2, want_mixes=True)
+    Rc = t["R"].clone()
+    Ro, *b = hcl.hc_post_mix_pre(t["x"], Rc, post, comb, W2, s2, b2, want_mixes=True, out_R=Rc)
+    torch.cuda.synchronize()
+    assert Ro.data_ptr() == Rc.data_ptr()
+    assert torch.equal(Ro.view(torch.int16), R1.view(torch.int16))
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.int16), v.view(torch.int16))
+
+
+def test_other_stream_count_many_tiles_sampled(orc):
+    # more 32-token tiles than the projection kernel's grid: its tile loop
+    # runs several times per workgroup
+    hc, d, n = 2, 64, 140_001
+    w = _hc_workload(hc, d)
+    t = hin.make_inputs(w, DEV, seed=14, n_tokens=n)
+    outs = run_fused(t["R"], t["W"], t["scale"], t["base"])
+    idx = np.concatenate([hin.sample_tokens(n, 200), [n - 1]])
+    compare_fused(orc, t["R"], t["W"], t["scale"], t["base"], outs, idx=idx, x=t["x"], label="hc=2 n=140001")
