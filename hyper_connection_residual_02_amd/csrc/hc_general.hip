@@ -7,8 +7,10 @@
 //
 //  * k_gmix  -- projection and RMS: a 32-token tile per workgroup, the
 //               reduction axis staged 64 elements at a time through LDS
-//               (tokens as float, weights as float), every (token, output)
-//               pair accumulated in double by one thread in feature order.
+//               (tokens as float, weights as float), each thread holding a
+//               4 x 4 block of (token, output) sums in double, accumulated
+//               in feature order (k_gmix_pairs: one pair per thread, for
+//               fewer than 48 outputs).
 //               Products of a bf16 and an fp32 value are exact in double,
 //               so the sums are those of a plain in-order fp64 loop.
 //  * k_gsplit -- split + epsilon-Sinkhorn, one token per thread, with the
@@ -37,82 +39,228 @@ constexpr int kGThreads = 256;
 constexpr int kGT = 32;      // tokens per projection tile (kGT * 8 == kGThreads)
 constexpr int kGKC = 64;     // reduction elements per staged step
 static_assert(kGT * 8 == kGThreads, "one 16-byte chunk of the token tile per thread");
+// Output count from which the projection uses 4 x 4 micro-tiles: below it too
+// few threads would own a tile (measured: at 8 outputs the per-pair mapping
+// is 2x faster, at 80 outputs the micro-tiles are 3x faster).
+constexpr int kGTileMinM = 48;
 
 // Mix formula of the "Mix projection" page: m_j = r * sum_i x_i W[j, i] with
-// r = 1 / sqrt(sum_i x_i^2 / K + norm_eps), K = hc * d.  Output j == M of
-// each token is its sum of squares.
+// r = 1 / sqrt(sum_i x_i^2 / K + norm_eps), K = hc * d.
+//
+// Threads 0..NW-1 each own a 4-token x 4-output micro-tile (tokens
+// tg + 8i, outputs 4 jg + u), so each staged step costs 8 LDS reads per 16
+// products; threads NW..NW+31 form one token's sum of squares each.  All
+// threads stage: the loads of step s + 1 are issued before the products of
+// step s.  Every sum runs over the features in order.
 template <int HC>
 __global__ __launch_bounds__(kGThreads) void k_gmix(const uint16_t* __restrict__ R, const float* __restrict__ W,
                                                     float* __restrict__ mixes, int64_t n, int d, float norm_eps) {
     constexpr int M = (2 + HC) * HC;
-    constexpr int NP = kGT * (M + 1);
-    constexpr int PPT = (NP + kGThreads - 1) / kGThreads;
-    __shared__ float xs[kGT][kGKC + 1];    // odd row stride: the pairs of a wave read distinct banks
+    constexpr int TT = 4, JJ = 4;
+    constexpr int NT = kGT / TT;                 // token groups
+    constexpr int NJ = (M + JJ - 1) / JJ;        // output groups (the last may be padded)
+    constexpr int NW = NT * NJ;                  // threads with a micro-tile
+    static_assert(NW + kGT <= kGThreads, "micro-tiles plus one sum-of-squares thread per token");
+    constexpr int WCH = M * (kGKC / 4);          // 16-byte weight chunks per step
+    constexpr int WPT = (WCH + kGThreads - 1) / kGThreads;
+    __shared__ float xs[kGT][kGKC + 1];          // odd row stride: a wave's rows fall in distinct banks
     __shared__ float ws[M][kGKC + 1];
     __shared__ double ssq[kGT];
     const int64_t K = (int64_t)HC * d;
     const int64_t ntiles = (n + kGT - 1) / kGT;
     const int tid = threadIdx.x;
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int64_t t0 = tile * kGT;
-    double acc[PPT];
-#pragma unroll
-    for (int p = 0; p < PPT; ++p) acc[p] = 0.0;
+    const int tg = tid % NT, jg = tid / NT;
+    const int st = tid - NW;
+    const int xt = tid >> 3, xq = tid & 7;       // staged x chunk of this thread
 
-    for (int64_t k0 = 0; k0 < K; k0 += kGKC) {
-        {
-            // K is a multiple of 8, so a chunk is either wholly inside the row or past its end
-            const int t = tid >> 3, q = tid & 7;
-            const int64_t k = k0 + q * 8;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (t0 + t < n && k < K) v = *reinterpret_cast<const uint4*>(R + (t0 + t) * K + k);
-            float* xr = &xs[t][q * 8];
-            xr[0] = bf_lo(v.x); xr[1] = bf_hi(v.x);
-            xr[2] = bf_lo(v.y); xr[3] = bf_hi(v.y);
-            xr[4] = bf_lo(v.z); xr[5] = bf_hi(v.z);
-            xr[6] = bf_lo(v.w); xr[7] = bf_hi(v.w);
+    // K is a multiple of 8: a chunk lies wholly inside its row or past its end
+    auto load = [&](int64_t t0, int64_t k0, uint4& xv, float4 (&wv)[WPT]) {
+        const int64_t k = k0 + xq * 8;
+        xv = make_uint4(0u, 0u, 0u, 0u);
+        if (t0 + xt < n && k < K) xv = *reinterpret_cast<const uint4*>(R + (t0 + xt) * K + k);
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            const int c = tid + i * kGThreads;
+            const int j = c / (kGKC / 4), q = c - j * (kGKC / 4);
+            const int64_t kk = k0 + q * 4;
+            wv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (c < WCH && kk < K) wv[i] = *reinterpret_cast<const float4*>(W + (int64_t)j * K + kk);
         }
-        for (int i = tid; i < M * (kGKC / 4); i += kGThreads) {
-            const int j = i / (kGKC / 4), q = i - j * (kGKC / 4);
-            const int64_t k = k0 + q * 4;
-            float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (k < K) w = *reinterpret_cast<const float4*>(W + (int64_t)j * K + k);
-            float* wr = &ws[j][q * 4];
-            wr[0] = w.x; wr[1] = w.y; wr[2] = w.z; wr[3] = w.w;
+    };
+    auto stage = [&](const uint4& xv, const float4 (&wv)[WPT]) {
+        float* xr = &xs[xt][xq * 8];
+        xr[0] = bf_lo(xv.x); xr[1] = bf_hi(xv.x);
+        xr[2] = bf_lo(xv.y); xr[3] = bf_hi(xv.y);
+        xr[4] = bf_lo(xv.z); xr[5] = bf_hi(xv.z);
+        xr[6] = bf_lo(xv.w); xr[7] = bf_hi(xv.w);
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            const int c = tid + i * kGThreads;
+            if (c < WCH) {
+                const int j = c / (kGKC / 4), q = c - j * (kGKC / 4);
+                float* wr = &ws[j][q * 4];
+                wr[0] = wv[i].x; wr[1] = wv[i].y; wr[2] = wv[i].z; wr[3] = wv[i].w;
+            }
+        }
+    };
+
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t t0 = tile * kGT;
+        double acc[TT][JJ];
+#pragma unroll
+        for (int i = 0; i < TT; ++i)
+#pragma unroll
+            for (int u = 0; u < JJ; ++u) acc[i][u] = 0.0;
+        double sacc = 0.0;
+        uint4 xv;
+        float4 wv[WPT];
+        load(t0, 0, xv, wv);
+        for (int64_t k0 = 0; k0 < K; k0 += kGKC) {
+            stage(xv, wv);
+            __syncthreads();
+            if (k0 + kGKC < K) load(t0, k0 + kGKC, xv, wv);
+            if (tid < NW) {
+                const float* xr[TT];
+                const float* wr[JJ];
+#pragma unroll
+                for (int i = 0; i < TT; ++i) xr[i] = xs[tg + NT * i];
+#pragma unroll
+                for (int u = 0; u < JJ; ++u) wr[u] = ws[jg * JJ + u < M ? jg * JJ + u : M - 1];
+#pragma unroll 8
+                for (int k = 0; k < kGKC; ++k) {
+                    double xk[TT], wk[JJ];
+#pragma unroll
+                    for (int i = 0; i < TT; ++i) xk[i] = xr[i][k];
+#pragma unroll
+                    for (int u = 0; u < JJ; ++u) wk[u] = wr[u][k];
+#pragma unroll
+                    for (int i = 0; i < TT; ++i)
+#pragma unroll
+                        for (int u = 0; u < JJ; ++u) acc[i][u] = __builtin_fma(xk[i], wk[u], acc[i][u]);
+                }
+            } else if (st < kGT) {
+#pragma unroll 16
+                for (int k = 0; k < kGKC; ++k) {
+                    const double v = xs[st][k];
+                    sacc = __builtin_fma(v, v, sacc);
+                }
+            }
+            __syncthreads();
+        }
+        if (st >= 0 && st < kGT) ssq[st] = sacc;
+        __syncthreads();
+        if (tid < NW) {
+#pragma unroll
+            for (int i = 0; i < TT; ++i) {
+                const int t = tg + NT * i;
+                if (t0 + t >= n) continue;
+                const double r = 1.0 / __builtin_sqrt(ssq[t] / (double)K + (double)norm_eps);
+#pragma unroll
+                for (int u = 0; u < JJ; ++u) {
+                    const int j = jg * JJ + u;
+                    if (j < M) mixes[(t0 + t) * M + j] = (float)(acc[i][u] * r);
+                }
+            }
+        }
+        __syncthreads();        // ssq and the staged tiles are rewritten by the next tile
+    }
+}
+
+// The same projection for few outputs ((2 + hc) * hc < 48): every
+// (token, output) pair, the sum of squares counted as output M, belongs to
+// one thread, so that all 256 threads share the products; the staging and
+// its prefetch are those of k_gmix.
+template <int HC>
+__global__ __launch_bounds__(kGThreads) void k_gmix_pairs(const uint16_t* __restrict__ R,
+                                                          const float* __restrict__ W, float* __restrict__ mixes,
+                                                          int64_t n, int d, float norm_eps) {
+    constexpr int M = (2 + HC) * HC;
+    constexpr int NP = kGT * (M + 1);
+    constexpr int PPT = (NP + kGThreads - 1) / kGThreads;
+    constexpr int WCH = M * (kGKC / 4);
+    constexpr int WPT = (WCH + kGThreads - 1) / kGThreads;
+    __shared__ float xs[kGT][kGKC + 1];
+    __shared__ float ws[M][kGKC + 1];
+    __shared__ double ssq[kGT];
+    const int64_t K = (int64_t)HC * d;
+    const int64_t ntiles = (n + kGT - 1) / kGT;
+    const int tid = threadIdx.x;
+    const int xt = tid >> 3, xq = tid & 7;
+
+    auto load = [&](int64_t t0, int64_t k0, uint4& xv, float4 (&wv)[WPT]) {
+        const int64_t k = k0 + xq * 8;
+        xv = make_uint4(0u, 0u, 0u, 0u);
+        if (t0 + xt < n && k < K) xv = *reinterpret_cast<const uint4*>(R + (t0 + xt) * K + k);
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            const int c = tid + i * kGThreads;
+            const int j = c / (kGKC / 4), q = c - j * (kGKC / 4);
+            const int64_t kk = k0 + q * 4;
+            wv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (c < WCH && kk < K) wv[i] = *reinterpret_cast<const float4*>(W + (int64_t)j * K + kk);
+        }
+    };
+    auto stage = [&](const uint4& xv, const float4 (&wv)[WPT]) {
+        float* xr = &xs[xt][xq * 8];
+        xr[0] = bf_lo(xv.x); xr[1] = bf_hi(xv.x);
+        xr[2] = bf_lo(xv.y); xr[3] = bf_hi(xv.y);
+        xr[4] = bf_lo(xv.z); xr[5] = bf_hi(xv.z);
+        xr[6] = bf_lo(xv.w); xr[7] = bf_hi(xv.w);
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            const int c = tid + i * kGThreads;
+            if (c < WCH) {
+                const int j = c / (kGKC / 4), q = c - j * (kGKC / 4);
+                float* wr = &ws[j][q * 4];
+                wr[0] = wv[i].x; wr[1] = wv[i].y; wr[2] = wv[i].z; wr[3] = wv[i].w;
+            }
+        }
+    };
+
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t t0 = tile * kGT;
+        double acc[PPT];
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) acc[p] = 0.0;
+        uint4 xv;
+        float4 wv[WPT];
+        load(t0, 0, xv, wv);
+        for (int64_t k0 = 0; k0 < K; k0 += kGKC) {
+            stage(xv, wv);
+            __syncthreads();
+            if (k0 + kGKC < K) load(t0, k0 + kGKC, xv, wv);
+#pragma unroll
+            for (int p = 0; p < PPT; ++p) {
+                const int pair = tid + p * kGThreads;
+                if (pair < NP) {
+                    const int t = pair / (M + 1), j = pair - t * (M + 1);
+                    const float* xr = xs[t];
+                    const float* wr = j < M ? ws[j] : xs[t];
+                    double a = acc[p];
+#pragma unroll 16
+                    for (int k = 0; k < kGKC; ++k) a = __builtin_fma((double)xr[k], (double)wr[k], a);
+                    acc[p] = a;
+                }
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) {
+            const int pair = tid + p * kGThreads;
+            const int t = pair / (M + 1), j = pair - t * (M + 1);
+            if (pair < NP && j == M) ssq[t] = acc[p];
         }
         __syncthreads();
 #pragma unroll
         for (int p = 0; p < PPT; ++p) {
             const int pair = tid + p * kGThreads;
-            if (pair < NP) {
-                const int t = pair / (M + 1), j = pair - t * (M + 1);
-                const float* xr = xs[t];
-                const float* wr = j < M ? ws[j] : xs[t];
-                double a = acc[p];
-#pragma unroll 16
-                for (int k = 0; k < kGKC; ++k) a = __builtin_fma((double)xr[k], (double)wr[k], a);
-                acc[p] = a;
+            const int t = pair / (M + 1), j = pair - t * (M + 1);
+            if (pair < NP && j < M && t0 + t < n) {
+                const double r = 1.0 / __builtin_sqrt(ssq[t] / (double)K + (double)norm_eps);
+                mixes[(t0 + t) * M + j] = (float)(acc[p] * r);
             }
         }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int p = 0; p < PPT; ++p) {
-        const int pair = tid + p * kGThreads;
-        const int t = pair / (M + 1), j = pair - t * (M + 1);
-        if (pair < NP && j == M) ssq[t] = acc[p];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < PPT; ++p) {
-        const int pair = tid + p * kGThreads;
-        const int t = pair / (M + 1), j = pair - t * (M + 1);
-        if (pair < NP && j < M && t0 + t < n) {
-            const double r = 1.0 / __builtin_sqrt(ssq[t] / (double)K + (double)norm_eps);
-            mixes[(t0 + t) * M + j] = (float)(acc[p] * r);
-        }
-    }
-    __syncthreads();        // ssq and the tiles are rewritten by the next tile
+        __syncthreads();        // ssq and the staged tiles are rewritten by the next tile
     }
 }
 
@@ -286,8 +434,14 @@ template <int HC>
 struct MixOp {
     static int run(const void* R, const float* W, float* mixes, int64_t n, int d, float norm_eps, hipStream_t s) {
         const int64_t tiles = (n + kGT - 1) / kGT, cap = (int64_t)num_cus() * 16;
-        hipLaunchKernelGGL(k_gmix<HC>, dim3((unsigned)(tiles < cap ? tiles : cap)), dim3(kGThreads), 0, s,
-                           static_cast<const uint16_t*>(R), W, mixes, n, d, norm_eps);
+        constexpr int M = (2 + HC) * HC;
+        const dim3 grid((unsigned)(tiles < cap ? tiles : cap));
+        if constexpr (M >= kGTileMinM)
+            hipLaunchKernelGGL(k_gmix<HC>, grid, dim3(kGThreads), 0, s, static_cast<const uint16_t*>(R), W, mixes,
+                               n, d, norm_eps);
+        else
+            hipLaunchKernelGGL(k_gmix_pairs<HC>, grid, dim3(kGThreads), 0, s, static_cast<const uint16_t*>(R), W,
+                               mixes, n, d, norm_eps);
         return hipGetLastError() == hipSuccess ? 0 : -1;
     }
 };

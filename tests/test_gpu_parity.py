@@ -532,12 +532,14 @@ def test_post_mix_pre_other_stream_counts(hc):
         assert torch.equal(u.view(torch.int16), v.view(torch.int16))
 
 
-def test_other_stream_count_many_tiles_sampled(orc):
+@pytest.mark.parametrize("hc,d", [(2, 64), (6, 8)])
+def test_other_stream_count_many_tiles_sampled(orc, hc, d):
     # more 32-token tiles than the projection kernel's grid: its tile loop
-    # runs several times per workgroup
-    hc, d, n = 2, 64, 140_001
+    # runs several times per workgroup (hc = 2: one pair per thread;
+    # hc = 6: 4 x 4 micro-tiles)
+    n = 140_001
     w = _hc_workload(hc, d)
     t = hin.make_inputs(w, DEV, seed=14, n_tokens=n)
     outs = run_fused(t["R"], t["W"], t["scale"], t["base"])
     idx = np.concatenate([hin.sample_tokens(n, 200), [n - 1]])
-    compare_fused(orc, t["R"], t["W"], t["scale"], t["base"], outs, idx=idx, x=t["x"], label="hc=2 n=140001")
+    compare_fused(orc, t["R"], t["W"], t["scale"], t["base"], outs, idx=idx, x=t["x"], label="hc=%d n=140001" % hc)
