@@ -35,7 +35,22 @@
  *   mixes  fp32 [n][24]        [0,4) pre logits, [4,8) post, [8,24) comb
  *                              logits row-major (j*4 + k)
  *   pre, post fp32 [n][hc];  comb fp32 [n][hc][hc] with comb[j][k] at j*hc + k
- * n = B*T tokens (the caller flattens batch and sequence).  hc must be 4.
+ * n = B*T tokens (the caller flattens batch and sequence).
+ *
+ * Stream counts: hc is 1..8.  The shapes above are those of hc = 4, the
+ * model's hc_mult; for another hc there are M = (2+hc)*hc mixes in place of
+ * 24 (hc_fn [M][hc*d], hc_base [M], mixes [n][M] with [0,hc) pre logits,
+ * [hc,2hc) post logits and [2hc,M) comb logits at 2hc + j*hc + k), as the
+ * split + Sinkhorn listing of the "Reading weights" page and the mix
+ * formula of the "Mix projection" page are written for any hc.  hc = 4 runs
+ * the tuned kernels each entry point describes.  Every other count runs
+ * plain kernels: the projection in double, each (token, output) sum taken
+ * over the features in order, then the split + Sinkhorn with the
+ * four-stream arithmetic, then hc_pre / hc_post rounded once as below.
+ * There the projection needs only d % 8 == 0, hc_mixes uses no workspace
+ * (it may be NULL), and the fused calls' workspace holds the mixes and pre
+ * of every token (hc_fused_workspace_bytes).  The packed-weight calls take
+ * hc = 4 only.
  *
  * Ownership: the caller owns every buffer.  The library never allocates,
  * frees or synchronises; each call enqueues its kernels on `stream` (a
@@ -69,8 +84,9 @@ typedef enum hc_status {
     HC_ERR_NULL = -1,        /* a required pointer is NULL */
     HC_ERR_SHAPE = -2,       /* n < 0, d <= 0, d % 8 != 0, or sizes overflow */
     HC_ERR_ALIGN = -3,       /* a pointer is not suitably aligned */
-    HC_ERR_UNSUPPORTED = -4, /* hc != 4, sinkhorn_iters < 1, or a d the
-                                projection kernels cannot tile */
+    HC_ERR_UNSUPPORTED = -4, /* hc outside 1..8 (hc != 4 for the packed
+                                weights), sinkhorn_iters < 1, or a d the
+                                four-stream projection cannot tile */
     HC_ERR_WORKSPACE = -5,   /* workspace missing or too small */
     HC_ERR_ALIAS = -6,       /* an output overlaps an input or another output */
     HC_ERR_VALUE = -7,       /* an epsilon is negative or not finite */
@@ -91,7 +107,7 @@ const char *hc_version(void);
  *   flattened features, j < 24.
  * The library's hc_mixes stops at the mixes; the pages' Block.hc_mixes
  * also runs the split (call hc_split_sinkhorn, or hc_fused_mix_pre).
- * Requires d % 32 == 0 and d / (32*k) <= 64 for some k in 1..5 (d = 5120:
+ * With hc = 4 it requires d % 32 == 0 and d / (32*k) <= 64 for some k in 1..5 (d = 5120:
  * k = 5, 32 workgroups per token group); otherwise HC_ERR_UNSUPPORTED.
  * hc_fn is used as given, fp32, with no precision reduced: each product is
  * formed exactly from a three-way bf16 split of the weight.
