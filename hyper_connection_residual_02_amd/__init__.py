@@ -10,8 +10,10 @@ or a GPU tensor every call raises.
 
 Tensor shapes follow the pages' Block methods ("Mix projection" page):
 residual ``R`` [..., hc, d] bf16, sublayer output ``x`` / input ``h``
-[..., d] bf16, ``hc_fn`` [24, hc*d] fp32, ``hc_scale`` [3], ``hc_base``
-[24] fp32, mixes [..., 24], pre/post [..., hc], comb [..., hc, hc] fp32.
+[..., d] bf16, ``hc_fn`` [M, hc*d] fp32, ``hc_scale`` [3], ``hc_base``
+[M] fp32, mixes [..., M], pre/post [..., hc], comb [..., hc, hc] fp32, where
+M = (2 + hc) * hc (24 at the model's hc = 4).  hc is read from ``R`` and may
+be 1..8; the packed-weight calls take hc = 4 only.
 """
 from __future__ import annotations
 
