@@ -128,7 +128,8 @@ def summarize_counters(d: str, n: int, dd: int, command: str):
     print("\n".join(lines))
 
 
-def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, steps: int = 0, tag: str = ""):
+def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, steps: int = 0, tag: str = "",
+                    hc: int = 4):
     """Per-kernel launch durations from a rocprofv3 --kernel-trace --stats
     run of the bench command under ``d``: the average over every dispatch
     (``*kernel_stats.csv``) and, when ``steps`` is given, the average over
@@ -156,16 +157,17 @@ def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, step
                 sel = [dur for _, dur in v[warmup:warmup + steps]]
                 if sel:
                     timed[name] = sum(sel) / len(sel) / 1e3
-    fb, pb = algorithmic_bytes(n, dd)
-    alg = {"k_spec": fb, "k_coop": fb, "k_post": pb}
-    lines = ["# Kernel durations, n=%d tokens, d=%d" % (n, dd), "", "Command:", "", "    " + command, "",
+    fb, pb = algorithmic_bytes(n, dd, hc)
+    alg = {"k_spec": fb, "k_coop": fb, "k_post": pb, "k_gpost": pb}
+    title = "# Kernel durations, n=%d tokens, d=%d" % (n, dd) + (", hc=%d" % hc if hc != 4 else "")
+    lines = [title, "", "Command:", "", "    " + command, "",
              "| kernel | calls | average us | min us | max us | algorithmic GB/s | of 8 TB/s | timed-region average us | of 8 TB/s |",
              "|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"]
         if "hc::" not in name:
             continue
-        short = name.split("hc::")[1].split("(")[0]
+        short = name.split("hc::")[1].replace("(anonymous namespace)::", "").split("(")[0]
         avg = float(r["AverageNs"]) / 1e3
         key = short.split("<")[0].split("::")[-1]
         gbs = alg[key] / (avg * 1e-6) / 1e9 if key in alg else None
@@ -186,6 +188,18 @@ def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, step
         tg = fb / (t * 1e-6) / 1e9 if t else None
         lines.append("| k_part + k_fin (hc_fused_mix_pre, two-pass) | %s | %.2f | - | - | %.1f | %.3f | %s | %s |" % (
             part[0]["Calls"], avg, gbs, gbs / HBM_PEAK_GBS, "%.2f" % t if t else "-",
+            "%.3f" % (tg / HBM_PEAK_GBS) if tg else "-"))
+    # other stream counts run the fused entry point as three plain launches
+    gen = [[r for r in rows if "::k_gmix" in r["Name"]], [r for r in rows if "::k_gsplit<" in r["Name"]],
+           [r for r in rows if "::k_gpre<" in r["Name"]]]
+    if all(gen):
+        avg = sum(float(g[0]["AverageNs"]) for g in gen) / 1e3
+        gbs = fb / (avg * 1e-6) / 1e9
+        ts = [timed.get(g[0]["Name"]) for g in gen]
+        t = sum(ts) if all(ts) else None
+        tg = fb / (t * 1e-6) / 1e9 if t else None
+        lines.append("| k_gmix + k_gsplit + k_gpre (hc_fused_mix_pre) | %s | %.2f | - | - | %.1f | %.3f | %s | %s |" % (
+            gen[0][0]["Calls"], avg, gbs, gbs / HBM_PEAK_GBS, "%.2f" % t if t else "-",
             "%.3f" % (tg / HBM_PEAK_GBS) if tg else "-"))
     lines.append("")
     if steps:
@@ -300,7 +314,7 @@ def main():
             summarize_counters(args.summarize_counters, w.n, w.d, args.profile_command)
         if args.summarize_trace:
             summarize_trace(args.summarize_trace, w.n, w.d, args.profile_command, args.warmup, args.steps,
-                            args.summary_tag)
+                            args.summary_tag, args.hc)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
