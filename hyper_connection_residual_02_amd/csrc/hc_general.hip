@@ -10,9 +10,16 @@
 //               (tokens as float, weights as float), each thread holding a
 //               4 x 4 block of (token, output) sums in double, accumulated
 //               in feature order (k_gmix_pairs: one pair per thread, for
-//               fewer than 48 outputs).
+//               fewer than 48 outputs and many tokens; k_gmix_wave: one
+//               wave per 2-4 tokens, lanes splitting the features, for few
+//               outputs or few tokens).
 //               Products of a bf16 and an fp32 value are exact in double,
-//               so the sums are those of a plain in-order fp64 loop.
+//               so the first two kernels' sums are those of a plain
+//               in-order fp64 loop; the wave kernel adds 64 per-lane
+//               partial sums in a fixed butterfly.  A token's fp32 mixes
+//               can therefore differ in the last bit between calls that
+//               take different kernels (hc = 3 or 5 on either side of
+//               16,384 tokens).
 //  * k_gsplit -- split + epsilon-Sinkhorn, one token per thread, with the
 //               gate, softmax and normalisation arithmetic of the four-stream
 //               kernel (same functions, same order).
@@ -43,6 +50,15 @@ static_assert(kGT * 8 == kGThreads, "one 16-byte chunk of the token tile per thr
 // few threads would own a tile (measured: at 8 outputs the per-pair mapping
 // is 2x faster, at 80 outputs the micro-tiles are 3x faster).
 constexpr int kGTileMinM = 48;
+// Below that, one wave per 2-4 tokens (k_gmix_wave) for at most 8 outputs
+// or fewer than 16,384 tokens, else one pair per thread (k_gmix_pairs).
+// The wave kernel fills the chip at small n but reads the weights once per
+// 2-4 tokens; measured (fused call, d = 5120): hc = 2, 4,096 tokens 69 us
+// against 311, 65,536 tokens 933 against 1,512; hc = 3, 4,096 tokens 225
+// against 478, 65,536 tokens 3,480 against 3,050; hc = 5, 4,096 tokens
+// 1,445 against 2,896, 65,536 tokens 18,813 against 10,827.
+constexpr int kGWaveMaxM = 8;
+constexpr int64_t kGWaveMaxN = 16384;
 
 // Mix formula of the "Mix projection" page: m_j = r * sum_i x_i W[j, i] with
 // r = 1 / sqrt(sum_i x_i^2 / K + norm_eps), K = hc * d.
@@ -410,6 +426,75 @@ __global__ __launch_bounds__(kGThreads) void k_gpost(const uint16_t* __restrict_
     }
 }
 
+// The projection for few outputs ((2 + hc) * hc < 48): one wave per TW
+// tokens.  Lane l takes the 8-feature chunks l, l + 64, ... of the
+// flattened stream and keeps, for each of its tokens, every output's
+// partial sum (and the sum of squares) in double, in chunk order; a
+// butterfly over the wave then adds the 64 partials in one fixed order, so
+// that every lane holds the same total and results do not depend on n.
+// The weights are read from memory (L2) once per TW tokens.
+template <int HC>
+__global__ __launch_bounds__(kGThreads) void k_gmix_wave(const uint16_t* __restrict__ R,
+                                                         const float* __restrict__ W, float* __restrict__ mixes,
+                                                         int64_t n, int d, float norm_eps) {
+    constexpr int M = (2 + HC) * HC;
+    constexpr int TW = M <= 15 ? 4 : 2;          // tokens per wave (register budget of the sums)
+    constexpr int WAVES = kGThreads / 64;
+    const int64_t K = (int64_t)HC * d;
+    const int64_t nch = K / 8;
+    const int lane = threadIdx.x & 63;
+    const int64_t groups = (n + TW - 1) / TW;
+    const int64_t stride = (int64_t)gridDim.x * WAVES;
+    for (int64_t g = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6); g < groups; g += stride) {
+        const int64_t t0 = g * TW;
+        double acc[TW][M + 1];
+#pragma unroll
+        for (int i = 0; i < TW; ++i)
+#pragma unroll
+            for (int j = 0; j <= M; ++j) acc[i][j] = 0.0;
+        for (int64_t c = lane; c < nch; c += 64) {
+            double x[TW][8];
+#pragma unroll
+            for (int i = 0; i < TW; ++i) {
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (t0 + i < n) v = *reinterpret_cast<const uint4*>(R + (t0 + i) * K + c * 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    x[i][e] = bf_at(v, e);
+                    acc[i][M] = __builtin_fma(x[i][e], x[i][e], acc[i][M]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < M; ++j) {
+                const float4 w0 = *reinterpret_cast<const float4*>(W + (int64_t)j * K + c * 8);
+                const float4 w1 = *reinterpret_cast<const float4*>(W + (int64_t)j * K + c * 8 + 4);
+                const double wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                for (int i = 0; i < TW; ++i)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[i][j] = __builtin_fma(x[i][e], wv[e], acc[i][j]);
+            }
+        }
+        // lane l and lane l ^ o add the same two values, so every lane ends
+        // with the same bits
+#pragma unroll
+        for (int i = 0; i < TW; ++i)
+#pragma unroll
+            for (int j = 0; j <= M; ++j)
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) acc[i][j] += __shfl_xor(acc[i][j], o);
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+            if (t0 + i >= n) break;
+            const double r = 1.0 / __builtin_sqrt(acc[i][M] / (double)K + (double)norm_eps);
+            double v = 0.0;
+#pragma unroll
+            for (int j = 0; j < M; ++j) v = lane == j ? acc[i][j] : v;
+            if (lane < M) mixes[(t0 + i) * M + lane] = (float)(v * r);
+        }
+    }
+}
+
 int grid_for(int64_t items) {
     const int64_t cap = (int64_t)num_cus() * 8;
     const int64_t need = (items + kGThreads - 1) / kGThreads;
@@ -431,6 +516,15 @@ int dispatch_hc(int hc_, A... args) {
 }
 
 template <int HC>
+int wave_grid(int64_t n) {
+    constexpr int M = (2 + HC) * HC;
+    constexpr int TW = M <= 15 ? 4 : 2;
+    const int64_t groups = (n + TW - 1) / TW, per = kGThreads / 64;
+    const int64_t need = (groups + per - 1) / per, cap = (int64_t)num_cus() * 16;
+    return (int)(need < cap ? need : cap);
+}
+
+template <int HC>
 struct MixOp {
     static int run(const void* R, const float* W, float* mixes, int64_t n, int d, float norm_eps, hipStream_t s) {
         const int64_t tiles = (n + kGT - 1) / kGT, cap = (int64_t)num_cus() * 16;
@@ -439,6 +533,9 @@ struct MixOp {
         if constexpr (M >= kGTileMinM)
             hipLaunchKernelGGL(k_gmix<HC>, grid, dim3(kGThreads), 0, s, static_cast<const uint16_t*>(R), W, mixes,
                                n, d, norm_eps);
+        else if (M <= kGWaveMaxM || n < kGWaveMaxN)
+            hipLaunchKernelGGL(k_gmix_wave<HC>, dim3(wave_grid<HC>(n)), dim3(kGThreads), 0, s,
+                               static_cast<const uint16_t*>(R), W, mixes, n, d, norm_eps);
         else
             hipLaunchKernelGGL(k_gmix_pairs<HC>, grid, dim3(kGThreads), 0, s, static_cast<const uint16_t*>(R), W,
                                mixes, n, d, norm_eps);

@@ -44,9 +44,11 @@
  * split + Sinkhorn listing of the "Reading weights" page and the mix
  * formula of the "Mix projection" page are written for any hc.  hc = 4 runs
  * the tuned kernels each entry point describes.  Every other count runs
- * plain kernels: the projection in double, each (token, output) sum taken
- * over the features in order, then the split + Sinkhorn with the
- * four-stream arithmetic, then hc_pre / hc_post rounded once as below.
+ * plain kernels: the projection in double (each (token, output) sum taken
+ * over the features in order, or, for few outputs or few tokens, as 64
+ * per-lane partial sums added in one fixed order), then the split +
+ * Sinkhorn with the four-stream arithmetic, then hc_pre / hc_post rounded
+ * once as below.
  * There the projection needs only d % 8 == 0, hc_mixes uses no workspace
  * (it may be NULL), and the fused calls' workspace holds the mixes and pre
  * of every token (hc_fused_workspace_bytes).  The packed-weight calls take

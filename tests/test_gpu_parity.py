@@ -532,11 +532,12 @@ def test_post_mix_pre_other_stream_counts(hc):
         assert torch.equal(u.view(torch.int16), v.view(torch.int16))
 
 
-@pytest.mark.parametrize("hc,d", [(2, 64), (6, 8)])
+@pytest.mark.parametrize("hc,d", [(2, 64), (3, 8), (6, 8)])
 def test_other_stream_count_many_tiles_sampled(orc, hc, d):
-    # more 32-token tiles than the projection kernel's grid: its tile loop
-    # runs several times per workgroup (hc = 2: one pair per thread;
-    # hc = 6: 4 x 4 micro-tiles)
+    # more token groups than the projection kernel's grid, so that its loop
+    # over them runs several times per workgroup; each stream count takes
+    # another projection kernel (hc = 2: one wave per 4 tokens; hc = 3 at
+    # this many tokens: one pair per thread; hc = 6: 4 x 4 micro-tiles)
     n = 140_001
     w = _hc_workload(hc, d)
     t = hin.make_inputs(w, DEV, seed=14, n_tokens=n)
