@@ -319,19 +319,22 @@ def test_packed_weights_match_unpacked_bitwise(d, n):
         assert torch.equal(u, v), (d, n, name)
 
 
-@pytest.mark.parametrize("d,n", [(5120, 64), (5120, 4096), (64, 77)])
-def test_graph_capture_replays_bitwise(d, n):
+@pytest.mark.parametrize("hc,d,n", [(4, 5120, 64), (4, 5120, 4096), (4, 64, 77), (2, 256, 50), (3, 8, 20_000),
+                                    (8, 64, 40)])
+def test_graph_capture_replays_bitwise(hc, d, n):
     # the fused call and hc_post captured into one HIP graph, on the
     # two-pass (64 tokens), persistent (4,096) and cooperative (d = 64)
-    # paths: every replay, with eager calls of the library in between,
-    # gives bitwise the eager results
-    w = hin.Workload("g%d" % d, 1, n, 4, d, 1.0 / np.sqrt(4 * d), 0.5, 2.0, 1.0)
+    # paths, and on the plain kernels of other stream counts (all three
+    # projection kernels): every replay, with eager calls of the library in
+    # between, gives bitwise the eager results
+    w = hin.Workload("g%d" % d, 1, n, hc, d, 1.0 / np.sqrt(hc * d), 0.5, 2.0, 1.0)
+    M = (2 + hc) * hc
     t = hin.make_inputs(w, DEV, seed=97)
     R, x, W, s, b = t["R"], t["x"], t["W"], t["scale"], t["base"]
     ws = hcl.Workspace()
-    outs = dict(h=torch.empty(1, n, d, dtype=torch.bfloat16, device=DEV), pre=torch.empty(1, n, 4, device=DEV),
-                post=torch.empty(1, n, 4, device=DEV), comb=torch.empty(1, n, 4, 4, device=DEV),
-                mixes=torch.empty(1, n, 24, device=DEV))
+    outs = dict(h=torch.empty(1, n, d, dtype=torch.bfloat16, device=DEV), pre=torch.empty(1, n, hc, device=DEV),
+                post=torch.empty(1, n, hc, device=DEV), comb=torch.empty(1, n, hc, hc, device=DEV),
+                mixes=torch.empty(1, n, M, device=DEV))
     Rout = torch.empty_like(R)
 
     def step():
