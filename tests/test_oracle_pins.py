@@ -494,3 +494,117 @@ def test_token_independence(orc):
     part = orc.fused(R[5:9], W, s, b)
     for a, c in zip(full, part):
         assert np.array_equal(a[5:9], c)
+
+
+# --------------------------------------------------------------------------
+# Stream counts other than four.  The split + Sinkhorn listing ("Reading
+# weights" page) and the mix formula ("Mix projection" page) are written for
+# any hc; the GPU's general-hc kernels are checked against the oracle at
+# hc = 1..8, so the oracle is pinned there too.
+
+OTHER_HC = [1, 2, 3, 5, 8]
+
+
+@pytest.mark.parametrize("hc", OTHER_HC)
+def test_uniform_logits_closed_form_any_hc(orc, hc):
+    # the softmax gives 1/hc + eps everywhere; each of the 39 normalisations
+    # then maps c to c / (hc c + eps), so u = 1/c obeys u' = hc + eps u and
+    # reaches hc / (1 - eps) up to eps^39: comb = (1 - eps) / hc
+    m, s, b = _logits_only(np.full((2, hc, hc), 1.25), hc)
+    _, _, comb = orc.split_sinkhorn(m, s, b, hc=hc)
+    assert comb.shape == (2, hc, hc)
+    assert np.allclose(comb, (1 - EPS) / hc, rtol=1e-15, atol=0)
+    _, _, c0 = orc.split_sinkhorn(m, s, b, hc=hc, eps=0.0)
+    assert np.allclose(c0, 1.0 / hc, rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("hc,spread,iters", [(2, 3.0, 20), (3, 6.0, 20), (3, 2.0, 1), (8, 2.0, 20), (5, 1.0, 3)])
+def test_sinkhorn_brute_force_any_hc(orc, hc, spread, iters):
+    rng = np.random.default_rng(100 + hc * 10 + iters)
+    L = rng.standard_normal((2, hc, hc)) * spread
+    m, s, b = _logits_only(L, hc)
+    _, _, C = orc.split_sinkhorn(m, s, b, hc=hc, iters=iters)
+    eps = mp.mpf("1e-6")
+    for t in range(2):
+        ref = _sinkhorn_scaling_vectors(L[t], eps, iters)
+        for j in range(hc):
+            for k in range(hc):
+                r = float(ref[j][k])
+                assert abs(C[t, j, k] - r) <= 1e-13 * max(abs(r), 1e-3), (hc, t, j, k)
+
+
+@pytest.mark.parametrize("hc", [2, 3, 8])
+def test_eps_zero_cross_ratios_any_hc(orc, hc):
+    # eps = 0: rows and columns are only rescaled, so the cross ratios of
+    # exp(L) survive; the last step leaves unit column sums
+    rng = np.random.default_rng(200 + hc)
+    L = rng.standard_normal((2, hc, hc))
+    m, s, b = _logits_only(L, hc)
+    _, _, C = orc.split_sinkhorn(m, s, b, hc=hc, eps=0.0)
+    for t in range(2):
+        for j in range(hc):
+            for jj in range(hc):
+                k, kk = j % hc, (j + 1) % hc
+                lhs = C[t, j, k] * C[t, jj, kk] / (C[t, j, kk] * C[t, jj, k])
+                rhs = math.exp(L[t, j, k] + L[t, jj, kk] - L[t, j, kk] - L[t, jj, k])
+                assert abs(lhs / rhs - 1) < 1e-12
+    assert np.allclose(C.sum(1), 1.0, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("hc", OTHER_HC)
+def test_gates_and_index_roles_any_hc(orc, hc):
+    # mixes [0, hc) feed pre, [hc, 2hc) post, [2hc, (2+hc)hc) the comb
+    # logits; at zero mixes the gates are the closed forms of the bases
+    mp.mp.dps = 40
+    M = (2 + hc) * hc
+    rng = np.random.default_rng(300 + hc)
+    base = rng.standard_normal(M).astype(np.float32)
+    s = np.array([1.3, 0.7, 2.1], np.float32)
+    pre, post, _ = orc.split_sinkhorn(np.zeros((1, M)), s, base, hc=hc)
+    for j in range(hc):
+        assert abs(pre[0, j] - float(_sig(mp.mpf(float(base[j]))) + mp.mpf("1e-6"))) < 1e-15
+        assert abs(post[0, j] - float(2 * _sig(mp.mpf(float(base[hc + j]))))) < 1e-15
+    m = rng.standard_normal((3, M))
+    ref = orc.split_sinkhorn(m, s, base, hc=hc)
+    for j in range(M):
+        m2 = m.copy()
+        m2[:, j] += 0.25
+        out = orc.split_sinkhorn(m2, s, base, hc=hc)
+        moved = [not np.array_equal(out[q], ref[q]) for q in range(3)]
+        # at hc = 1 the comb is a 1 x 1 softmax, 1 whatever its logit
+        assert moved == [j < hc, hc <= j < 2 * hc, j >= 2 * hc and hc > 1], (hc, j)
+
+
+@pytest.mark.parametrize("hc", OTHER_HC)
+def test_mixes_matches_numpy_fp64_any_hc(orc, hc):
+    rng = np.random.default_rng(400 + hc)
+    n, d = 4, 32
+    M = (2 + hc) * hc
+    R = _rand_bits(rng, (n, hc, d))
+    W = (rng.standard_normal((M, hc * d)) * 0.05).astype(np.float32)
+    got = orc.mixes(R, W)
+    assert got.shape == (n, M)
+    X = orc.bf16_to_f64(R).reshape(n, hc * d)          # stream-major flattening
+    ref = (X @ W.astype(np.float64).T) / np.sqrt((X * X).mean(1, keepdims=True) + NEPS)
+    assert np.allclose(got, ref, rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("hc", [1, 2, 3, 8])
+def test_pre_and_post_special_cases_any_hc(orc, hc):
+    rng = np.random.default_rng(500 + hc)
+    n, d = 3, 32
+    R = _rand_bits(rng, (n, hc, d))
+    x = _rand_bits(rng, (n, d))
+    for k in range(hc):
+        w = np.zeros((n, hc))
+        w[:, k] = 1.0
+        assert np.array_equal(orc.pre(R, w), R[:, k, :])
+    zeros = np.zeros((n, hc))
+    eye = np.broadcast_to(np.eye(hc), (n, hc, hc)).copy()
+    assert np.array_equal(orc.post(x, R, zeros, eye), R)
+    out = orc.post(x, R, np.ones((n, hc)), np.zeros((n, hc, hc)))
+    assert all(np.array_equal(out[:, k], x) for k in range(hc))
+    j, k = hc - 1, 0
+    cb = np.zeros((n, hc, hc))
+    cb[:, j, k] = 1.0
+    assert np.array_equal(orc.post(x, R, zeros, cb)[:, k], R[:, j])
