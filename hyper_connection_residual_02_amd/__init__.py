@@ -178,7 +178,8 @@ def hc_mixes(R: torch.Tensor, hc_fn: torch.Tensor, norm_eps: float = 1e-20,
     if out is None:
         out = torch.empty(*lead, M, dtype=torch.float32, device=dev)
     _check(out, "out", torch.float32, dev)
-    wp, wb = _workspace(workspace, hc_fused_workspace_bytes(n, hc, d), dev)
+    # other stream counts run a plain kernel that takes no workspace
+    wp, wb = _workspace(workspace, hc_fused_workspace_bytes(n, hc, d), dev) if hc == 4 else (None, 0)
     with torch.cuda.device(dev):
         _call("hc_mixes", _ptr(R), _ptr(hc_fn), _ptr(out), n, hc, d, float(norm_eps), wp, wb,
               _stream(dev))
