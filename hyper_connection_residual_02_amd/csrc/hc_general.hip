@@ -63,33 +63,43 @@ constexpr int64_t kGWaveMaxN = 16384;
 // Mix formula of the "Mix projection" page: m_j = r * sum_i x_i W[j, i] with
 // r = 1 / sqrt(sum_i x_i^2 / K + norm_eps), K = hc * d.
 //
-// Threads 0..NW-1 each own a 4-token x 4-output micro-tile (tokens
-// tg + 8i, outputs 4 jg + u), so each staged step costs 8 LDS reads per 16
-// products; threads NW..NW+31 form one token's sum of squares each.  All
-// threads stage: the loads of step s + 1 are issued before the products of
-// step s.  Every sum runs over the features in order.
-template <int HC>
-__global__ __launch_bounds__(kGThreads) void k_gmix(const uint16_t* __restrict__ R, const float* __restrict__ W,
-                                                    float* __restrict__ mixes, int64_t n, int d, float norm_eps) {
+// H groups ("halves") of 256 threads take interleaved staged steps (group h
+// the steps H s + h), each with its own LDS tiles, so that with H = 2 a
+// thread walks half the reduction axis: that pays while the tiles alone
+// leave compute units idle, and costs LDS and occupancy otherwise.  In a
+// group, threads 0..NW-1 each own a 4-token x 4-output
+// micro-tile (tokens tg + 8i, outputs 4 jg + u), so each step costs 8 LDS
+// reads per 16 products; threads NW..NW+31 form one token's sum of squares.
+// The loads of a half's next step are issued before the products of its
+// current one.  Each group sums its steps in feature order; with H = 2 the
+// two partial sums are added as (even steps) + (odd steps).
+template <int HC, int H>
+__global__ __launch_bounds__(H * kGThreads) void k_gmix(const uint16_t* __restrict__ R, const float* __restrict__ W,
+                                                        float* __restrict__ mixes, int64_t n, int d, float norm_eps) {
     constexpr int M = (2 + HC) * HC;
     constexpr int TT = 4, JJ = 4;
     constexpr int NT = kGT / TT;                 // token groups
     constexpr int NJ = (M + JJ - 1) / JJ;        // output groups (the last may be padded)
-    constexpr int NW = NT * NJ;                  // threads with a micro-tile
+    constexpr int NW = NT * NJ;                  // threads of a half with a micro-tile
     static_assert(NW + kGT <= kGThreads, "micro-tiles plus one sum-of-squares thread per token");
     constexpr int WCH = M * (kGKC / 4);          // 16-byte weight chunks per step
     constexpr int WPT = (WCH + kGThreads - 1) / kGThreads;
-    __shared__ float xs[kGT][kGKC + 1];          // odd row stride: a wave's rows fall in distinct banks
-    __shared__ float ws[M][kGKC + 1];
+    static_assert(H == 1 || H == 2, "one or two groups");
+    __shared__ float xs[H][kGT][kGKC + 1];       // odd row stride: a wave's rows fall in distinct banks
+    __shared__ float ws[H][M][kGKC + 1];
+    __shared__ double red[H == 2 ? NW : 1][TT * JJ];   // odd-step sums of group 1, added by group 0
+    __shared__ double sred[H == 2 ? kGT : 1];
     __shared__ double ssq[kGT];
     const int64_t K = (int64_t)HC * d;
     const int64_t ntiles = (n + kGT - 1) / kGT;
-    const int tid = threadIdx.x;
+    const int h = threadIdx.x / kGThreads;       // group
+    const int tid = threadIdx.x - h * kGThreads;
     const int tg = tid % NT, jg = tid / NT;
     const int st = tid - NW;
     const int xt = tid >> 3, xq = tid & 7;       // staged x chunk of this thread
 
-    // K is a multiple of 8: a chunk lies wholly inside its row or past its end
+    // K is a multiple of 8: a chunk lies wholly inside its row or past its
+    // end; past K every staged value is zero
     auto load = [&](int64_t t0, int64_t k0, uint4& xv, float4 (&wv)[WPT]) {
         const int64_t k = k0 + xq * 8;
         xv = make_uint4(0u, 0u, 0u, 0u);
@@ -104,7 +114,7 @@ __global__ __launch_bounds__(kGThreads) void k_gmix(const uint16_t* __restrict__
         }
     };
     auto stage = [&](const uint4& xv, const float4 (&wv)[WPT]) {
-        float* xr = &xs[xt][xq * 8];
+        float* xr = &xs[h][xt][xq * 8];
         xr[0] = bf_lo(xv.x); xr[1] = bf_hi(xv.x);
         xr[2] = bf_lo(xv.y); xr[3] = bf_hi(xv.y);
         xr[4] = bf_lo(xv.z); xr[5] = bf_hi(xv.z);
@@ -114,7 +124,7 @@ __global__ __launch_bounds__(kGThreads) void k_gmix(const uint16_t* __restrict__
             const int c = tid + i * kGThreads;
             if (c < WCH) {
                 const int j = c / (kGKC / 4), q = c - j * (kGKC / 4);
-                float* wr = &ws[j][q * 4];
+                float* wr = &ws[h][j][q * 4];
                 wr[0] = wv[i].x; wr[1] = wv[i].y; wr[2] = wv[i].z; wr[3] = wv[i].w;
             }
         }
@@ -130,18 +140,21 @@ __global__ __launch_bounds__(kGThreads) void k_gmix(const uint16_t* __restrict__
         double sacc = 0.0;
         uint4 xv;
         float4 wv[WPT];
-        load(t0, 0, xv, wv);
-        for (int64_t k0 = 0; k0 < K; k0 += kGKC) {
+        load(t0, h * kGKC, xv, wv);
+        for (int64_t k0 = 0; k0 < K; k0 += H * kGKC) {
+            const int64_t kh = k0 + h * kGKC;    // this group's step
             stage(xv, wv);
             __syncthreads();
-            if (k0 + kGKC < K) load(t0, k0 + kGKC, xv, wv);
+            // always: past K it stages zeros (with an odd step count group 1
+            // runs one step more than it has data for)
+            load(t0, kh + H * kGKC, xv, wv);
             if (tid < NW) {
                 const float* xr[TT];
                 const float* wr[JJ];
 #pragma unroll
-                for (int i = 0; i < TT; ++i) xr[i] = xs[tg + NT * i];
+                for (int i = 0; i < TT; ++i) xr[i] = xs[h][tg + NT * i];
 #pragma unroll
-                for (int u = 0; u < JJ; ++u) wr[u] = ws[jg * JJ + u < M ? jg * JJ + u : M - 1];
+                for (int u = 0; u < JJ; ++u) wr[u] = ws[h][jg * JJ + u < M ? jg * JJ + u : M - 1];
 #pragma unroll 8
                 for (int k = 0; k < kGKC; ++k) {
                     double xk[TT], wk[JJ];
@@ -157,15 +170,26 @@ __global__ __launch_bounds__(kGThreads) void k_gmix(const uint16_t* __restrict__
             } else if (st < kGT) {
 #pragma unroll 16
                 for (int k = 0; k < kGKC; ++k) {
-                    const double v = xs[st][k];
+                    const double v = xs[h][st][k];
                     sacc = __builtin_fma(v, v, sacc);
                 }
             }
             __syncthreads();
         }
-        if (st >= 0 && st < kGT) ssq[st] = sacc;
+        if (H == 2 && h == 1) {
+            if (tid < NW) {
+#pragma unroll
+                for (int i = 0; i < TT; ++i)
+#pragma unroll
+                    for (int u = 0; u < JJ; ++u) red[tid][i * JJ + u] = acc[i][u];
+            } else if (st < kGT) {
+                sred[st] = sacc;
+            }
+        }
         __syncthreads();
-        if (tid < NW) {
+        if (h == 0 && st >= 0 && st < kGT) ssq[st] = H == 2 ? sacc + sred[st] : sacc;
+        __syncthreads();
+        if (h == 0 && tid < NW) {
 #pragma unroll
             for (int i = 0; i < TT; ++i) {
                 const int t = tg + NT * i;
@@ -174,11 +198,12 @@ __global__ __launch_bounds__(kGThreads) void k_gmix(const uint16_t* __restrict__
 #pragma unroll
                 for (int u = 0; u < JJ; ++u) {
                     const int j = jg * JJ + u;
-                    if (j < M) mixes[(t0 + t) * M + j] = (float)(acc[i][u] * r);
+                    const double sum = H == 2 ? acc[i][u] + red[tid][i * JJ + u] : acc[i][u];
+                    if (j < M) mixes[(t0 + t) * M + j] = (float)(sum * r);
                 }
             }
         }
-        __syncthreads();        // ssq and the staged tiles are rewritten by the next tile
+        __syncthreads();        // the staged tiles, red and ssq are rewritten by the next tile
     }
 }
 
@@ -530,9 +555,20 @@ struct MixOp {
         const int64_t tiles = (n + kGT - 1) / kGT, cap = (int64_t)num_cus() * 16;
         constexpr int M = (2 + HC) * HC;
         const dim3 grid((unsigned)(tiles < cap ? tiles : cap));
-        if constexpr (M >= kGTileMinM)
-            hipLaunchKernelGGL(k_gmix<HC>, grid, dim3(kGThreads), 0, s, static_cast<const uint16_t*>(R), W, mixes,
-                               n, d, norm_eps);
+        if constexpr (M >= kGTileMinM) {
+            // two groups per tile while fewer than two tiles per compute unit
+            // (measured at d = 5120, 4,096 tokens: hc = 6 2,064 against
+            // 2,840 us, hc = 8 2,840 against 3,799; at 65,536 tokens one group
+            // is faster: 12,020 against 17,198 and 19,477 against 23,707)
+            const auto two = k_gmix<HC, 2>;
+            const auto one = k_gmix<HC, 1>;
+            if (tiles < 2 * (int64_t)num_cus())
+                hipLaunchKernelGGL(two, grid, dim3(2 * kGThreads), 0, s, static_cast<const uint16_t*>(R), W, mixes,
+                                   n, d, norm_eps);
+            else
+                hipLaunchKernelGGL(one, grid, dim3(kGThreads), 0, s, static_cast<const uint16_t*>(R), W, mixes, n,
+                                   d, norm_eps);
+        }
         else if (M <= kGWaveMaxM || n < kGWaveMaxN)
             hipLaunchKernelGGL(k_gmix_wave<HC>, dim3(wave_grid<HC>(n)), dim3(kGThreads), 0, s,
                                static_cast<const uint16_t*>(R), W, mixes, n, d, norm_eps);
