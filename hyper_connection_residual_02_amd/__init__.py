@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "HCError", "load", "lib_path", "hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post",
-    "hc_fused_mix_pre", "hc_post_mix_pre", "hc_pack_weights", "hc_diag_scale", "hc_fused_workspace_bytes",
+    "hc_fused_mix_pre", "hc_fused_mix_pre_noalloc", "hc_post_mix_pre", "hc_pack_weights", "hc_diag_scale", "hc_fused_workspace_bytes",
     "Workspace",
 ]
 
@@ -67,6 +67,7 @@ def load():
         "hc_pack_weights": [P, P, SZ, I32, I32, P],
         "hc_fused_mix_pre_packed": [P, P, SZ, P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, F32, F32, P],
         "hc_diag_scale": [P, P, P, I64, I32, P],
+        "hc_fused_mix_pre_noalloc": [P, P, P, P, P, P, P, P, P, I64, I32, I32, I32, F32, F32, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -76,6 +77,8 @@ def load():
     lib.hc_fused_workspace_bytes.restype = SZ
     lib.hc_packed_weights_bytes.argtypes = [I32, I32]
     lib.hc_packed_weights_bytes.restype = SZ
+    lib.hc_scratch_bytes.argtypes = []
+    lib.hc_scratch_bytes.restype = SZ
     lib.hc_status_str.argtypes = [ctypes.c_int]
     lib.hc_status_str.restype = ctypes.c_char_p
     lib.hc_version.argtypes = []
@@ -308,6 +311,43 @@ def hc_fused_mix_pre(R: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tenso
             _call("hc_fused_mix_pre", _ptr(R), _ptr(hc_fn), _ptr(hc_scale), _ptr(hc_base), _ptr(h),
                   _ptr(pre), _ptr(post), _ptr(comb), _ptr(mixes), wp, wb, n, hc, d,
                   int(sinkhorn_iters), float(hc_eps), float(norm_eps), _stream(dev))
+    return h, pre, post, comb, mixes
+
+
+def hc_fused_mix_pre_noalloc(R: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tensor,
+                             hc_base: torch.Tensor, sinkhorn_iters: int = 20, hc_eps: float = 1e-6,
+                             norm_eps: float = 1e-20, out=None):
+    """hc_fused_mix_pre with the library's static scratch as its workspace:
+    the C call allocates nothing.  ``out`` is a dict with the preallocated
+    outputs h, post, comb (required) and pre, mixes (optional), so that this
+    wrapper allocates nothing either.  Returns (h, pre, post, comb, mixes)."""
+    dev = R.device
+    _check(R, "R", torch.bfloat16)
+    for t, nm in ((hc_fn, "hc_fn"), (hc_scale, "hc_scale"), (hc_base, "hc_base")):
+        _check(t, nm, torch.float32, dev)
+    hc = _streams(R)
+    M = (2 + hc) * hc
+    lead, n, d = _lead(R, hc)
+    if tuple(hc_fn.shape) != (M, hc * d):
+        raise ValueError("hc_fn must be [%d, %d]" % (M, hc * d))
+    o = dict(out or {})
+    for k in ("h", "post", "comb"):
+        if o.get(k) is None:
+            raise ValueError("out[%r] is required (this call allocates nothing)" % k)
+    h, post, comb, pre, mixes = o["h"], o["post"], o["comb"], o.get("pre"), o.get("mixes")
+    _check(h, "h", torch.bfloat16, dev)
+    for t, nm, shape in ((post, "post", lead + (hc,)), (comb, "comb", lead + (hc, hc)),
+                         (pre, "pre", lead + (hc,)), (mixes, "mixes", lead + (M,))):
+        if t is not None:
+            _check(t, nm, torch.float32, dev)
+            if tuple(t.shape) != tuple(shape):
+                raise ValueError("%s must be %s" % (nm, shape))
+    if tuple(h.shape) != lead + (d,):
+        raise ValueError("h must be %s" % (lead + (d,),))
+    with torch.cuda.device(dev):
+        _call("hc_fused_mix_pre_noalloc", _ptr(R), _ptr(hc_fn), _ptr(hc_scale), _ptr(hc_base), _ptr(h),
+              _ptr(pre), _ptr(post), _ptr(comb), _ptr(mixes), n, hc, d, int(sinkhorn_iters), float(hc_eps),
+              float(norm_eps), _stream(dev))
     return h, pre, post, comb, mixes
 
 

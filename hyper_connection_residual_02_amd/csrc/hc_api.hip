@@ -25,6 +25,29 @@ int num_cus() {
     return g_cus[dev];
 }
 
+// ------------------------------------------------ static scratch (no-alloc)
+// Workspace of hc_fused_mix_pre_noalloc, for callers that cannot allocate:
+// one array per device, held until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: the
+// device address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[HC_SCRATCH_BYTES];
+static void* g_scratch[64];
+
+// Device address of this device's scratch array, or null if it cannot be
+// resolved (no device, or the symbol lookup failed).
+void* scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch[dev] = p;
+    }
+    return g_scratch[dev];
+}
+
 }  // namespace hc
 
 namespace {
@@ -65,6 +88,7 @@ const char* hc_status_str(int s) {
         case HC_ERR_VALUE: return "HC_ERR_VALUE: epsilon must be finite and >= 0";
         case HC_ERR_LAUNCH: return "HC_ERR_LAUNCH: the HIP runtime refused a kernel launch";
         case HC_ERR_DEVICE: return "HC_ERR_DEVICE: device query failed";
+        case HC_ERR_SCRATCH: return "HC_ERR_SCRATCH: the call needs more workspace than the static scratch holds (hc_scratch_bytes)";
         default: return "HC_ERR_?: unknown status";
     }
 }
@@ -341,6 +365,23 @@ int hc_fused_mix_pre_packed(const void* R, const void* packed, size_t packed_byt
     if (!packed && n > 0) return HC_ERR_NULL;
     return fused_impl(R, nullptr, packed, packed_bytes, hc_scale, hc_base, h, pre, post, comb, mixes, workspace,
                       workspace_bytes, n, hc_, d, sinkhorn_iters, hc_eps, norm_eps, stream);
+}
+
+size_t hc_scratch_bytes(void) { return HC_SCRATCH_BYTES; }
+
+int hc_fused_mix_pre_noalloc(const void* R, const float* hc_fn, const float* hc_scale, const float* hc_base,
+                             void* h, float* pre, float* post, float* comb, float* mixes, int64_t n, int32_t hc_,
+                             int32_t d, int32_t sinkhorn_iters, float hc_eps, float norm_eps, void* stream) {
+    int st = check_nd(n, hc_, d);
+    if (st) return st;
+    if (n == 0) return HC_OK;
+    // the workspace this call needs must fit the static array; unsupported
+    // shapes (size 0) are reported by the call itself
+    if (hc_fused_workspace_bytes(n, hc_, d) > HC_SCRATCH_BYTES) return HC_ERR_SCRATCH;
+    void* ws = hc::scratch_ptr();
+    if (!ws) return HC_ERR_DEVICE;
+    return fused_impl(R, hc_fn, nullptr, 0, hc_scale, hc_base, h, pre, post, comb, mixes, ws, HC_SCRATCH_BYTES, n,
+                      hc_, d, sinkhorn_iters, hc_eps, norm_eps, stream);
 }
 
 int hc_post_mix_pre(const void* x, const void* R, const float* post, const float* comb, void* R_out,

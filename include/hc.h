@@ -93,7 +93,9 @@ typedef enum hc_status {
     HC_ERR_ALIAS = -6,       /* an output overlaps an input or another output */
     HC_ERR_VALUE = -7,       /* an epsilon is negative or not finite */
     HC_ERR_LAUNCH = -8,      /* the HIP runtime refused a launch */
-    HC_ERR_DEVICE = -9       /* device query failed (no device, bad id) */
+    HC_ERR_DEVICE = -9,      /* device query failed (no device, bad id) */
+    HC_ERR_SCRATCH = -11     /* hc_fused_mix_pre_noalloc: the call needs more
+                                workspace than the static scratch holds */
 } hc_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -260,6 +262,37 @@ int hc_fused_mix_pre_packed(const void *R, const void *packed,
                             void *workspace, size_t workspace_bytes, int64_t n,
                             int32_t hc, int32_t d, int32_t sinkhorn_iters,
                             float hc_eps, float norm_eps, void *stream);
+
+/*
+ * hc_fused_mix_pre_noalloc -- hc_fused_mix_pre for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, outputs, rules and
+ * results (bitwise) as hc_fused_mix_pre, without the workspace arguments:
+ * the workspace is a static device array of HC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends.  The call itself
+ * allocates nothing and calls no allocating routine; its first call on a
+ * device looks up that device's copy of the array (hipGetSymbolAddress).
+ *
+ * Limit: a call whose workspace (hc_fused_workspace_bytes(n, hc, d)) would
+ * exceed HC_SCRATCH_BYTES returns HC_ERR_SCRATCH before any launch
+ * (at hc = 4, d = 5120 every call of up to 125,608 tokens fits).  The array
+ * keeps the last call's contents, which the
+ * workspace header makes harmless to the next call.  Every call on one GPU
+ * shares that GPU's array: calls that may overlap in time on one GPU (on
+ * different streams, or from different threads) race and must not be made;
+ * use hc_fused_mix_pre with a workspace of their own instead.
+ */
+#define HC_SCRATCH_BYTES ((size_t)16 << 20)
+
+int hc_fused_mix_pre_noalloc(const void *R, const float *hc_fn,
+                             const float *hc_scale, const float *hc_base,
+                             void *h, float *pre, float *post, float *comb,
+                             float *mixes, int64_t n, int32_t hc, int32_t d,
+                             int32_t sinkhorn_iters, float hc_eps,
+                             float norm_eps, void *stream);
+
+/* HC_SCRATCH_BYTES, the static scratch of hc_fused_mix_pre_noalloc (host only). */
+size_t hc_scratch_bytes(void);
 
 /*
  * Bytes of device workspace hc_mixes / hc_fused_mix_pre need for these

@@ -216,6 +216,24 @@ def test_workspace_query(lib):
     assert lib.hc_fused_workspace_bytes(65536, 4, 5120) > 0
 
 
+def test_noalloc_checks(lib):
+    cap = lib.hc_scratch_bytes()
+    assert cap == 16 << 20
+
+    def call(n, hc=4, d=5120, R=A):
+        return lib.hc_fused_mix_pre_noalloc(P(R), P(B), P(C), P(D_), P(E), None, P(F_), P(F_ + 4096), None,
+                                            n, hc, d, 20, 1e-6, 1e-20, None)
+    assert call(0) == OK
+    assert call(-1) == SHAPE
+    assert call(4, d=60) == SHAPE
+    assert call(4, hc=9) == UNSUP
+    big = 1
+    while lib.hc_fused_workspace_bytes(big, 4, 5120) <= cap:
+        big *= 2
+    assert call(big) == -11                   # beyond the static scratch: rejected before any launch
+    assert lib.hc_status_str(-11).decode().startswith("HC_ERR_SCRATCH")
+
+
 def test_diag_checks(lib):
     f = lambda h=A, Dp=B, x=C, n=4, d=64: lib.hc_diag_scale(P(h), P(Dp), P(x), n, d, None)
     assert f(n=0) == OK
