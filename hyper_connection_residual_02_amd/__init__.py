@@ -25,7 +25,7 @@ import torch
 __all__ = [
     "HCError", "load", "lib_path", "hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post",
     "hc_fused_mix_pre", "hc_fused_mix_pre_noalloc", "hc_post_mix_pre", "hc_pack_weights", "hc_diag_scale", "hc_fused_workspace_bytes",
-    "Workspace",
+    "Workspace", "workspace_status", "check_workspace", "noalloc_status", "debug_force_timeout",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +77,12 @@ def load():
     lib.hc_fused_workspace_bytes.restype = SZ
     lib.hc_packed_weights_bytes.argtypes = [I32, I32]
     lib.hc_packed_weights_bytes.restype = SZ
+    lib.hc_workspace_status.argtypes = [P, SZ, ctypes.c_int]
+    lib.hc_workspace_status.restype = ctypes.c_int
+    lib.hc_noalloc_status.argtypes = [ctypes.c_int]
+    lib.hc_noalloc_status.restype = ctypes.c_int
+    lib.hc_debug_force_timeout.argtypes = [ctypes.c_int]
+    lib.hc_debug_force_timeout.restype = ctypes.c_int
     lib.hc_scratch_bytes.argtypes = []
     lib.hc_scratch_bytes.restype = SZ
     lib.hc_status_str.argtypes = [ctypes.c_int]
@@ -122,29 +128,84 @@ def hc_fused_workspace_bytes(n: int, hc: int, d: int) -> int:
 
 
 class Workspace:
-    """A reusable, 256-byte aligned device workspace that grows on demand."""
+    """A reusable, 256-byte aligned device workspace that grows on demand.
+
+    Calls that may run at the same time (on different streams) each need a
+    workspace of their own.  When one is used on a stream other than the one
+    its memory was allocated on, the memory is recorded on that stream, so
+    that growing it never hands memory still in use back to the allocator."""
 
     def __init__(self, device=None):
         self.device = torch.device(device) if device is not None else None
         self._buf = None
         self._off = 0
+        self._alloc_stream = None
         self.nbytes = 0
 
     def get(self, nbytes: int, device: torch.device):
+        cur = torch.cuda.current_stream(device)
         if self._buf is None or nbytes > self.nbytes or self._buf.device != device:
             self._buf = torch.empty(int(nbytes) + 256, dtype=torch.uint8, device=device)
             self._off = (-self._buf.data_ptr()) % 256
+            self._alloc_stream = cur
             self.nbytes = int(nbytes)
+        elif cur != self._alloc_stream:
+            self._buf.record_stream(cur)
         return ctypes.c_void_p(self._buf.data_ptr() + self._off), self.nbytes
 
+    def status(self, clear: bool = True) -> int:
+        """hc_workspace_status of this workspace (0, or -10 when a call on it
+        gave up a bounded wait); synchronise with its calls first."""
+        if self._buf is None:
+            return 0
+        with torch.cuda.device(self._buf.device):
+            return int(load().hc_workspace_status(ctypes.c_void_p(self._buf.data_ptr() + self._off),
+                                                  self.nbytes, int(bool(clear))))
 
+
+# default workspaces, one per (device, stream): calls on different streams
+# may run at the same time, so they never share one
 _default_ws = {}
 
 
 def _workspace(ws, nbytes, dev):
     if ws is None:
-        ws = _default_ws.setdefault(str(dev), Workspace())
+        key = (str(dev), torch.cuda.current_stream(dev).cuda_stream)
+        ws = _default_ws.setdefault(key, Workspace())
     return ws.get(max(int(nbytes), 256), dev)
+
+
+def workspace_status(workspace: Workspace | None = None, device=None, clear: bool = True) -> int:
+    """0 if no call on ``workspace`` (default: every default workspace of
+    ``device``) gave up a bounded wait since the last clear, else -10
+    (HC_ERR_TIMEOUT).  Synchronise with the calls first."""
+    if workspace is not None:
+        return workspace.status(clear)
+    dev = str(torch.device(device if device is not None else "cuda"))
+    worst = 0
+    for (d, _), ws in list(_default_ws.items()):
+        if device is None or d == dev:
+            worst = min(worst, ws.status(clear))
+    return worst
+
+
+def check_workspace(workspace: Workspace | None = None, device=None):
+    """Raise HCError when workspace_status reports a failed call."""
+    st = workspace_status(workspace, device, clear=True)
+    if st != 0:
+        raise HCError("hc_workspace_status", st)
+
+
+def noalloc_status(device=None, clear: bool = True) -> int:
+    """hc_noalloc_status: the same for the static scratch of the no-alloc call."""
+    with torch.cuda.device(torch.device(device if device is not None else "cuda")):
+        return int(load().hc_noalloc_status(int(bool(clear))))
+
+
+def debug_force_timeout(calls: int = 1):
+    """Diagnostics: the next ``calls`` launches of the waiting kernels on this
+    thread give up at their first exchange (hc_debug_force_timeout)."""
+    _call("hc_debug_force_timeout", int(calls))
 
 
 def _streams(R: torch.Tensor) -> int:

@@ -88,6 +88,7 @@ const char* hc_status_str(int s) {
         case HC_ERR_VALUE: return "HC_ERR_VALUE: epsilon must be finite and >= 0";
         case HC_ERR_LAUNCH: return "HC_ERR_LAUNCH: the HIP runtime refused a kernel launch";
         case HC_ERR_DEVICE: return "HC_ERR_DEVICE: device query failed";
+        case HC_ERR_TIMEOUT: return "HC_ERR_TIMEOUT: a call on this workspace stopped early (a bounded wait between workgroups gave up); its outputs are undefined";
         case HC_ERR_SCRATCH: return "HC_ERR_SCRATCH: the call needs more workspace than the static scratch holds (hc_scratch_bytes)";
         default: return "HC_ERR_?: unknown status";
     }
@@ -287,7 +288,7 @@ static int gen_fused(const hc::PostIn* prev, const void* R, const float* hc_fn, 
 static int fused_impl(const void* R, const float* hc_fn, const void* packed, size_t packed_bytes,
                       const float* hc_scale, const float* hc_base, void* h, float* pre, float* post, float* comb,
                       float* mixes, void* workspace, size_t workspace_bytes, int64_t n, int32_t hc_, int32_t d,
-                      int32_t sinkhorn_iters, float hc_eps, float norm_eps, void* stream) {
+                      int32_t sinkhorn_iters, float hc_eps, float norm_eps, void* stream, bool gate = true) {
     if (hc_ != 4) {
         if (packed) return HC_ERR_UNSUPPORTED;
         return gen_fused(nullptr, R, hc_fn, hc_scale, hc_base, h, pre, post, comb, mixes, workspace,
@@ -325,6 +326,7 @@ static int fused_impl(const void* R, const float* hc_fn, const void* packed, siz
         for (int j = i + 1; j < no; ++j)
             if (overlap(outs[i], outs[j])) return HC_ERR_ALIAS;
     }
+    p.gate = gate;
     return hc::launch_coop(p, R, hc_fn, hc_scale, hc_base, h, pre, post, comb, mixes, workspace, n, d,
                            sinkhorn_iters, hc_eps, norm_eps, true, (hipStream_t)stream, nullptr, packed)
                ? HC_ERR_LAUNCH
@@ -380,8 +382,31 @@ int hc_fused_mix_pre_noalloc(const void* R, const float* hc_fn, const float* hc_
     if (hc_fused_workspace_bytes(n, hc_, d) > HC_SCRATCH_BYTES) return HC_ERR_SCRATCH;
     void* ws = hc::scratch_ptr();
     if (!ws) return HC_ERR_DEVICE;
+    // no launch ordering across streams here: that would create an event
+    // (calls that overlap on one GPU race on the one array anyway)
     return fused_impl(R, hc_fn, nullptr, 0, hc_scale, hc_base, h, pre, post, comb, mixes, ws, HC_SCRATCH_BYTES, n,
-                      hc_, d, sinkhorn_iters, hc_eps, norm_eps, stream);
+                      hc_, d, sinkhorn_iters, hc_eps, norm_eps, stream, false);
+}
+
+int hc_workspace_status(const void* workspace, size_t workspace_bytes, int clear) {
+    if (!workspace) return HC_ERR_NULL;
+    if ((uintptr_t)workspace & 255u) return HC_ERR_ALIGN;
+    if (workspace_bytes < 256) return HC_ERR_WORKSPACE;
+    const int r = hc::ws_status(workspace, clear != 0);
+    return r < 0 ? HC_ERR_DEVICE : (r ? HC_ERR_TIMEOUT : HC_OK);
+}
+
+int hc_noalloc_status(int clear) {
+    void* ws = hc::scratch_ptr();
+    if (!ws) return HC_ERR_DEVICE;
+    const int r = hc::ws_status(ws, clear != 0);
+    return r < 0 ? HC_ERR_DEVICE : (r ? HC_ERR_TIMEOUT : HC_OK);
+}
+
+int hc_debug_force_timeout(int calls) {
+    if (calls < 0) return HC_ERR_VALUE;
+    hc::set_force_timeout(calls);
+    return HC_OK;
 }
 
 int hc_post_mix_pre(const void* x, const void* R, const float* post, const float* comb, void* R_out,

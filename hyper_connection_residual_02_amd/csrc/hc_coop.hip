@@ -48,6 +48,8 @@
 //    workspace header and the workgroup stops.
 
 #include <atomic>
+#include <mutex>
+#include <stddef.h>
 
 #include "hc_device.hpp"
 #include "hc_launch.hpp"
@@ -70,19 +72,21 @@ constexpr uint32_t kEpochMask = 0xFFFFFu;            // 20-bit call epoch in eac
 constexpr int kBufDword3 = 0x00020000;               // raw buffer resource, dword 3
 constexpr int kOOB = 0x7FFFFFF0;   // buffer offset past every resource: loads read 0, stores drop
 
-// Workspace header (first 256 bytes): magic, call epoch, error flag, and
-// the length (16-byte records) of the record area known to hold only
-// tagged records or zeros.
+// Workspace header (first 256 bytes): magic, call epoch, error flags, the
+// length (16-byte records) of the record area known to hold only tagged
+// records or zeros, and the per-group arrival words of the wave-specialised
+// kernel's start-up.
+constexpr int kMaxGroups = 32;     // token groups of the wave-specialised kernel (G >= 8)
 struct WsHeader {
     uint64_t magic;
     uint32_t epoch;
-    uint32_t err;
+    uint32_t err;       // this call: a bounded wait gave up (the call's workgroups stop)
     int64_t clean;
-    uint32_t xbad;      // workgroups not on the XCD their group is placed on (this call)
-    uint32_t arrive;    // workgroups past the placement check (this call)
     uint64_t ready;     // number of the call whose header update is complete
     uint32_t clear;     // this call clears its record area before use
-    uint32_t pad;
+    uint32_t failed;    // sticky: a call on this workspace gave up; cleared by the host status query
+    uint32_t garr[kMaxGroups];   // group g, this call: members arrived (low 16 bits) and
+                                 // members not on the group's XCD (high 16 bits)
 };
 
 static_assert(sizeof(WsHeader) <= 256, "the header occupies the first 256 bytes of the workspace");
@@ -98,15 +102,16 @@ __host__ __device__ inline uint32_t epoch_of(uint64_t call) { return 1u + (uint3
 // carries a current tag before this call writes it.  Past this call's
 // record area the workspace may receive mixes, so only that area stays
 // known clean.  Returns whether to clear.
-__device__ inline bool header_update(WsHeader* hdr, uint64_t call, int64_t nchunks) {
+__device__ inline bool header_update(WsHeader* hdr, uint64_t call, int64_t nchunks, int ngroups) {
     const uint32_t ep = epoch_of(call);
-    const bool clear = hdr->magic != kMagic || ep <= hdr->epoch || hdr->clean < nchunks;
+    const bool fresh = hdr->magic != kMagic;
+    const bool clear = fresh || ep <= hdr->epoch || hdr->clean < nchunks;
+    if (fresh) hdr->failed = 0u;
     hdr->magic = kMagic;
     hdr->epoch = ep;
     hdr->err = 0u;
     hdr->clean = nchunks;
-    hdr->xbad = 0u;
-    hdr->arrive = 0u;
+    for (int g = 0; g < ngroups && g < kMaxGroups; ++g) hdr->garr[g] = 0u;
     hdr->clear = clear ? 1u : 0u;
     return clear;
 }
@@ -138,7 +143,16 @@ struct CoopArgs {
     uint64_t call;      // process-wide number of this call (sets the record epoch)
     const u32x4* Wp;    // weights already split into MFMA pieces (hc_pack_weights), or null
     int ext_init;       // k_spec: the header was updated by a launch just before (k_hdr)
+    uint64_t spin;      // bound of an exchange wait, in s_memrealtime ticks (100 MHz)
+    uint32_t force_tag; // 0; nonzero (diagnostics only) makes every exchange record look stale
 };
+
+// A bounded wait of this call gave up: peers stop when they see err, and
+// the sticky failed word tells the host (hc_workspace_status).
+__device__ __forceinline__ void give_up(const CoopArgs& a) {
+    __hip_atomic_store(&a.hdr->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&a.hdr->failed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Field f of a partial record (0..23 = the 24 dot products, 24 = sum of
 // squares, 25 = sum of squares of the values times 2^-72) by chunk and
@@ -457,7 +471,7 @@ __device__ __forceinline__ void chunk_sum(const u32x4& v, const CoopArgs& a, flo
 template <int PI, int KS, bool FUSED>
 __device__ __forceinline__ bool exchange(XLoads<PI>& X, const CoopArgs& a, const RoundCtx& c, Lds<KS>& L,
                                          int r) {
-    const uint32_t tag = tag_of(c, r);
+    const uint32_t tag = tag_of(c, r) ^ a.force_tag;
     int chunk, t, m;
     bool stale = false;
     if (FUSED) {
@@ -486,9 +500,9 @@ __device__ __forceinline__ bool exchange(XLoads<PI>& X, const CoopArgs& a, const
                     again |= X.own[j][3] != tag;
                 }
             if (!__builtin_amdgcn_ballot_w64(again)) break;
-            if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull ||
+            if (__builtin_amdgcn_s_memrealtime() - t0 > a.spin ||
                 __hip_atomic_load(&a.hdr->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-                __hip_atomic_store(&a.hdr->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                give_up(a);
                 bad = 1;
                 break;
             }
@@ -1142,7 +1156,7 @@ __device__ __forceinline__ void x_issue(XState<KS>& X, const CoopArgs& a, const 
 template <int KS, bool FUSED, bool LOCAL>
 __device__ __forceinline__ bool x_exchange(XState<KS>& X, const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, int xw,
                                            int r) {
-    const uint32_t tag = tag_of(c, r);
+    const uint32_t tag = tag_of(c, r) ^ a.force_tag;
     const int l = c.l, e = l & 15;
     const int otk = c.q + a.G * xw;
     const int64_t tok0 = tile_of(c, a, r) * kT;
@@ -1165,9 +1179,9 @@ __device__ __forceinline__ bool x_exchange(XState<KS>& X, const CoopArgs& a, con
 #pragma unroll
             for (int s = 0; s < kXL; ++s) again |= own_live(a, c, xw, s) && X.O[s][3] != tag;
             if (!__builtin_amdgcn_ballot_w64(again)) break;
-            if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull ||
+            if (__builtin_amdgcn_s_memrealtime() - t0 > a.spin ||
                 __hip_atomic_load(&a.hdr->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-                __hip_atomic_store(&a.hdr->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                give_up(a);
                 bad = true;
                 break;
             }
@@ -1370,16 +1384,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
     c.bpre = FUSED ? base_of_lane(a.base, (threadIdx.x & 63) >> 4) : 0.0f;
 
     // Start of the call.  Workgroup 0 updates the workspace header and
-    // publishes this call's number; every workgroup waits for it, clears its
-    // share of the record area if the header says so, and only then counts
-    // itself in below, so no record is written before the area is clean.
-    // Placement: with NG a multiple of 8, the members of group g are the
-    // workgroups b = g (mod 8); if every workgroup runs on XCD b % 8 (read
-    // from the XCC id register), each group sits on one XCD and its records
-    // can stay in that XCD's L2.  All workgroups agree through one grid-wide
-    // count before the first record is written.  Both waits are bounded: a
-    // workgroup that is not resident within about two seconds (the launch
-    // does not reserve the device) makes the call stop with the error flag.
+    // publishes this call's number; every workgroup waits for it.  Then the
+    // members of each group clear the group's share of the record area (if
+    // the header says so) and count themselves in on the group's arrival
+    // word, and a group starts once all G of its members have arrived: no
+    // record is written before the group's area is clean, and no workgroup
+    // waits for one outside its own group (there is no grid-wide count, so
+    // one group's members being held back by other work does not stall the
+    // others).  Placement: with NG a multiple of 8, the members of group g
+    // are the workgroups b = g (mod 8), which the dispatcher places on XCD
+    // b % 8 (checked against the XCC id register); a group whose members all
+    // sit on that XCD keeps its records in the XCD's L2.  Every wait is
+    // bounded (about two seconds): a member that is not resident in time
+    // makes the call give up (error flag, reported by hc_workspace_status).
     const int64_t nchunks = a.part_bytes / 16;
     if (threadIdx.x == 0 && a.ext_init) {
         // the header was updated by k_hdr, launched just before this kernel
@@ -1387,7 +1404,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
     } else if (threadIdx.x == 0) {
         bool ok = true;
         if (blockIdx.x == 0) {
-            header_update(a.hdr, a.call, nchunks);
+            header_update(a.hdr, a.call, nchunks, a.NG);
             __hip_atomic_store(&a.hdr->ready, a.call, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         } else {
             const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -1403,32 +1420,38 @@ __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
     }
     __syncthreads();
     if (local_mode < 0) {
-        if (threadIdx.x == 0) __hip_atomic_store(&a.hdr->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0) give_up(a);
         return;
     }
     if (local_mode) {
-        const int64_t per = (nchunks + gridDim.x - 1) / gridDim.x;
-        const int64_t lo = per * blockIdx.x, hi = lo + per < nchunks ? lo + per : nchunks;
+        // this member's part of group g's records (a group's records are
+        // contiguous: [g][slot][member][record])
+        const int64_t gchunks = nchunks / a.NG;
+        const int64_t per = (gchunks + a.G - 1) / a.G;
+        const int64_t gend = (int64_t)(c.g + 1) * gchunks;
+        const int64_t lo = (int64_t)c.g * gchunks + per * c.q, hi = lo + per < gend ? lo + per : gend;
         for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x) a.part[i] = u32x4{0u, 0u, 0u, 0u};
         __threadfence();
     }
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11)) & 0xFu;
-        if (xcc != (blockIdx.x & 7u)) __hip_atomic_fetch_add(&a.hdr->xbad, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(&a.hdr->arrive, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t add = 1u + (xcc != (blockIdx.x & 7u) ? 0x10000u : 0u);
+        uint32_t* gw = &a.hdr->garr[c.g];
+        __hip_atomic_fetch_add(gw, add, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
         bool ok = true;
-        while (__hip_atomic_load(&a.hdr->arrive, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x) {
-            if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull) {
-                __hip_atomic_store(&a.hdr->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t v;
+        while (((v = __hip_atomic_load(gw, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)) & 0xFFFFu) < (uint32_t)a.G) {
+            if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull ||
+                __hip_atomic_load(&a.hdr->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+                give_up(a);
                 ok = false;
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
         }
-        const bool local =
-            a.NG % 8 == 0 && __hip_atomic_load(&a.hdr->xbad, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u;
+        const bool local = a.NG % 8 == 0 && (v >> 16) == 0u;
         local_mode = ok ? (local ? 1 : 0) : -1;
         L.stop = 0;
     }
@@ -1693,8 +1716,8 @@ __global__ __launch_bounds__(256) void k_fin(CoopArgs a, int splits) {
 // update.  With the update in a launch of its own, kernel order does it on
 // every replay (and since a replay repeats the epoch, the update orders the
 // record area cleared, which k_spec's workgroups then do in parallel).
-__global__ void k_hdr(WsHeader* hdr, int64_t nchunks, uint64_t call) {
-    if (threadIdx.x == 0) header_update(hdr, call, nchunks);
+__global__ void k_hdr(WsHeader* hdr, int64_t nchunks, uint64_t call, int ngroups) {
+    if (threadIdx.x == 0) header_update(hdr, call, nchunks, ngroups);
 }
 
 // Header update and record-area clearing before a call of the cooperative
@@ -1702,7 +1725,7 @@ __global__ void k_hdr(WsHeader* hdr, int64_t nchunks, uint64_t call) {
 // at its own start).
 __global__ __launch_bounds__(1024) void k_init(WsHeader* hdr, u32x4* part, int64_t nchunks, uint64_t call) {
     __shared__ int clear;
-    if (threadIdx.x == 0) clear = header_update(hdr, call, nchunks);
+    if (threadIdx.x == 0) clear = header_update(hdr, call, nchunks, 0);
     __syncthreads();
     if (clear)
         for (int64_t i = threadIdx.x; i < nchunks; i += blockDim.x) part[i] = u32x4{0u, 0u, 0u, 0u};
@@ -1712,6 +1735,40 @@ __global__ __launch_bounds__(1024) void k_init(WsHeader* hdr, u32x4* part, int64
 // Calls are numbered process-wide; the number sets the epoch in the record
 // tags, so no per-call initialisation launch is needed.
 static std::atomic<uint64_t> g_calls{0};
+
+// Bound of an exchange wait: 2 s of the 100 MHz s_memrealtime counter.
+constexpr uint64_t kSpin = 200000000ull;
+
+// Diagnostics: the next t_force persistent-kernel launches of this thread
+// take every exchange record for stale and bound their waits to zero time,
+// so their waits give up at once (hc_debug_force_timeout).
+static thread_local int t_force = 0;
+void set_force_timeout(int calls) { t_force = calls; }
+
+// Persistent-kernel launches of one device in this process run one after
+// another: a launch on another stream than the previous one first waits
+// for the previous one (an event), so two persistent grids never share the
+// compute units, each needing all of its group's workgroups resident.
+struct Gate {
+    std::mutex mu;
+    hipEvent_t ev = nullptr;
+    hipStream_t last = nullptr;
+    bool used = false;
+};
+static Gate g_gate[64];
+
+int ws_status(const void* ws, bool clear) {
+    WsHeader h;
+    if (hipMemcpy(&h, ws, sizeof h, hipMemcpyDeviceToHost) != hipSuccess) return -1;
+    if (h.magic != kMagic || h.failed == 0u) return 0;
+    if (clear) {
+        const uint32_t z = 0u;
+        if (hipMemcpy(static_cast<char*>(const_cast<void*>(ws)) + offsetof(WsHeader, failed), &z, sizeof z,
+                      hipMemcpyHostToDevice) != hipSuccess)
+            return -1;
+    }
+    return 1;
+}
 
 int coop_ks(int d) {
     if (d <= 0 || d % 32 != 0) return 0;
@@ -1748,8 +1805,10 @@ bool coop_plan(int64_t n, int d, CoopPlan& p) {
     const int cus = num_cus();
     int ng = cus / p.G;
     if (ng < 1) ng = 1;
+    if (spec_width(p.G) && ng > kMaxGroups) ng = kMaxGroups;     // one header arrival word per group
     if (ng > p.ntiles) ng = (int)(p.ntiles > 0 ? p.ntiles : 1);
     p.NG = ng;
+    p.gate = true;
     p.ws_part = 256;
     p.two_pass = spec_width(p.G) && n <= kTwoPassMaxN;
     p.splits = 1;
@@ -1870,6 +1929,8 @@ int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* s
     a.K = (float)(kHC * d);
     a.part_bytes = (int)(p.ws_mix - p.ws_part);
     a.call = g_calls.fetch_add(1, std::memory_order_relaxed) + 1;
+    a.spin = kSpin;
+    a.force_tag = 0u;
     int rc = -1;
     if (p.two_pass) {
         // mixes go only where the caller asked for them; pass 2 does the split
@@ -1883,16 +1944,37 @@ int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* s
         }
         return -1;
     }
+    // the persistent kernels: waits between workgroups
+    if (t_force > 0) {
+        --t_force;
+        a.spin = 0;
+        a.force_tag = 0x80000000u;
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return -1;
+    const bool capturing = cs != hipStreamCaptureStatusNone;
+    Gate* gate = nullptr;
+    std::unique_lock<std::mutex> lk;
+    if (p.gate && !capturing) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+        gate = &g_gate[dev];
+        lk = std::unique_lock<std::mutex>(gate->mu);
+        if (!gate->ev && hipEventCreateWithFlags(&gate->ev, hipEventDisableTiming) != hipSuccess) {
+            gate->ev = nullptr;
+            return -1;
+        }
+        if (gate->used && gate->last != s && hipStreamWaitEvent(s, gate->ev, 0) != hipSuccess) return -1;
+    }
     if (!use_spec(p)) {
         k_init<<<1, 1024, 0, s>>>(a.hdr, a.part, (int64_t)(a.part_bytes / 16), a.call);
         if (hipGetLastError() != hipSuccess) return -1;
     }
     a.ext_init = 0;
     if (use_spec(p)) {
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+        if (capturing) {
             a.ext_init = 1;
-            k_hdr<<<1, 64, 0, s>>>(a.hdr, (int64_t)(a.part_bytes / 16), a.call);
+            k_hdr<<<1, 64, 0, s>>>(a.hdr, (int64_t)(a.part_bytes / 16), a.call, a.NG);
             if (hipGetLastError() != hipSuccess) return -1;
         }
         switch (p.KS) {
@@ -1908,6 +1990,11 @@ int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* s
         case 3: rc = launch_ks<3>(p, a, fused, s); break;
         case 4: rc = launch_ks<4>(p, a, fused, s); break;
         case 5: rc = launch_ks<5>(p, a, fused, s); break;
+    }
+    if (gate && !rc) {
+        if (hipEventRecord(gate->ev, s) != hipSuccess) return -1;
+        gate->last = s;
+        gate->used = true;
     }
     if (rc || !fused) return rc;
     // post and comb (and pre when not written above): the split + Sinkhorn of

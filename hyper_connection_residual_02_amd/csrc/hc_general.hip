@@ -13,13 +13,12 @@
 //               fewer than 48 outputs and many tokens; k_gmix_wave: one
 //               wave per 2-4 tokens, lanes splitting the features, for few
 //               outputs or few tokens).
-//               Products of a bf16 and an fp32 value are exact in double,
-//               so the first two kernels' sums are those of a plain
-//               in-order fp64 loop; the wave kernel adds 64 per-lane
-//               partial sums in a fixed butterfly.  A token's fp32 mixes
-//               can therefore differ in the last bit between calls that
-//               take different kernels (hc = 3 or 5 on either side of
-//               16,384 tokens).
+//               Products of a bf16 and an fp32 value are exact in double;
+//               k_gmix_pairs sums in feature order, k_gmix as (even staged
+//               steps) + (odd staged steps), and the wave kernel adds 64
+//               per-lane partial sums in a fixed butterfly.  Each stream
+//               count takes one summation order whatever the call's size,
+//               so a token's mixes never depend on the rest of its call.
 //  * k_gsplit -- split + epsilon-Sinkhorn, one token per thread, with the
 //               gate, softmax and normalisation arithmetic of the four-stream
 //               kernel (same functions, same order).
@@ -50,15 +49,16 @@ static_assert(kGT * 8 == kGThreads, "one 16-byte chunk of the token tile per thr
 // few threads would own a tile (measured: at 8 outputs the per-pair mapping
 // is 2x faster, at 80 outputs the micro-tiles are 3x faster).
 constexpr int kGTileMinM = 48;
-// Below that, one wave per 2-4 tokens (k_gmix_wave) for at most 8 outputs
-// or fewer than 16,384 tokens, else one pair per thread (k_gmix_pairs).
-// The wave kernel fills the chip at small n but reads the weights once per
-// 2-4 tokens; measured (fused call, d = 5120): hc = 2, 4,096 tokens 69 us
+// Below that, one wave per 2-4 tokens (k_gmix_wave) for at most 15 outputs
+// (hc = 1, 2, 3), else one pair per thread (k_gmix_pairs, hc = 5), at every
+// n: the two add in different orders, so a size threshold between them
+// would let a token's last mix bit depend on its call's size.  The wave
+// kernel fills the chip at small n but reads the weights once per 2-4
+// tokens; measured (fused call, d = 5120): hc = 2, 4,096 tokens 69 us
 // against 311, 65,536 tokens 933 against 1,512; hc = 3, 4,096 tokens 225
 // against 478, 65,536 tokens 3,480 against 3,050; hc = 5, 4,096 tokens
 // 1,445 against 2,896, 65,536 tokens 18,813 against 10,827.
-constexpr int kGWaveMaxM = 8;
-constexpr int64_t kGWaveMaxN = 16384;
+constexpr int kGWaveMaxM = 15;
 
 // Mix formula of the "Mix projection" page: m_j = r * sum_i x_i W[j, i] with
 // r = 1 / sqrt(sum_i x_i^2 / K + norm_eps), K = hc * d.
@@ -71,8 +71,10 @@ constexpr int64_t kGWaveMaxN = 16384;
 // micro-tile (tokens tg + 8i, outputs 4 jg + u), so each step costs 8 LDS
 // reads per 16 products; threads NW..NW+31 form one token's sum of squares.
 // The loads of a half's next step are issued before the products of its
-// current one.  Each group sums its steps in feature order; with H = 2 the
-// two partial sums are added as (even steps) + (odd steps).
+// current one.  Every sum is formed as (even steps) + (odd steps), each part
+// in feature order: with H = 2 the two groups hold the two parts, with H = 1
+// one thread keeps both, so the two variants give the same bits and a
+// token's mixes do not depend on which one its call takes.
 template <int HC, int H>
 __global__ __launch_bounds__(H * kGThreads) void k_gmix(const uint16_t* __restrict__ R, const float* __restrict__ W,
                                                         float* __restrict__ mixes, int64_t n, int d, float norm_eps) {
@@ -132,22 +134,16 @@ __global__ __launch_bounds__(H * kGThreads) void k_gmix(const uint16_t* __restri
 
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         const int64_t t0 = tile * kGT;
-        double acc[TT][JJ];
+        // acc / sacc: the even steps (H = 2: this group's steps); acc1 /
+        // sacc1: the odd steps (H = 1 only)
+        double acc[TT][JJ], acc1[TT][JJ];
 #pragma unroll
         for (int i = 0; i < TT; ++i)
 #pragma unroll
-            for (int u = 0; u < JJ; ++u) acc[i][u] = 0.0;
-        double sacc = 0.0;
-        uint4 xv;
-        float4 wv[WPT];
-        load(t0, h * kGKC, xv, wv);
-        for (int64_t k0 = 0; k0 < K; k0 += H * kGKC) {
-            const int64_t kh = k0 + h * kGKC;    // this group's step
-            stage(xv, wv);
-            __syncthreads();
-            // always: past K it stages zeros (with an odd step count group 1
-            // runs one step more than it has data for)
-            load(t0, kh + H * kGKC, xv, wv);
+            for (int u = 0; u < JJ; ++u) acc[i][u] = acc1[i][u] = 0.0;
+        double sacc = 0.0, sacc1 = 0.0;
+        // one staged step into the accumulators a / sa
+        auto step = [&](double (&a)[TT][JJ], double& sa) {
             if (tid < NW) {
                 const float* xr[TT];
                 const float* wr[JJ];
@@ -165,16 +161,41 @@ __global__ __launch_bounds__(H * kGThreads) void k_gmix(const uint16_t* __restri
 #pragma unroll
                     for (int i = 0; i < TT; ++i)
 #pragma unroll
-                        for (int u = 0; u < JJ; ++u) acc[i][u] = __builtin_fma(xk[i], wk[u], acc[i][u]);
+                        for (int u = 0; u < JJ; ++u) a[i][u] = __builtin_fma(xk[i], wk[u], a[i][u]);
                 }
             } else if (st < kGT) {
 #pragma unroll 16
                 for (int k = 0; k < kGKC; ++k) {
                     const double v = xs[h][st][k];
-                    sacc = __builtin_fma(v, v, sacc);
+                    sa = __builtin_fma(v, v, sa);
                 }
             }
+        };
+        uint4 xv;
+        float4 wv[WPT];
+        load(t0, h * kGKC, xv, wv);
+        bool odd = false;
+        for (int64_t k0 = 0; k0 < K; k0 += H * kGKC) {
+            const int64_t kh = k0 + h * kGKC;    // this group's step
+            stage(xv, wv);
             __syncthreads();
+            // always: past K it stages zeros (with an odd step count group 1
+            // runs one step more than it has data for)
+            load(t0, kh + H * kGKC, xv, wv);
+            if (H == 1 && odd)
+                step(acc1, sacc1);
+            else
+                step(acc, sacc);
+            odd = !odd;
+            __syncthreads();
+        }
+        if (H == 1) {
+            // the odd steps' sums in the place of group 1's (red / sred)
+#pragma unroll
+            for (int i = 0; i < TT; ++i)
+#pragma unroll
+                for (int u = 0; u < JJ; ++u) acc[i][u] = acc[i][u] + acc1[i][u];
+            sacc = sacc + sacc1;
         }
         if (H == 2 && h == 1) {
             if (tid < NW) {
@@ -569,7 +590,7 @@ struct MixOp {
                 hipLaunchKernelGGL(one, grid, dim3(kGThreads), 0, s, static_cast<const uint16_t*>(R), W, mixes, n,
                                    d, norm_eps);
         }
-        else if (M <= kGWaveMaxM || n < kGWaveMaxN)
+        else if (M <= kGWaveMaxM)
             hipLaunchKernelGGL(k_gmix_wave<HC>, dim3(wave_grid<HC>(n)), dim3(kGThreads), 0, s,
                                static_cast<const uint16_t*>(R), W, mixes, n, d, norm_eps);
         else
@@ -633,9 +654,14 @@ int launch_gen_post(const void* x, const void* R, const float* post, const float
 int launch_gen_fused(const void* R, const float* W, const float* scale, const float* base, void* h, float* pre,
                      float* post, float* comb, float* mixes, void* ws, int64_t n, int hc_, int d, int iters,
                      float eps, float norm_eps, hipStream_t s) {
+    // what this call keeps in the workspace starts at offset 0, so that the
+    // four-stream kernels' header (its first 256 bytes) is overwritten and a
+    // later four-stream call on the same workspace takes it as fresh
+    // (clearing its record area) rather than trusting stale contents
     const size_t M = (size_t)(2 + hc_) * hc_;
-    float* mx = mixes ? mixes : static_cast<float*>(ws);
-    float* pr = pre ? pre : reinterpret_cast<float*>(static_cast<char*>(ws) + align256((size_t)n * M * 4));
+    char* w = static_cast<char*>(ws);
+    float* mx = mixes ? mixes : reinterpret_cast<float*>(w);
+    float* pr = pre ? pre : reinterpret_cast<float*>(w + (mixes ? 0 : align256((size_t)n * M * 4)));
     if (launch_gen_mixes(R, W, mx, n, hc_, d, norm_eps, s)) return -1;
     if (launch_gen_split(mx, scale, base, pr, post, comb, n, hc_, iters, eps, s)) return -1;
     return launch_gen_pre(R, pr, h, n, hc_, d, s);

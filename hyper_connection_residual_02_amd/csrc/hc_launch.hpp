@@ -53,6 +53,7 @@ struct CoopPlan {
     size_t ws_bytes;
     bool two_pass;   // short run: k_part + k_fin instead of the persistent kernel
     int splits;      // two-pass: column parts of h per block of 4 tokens
+    bool gate;       // order persistent launches across streams (off for the no-alloc call)
 };
 // K-steps per wave for d (0: d cannot be tiled).  Host only, no HIP calls.
 int coop_ks(int d);
@@ -74,6 +75,16 @@ int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* s
                 void* h, float* pre, float* post, float* comb, float* mixes, void* ws, int64_t n, int d,
                 int iters, float eps, float norm_eps, bool fused, hipStream_t s, const PostIn* prev = nullptr,
                 const void* Wp = nullptr);
+// Host status of a workspace's header: 1 if a call on it gave up since the
+// last clear (then cleared if `clear`), 0 if not, -1 if the header could not
+// be read.  Synchronous (copies the header to the host).
+int ws_status(const void* ws, bool clear);
+// Diagnostics: the next `calls` persistent-kernel launches of this thread
+// give up at their first exchange wait.
+void set_force_timeout(int calls);
+// Device address of this device's static scratch (hc_api.hip), or null.
+void* scratch_ptr();
+
 // Bytes of packed weights for width d (0: d is not served by the
 // wave-specialised kernels), and the packing launch.
 size_t packed_weights_bytes(int d);

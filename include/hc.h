@@ -45,8 +45,10 @@
  * formula of the "Mix projection" page are written for any hc.  hc = 4 runs
  * the tuned kernels each entry point describes.  Every other count runs
  * plain kernels: the projection in double (each (token, output) sum taken
- * over the features in order, or, for few outputs or few tokens, as 64
- * per-lane partial sums added in one fixed order), then the split +
+ * in one fixed order per stream count, whatever the call's size: over the
+ * features in order at hc = 5, as 64 per-lane partial sums added in one
+ * fixed order at hc = 1..3, as (even 64-feature steps) + (odd steps) at
+ * hc >= 6), then the split +
  * Sinkhorn with the four-stream arithmetic, then hc_pre / hc_post rounded
  * once as below.
  * There the projection needs only d % 8 == 0, hc_mixes uses no workspace
@@ -94,6 +96,9 @@ typedef enum hc_status {
     HC_ERR_VALUE = -7,       /* an epsilon is negative or not finite */
     HC_ERR_LAUNCH = -8,      /* the HIP runtime refused a launch */
     HC_ERR_DEVICE = -9,      /* device query failed (no device, bad id) */
+    HC_ERR_TIMEOUT = -10,    /* hc_workspace_status: a call on the workspace
+                                stopped early (a bounded wait between
+                                workgroups gave up); its outputs are undefined */
     HC_ERR_SCRATCH = -11     /* hc_fused_mix_pre_noalloc: the call needs more
                                 workspace than the static scratch holds */
 } hc_status;
@@ -128,13 +133,18 @@ const char *hc_version(void);
  * streams, each need their own workspace.
  *
  * Calls of more than 2,048 tokens (and every call at widths outside the
- * d = 5120 family) run one ordinary launch whose grid (at most one
- * workgroup per compute unit) fits the device at once; its workgroups wait
- * for each other's partial sums.  Every such wait is bounded: a workgroup
- * that is not resident within about two seconds (say, while long-running
- * work on another stream holds compute units), or a peer that stops, makes
- * the kernel stop early and set an error word in the workspace header;
- * outputs are then undefined.  Shorter calls at widths d = 32*k*G with
+ * d = 5120 family) run one ordinary launch of at most one workgroup per
+ * compute unit, in groups of G workgroups (one XCD's worth at d = 5120)
+ * that wait for each other's partial sums; a group starts once all of its
+ * members are resident, and no workgroup waits for one outside its group.
+ * The library orders these launches across streams: within one process, a
+ * launch on another stream than the previous one on the same device first
+ * waits (a HIP event) for that one to finish, so two such grids never
+ * compete for the compute units (the no-alloc call below is not ordered).
+ * Every wait is bounded: a member that is not resident within about two
+ * seconds (say, while long-running work of another process holds compute
+ * units), or a peer that stops, makes the call stop early; its outputs are
+ * then undefined, and hc_workspace_status reports it.  Shorter calls at widths d = 32*k*G with
  * 8 <= G <= 32 (d = 5120 among them) run two ordinary launches with no
  * waits between workgroups: the partial sums go through the workspace.
  * Both give bitwise the same results for a token, so a token's mixes do not
@@ -262,6 +272,34 @@ int hc_fused_mix_pre_packed(const void *R, const void *packed,
                             void *workspace, size_t workspace_bytes, int64_t n,
                             int32_t hc, int32_t d, int32_t sinkhorn_iters,
                             float hc_eps, float norm_eps, void *stream);
+
+/*
+ * hc_workspace_status -- whether a call on this workspace stopped early.
+ * A call that gives up a bounded wait (see hc_mixes) sets a word in the
+ * workspace header that stays set until this query clears it.  Call it
+ * after synchronising with the calls in question (it copies the header to
+ * the host with a synchronous hipMemcpy -- the one call in this library
+ * that synchronises).  Returns HC_OK (no call gave up, or the workspace
+ * was never used by the calls that wait), HC_ERR_TIMEOUT (some call gave
+ * up since the last clear; with clear != 0 the word is reset), or
+ * HC_ERR_NULL / HC_ERR_ALIGN / HC_ERR_WORKSPACE (bytes < 256) /
+ * HC_ERR_DEVICE (the header could not be read).
+ * hc_noalloc_status: the same for this device's static scratch of
+ * hc_fused_mix_pre_noalloc.
+ */
+int hc_workspace_status(const void *workspace, size_t workspace_bytes,
+                        int clear);
+int hc_noalloc_status(int clear);
+
+/*
+ * hc_debug_force_timeout -- diagnostics for tests of the failure path:
+ * the next `calls` launches of the waiting kernels (see hc_mixes) made by
+ * the calling host thread take every exchanged partial sum for stale and
+ * bound their waits to zero time, so each such call gives up at its first
+ * exchange, its kernels exit normally, and hc_workspace_status reports
+ * HC_ERR_TIMEOUT.  0 cancels.  HC_ERR_VALUE if calls < 0.
+ */
+int hc_debug_force_timeout(int calls);
 
 /*
  * hc_fused_mix_pre_noalloc -- hc_fused_mix_pre for callers that cannot

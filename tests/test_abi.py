@@ -41,7 +41,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(-9, 1):
+    assert lib.hc_status_str(-10).decode().startswith("HC_ERR_TIMEOUT")
+    for code in range(-11, 1):
         s = lib.hc_status_str(code).decode()
         assert s.startswith("HC_")
     assert lib.hc_status_str(-100).decode().startswith("HC_ERR_?")
@@ -232,6 +233,15 @@ def test_noalloc_checks(lib):
         big *= 2
     assert call(big) == -11                   # beyond the static scratch: rejected before any launch
     assert lib.hc_status_str(-11).decode().startswith("HC_ERR_SCRATCH")
+
+
+def test_status_query_and_diagnostics_checks(lib):
+    # argument checks only (no device memory is read on these paths)
+    assert lib.hc_workspace_status(None, 4096, 1) == NULL
+    assert lib.hc_workspace_status(P(A + 16), 4096, 1) == ALIGN
+    assert lib.hc_workspace_status(P(A), 255, 1) == WS
+    assert lib.hc_debug_force_timeout(-1) == VALUE
+    assert lib.hc_debug_force_timeout(0) == OK
 
 
 def test_diag_checks(lib):

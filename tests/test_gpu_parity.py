@@ -539,8 +539,8 @@ def test_post_mix_pre_other_stream_counts(hc):
 def test_other_stream_count_many_tiles_sampled(orc, hc, d):
     # more token groups than the projection kernel's grid, so that its loop
     # over them runs several times per workgroup; each stream count takes
-    # another projection kernel (hc = 2: one wave per 4 tokens; hc = 3 at
-    # this many tokens: one pair per thread; hc = 6: 4 x 4 micro-tiles)
+    # another projection kernel (hc = 2: one wave per 4 tokens; hc = 3: one
+    # wave per 4 tokens with 15 outputs; hc = 6: 4 x 4 micro-tiles, one group)
     n = 140_001
     w = _hc_workload(hc, d)
     t = hin.make_inputs(w, DEV, seed=14, n_tokens=n)
@@ -549,16 +549,16 @@ def test_other_stream_count_many_tiles_sampled(orc, hc, d):
     compare_fused(orc, t["R"], t["W"], t["scale"], t["base"], outs, idx=idx, x=t["x"], label="hc=%d n=140001" % hc)
 
 
-@pytest.mark.parametrize("hc,d,n,span", [(2, 256, 101, 37), (5, 64, 101, 37), (3, 8, 50_001, 20_000),
-                                         (8, 64, 101, 37), (6, 8, 20_001, 17_000)])
+@pytest.mark.parametrize("hc,d,n,span", [(2, 256, 101, 37), (5, 64, 20_001, 37), (3, 8, 50_001, 1_000),
+                                         (8, 64, 101, 37), (6, 8, 20_001, 300), (8, 8, 17_001, 40)])
 def test_other_stream_counts_batch_invariant_and_deterministic(hc, d, n, span):
     # a token's results do not depend on the other tokens of its call, and
-    # repeated calls agree bit for bit: the wave kernel (hc = 2, 5 at 101
-    # tokens), one pair per thread (hc = 3: both calls above 16,384 tokens)
-    # and the micro-tiles (hc = 8 at 101 tokens: two groups per tile; hc = 6
-    # with both calls above 16,384 tokens: one group).  Kernel choices change
-    # at 16,384 tokens, where the summation order, and so possibly the last
-    # bit of a mix, changes too: both calls stay on one side of it.
+    # repeated calls agree bit for bit, for every projection kernel: the wave
+    # kernel (hc = 2, 3), one pair per thread (hc = 5) and the micro-tiles
+    # (hc = 6, 8).  The long and short calls straddle 16,384 tokens, where the
+    # micro-tile kernel switches from two groups per tile to one (both add
+    # (even steps) + (odd steps)), and where hc = 3 and 5 once switched
+    # kernels.
     w = _hc_workload(hc, d)
     t = hin.make_inputs(w, DEV, seed=15, n_tokens=n)
     lo = n // 3 + 1
