@@ -16,6 +16,10 @@ arrays.  Every function follows a passage of the pages:
                         hc_split_sinkhorn kernel listing.
 * ``pre``, ``post``  -- "Mix projection" page, Block.hc_pre / Block.hc_post.
 * ``diag_scale``     -- the chained-stack workload's stand-in sublayer.
+* ``post_backward``, ``pre_backward``, ``split_sinkhorn_backward``,
+  ``mixes_backward``, ``backward`` -- the gradient of a scalar loss through
+  the same steps (chain rule over the forward in reverse order; the pages
+  give the forward only).
 * ``round_bf16``     -- round-to-nearest-even from double to bf16.
 
 bf16 tensors cross this interface as ``numpy.uint16`` bit patterns.
@@ -66,6 +70,14 @@ def _load():
     lib.hco_post.restype = None
     lib.hco_diag_scale.argtypes = [P, P, I64, I32, P]
     lib.hco_diag_scale.restype = None
+    lib.hco_post_backward.argtypes = [P, P, P, P, P, I64, I32, I32, P, P, P, P]
+    lib.hco_post_backward.restype = None
+    lib.hco_pre_backward.argtypes = [P, P, P, I64, I32, I32, P, P]
+    lib.hco_pre_backward.restype = None
+    lib.hco_split_sinkhorn_backward.argtypes = [P, P, P, P, P, P, I64, I32, I32, F64, P, P, P]
+    lib.hco_split_sinkhorn_backward.restype = ctypes.c_int
+    lib.hco_mixes_backward.argtypes = [P, P, P, I64, I32, I32, F64, P, P]
+    lib.hco_mixes_backward.restype = None
     lib.hco_round_bf16.argtypes = [F64]
     lib.hco_round_bf16.restype = ctypes.c_uint16
     lib.hco_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -176,3 +188,96 @@ def fused(R_bits, W, scale, base, iters: int = 20, eps: float = 1e-6,
     p, q, c = split_sinkhorn(m, scale, base, hc, iters, eps)
     h = pre(R, p)
     return h, p, q, c, m
+
+
+# ------------------------------------------------------------------ backward
+
+def post_backward(x_bits, R_bits, post_w, comb, gRout_bits):
+    """Gradient through hc_post: (gx[n,d], gpost[n,hc], gcomb[n,hc,hc],
+    gR[n,hc,d]) float64 from dL/dR' (bf16 patterns)."""
+    R, pR = _c(R_bits, np.uint16)
+    n, hc, d = R.shape
+    x, px = _c(x_bits, np.uint16)
+    g, pg = _c(gRout_bits, np.uint16)
+    p, pp = _c(post_w, np.float64)
+    cb, pc = _c(comb, np.float64)
+    assert x.shape == (n, d) and g.shape == (n, hc, d)
+    assert p.shape == (n, hc) and cb.shape == (n, hc, hc)
+    gx = np.empty((n, d)); gp = np.empty((n, hc)); gc = np.empty((n, hc, hc))
+    gR = np.empty((n, hc, d))
+    _load().hco_post_backward(px, pR, pp, pc, pg, n, hc, d, gx.ctypes.data, gp.ctypes.data,
+                              gc.ctypes.data, gR.ctypes.data)
+    return gx, gp, gc, gR
+
+
+def pre_backward(R_bits, pre_w, gh_bits):
+    """Gradient through hc_pre: (gpre[n,hc], gR[n,hc,d]) float64 from dL/dh."""
+    R, pR = _c(R_bits, np.uint16)
+    n, hc, d = R.shape
+    g, pg = _c(gh_bits, np.uint16)
+    p, pp = _c(pre_w, np.float64)
+    assert g.shape == (n, d) and p.shape == (n, hc)
+    gpre = np.empty((n, hc)); gR = np.empty((n, hc, d))
+    _load().hco_pre_backward(pR, pp, pg, n, hc, d, gpre.ctypes.data, gR.ctypes.data)
+    return gpre, gR
+
+
+def split_sinkhorn_backward(mix, scale, base, gpre, gpost, gcomb, hc: int = 4,
+                            iters: int = 20, eps: float = 1e-6):
+    """Gradient through the split + Sinkhorn: (gmixes[n,M], gscale[3],
+    gbase[M], gscale_tok[n,3], gbase_tok[n,M]) float64; gscale and gbase are
+    the per-token contributions summed over tokens in order."""
+    m, pm = _c(mix, np.float64)
+    n = m.shape[0]
+    M = (2 + hc) * hc
+    assert m.shape == (n, M)
+    s, ps = _c(scale, np.float32)
+    b, pb = _c(base, np.float32)
+    gp, pgp = _c(gpre, np.float64)
+    gq, pgq = _c(gpost, np.float64)
+    gc, pgc = _c(gcomb, np.float64)
+    assert gp.shape == (n, hc) and gq.shape == (n, hc) and gc.shape == (n, hc, hc)
+    gm = np.empty((n, M)); gs = np.empty((n, 3)); gb = np.empty((n, M))
+    rc = _load().hco_split_sinkhorn_backward(pm, ps, pb, pgp, pgq, pgc, n, hc, int(iters), float(eps),
+                                             gm.ctypes.data, gs.ctypes.data, gb.ctypes.data)
+    if rc != 0:
+        raise ValueError("split_sinkhorn_backward: unsupported hc=%d or iters=%d" % (hc, iters))
+    gsum = np.zeros(3); bsum = np.zeros(M)
+    for t in range(n):
+        gsum += gs[t]
+        bsum += gb[t]
+    return gm, gsum, bsum, gs, gb
+
+
+def mixes_backward(R_bits, W, gmix, norm_eps: float = 1e-20):
+    """Gradient through the mix formula: (gR[n,hc,d], gW[M,hc*d]) float64."""
+    R, pR = _c(R_bits, np.uint16)
+    n, hc, d = R.shape
+    Wc, pW = _c(W, np.float32)
+    M = (2 + hc) * hc
+    g, pg = _c(gmix, np.float64)
+    assert Wc.shape == (M, hc * d) and g.shape == (n, M)
+    gR = np.empty((n, hc, d)); gW = np.empty((M, hc * d))
+    _load().hco_mixes_backward(pR, pW, pg, n, hc, d, float(norm_eps), gR.ctypes.data, gW.ctypes.data)
+    return gR, gW
+
+
+def backward(R_bits, x_bits, W, scale, base, gRout_bits, gh_bits, iters: int = 20,
+             eps: float = 1e-6, norm_eps: float = 1e-20, mix=None):
+    """The whole gradient of one sublayer's mixing, given dL/dR' and dL/dh:
+    the forward coefficients (from ``mix`` when given, else the oracle's own
+    mixes), then hc_post's, hc_pre's, the split's and the projection's
+    backward.  Returns a dict of float64 arrays: gR (the three shares
+    summed), gR_post, gR_pre, gR_mix, gx, gpost, gcomb, gpre, gmixes, gW,
+    gscale, gbase, and the coefficients pre, post, comb, mixes used."""
+    R = np.asarray(R_bits, dtype=np.uint16)
+    hc = R.shape[1]
+    m = mixes(R, W, norm_eps) if mix is None else np.asarray(mix, dtype=np.float64)
+    p, q, c = split_sinkhorn(m, scale, base, hc, iters, eps)
+    gx, gpost, gcomb, gR_post = post_backward(x_bits, R, q, c, gRout_bits)
+    gpre, gR_pre = pre_backward(R, p, gh_bits)
+    gm, gs, gb, _, _ = split_sinkhorn_backward(m, scale, base, gpre, gpost, gcomb, hc, iters, eps)
+    gR_mix, gW = mixes_backward(R, W, gm, norm_eps)
+    return dict(gR=gR_post + gR_pre + gR_mix, gR_post=gR_post, gR_pre=gR_pre, gR_mix=gR_mix, gx=gx,
+                gpost=gpost, gcomb=gcomb, gpre=gpre, gmixes=gm, gW=gW, gscale=gs, gbase=gb,
+                pre=p, post=q, comb=c, mixes=m)

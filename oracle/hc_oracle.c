@@ -31,8 +31,10 @@
  *
  * Parity status: every function here is pinned by tests against closed
  * forms, invariants, special cases, an independent library routine or a
- * high-precision brute force in a different formulation; none is
- * "parity unpinned".
+ * high-precision brute force in a different formulation (the backward
+ * functions: finite differences of the forward in fp64 and in 40-digit
+ * arithmetic, chain-rule identities, scale and shift invariances, and the
+ * closed form at W = 0); none is "parity unpinned".
  */
 #include <math.h>
 #include <stdint.h>
@@ -265,6 +267,302 @@ void hco_diag_scale(const uint16_t *h, const uint16_t *D, int64_t n, int d,
             x[t * (int64_t)d + c] = hco_round_bf16(
                 hco_bf16_to_double(h[t * (int64_t)d + c]) *
                 hco_bf16_to_double(D[c]));
+}
+
+/* ====================================================================
+ * Backward pass (gradients of a scalar loss through one sublayer's
+ * mixing).  The pages give the forward only; its gradient is defined by
+ * the chain rule over the forward's steps, taken here in reverse order.
+ * The bf16 roundings of h and R' are outputs' storage, not steps of the
+ * function: the gradient is that of the real-valued forward (each output
+ * before its rounding).  Inputs that the GPU holds in bf16 (R, x and the
+ * incoming gradients gRout, gh) come as bf16 patterns; coefficients as
+ * double; every result is double.
+ * ==================================================================== */
+
+/*
+ * Backward of [MP] Block.hc_post, R'_{k,c} = post_k x_c + sum_j comb[j][k] R_{j,c}:
+ *   gx[t][c]       = sum_k post_k gRout_{k,c}
+ *   gpost[t][k]    = sum_c x_c gRout_{k,c}
+ *   gcomb[t][j][k] = sum_c R_{j,c} gRout_{k,c}
+ *   gR[t][j][c]    = sum_k comb[j][k] gRout_{k,c}     (hc_post's share of dL/dR)
+ */
+void hco_post_backward(const uint16_t *x, const uint16_t *R, const double *post,
+                       const double *comb, const uint16_t *gRout, int64_t n,
+                       int hc, int d, double *gx, double *gpost, double *gcomb,
+                       double *gR)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        const uint16_t *xt = x + t * (int64_t)d;
+        const uint16_t *Rt = R + t * (int64_t)hc * d;
+        const uint16_t *gt = gRout + t * (int64_t)hc * d;
+        const double *pt = post + t * hc, *ct = comb + t * hc * hc;
+        for (int c = 0; c < d; ++c) {
+            double a = 0.0;
+            for (int k = 0; k < hc; ++k)
+                a += pt[k] * hco_bf16_to_double(gt[(int64_t)k * d + c]);
+            gx[t * (int64_t)d + c] = a;
+        }
+        for (int k = 0; k < hc; ++k) {
+            double a = 0.0;
+            for (int c = 0; c < d; ++c)
+                a += hco_bf16_to_double(xt[c]) *
+                     hco_bf16_to_double(gt[(int64_t)k * d + c]);
+            gpost[t * hc + k] = a;
+        }
+        for (int j = 0; j < hc; ++j)
+            for (int k = 0; k < hc; ++k) {
+                double a = 0.0;
+                for (int c = 0; c < d; ++c)
+                    a += hco_bf16_to_double(Rt[(int64_t)j * d + c]) *
+                         hco_bf16_to_double(gt[(int64_t)k * d + c]);
+                gcomb[(t * hc + j) * hc + k] = a;
+            }
+        for (int j = 0; j < hc; ++j)
+            for (int c = 0; c < d; ++c) {
+                double a = 0.0;
+                for (int k = 0; k < hc; ++k)
+                    a += ct[j * hc + k] *
+                         hco_bf16_to_double(gt[(int64_t)k * d + c]);
+                gR[(t * hc + j) * (int64_t)d + c] = a;
+            }
+    }
+}
+
+/*
+ * Backward of [MP] Block.hc_pre, h_c = sum_k pre_k R_{k,c}:
+ *   gpre[t][k]  = sum_c gh_c R_{k,c}
+ *   gR[t][k][c] = pre_k gh_c                          (hc_pre's share of dL/dR)
+ */
+void hco_pre_backward(const uint16_t *R, const double *pre, const uint16_t *gh,
+                      int64_t n, int hc, int d, double *gpre, double *gR)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        const uint16_t *ght = gh + t * (int64_t)d;
+        for (int k = 0; k < hc; ++k) {
+            const uint16_t *Rk = R + (t * hc + k) * (int64_t)d;
+            double a = 0.0;
+            for (int c = 0; c < d; ++c)
+                a += hco_bf16_to_double(ght[c]) * hco_bf16_to_double(Rk[c]);
+            gpre[t * hc + k] = a;
+            for (int c = 0; c < d; ++c)
+                gR[(t * hc + k) * (int64_t)d + c] =
+                    pre[t * hc + k] * hco_bf16_to_double(ght[c]);
+        }
+    }
+}
+
+/*
+ * Backward of one normalisation step Y = X / (s + eps), s the sum of X
+ * along the step's axis (rows: axis 1, columns: axis 0).  With Y and the
+ * denominators D = s + eps of the forward step:
+ *   dY_jk / dX_jl = (delta_kl - Y_jk) / D_j     (a row step; columns alike)
+ * so gX = (gY - sum_along(gY * Y)) / D.  g holds gY on entry, gX on exit.
+ */
+static void normalise_backward(double g[HCO_MAX_HC][HCO_MAX_HC],
+                               const double Y[HCO_MAX_HC][HCO_MAX_HC],
+                               const double *D, int hc, int rows)
+{
+    for (int a = 0; a < hc; ++a) {
+        double dot = 0.0;
+        for (int b = 0; b < hc; ++b)
+            dot += rows ? g[a][b] * Y[a][b] : g[b][a] * Y[b][a];
+        for (int b = 0; b < hc; ++b) {
+            if (rows)
+                g[a][b] = (g[a][b] - dot) / D[a];
+            else
+                g[b][a] = (g[b][a] - dot) / D[a];
+        }
+    }
+}
+
+static double sigmoid_slope(double z)
+{
+    double s = sigmoid(z);
+    return s * (1.0 - s);
+}
+
+/*
+ * Backward of the [RW] split and epsilon-Sinkhorn (hco_split_sinkhorn),
+ * per token.  The forward's matrices after each step are recomputed and
+ * kept; then, in reverse order:
+ *   each normalisation step: normalise_backward;
+ *   "+ eps": the identity;
+ *   row softmax P = softmax(L): gL_jk = P_jk (gP_jk - sum_k' gP_jk' P_jk');
+ *   the gates and logits, z = s * m + b: gm = s gz, gs = m gz, gb = gz,
+ *   with gz = gpre sigma'(z) for pre, gpost * 2 sigma'(z) for post, and
+ *   gz = gL for the comb logits.
+ * Outputs: gmixes[t][M], and each token's contributions to the scale and
+ * base gradients, gscale_tok[t][3] and gbase_tok[t][M] (their sums over
+ * tokens are the gradients of hc_scale and hc_base).  Returns 0, or -1 if
+ * hc is out of range or iters < 1.
+ */
+int hco_split_sinkhorn_backward(const double *mixes, const float *scale,
+                                const float *base, const double *gpre,
+                                const double *gpost, const double *gcomb,
+                                int64_t n, int hc, int iters, double eps,
+                                double *gmixes, double *gscale_tok,
+                                double *gbase_tok)
+{
+    if (hc < 1 || hc > HCO_MAX_HC || iters < 1)
+        return -1;
+    const int M = (2 + hc) * hc;
+    const double s[3] = {scale[0], scale[1], scale[2]};
+    /* normalisation steps after the softmax: one column step, then
+     * (iters - 1) pairs of a row and a column step */
+    const int nsteps = 2 * iters - 1;
+    int bad = 0;
+#pragma omp parallel
+    {
+        /* forward states: Ys[k] after normalisation step k, Ds[k] its denominators */
+        double (*Ys)[HCO_MAX_HC][HCO_MAX_HC] =
+            malloc(sizeof(*Ys) * (size_t)nsteps);
+        double *Ds = malloc(sizeof(double) * (size_t)nsteps * HCO_MAX_HC);
+        if (!Ys || !Ds) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < n; ++t) {
+            if (!Ys || !Ds)
+                continue;
+            const double *m = mixes + t * M;
+            double *gm = gmixes + t * M, *gs = gscale_tok + t * 3,
+                   *gb = gbase_tok + t * M;
+            gs[0] = gs[1] = gs[2] = 0.0;
+            /* gates */
+            for (int j = 0; j < hc; ++j) {
+                double z = s[0] * m[j] + (double)base[j];
+                double gz = gpre[t * hc + j] * sigmoid_slope(z);
+                gm[j] = s[0] * gz;
+                gs[0] += m[j] * gz;
+                gb[j] = gz;
+                double y = s[1] * m[hc + j] + (double)base[hc + j];
+                double gy = gpost[t * hc + j] * 2.0 * sigmoid_slope(y);
+                gm[hc + j] = s[1] * gy;
+                gs[1] += m[hc + j] * gy;
+                gb[hc + j] = gy;
+            }
+            /* forward of the comb, keeping every step */
+            double P[HCO_MAX_HC][HCO_MAX_HC], X[HCO_MAX_HC][HCO_MAX_HC];
+            for (int j = 0; j < hc; ++j) {
+                double L[HCO_MAX_HC], mx = -INFINITY, z = 0.0;
+                for (int k = 0; k < hc; ++k) {
+                    L[k] = s[2] * m[2 * hc + j * hc + k] +
+                           (double)base[2 * hc + j * hc + k];
+                    if (L[k] > mx)
+                        mx = L[k];
+                }
+                for (int k = 0; k < hc; ++k) {
+                    P[j][k] = exp(L[k] - mx);
+                    z += P[j][k];
+                }
+                for (int k = 0; k < hc; ++k) {
+                    P[j][k] /= z;
+                    X[j][k] = P[j][k] + eps;
+                }
+            }
+            for (int st = 0; st < nsteps; ++st) {
+                /* step 0 is a column step; then rows and columns alternate */
+                const int rows = st % 2 == 1;
+                double *D = Ds + (size_t)st * HCO_MAX_HC;
+                for (int a = 0; a < hc; ++a) {
+                    double sum = 0.0;
+                    for (int b = 0; b < hc; ++b)
+                        sum += rows ? X[a][b] : X[b][a];
+                    D[a] = sum + eps;
+                    for (int b = 0; b < hc; ++b) {
+                        if (rows)
+                            X[a][b] = X[a][b] / D[a];
+                        else
+                            X[b][a] = X[b][a] / D[a];
+                    }
+                }
+                memcpy(Ys[st], X, sizeof(X));
+            }
+            /* reverse */
+            double g[HCO_MAX_HC][HCO_MAX_HC];
+            for (int j = 0; j < hc; ++j)
+                for (int k = 0; k < hc; ++k)
+                    g[j][k] = gcomb[(t * hc + j) * hc + k];
+            for (int st = nsteps - 1; st >= 0; --st)
+                normalise_backward(g, Ys[st], Ds + (size_t)st * HCO_MAX_HC,
+                                   hc, st % 2 == 1);
+            /* g is now the gradient of P (the "+ eps" passes it through) */
+            for (int j = 0; j < hc; ++j) {
+                double dot = 0.0;
+                for (int k = 0; k < hc; ++k)
+                    dot += g[j][k] * P[j][k];
+                for (int k = 0; k < hc; ++k) {
+                    const int i = 2 * hc + j * hc + k;
+                    double gL = P[j][k] * (g[j][k] - dot);
+                    gm[i] = s[2] * gL;
+                    gs[2] += m[i] * gL;
+                    gb[i] = gL;
+                }
+            }
+        }
+        free(Ys);
+        free(Ds);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Backward of the [MP] mix formula, m_j = r dot_j with dot_j = sum_i W_ji X_i
+ * and r = (sum_i X_i^2 / K + norm_eps)^(-1/2), r and dot recomputed from R:
+ *   gdot_j = r gm_j
+ *   dr/dss = -r^3 / (2K), so gss = -(r^3 / (2K)) sum_j gm_j dot_j
+ *   gR[t][i] = sum_j gdot_j W_ji + 2 X_i gss        (the projection's share of dL/dR)
+ *   gW[j][i] = sum_t gdot_tj X_ti                   (summed over tokens in order)
+ * gR is [n][hc*d] (flattened like the forward), gW is [M][hc*d].
+ */
+void hco_mixes_backward(const uint16_t *R, const float *W, const double *gmixes,
+                        int64_t n, int hc, int d, double norm_eps, double *gR,
+                        double *gW)
+{
+    const int64_t K = (int64_t)hc * d;
+    const int M = (2 + hc) * hc;
+    double *gdot = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * M);
+    if (!gdot)
+        return;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        const uint16_t *x = R + t * K;
+        double ss = 0.0;
+        for (int64_t i = 0; i < K; ++i) {
+            double v = hco_bf16_to_double(x[i]);
+            ss += v * v;
+        }
+        const double r = 1.0 / sqrt(ss / (double)K + norm_eps);
+        double gr = 0.0;
+        for (int j = 0; j < M; ++j) {
+            double dot = 0.0;
+            for (int64_t i = 0; i < K; ++i)
+                dot += (double)W[(int64_t)j * K + i] * hco_bf16_to_double(x[i]);
+            gr += gmixes[t * M + j] * dot;
+            gdot[t * M + j] = r * gmixes[t * M + j];
+        }
+        const double gss = gr * (-(r * r * r) / (2.0 * (double)K));
+        for (int64_t i = 0; i < K; ++i) {
+            double a = 0.0;
+            for (int j = 0; j < M; ++j)
+                a += gdot[t * M + j] * (double)W[(int64_t)j * K + i];
+            gR[t * K + i] = a + 2.0 * hco_bf16_to_double(x[i]) * gss;
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t ji = 0; ji < (int64_t)M * K; ++ji) {
+        const int j = (int)(ji / K);
+        const int64_t i = ji - (int64_t)j * K;
+        double a = 0.0;
+        for (int64_t t = 0; t < n; ++t)
+            a += gdot[t * M + j] * hco_bf16_to_double(R[t * K + i]);
+        gW[ji] = a;
+    }
+    free(gdot);
 }
 
 /* Number of OpenMP threads a parallel region would use (for reporting). */
