@@ -159,6 +159,9 @@ def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, step
                     timed[name] = sum(sel) / len(sel) / 1e3
     fb, pb = algorithmic_bytes(n, dd, hc)
     alg = {"k_spec": fb, "k_coop": fb, "k_post": pb, "k_gpost": pb}
+    if hc == 4:
+        bp, _, bk_pre, bk_mix = backward_bytes(n, dd, min(32, max(1, (n + 255) // 256)))
+        alg.update(k_post_bwd=bp, k_pre_bwd=bk_pre, k_mix_bwd=bk_mix)
     title = "# Kernel durations, n=%d tokens, d=%d" % (n, dd) + (", hc=%d" % hc if hc != 4 else "")
     lines = [title, "", "Command:", "", "    " + command, "",
              "| kernel | calls | average us | min us | max us | algorithmic GB/s | of 8 TB/s | timed-region average us | of 8 TB/s |",
@@ -211,6 +214,124 @@ def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, step
     print("\n".join(lines))
 
 
+DTYPE = ("bf16 storage; mix products fp32-exact (bf16 MFMA on an exact 3-piece split of the fp32 weights, "
+         "fp32 sums); split + Sinkhorn fp32; h and R' summed in fp64, rounded once")
+DTYPE_BWD = ("bf16 storage; per-token sums over d in fp64; split + Sinkhorn backward fp32; dL/dR summed in fp32, "
+             "rounded once; dL/dW fp32 partial sums added in fp64")
+
+
+def backward_bytes(n: int, d: int, ntg: int):
+    """Minimum HBM bytes per launch of the backward's entry points (every
+    input read once, every output written once).  hc_post_backward: x, R,
+    dL/dR', post, comb in; dL/dx, dL/dpost, dL/dcomb out.
+    hc_mix_pre_backward: R, dL/dh, dL/dR', mixes, dL/dpost, dL/dcomb, the
+    weights, scale and base in; dL/dR and the weight, scale and base
+    gradients out.  Its kernels: k_pre_bwd (R, dL/dh, mixes, dL/dpost,
+    dL/dcomb in; 192 B of coefficients and 112 B of scale/base terms per
+    token out) and k_mix_bwd (R, dL/dh, dL/dR', the coefficients and the
+    weights in; dL/dR and ntg partial weight gradients out)."""
+    hc, M = 4, 24
+    K = hc * d
+    post_b = n * (d * 2 + K * 2 + K * 2 + (hc + hc * hc) * 4 + d * 2 + (hc + hc * hc) * 4)
+    mix_pre = n * (K * 2 + d * 2 + K * 2 + M * 4 + (hc + hc * hc) * 4 + K * 2) + 2 * M * K * 4 + (3 + M) * 4 * 2
+    k_pre = n * (K * 2 + d * 2 + M * 4 + (hc + hc * hc) * 4 + 48 * 4 + 28 * 4)
+    k_mix = n * (K * 2 + d * 2 + K * 2 + 48 * 4 + K * 2) + M * K * 4 + ntg * M * K * 4
+    return post_b, mix_pre, k_pre, k_mix
+
+
+def bench_backward(args, hcl, hin, torch, np, w, t, dev):
+    """--backward: the step is one sublayer's backward, hc_post_backward then
+    hc_mix_pre_backward, from dL/dR' and dL/dh (seeded N(0,1), bf16) and the
+    forward's mixes.  Prints one JSON line like the default step."""
+    n, d = w.n, w.d
+    R, x, W, s, b = t["R"], t["x"], t["W"], t["scale"], t["base"]
+    gRo = hin.randn(tuple(R.shape), 1.0, dev, 0, 40, torch.bfloat16)
+    gh = hin.randn(tuple(x.shape), 1.0, dev, 0, 41, torch.bfloat16)
+    _, pre, post, comb, mixes = hcl.hc_fused_mix_pre(R, W, s, b, want_mixes=True)
+    ws = hcl.Workspace()
+
+    def post_b():
+        return hcl.hc_post_backward(x, R, post, comb, gRo)
+
+    def mix_b(gpost, gcomb):
+        return hcl.hc_mix_pre_backward(R, W, s, b, mixes, gh, gRo, gpost, gcomb, sinkhorn_iters=w.iters,
+                                       hc_eps=w.hc_eps, norm_eps=w.norm_eps, workspace=ws)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        _, gp, gc = post_b()
+        mix_b(gp, gc)
+    torch.cuda.synchronize()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+    e0, e1 = ev(), ev()
+    inner = [(ev(), ev(), ev(), ev()) for _ in range(args.steps)]
+    keep = []
+    e0.record(stream)
+    for pa, pz, ma, mz in inner:
+        pa.record(stream)
+        o = post_b()
+        pz.record(stream)
+        ma.record(stream)
+        keep.append(mix_b(o[1], o[2]))
+        mz.record(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del keep
+    ms = e0.elapsed_time(e1) / args.steps
+
+    def stats(pairs):
+        v = np.array([a.elapsed_time(z) for a, z in pairs]) * 1e3
+        return float(v.mean()), float(np.median(v)), float(v.min())
+    p = stats([(a, z) for a, z, _, _ in inner])
+    m = stats([(a, z) for _, _, a, z in inner])
+    ntg = min(32, max(1, (n + 255) // 256))
+    pb, mb, _, _ = backward_bytes(n, d, ntg)
+    p_gbs, m_gbs = pb / (p[0] * 1e-6) / 1e9, mb / (m[0] * 1e-6) / 1e9
+    dom = ("hc_mix_pre_backward", m, mb, m_gbs) if m[0] >= p[0] else ("hc_post_backward", p, pb, p_gbs)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        k = min(256, n)
+        Rb = hin.bits(R.reshape(n, 4, d)[:k])
+        args_o = (Rb, hin.bits(x.reshape(n, d)[:k]), W.cpu().numpy(), s.cpu().numpy(), b.cpu().numpy(),
+                  hin.bits(gRo.reshape(n, 4, d)[:k]), hin.bits(gh.reshape(n, d)[:k]))
+        passes = 0
+        c0 = time.perf_counter()
+        while passes < 4 and (passes == 0 or time.perf_counter() - c0 < args.cpu_seconds):
+            oracle.backward(*args_o, w.iters, w.hc_eps, w.norm_eps)
+            passes += 1
+        csec = time.perf_counter() - c0
+        cpu = {"value": passes * k / csec, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": "%d pass(es) of the oracle's whole backward over the first %d of %d tokens of the "
+                         "same inputs (its weight gradient sums those tokens only), %.1f s" % (passes, k, n, csec)}
+
+    def kd(v, bytes_, gbs):
+        return {"avg_us": round(v[0], 2), "median_us": round(v[1], 2), "min_us": round(v[2], 2),
+                "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                "tokens/s": round(n / (v[0] * 1e-6), 1), "bytes": bytes_}
+    line = {
+        "metric": "tokens/s + achieved HBM GB/s (% of peak), backward of the hc mixing (hc_post_backward + "
+                  "hc_mix_pre_backward), d=5120",
+        "value": round(n / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": DTYPE_BWD,
+        "data": "synthetic (seeded N(0,1) residual, sublayer output and incoming gradients, N(0,0.007) weights)",
+        "config": {"workload": "%s: B=%d T=%d hc=4 d=%d (%d tokens), sinkhorn_iters=%d, step = one sublayer's "
+                               "backward" % (w.name, w.B, w.T, d, n, w.iters),
+                   "tokens": n, "d": d, "hc": 4, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dom[0], "achieved": round(dom[3], 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dom[3] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": dom[2], "avg_launch_us": round(dom[1][0], 2)},
+        "kernels": {"hc_post_backward": kd(p, pb, p_gbs), "hc_mix_pre_backward": kd(m, mb, m_gbs)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def boundary_bytes(n: int, d: int):
     """Minimum HBM bytes of one hc_post_mix_pre call: x, R and this
     sublayer's post/comb read once, R' and h written once, the next
@@ -257,7 +378,7 @@ def bench_boundary(args, hcl, hin, torch, np, w, t, ws, outs, Rout, dev):
         "metric": "tokens/s + achieved HBM GB/s (% of peak), fused hc mix+pre and hc_post, d=5120",
         "value": round(n / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16",
+        "vs_baseline": None, "dtype": DTYPE,
         "data": "synthetic (seeded N(0,1) residual and sublayer output, N(0,0.007) weights)",
         "config": {"workload": "%s: B=%d T=%d hc=4 d=%d (%d tokens), sinkhorn_iters=%d, step = one "
                                "hc_post_mix_pre sublayer boundary" % (w.name, w.B, w.T, d, n, w.iters),
@@ -301,6 +422,8 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from a HIP graph (captured once before timing); "
                          "value is then the replay rate")
+    ap.add_argument("--backward", action="store_true",
+                    help="time one sublayer's backward instead: hc_post_backward then hc_mix_pre_backward")
     ap.add_argument("--boundary", action="store_true",
                     help="time the sublayer boundary instead: one hc_post_mix_pre call (hc_post of "
                          "this sublayer, then the next one's fused mix + Sinkhorn + hc_pre)")
@@ -353,6 +476,13 @@ def main():
     packed = hcl.hc_pack_weights(W) if args.packed else None
     if args.boundary:
         bench_boundary(args, hcl, hin, torch, np, w, t, ws, outs, Rout, dev)
+        return
+    if args.backward:
+        if w.hc != 4:
+            print("--backward runs four streams only", file=sys.stderr)
+            sys.exit(2)
+        del Rout, outs
+        bench_backward(args, hcl, hin, torch, np, w, t, dev)
         return
 
     def fused():
@@ -518,7 +648,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": DTYPE if w.hc == 4 else "bf16 storage; projection, h and R' summed in fp64; split + Sinkhorn fp32",
         "data": "synthetic (seeded N(0,1) residual and sublayer output, N(0,0.007) weights)",
         "config": {"workload": "%s: B=%d T=%d hc=%d d=%d (%d tokens), sinkhorn_iters=%d%s%s"
                                % (w.name, w.B, w.T, w.hc, d, n, w.iters,

@@ -25,6 +25,7 @@ import torch
 __all__ = [
     "HCError", "load", "lib_path", "hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post",
     "hc_fused_mix_pre", "hc_fused_mix_pre_noalloc", "hc_post_mix_pre", "hc_pack_weights", "hc_diag_scale", "hc_fused_workspace_bytes",
+    "hc_post_backward", "hc_mix_pre_backward", "hc_backward_workspace_bytes",
     "Workspace", "workspace_status", "check_workspace", "noalloc_status", "debug_force_timeout",
 ]
 
@@ -68,6 +69,8 @@ def load():
         "hc_fused_mix_pre_packed": [P, P, SZ, P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, F32, F32, P],
         "hc_diag_scale": [P, P, P, I64, I32, P],
         "hc_fused_mix_pre_noalloc": [P, P, P, P, P, P, P, P, P, I64, I32, I32, I32, F32, F32, P],
+        "hc_post_backward": [P, P, P, P, P, P, P, P, I64, I32, I32, P],
+        "hc_mix_pre_backward": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, F32, F32, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -83,6 +86,8 @@ def load():
     lib.hc_noalloc_status.restype = ctypes.c_int
     lib.hc_debug_force_timeout.argtypes = [ctypes.c_int]
     lib.hc_debug_force_timeout.restype = ctypes.c_int
+    lib.hc_backward_workspace_bytes.argtypes = [I64, I32, I32]
+    lib.hc_backward_workspace_bytes.restype = SZ
     lib.hc_scratch_bytes.argtypes = []
     lib.hc_scratch_bytes.restype = SZ
     lib.hc_status_str.argtypes = [ctypes.c_int]
@@ -470,3 +475,68 @@ def hc_diag_scale(h: torch.Tensor, D: torch.Tensor, out: torch.Tensor | None = N
     with torch.cuda.device(dev):
         _call("hc_diag_scale", _ptr(h), _ptr(D), _ptr(out), n, d, _stream(dev))
     return out
+
+
+# ------------------------------------------------------------- backward
+
+def hc_backward_workspace_bytes(n: int, hc: int, d: int) -> int:
+    """Workspace bytes hc_mix_pre_backward needs (host-only query)."""
+    return int(load().hc_backward_workspace_bytes(int(n), int(hc), int(d)))
+
+
+def hc_post_backward(x: torch.Tensor, R: torch.Tensor, post: torch.Tensor, comb: torch.Tensor,
+                     gRout: torch.Tensor):
+    """Gradient through hc_post from dL/dR' (bf16, R's shape): returns
+    (gx bf16 [..., d], gpost fp32 [..., 4], gcomb fp32 [..., 4, 4])."""
+    dev = R.device
+    _check(R, "R", torch.bfloat16)
+    _check(x, "x", torch.bfloat16, dev)
+    _check(gRout, "gRout", torch.bfloat16, dev)
+    _check(post, "post", torch.float32, dev)
+    _check(comb, "comb", torch.float32, dev)
+    hc = _streams(R)
+    lead, n, d = _lead(R, hc)
+    if tuple(x.shape) != lead + (d,) or tuple(gRout.shape) != tuple(R.shape) or \
+            tuple(post.shape) != lead + (hc,) or tuple(comb.shape) != lead + (hc, hc):
+        raise ValueError("shape mismatch among x, R, post, comb, gRout")
+    gx = torch.empty_like(x)
+    gpost = torch.empty_like(post)
+    gcomb = torch.empty_like(comb)
+    with torch.cuda.device(dev):
+        _call("hc_post_backward", _ptr(x), _ptr(R), _ptr(post), _ptr(comb), _ptr(gRout), _ptr(gx), _ptr(gpost),
+              _ptr(gcomb), n, hc, d, _stream(dev))
+    return gx, gpost, gcomb
+
+
+def hc_mix_pre_backward(R: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tensor, hc_base: torch.Tensor,
+                        mixes: torch.Tensor, gh: torch.Tensor, gRout: torch.Tensor, gpost: torch.Tensor,
+                        gcomb: torch.Tensor, sinkhorn_iters: int = 20, hc_eps: float = 1e-6,
+                        norm_eps: float = 1e-20, want_gmixes: bool = False, workspace: Workspace | None = None):
+    """The rest of the sublayer's gradient: returns (gR bf16 [..., 4, d],
+    g_hc_fn fp32 [24, 4d], g_hc_scale fp32 [3], g_hc_base fp32 [24],
+    gmixes fp32 [..., 24] or None)."""
+    dev = R.device
+    _check(R, "R", torch.bfloat16)
+    for t, nm in ((hc_fn, "hc_fn"), (hc_scale, "hc_scale"), (hc_base, "hc_base"), (mixes, "mixes"),
+                  (gpost, "gpost"), (gcomb, "gcomb")):
+        _check(t, nm, torch.float32, dev)
+    _check(gh, "gh", torch.bfloat16, dev)
+    _check(gRout, "gRout", torch.bfloat16, dev)
+    hc = _streams(R)
+    M = (2 + hc) * hc
+    lead, n, d = _lead(R, hc)
+    if tuple(hc_fn.shape) != (M, hc * d) or tuple(mixes.shape) != lead + (M,) or tuple(gh.shape) != lead + (d,) \
+            or tuple(gRout.shape) != tuple(R.shape) or tuple(gpost.shape) != lead + (hc,) \
+            or tuple(gcomb.shape) != lead + (hc, hc):
+        raise ValueError("shape mismatch among the backward's inputs")
+    gR = torch.empty_like(R)
+    gW = torch.empty_like(hc_fn)
+    gs = torch.empty_like(hc_scale)
+    gb = torch.empty_like(hc_base)
+    gm = torch.empty_like(mixes) if want_gmixes else None
+    wp, wb = _workspace(workspace, hc_backward_workspace_bytes(n, hc, d), dev)
+    with torch.cuda.device(dev):
+        _call("hc_mix_pre_backward", _ptr(R), _ptr(hc_fn), _ptr(hc_scale), _ptr(hc_base), _ptr(mixes), _ptr(gh),
+              _ptr(gRout), _ptr(gpost), _ptr(gcomb), _ptr(gR), _ptr(gW), _ptr(gs), _ptr(gb), _ptr(gm), wp, wb, n,
+              hc, d, int(sinkhorn_iters), float(hc_eps), float(norm_eps), _stream(dev))
+    return gR, gW, gs, gb, gm

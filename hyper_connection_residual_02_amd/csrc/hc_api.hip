@@ -409,6 +409,80 @@ int hc_debug_force_timeout(int calls) {
     return HC_OK;
 }
 
+int hc_post_backward(const void* x, const void* R, const float* post, const float* comb, const void* gRout,
+                     void* gx, float* gpost, float* gcomb, int64_t n, int32_t hc_, int32_t d, void* stream) {
+    int st = check_nd(n, hc_, d);
+    if (st) return st;
+    if (hc_ != 4) return HC_ERR_UNSUPPORTED;
+    if (n == 0) return HC_OK;
+    if (!x || !R || !post || !comb || !gRout || !gx || !gpost || !gcomb) return HC_ERR_NULL;
+    if (!al16(x) || !al16(R) || !al16(post) || !al16(comb) || !al16(gRout) || !al16(gx) || !al16(gpost) ||
+        !al16(gcomb))
+        return HC_ERR_ALIGN;
+    const uint64_t nd = (uint64_t)n * d;
+    const Span ins[] = {span(x, nd * 2), span(R, nd * 8), span(post, (uint64_t)n * 16), span(comb, (uint64_t)n * 64),
+                        span(gRout, nd * 8)};
+    const Span outs[] = {span(gx, nd * 2), span(gpost, (uint64_t)n * 16), span(gcomb, (uint64_t)n * 64)};
+    for (int i = 0; i < 3; ++i) {
+        for (const Span& in : ins)
+            if (overlap(outs[i], in)) return HC_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return HC_ERR_ALIAS;
+    }
+    return hc::launch_post_bwd(x, R, post, comb, gRout, gx, gpost, gcomb, n, d, (hipStream_t)stream) ? HC_ERR_LAUNCH
+                                                                                                    : HC_OK;
+}
+
+size_t hc_backward_workspace_bytes(int64_t n, int32_t hc_, int32_t d) {
+    if (check_nd(n, hc_, d) != HC_OK || n == 0 || !hc::bwd_supported(hc_, d, 1)) return 0;
+    return hc::bwd_ws_bytes(n, d);
+}
+
+int hc_mix_pre_backward(const void* R, const float* hc_fn, const float* hc_scale, const float* hc_base,
+                        const float* mixes, const void* gh, const void* gRout, const float* gpost,
+                        const float* gcomb, void* gR, float* g_hc_fn, float* g_hc_scale, float* g_hc_base,
+                        float* gmixes, void* workspace, size_t workspace_bytes, int64_t n, int32_t hc_, int32_t d,
+                        int32_t sinkhorn_iters, float hc_eps, float norm_eps, void* stream) {
+    int st = check_nd(n, hc_, d);
+    if (st) return st;
+    if (!hc::bwd_supported(hc_, d, sinkhorn_iters)) return HC_ERR_UNSUPPORTED;
+    if (!finite_nonneg(hc_eps) || !finite_nonneg(norm_eps)) return HC_ERR_VALUE;
+    if (n == 0) return HC_OK;
+    if (!R || !hc_fn || !hc_scale || !hc_base || !mixes || !gh || !gRout || !gpost || !gcomb || !gR || !g_hc_fn ||
+        !g_hc_scale || !g_hc_base)
+        return HC_ERR_NULL;
+    if (!workspace) return HC_ERR_WORKSPACE;
+    const size_t wsb = hc::bwd_ws_bytes(n, d);
+    if (workspace_bytes < wsb) return HC_ERR_WORKSPACE;
+    if (!al16(R) || !al16(hc_fn) || !al4(hc_scale) || !al4(hc_base) || !al16(mixes) || !al16(gh) || !al16(gRout) ||
+        !al16(gpost) || !al16(gcomb) || !al16(gR) || !al16(g_hc_fn) || !al4(g_hc_scale) || !al4(g_hc_base) ||
+        (gmixes && !al16(gmixes)) || ((uintptr_t)workspace & 255u))
+        return HC_ERR_ALIGN;
+    const uint64_t nd = (uint64_t)n * d, K = (uint64_t)4 * d;
+    const Span ins[] = {span(R, nd * 8),           span(hc_fn, 24 * K * 4),        span(hc_scale, 12),
+                        span(hc_base, 96),         span(mixes, (uint64_t)n * 96), span(gh, nd * 2),
+                        span(gRout, nd * 8),       span(gpost, (uint64_t)n * 16), span(gcomb, (uint64_t)n * 64),
+                        span(workspace, wsb)};
+    Span outs[5];
+    int no = 0;
+    outs[no++] = span(gR, nd * 8);
+    outs[no++] = span(g_hc_fn, 24 * K * 4);
+    outs[no++] = span(g_hc_scale, 12);
+    outs[no++] = span(g_hc_base, 96);
+    if (gmixes) outs[no++] = span(gmixes, (uint64_t)n * 96);
+    for (int i = 0; i < no; ++i) {
+        for (const Span& in : ins)
+            if (overlap(outs[i], in)) return HC_ERR_ALIAS;
+        for (int j = i + 1; j < no; ++j)
+            if (overlap(outs[i], outs[j])) return HC_ERR_ALIAS;
+    }
+    return hc::launch_mix_pre_bwd(R, hc_fn, hc_scale, hc_base, mixes, gh, gRout, gpost, gcomb, gR, g_hc_fn,
+                                  g_hc_scale, g_hc_base, gmixes, workspace, n, d, sinkhorn_iters, hc_eps, norm_eps,
+                                  (hipStream_t)stream)
+               ? HC_ERR_LAUNCH
+               : HC_OK;
+}
+
 int hc_post_mix_pre(const void* x, const void* R, const float* post, const float* comb, void* R_out,
                     const float* hc_fn, const float* hc_scale, const float* hc_base, void* h, float* pre_next,
                     float* post_next, float* comb_next, float* mixes_next, void* workspace, size_t workspace_bytes,

@@ -85,6 +85,16 @@ void set_force_timeout(int calls);
 // Device address of this device's static scratch (hc_api.hip), or null.
 void* scratch_ptr();
 
+// Backward pass, four streams (hc_backward.hip).
+bool bwd_supported(int hc, int d, int iters);
+size_t bwd_ws_bytes(int64_t n, int d);
+int launch_post_bwd(const void* x, const void* R, const float* post, const float* comb, const void* gRo, void* gx,
+                    float* gpost, float* gcomb, int64_t n, int d, hipStream_t s);
+int launch_mix_pre_bwd(const void* R, const float* W, const float* scale, const float* base, const float* mixes,
+                       const void* gh, const void* gRo, const float* gpost, const float* gcomb, void* gR, float* gW,
+                       float* gscale, float* gbase, float* gmixes, void* ws, int64_t n, int d, int iters, float eps,
+                       float norm_eps, hipStream_t s);
+
 // Bytes of packed weights for width d (0: d is not served by the
 // wave-specialised kernels), and the packing launch.
 size_t packed_weights_bytes(int d);

@@ -274,6 +274,66 @@ int hc_fused_mix_pre_packed(const void *R, const void *packed,
                             float hc_eps, float norm_eps, void *stream);
 
 /*
+ * Backward pass (training).  The pages give the forward; these return the
+ * gradient of a scalar loss L through it, by the chain rule over the
+ * forward's steps in reverse order, on the real-valued forward (the bf16
+ * roundings of h and R' are storage, not steps).  Four streams only
+ * (hc != 4: HC_ERR_UNSUPPORTED).  In a model's backward, a sublayer runs
+ * hc_post_backward first (its dL/dx feeds the sublayer's own backward,
+ * which yields dL/dh), then hc_mix_pre_backward.
+ *
+ * hc_post_backward -- the gradient through Block.hc_post ("Mix projection"
+ * page), from gRout = dL/dR' (bf16 [n][4][d]):
+ *   gx[t][c]       = bf16( sum_k post_k gRout[t][k][c] )  (correctly rounded)
+ *   gpost[t][k]    = sum_c x[t][c] gRout[t][k][c]          (fp32 [n][4])
+ *   gcomb[t][j][k] = sum_c R[t][j][c] gRout[t][k][c]       (fp32 [n][4][4])
+ * The sums over c are accumulated in double and rounded once to float.
+ * d % 8 == 0.  No output may overlap an input or another output.
+ */
+int hc_post_backward(const void *x, const void *R, const float *post,
+                     const float *comb, const void *gRout, void *gx,
+                     float *gpost, float *gcomb, int64_t n, int32_t hc,
+                     int32_t d, void *stream);
+
+/*
+ * hc_mix_pre_backward -- the rest of the sublayer's gradient: through
+ * Block.hc_pre, the split + epsilon-Sinkhorn ("Reading weights" listing) and
+ * the mix formula, plus hc_post's share of dL/dR.  Inputs: the forward's
+ * R, hc_fn, hc_scale, hc_base and its mixes (fp32 [n][24], from hc_mixes or
+ * hc_fused_mix_pre); gh = dL/dh (bf16 [n][d]); gRout = dL/dR' and gpost,
+ * gcomb from hc_post_backward.  Outputs:
+ *   gR       bf16 [n][4][d]: dL/dR = sum_k comb[j][k] gRout_k + pre_j gh
+ *            + sum_m gdot_m hc_fn[m][j*d + c] + 2 R[j][c] gss, in float,
+ *            rounded once; pre and comb are recomputed from the mixes with
+ *            the forward's arithmetic (bitwise the forward's), gdot = r dL/dm
+ *            and gss = -(r^2 / 2K) sum_m dL/dm_m m_m with r the forward's
+ *            RMS normaliser (K = 4d);
+ *   g_hc_fn  fp32 [24][4d]: dL/dhc_fn = sum_t gdot[t][m] R[t][i];
+ *   g_hc_scale fp32 [3], g_hc_base fp32 [24]: sums over tokens;
+ *   gmixes   fp32 [n][24], dL/dmixes (may be NULL).
+ * The split + Sinkhorn backward replays the forward's steps in float,
+ * keeping every step, and runs them backwards; sums over tokens are added
+ * in one fixed order, so results are deterministic.  Requires d % 128 == 0
+ * and 1 <= sinkhorn_iters <= 64.  Workspace: hc_backward_workspace_bytes
+ * (n, hc, d) bytes, 256-byte aligned (per-token coefficients and partial
+ * sums of dL/dhc_fn; about 190 B per token plus up to 32 x 24 x 4d floats).
+ * With n == 0 nothing is launched and nothing is written.
+ */
+int hc_mix_pre_backward(const void *R, const float *hc_fn,
+                        const float *hc_scale, const float *hc_base,
+                        const float *mixes, const void *gh, const void *gRout,
+                        const float *gpost, const float *gcomb, void *gR,
+                        float *g_hc_fn, float *g_hc_scale, float *g_hc_base,
+                        float *gmixes, void *workspace, size_t workspace_bytes,
+                        int64_t n, int32_t hc, int32_t d,
+                        int32_t sinkhorn_iters, float hc_eps, float norm_eps,
+                        void *stream);
+
+/* Workspace bytes of hc_mix_pre_backward (0 for n == 0 or an unsupported
+ * shape).  Host-only query. */
+size_t hc_backward_workspace_bytes(int64_t n, int32_t hc, int32_t d);
+
+/*
  * hc_workspace_status -- whether a call on this workspace stopped early.
  * A call that gives up a bounded wait (see hc_mixes) sets a word in the
  * workspace header that stays set until this query clears it.  Call it

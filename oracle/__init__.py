@@ -78,6 +78,8 @@ def _load():
     lib.hco_split_sinkhorn_backward.restype = ctypes.c_int
     lib.hco_mixes_backward.argtypes = [P, P, P, I64, I32, I32, F64, P, P]
     lib.hco_mixes_backward.restype = None
+    lib.hco_round_bf16_array.argtypes = [P, I64, P]
+    lib.hco_round_bf16_array.restype = None
     lib.hco_round_bf16.argtypes = [F64]
     lib.hco_round_bf16.restype = ctypes.c_uint16
     lib.hco_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -107,6 +109,14 @@ def bf16_to_f64(bits) -> np.ndarray:
 def round_bf16(v: float) -> int:
     """Round one double to a bf16 bit pattern (nearest, ties to even)."""
     return int(_load().hco_round_bf16(float(v)))
+
+
+def round_bf16_array(v) -> np.ndarray:
+    """Round every double of ``v`` to a bf16 bit pattern (uint16, same shape)."""
+    a, pa = _c(v, np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().hco_round_bf16_array(pa, a.size, out.ctypes.data)
+    return out
 
 
 def mixes(R_bits, W, norm_eps: float = 1e-20) -> np.ndarray:

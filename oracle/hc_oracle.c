@@ -86,6 +86,14 @@ uint16_t hco_round_bf16(double v)
     return sign | (uint16_t)(u >> 16);
 }
 
+/* hco_round_bf16 over an array. */
+void hco_round_bf16_array(const double *v, int64_t n, uint16_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = hco_round_bf16(v[i]);
+}
+
 /* Logistic function, evaluated without overflow for either sign. */
 static double sigmoid(double z)
 {

@@ -244,6 +244,34 @@ def test_status_query_and_diagnostics_checks(lib):
     assert lib.hc_debug_force_timeout(0) == OK
 
 
+def test_backward_checks(lib):
+    def post_b(n=4, hc=4, d=256, gx=E):
+        return lib.hc_post_backward(P(A), P(B), P(C), P(D_), P(F_), P(gx), P(0x7E000000), P(0x7F000000), n, hc, d,
+                                    None)
+    assert post_b(n=0) == OK
+    assert post_b(hc=3) == UNSUP
+    assert post_b(d=60) == SHAPE
+    assert post_b(gx=0) == NULL
+    assert post_b(gx=E + 2) == ALIGN
+    assert post_b(gx=B + 32) == ALIAS
+
+    def mix_b(n=4, hc=4, d=256, iters=20, ws=0x78000000, wsb=1 << 24, gR=0x7A000000):
+        return lib.hc_mix_pre_backward(P(A), P(B), P(C), P(C + 64), P(D_), P(E), P(F_), P(0x7E000000),
+                                       P(0x7F000000), P(gR), P(0x7B000000), P(0x7C800000), P(0x7C900000), None,
+                                       P(ws), wsb, n, hc, d, iters, 1e-6, 1e-20, None)
+    assert mix_b(n=0) == OK
+    assert mix_b(hc=2) == UNSUP
+    assert mix_b(d=64) == UNSUP                  # d % 128 != 0
+    assert mix_b(iters=65) == UNSUP and mix_b(iters=0) == UNSUP
+    assert mix_b(ws=0) == WS
+    assert mix_b(wsb=100) == WS
+    assert mix_b(gR=0) == NULL
+    assert mix_b(ws=0x78000010) == ALIGN
+    assert mix_b(gR=B) == ALIAS
+    assert lib.hc_backward_workspace_bytes(4, 4, 256) > 0
+    assert lib.hc_backward_workspace_bytes(4, 3, 256) == 0
+
+
 def test_diag_checks(lib):
     f = lambda h=A, Dp=B, x=C, n=4, d=64: lib.hc_diag_scale(P(h), P(Dp), P(x), n, d, None)
     assert f(n=0) == OK
