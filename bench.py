@@ -332,6 +332,85 @@ def bench_backward(args, hcl, hin, torch, np, w, t, dev):
     print(json.dumps(line), flush=True)
 
 
+def bench_chain(args, hcl, hin, torch, np, w, dev):
+    """--chain: the chained stack's 80 sublayers (fused call, stand-in
+    sublayer, hc_post in place) on the chosen workload's tokens, each
+    sublayer with its own weights, scale, base and diagonal; timed eagerly and
+    replayed from one HIP graph that captures the whole chain.  The step is
+    one sublayer (the chain's time over 80)."""
+    wc = hin.WORKLOADS["chained"]
+    L = wc.layers
+    n, d = w.n, w.d
+    R0 = hin.randn((w.B, w.T, 4, d), 1.0, dev, 0, 1, torch.bfloat16)
+    params = [hin.make_params(wc, dev, layer=l) for l in range(L)]
+    diags = [hin.make_diag(wc, l, dev) for l in range(L)]
+    packed = [hcl.hc_pack_weights(p[0]) for p in params] if args.packed else [None] * L
+    R = R0.clone()
+    ws = hcl.Workspace()
+    outs = dict(h=torch.empty(w.B, w.T, d, dtype=torch.bfloat16, device=dev),
+                post=torch.empty(w.B, w.T, 4, device=dev), comb=torch.empty(w.B, w.T, 4, 4, device=dev))
+    x = torch.empty_like(outs["h"])
+
+    def chain():
+        R.copy_(R0)
+        for l in range(L):
+            W, sc, bs = params[l]
+            hcl.hc_fused_mix_pre(R, W, sc, bs, sinkhorn_iters=wc.iters, hc_eps=wc.hc_eps, norm_eps=wc.norm_eps,
+                                 want_pre=False, workspace=ws, out=outs, packed=packed[l])
+            hcl.hc_diag_scale(outs["h"], diags[l], out=x)
+            hcl.hc_post(x, R, outs["post"], outs["comb"], out=R)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        chain()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        chain()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / args.steps
+    eager_bits = hin.bits(R).copy()
+    side = torch.cuda.Stream(dev)
+    with torch.cuda.stream(side):
+        chain()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        chain()
+    for _ in range(args.warmup):
+        gr.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(args.steps):
+        gr.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / args.steps
+    same = bool(np.array_equal(hin.bits(R), eager_bits))
+    del gr
+    per_us = graph_ms * 1e3 / L
+    line = {
+        "metric": "tokens/s + achieved HBM GB/s (% of peak), fused hc mix+pre and hc_post, d=5120",
+        "value": round(n / (per_us * 1e-6), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(per_us * 1e-3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE,
+        "data": "synthetic (seeded N(0,1) residual; the chained stack's per-layer weights, scales, bases and "
+                "diagonals)",
+        "config": {"workload": "%s tokens through the chained stack's %d sublayers (fused call, stand-in "
+                               "diagonal sublayer, hc_post in place)%s; the chain replayed from one HIP graph; "
+                               "step = one sublayer" % (n, L, ", weights packed once" if args.packed else ""),
+                   "tokens": n, "d": d, "hc": 4, "parallelism": "single GPU"},
+        "chain": {"sublayers": L, "graph_chain_ms": round(graph_ms, 4), "eager_chain_ms": round(eager_ms, 4),
+                  "graph_us_per_sublayer": round(per_us, 2), "eager_us_per_sublayer": round(eager_ms * 1e3 / L, 2),
+                  "replay_bitwise_eager": same},
+        "roofline": None, "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def boundary_bytes(n: int, d: int):
     """Minimum HBM bytes of one hc_post_mix_pre call: x, R and this
     sublayer's post/comb read once, R' and h written once, the next
@@ -422,6 +501,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from a HIP graph (captured once before timing); "
                          "value is then the replay rate")
+    ap.add_argument("--chain", action="store_true",
+                    help="run the chained stack's 80 sublayers on the workload's tokens, eagerly and replayed "
+                         "from one HIP graph; the step is one sublayer")
     ap.add_argument("--backward", action="store_true",
                     help="time one sublayer's backward instead: hc_post_backward then hc_mix_pre_backward")
     ap.add_argument("--boundary", action="store_true",
@@ -465,6 +547,12 @@ def main():
         import dataclasses
         w = dataclasses.replace(w, hc=args.hc)
     n, d = w.n, w.d
+    if args.chain:
+        if w.hc != 4:
+            print("--chain runs four streams only", file=sys.stderr)
+            sys.exit(2)
+        bench_chain(args, hcl, hin, torch, np, w, dev)
+        return
     t = hin.make_inputs(w, dev)
     R, x, W, s, b = t["R"], t["x"], t["W"], t["scale"], t["base"]
     ws = hcl.Workspace()

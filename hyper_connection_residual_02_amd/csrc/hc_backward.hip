@@ -24,7 +24,7 @@
 //    sum_t dL/ddot_tm x_ti.  A workgroup owns 128 features of every stream
 //    (wave j: stream j) and walks a contiguous range of tokens; each thread
 //    keeps its 2 x 24 weights and 2 x 24 partial sums in registers.
-//  * k_gw_reduce, k_sb_reduce: the partial sums over token groups, and the
+//  * k_gw_reduce, k_sb_partial + k_sb_final: the partial sums over token groups, and the
 //    per-token scale and base contributions over tokens, each added in one
 //    fixed order (double), so the results are deterministic.
 #include "hc_device.hpp"
@@ -347,24 +347,43 @@ __global__ __launch_bounds__(256) void k_gw_reduce(const float* __restrict__ par
     }
 }
 
-// Column c of the per-token [n][kSB] contributions summed over tokens:
-// thread i adds tokens i, i + 256, ... in order, then a fixed tree.
-__global__ __launch_bounds__(256) void k_sb_reduce(const float* __restrict__ sb, float* __restrict__ gscale,
-                                                   float* __restrict__ gbase, int64_t n) {
-    __shared__ double red[256];
-    const int c = blockIdx.x;          // 0..2 scale, 3..26 base
+// The per-token [n][kSB] scale and base contributions summed over tokens,
+// in two fixed-order stages: block b stages its contiguous range of up to
+// 256 tokens in LDS (every load in flight at once) and lane c adds column c
+// over them in token order; then one wave adds the blocks' sums in block
+// order.
+constexpr int kSbBlocks = 256;
+__global__ __launch_bounds__(256) void k_sb_partial(const float* __restrict__ sb, double* __restrict__ part,
+                                                    int64_t n) {
+    __shared__ __attribute__((aligned(16))) float rows[256][kSB];
+    const int64_t per = (n + kSbBlocks - 1) / kSbBlocks;
+    const int64_t t0 = per * blockIdx.x, t1 = t0 + per < n ? t0 + per : n;
     double s = 0.0;
-    for (int64_t t = threadIdx.x; t < n; t += 256) s += (double)sb[t * kSB + c];
-    red[threadIdx.x] = s;
-    __syncthreads();
-    for (int o = 128; o >= 1; o >>= 1) {
-        if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    for (int64_t c0 = t0; c0 < t1; c0 += 256) {
+        const int cnt = (int)(t1 - c0 < 256 ? t1 - c0 : 256);
+        if ((int)threadIdx.x < cnt) {
+            const f32x4* src = reinterpret_cast<const f32x4*>(sb + (c0 + threadIdx.x) * kSB);
+#pragma unroll
+            for (int q = 0; q < kSB / 4; ++q) *reinterpret_cast<f32x4*>(&rows[threadIdx.x][4 * q]) = src[q];
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < kSB)
+            for (int i = 0; i < cnt; ++i) s += (double)rows[i][threadIdx.x];
         __syncthreads();
     }
-    if (threadIdx.x == 0) {
-        if (c < 3) gscale[c] = (float)red[0];
-        else gbase[c - 3] = (float)red[0];
-    }
+    if ((int)threadIdx.x < kSB) part[blockIdx.x * kSB + threadIdx.x] = s;
+}
+__global__ __launch_bounds__(256) void k_sb_final(const double* __restrict__ part, float* __restrict__ gscale,
+                                                  float* __restrict__ gbase) {
+    __shared__ double sums[kSbBlocks][kSB];
+    for (int i = threadIdx.x; i < kSbBlocks * kSB; i += 256) (&sums[0][0])[i] = part[i];
+    __syncthreads();
+    const int c = threadIdx.x;
+    if (c >= 3 + kMix) return;
+    double s = 0.0;
+    for (int b = 0; b < kSbBlocks; ++b) s += sums[b][c];
+    if (c < 3) gscale[c] = (float)s;
+    else gbase[c - 3] = (float)s;
 }
 
 int token_groups(int64_t n) {
@@ -384,7 +403,7 @@ bool bwd_supported(int hc_, int d, int iters) {
 size_t bwd_ws_bytes(int64_t n, int d) {
     const int64_t K = (int64_t)kHC * d;
     return al256((size_t)n * kCoef * 4) + al256((size_t)n * kSB * 4) +
-           al256((size_t)token_groups(n) * kMix * K * 4);
+           al256((size_t)token_groups(n) * kMix * K * 4) + al256((size_t)kSbBlocks * kSB * 8);
 }
 
 int launch_post_bwd(const void* x, const void* R, const float* post, const float* comb, const void* gRo, void* gx,
@@ -404,6 +423,8 @@ int launch_mix_pre_bwd(const void* R, const float* W, const float* scale, const 
     float* coef = reinterpret_cast<float*>(w);
     float* sb = reinterpret_cast<float*>(w + al256((size_t)n * kCoef * 4));
     float* part = reinterpret_cast<float*>(w + al256((size_t)n * kCoef * 4) + al256((size_t)n * kSB * 4));
+    double* sbp = reinterpret_cast<double*>(w + al256((size_t)n * kCoef * 4) + al256((size_t)n * kSB * 4) +
+                                            al256((size_t)token_groups(n) * kMix * K * 4));
     PreBwdArgs pa{(const u32x4*)R, (const u32x4*)gh, mixes, scale, base, gpost, gcomb, coef, sb, gmixes, n, d,
                   iters, eps, norm_eps};
     k_pre_bwd<<<(unsigned)((n + 3) / 4), 256, 0, s>>>(pa);
@@ -418,7 +439,9 @@ int launch_mix_pre_bwd(const void* R, const float* W, const float* scale, const 
     if (blocks > (int64_t)num_cus() * 8) blocks = (int64_t)num_cus() * 8;
     k_gw_reduce<<<(unsigned)blocks, 256, 0, s>>>(part, gW, total, ntg);
     if (hipGetLastError() != hipSuccess) return -1;
-    k_sb_reduce<<<3 + kMix, 256, 0, s>>>(sb, gscale, gbase, n);
+    k_sb_partial<<<kSbBlocks, 256, 0, s>>>(sb, sbp, n);
+    if (hipGetLastError() != hipSuccess) return -1;
+    k_sb_final<<<1, 256, 0, s>>>(sbp, gscale, gbase);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
