@@ -63,10 +63,22 @@ def measured_traffic(kernel: str, n: int, d: int):
 
 
 # the projection kernel of d = 5120 (wave-specialised, calls of more than
-# 2,048 tokens), that of other widths, and hc_post's kernel; shorter calls
-# run the two-pass pair k_part + k_fin (summarised together)
-KERNELS = {"k_spec": "hc_fused_mix_pre", "k_coop": "hc_fused_mix_pre", "k_post": "hc_post"}
+# 2,048 tokens), its sublayer-boundary variant (hc_post_mix_pre in one pass,
+# k_spec<KS, true, true>), that of other widths, and hc_post's kernel;
+# shorter calls run the two-pass pair k_part + k_fin (summarised together)
+KERNELS = {"k_spec": "hc_fused_mix_pre", "k_spec_post": "hc_post_mix_pre", "k_coop": "hc_fused_mix_pre",
+           "k_post": "hc_post"}
 COPY_CALIB_BYTES = 1 << 30
+
+
+def kernel_key(name: str) -> str:
+    """Short key of an hc kernel from its demangled name: the function name,
+    and k_spec_post for the sublayer-boundary variant of k_spec."""
+    short = name.split("hc::")[1].replace("(anonymous namespace)::", "").split("(")[0] if "hc::" in name else name
+    key = short.split("<")[0].split("::")[-1]
+    if key == "k_spec" and short.replace(" ", "").endswith("true,true>"):
+        key = "k_spec_post"
+    return key
 
 
 def _counter_rows(d: str, counter: str):
@@ -81,7 +93,7 @@ def _counter_rows(d: str, counter: str):
     return rows
 
 
-def summarize_counters(d: str, n: int, dd: int, command: str):
+def summarize_counters(d: str, n: int, dd: int, command: str, tag: str = ""):
     """Turn the FETCH_SIZE / WRITE_SIZE passes (rocprofv3 --pmc ... --output-format
     csv, one pass per counter, each run with --copy-calib) under ``d`` into HBM
     bytes per launch of each hc kernel.  Each counter is scaled by what it
@@ -97,7 +109,7 @@ def summarize_counters(d: str, n: int, dd: int, command: str):
     kib = COPY_CALIB_BYTES / 1024.0
     f_scale, w_scale = kib / f_copy, kib / w_copy
     fb, pb = algorithmic_bytes(n, dd)
-    alg = {"k_spec": fb, "k_coop": fb, "k_post": pb}
+    alg = {"k_spec": fb, "k_spec_post": boundary_bytes(n, dd), "k_coop": fb, "k_post": pb}
     src = kernel_source_hash()
     lines = ["# HBM traffic per launch, n=%d tokens, d=%d" % (n, dd), "",
              "Command (one pass per counter):", "", "    " + command, "",
@@ -107,8 +119,8 @@ def summarize_counters(d: str, n: int, dd: int, command: str):
              "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes | algorithmic bytes | ratio |",
              "|---|---|---|---|---|---|---|"]
     for k, api in KERNELS.items():
-        fv = [float(r["Counter_Value"]) for r in fetch if ("::%s<" % k) in r["Kernel_Name"]]
-        wv = [float(r["Counter_Value"]) for r in write if ("::%s<" % k) in r["Kernel_Name"]]
+        fv = [float(r["Counter_Value"]) for r in fetch if "hc::" in r["Kernel_Name"] and kernel_key(r["Kernel_Name"]) == k]
+        wv = [float(r["Counter_Value"]) for r in write if "hc::" in r["Kernel_Name"] and kernel_key(r["Kernel_Name"]) == k]
         if not fv or not wv:
             continue
         fm, wm = sum(fv) / len(fv), sum(wv) / len(wv)
@@ -123,7 +135,7 @@ def summarize_counters(d: str, n: int, dd: int, command: str):
                      % (k, api, len(fv), fm, wm, total, alg[k], total / alg[k]))
     lines.append("")
     lines.append("Kernel sources hash (sha256 of csrc/, first 16 hex): %s" % src)
-    with open(os.path.join(PROFILE_DIR, "hbm_traffic_n%d_d%d.md" % (n, dd)), "w") as fh:
+    with open(os.path.join(PROFILE_DIR, "hbm_traffic_%sn%d_d%d.md" % (tag + "_" if tag else "", n, dd)), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -160,6 +172,8 @@ def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, step
     fb, pb = algorithmic_bytes(n, dd, hc)
     alg = {"k_spec": fb, "k_coop": fb, "k_post": pb, "k_gpost": pb}
     if hc == 4:
+        alg["k_spec_post"] = boundary_bytes(n, dd)
+    if hc == 4:
         bp, _, bk_pre, bk_mix = backward_bytes(n, dd, min(32, max(1, (n + 255) // 256)))
         alg.update(k_post_bwd=bp, k_pre_bwd=bk_pre, k_mix_bwd=bk_mix)
     title = "# Kernel durations, n=%d tokens, d=%d" % (n, dd) + (", hc=%d" % hc if hc != 4 else "")
@@ -172,7 +186,7 @@ def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, step
             continue
         short = name.split("hc::")[1].replace("(anonymous namespace)::", "").split("(")[0]
         avg = float(r["AverageNs"]) / 1e3
-        key = short.split("<")[0].split("::")[-1]
+        key = kernel_key(name)
         gbs = alg[key] / (avg * 1e-6) / 1e9 if key in alg else None
         t = timed.get(name)
         tg = alg[key] / (t * 1e-6) / 1e9 if (t and key in alg) else None
@@ -453,6 +467,14 @@ def bench_boundary(args, hcl, hin, torch, np, w, t, ws, outs, Rout, dev):
     v = np.array([a.elapsed_time(z) for a, z in evs]) * 1e3
     bb = boundary_bytes(n, d)
     gbs = bb / (v.mean() * 1e-6) / 1e9
+    if args.copy_calib:
+        src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    # calls of more than 2,048 tokens at d = 5120 run the one-pass kernel
+    traffic = measured_traffic("k_spec_post", n, d)
     line = {
         "metric": "tokens/s + achieved HBM GB/s (% of peak), fused hc mix+pre and hc_post, d=5120",
         "value": round(n / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -464,7 +486,7 @@ def bench_boundary(args, hcl, hin, torch, np, w, t, ws, outs, Rout, dev):
                    "tokens": n, "d": d, "hc": 4, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "hc_post_mix_pre", "achieved": round(gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes": bb, "avg_launch_us": round(float(v.mean()), 2)},
+                     "traffic": traffic, "algorithmic_bytes": bb, "avg_launch_us": round(float(v.mean()), 2)},
         "kernels": {"hc_post_mix_pre": {"avg_us": round(float(v.mean()), 2), "median_us": round(float(np.median(v)), 2),
                                         "min_us": round(float(v.min()), 2), "GB/s": round(gbs, 1),
                                         "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": bb}},
@@ -516,7 +538,7 @@ def main():
         w = hin.WORKLOADS[args.workload]
         os.makedirs(PROFILE_DIR, exist_ok=True)
         if args.summarize_counters:
-            summarize_counters(args.summarize_counters, w.n, w.d, args.profile_command)
+            summarize_counters(args.summarize_counters, w.n, w.d, args.profile_command, args.summary_tag)
         if args.summarize_trace:
             summarize_trace(args.summarize_trace, w.n, w.d, args.profile_command, args.warmup, args.steps,
                             args.summary_tag, args.hc)

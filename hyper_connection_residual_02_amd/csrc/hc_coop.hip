@@ -145,6 +145,13 @@ struct CoopArgs {
     int ext_init;       // k_spec: the header was updated by a launch just before (k_hdr)
     uint64_t spin;      // bound of an exchange wait, in s_memrealtime ticks (100 MHz)
     uint32_t force_tag; // 0; nonzero (diagnostics only) makes every exchange record look stale
+    // hc_post_mix_pre in one pass (k_spec, PO): R' = hc_post(x, R, post, comb)
+    // is formed from each round of R on its way through LDS, written to Rout
+    // (which may be R), and projected in place of R.
+    const uint16_t* x;  // sublayer output [n][d]
+    const float* postp; // the previous sublayer's post [n][4] and comb [n][4][4]
+    const float* combp;
+    uint16_t* Rout;
 };
 
 // A bounded wait of this call gave up: peers stop when they see err, and
@@ -743,29 +750,53 @@ __global__ __launch_bounds__(kThreads, 1) void k_coop(CoopArgs a) {
 namespace spec {
 
 constexpr int kMW = 4;                  // MFMA waves
-constexpr int kNSlot = 3;               // residual rounds held in LDS
 constexpr int kTokX = kT / 4;           // tokens per exchange wave
 constexpr int kXL = 8;                  // exchange loads per lane and pass: 32 members / 4 lane groups
 
-template <int KS>
+// Slot geometry.  A slot holds one round of the member's residual slice,
+// 32 token rows.  PO (the sublayer-boundary variant, hc_post_mix_pre): rows
+// carry no pad (their 16-byte chunks are XOR-swizzled instead, see roff),
+// so that three slots still fit beside a two-slot ring of the round's x
+// rows and the previous sublayer's post and comb, and the partials are
+// single-buffered.
+template <int KS, bool PO = false>
 struct Geo {
-    static constexpr int kRowB = 4 * 64 * KS + 16;             // bytes per token in a slot (+16 pad)
-    static constexpr int kSlotB = (kT * kRowB + 4095) / 4096 * 4096;
-    static constexpr int kDma = kSlotB / 1024;                 // 1 KB load instructions per round
-    static constexpr int kDmaW = kDma / kMW;                   // per MFMA wave
+    static constexpr int kRowB = PO ? 4 * 64 * KS : 4 * 64 * KS + 16;   // bytes per token row of R
+    static constexpr int kRDma = PO ? 8 * KS : (kT * kRowB + 1023) / 1024;   // 1 KB loads of R per round
+    static constexpr int kPostOff = 2 * KS * 1024;             // PO, x slot: x rows (64*KS bytes each) first,
+    static constexpr int kCombOff = kPostOff + kT * 16;        // then post (16 B per token), comb (64 B)
+    static constexpr int kXSlotB = kCombOff + kT * 64;
+    static constexpr int kNeed = PO ? 10 * KS + 3 : kRDma;     // 1 KB loads per round
+    static constexpr int kDmaW = (kNeed + kMW - 1) / kMW;      // per MFMA wave
+    static constexpr int kSlotB = PO ? kRDma * 1024 : kDmaW * kMW * 1024;
+    static constexpr int kNSlot = 3;                           // residual rounds held in LDS
+    static constexpr int kNRed = PO ? 1 : 2;                   // partial buffers
     static constexpr int kBlk = 8 * KS;                        // 4-feature blocks per token and stream
     static constexpr int kItems = kTokX * kBlk;                // h items (token, block) per exchange wave
     static constexpr int kPass = (kItems + 63) / 64;           // KS = 5: 320 items, 5 full passes
+    static constexpr int kPostItems = kT * 4 * KS;             // PO: hc_post items (token, 8 features)
 };
 
-template <int KS>
+template <int KS, bool PO = false>
 struct Lds {
-    uint8_t slot[kNSlot][Geo<KS>::kSlotB];
-    float red[2][kMW][kT][kRed];           // per-MFMA-wave partials, double-buffered by round parity
+    uint8_t slot[Geo<KS, PO>::kNSlot][Geo<KS, PO>::kSlotB];
+    uint8_t xs[PO ? 2 : 1][PO ? Geo<KS, PO>::kXSlotB : 16];   // PO: x, post, comb of rounds by parity
+    float red[Geo<KS, PO>::kNRed][kMW][kT][kRed];   // per-MFMA-wave partials (by round parity if two)
     float xpre[4][kTokX][4];               // pre of each exchange wave's tokens
     float xown[4][10][4];                  // member sums of the owned token's records
     int stop;                              // set when a wait timed out
+    uint32_t acnt;                         // PO: MFMA-wave arrivals, one per wave and tick
 };
+
+// Byte offset of byte b of token row tk's residual in a slot.  PO rows have
+// no pad: their 16-byte chunk c sits at chunk c ^ (tk & 15), a permutation
+// inside each aligned run of 16 chunks (a row has 16*KS), so that the 16
+// rows of an MFMA operand read still fall on distinct LDS banks.
+template <int KS, bool PO>
+__device__ __forceinline__ int roff(int tk, int b) {
+    if (!PO) return tk * Geo<KS, PO>::kRowB + b;
+    return tk * Geo<KS, PO>::kRowB + ((((b >> 4) ^ (tk & 15))) << 4) + (b & 15);
+}
 
 typedef __attribute__((ext_vector_type(4))) uint32_t v4u;
 
@@ -806,10 +837,10 @@ __device__ __forceinline__ int64_t packed_index(int q, int w, int st, int ct, in
     return ((((int64_t)q * kHC + w) * KS + st) * kTiles + ct) * 64 + l;
 }
 
-template <int KS>
+template <int KS, bool PO = false>
 struct MState {
     bf16x8 w[KS][kTiles];                  // weight slice of stream w, MFMA B layout
-    uint32_t dvoff[Geo<KS>::kDmaW];        // lane byte offsets of this wave's loads within a round
+    uint32_t dvoff[Geo<KS, PO>::kDmaW];    // lane byte offsets of this wave's loads within a round
 };
 
 template <int KS>
@@ -842,8 +873,8 @@ __device__ __forceinline__ void st_rec(const RoundCtx& c, int off, u32x4 v) {
 // the member slice, as the bf16 piece (hi, mid or lo) of column tile ct.
 // Each fragment is pinned in registers, which keeps the compiler from
 // re-forming the pieces inside the round loop.
-template <int KS>
-__device__ __forceinline__ void m_split_weights(MState<KS>& S, const CoopArgs& a, const RoundCtx& c) {
+template <int KS, bool PO = false>
+__device__ __forceinline__ void m_split_weights(MState<KS, PO>& S, const CoopArgs& a, const RoundCtx& c) {
     const int64_t K = (int64_t)kHC * a.d;
     // piece (0 hi, 1 mid, 2 lo, -1 none) and weight row of column tile ct
     auto tile_piece = [&](int ct, int& piece, int& j) {
@@ -897,8 +928,8 @@ __device__ __forceinline__ void m_split_weights(MState<KS>& S, const CoopArgs& a
 
 // The same fragments from weights split once by k_pack, stored in this
 // register layout: every load is issued before the first pin.
-template <int KS>
-__device__ __forceinline__ void m_load_packed(MState<KS>& S, const CoopArgs& a, const RoundCtx& c) {
+template <int KS, bool PO = false>
+__device__ __forceinline__ void m_load_packed(MState<KS, PO>& S, const CoopArgs& a, const RoundCtx& c) {
     u32x4 pk[KS][kTiles];
 #pragma unroll
     for (int st = 0; st < KS; ++st)
@@ -914,33 +945,115 @@ __device__ __forceinline__ void m_load_packed(MState<KS>& S, const CoopArgs& a, 
         }
 }
 
-template <int KS>
-__device__ __forceinline__ void m_setup(MState<KS>& S, const CoopArgs& a, const RoundCtx& c) {
-    if (a.Wp) m_load_packed<KS>(S, a, c);
-    else m_split_weights<KS>(S, a, c);
+// Source of the 1 KB load instruction I of a round: 0 the residual, and
+// with PO 1 the rows of x, 2 post (32 lanes), 3 comb.  Instructions past
+// the round's (PO: the last wave's last one to three) repeat instruction
+// I - 3 of the same wave: the same bytes to the same place, so that every
+// wave issues kDmaW loads per round and the wait counts stay exact.
+template <int KS, bool PO>
+__host__ __device__ constexpr int dma_kind(int I) {
+    if (!PO) return I < Geo<KS, PO>::kRDma ? 0 : -1;
+    if (I >= 10 * KS + 3) I -= 3;
+    if (I < 8 * KS) return 0;
+    if (I < 10 * KS) return 1;
+    return I == 10 * KS ? 2 : 3;
+}
+template <int KS, bool PO>
+__host__ __device__ constexpr int dma_real(int I) { return PO && I >= 10 * KS + 3 ? I - 3 : I; }
+
+// The loads of one MFMA wave W (PO), each instruction's source and
+// destination fixed at compile time (no per-instruction branches).
+struct DmaSrc {
+    v4u rs, rx, rp, rc;
+    uint32_t rbase, xbase;
+    int lane;
+};
+template <int KS, int W, int I0, int N>
+struct DmaRun {
+    template <typename Off>
+    __device__ __forceinline__ static void go(const DmaSrc& d, const Off& off) {
+        if constexpr (N > 0) {
+            using GG = Geo<KS, true>;
+            constexpr int I = dma_real<KS, true>(W * GG::kDmaW + I0);
+            constexpr int kind = dma_kind<KS, true>(I);
+            if constexpr (kind == 0) {
+                dma16(d.rs, d.rbase + I * 1024, off[I0]);
+            } else if constexpr (kind == 1) {
+                dma16(d.rx, d.xbase + (I - 8 * KS) * 1024, off[I0]);
+            } else if constexpr (kind == 2) {
+                // half an instruction's worth: only lanes 0..31 write, so
+                // that comb can follow right after post
+                if (d.lane < kT) dma16(d.rp, d.xbase + GG::kPostOff, off[I0]);
+            } else {
+                dma16(d.rc, d.xbase + GG::kCombOff + (I - 10 * KS - 1) * 1024, off[I0]);
+            }
+            DmaRun<KS, W, I0 + 1, N - 1>::go(d, off);
+        }
+    }
+};
+
+template <int KS, bool PO = false>
+__device__ __forceinline__ void m_setup(MState<KS, PO>& S, const CoopArgs& a, const RoundCtx& c) {
+    using GG = Geo<KS, PO>;
+    if (a.Wp) m_load_packed<KS, PO>(S, a, c);
+    else m_split_weights<KS, PO>(S, a, c);
 #pragma unroll
-    for (int i = 0; i < Geo<KS>::kDmaW; ++i) {
-        const int I = c.w * Geo<KS>::kDmaW + i;
-        const int pos = I * 1024 + 16 * c.l;
-        const int tk = pos / Geo<KS>::kRowB, wb = pos - tk * Geo<KS>::kRowB;
-        const int k = wb / (64 * KS), off = wb - k * (64 * KS);
-        S.dvoff[i] = (tk < kT && k < kHC) ? (uint32_t)(tk * 8 * a.d + k * 2 * a.d + c.q * (64 * KS) + off)
-                                          : (uint32_t)kOOB;
+    for (int i = 0; i < GG::kDmaW; ++i) {
+        const int I = dma_real<KS, PO>(c.w * GG::kDmaW + i);
+        const int kind = dma_kind<KS, PO>(I);
+        uint32_t v = (uint32_t)kOOB;
+        if (kind == 0) {
+            // residual: token tk, stream k, byte off of the member's slice
+            const int pos = I * 1024 + 16 * c.l;
+            const int tk = pos / GG::kRowB, wb = pos - tk * GG::kRowB;
+            const int lb = PO ? (((wb >> 4) ^ (tk & 15)) << 4) : wb;      // roff's inverse
+            const int k = lb / (64 * KS), off = lb - k * (64 * KS);
+            if (tk < kT && k < kHC) v = (uint32_t)(tk * 8 * a.d + k * 2 * a.d + c.q * (64 * KS) + off);
+        } else if (kind == 1) {
+            // x: token tk, byte off of the member's slice
+            const int pos = (I - 8 * KS) * 1024 + 16 * c.l;
+            const int tk = pos / (64 * KS), off = pos - tk * (64 * KS);
+            v = (uint32_t)(tk * 2 * a.d + c.q * (64 * KS) + off);
+        } else if (kind == 2) {
+            v = (uint32_t)(16 * c.l);                                  // post, 16 B per token
+        } else if (kind == 3) {
+            v = (uint32_t)((I - 10 * KS - 1) * 1024 + 16 * c.l);      // comb, 64 B per token
+        }
+        S.dvoff[i] = v;
     }
 }
 
-// Round r of this group into slot r % 3 (rounds past the end: zeros).
-template <int KS>
-__device__ __forceinline__ void m_dma(const MState<KS>& S, const CoopArgs& a, const RoundCtx& c, Lds<KS>& L,
-                                      int r) {
+// Round r of this group (rounds past the end: zeros) into slot r % 3; with
+// PO the round's x rows and the previous sublayer's post and comb go to x
+// slot r % 2, each from a resource bounded to the round's tokens.
+template <int KS, bool PO = false>
+__device__ __forceinline__ void m_dma(const MState<KS, PO>& S, const CoopArgs& a, const RoundCtx& c,
+                                      Lds<KS, PO>& L, int r) {
+    using GG = Geo<KS, PO>;
     const int64_t tok0 = tile_of(c, a, r) * kT;
     int64_t valid = a.n - tok0;
     valid = valid < 0 ? 0 : (valid > kT ? kT : valid);
-    const v4u rs = rsrc_words(reinterpret_cast<uintptr_t>(a.R) + (uintptr_t)(valid > 0 ? tok0 : 0) * 8 * a.d,
+    const int64_t t0 = valid > 0 ? tok0 : 0;
+    const v4u rs = rsrc_words(reinterpret_cast<uintptr_t>(a.R) + (uintptr_t)t0 * 8 * a.d,
                               (uint32_t)(valid * 8 * a.d));
-    const uint32_t base = lds_addr(&L.slot[r % kNSlot][0]) + c.w * Geo<KS>::kDmaW * 1024;
+    const uint32_t rbase = lds_addr(&L.slot[r % GG::kNSlot][0]);
+    if constexpr (!PO) {
+        const uint32_t base = rbase + c.w * GG::kDmaW * 1024;
 #pragma unroll
-    for (int i = 0; i < Geo<KS>::kDmaW; ++i) dma16(rs, base + i * 1024, S.dvoff[i]);
+        for (int i = 0; i < GG::kDmaW; ++i) dma16(rs, base + i * 1024, S.dvoff[i]);
+    } else {
+        const v4u rx = rsrc_words(reinterpret_cast<uintptr_t>(a.x) + (uintptr_t)t0 * 2 * a.d,
+                                  (uint32_t)(valid * 2 * a.d));
+        const v4u rp = rsrc_words(reinterpret_cast<uintptr_t>(a.postp) + (uintptr_t)t0 * 16, (uint32_t)(valid * 16));
+        const v4u rc = rsrc_words(reinterpret_cast<uintptr_t>(a.combp) + (uintptr_t)t0 * 64, (uint32_t)(valid * 64));
+        const DmaSrc d{rs, rx, rp, rc, rbase, lds_addr(&L.xs[r & 1][0]), c.l};
+        switch (c.w) {                        // wave-uniform
+            case 0: DmaRun<KS, 0, 0, GG::kDmaW>::go(d, S.dvoff); break;
+            case 1: DmaRun<KS, 1, 0, GG::kDmaW>::go(d, S.dvoff); break;
+            case 2: DmaRun<KS, 2, 0, GG::kDmaW>::go(d, S.dvoff); break;
+            default: DmaRun<KS, 3, 0, GG::kDmaW>::go(d, S.dvoff); break;
+        }
+    }
 }
 
 // Record layout of this kernel, per (group, slot): member-major.  A
@@ -993,8 +1106,8 @@ __device__ __forceinline__ PubMap pub_map(RecOf rec_of) {
 
 // Record p of the lane for the partials of round parity b: the four MFMA
 // waves' partials of each field added in wave order.
-template <int KS>
-__device__ __forceinline__ u32x4 pub_value(const Lds<KS>& L, int b, const PubMap& m, int p) {
+template <int KS, bool PO = false>
+__device__ __forceinline__ u32x4 pub_value(const Lds<KS, PO>& L, int b, const PubMap& m, int p) {
     const float* red = &L.red[b][0][0][0];
     constexpr int kW = kT * kRed;          // floats between two waves' partials
     float x[3];
@@ -1023,28 +1136,28 @@ __device__ __forceinline__ void srec_of(int id, int& tk, int& ch) {
 // Records of round r from the partials of the four MFMA waves (two store
 // instructions per wave, always; past the group's rounds they are dropped).
 // Lane idx writes record idx of this member.
-template <int KS, bool LOCAL>
-__device__ __forceinline__ void m_publish(const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, const PubMap& M,
+template <int KS, bool LOCAL, bool PO = false>
+__device__ __forceinline__ void m_publish(const CoopArgs& a, const RoundCtx& c, Lds<KS, PO>& L, const PubMap& M,
                                           int r) {
     const int tid = threadIdx.x;
     const bool live = r >= 0 && r < c.nr;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int idx = p * (kMW * 64) + tid;
-        u32x4 v = pub_value<KS>(L, r & 1, M, p);
+        u32x4 v = pub_value<KS, PO>(L, Geo<KS, PO>::kNRed == 1 ? 0 : (r & 1), M, p);
         v[3] = tag_of(c, r);
         st_rec<LOCAL>(c, live && idx < kRecMember ? srec_off(a, c, r, c.q, idx) : kOOB, v);
     }
 }
 
 // Partial mixes and sums of squares of stream w for round r (slot r % 3).
-template <int KS>
-__device__ __forceinline__ void m_mfma(const MState<KS>& S, const RoundCtx& c, Lds<KS>& L, int r) {
-    const uint8_t* slot = &L.slot[r % kNSlot][0];
-    const int b = r & 1;
+template <int KS, bool PO = false>
+__device__ __forceinline__ void m_mfma(const MState<KS, PO>& S, const RoundCtx& c, Lds<KS, PO>& L, int r) {
+    const uint8_t* slot = &L.slot[r % Geo<KS, PO>::kNSlot][0];
+    const int b = Geo<KS, PO>::kNRed == 1 ? 0 : (r & 1);
     auto operand = [&](int tt, int st) {
-        return *reinterpret_cast<const u32x4*>(slot + (16 * tt + c.row) * Geo<KS>::kRowB + c.w * (64 * KS) +
-                                              64 * st + 16 * c.grp);
+        return *reinterpret_cast<const u32x4*>(slot + roff<KS, PO>(16 * tt + c.row, c.w * (64 * KS) + 64 * st +
+                                                                                         16 * c.grp));
     };
     // the products of both 16-token tiles go to the matrix core before
     // either tile's sums are read back, so that the read-back of one
@@ -1093,6 +1206,116 @@ __device__ __forceinline__ void m_mfma(const MState<KS>& S, const RoundCtx& c, L
             L.red[b][c.w][t][c.row] = v0;
             if (c.row < 8) L.red[b][c.w][t][16 + c.row] = v1;
         }
+    }
+}
+
+// The one sync inside a tick (PO), on an LDS counter rather than a
+// workgroup barrier, so that the two wave roles keep their own pace: in tick
+// t each MFMA wave counts itself in on `acnt` once its own loads of round
+// t+1 have landed (a wave only waits for the loads it issued) and its
+// publication of round t-1 has read the partials; when the count reaches
+// 4(t+2) round t+1 may be read by every wave and the partials rewritten
+// (the prologue's arrival, for round 0, is the first).  A wait is bounded in
+// time like every other wait (about 2 s) and stops early when the call has
+// given up; it returns true then.
+__device__ __forceinline__ void m_arrive(uint32_t* cnt) {
+    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ bool m_wait(const CoopArgs& a, const uint32_t* cnt, uint32_t target) {
+    if (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return false;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+        __builtin_amdgcn_s_sleep(1);
+        if (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return false;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull ||
+            __hip_atomic_load(&a.hdr->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+            give_up(a);
+            return true;
+        }
+    }
+}
+
+// hc_post of round r in its slot (PO): R'_{k,c} = bf16(post_k x_c +
+// sum_j comb[j][k] R_{j,c}) for the four streams of every feature of the
+// member's slice ("Mix projection" page, Block.hc_post), with the
+// arithmetic of the standalone hc_post (post_words_lean: the same double
+// sums and rounding), so the results are bitwise its results.  R' replaces
+// R in the slot, so the products, the sums of squares and h of this round
+// see R'; the exchange waves write it to Rout from their copy of the round
+// (x_store).  A lane's item is (token, 8 features) of all four streams in
+// the full runs and (token, 4 features) in the half runs: the round's
+// 128*KS items of 8 features are 2*KS runs of 64, the MFMA waves take run
+// j by wave j % 4 and, when the run count is not a multiple of four, the
+// last two runs as four runs of 64 half items, one per wave, so that the
+// four waves do the same work.
+template <int KS>
+__device__ __forceinline__ void post_item(uint8_t* slot, const uint8_t* xs, int tk, int b0, bool half,
+                                          int hoff) {
+    using GG = Geo<KS, true>;
+    const f32x4 q = *reinterpret_cast<const f32x4*>(xs + GG::kPostOff + 16 * tk);
+    f32x4 cb[kHC];
+#pragma unroll
+    for (int j = 0; j < kHC; ++j) cb[j] = *reinterpret_cast<const f32x4*>(xs + GG::kCombOff + 64 * tk + 16 * j);
+    if (!half) {
+        uint32_t rv[kHC][4], xv[4], out[kHC][4];
+#pragma unroll
+        for (int k = 0; k < kHC; ++k) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(slot + roff<KS, true>(tk, k * (64 * KS) + b0));
+#pragma unroll
+            for (int w = 0; w < 4; ++w) rv[k][w] = v[w];
+        }
+        const u32x4 x4 = *reinterpret_cast<const u32x4*>(xs + tk * (64 * KS) + b0);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) xv[w] = x4[w];
+        post_words_lean<4>(q, cb, xv, rv, out);
+#pragma unroll
+        for (int k = 0; k < kHC; ++k)
+            *reinterpret_cast<u32x4*>(slot + roff<KS, true>(tk, k * (64 * KS) + b0)) =
+                u32x4{out[k][0], out[k][1], out[k][2], out[k][3]};
+    } else {
+        uint32_t rv[kHC][2], xv[2], out[kHC][2];
+#pragma unroll
+        for (int k = 0; k < kHC; ++k) {
+            const u32x2 v = *reinterpret_cast<const u32x2*>(slot + roff<KS, true>(tk, k * (64 * KS) + b0 + hoff));
+            rv[k][0] = v[0];
+            rv[k][1] = v[1];
+        }
+        const u32x2 x2 = *reinterpret_cast<const u32x2*>(xs + tk * (64 * KS) + b0 + hoff);
+        xv[0] = x2[0];
+        xv[1] = x2[1];
+        post_words_lean<2>(q, cb, xv, rv, out);
+#pragma unroll
+        for (int k = 0; k < kHC; ++k)
+            *reinterpret_cast<u32x2*>(slot + roff<KS, true>(tk, k * (64 * KS) + b0 + hoff)) = u32x2{out[k][0], out[k][1]};
+    }
+}
+
+template <int KS>
+__device__ __forceinline__ void m_post(const CoopArgs& a, const RoundCtx& c, Lds<KS, true>& L, int r) {
+    using GG = Geo<KS, true>;
+    constexpr int kCh = 4 * KS;            // 8-feature chunks per (token, stream) of the slice
+    static_assert(GG::kPostItems % 64 == 0, "whole runs of 64 hc_post items");
+    constexpr int kRuns = GG::kPostItems / 64;
+    constexpr int kFull = kRuns % kMW == 0 ? kRuns : kRuns - 2;     // runs taken whole
+    static_assert(kRuns % kMW == 0 || kRuns % kMW == 2, "runs split evenly over the MFMA waves");
+    uint8_t* slot = &L.slot[r % GG::kNSlot][0];
+    const uint8_t* xs = &L.xs[r & 1][0];
+#pragma unroll 1
+    for (int j = c.w; j < kFull; j += kMW) {                 // c.w is wave-uniform
+        int it = j * 64 + c.l;
+        // formed anew in every round: held across the round loop, the
+        // item's offsets would take registers
+        asm volatile("" : "+v"(it));
+        const int tk = it / kCh, ch = it - tk * kCh;
+        post_item<KS>(slot, xs, tk, 16 * ch, false, 0);
+    }
+    if constexpr (kFull < kRuns) {
+        // the last two runs as 256 half items, 64 per wave
+        int hi = c.w * 64 + c.l;
+        asm volatile("" : "+v"(hi));
+        const int it = kFull * 64 + (hi >> 1);
+        const int tk = it / kCh, ch = it - tk * kCh;
+        post_item<KS>(slot, xs, tk, 16 * ch, true, 8 * (hi & 1));
     }
 }
 
@@ -1153,8 +1376,8 @@ __device__ __forceinline__ void x_issue(XState<KS>& X, const CoopArgs& a, const 
 // tokens this member owns) and the mixes of owned token xw.  A record that
 // still carries an older tag is re-read until current (bounded in time).
 // Returns true on a timeout.
-template <int KS, bool FUSED, bool LOCAL>
-__device__ __forceinline__ bool x_exchange(XState<KS>& X, const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, int xw,
+template <int KS, bool FUSED, bool LOCAL, bool PO = false>
+__device__ __forceinline__ bool x_exchange(XState<KS>& X, const CoopArgs& a, const RoundCtx& c, Lds<KS, PO>& L, int xw,
                                            int r) {
     const uint32_t tag = tag_of(c, r) ^ a.force_tag;
     const int l = c.l, e = l & 15;
@@ -1231,9 +1454,9 @@ __device__ __forceinline__ bool x_exchange(XState<KS>& X, const CoopArgs& a, con
 
 // h of round r for exchange wave xw from the residual copy rb (items of 4
 // features: token tk, block b).
-template <int KS>
+template <int KS, bool PO = false>
 __device__ __forceinline__ void x_h(const u32x2 (&rb)[Geo<KS>::kPass][kHC], const CoopArgs& a, const RoundCtx& c,
-                                    Lds<KS>& L, int xw, int r) {
+                                    Lds<KS, PO>& L, int xw, int r) {
     const int64_t tok0 = tile_of(c, a, r) * kT;
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(a.h, (int64_t)a.d * 2, tok0, a.n, kT);
     // pre of every pass's token, read from LDS together (one wait, not one
@@ -1284,10 +1507,10 @@ __device__ __forceinline__ void x_h(const u32x2 (&rb)[Geo<KS>::kPass][kHC], cons
 }
 
 // Copy of round r's residual (slot r % 3) for this wave's h items.
-template <int KS>
-__device__ __forceinline__ void x_copy(u32x2 (&rb)[Geo<KS>::kPass][kHC], const RoundCtx& c, Lds<KS>& L, int xw,
+template <int KS, bool PO = false>
+__device__ __forceinline__ void x_copy(u32x2 (&rb)[Geo<KS>::kPass][kHC], const RoundCtx& c, Lds<KS, PO>& L, int xw,
                                        int r) {
-    const uint8_t* slot = &L.slot[r % kNSlot][0];
+    const uint8_t* slot = &L.slot[r % Geo<KS, PO>::kNSlot][0];
 #pragma unroll
     for (int p = 0; p < Geo<KS>::kPass; ++p) {
         const int item = p * 64 + c.l;
@@ -1295,22 +1518,47 @@ __device__ __forceinline__ void x_copy(u32x2 (&rb)[Geo<KS>::kPass][kHC], const R
         const int tk = it / Geo<KS>::kBlk, b = it - tk * Geo<KS>::kBlk;
 #pragma unroll
         for (int k = 0; k < kHC; ++k)
-            rb[p][k] = *reinterpret_cast<const u32x2*>(slot + (kTokX * xw + tk) * Geo<KS>::kRowB + k * (64 * KS) +
-                                                      8 * b);
+            rb[p][k] = *reinterpret_cast<const u32x2*>(slot + roff<KS, PO>(kTokX * xw + tk, k * (64 * KS) + 8 * b));
+    }
+}
+
+// PO: round r's R' to Rout from the copy just taken (the exchange waves'
+// items cover the whole round), with non-temporal stores: this call does
+// not read it back.  Taking the stores off the MFMA waves keeps them out of
+// the way of those waves' residual loads.
+template <int KS>
+__device__ __forceinline__ void x_store(const u32x2 (&rb)[Geo<KS>::kPass][kHC], const CoopArgs& a,
+                                        const RoundCtx& c, int xw, int r) {
+    const int64_t tok0 = tile_of(c, a, r) * kT;
+    int64_t valid = a.n - tok0;
+    valid = valid < 0 ? 0 : (valid > kT ? kT : valid);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        a.Rout + (valid > 0 ? tok0 : 0) * 4 * a.d, 0, (int)(valid * 8 * a.d), kBufDword3);
+#pragma unroll
+    for (int p = 0; p < Geo<KS>::kPass; ++p) {
+        const int it = p * 64 + c.l;
+        const int tk = it / Geo<KS>::kBlk, b = it - tk * Geo<KS>::kBlk;
+        const int vo = (kTokX * xw + tk) * 8 * a.d + c.q * (64 * KS) + 8 * b;
+#pragma unroll
+        for (int k = 0; k < kHC; ++k)      // stream k's offset in the scalar operand
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((__vector_size__(8))) int, rb[p][k]),
+                                                  ro, vo, k * 2 * a.d, 2);
     }
 }
 
 // Exchange-wave part of tick t; P is the parity of t (selects the residual
 // copy).  Returns true on a timeout.
-template <int KS, bool FUSED, bool LOCAL, int P>
-__device__ __forceinline__ bool x_tick(XState<KS>& X, const CoopArgs& a, const RoundCtx& c, Lds<KS>& L, int t) {
+template <int KS, bool FUSED, bool LOCAL, int P, bool PO = false>
+__device__ __forceinline__ bool x_tick(XState<KS>& X, const CoopArgs& a, const RoundCtx& c, Lds<KS, PO>& L, int t) {
     const int xw = c.w - kMW;
     bool bad = false;
-    if (t >= 2 && t - 2 < c.nr) {
-        bad = x_exchange<KS, FUSED, LOCAL>(X, a, c, L, xw, t - 2);
-        if (FUSED && !bad) x_h<KS>(X.rb[P], a, c, L, xw, t - 2);
+    const bool xr = t >= 2 && t - 2 < c.nr;
+    if (xr) bad = x_exchange<KS, FUSED, LOCAL, PO>(X, a, c, L, xw, t - 2);
+    if (FUSED && xr && !bad) x_h<KS, PO>(X.rb[P], a, c, L, xw, t - 2);
+    if (FUSED) x_copy<KS, PO>(X.rb[P], c, L, xw, t);
+    if constexpr (PO) {
+        if (t < c.nr) x_store<KS>(X.rb[P], a, c, xw, t);
     }
-    if (FUSED) x_copy<KS>(X.rb[P], c, L, xw, t);
     // records of round t-1 (published at the start of this tick) for the
     // next tick's exchange: their latency overlaps the barrier
     if (t >= 1 && t - 1 < c.nr) x_issue<KS, FUSED, LOCAL>(X, a, c, xw, t - 1);
@@ -1321,28 +1569,60 @@ __device__ __forceinline__ bool x_tick(XState<KS>& X, const CoopArgs& a, const R
 // prologue barrier, then one barrier per tick t = 0 .. nr+1 (the exchange of
 // the last round happens in tick nr+1); after each barrier both read the
 // stop flag, so both leave after the same tick.
-template <int KS, bool FUSED, bool LOCAL>
-__device__ __forceinline__ void spec_body(const CoopArgs& a, const RoundCtx& c, Lds<KS>& L) {
+//
+// PO (hc_post_mix_pre): in tick t the MFMA waves publish round t-1, issue
+// round t+2 (residual, x, post, comb) into the slots round t-1 left, count
+// themselves in once their loads of round t+1 have landed, multiply round t
+// (turned into R' last tick), and then turn round t+1 into R' in place
+// (m_post), which the tick's closing barrier orders before round t+1's
+// products and the exchange waves' copy of it.
+template <int KS, bool FUSED, bool LOCAL, bool PO = false>
+__device__ __forceinline__ void spec_body(const CoopArgs& a, const RoundCtx& c, Lds<KS, PO>& L) {
     const int last = c.nr + 1;
     if (c.w < kMW) {
-        MState<KS> S;
-        m_setup<KS>(S, a, c);
+        MState<KS, PO> S;
+        m_setup<KS, PO>(S, a, c);
         const PubMap M = pub_map(srec_of);
-        m_dma<KS>(S, a, c, L, 0);
-        m_dma<KS>(S, a, c, L, 1);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW) : "memory");   // round 0 landed
+        m_dma<KS, PO>(S, a, c, L, 0);
+        m_dma<KS, PO>(S, a, c, L, 1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS, PO>::kDmaW) : "memory");   // round 0 landed
+        if constexpr (PO) {
+            // round 0 into R' before the first tick
+            m_arrive(&L.acnt);
+            const bool bad = m_wait(a, &L.acnt, 4u);
+            if (!bad) m_post<KS>(a, c, L, 0);
+            else L.stop = 1;
+        }
         __syncthreads();
         for (int t = 0;; ++t) {
             // records first (peers are waiting for them), then the residual
-            // of round t+2, then the products of round t
-            m_publish<KS, LOCAL>(a, c, L, M, t - 1);
-            m_dma<KS>(S, a, c, L, t + 2);
-            m_mfma<KS>(S, c, L, t);
-            // round t+1 (issued last tick, its loads the youngest memory
-            // instructions of that tick) must be in LDS before the barrier:
-            // younger than them are only this tick's two record stores and
-            // its loads
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW + 2) : "memory");
+            // loads, then the products of round t
+            m_publish<KS, LOCAL, PO>(a, c, L, M, t - 1);
+            if constexpr (PO) {
+                // round t+2 into the slots round t-1 left; round t (R' since
+                // last tick) is multiplied; round t+1 is turned into R'
+                m_dma<KS, PO>(S, a, c, L, t + 2);
+                // round t+1 landed (issued last tick): younger than its loads
+                // are at most last tick's R' stores, this tick's two record
+                // stores and its loads, and the R' stores are older than the
+                // last kDmaW + 2, so waiting down to kDmaW + 2 covers round
+                // t+1 (and those stores)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS, PO>::kDmaW + 2) : "memory");
+                m_arrive(&L.acnt);
+                // every MFMA wave's publication has read the (single) partials
+                const bool bad = m_wait(a, &L.acnt, 4u * (t + 2));
+                if (bad) L.stop = 1;
+                m_mfma<KS, PO>(S, c, L, t);
+                if (t + 1 < c.nr && !bad) m_post<KS>(a, c, L, t + 1);
+            } else {
+                m_dma<KS>(S, a, c, L, t + 2);
+                m_mfma<KS>(S, c, L, t);
+                // round t+1 (issued last tick, its loads the youngest memory
+                // instructions of that tick) must be in LDS before the barrier:
+                // younger than them are only this tick's two record stores and
+                // its loads
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW + 2) : "memory");
+            }
             __syncthreads();
             if (L.stop || t + 1 > last) break;
         }
@@ -1353,19 +1633,19 @@ __device__ __forceinline__ void spec_body(const CoopArgs& a, const RoundCtx& c, 
         x_offsets<KS>(X, a, c, c.w - kMW);
         __syncthreads();
         for (int t = 0;; t += 2) {
-            if (x_tick<KS, FUSED, LOCAL, 0>(X, a, c, L, t)) L.stop = 1;
+            if (x_tick<KS, FUSED, LOCAL, 0, PO>(X, a, c, L, t)) L.stop = 1;
             __syncthreads();
             if (L.stop || t + 1 > last) break;
-            if (x_tick<KS, FUSED, LOCAL, 1>(X, a, c, L, t + 1)) L.stop = 1;
+            if (x_tick<KS, FUSED, LOCAL, 1, PO>(X, a, c, L, t + 1)) L.stop = 1;
             __syncthreads();
             if (L.stop || t + 2 > last) break;
         }
     }
 }
 
-template <int KS, bool FUSED>
+template <int KS, bool FUSED, bool PO = false>
 __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
-    __shared__ __attribute__((aligned(16))) Lds<KS> L;
+    __shared__ __attribute__((aligned(16))) Lds<KS, PO> L;
     __shared__ int local_mode;
     RoundCtx c;
     c.g = blockIdx.x % a.NG;
@@ -1454,12 +1734,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
         const bool local = a.NG % 8 == 0 && (v >> 16) == 0u;
         local_mode = ok ? (local ? 1 : 0) : -1;
         L.stop = 0;
+        L.acnt = 0u;
     }
     __syncthreads();
     const int mode = local_mode;
     if (mode < 0 || c.g >= a.ntiles) return;
-    if (mode) spec_body<KS, FUSED, true>(a, c, L);
-    else spec_body<KS, FUSED, false>(a, c, L);
+    if (mode) spec_body<KS, FUSED, true, PO>(a, c, L);
+    else spec_body<KS, FUSED, false, PO>(a, c, L);
 }
 
 
@@ -1882,9 +2163,11 @@ static int launch_two_pass(const CoopPlan& p, CoopArgs& a, bool fused, hipStream
 }
 
 template <int KS>
-static int launch_spec(const CoopPlan& p, CoopArgs& a, bool fused, hipStream_t s) {
+static int launch_spec(const CoopPlan& p, CoopArgs& a, bool fused, bool post, hipStream_t s) {
     void* args[] = {&a};
-    const void* f = fused ? (const void*)spec::k_spec<KS, true> : (const void*)spec::k_spec<KS, false>;
+    const void* f = post    ? (const void*)spec::k_spec<KS, true, true>
+                    : fused ? (const void*)spec::k_spec<KS, true>
+                            : (const void*)spec::k_spec<KS, false>;
     hipError_t e = hipLaunchKernel(f, dim3(p.G * p.NG), dim3(kThreads), args, 0, s);
     return e == hipSuccess ? 0 : -1;
 }
@@ -1894,7 +2177,11 @@ int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* s
                 int iters, float eps, float norm_eps, bool fused, hipStream_t s, const PostIn* prev,
                 const void* Wp) {
     char* wsb = static_cast<char*>(ws);
-    if (prev) {
+    // The sublayer boundary in one pass: the persistent kernel forms R' from
+    // each round of R in LDS (k_spec, PO), so R is read once for hc_post,
+    // the projection and h.
+    const bool one_pass = prev && fused && !p.two_pass && use_spec(p);
+    if (prev && !one_pass) {
         // hc_post, then the projection of its output.  (Applying hc_post to
         // each round inside k_part, while the residual is in LDS, was
         // slower: its exact-rounding work then runs on the few CUs of a
@@ -1931,6 +2218,12 @@ int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* s
     a.call = g_calls.fetch_add(1, std::memory_order_relaxed) + 1;
     a.spin = kSpin;
     a.force_tag = 0u;
+    if (one_pass) {
+        a.x = static_cast<const uint16_t*>(prev->x);
+        a.postp = prev->post;
+        a.combp = prev->comb;
+        a.Rout = static_cast<uint16_t*>(prev->Rout);
+    }
     int rc = -1;
     if (p.two_pass) {
         // mixes go only where the caller asked for them; pass 2 does the split
@@ -1978,11 +2271,11 @@ int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* s
             if (hipGetLastError() != hipSuccess) return -1;
         }
         switch (p.KS) {
-            case 1: rc = launch_spec<1>(p, a, fused, s); break;
-            case 2: rc = launch_spec<2>(p, a, fused, s); break;
-            case 3: rc = launch_spec<3>(p, a, fused, s); break;
-            case 4: rc = launch_spec<4>(p, a, fused, s); break;
-            case 5: rc = launch_spec<5>(p, a, fused, s); break;
+            case 1: rc = launch_spec<1>(p, a, fused, one_pass, s); break;
+            case 2: rc = launch_spec<2>(p, a, fused, one_pass, s); break;
+            case 3: rc = launch_spec<3>(p, a, fused, one_pass, s); break;
+            case 4: rc = launch_spec<4>(p, a, fused, one_pass, s); break;
+            case 5: rc = launch_spec<5>(p, a, fused, one_pass, s); break;
         }
     } else switch (p.KS) {
         case 1: rc = launch_ks<1>(p, a, fused, s); break;

@@ -61,6 +61,15 @@ __device__ __forceinline__ float f32_mid(double y, bool& mid) {
 // Pack two bf16 bit patterns into one word (element 0 low).
 __device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
 
+// Two floats to one word of bf16 bits, each rounded to nearest even (one
+// v_cvt_pk_bf16_f32; the same rounding as bf16_rn on each): pack2(bf16_rn(lo),
+// bf16_rn(hi)) in one instruction.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rn(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){lo, hi}, bf16x2v));
+}
+
 // h of one 16-byte chunk (8 consecutive features) from the four streams'
 // chunks r0..r3 and the token's pre p ("Mix projection" page, Block.hc_pre):
 // each output is the correctly rounded bf16 of sum_k p_k R_k, accumulated in
@@ -132,6 +141,41 @@ __device__ __forceinline__ void post_chunk8(const f32x4 q, const f32x4 (&cb)[kHC
         for (int k = 0; k < kHC; ++k)
 #pragma unroll
             for (int w = 0; w < 4; ++w) out[k][w] = pack2(bf16_rn(f[k][w][0]), bf16_rn(f[k][w][1]));
+    }
+}
+
+// post_chunk8 with the work ordered by input word: for each 32-bit word w
+// (two features) the eight outputs of the four streams, so that only that
+// word's inputs are live as doubles.  NW words per stream (4: a 16-byte
+// chunk, 2: half of one).  The same double sums, so the same bits (each
+// output is bf16_rn_f64 of its sum whichever path a wave takes), for
+// callers short of registers.
+template <int NW>
+__device__ __forceinline__ void post_words_lean(const f32x4 q, const f32x4 (&cb)[kHC], const uint32_t (&xv)[NW],
+                                                const uint32_t (&r)[kHC][NW], uint32_t (&out)[kHC][NW]) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        auto sum = [&](int k, int e) {
+            auto v = [&](uint32_t word) { return (double)(e ? bf_hi(word) : bf_lo(word)); };
+            double y = (double)q[k] * v(xv[w]);
+#pragma unroll
+            for (int j = 0; j < kHC; ++j) y = __builtin_fma((double)cb[j][k], v(r[j][w]), y);
+            return y;
+        };
+        float f[kHC][2];
+        bool mid = false;
+#pragma unroll
+        for (int k = 0; k < kHC; ++k) {
+            f[k][0] = f32_mid(sum(k, 0), mid);
+            f[k][1] = f32_mid(sum(k, 1), mid);
+        }
+        if (__builtin_amdgcn_ballot_w64(mid)) {
+#pragma unroll
+            for (int k = 0; k < kHC; ++k) out[k][w] = pack2(bf16_rn_f64(sum(k, 0)), bf16_rn_f64(sum(k, 1)));
+        } else {
+#pragma unroll
+            for (int k = 0; k < kHC; ++k) out[k][w] = bf16x2_rn(f[k][0], f[k][1]);
+        }
     }
 }
 

@@ -227,8 +227,12 @@ int hc_fused_mix_pre(const void *R, const float *hc_fn,
  * (the residual updated in place); R_out must not otherwise overlap R, and
  * no output may overlap an input or another output.  Same constraints on d
  * and the same workspace (hc_fused_workspace_bytes) as hc_fused_mix_pre.
- * The call runs hc_post's kernel and then hc_fused_mix_pre's kernels on
- * `stream`: one call per sublayer boundary instead of two.
+ * Calls of more than 2,048 tokens at the widths of the wave-specialised
+ * projection (d = 32*k*G, 8 <= G <= 32, d = 5120 among them) run one pass
+ * over R: the projection kernel forms R' from each round of R on its way
+ * through on-chip memory, writes it to R_out and projects it, so R is read
+ * once for hc_post, the mixes and h.  Other calls run hc_post's kernel and
+ * then hc_fused_mix_pre's kernels on `stream`.
  */
 int hc_post_mix_pre(const void *x, const void *R, const float *post,
                     const float *comb, void *R_out, const float *hc_fn,

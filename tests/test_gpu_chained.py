@@ -138,14 +138,16 @@ def _same_bits(a, b):
 
 
 @pytest.mark.timeout(300)
-def test_chained_stack_with_fused_boundaries():
-    # The 80-sublayer stack on 64 decode tokens, with hc_post of sublayer l
-    # fused into sublayer l+1's projection (hc_post_mix_pre) and the
-    # residual updated in place: at every sublayer h, and at the end the
-    # residual, are bitwise those of the chain of separate calls (compared
-    # as bit patterns, since the stack overflows bf16 near its end).
+@pytest.mark.parametrize("n", [64, 4100])
+def test_chained_stack_with_fused_boundaries(n):
+    # The 80-sublayer stack with hc_post of sublayer l fused into sublayer
+    # l+1's projection (hc_post_mix_pre) and the residual updated in place:
+    # at every sublayer h, and at the end the residual, are bitwise those of
+    # the chain of separate calls (compared as bit patterns, since the stack
+    # overflows bf16 near its end).  64 decode tokens run the two-pass path;
+    # 4,100 tokens run the persistent kernel that forms R' in LDS.
     w = hin.WORKLOADS["chained"]
-    hc, d, n = w.hc, w.d, 64
+    hc, d = w.hc, w.d
     R0 = hin.make_inputs(w, DEV)["R"].reshape(-1, hc, d)[:n].contiguous()
     params = [hin.make_params(w, DEV, layer=l) for l in range(w.layers)]
     diags = [hin.make_diag(w, l, DEV) for l in range(w.layers)]

@@ -275,12 +275,16 @@ def test_two_pass_and_persistent_paths_agree_bitwise(d):
 
 
 @pytest.mark.parametrize("d,n", [(5120, 1), (5120, 64), (5120, 256), (5120, 257), (5120, 2100),
+                                 (5120, 4097), (5120, 20011), (5120, 65536),
+                                 (256, 3000), (1024, 2049), (2048, 2500), (2560, 2200), (3072, 4133),
                                  (256, 77), (64, 40)])
 def test_post_mix_pre_matches_the_two_calls(orc, d, n):
     # hc_post of sublayer l and then the fused call of sublayer l+1 on its
     # output, as one entry point: bitwise the two calls in sequence, out of
-    # place and in place (R_out == R), on the two-pass and the persistent
-    # path and at a width of the cooperative kernel.
+    # place and in place (R_out == R), on the two-pass path, on the
+    # persistent kernel that forms R' from each round in LDS (every slice
+    # width it serves, ragged last rounds, the large workload's size) and at
+    # widths of the cooperative kernel.
     w = hin.Workload("pmp%d" % d, 1, n, 4, d, 1.0 / np.sqrt(4 * d), 0.5, 2.0, 1.0)
     t = hin.make_inputs(w, DEV, seed=61)
     nxt = hin.make_inputs(w, DEV, seed=62)          # sublayer l+1's weights, scale and base
