@@ -206,17 +206,22 @@ def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, step
         lines.append("| k_part + k_fin (hc_fused_mix_pre, two-pass) | %s | %.2f | - | - | %.1f | %.3f | %s | %s |" % (
             part[0]["Calls"], avg, gbs, gbs / HBM_PEAK_GBS, "%.2f" % t if t else "-",
             "%.3f" % (tg / HBM_PEAK_GBS) if tg else "-"))
-    # other stream counts run the fused entry point as three plain launches
-    gen = [[r for r in rows if "::k_gmix" in r["Name"]], [r for r in rows if "::k_gsplit<" in r["Name"]],
+    # other stream counts run the fused entry point as the projection (k_gmm,
+    # with k_gred when its reduction is split over workgroups), the split and
+    # hc_pre
+    gen = [[r for r in rows if "::k_gmm<" in r["Name"]], [r for r in rows if "::k_gsplit<" in r["Name"]],
            [r for r in rows if "::k_gpre<" in r["Name"]]]
+    red = [r for r in rows if "::k_gred<" in r["Name"]]
+    if red:
+        gen.append(red)
     if all(gen):
         avg = sum(float(g[0]["AverageNs"]) for g in gen) / 1e3
         gbs = fb / (avg * 1e-6) / 1e9
         ts = [timed.get(g[0]["Name"]) for g in gen]
         t = sum(ts) if all(ts) else None
         tg = fb / (t * 1e-6) / 1e9 if t else None
-        lines.append("| k_gmix + k_gsplit + k_gpre (hc_fused_mix_pre) | %s | %.2f | - | - | %.1f | %.3f | %s | %s |" % (
-            gen[0][0]["Calls"], avg, gbs, gbs / HBM_PEAK_GBS, "%.2f" % t if t else "-",
+        lines.append("| k_gmm%s + k_gsplit + k_gpre (hc_fused_mix_pre) | %s | %.2f | - | - | %.1f | %.3f | %s | %s |" % (
+            " + k_gred" if red else "", gen[0][0]["Calls"], avg, gbs, gbs / HBM_PEAK_GBS, "%.2f" % t if t else "-",
             "%.3f" % (tg / HBM_PEAK_GBS) if tg else "-"))
     lines.append("")
     if steps:
@@ -720,7 +725,7 @@ def main():
     else:
         dom = dict(name="hc_fused_mix_pre", kernel="k_spec", us=f_mean, bytes=fb, gbs=f_gbs)
     if w.hc != 4:
-        dom["kernel"] = "k_gpost" if dom["name"] == "hc_post" else "k_gmix + k_gsplit + k_gpre"
+        dom["kernel"] = "k_gpost" if dom["name"] == "hc_post" else "k_gmm + k_gsplit + k_gpre"
     traffic = measured_traffic(dom["kernel"], n, d) if w.hc == 4 else None
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample of the same workload

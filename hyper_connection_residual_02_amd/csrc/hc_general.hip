@@ -5,26 +5,30 @@
 // numbers for any hc; four streams take the tuned kernels of the other
 // files.  Here every step is a plain kernel, one template instance per hc:
 //
-//  * k_gmix  -- projection and RMS: a 32-token tile per workgroup, the
-//               reduction axis staged 64 elements at a time through LDS
-//               (tokens as float, weights as float), each thread holding a
-//               4 x 4 block of (token, output) sums in double, accumulated
-//               in feature order (k_gmix_pairs: one pair per thread, for
-//               fewer than 48 outputs and many tokens; k_gmix_wave: one
-//               wave per 2-4 tokens, lanes splitting the features, for few
-//               outputs or few tokens).
-//               Products of a bf16 and an fp32 value are exact in double;
-//               k_gmix_pairs sums in feature order, k_gmix as (even staged
-//               steps) + (odd staged steps), and the wave kernel adds 64
-//               per-lane partial sums in a fixed butterfly.  Each stream
-//               count takes one summation order whatever the call's size,
-//               so a token's mixes never depend on the rest of its call.
+//  * k_gmm   -- projection and RMS on the matrix cores: a tile of 32..256
+//               tokens per workgroup (one wave per 32), the reduction axis
+//               in 64-element chunks staged through LDS, the fp32 weights
+//               split exactly into three bf16 pieces (w = hi + mid + lo)
+//               as they are staged, so every product is that of fp32
+//               arithmetic; the sums are fp32 (v_mfma_f32_16x16x32_bf16),
+//               the sums of squares come from A A^T on the same operands
+//               (plain and scaled by 2^-72, for streams whose squares
+//               overflow fp32).  The axis is cut into kSeg fixed segments,
+//               each summed on its own and the segments added in order:
+//               one workgroup may take all of them (large calls, and
+//               hc_mixes, which has no workspace) or each its own with the
+//               partial sums going through the workspace to k_gred (short
+//               calls, to fill the chip).  The two give the same bits, and
+//               the tile size does not matter to a token's sums, so a
+//               token's mixes never depend on the rest of its call.
 //  * k_gsplit -- split + epsilon-Sinkhorn, one token per thread, with the
 //               gate, softmax and normalisation arithmetic of the four-stream
 //               kernel (same functions, same order).
 //  * k_gpre, k_gpost -- hc_pre and hc_post over 16-byte chunks (8 features
 //               of one token), summed in double in the order of the formula
 //               and rounded once to bf16 (nearest even).
+#include <type_traits>
+
 #include "hc_device.hpp"
 #include "hc_launch.hpp"
 
@@ -34,295 +38,323 @@ bool gen_hc(int hc_) { return hc_ >= 1 && hc_ <= kGenMaxHC && hc_ != kHC; }
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// The fused call's workspace: k_gmm's partial sums (kSeg segments of
+// (2 + hc) * hc + 2 floats per token), then the mixes and pre.
 size_t gen_ws_bytes(int64_t n, int hc_) {
     const size_t M = (size_t)(2 + hc_) * hc_;
-    return align256((size_t)n * M * 4) + align256((size_t)n * hc_ * 4);
+    return align256((size_t)n * 8 * (M + 2) * 4) + align256((size_t)n * M * 4) + align256((size_t)n * hc_ * 4);
 }
 
 namespace {
 
 constexpr int kGThreads = 256;
-constexpr int kGT = 32;      // tokens per projection tile (kGT * 8 == kGThreads)
-constexpr int kGKC = 64;     // reduction elements per staged step
-static_assert(kGT * 8 == kGThreads, "one 16-byte chunk of the token tile per thread");
-// Output count from which the projection uses 4 x 4 micro-tiles: below it too
-// few threads would own a tile (measured: at 8 outputs the per-pair mapping
-// is 2x faster, at 80 outputs the micro-tiles are 3x faster).
-constexpr int kGTileMinM = 48;
-// Below that, one wave per 2-4 tokens (k_gmix_wave) for at most 15 outputs
-// (hc = 1, 2, 3), else one pair per thread (k_gmix_pairs, hc = 5), at every
-// n: the two add in different orders, so a size threshold between them
-// would let a token's last mix bit depend on its call's size.  The wave
-// kernel fills the chip at small n but reads the weights once per 2-4
-// tokens; measured (fused call, d = 5120): hc = 2, 4,096 tokens 69 us
-// against 311, 65,536 tokens 933 against 1,512; hc = 3, 4,096 tokens 225
-// against 478, 65,536 tokens 3,480 against 3,050; hc = 5, 4,096 tokens
-// 1,445 against 2,896, 65,536 tokens 18,813 against 10,827.
-constexpr int kGWaveMaxM = 15;
 
 // Mix formula of the "Mix projection" page: m_j = r * sum_i x_i W[j, i] with
-// r = 1 / sqrt(sum_i x_i^2 / K + norm_eps), K = hc * d.
-//
-// H groups ("halves") of 256 threads take interleaved staged steps (group h
-// the steps H s + h), each with its own LDS tiles, so that with H = 2 a
-// thread walks half the reduction axis: that pays while the tiles alone
-// leave compute units idle, and costs LDS and occupancy otherwise.  In a
-// group, threads 0..NW-1 each own a 4-token x 4-output
-// micro-tile (tokens tg + 8i, outputs 4 jg + u), so each step costs 8 LDS
-// reads per 16 products; threads NW..NW+31 form one token's sum of squares.
-// The loads of a half's next step are issued before the products of its
-// current one.  Every sum is formed as (even steps) + (odd steps), each part
-// in feature order: with H = 2 the two groups hold the two parts, with H = 1
-// one thread keeps both, so the two variants give the same bits and a
-// token's mixes do not depend on which one its call takes.
-template <int HC, int H>
-__global__ __launch_bounds__(H * kGThreads) void k_gmix(const uint16_t* __restrict__ R, const float* __restrict__ W,
-                                                        float* __restrict__ mixes, int64_t n, int d, float norm_eps) {
-    constexpr int M = (2 + HC) * HC;
-    constexpr int TT = 4, JJ = 4;
-    constexpr int NT = kGT / TT;                 // token groups
-    constexpr int NJ = (M + JJ - 1) / JJ;        // output groups (the last may be padded)
-    constexpr int NW = NT * NJ;                  // threads of a half with a micro-tile
-    static_assert(NW + kGT <= kGThreads, "micro-tiles plus one sum-of-squares thread per token");
-    constexpr int WCH = M * (kGKC / 4);          // 16-byte weight chunks per step
-    constexpr int WPT = (WCH + kGThreads - 1) / kGThreads;
-    static_assert(H == 1 || H == 2, "one or two groups");
-    __shared__ float xs[H][kGT][kGKC + 1];       // odd row stride: a wave's rows fall in distinct banks
-    __shared__ float ws[H][M][kGKC + 1];
-    __shared__ double red[H == 2 ? NW : 1][TT * JJ];   // odd-step sums of group 1, added by group 0
-    __shared__ double sred[H == 2 ? kGT : 1];
-    __shared__ double ssq[kGT];
-    const int64_t K = (int64_t)HC * d;
-    const int64_t ntiles = (n + kGT - 1) / kGT;
-    const int h = threadIdx.x / kGThreads;       // group
-    const int tid = threadIdx.x - h * kGThreads;
-    const int tg = tid % NT, jg = tid / NT;
-    const int st = tid - NW;
-    const int xt = tid >> 3, xq = tid & 7;       // staged x chunk of this thread
+// r = 1 / sqrt(sum_i x_i^2 / K + norm_eps), K = hc * d, over the flattened
+// stream (x = R[t] read as K contiguous values).
+constexpr int kSeg = 8;      // segments of the reduction axis, added in order
+constexpr int kKC = 64;      // reduction elements per staged chunk (two MFMA k-steps)
 
-    // K is a multiple of 8: a chunk lies wholly inside its row or past its
-    // end; past K every staged value is zero
-    auto load = [&](int64_t t0, int64_t k0, uint4& xv, float4 (&wv)[WPT]) {
-        const int64_t k = k0 + xq * 8;
-        xv = make_uint4(0u, 0u, 0u, 0u);
-        if (t0 + xt < n && k < K) xv = *reinterpret_cast<const uint4*>(R + (t0 + xt) * K + k);
-#pragma unroll
-        for (int i = 0; i < WPT; ++i) {
-            const int c = tid + i * kGThreads;
-            const int j = c / (kGKC / 4), q = c - j * (kGKC / 4);
-            const int64_t kk = k0 + q * 4;
-            wv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (c < WCH && kk < K) wv[i] = *reinterpret_cast<const float4*>(W + (int64_t)j * K + kk);
-        }
-    };
-    auto stage = [&](const uint4& xv, const float4 (&wv)[WPT]) {
-        float* xr = &xs[h][xt][xq * 8];
-        xr[0] = bf_lo(xv.x); xr[1] = bf_hi(xv.x);
-        xr[2] = bf_lo(xv.y); xr[3] = bf_hi(xv.y);
-        xr[4] = bf_lo(xv.z); xr[5] = bf_hi(xv.z);
-        xr[6] = bf_lo(xv.w); xr[7] = bf_hi(xv.w);
-#pragma unroll
-        for (int i = 0; i < WPT; ++i) {
-            const int c = tid + i * kGThreads;
-            if (c < WCH) {
-                const int j = c / (kGKC / 4), q = c - j * (kGKC / 4);
-                float* wr = &ws[h][j][q * 4];
-                wr[0] = wv[i].x; wr[1] = wv[i].y; wr[2] = wv[i].z; wr[3] = wv[i].w;
-            }
-        }
-    };
+template <int HC>
+struct Gmm {
+    static constexpr int M = (2 + HC) * HC;          // mixes per token
+    static constexpr int CT = (M + 15) / 16;         // 16-column MFMA tiles
+    static constexpr int F = M + 2;                  // partial fields: the M dots, sum of squares, scaled sum
+};
 
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int64_t t0 = tile * kGT;
-        // acc / sacc: the even steps (H = 2: this group's steps); acc1 /
-        // sacc1: the odd steps (H = 1 only)
-        double acc[TT][JJ], acc1[TT][JJ];
+// LDS of a k_gmm workgroup of T tokens.  a: the chunk of each token row,
+// padded to 72 elements (144 bytes) so the 16 rows of an MFMA operand read
+// fall on distinct banks; b: the weight pieces as MFMA B fragments,
+// [k-step][piece][column tile][lane] of 8 bf16 (columns past M stay zero).
+template <int HC, int T>
+struct GmmLds {
+    bf16x8 b[2][2][3][Gmm<HC>::CT][64];
+    uint16_t a[2][T][kKC + 8];
+    float ssb[T][2];
+};
+
+// Chunk ch of the reduction axis for this workgroup's tokens t0..t0+T-1,
+// loaded into registers (zeros past n and past K): residual pieces of 8
+// elements (token, 16-byte piece) and weight pieces of 4 (row j, 4 floats).
+template <int HC, int T>
+struct GmmRegs {
+    static constexpr int kA = (T * (kKC / 8) + 2 * T - 1) / (2 * T);      // residual pieces per thread
+    static constexpr int kW = (Gmm<HC>::M * (kKC / 4) + 2 * T - 1) / (2 * T);   // weight pieces per thread
+    uint4 a[kA];
+    float4 w[kW];
+};
+
+template <int HC, int T>
+__device__ __forceinline__ void gmm_load(GmmRegs<HC, T>& g, const uint16_t* __restrict__ R,
+                                         const float* __restrict__ W, int64_t t0, int64_t n, int64_t K, int64_t ch) {
+    constexpr int M = Gmm<HC>::M;
+    const int tid = threadIdx.x;
 #pragma unroll
-        for (int i = 0; i < TT; ++i)
+    for (int i = 0; i < GmmRegs<HC, T>::kA; ++i) {
+        const int p = i * 2 * T + tid;                  // piece p: token p / 8, elements 8 (p % 8) of the chunk
+        const int tk = p >> 3;
+        const int64_t k = ch * kKC + 8 * (p & 7);
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (p < T * 8 && t0 + tk < n && k < K) v = *reinterpret_cast<const uint4*>(R + (t0 + tk) * K + k);
+        g.a[i] = v;
+    }
 #pragma unroll
-            for (int u = 0; u < JJ; ++u) acc[i][u] = acc1[i][u] = 0.0;
-        double sacc = 0.0, sacc1 = 0.0;
-        // one staged step into the accumulators a / sa
-        auto step = [&](double (&a)[TT][JJ], double& sa) {
-            if (tid < NW) {
-                const float* xr[TT];
-                const float* wr[JJ];
-#pragma unroll
-                for (int i = 0; i < TT; ++i) xr[i] = xs[h][tg + NT * i];
-#pragma unroll
-                for (int u = 0; u < JJ; ++u) wr[u] = ws[h][jg * JJ + u < M ? jg * JJ + u : M - 1];
-#pragma unroll 8
-                for (int k = 0; k < kGKC; ++k) {
-                    double xk[TT], wk[JJ];
-#pragma unroll
-                    for (int i = 0; i < TT; ++i) xk[i] = xr[i][k];
-#pragma unroll
-                    for (int u = 0; u < JJ; ++u) wk[u] = wr[u][k];
-#pragma unroll
-                    for (int i = 0; i < TT; ++i)
-#pragma unroll
-                        for (int u = 0; u < JJ; ++u) a[i][u] = __builtin_fma(xk[i], wk[u], a[i][u]);
-                }
-            } else if (st < kGT) {
-#pragma unroll 16
-                for (int k = 0; k < kGKC; ++k) {
-                    const double v = xs[h][st][k];
-                    sa = __builtin_fma(v, v, sa);
-                }
-            }
-        };
-        uint4 xv;
-        float4 wv[WPT];
-        load(t0, h * kGKC, xv, wv);
-        bool odd = false;
-        for (int64_t k0 = 0; k0 < K; k0 += H * kGKC) {
-            const int64_t kh = k0 + h * kGKC;    // this group's step
-            stage(xv, wv);
-            __syncthreads();
-            // always: past K it stages zeros (with an odd step count group 1
-            // runs one step more than it has data for)
-            load(t0, kh + H * kGKC, xv, wv);
-            if (H == 1 && odd)
-                step(acc1, sacc1);
-            else
-                step(acc, sacc);
-            odd = !odd;
-            __syncthreads();
-        }
-        if (H == 1) {
-            // the odd steps' sums in the place of group 1's (red / sred)
-#pragma unroll
-            for (int i = 0; i < TT; ++i)
-#pragma unroll
-                for (int u = 0; u < JJ; ++u) acc[i][u] = acc[i][u] + acc1[i][u];
-            sacc = sacc + sacc1;
-        }
-        if (H == 2 && h == 1) {
-            if (tid < NW) {
-#pragma unroll
-                for (int i = 0; i < TT; ++i)
-#pragma unroll
-                    for (int u = 0; u < JJ; ++u) red[tid][i * JJ + u] = acc[i][u];
-            } else if (st < kGT) {
-                sred[st] = sacc;
-            }
-        }
-        __syncthreads();
-        if (h == 0 && st >= 0 && st < kGT) ssq[st] = H == 2 ? sacc + sred[st] : sacc;
-        __syncthreads();
-        if (h == 0 && tid < NW) {
-#pragma unroll
-            for (int i = 0; i < TT; ++i) {
-                const int t = tg + NT * i;
-                if (t0 + t >= n) continue;
-                const double r = 1.0 / __builtin_sqrt(ssq[t] / (double)K + (double)norm_eps);
-#pragma unroll
-                for (int u = 0; u < JJ; ++u) {
-                    const int j = jg * JJ + u;
-                    const double sum = H == 2 ? acc[i][u] + red[tid][i * JJ + u] : acc[i][u];
-                    if (j < M) mixes[(t0 + t) * M + j] = (float)(sum * r);
-                }
-            }
-        }
-        __syncthreads();        // the staged tiles, red and ssq are rewritten by the next tile
+    for (int i = 0; i < GmmRegs<HC, T>::kW; ++i) {
+        const int p = i * 2 * T + tid;                  // piece p: row p / 16, elements 4 (p % 16) of the chunk
+        const int j = p >> 4;
+        const int64_t k = ch * kKC + 4 * (p & 15);
+        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (j < M && k < K) v = *reinterpret_cast<const float4*>(W + (int64_t)j * K + k);
+        g.w[i] = v;
     }
 }
 
-// The same projection for few outputs ((2 + hc) * hc < 48): every
-// (token, output) pair, the sum of squares counted as output M, belongs to
-// one thread, so that all 256 threads share the products; the staging and
-// its prefetch are those of k_gmix.
-template <int HC>
-__global__ __launch_bounds__(kGThreads) void k_gmix_pairs(const uint16_t* __restrict__ R,
-                                                          const float* __restrict__ W, float* __restrict__ mixes,
-                                                          int64_t n, int d, float norm_eps) {
-    constexpr int M = (2 + HC) * HC;
-    constexpr int NP = kGT * (M + 1);
-    constexpr int PPT = (NP + kGThreads - 1) / kGThreads;
-    constexpr int WCH = M * (kGKC / 4);
-    constexpr int WPT = (WCH + kGThreads - 1) / kGThreads;
-    __shared__ float xs[kGT][kGKC + 1];
-    __shared__ float ws[M][kGKC + 1];
-    __shared__ double ssq[kGT];
-    const int64_t K = (int64_t)HC * d;
-    const int64_t ntiles = (n + kGT - 1) / kGT;
+// The loaded chunk into LDS buffer q: residual rows as they are, weights
+// split into their three exact bf16 pieces in B-fragment order.
+template <int HC, int T>
+__device__ __forceinline__ void gmm_store(const GmmRegs<HC, T>& g, GmmLds<HC, T>& L, int q) {
+    constexpr int M = Gmm<HC>::M;
     const int tid = threadIdx.x;
-    const int xt = tid >> 3, xq = tid & 7;
-
-    auto load = [&](int64_t t0, int64_t k0, uint4& xv, float4 (&wv)[WPT]) {
-        const int64_t k = k0 + xq * 8;
-        xv = make_uint4(0u, 0u, 0u, 0u);
-        if (t0 + xt < n && k < K) xv = *reinterpret_cast<const uint4*>(R + (t0 + xt) * K + k);
 #pragma unroll
-        for (int i = 0; i < WPT; ++i) {
-            const int c = tid + i * kGThreads;
-            const int j = c / (kGKC / 4), q = c - j * (kGKC / 4);
-            const int64_t kk = k0 + q * 4;
-            wv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (c < WCH && kk < K) wv[i] = *reinterpret_cast<const float4*>(W + (int64_t)j * K + kk);
-        }
-    };
-    auto stage = [&](const uint4& xv, const float4 (&wv)[WPT]) {
-        float* xr = &xs[xt][xq * 8];
-        xr[0] = bf_lo(xv.x); xr[1] = bf_hi(xv.x);
-        xr[2] = bf_lo(xv.y); xr[3] = bf_hi(xv.y);
-        xr[4] = bf_lo(xv.z); xr[5] = bf_hi(xv.z);
-        xr[6] = bf_lo(xv.w); xr[7] = bf_hi(xv.w);
+    for (int i = 0; i < GmmRegs<HC, T>::kA; ++i) {
+        const int p = i * 2 * T + tid;
+        if (p < T * 8) *reinterpret_cast<uint4*>(&L.a[q][p >> 3][8 * (p & 7)]) = g.a[i];
+    }
 #pragma unroll
-        for (int i = 0; i < WPT; ++i) {
-            const int c = tid + i * kGThreads;
-            if (c < WCH) {
-                const int j = c / (kGKC / 4), q = c - j * (kGKC / 4);
-                float* wr = &ws[j][q * 4];
-                wr[0] = wv[i].x; wr[1] = wv[i].y; wr[2] = wv[i].z; wr[3] = wv[i].w;
+    for (int i = 0; i < GmmRegs<HC, T>::kW; ++i) {
+        const int p = i * 2 * T + tid;
+        const int j = p >> 4;
+        if (j >= M) continue;
+        const int kc = 4 * (p & 15);                   // element of the chunk
+        const int st = kc >> 5, kk = kc & 31, grp = kk >> 3, e0 = kk & 7;
+        const int ct = j >> 4, lane = (j & 15) + 16 * grp;
+        const float x[4] = {g.w[i].x, g.w[i].y, g.w[i].z, g.w[i].w};
+        uint32_t pc[3][2];
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+            uint32_t hw[3][2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const float v = x[e + u];
+                const __bf16 hi = (__bf16)v;
+                const float r1 = v - (float)hi;
+                const __bf16 mid = (__bf16)r1;
+                const __bf16 lo = (__bf16)(r1 - (float)mid);
+                hw[0][u] = (uint32_t)__builtin_bit_cast(uint16_t, hi);
+                hw[1][u] = (uint32_t)__builtin_bit_cast(uint16_t, mid);
+                hw[2][u] = (uint32_t)__builtin_bit_cast(uint16_t, lo);
             }
+#pragma unroll
+            for (int pc_ = 0; pc_ < 3; ++pc_) pc[pc_][e >> 1] = pack2(hw[pc_][0], hw[pc_][1]);
         }
-    };
+#pragma unroll
+        for (int pc_ = 0; pc_ < 3; ++pc_)
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(&L.b[q][st][pc_][ct][lane]) + e0) =
+                u32x2{pc[pc_][0], pc[pc_][1]};
+    }
+}
 
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int64_t t0 = tile * kGT;
-        double acc[PPT];
+// Per-wave sums of one 32-token slice: tt = 16-token MFMA tile.
+template <int HC>
+struct GmmAcc {
+    f32x4 dot[2][Gmm<HC>::CT];
+    f32x4 sq[2], sb[2];
+};
+
+template <int HC>
+__device__ __forceinline__ void gmm_zero(GmmAcc<HC>& A) {
 #pragma unroll
-        for (int p = 0; p < PPT; ++p) acc[p] = 0.0;
-        uint4 xv;
-        float4 wv[WPT];
-        load(t0, 0, xv, wv);
-        for (int64_t k0 = 0; k0 < K; k0 += kGKC) {
-            stage(xv, wv);
-            __syncthreads();
-            if (k0 + kGKC < K) load(t0, k0 + kGKC, xv, wv);
+    for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-            for (int p = 0; p < PPT; ++p) {
-                const int pair = tid + p * kGThreads;
-                if (pair < NP) {
-                    const int t = pair / (M + 1), j = pair - t * (M + 1);
-                    const float* xr = xs[t];
-                    const float* wr = j < M ? ws[j] : xs[t];
-                    double a = acc[p];
-#pragma unroll 16
-                    for (int k = 0; k < kGKC; ++k) a = __builtin_fma((double)xr[k], (double)wr[k], a);
-                    acc[p] = a;
+        for (int ct = 0; ct < Gmm<HC>::CT; ++ct) A.dot[tt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        A.sq[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        A.sb[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+}
+
+// Products of LDS buffer q for this wave's 32 tokens: per k-step, each
+// column tile takes the hi, mid and lo pieces into one accumulator, and
+// the operand against itself gives the sums of squares on the diagonal.
+template <int HC, int T>
+__device__ __forceinline__ void gmm_mma(GmmAcc<HC>& A, const GmmLds<HC, T>& L, int q) {
+    const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int row = l & 15, grp = l >> 4;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        bf16x8 ab[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const u32x4 av = *reinterpret_cast<const u32x4*>(&L.a[q][32 * wv + 16 * tt + row][32 * st + 8 * grp]);
+            ab[tt] = __builtin_bit_cast(bf16x8, av);
+            A.sq[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab[tt], ab[tt], A.sq[tt], 0, 0, 0);
+            const u32x4 as = u32x4{scaled_x2(av[0]), scaled_x2(av[1]), scaled_x2(av[2]), scaled_x2(av[3])};
+            const bf16x8 sbf = __builtin_bit_cast(bf16x8, as);
+            A.sb[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sbf, sbf, A.sb[tt], 0, 0, 0);
+        }
+        // each weight fragment is read once for both 16-token tiles (LDS
+        // bandwidth, not the matrix cores, bounds this loop at many outputs)
+#pragma unroll
+        for (int ct = 0; ct < Gmm<HC>::CT; ++ct)
+#pragma unroll
+            for (int pc = 0; pc < 3; ++pc) {
+                const bf16x8 b = L.b[q][st][pc][ct][l];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+                    A.dot[tt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab[tt], b, A.dot[tt][ct], 0, 0, 0);
+            }
+        // one k-step's fragments at a time: loaded further ahead they
+        // would take the registers of the sums
+        asm volatile("" ::: "memory");
+    }
+}
+
+// One workgroup: token tile blockIdx.x / G, segments sg * (kSeg / G) ..
+// (sg + 1) * (kSeg / G) - 1 with sg = blockIdx.x % G (G = 1 or kSeg).
+// Segment s covers chunks s*C/kSeg .. (s+1)*C/kSeg - 1 (C = chunks of K);
+// its sums start from zero and are added to the previous segments' total in
+// order.  G = 1: the totals give the mixes here.  G = kSeg: each segment's
+// sums go to part[t][s][F] (the dots, then the two sums of squares), and
+// k_gred adds them in the same order.
+template <int HC, int T>
+__global__ __launch_bounds__(2 * T) void k_gmm(const uint16_t* __restrict__ R, const float* __restrict__ W,
+                                               float* __restrict__ mixes, float* __restrict__ part, int64_t n, int d,
+                                               int G, float norm_eps) {
+    constexpr int M = Gmm<HC>::M, CT = Gmm<HC>::CT, F = Gmm<HC>::F;
+    __shared__ __attribute__((aligned(16))) GmmLds<HC, T> L;
+    const int64_t K = (int64_t)HC * d;
+    const int64_t C = (K + kKC - 1) / kKC;
+    const int64_t tile = blockIdx.x / G;
+    const int sg = (int)(blockIdx.x - tile * G);
+    const int per = kSeg / G;
+    const int64_t t0 = tile * T;
+    const int l = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    // the padding columns of the weight fragments stay zero
+    for (int i = threadIdx.x; i < (int)(sizeof(L.b) / 16); i += 2 * T)
+        reinterpret_cast<uint4*>(&L.b[0][0][0][0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+
+    GmmAcc<HC> tot, seg;
+    gmm_zero<HC>(tot);
+    gmm_zero<HC>(seg);
+    const int s0 = sg * per, s1 = s0 + per;
+    const int64_t c0 = s0 * C / kSeg, c1 = s1 * C / kSeg;
+    // chunks in flight: kPD register sets, chunk c in set (c - c0) % kPD,
+    // each loaded kPD - 1 chunks ahead of its turn in LDS
+    constexpr int kPD = Gmm<HC>::M > 48 ? 2 : 3;
+    GmmRegs<HC, T> g[kPD];
+    int s = s0;
+    int64_t send = (int64_t)(s + 1) * C / kSeg;        // first chunk past segment s
+#pragma unroll
+    for (int i = 0; i < kPD; ++i)
+        if (c0 + i < c1) gmm_load<HC, T>(g[i], R, W, t0, n, K, c0 + i);
+    if (c0 < c1) gmm_store<HC, T>(g[0], L, 0);
+    __syncthreads();
+    auto close = [&]() {
+        // segment s complete: into the total (or the partial sums)
+        if (G == 1) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) tot.dot[tt][ct] = s == 0 ? seg.dot[tt][ct] : tot.dot[tt][ct] + seg.dot[tt][ct];
+                tot.sq[tt] = s == 0 ? seg.sq[tt] : tot.sq[tt] + seg.sq[tt];
+                tot.sb[tt] = s == 0 ? seg.sb[tt] : tot.sb[tt] + seg.sb[tt];
+            }
+        } else {
+            const int row = l & 15, grp = l >> 4;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t t = t0 + 32 * wv + 16 * tt + 4 * grp + r;
+                    float* pt = part + (t * kSeg + s) * F;
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+                        if (t < n && 16 * ct + row < M) pt[16 * ct + row] = seg.dot[tt][ct][r];
+                    // the diagonal of A A^T: token 4 grp + r of the tile is row == 4 grp + r
+                    if (t < n && row == 4 * grp + r) {
+                        pt[M] = seg.sq[tt][r];
+                        pt[M + 1] = seg.sb[tt][r];
+                    }
                 }
-            }
-            __syncthreads();
         }
-#pragma unroll
-        for (int p = 0; p < PPT; ++p) {
-            const int pair = tid + p * kGThreads;
-            const int t = pair / (M + 1), j = pair - t * (M + 1);
-            if (pair < NP && j == M) ssq[t] = acc[p];
+        gmm_zero<HC>(seg);
+    };
+    // empty segments before the first chunk (short axes)
+    while (s < s1 && send <= c0) {
+        close();
+        ++s;
+        send = (int64_t)(s + 1) * C / kSeg;
+    }
+    // chunk ch (in set I): its products from LDS buffer (ch - c0) & 1,
+    // then chunk ch + 1 (set I + 1) into the other buffer, and set I
+    // refilled with chunk ch + kPD
+    auto step = [&](int64_t ch, auto I) {
+        constexpr int i = decltype(I)::value;
+        const int q = (int)((ch - c0) & 1);
+        gmm_mma<HC, T>(seg, L, q);
+        // segments that end here (and empty ones after them)
+        while (s < s1 && send <= ch + 1) {
+            close();
+            ++s;
+            send = (int64_t)(s + 1) * C / kSeg;
         }
+        if (ch + 1 < c1) gmm_store<HC, T>(g[(i + 1) % kPD], L, q ^ 1);
+        if (ch + kPD < c1) gmm_load<HC, T>(g[i], R, W, t0, n, K, ch + kPD);
         __syncthreads();
+    };
+    for (int64_t ch = c0; ch < c1; ch += kPD) {
+        step(ch, std::integral_constant<int, 0>{});
+        if (ch + 1 < c1) step(ch + 1, std::integral_constant<int, 1>{});
+        if constexpr (kPD > 2)
+            if (ch + 2 < c1) step(ch + 2, std::integral_constant<int, 2>{});
+    }
+    while (s < s1) {            // empty segments at the end
+        close();
+        ++s;
+    }
+    if (G != 1) return;
+    // the mixes of this wave's 32 tokens: sums of squares from the diagonal
+    const int row = l & 15, grp = l >> 4;
 #pragma unroll
-        for (int p = 0; p < PPT; ++p) {
-            const int pair = tid + p * kGThreads;
-            const int t = pair / (M + 1), j = pair - t * (M + 1);
-            if (pair < NP && j < M && t0 + t < n) {
-                const double r = 1.0 / __builtin_sqrt(ssq[t] / (double)K + (double)norm_eps);
-                mixes[(t0 + t) * M + j] = (float)(acc[p] * r);
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (row == 4 * grp + r) {
+                L.ssb[32 * wv + 16 * tt + row][0] = tot.sq[tt][r];
+                L.ssb[32 * wv + 16 * tt + row][1] = tot.sb[tt][r];
             }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");     // the wave reads back its own LDS writes
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tl = 32 * wv + 16 * tt + 4 * grp + r;
+            const int64_t t = t0 + tl;
+            const MixScale ms = mix_scale(L.ssb[tl][0], L.ssb[tl][1], (float)K, norm_eps);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                if (t < n && 16 * ct + row < M) mixes[t * M + 16 * ct + row] = mix_value(tot.dot[tt][ct][r], ms);
         }
-        __syncthreads();        // ssq and the staged tiles are rewritten by the next tile
+}
+
+// The partial sums of k_gmm's segments, added in segment order (the order
+// of a workgroup that takes them all), then the mixes.  One thread per token.
+template <int HC>
+__global__ __launch_bounds__(kGThreads) void k_gred(const float* __restrict__ part, float* __restrict__ mixes,
+                                                    int64_t n, float K, float norm_eps) {
+    constexpr int M = Gmm<HC>::M, F = Gmm<HC>::F;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += stride) {
+        const float* p = part + t * kSeg * F;
+        float acc[F];
+#pragma unroll
+        for (int f = 0; f < F; ++f) acc[f] = p[f];
+        for (int s = 1; s < kSeg; ++s)
+#pragma unroll
+            for (int f = 0; f < F; ++f) acc[f] = acc[f] + p[s * F + f];
+        const MixScale ms = mix_scale(acc[M], acc[M + 1], K, norm_eps);
+#pragma unroll
+        for (int j = 0; j < M; ++j) mixes[t * M + j] = mix_value(acc[j], ms);
     }
 }
 
@@ -407,32 +439,54 @@ __device__ __forceinline__ uint4 pack8(const uint32_t (&o)[8]) {
     return make_uint4(pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7]));
 }
 
-// hc_pre of the "Mix projection" page: h_c = bf16(sum_k pre_k R_{k,c}).
+// hc_pre of the "Mix projection" page: h_c = bf16(sum_k pre_k R_{k,c}),
+// summed in double in stream order and rounded once (the float fast path
+// of f32_mid, redone with bf16_rn_f64 by a wave in which any lane hit a
+// float halfway point: the same bits either way).  Streaming accesses are
+// non-temporal; a wave's 64 chunks share one token when 8 * 64 divides d,
+// and its pre then comes through scalar loads.
 template <int HC>
 __global__ __launch_bounds__(kGThreads) void k_gpre(const uint16_t* __restrict__ R, const float* __restrict__ pre,
                                                     uint16_t* __restrict__ h, int64_t n, int d) {
     const int cpt = d / 8;
+    const bool uniform = cpt % 64 == 0;
     const int64_t items = n * cpt;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items; it += stride) {
-        const int64_t t = it / cpt;
+        int64_t t = it / cpt;
+        if (uniform)
+            t = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)t) |
+                ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)t >> 32)) << 32);
         const int c0 = (int)(it - t * cpt) * 8;
-        uint4 r[HC];
+        u32x4 r[HC];
         double p[HC];
 #pragma unroll
         for (int k = 0; k < HC; ++k) {
-            r[k] = *reinterpret_cast<const uint4*>(R + (t * HC + k) * d + c0);
+            r[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(R + (t * HC + k) * d + c0));
             p[k] = pre[t * HC + k];
         }
-        uint32_t o[8];
+        auto sum = [&](int w, int e) {
+            double y = p[0] * (double)(e ? bf_hi(r[0][w]) : bf_lo(r[0][w]));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            double y = p[0] * bf_at(r[0], e);
+            for (int k = 1; k < HC; ++k) y = __builtin_fma(p[k], (double)(e ? bf_hi(r[k][w]) : bf_lo(r[k][w])), y);
+            return y;
+        };
+        float f[4][2];
+        bool mid = false;
 #pragma unroll
-            for (int k = 1; k < HC; ++k) y = __builtin_fma(p[k], bf_at(r[k], e), y);
-            o[e] = bf16_rn_f64(y);
+        for (int w = 0; w < 4; ++w) {
+            f[w][0] = f32_mid(sum(w, 0), mid);
+            f[w][1] = f32_mid(sum(w, 1), mid);
         }
-        *reinterpret_cast<uint4*>(h + t * d + c0) = pack8(o);
+        u32x4 out;
+        if (__builtin_amdgcn_ballot_w64(mid)) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) out[w] = pack2(bf16_rn_f64(sum(w, 0)), bf16_rn_f64(sum(w, 1)));
+        } else {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) out[w] = bf16x2_rn(f[w][0], f[w][1]);
+        }
+        __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(h + t * d + c0));
     }
 }
 
@@ -472,75 +526,6 @@ __global__ __launch_bounds__(kGThreads) void k_gpost(const uint16_t* __restrict_
     }
 }
 
-// The projection for few outputs ((2 + hc) * hc < 48): one wave per TW
-// tokens.  Lane l takes the 8-feature chunks l, l + 64, ... of the
-// flattened stream and keeps, for each of its tokens, every output's
-// partial sum (and the sum of squares) in double, in chunk order; a
-// butterfly over the wave then adds the 64 partials in one fixed order, so
-// that every lane holds the same total and results do not depend on n.
-// The weights are read from memory (L2) once per TW tokens.
-template <int HC>
-__global__ __launch_bounds__(kGThreads) void k_gmix_wave(const uint16_t* __restrict__ R,
-                                                         const float* __restrict__ W, float* __restrict__ mixes,
-                                                         int64_t n, int d, float norm_eps) {
-    constexpr int M = (2 + HC) * HC;
-    constexpr int TW = M <= 15 ? 4 : 2;          // tokens per wave (register budget of the sums)
-    constexpr int WAVES = kGThreads / 64;
-    const int64_t K = (int64_t)HC * d;
-    const int64_t nch = K / 8;
-    const int lane = threadIdx.x & 63;
-    const int64_t groups = (n + TW - 1) / TW;
-    const int64_t stride = (int64_t)gridDim.x * WAVES;
-    for (int64_t g = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6); g < groups; g += stride) {
-        const int64_t t0 = g * TW;
-        double acc[TW][M + 1];
-#pragma unroll
-        for (int i = 0; i < TW; ++i)
-#pragma unroll
-            for (int j = 0; j <= M; ++j) acc[i][j] = 0.0;
-        for (int64_t c = lane; c < nch; c += 64) {
-            double x[TW][8];
-#pragma unroll
-            for (int i = 0; i < TW; ++i) {
-                uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                if (t0 + i < n) v = *reinterpret_cast<const uint4*>(R + (t0 + i) * K + c * 8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    x[i][e] = bf_at(v, e);
-                    acc[i][M] = __builtin_fma(x[i][e], x[i][e], acc[i][M]);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < M; ++j) {
-                const float4 w0 = *reinterpret_cast<const float4*>(W + (int64_t)j * K + c * 8);
-                const float4 w1 = *reinterpret_cast<const float4*>(W + (int64_t)j * K + c * 8 + 4);
-                const double wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-                for (int i = 0; i < TW; ++i)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[i][j] = __builtin_fma(x[i][e], wv[e], acc[i][j]);
-            }
-        }
-        // lane l and lane l ^ o add the same two values, so every lane ends
-        // with the same bits
-#pragma unroll
-        for (int i = 0; i < TW; ++i)
-#pragma unroll
-            for (int j = 0; j <= M; ++j)
-#pragma unroll
-                for (int o = 32; o >= 1; o >>= 1) acc[i][j] += __shfl_xor(acc[i][j], o);
-#pragma unroll
-        for (int i = 0; i < TW; ++i) {
-            if (t0 + i >= n) break;
-            const double r = 1.0 / __builtin_sqrt(acc[i][M] / (double)K + (double)norm_eps);
-            double v = 0.0;
-#pragma unroll
-            for (int j = 0; j < M; ++j) v = lane == j ? acc[i][j] : v;
-            if (lane < M) mixes[(t0 + i) * M + lane] = (float)(v * r);
-        }
-    }
-}
-
 int grid_for(int64_t items) {
     const int64_t cap = (int64_t)num_cus() * 8;
     const int64_t need = (items + kGThreads - 1) / kGThreads;
@@ -561,42 +546,53 @@ int dispatch_hc(int hc_, A... args) {
     }
 }
 
+// Bytes of k_gmm's per-segment partial sums for n tokens.
 template <int HC>
-int wave_grid(int64_t n) {
-    constexpr int M = (2 + HC) * HC;
-    constexpr int TW = M <= 15 ? 4 : 2;
-    const int64_t groups = (n + TW - 1) / TW, per = kGThreads / 64;
-    const int64_t need = (groups + per - 1) / per, cap = (int64_t)num_cus() * 16;
-    return (int)(need < cap ? need : cap);
+size_t gmm_part_bytes(int64_t n) { return align256((size_t)n * kSeg * Gmm<HC>::F * 4); }
+
+template <int HC, int T>
+int gmm_launch(const void* R, const float* W, float* mixes, float* part, int64_t n, int d, int G, float norm_eps,
+               hipStream_t s) {
+    const int64_t tiles = (n + T - 1) / T;
+    hipLaunchKernelGGL((k_gmm<HC, T>), dim3((unsigned)(tiles * G)), dim3(2 * T), 0, s,
+                       static_cast<const uint16_t*>(R), W, mixes, part, n, d, G, norm_eps);
+    if (hipGetLastError() != hipSuccess) return -1;
+    if (G != 1) {
+        hipLaunchKernelGGL(k_gred<HC>, dim3(grid_for(n)), dim3(kGThreads), 0, s, part, mixes, n,
+                           (float)((int64_t)HC * d), norm_eps);
+        if (hipGetLastError() != hipSuccess) return -1;
+    }
+    return 0;
 }
 
+// The projection.  Tiles of 256 tokens while they fill the compute units
+// on their own; shorter calls take smaller tiles, and with a workspace for
+// the partial sums (part) one workgroup per segment as well.  Every choice
+// gives the same bits.
 template <int HC>
 struct MixOp {
-    static int run(const void* R, const float* W, float* mixes, int64_t n, int d, float norm_eps, hipStream_t s) {
-        const int64_t tiles = (n + kGT - 1) / kGT, cap = (int64_t)num_cus() * 16;
-        constexpr int M = (2 + HC) * HC;
-        const dim3 grid((unsigned)(tiles < cap ? tiles : cap));
-        if constexpr (M >= kGTileMinM) {
-            // two groups per tile while fewer than two tiles per compute unit
-            // (measured at d = 5120, 4,096 tokens: hc = 6 2,064 against
-            // 2,840 us, hc = 8 2,840 against 3,799; at 65,536 tokens one group
-            // is faster: 12,020 against 17,198 and 19,477 against 23,707)
-            const auto two = k_gmix<HC, 2>;
-            const auto one = k_gmix<HC, 1>;
-            if (tiles < 2 * (int64_t)num_cus())
-                hipLaunchKernelGGL(two, grid, dim3(2 * kGThreads), 0, s, static_cast<const uint16_t*>(R), W, mixes,
-                                   n, d, norm_eps);
-            else
-                hipLaunchKernelGGL(one, grid, dim3(kGThreads), 0, s, static_cast<const uint16_t*>(R), W, mixes, n,
-                                   d, norm_eps);
-        }
-        else if (M <= kGWaveMaxM)
-            hipLaunchKernelGGL(k_gmix_wave<HC>, dim3(wave_grid<HC>(n)), dim3(kGThreads), 0, s,
-                               static_cast<const uint16_t*>(R), W, mixes, n, d, norm_eps);
-        else
-            hipLaunchKernelGGL(k_gmix_pairs<HC>, grid, dim3(kGThreads), 0, s, static_cast<const uint16_t*>(R), W,
-                               mixes, n, d, norm_eps);
-        return hipGetLastError() == hipSuccess ? 0 : -1;
+    static int run(const void* R, const float* W, float* mixes, float* part, int64_t n, int d, float norm_eps,
+                   hipStream_t s) {
+        const int64_t cus = num_cus();
+        const int G = (part && (n + 255) / 256 < cus) ? kSeg : 1;
+        const int64_t want = G == 1 ? cus : (cus + kSeg - 1) / kSeg;      // tiles that fill the chip
+        // smallest tile: the weight chunk (M x 64 floats) spread over its
+        // threads stays within 8 loads each
+        constexpr int M = Gmm<HC>::M;
+        if ((n + 255) / 256 >= want) return gmm_launch<HC, 256>(R, W, mixes, part, n, d, G, norm_eps, s);
+        if constexpr (M > 48) return gmm_launch<HC, 128>(R, W, mixes, part, n, d, G, norm_eps, s);
+        if ((n + 127) / 128 >= want) return gmm_launch<HC, 128>(R, W, mixes, part, n, d, G, norm_eps, s);
+        if constexpr (M > 16) return gmm_launch<HC, 64>(R, W, mixes, part, n, d, G, norm_eps, s);
+        if ((n + 63) / 64 >= want) return gmm_launch<HC, 64>(R, W, mixes, part, n, d, G, norm_eps, s);
+        return gmm_launch<HC, 32>(R, W, mixes, part, n, d, G, norm_eps, s);
+    }
+};
+
+template <int HC>
+struct PartOp {
+    static int run(int64_t n, size_t* out) {
+        *out = gmm_part_bytes<HC>(n);
+        return 0;
     }
 };
 
@@ -634,7 +630,7 @@ struct PostOp {
 
 int launch_gen_mixes(const void* R, const float* W, float* mixes, int64_t n, int hc_, int d, float norm_eps,
                      hipStream_t s) {
-    return dispatch_hc<MixOp>(hc_, R, W, mixes, n, d, norm_eps, s);
+    return dispatch_hc<MixOp>(hc_, R, W, mixes, (float*)nullptr, n, d, norm_eps, s);
 }
 
 int launch_gen_split(const float* mixes, const float* scale, const float* base, float* pre, float* post,
@@ -654,15 +650,22 @@ int launch_gen_post(const void* x, const void* R, const float* post, const float
 int launch_gen_fused(const void* R, const float* W, const float* scale, const float* base, void* h, float* pre,
                      float* post, float* comb, float* mixes, void* ws, int64_t n, int hc_, int d, int iters,
                      float eps, float norm_eps, hipStream_t s) {
-    // what this call keeps in the workspace starts at offset 0, so that the
-    // four-stream kernels' header (its first 256 bytes) is overwritten and a
-    // later four-stream call on the same workspace takes it as fresh
-    // (clearing its record area) rather than trusting stale contents
+    // the workspace holds the projection's partial sums, then the mixes and
+    // pre when the caller does not keep them, each from offset 0 on, so
+    // that a four-stream call's header (its first 256 bytes) is always
+    // overwritten and a later four-stream call on the same workspace takes
+    // it as fresh (clearing its record area) rather than trusting stale
+    // contents
     const size_t M = (size_t)(2 + hc_) * hc_;
     char* w = static_cast<char*>(ws);
-    float* mx = mixes ? mixes : reinterpret_cast<float*>(w);
-    float* pr = pre ? pre : reinterpret_cast<float*>(w + (mixes ? 0 : align256((size_t)n * M * 4)));
-    if (launch_gen_mixes(R, W, mx, n, hc_, d, norm_eps, s)) return -1;
+    size_t pb = 0;
+    if (dispatch_hc<PartOp>(hc_, n, &pb)) return -1;
+    float* part = reinterpret_cast<float*>(w);
+    size_t off = pb;
+    float* mx = mixes ? mixes : reinterpret_cast<float*>(w + off);
+    if (!mixes) off += align256((size_t)n * M * 4);
+    float* pr = pre ? pre : reinterpret_cast<float*>(w + off);
+    if (dispatch_hc<MixOp>(hc_, R, W, mx, part, n, d, norm_eps, s)) return -1;
     if (launch_gen_split(mx, scale, base, pr, post, comb, n, hc_, iters, eps, s)) return -1;
     return launch_gen_pre(R, pr, h, n, hc_, d, s);
 }

@@ -43,18 +43,17 @@
  * [hc,2hc) post logits and [2hc,M) comb logits at 2hc + j*hc + k), as the
  * split + Sinkhorn listing of the "Reading weights" page and the mix
  * formula of the "Mix projection" page are written for any hc.  hc = 4 runs
- * the tuned kernels each entry point describes.  Every other count runs
- * plain kernels: the projection in double (each (token, output) sum taken
- * in one fixed order per stream count, whatever the call's size: over the
- * features in order at hc = 5, as 64 per-lane partial sums added in one
- * fixed order at hc = 1..3, as (even 64-feature steps) + (odd steps) at
- * hc >= 6), then the split +
- * Sinkhorn with the four-stream arithmetic, then hc_pre / hc_post rounded
- * once as below.
+ * the tuned kernels each entry point describes.  Every other count runs the
+ * projection on the matrix cores: tiles of tokens over the whole flattened
+ * stream, the fp32 weights split exactly into three bf16 pieces so every
+ * product is that of fp32 arithmetic, fp32 sums over 8 fixed segments of
+ * the reduction axis added in order (so a token's mixes do not depend on
+ * the size of its call); then the split + Sinkhorn with the four-stream
+ * arithmetic, then hc_pre / hc_post rounded once as below.
  * There the projection needs only d % 8 == 0, hc_mixes uses no workspace
- * (it may be NULL), and the fused calls' workspace holds the mixes and pre
- * of every token (hc_fused_workspace_bytes).  The packed-weight calls take
- * hc = 4 only.
+ * (it may be NULL), and the fused calls' workspace holds the projection's
+ * per-segment partial sums and the mixes and pre of every token
+ * (hc_fused_workspace_bytes).  The packed-weight calls take hc = 4 only.
  *
  * Ownership: the caller owns every buffer.  The library never allocates,
  * frees or synchronises; each call enqueues its kernels on `stream` (a

@@ -74,8 +74,10 @@ def test_summarize_trace_general_stream_count(tmp_path, monkeypatch):
     tdir.mkdir()
     # two warmup dispatches, then two timed ones of each kernel
     _write_trace(str(tdir), {
-        "void hc::(anonymous namespace)::k_gmix_wave<2>(unsigned short const*, float const*, float*, long, int, float)":
-            [90_000, 90_000, 40_000, 40_000],
+        "void hc::(anonymous namespace)::k_gmm<2, 128>(unsigned short const*, float const*, float*, float*, long, int, int, float)":
+            [90_000, 90_000, 30_000, 30_000],
+        "void hc::(anonymous namespace)::k_gred<2>(float const*, float*, long, float, float)":
+            [10_000, 10_000, 10_000, 10_000],
         "void hc::(anonymous namespace)::k_gsplit<2>(float const*, float const*, float const*, float*, float*, float*, long, int, float)":
             [5_000, 5_000, 4_000, 4_000],
         "void hc::(anonymous namespace)::k_gpre<2>(unsigned short const*, float const*, unsigned short*, long, int)":
@@ -86,11 +88,11 @@ def test_summarize_trace_general_stream_count(tmp_path, monkeypatch):
     bench.summarize_trace(str(tdir), 4096, 5120, "cmd", warmup=2, steps=2, tag="hc2", hc=2)
     text = (tmp_path / "kernel_trace_hc2_n4096_d5120.md").read_text()
     assert "n=4096 tokens, d=5120, hc=2" in text
-    assert "| k_gmix_wave<2> |" in text and "| k_gpost<2> |" in text
+    assert "| k_gmm<2, 128> |" in text and "| k_gpost<2> |" in text
     fused, post = bench.algorithmic_bytes(4096, 5120, 2)
-    row = [l for l in text.splitlines() if l.startswith("| k_gmix + k_gsplit + k_gpre")][0]
+    row = [l for l in text.splitlines() if l.startswith("| k_gmm + k_gred + k_gsplit + k_gpre")][0]
     cells = [c.strip() for c in row.strip("|").split("|")]
-    # timed region: 40 + 4 + 20 us
+    # timed region: 30 + 10 + 4 + 20 us
     assert float(cells[7]) == pytest.approx(64.0)
     assert float(cells[8]) == pytest.approx(fused / 64e-6 / 1e9 / bench.HBM_PEAK_GBS, abs=1e-3)
     prow = [l for l in text.splitlines() if l.startswith("| k_gpost<2> |")][0]

@@ -539,13 +539,14 @@ def test_post_mix_pre_other_stream_counts(hc):
         assert torch.equal(u.view(torch.int16), v.view(torch.int16))
 
 
-@pytest.mark.parametrize("hc,d", [(2, 64), (3, 8), (6, 8)])
-def test_other_stream_count_many_tiles_sampled(orc, hc, d):
-    # more token groups than the projection kernel's grid, so that its loop
-    # over them runs several times per workgroup; each stream count takes
-    # another projection kernel (hc = 2: one wave per 4 tokens; hc = 3: one
-    # wave per 4 tokens with 15 outputs; hc = 6: 4 x 4 micro-tiles, one group)
-    n = 140_001
+@pytest.mark.parametrize("hc,d,n", [(2, 64, 140_001), (3, 8, 140_001), (6, 8, 140_001), (3, 72, 9_001),
+                                    (2, 5120, 65_536), (3, 5120, 65_536), (8, 5120, 65_536)])
+def test_other_stream_count_many_tiles_sampled(orc, hc, d, n):
+    # the matrix-core projection with one workgroup per 256-token tile taking
+    # every segment of the reduction axis (at least as many tiles as compute
+    # units), sampled against the oracle: reduction axes shorter than one
+    # staged chunk (d = 8), not a multiple of it (hc = 3, d = 72), and the
+    # large workload's 65,536 tokens at d = 5120
     w = _hc_workload(hc, d)
     t = hin.make_inputs(w, DEV, seed=14, n_tokens=n)
     outs = run_fused(t["R"], t["W"], t["scale"], t["base"])
@@ -554,15 +555,16 @@ def test_other_stream_count_many_tiles_sampled(orc, hc, d):
 
 
 @pytest.mark.parametrize("hc,d,n,span", [(2, 256, 101, 37), (5, 64, 20_001, 37), (3, 8, 50_001, 1_000),
-                                         (8, 64, 101, 37), (6, 8, 20_001, 300), (8, 8, 17_001, 40)])
+                                         (8, 64, 101, 37), (6, 8, 20_001, 300), (8, 8, 17_001, 40),
+                                         (2, 5120, 70_000, 37), (3, 1024, 70_000, 5_000), (8, 512, 70_000, 300),
+                                         (7, 256, 66_000, 20_000)])
 def test_other_stream_counts_batch_invariant_and_deterministic(hc, d, n, span):
     # a token's results do not depend on the other tokens of its call, and
-    # repeated calls agree bit for bit, for every projection kernel: the wave
-    # kernel (hc = 2, 3), one pair per thread (hc = 5) and the micro-tiles
-    # (hc = 6, 8).  The long and short calls straddle 16,384 tokens, where the
-    # micro-tile kernel switches from two groups per tile to one (both add
-    # (even steps) + (odd steps)), and where hc = 3 and 5 once switched
-    # kernels.
+    # repeated calls agree bit for bit, whichever way the projection runs:
+    # long calls (70,000 tokens: at least a tile of 256 per compute unit) have
+    # one workgroup per tile add every segment of the reduction axis, shorter
+    # ones one workgroup per segment with the partial sums added afterwards,
+    # and the tile size (32 .. 256 tokens) follows the call's size.
     w = _hc_workload(hc, d)
     t = hin.make_inputs(w, DEV, seed=15, n_tokens=n)
     lo = n // 3 + 1
