@@ -70,6 +70,8 @@ def _load():
     lib.hco_post.restype = None
     lib.hco_diag_scale.argtypes = [P, P, I64, I32, P]
     lib.hco_diag_scale.restype = None
+    lib.hco_rmsnorm.argtypes = [P, P, I64, I32, ctypes.c_double, P]
+    lib.hco_rmsnorm.restype = None
     lib.hco_post_backward.argtypes = [P, P, P, P, P, I64, I32, I32, P, P, P, P]
     lib.hco_post_backward.restype = None
     lib.hco_pre_backward.argtypes = [P, P, P, I64, I32, I32, P, P]
@@ -185,6 +187,21 @@ def diag_scale(h_bits, D_bits) -> np.ndarray:
     assert D.shape == (d,)
     out = np.empty((n, d), dtype=np.uint16)
     _load().hco_diag_scale(ph, pD, n, d, out.ctypes.data)
+    return out
+
+
+def rmsnorm(h_bits, gamma, norm_eps: float = 1e-20) -> np.ndarray:
+    """The pre-sublayer RMSNorm of the "Mix projection" page's Block.__init__
+    (a reading: the pages print no formula) on hc_pre's bf16 output:
+    y_c = bf16(h_c / sqrt(mean(h^2) + norm_eps) * gamma_c), in double, rounded
+    once.  h_bits [..., d] uint16, gamma float32 [d]; returns uint16 [..., d]."""
+    hb = np.ascontiguousarray(h_bits, dtype=np.uint16)
+    g = np.ascontiguousarray(gamma, dtype=np.float32)
+    d = hb.shape[-1]
+    n = hb.size // d if d else 0
+    out = np.empty_like(hb)
+    if n:
+        _load().hco_rmsnorm(hb.ctypes.data, g.ctypes.data, n, d, float(norm_eps), out.ctypes.data)
     return out
 
 

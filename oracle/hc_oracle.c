@@ -277,6 +277,35 @@ void hco_diag_scale(const uint16_t *h, const uint16_t *D, int64_t n, int d,
                 hco_bf16_to_double(D[c]));
 }
 
+/*
+ * The pre-sublayer RMSNorm of [MP] Block.__init__ (attn_norm / ffn_norm,
+ * RMSNorm(dim, norm_eps)), applied to the bf16 output h of hc_pre.  The
+ * pages construct it but print no formula; this is the reading the rest of
+ * them supports: the same root-mean-square normalisation as the mix formula
+ * (x * rsqrt(mean(x^2) + norm_eps), over the last axis, in float), times a
+ * learned per-feature weight gamma[d], the result in h's dtype:
+ *   r   = 1 / sqrt( sum_c h_c^2 / d + norm_eps )
+ *   y_c = bf16( h_c * r * gamma_c )
+ * h_c is the bf16 value (the norm sees hc_pre's stored output); everything
+ * is double here and rounded once.
+ */
+void hco_rmsnorm(const uint16_t *h, const float *gamma, int64_t n, int d,
+                 double norm_eps, uint16_t *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        double ss = 0.0;
+        for (int c = 0; c < d; ++c) {
+            const double v = hco_bf16_to_double(h[t * (int64_t)d + c]);
+            ss += v * v;
+        }
+        const double r = 1.0 / sqrt(ss / (double)d + norm_eps);
+        for (int c = 0; c < d; ++c)
+            y[t * (int64_t)d + c] = hco_round_bf16(
+                hco_bf16_to_double(h[t * (int64_t)d + c]) * r * (double)gamma[c]);
+    }
+}
+
 /* ====================================================================
  * Backward pass (gradients of a scalar loss through one sublayer's
  * mixing).  The pages give the forward only; its gradient is defined by

@@ -608,3 +608,86 @@ def test_pre_and_post_special_cases_any_hc(orc, hc):
     cb = np.zeros((n, hc, hc))
     cb[:, j, k] = 1.0
     assert np.array_equal(orc.post(x, R, zeros, cb)[:, k], R[:, j])
+
+
+# --------------------------------------------------------------------------
+# The pre-sublayer RMSNorm ("Mix projection" page, Block.__init__ builds
+# RMSNorm(dim, norm_eps); the formula is a reading: the page's own mix
+# formula normalisation, times a per-feature weight, on hc_pre's bf16 output)
+
+
+def _bits_to_f64(bits):
+    return np.asarray(bits, np.uint16).astype(np.uint32).__lshift__(16).view(np.float32).astype(np.float64)
+
+
+def test_rmsnorm_constant_token_is_unit(orc):
+    # h_c = c for every c: mean(h^2) = c^2, so y = c / |c| = +-1 exactly
+    # with norm_eps = 0 (with 1e-20 too where c^2 dwarfs it)
+    for c, eps in ((1.0, NEPS), (-3.5, NEPS), (1e20, NEPS), (2.0 ** -30, 0.0), (-(2.0 ** -100), 0.0)):
+        h = _bf16_bits_of([c] * 64).reshape(1, 64)
+        y = orc.rmsnorm(h, np.ones(64, np.float32), eps)
+        assert (y == _bf16_bits_of([math.copysign(1.0, c)] * 64)).all(), c
+
+
+def test_rmsnorm_matches_numpy(orc):
+    # an independent formulation: numpy's mean and sqrt in double, then the
+    # oracle's output must be the nearest bf16 of that value
+    rng = np.random.default_rng(31)
+    h = _rand_bits(rng, (6, 320), scale=2.0)
+    g = (rng.standard_normal(320) * 0.3 + 1.0).astype(np.float32)
+    y = orc.rmsnorm(h, g, NEPS)
+    hf = _bits_to_f64(h)
+    ref = hf / np.sqrt(np.mean(hf * hf, axis=-1, keepdims=True) + NEPS) * g.astype(np.float64)
+    yf = _bits_to_f64(y)
+    ulp = np.spacing(np.abs(yf).astype(np.float32)).astype(np.float64) * 2.0 ** 16
+    assert np.all(np.abs(yf - ref) <= 0.5 * ulp * (1 + 1e-12) + 1e-300)
+
+
+def test_rmsnorm_power_of_two_scale_invariant(orc):
+    # with norm_eps = 0, RMSNorm(2^e h) = RMSNorm(h) bit for bit: the mean
+    # of squares and its square root scale exactly by powers of two
+    rng = np.random.default_rng(32)
+    h = _rand_bits(rng, (3, 256))
+    g = rng.standard_normal(256).astype(np.float32)
+    y0 = orc.rmsnorm(h, g, 0.0)
+    for e in (-40, -7, 9, 60):
+        hs = hin.bits(torch.from_numpy(_bits_to_f64(h).astype(np.float32) * np.float32(2.0 ** e)).to(torch.bfloat16))
+        assert (orc.rmsnorm(hs, g, 0.0) == y0).all(), e
+
+
+def test_rmsnorm_gamma_and_eps_roles(orc):
+    rng = np.random.default_rng(33)
+    h = _rand_bits(rng, (2, 128))
+    # one-hot gamma: a single output survives, the others are (signed) zero
+    g = np.zeros(128, np.float32)
+    g[17] = 1.0
+    y = orc.rmsnorm(h, g, NEPS)
+    assert all(_bits_to_f64(y[t])[c] == 0.0 for t in range(2) for c in range(128) if c != 17)
+    assert all(_bits_to_f64(y[t])[17] != 0.0 for t in range(2))
+    # gamma doubled: every output doubled, bit for bit
+    g1 = rng.standard_normal(128).astype(np.float32)
+    assert (_bits_to_f64(orc.rmsnorm(h, 2 * g1, NEPS)) == 2 * _bits_to_f64(orc.rmsnorm(h, g1, NEPS))).all()
+    # an all-zero token gives zeros, not NaN
+    z = np.zeros((1, 128), np.uint16)
+    assert (orc.rmsnorm(z, g1, NEPS) & 0x7FFF == 0).all()
+    # norm_eps dominates a tiny token: y = h / sqrt(mean(h^2) + eps) ~ h * 1e10
+    tiny = _bf16_bits_of([2.0 ** -80] * 128).reshape(1, 128)
+    yt = _bits_to_f64(orc.rmsnorm(tiny, np.ones(128, np.float32), NEPS))
+    exact = 2.0 ** -80 / math.sqrt(2.0 ** -160 + NEPS)
+    assert np.all(np.abs(yt - exact) <= exact * 2.0 ** -8)
+
+
+def test_rmsnorm_mpmath_brute_force(orc):
+    # 50 digits, the definition written out element by element
+    mp.mp.dps = 50
+    rng = np.random.default_rng(34)
+    h = _rand_bits(rng, (2, 40), scale=0.5)
+    g = rng.standard_normal(40).astype(np.float32)
+    y = orc.rmsnorm(h, g, 1e-3)      # an eps that matters at this scale
+    hf = _bits_to_f64(h)
+    for t in range(2):
+        ms = mp.fsum(mp.mpf(float(v)) ** 2 for v in hf[t]) / 40
+        r = 1 / mp.sqrt(ms + mp.mpf(1e-3))
+        for c in range(40):
+            v = mp.mpf(float(hf[t][c])) * r * mp.mpf(float(g[c]))
+            assert y[t][c] == orc.round_bf16(float(v)), (t, c)
