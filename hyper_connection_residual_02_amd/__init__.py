@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "HCError", "load", "lib_path", "hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post",
-    "hc_fused_mix_pre", "hc_fused_mix_pre_noalloc", "hc_post_mix_pre", "hc_pack_weights", "hc_diag_scale", "hc_fused_workspace_bytes",
+    "hc_rmsnorm", "hc_pre_norm", "hc_fused_mix_pre", "hc_fused_mix_pre_noalloc", "hc_post_mix_pre", "hc_pack_weights", "hc_diag_scale", "hc_fused_workspace_bytes",
     "hc_post_backward", "hc_mix_pre_backward", "hc_backward_workspace_bytes",
     "Workspace", "workspace_status", "check_workspace", "noalloc_status", "debug_force_timeout",
 ]
@@ -62,6 +62,8 @@ def load():
         "hc_mixes": [P, P, P, I64, I32, I32, F32, P, SZ, P],
         "hc_split_sinkhorn": [P, P, P, P, P, P, I64, I32, I32, F32, P],
         "hc_pre": [P, P, P, I64, I32, I32, P],
+        "hc_rmsnorm": [P, P, P, I64, I32, F32, P],
+        "hc_pre_norm": [P, P, P, P, P, I64, I32, I32, F32, P],
         "hc_post": [P, P, P, P, P, I64, I32, I32, P],
         "hc_fused_mix_pre": [P, P, P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, F32, F32, P],
         "hc_post_mix_pre": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, F32, F32, P],
@@ -292,6 +294,49 @@ def hc_pre(R: torch.Tensor, pre: torch.Tensor, out: torch.Tensor | None = None) 
     with torch.cuda.device(dev):
         _call("hc_pre", _ptr(R), _ptr(pre), _ptr(out), n, hc, d, _stream(dev))
     return out
+
+
+def hc_rmsnorm(h: torch.Tensor, gamma: torch.Tensor, norm_eps: float = 1e-20,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = bf16(h * gamma / sqrt(mean(h^2) + norm_eps)) over the last axis; [..., d] bf16."""
+    dev = h.device
+    _check(h, "h", torch.bfloat16)
+    _check(gamma, "gamma", torch.float32, dev)
+    d = h.shape[-1]
+    n = h.numel() // d if d else 0
+    if tuple(gamma.shape) != (d,):
+        raise ValueError("gamma must be (%d,)" % d)
+    if out is None:
+        out = torch.empty_like(h)
+    _check(out, "out", torch.bfloat16, dev)
+    if tuple(out.shape) != tuple(h.shape):
+        raise ValueError("out must be %s" % (tuple(h.shape),))
+    with torch.cuda.device(dev):
+        _call("hc_rmsnorm", _ptr(h), _ptr(gamma), _ptr(out), n, d, norm_eps, _stream(dev))
+    return out
+
+
+def hc_pre_norm(R: torch.Tensor, pre: torch.Tensor, gamma: torch.Tensor, norm_eps: float = 1e-20,
+                want_h: bool = False, out: torch.Tensor | None = None):
+    """hc_pre then hc_rmsnorm in one pass over R: returns y, or (y, h) with ``want_h``."""
+    dev = R.device
+    _check(R, "R", torch.bfloat16)
+    _check(pre, "pre", torch.float32, dev)
+    _check(gamma, "gamma", torch.float32, dev)
+    hc = _streams(R)
+    lead, n, d = _lead(R, hc)
+    if tuple(pre.shape) != lead + (hc,):
+        raise ValueError("pre must be %s" % (lead + (hc,),))
+    if tuple(gamma.shape) != (d,):
+        raise ValueError("gamma must be (%d,)" % d)
+    if out is None:
+        out = torch.empty(*lead, d, dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, dev)
+    h = torch.empty(*lead, d, dtype=torch.bfloat16, device=dev) if want_h else None
+    with torch.cuda.device(dev):
+        _call("hc_pre_norm", _ptr(R), _ptr(pre), _ptr(gamma), _ptr(h),
+              _ptr(out), n, hc, d, norm_eps, _stream(dev))
+    return (out, h) if want_h else out
 
 
 def hc_post(x: torch.Tensor, R: torch.Tensor, post: torch.Tensor, comb: torch.Tensor,

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libhc.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["hc_api.hip", "hc_stream.hip", "hc_sinkhorn.hip", "hc_coop.hip", "hc_general.hip", "hc_backward.hip"]
+SOURCES = ["hc_api.hip", "hc_stream.hip", "hc_sinkhorn.hip", "hc_coop.hip", "hc_general.hip", "hc_backward.hip",
+           "hc_norm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -105,8 +105,48 @@ int hc_pre(const void* R, const float* pre, void* h, int64_t n, int32_t hc_, int
     const uint64_t nd = (uint64_t)n * d;
     Span sh = span(h, nd * 2);
     if (overlap(sh, span(R, nd * hc_ * 2)) || overlap(sh, span(pre, (uint64_t)n * hc_ * 4))) return HC_ERR_ALIAS;
-    const int e = hc_ == 4 ? hc::launch_pre(R, pre, h, n, d, (hipStream_t)stream)
-                           : hc::launch_gen_pre(R, pre, h, n, hc_, d, (hipStream_t)stream);
+    // one workgroup per token (or four), h only, up to 32,768 features; the
+    // grid-stride kernels beyond
+    int e;
+    if (hc::norm_waves(d))
+        e = hc::launch_pre_norm(R, pre, nullptr, h, nullptr, n, hc_, d, 0.0f, (hipStream_t)stream);
+    else
+        e = hc_ == 4 ? hc::launch_pre(R, pre, h, n, d, (hipStream_t)stream)
+                     : hc::launch_gen_pre(R, pre, h, n, hc_, d, (hipStream_t)stream);
+    return e ? HC_ERR_LAUNCH : HC_OK;
+}
+
+int hc_rmsnorm(const void* h, const float* gamma, void* y, int64_t n, int32_t d, float norm_eps, void* stream) {
+    int st = check_nd(n, 1, d);
+    if (st) return st;
+    if (!finite_nonneg(norm_eps)) return HC_ERR_VALUE;
+    if (hc::norm_waves(d) == 0) return HC_ERR_UNSUPPORTED;
+    if (n == 0) return HC_OK;
+    if (!h || !gamma || !y) return HC_ERR_NULL;
+    if (!al16(h) || !al16(gamma) || !al16(y)) return HC_ERR_ALIGN;
+    const uint64_t nd = (uint64_t)n * d;
+    Span sy = span(y, nd * 2);
+    if (overlap(sy, span(h, nd * 2)) || overlap(sy, span(gamma, (uint64_t)d * 4))) return HC_ERR_ALIAS;
+    const int e = hc::launch_pre_norm(h, nullptr, gamma, nullptr, y, n, 0, d, norm_eps, (hipStream_t)stream);
+    return e ? HC_ERR_LAUNCH : HC_OK;
+}
+
+int hc_pre_norm(const void* R, const float* pre, const float* gamma, void* h, void* y, int64_t n, int32_t hc_,
+                int32_t d, float norm_eps, void* stream) {
+    int st = check_nd(n, hc_, d);
+    if (st) return st;
+    if (!finite_nonneg(norm_eps)) return HC_ERR_VALUE;
+    if (hc::norm_waves(d) == 0) return HC_ERR_UNSUPPORTED;
+    if (n == 0) return HC_OK;
+    if (!R || !pre || !gamma || !y) return HC_ERR_NULL;
+    if (!al16(R) || !al16(pre) || !al16(gamma) || !al16(y) || (h && !al16(h))) return HC_ERR_ALIGN;
+    const uint64_t nd = (uint64_t)n * d;
+    const Span in[3] = {span(R, nd * hc_ * 2), span(pre, (uint64_t)n * hc_ * 4), span(gamma, (uint64_t)d * 4)};
+    Span sy = span(y, nd * 2);
+    for (const Span& x : in)
+        if (overlap(sy, x) || (h && overlap(span(h, nd * 2), x))) return HC_ERR_ALIAS;
+    if (h && overlap(sy, span(h, nd * 2))) return HC_ERR_ALIAS;
+    const int e = hc::launch_pre_norm(R, pre, gamma, h, y, n, hc_, d, norm_eps, (hipStream_t)stream);
     return e ? HC_ERR_LAUNCH : HC_OK;
 }
 

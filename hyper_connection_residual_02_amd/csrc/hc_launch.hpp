@@ -17,6 +17,13 @@ int launch_post(const void* x, const void* R, const float* post, const float* co
                 int64_t n, int d, hipStream_t s);
 int launch_diag(const void* h, const void* D, void* x, int64_t n, int d, hipStream_t s);
 
+// Pre-sublayer RMSNorm (hc_norm.hip): hc = 0 normalises h = R itself (pre
+// unused, h unused); hc >= 1 forms h = hc_pre(R, pre) first, written to h
+// unless it is null.  norm_waves(d) is 0 if d is too wide.
+int norm_waves(int d);
+int launch_pre_norm(const void* R, const float* pre, const float* gamma, void* h, void* y, int64_t n, int hc,
+                    int d, float norm_eps, hipStream_t s);
+
 // Standalone split + Sinkhorn (hc_sinkhorn.hip); pre may be NULL (not written).
 int launch_split(const float* mixes, const float* scale, const float* base, float* pre, float* post,
                  float* comb, int64_t n, int iters, float eps, hipStream_t s);

@@ -130,6 +130,11 @@ def make_diag(w: Workload, layer: int, device="cpu", seed=None):
                    torch.bfloat16)
 
 
+def make_gamma(d: int, device="cpu", seed: int = 7, std: float = 0.25):
+    """Pre-sublayer RMSNorm weight: fp32[d] drawn as 1 + N(0, std)."""
+    return randn((d,), std, device, seed, 9).add_(1.0)
+
+
 def sample_tokens(n: int, k: int, seed: int = 0) -> np.ndarray:
     """Sorted token indices for sampled checks: the first and last tokens,
     token boundaries of common tile sizes, and random ones."""

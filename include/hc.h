@@ -179,6 +179,34 @@ int hc_pre(const void *R, const float *pre, void *h, int64_t n, int32_t hc,
            int32_t d, void *stream);
 
 /*
+ * hc_rmsnorm -- the pre-sublayer RMSNorm ("Mix projection" page,
+ * Block.__init__ builds RMSNorm(dim, norm_eps); its formula is not printed
+ * and is read as the page's mix-formula normalisation over the d features,
+ * times a per-feature weight):
+ *   y[t][c] = bf16( h[t][c] * r[t] * gamma[c] ),
+ *   r[t] = 1 / sqrt( sum_c h[t][c]^2 / d + norm_eps ).
+ * h, y: bf16 [n][d]; gamma: fp32 [d].  The sum of squares, r and the
+ * products are taken in double and y is rounded once (nearest-even), so y
+ * is the correctly rounded result up to the order of the sum of squares.
+ * d % 8 == 0 and d <= 32,768 (wider: HC_ERR_UNSUPPORTED); norm_eps finite
+ * and >= 0 (HC_ERR_VALUE); y must not overlap h or gamma (HC_ERR_ALIAS).
+ * All pointers 16-byte aligned.  Asynchronous on `stream`; no workspace.
+ */
+int hc_rmsnorm(const void *h, const float *gamma, void *y, int64_t n,
+               int32_t d, float norm_eps, void *stream);
+
+/*
+ * hc_pre_norm -- hc_pre followed by hc_rmsnorm in one pass over R:
+ *   h = hc_pre(R, pre) (bitwise hc_pre's result), y = hc_rmsnorm(h, gamma).
+ * h may be NULL (then only y is written: R is read once and y written once,
+ * 2 (hc + 1) d bytes per token).  Shapes and rules as hc_pre and
+ * hc_rmsnorm; no output may overlap an input or the other output.
+ */
+int hc_pre_norm(const void *R, const float *pre, const float *gamma, void *h,
+                void *y, int64_t n, int32_t hc, int32_t d, float norm_eps,
+                void *stream);
+
+/*
  * hc_post -- "Mix projection" page, Block.hc_post:
  *   R_out[t][k][c] = bf16( post[t][k] * x[t][c]
  *                          + sum_j comb[t][j][k] * R[t][j][c] )

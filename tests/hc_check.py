@@ -99,3 +99,21 @@ def post_terms(x_bits, R_bits, post, comb):
     X = np.abs(bf16_f64(x_bits))
     Rv = np.abs(bf16_f64(R_bits))
     return np.abs(post)[:, :, None] * X[:, None, :] + np.einsum("njk,njd->nkd", np.abs(comb), Rv)
+
+
+def check_norm(got, ref, name, max_frac=1e-6):
+    """RMSNorm outputs: NaN exactly where the oracle has NaN, every other
+    output within 1 bf16 ulp, and at most max_frac of them (plus two) off by
+    that ulp: only the order of the double sum of squares differs, which
+    moves r by at most an ulp of double.  Returns the 1-ulp count."""
+    got = np.asarray(got, np.uint16)
+    ref = np.asarray(ref, np.uint16)
+    gn = (got & 0x7FFF) > 0x7F80
+    rn = (ref & 0x7FFF) > 0x7F80
+    assert (gn == rn).all(), "%s: NaN at %d outputs, oracle %d" % (name, int(gn.sum()), int(rn.sum()))
+    du = ulp_dist(got[~rn], ref[~rn])
+    worst = int(du.max()) if du.size else 0
+    assert worst <= 1, "%s: an output %d bf16 ulp off" % (name, worst)
+    off = int((du == 1).sum())
+    assert off <= max_frac * du.size + 2, "%s: %d of %d outputs 1 ulp off" % (name, off, du.size)
+    return off

@@ -91,6 +91,43 @@ def test_pre_checks(lib):
     assert f(h=A + 64) == ALIAS
 
 
+def test_norm_checks(lib):
+    f = lambda h=A, g=B, y=C, n=4, d=64, eps=1e-20: lib.hc_rmsnorm(P(h), P(g), P(y), n, d, eps, None)
+    assert f(n=0) == OK
+    assert f(n=-1) == SHAPE
+    assert f(d=12) == SHAPE
+    assert f(d=32768 + 8) == UNSUP         # wider than the kernel holds
+    assert f(n=0, d=32768 + 8) == UNSUP
+    assert f(eps=-1.0) == VALUE
+    assert f(eps=float("nan")) == VALUE
+    assert f(h=0) == NULL
+    assert f(g=0) == NULL
+    assert f(y=0) == NULL
+    assert f(g=B + 4) == ALIGN
+    assert f(y=A + 256) == ALIAS            # h spans 4 * 64 * 2 bytes
+    assert f(y=B + 128) == ALIAS            # gamma spans 64 * 4 bytes
+    g = lambda R=A, p=B, gm=B + 4096, h=C, y=D_, n=4, hc=4, d=64, eps=1e-20: \
+        lib.hc_pre_norm(P(R), P(p), P(gm), P(h), P(y), n, hc, d, eps, None)
+    assert g(n=0) == OK
+    assert g(n=0, h=0) == OK
+    assert g(hc=9) == UNSUP
+    assert g(hc=0) == UNSUP
+    assert g(d=12) == SHAPE
+    assert g(d=32768 + 8) == UNSUP
+    assert g(eps=float("inf")) == VALUE
+    assert g(R=0) == NULL
+    assert g(p=0) == NULL
+    assert g(gm=0) == NULL
+    assert g(y=0) == NULL
+    assert g(h=C + 8) == ALIGN
+    assert g(y=D_ + 2) == ALIGN
+    assert g(y=A + 1024) == ALIAS           # R spans 4 * 4 * 64 * 2 bytes
+    assert g(h=A + 2032) == ALIAS
+    assert g(y=C + 64) == ALIAS             # y overlaps h
+    assert g(h=B + 4096 + 128) == ALIAS     # h overlaps gamma
+    assert g(y=B + 16) == ALIAS             # y overlaps pre
+
+
 def test_split_checks(lib):
     f = lambda m=A, s=B, b=B + 64, pre=C, post=D_, comb=E, n=4, hc=4, it=20, eps=1e-6: \
         lib.hc_split_sinkhorn(P(m), P(s), P(b), P(pre), P(post), P(comb), n, hc, it, eps, None)
