@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "HCError", "load", "lib_path", "hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post",
-    "hc_rmsnorm", "hc_pre_norm", "hc_fused_mix_pre", "hc_fused_mix_pre_noalloc", "hc_post_mix_pre", "hc_pack_weights", "hc_diag_scale", "hc_fused_workspace_bytes",
+    "hc_rmsnorm", "hc_pre_norm", "hc_fused_mix_pre", "hc_fused_mix_pre_norm", "hc_fused_mix_pre_noalloc", "hc_post_mix_pre", "hc_pack_weights", "hc_diag_scale", "hc_fused_workspace_bytes",
     "hc_post_backward", "hc_mix_pre_backward", "hc_backward_workspace_bytes",
     "Workspace", "workspace_status", "check_workspace", "noalloc_status", "debug_force_timeout",
 ]
@@ -66,6 +66,7 @@ def load():
         "hc_pre_norm": [P, P, P, P, P, I64, I32, I32, F32, P],
         "hc_post": [P, P, P, P, P, I64, I32, I32, P],
         "hc_fused_mix_pre": [P, P, P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, F32, F32, P],
+        "hc_fused_mix_pre_norm": [P, P, P, P, P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, F32, F32, P],
         "hc_post_mix_pre": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, F32, F32, P],
         "hc_pack_weights": [P, P, SZ, I32, I32, P],
         "hc_fused_mix_pre_packed": [P, P, SZ, P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, F32, F32, P],
@@ -423,6 +424,46 @@ def hc_fused_mix_pre(R: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tenso
                   _ptr(pre), _ptr(post), _ptr(comb), _ptr(mixes), wp, wb, n, hc, d,
                   int(sinkhorn_iters), float(hc_eps), float(norm_eps), _stream(dev))
     return h, pre, post, comb, mixes
+
+
+def hc_fused_mix_pre_norm(R: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tensor,
+                          hc_base: torch.Tensor, gamma: torch.Tensor, sinkhorn_iters: int = 20,
+                          hc_eps: float = 1e-6, norm_eps: float = 1e-20, want_h: bool = False,
+                          want_pre: bool = True, want_mixes: bool = False,
+                          workspace: Workspace | None = None, out=None):
+    """hc_fused_mix_pre followed by the pre-sublayer RMSNorm of h.
+    Returns (y, h or None, pre or None, post, comb, mixes or None).  ``out``
+    may be a dict of preallocated outputs (keys y, h, pre, post, comb, mixes)."""
+    dev = R.device
+    _check(R, "R", torch.bfloat16)
+    for t, nm in ((hc_fn, "hc_fn"), (hc_scale, "hc_scale"), (hc_base, "hc_base"), (gamma, "gamma")):
+        _check(t, nm, torch.float32, dev)
+    hc = _streams(R)
+    M = (2 + hc) * hc
+    lead, n, d = _lead(R, hc)
+    if tuple(hc_fn.shape) != (M, hc * d):
+        raise ValueError("hc_fn must be [%d, %d]" % (M, hc * d))
+    if tuple(gamma.shape) != (d,):
+        raise ValueError("gamma must be (%d,)" % d)
+    o = dict(out or {})
+
+    def get(key, want, shape, dtype):
+        t = o.get(key)
+        if t is None and want:
+            t = torch.empty(*shape, dtype=dtype, device=dev)
+        return t
+    y = get("y", True, lead + (d,), torch.bfloat16)
+    h = get("h", want_h, lead + (d,), torch.bfloat16)
+    post = get("post", True, lead + (hc,), torch.float32)
+    comb = get("comb", True, lead + (hc, hc), torch.float32)
+    pre = get("pre", want_pre, lead + (hc,), torch.float32)
+    mixes = get("mixes", want_mixes, lead + (M,), torch.float32)
+    wp, wb = _workspace(workspace, hc_fused_workspace_bytes(n, hc, d), dev)
+    with torch.cuda.device(dev):
+        _call("hc_fused_mix_pre_norm", _ptr(R), _ptr(hc_fn), _ptr(hc_scale), _ptr(hc_base), _ptr(gamma),
+              _ptr(h), _ptr(y), _ptr(pre), _ptr(post), _ptr(comb), _ptr(mixes), wp, wb, n, hc, d,
+              int(sinkhorn_iters), float(hc_eps), float(norm_eps), _stream(dev))
+    return y, h, pre, post, comb, mixes
 
 
 def hc_fused_mix_pre_noalloc(R: torch.Tensor, hc_fn: torch.Tensor, hc_scale: torch.Tensor,

@@ -325,14 +325,29 @@ static int gen_fused(const hc::PostIn* prev, const void* R, const float* hc_fn, 
 
 // hc_fused_mix_pre with the weights as given (hc_fn) or already split
 // (packed, from hc_pack_weights).
+// The pre-sublayer RMSNorm of hc_fused_mix_pre_norm: y and gamma, checked
+// by the caller.  h may then be null: y stands in for it in the checks and
+// receives h, which the norm kernel then normalises in place.
+struct NormOut {
+    void* y;
+    const float* gamma;
+};
+
 static int fused_impl(const void* R, const float* hc_fn, const void* packed, size_t packed_bytes,
-                      const float* hc_scale, const float* hc_base, void* h, float* pre, float* post, float* comb,
+                      const float* hc_scale, const float* hc_base, void* h_, float* pre, float* post, float* comb,
                       float* mixes, void* workspace, size_t workspace_bytes, int64_t n, int32_t hc_, int32_t d,
-                      int32_t sinkhorn_iters, float hc_eps, float norm_eps, void* stream, bool gate = true) {
+                      int32_t sinkhorn_iters, float hc_eps, float norm_eps, void* stream, bool gate = true,
+                      const NormOut* norm = nullptr) {
+    void* h = h_ ? h_ : (norm ? norm->y : nullptr);
     if (hc_ != 4) {
         if (packed) return HC_ERR_UNSUPPORTED;
-        return gen_fused(nullptr, R, hc_fn, hc_scale, hc_base, h, pre, post, comb, mixes, workspace,
-                         workspace_bytes, n, hc_, d, sinkhorn_iters, hc_eps, norm_eps, stream);
+        const int st = gen_fused(nullptr, R, hc_fn, hc_scale, hc_base, h, pre, post, comb, mixes, workspace,
+                                 workspace_bytes, n, hc_, d, sinkhorn_iters, hc_eps, norm_eps, stream);
+        if (st || !norm || n == 0) return st;
+        return hc::launch_pre_norm(h, nullptr, norm->gamma, nullptr, norm->y, n, 0, d, norm_eps,
+                                   (hipStream_t)stream)
+                   ? HC_ERR_LAUNCH
+                   : HC_OK;
     }
     if (sinkhorn_iters < 1) return HC_ERR_UNSUPPORTED;
     if (!finite_nonneg(hc_eps)) return HC_ERR_VALUE;
@@ -367,10 +382,13 @@ static int fused_impl(const void* R, const float* hc_fn, const void* packed, siz
             if (overlap(outs[i], outs[j])) return HC_ERR_ALIAS;
     }
     p.gate = gate;
-    return hc::launch_coop(p, R, hc_fn, hc_scale, hc_base, h, pre, post, comb, mixes, workspace, n, d,
-                           sinkhorn_iters, hc_eps, norm_eps, true, (hipStream_t)stream, nullptr, packed)
-               ? HC_ERR_LAUNCH
-               : HC_OK;
+    if (hc::launch_coop(p, R, hc_fn, hc_scale, hc_base, h, pre, post, comb, mixes, workspace, n, d, sinkhorn_iters,
+                        hc_eps, norm_eps, true, (hipStream_t)stream, nullptr, packed))
+        return HC_ERR_LAUNCH;
+    if (norm && hc::launch_pre_norm(h, nullptr, norm->gamma, nullptr, norm->y, n, 0, d, norm_eps,
+                                    (hipStream_t)stream))
+        return HC_ERR_LAUNCH;
+    return HC_OK;
 }
 
 extern "C" {
@@ -381,6 +399,36 @@ int hc_fused_mix_pre(const void* R, const float* hc_fn, const float* hc_scale, c
                      void* stream) {
     return fused_impl(R, hc_fn, nullptr, 0, hc_scale, hc_base, h, pre, post, comb, mixes, workspace,
                       workspace_bytes, n, hc_, d, sinkhorn_iters, hc_eps, norm_eps, stream);
+}
+
+int hc_fused_mix_pre_norm(const void* R, const float* hc_fn, const float* hc_scale, const float* hc_base,
+                          const float* gamma, void* h, void* y, float* pre, float* post, float* comb, float* mixes,
+                          void* workspace, size_t workspace_bytes, int64_t n, int32_t hc_, int32_t d,
+                          int32_t sinkhorn_iters, float hc_eps, float norm_eps, void* stream) {
+    int st = check_nd(n, hc_, d);
+    if (st) return st;
+    if (!finite_nonneg(norm_eps)) return HC_ERR_VALUE;
+    if (hc::norm_waves(d) == 0) return HC_ERR_UNSUPPORTED;
+    if (n > 0) {
+        if (!gamma || !y) return HC_ERR_NULL;
+        if (!al16(gamma) || !al16(y)) return HC_ERR_ALIGN;
+        const uint64_t K = (uint64_t)hc_ * d, M = (uint64_t)(2 + hc_) * hc_;
+        const Span sy = span(y, (uint64_t)n * d * 2), sg = span(gamma, (uint64_t)d * 4);
+        // y and gamma against everything else (the rest is checked below,
+        // with y standing in for h when h is null)
+        const Span others[] = {span(R, (uint64_t)n * K * 2), span(hc_fn, M * K * 4), span(hc_scale, 12),
+                               span(hc_base, M * 4), span(workspace, workspace_bytes), span(h, h ? (uint64_t)n * d * 2 : 0),
+                               span(post, (uint64_t)n * hc_ * 4), span(comb, (uint64_t)n * hc_ * hc_ * 4),
+                               span(pre, pre ? (uint64_t)n * hc_ * 4 : 0), span(mixes, mixes ? (uint64_t)n * M * 4 : 0)};
+        if (overlap(sy, sg)) return HC_ERR_ALIAS;
+        for (int i = 0; i < 10; ++i) {
+            if (overlap(sy, others[i])) return HC_ERR_ALIAS;
+            if (i >= 5 && overlap(sg, others[i])) return HC_ERR_ALIAS;     // gamma is an input: outputs only
+        }
+    }
+    const NormOut no{y, gamma};
+    return fused_impl(R, hc_fn, nullptr, 0, hc_scale, hc_base, h, pre, post, comb, mixes, workspace,
+                      workspace_bytes, n, hc_, d, sinkhorn_iters, hc_eps, norm_eps, stream, true, &no);
 }
 
 size_t hc_packed_weights_bytes(int32_t hc_, int32_t d) {

@@ -95,11 +95,13 @@ __device__ __forceinline__ u32x4 y_chunk(const u32x4 hv, double r, const f32x4 g
 }
 
 // Block: max(4, W) waves; token t = t0 + blockIdx.x * (waves / W) + wave / W.
+// With HC = 0, y may be X itself (normalised in place): a token's chunks
+// are all loaded before the reduction that every store depends on (and the
+// barrier, when W > 1).
 template <int HC, int NIT>
-__global__ __launch_bounds__(64 * kNormMaxW) void k_pre_norm(const uint16_t* __restrict__ X,
-                                                               const float* __restrict__ pre,
-                                                               const float* __restrict__ gamma,
-                                                               uint16_t* __restrict__ h, uint16_t* __restrict__ y,
+__global__ __launch_bounds__(64 * kNormMaxW) void k_pre_norm(const uint16_t* X, const float* __restrict__ pre,
+                                                               const float* __restrict__ gamma, uint16_t* h,
+                                                               uint16_t* y,
                                                                int64_t t0, int64_t n, int d, int W, float norm_eps) {
     __shared__ double red[kNormMaxW];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;

@@ -240,6 +240,30 @@ int hc_fused_mix_pre(const void *R, const float *hc_fn,
                      float hc_eps, float norm_eps, void *stream);
 
 /*
+ * hc_fused_mix_pre_norm -- hc_fused_mix_pre followed by the pre-sublayer
+ * RMSNorm of its h (hc_rmsnorm; the norm is a reading of the "Mix
+ * projection" page, whose Block.__init__ builds RMSNorm(dim, norm_eps) but
+ * prints no formula):  y = bf16(h * r * gamma),
+ * r = 1 / sqrt(sum_c h_c^2 / d + norm_eps), per token.
+ * Arguments as hc_fused_mix_pre, plus gamma (fp32 [d]) and y (bf16 [n][d],
+ * required); h may be NULL (then it is not written).  The coefficients and
+ * h are bitwise hc_fused_mix_pre's; y is hc_rmsnorm's result for that h
+ * (within one bf16 ulp of the correctly rounded norm: only the order of
+ * the double sum of squares is free).  Same workspace
+ * (hc_fused_workspace_bytes).  Runs hc_fused_mix_pre's kernels, writing h
+ * to h (or, when h is NULL, to y), and then the norm kernel (in place on
+ * y when h is NULL).  d <= 32,768 (else HC_ERR_UNSUPPORTED); y must not
+ * overlap any input or output, gamma no output.
+ */
+int hc_fused_mix_pre_norm(const void *R, const float *hc_fn,
+                          const float *hc_scale, const float *hc_base,
+                          const float *gamma, void *h, void *y, float *pre,
+                          float *post, float *comb, float *mixes,
+                          void *workspace, size_t workspace_bytes, int64_t n,
+                          int32_t hc, int32_t d, int32_t sinkhorn_iters,
+                          float hc_eps, float norm_eps, void *stream);
+
+/*
  * hc_post_mix_pre -- one sublayer boundary: hc_post of sublayer l, then
  * hc_fused_mix_pre of sublayer l+1 on its output ("Mix projection" page,
  * Block.hc_post followed by Block.hc_mixes and Block.hc_pre; the coefficients

@@ -190,6 +190,40 @@ def test_fused_and_mixes_checks(lib):
     assert m(hc=5, out=A) == ALIAS
 
 
+def test_fused_norm_checks(lib):
+    GM, Y = 0x50000000, 0x58000000
+
+    def f(R=A, W=B, s=C, b=C + 64, g=GM, h=D_, y=Y, pre=E, post=E + 4096, comb=E + 8192, mix=0, ws=F_,
+          wsb=1 << 30, n=4, hc=4, d=64, it=20, eps=1e-6, neps=1e-20):
+        return lib.hc_fused_mix_pre_norm(P(R), P(W), P(s), P(b), P(g), P(h), P(y), P(pre), P(post),
+                                         P(comb), P(mix), P(ws), wsb, n, hc, d, it, eps, neps, None)
+    assert f(n=0) == OK
+    assert f(n=0, h=0) == OK
+    assert f(n=-1) == SHAPE
+    assert f(d=48) == UNSUP               # the projection cannot tile it
+    assert f(d=32768 + 32) == UNSUP       # wider than the norm kernel holds
+    assert f(hc=9) == UNSUP
+    assert f(neps=-1.0) == VALUE
+    assert f(it=0) == UNSUP
+    assert f(g=0) == NULL
+    assert f(y=0) == NULL
+    assert f(h=0, y=0) == NULL
+    assert f(R=0) == NULL
+    assert f(g=GM + 4) == ALIGN
+    assert f(y=Y + 2) == ALIGN
+    assert f(y=A) == ALIAS                # y overlaps R
+    assert f(y=D_ + 256) == ALIAS         # y overlaps h
+    assert f(y=GM + 128) == ALIAS         # y overlaps gamma
+    assert f(g=D_) == ALIAS               # gamma overlaps h (an output)
+    assert f(g=E + 4096) == ALIAS         # gamma overlaps post
+    assert f(y=F_ + 64) == ALIAS          # y inside the workspace
+    assert f(h=0, y=A + 64) == ALIAS      # y standing in for h overlaps R
+    assert f(h=0, ws=0) == WS
+    assert f(hc=2, y=A) == ALIAS
+    assert f(hc=2, g=0) == NULL
+    assert f(hc=2, wsb=16) == WS
+
+
 def test_post_mix_pre_checks(lib):
     H = 0x74000000
 

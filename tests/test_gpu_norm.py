@@ -122,3 +122,97 @@ def test_norm_batch_invariant():
         part = hcl.hc_rmsnorm(h[:m].contiguous(), g, NEPS)
         torch.cuda.synchronize()
         check_bf16_exact(hin.bits(part), hin.bits(full[:m]), "y of %d tokens" % m)
+
+
+# ------------------------------------------------- hc_fused_mix_pre_norm
+# The fused kernels (every path: two-pass, wave-specialised, other widths,
+# other stream counts), then the norm kernel on h, or in place on y when h
+# is not kept.  The coefficients and h are bitwise hc_fused_mix_pre's, and y
+# is graded against the oracle's norm of that h.
+
+import dataclasses
+
+
+def _wl(hc, d):
+    return dataclasses.replace(hin.WORKLOADS["prefill"], hc=hc, d=d)
+
+
+def _fused_norm_case(hc, d, n, seed, want_h, sample=None):
+    w = _wl(hc, d)
+    t = hin.make_inputs(w, DEV, seed=seed, n_tokens=n)
+    g = hin.make_gamma(d, DEV, seed=seed)
+    y, h, pre, post, comb, mixes = hcl.hc_fused_mix_pre_norm(t["R"], t["W"], t["scale"], t["base"], g,
+                                                             norm_eps=NEPS, want_h=want_h, want_mixes=True)
+    ref = hcl.hc_fused_mix_pre(t["R"], t["W"], t["scale"], t["base"], norm_eps=NEPS, want_mixes=True)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("pre", "post", "comb", "mixes"), (pre, post, comb, mixes), ref[1:]):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), name
+    if want_h:
+        assert torch.equal(h.view(torch.int16), ref[0].view(torch.int16)), "h"
+    idx = np.arange(n) if sample is None else hin.sample_tokens(n, sample, seed=seed)
+    ti = torch.from_numpy(idx).to(DEV)
+    hb = hin.bits(ref[0].reshape(n, d).index_select(0, ti))
+    off = check_norm(hin.bits(y.reshape(n, d).index_select(0, ti)), oracle.rmsnorm(hb, g.cpu().numpy(), NEPS), "y")
+    return t, g, y, off
+
+
+@pytest.mark.parametrize("hc,d,n,want_h", [
+    (4, 5120, 2049, False), (4, 5120, 4097, True), (4, 5120, 20011, False),   # persistent kernel, ragged tails
+    (4, 2560, 3000, True), (4, 1024, 2500, False), (4, 256, 2200, True),      # other wave-specialised widths
+    (4, 5120, 64, False), (4, 5120, 2048, True),                              # two-pass path + norm kernel
+    (4, 64, 300, True), (4, 6144, 2100, False),                               # other widths (k_coop)
+    (2, 5120, 3000, False), (3, 1000, 37, True), (8, 512, 2100, False)])      # other stream counts
+def test_fused_norm_matches_oracle(hc, d, n, want_h):
+    _fused_norm_case(hc, d, n, 21, want_h)
+
+
+def test_fused_norm_full_size_sampled():
+    # the large prefill workload (65,536 tokens x 4 x 5120), in the launch
+    # configuration the benchmark times, on sampled tokens
+    _fused_norm_case(4, 5120, 65536, 22, False, sample=300)
+
+
+def test_fused_norm_agrees_with_pre_norm_and_is_deterministic():
+    # the fused call's norm and the one-pass hc_pre_norm on the same pre
+    # (one ulp at most: their sums of squares run in different orders);
+    # repeated calls agree bit for bit, and a token's y does not depend on
+    # the other tokens of its call
+    n, d = 20011, 5120
+    t, g, y, _ = _fused_norm_case(4, d, n, 23, False)
+    y2 = hcl.hc_fused_mix_pre_norm(t["R"], t["W"], t["scale"], t["base"], g, norm_eps=NEPS)[0]
+    lo, hi = 5000, 5000 + 3001
+    y3 = hcl.hc_fused_mix_pre_norm(t["R"][:, lo:hi].contiguous(), t["W"], t["scale"], t["base"], g,
+                                   norm_eps=NEPS)[0]
+    pre = hcl.hc_fused_mix_pre(t["R"], t["W"], t["scale"], t["base"], norm_eps=NEPS)[1]
+    yp = hcl.hc_pre_norm(t["R"].reshape(n, 4, d), pre.reshape(n, 4), g, NEPS)
+    torch.cuda.synchronize()
+    check_bf16_exact(hin.bits(y2), hin.bits(y), "y, second call")
+    check_bf16_exact(hin.bits(y3), hin.bits(y[:, lo:hi].contiguous()), "y of a slice")
+    check_norm(hin.bits(yp), hin.bits(y).reshape(n, d), "y vs hc_pre_norm")
+
+
+def test_fused_norm_graph_replay():
+    # captured once, replayed three times with eager work between replays:
+    # every replay equals the eager call
+    n, d = 4097, 5120
+    w = _wl(4, d)
+    t = hin.make_inputs(w, DEV, seed=24, n_tokens=n)
+    g = hin.make_gamma(d, DEV, seed=24)
+    ws = hcl.Workspace(DEV)
+    eager = hcl.hc_fused_mix_pre_norm(t["R"], t["W"], t["scale"], t["base"], g, norm_eps=NEPS, workspace=ws)[0]
+    out = {"y": torch.empty_like(eager), "post": torch.empty(1, n, 4, device=DEV),
+           "comb": torch.empty(1, n, 4, 4, device=DEV), "pre": torch.empty(1, n, 4, device=DEV)}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            hcl.hc_fused_mix_pre_norm(t["R"], t["W"], t["scale"], t["base"], g, norm_eps=NEPS, workspace=ws,
+                                      out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    for k in range(3):
+        out["y"].zero_()
+        graph.replay()
+        hcl.hc_rmsnorm(eager.reshape(n, d), g, NEPS)      # eager work between replays
+        torch.cuda.synchronize()
+        check_bf16_exact(hin.bits(out["y"]), hin.bits(eager), "replay %d" % k)
