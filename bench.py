@@ -67,7 +67,7 @@ def measured_traffic(kernel: str, n: int, d: int):
 # k_spec<KS, true, true>), that of other widths, and hc_post's kernel;
 # shorter calls run the two-pass pair k_part + k_fin (summarised together)
 KERNELS = {"k_spec": "hc_fused_mix_pre", "k_spec_post": "hc_post_mix_pre", "k_coop": "hc_fused_mix_pre",
-           "k_post": "hc_post"}
+           "k_post": "hc_post", "k_pre_norm": "hc_pre_norm", "k_rmsnorm": "hc_rmsnorm"}
 COPY_CALIB_BYTES = 1 << 30
 
 
@@ -78,6 +78,8 @@ def kernel_key(name: str) -> str:
     key = short.split("<")[0].split("::")[-1]
     if key == "k_spec" and short.replace(" ", "").endswith("true,true>"):
         key = "k_spec_post"
+    if key == "k_pre_norm" and short.replace(" ", "").startswith("k_pre_norm<0,"):
+        key = "k_rmsnorm"          # the norm kernel on h (hc_rmsnorm, and the fused call's norm)
     return key
 
 
@@ -109,7 +111,9 @@ def summarize_counters(d: str, n: int, dd: int, command: str, tag: str = ""):
     kib = COPY_CALIB_BYTES / 1024.0
     f_scale, w_scale = kib / f_copy, kib / w_copy
     fb, pb = algorithmic_bytes(n, dd)
-    alg = {"k_spec": fb, "k_spec_post": boundary_bytes(n, dd), "k_coop": fb, "k_post": pb}
+    _, bn_pre, bn_rms = norm_bytes(n, dd)
+    alg = {"k_spec": fb, "k_spec_post": boundary_bytes(n, dd), "k_coop": fb, "k_post": pb,
+           "k_pre_norm": bn_pre, "k_rmsnorm": bn_rms}
     src = kernel_source_hash()
     lines = ["# HBM traffic per launch, n=%d tokens, d=%d" % (n, dd), "",
              "Command (one pass per counter):", "", "    " + command, "",
@@ -176,6 +180,8 @@ def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, step
     if hc == 4:
         bp, _, bk_pre, bk_mix = backward_bytes(n, dd, min(32, max(1, (n + 255) // 256)))
         alg.update(k_post_bwd=bp, k_pre_bwd=bk_pre, k_mix_bwd=bk_mix)
+    _, bn_pre, bn_rms = norm_bytes(n, dd, hc)
+    alg.update(k_pre_norm=bn_pre, k_rmsnorm=bn_rms)      # hc_pre_norm (y only) and the norm of h
     title = "# Kernel durations, n=%d tokens, d=%d" % (n, dd) + (", hc=%d" % hc if hc != 4 else "")
     lines = [title, "", "Command:", "", "    " + command, "",
              "| kernel | calls | average us | min us | max us | algorithmic GB/s | of 8 TB/s | timed-region average us | of 8 TB/s |",
@@ -500,6 +506,97 @@ def bench_boundary(args, hcl, hin, torch, np, w, t, ws, outs, Rout, dev):
     print(json.dumps(line), flush=True)
 
 
+def norm_bytes(n: int, d: int, hc: int = 4):
+    """Minimum HBM bytes of the pre-sublayer RMSNorm calls.  The fused call
+    (y only): R read, y and pre/post/comb written, the weights, scale, base
+    and the norm weight read once.  hc_pre_norm (y only): R and pre read, y
+    written, the norm weight read once.  hc_rmsnorm: h read, y written."""
+    M = (2 + hc) * hc
+    fused = n * (hc * d * 2 + d * 2 + (hc + hc + hc * hc) * 4) + M * hc * d * 4 + (3 + M) * 4 + d * 4
+    pre_norm = n * (hc * d * 2 + hc * 4 + d * 2) + d * 4
+    rms = n * d * 4 + d * 4
+    return fused, pre_norm, rms
+
+
+def bench_norm(args, hcl, hin, torch, np, w, t, ws, dev):
+    """--norm: the step is one hc_fused_mix_pre_norm call (y only: the fused
+    mix + Sinkhorn + hc_pre, then the pre-sublayer RMSNorm); hc_pre_norm (the
+    one-pass hc_pre + norm kernel, the roofline entry) and hc_rmsnorm are
+    timed beside it.  Prints one JSON line like the default step."""
+    n, d, hc = w.n, w.d, w.hc
+    R, W, s, b = t["R"], t["W"], t["scale"], t["base"]
+    g = hin.make_gamma(d, dev)
+    out = dict(y=torch.empty(w.B, w.T, d, dtype=torch.bfloat16, device=dev),
+               pre=torch.empty(w.B, w.T, hc, device=dev), post=torch.empty(w.B, w.T, hc, device=dev),
+               comb=torch.empty(w.B, w.T, hc, hc, device=dev))
+    y2 = torch.empty_like(out["y"])
+    h = torch.empty_like(out["y"])
+
+    def fused_norm():
+        hcl.hc_fused_mix_pre_norm(R, W, s, b, g, sinkhorn_iters=w.iters, hc_eps=w.hc_eps, norm_eps=w.norm_eps,
+                                  workspace=ws, out=out)
+
+    def pre_norm():
+        hcl.hc_pre_norm(R, out["pre"], g, w.norm_eps, out=y2)
+
+    def rms():
+        hcl.hc_rmsnorm(h, g, w.norm_eps, out=y2)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for a, z in evs:
+            a.record(stream)
+            fn()
+            z.record(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps, np.array([a.elapsed_time(z) for a, z in evs]) * 1e3
+
+    ms, vf = timed(fused_norm)
+    hcl.hc_pre(R, out["pre"], out=h)
+    _, vp = timed(pre_norm)
+    _, vr = timed(rms)
+    bf, bp, br = norm_bytes(n, d, hc)
+
+    def entry(v, nbytes):
+        gbs = nbytes / (v.mean() * 1e-6) / 1e9
+        return {"avg_us": round(float(v.mean()), 2), "median_us": round(float(np.median(v)), 2),
+                "min_us": round(float(v.min()), 2), "GB/s": round(gbs, 1),
+                "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes}
+    kp = entry(vp, bp)
+    if args.copy_calib:
+        src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    line = {
+        "metric": "tokens/s + achieved HBM GB/s (% of peak), fused hc mix+pre and hc_post, d=5120",
+        "value": round(n / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": DTYPE,
+        "data": "synthetic (seeded N(0,1) residual, N(0,0.007) weights, 1 + N(0,0.25) norm weight)",
+        "config": {"workload": "%s: B=%d T=%d hc=%d d=%d (%d tokens), sinkhorn_iters=%d, step = one "
+                               "hc_fused_mix_pre_norm call (y only)" % (w.name, w.B, w.T, hc, d, n, w.iters),
+                   "tokens": n, "d": d, "hc": hc, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "k_pre_norm (hc_pre_norm, y only)", "achieved": kp["GB/s"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kp["frac_of_peak"],
+                     "traffic": measured_traffic("k_pre_norm", n, d), "algorithmic_bytes": bp,
+                     "avg_launch_us": kp["avg_us"]},
+        "kernels": {"hc_fused_mix_pre_norm": entry(vf, bf), "hc_pre_norm": kp, "hc_rmsnorm": entry(vr, br)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -533,6 +630,9 @@ def main():
                          "from one HIP graph; the step is one sublayer")
     ap.add_argument("--backward", action="store_true",
                     help="time one sublayer's backward instead: hc_post_backward then hc_mix_pre_backward")
+    ap.add_argument("--norm", action="store_true",
+                    help="time the pre-sublayer RMSNorm instead: one hc_fused_mix_pre_norm call, with "
+                         "hc_pre_norm and hc_rmsnorm timed beside it")
     ap.add_argument("--boundary", action="store_true",
                     help="time the sublayer boundary instead: one hc_post_mix_pre call (hc_post of "
                          "this sublayer, then the next one's fused mix + Sinkhorn + hc_pre)")
@@ -591,6 +691,10 @@ def main():
     packed = hcl.hc_pack_weights(W) if args.packed else None
     if args.boundary:
         bench_boundary(args, hcl, hin, torch, np, w, t, ws, outs, Rout, dev)
+        return
+    if args.norm:
+        del Rout, outs
+        bench_norm(args, hcl, hin, torch, np, w, t, ws, dev)
         return
     if args.backward:
         if w.hc != 4:
