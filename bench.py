@@ -597,6 +597,77 @@ def bench_norm(args, hcl, hin, torch, np, w, t, ws, dev):
     print(json.dumps(line), flush=True)
 
 
+def bench_probe(args, hcl, torch, np, w, dev):
+    """--probe: the streaming ceilings the kernels' roofline fractions are
+    read against, from the library's bandwidth probe (hc_probe_stream: the
+    streaming kernels' access pattern) and torch's copy, on buffers of the
+    workload's residual size (and 1 GiB): a copy (read + write), a read, and
+    an immediate second read of the same buffer.  Prints one JSON line."""
+    stream = torch.cuda.current_stream(dev)
+    nbytes = w.n * w.hc * w.d * 2
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        v = []
+        for _ in range(args.steps):
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            z.record(stream)
+            torch.cuda.synchronize()
+            v.append(a.elapsed_time(z) * 1e3)
+        return np.array(v)
+
+    res = {}
+    for label, size in (("residual", nbytes), ("1GiB", 1 << 30)):
+        src = torch.empty(size, dtype=torch.uint8, device=dev)
+        src.random_(0, 255)
+        dst = torch.empty_like(src)
+        # the probe over 1..16 workgroups per compute unit: each figure is the
+        # best launch shape's
+        for name, fn, moved in (("probe_copy", lambda g: hcl.probe_stream(src, dst, g), 2 * size),
+                                ("probe_read", lambda g: hcl.probe_stream(src, None, g), size),
+                                ("torch_copy", None, 2 * size)):
+            shapes = (1, 2, 4, 8, 16) if fn else (0,)
+            best = None
+            for g in shapes:
+                v = timed((lambda g=g: fn(g)) if fn else (lambda: dst.copy_(src)))
+                if best is None or v.mean() < best[1].mean():
+                    best = (g, v)
+            g, v = best
+            res["%s_%s" % (name, label)] = {"bytes": moved, "avg_us": round(float(v.mean()), 2),
+                                            "min_us": round(float(v.min()), 2),
+                                            "GB/s": round(moved / (v.mean() * 1e-6) / 1e9, 1),
+                                            "frac_of_peak": round(moved / (v.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            if fn:
+                res["%s_%s" % (name, label)]["wg_per_cu"] = g
+        # an immediate re-read: the same buffer read twice back to back, the second timed
+        rr = []
+        gr = res["probe_read_%s" % label]["wg_per_cu"]
+        for _ in range(args.steps):
+            hcl.probe_stream(src, None, gr)
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            hcl.probe_stream(src, None, gr)
+            z.record(stream)
+            torch.cuda.synchronize()
+            rr.append(a.elapsed_time(z) * 1e3)
+        rr = np.array(rr)
+        res["probe_reread_%s" % label] = {"bytes": size, "avg_us": round(float(rr.mean()), 2),
+                                          "GB/s": round(size / (rr.mean() * 1e-6) / 1e9, 1),
+                                          "frac_of_peak": round(size / (rr.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del src, dst
+        torch.cuda.empty_cache()
+    best = res["probe_copy_residual"]["GB/s"]
+    line = {"metric": "HBM streaming ceilings (bandwidth probe)", "value": best, "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "vs_baseline": None,
+            "data": "random bytes", "config": {"workload": "%s residual size: %d bytes" % (w.name, nbytes)},
+            "probes": res}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -630,6 +701,9 @@ def main():
                          "from one HIP graph; the step is one sublayer")
     ap.add_argument("--backward", action="store_true",
                     help="time one sublayer's backward instead: hc_post_backward then hc_mix_pre_backward")
+    ap.add_argument("--probe", action="store_true",
+                    help="measure the streaming ceilings instead: the library's bandwidth probe (copy, read, "
+                         "re-read) and torch's copy on residual-sized and 1 GiB buffers")
     ap.add_argument("--norm", action="store_true",
                     help="time the pre-sublayer RMSNorm instead: one hc_fused_mix_pre_norm call, with "
                          "hc_pre_norm and hc_rmsnorm timed beside it")
@@ -674,6 +748,9 @@ def main():
         import dataclasses
         w = dataclasses.replace(w, hc=args.hc)
     n, d = w.n, w.d
+    if args.probe:
+        bench_probe(args, hcl, torch, np, w, dev)
+        return
     if args.chain:
         if w.hc != 4:
             print("--chain runs four streams only", file=sys.stderr)

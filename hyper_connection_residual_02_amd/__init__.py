@@ -26,7 +26,7 @@ __all__ = [
     "HCError", "load", "lib_path", "hc_mixes", "hc_split_sinkhorn", "hc_pre", "hc_post",
     "hc_rmsnorm", "hc_pre_norm", "hc_fused_mix_pre", "hc_fused_mix_pre_norm", "hc_fused_mix_pre_noalloc", "hc_post_mix_pre", "hc_pack_weights", "hc_diag_scale", "hc_fused_workspace_bytes",
     "hc_post_backward", "hc_mix_pre_backward", "hc_backward_workspace_bytes",
-    "Workspace", "workspace_status", "check_workspace", "noalloc_status", "debug_force_timeout",
+    "Workspace", "workspace_status", "probe_stream", "check_workspace", "noalloc_status", "debug_force_timeout",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +71,7 @@ def load():
         "hc_pack_weights": [P, P, SZ, I32, I32, P],
         "hc_fused_mix_pre_packed": [P, P, SZ, P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, F32, F32, P],
         "hc_diag_scale": [P, P, P, I64, I32, P],
+        "hc_probe_stream": [P, P, SZ, I32, P],
         "hc_fused_mix_pre_noalloc": [P, P, P, P, P, P, P, P, P, I64, I32, I32, I32, F32, F32, P],
         "hc_post_backward": [P, P, P, P, P, P, P, P, I64, I32, I32, P],
         "hc_mix_pre_backward": [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, I64, I32, I32, I32, F32, F32, P],
@@ -128,6 +129,21 @@ def _call(fn: str, *args):
     st = getattr(load(), fn)(*args)
     if st != 0:
         raise HCError(fn, st)
+
+
+def probe_stream(src: torch.Tensor, dst: torch.Tensor | None = None, wg_per_cu: int = 0) -> None:
+    """The bandwidth probe: copy src into dst (same size), or read src when
+    dst is None, with the streaming kernels' access pattern, on wg_per_cu
+    workgroups per compute unit (0: two)."""
+    dev = src.device
+    if src.device.type != "cuda" or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    nbytes = src.numel() * src.element_size()
+    if dst is not None and (dst.device != dev or not dst.is_contiguous()
+                            or dst.numel() * dst.element_size() != nbytes):
+        raise ValueError("dst must be a contiguous GPU tensor of src's size, on its device")
+    with torch.cuda.device(dev):
+        _call("hc_probe_stream", _ptr(src), _ptr(dst), nbytes, int(wg_per_cu), _stream(dev))
 
 
 def hc_fused_workspace_bytes(n: int, hc: int, d: int) -> int:

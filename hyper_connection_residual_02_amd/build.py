@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libhc.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["hc_api.hip", "hc_stream.hip", "hc_sinkhorn.hip", "hc_coop.hip", "hc_general.hip", "hc_backward.hip",
-           "hc_norm.hip"]
+           "hc_norm.hip", "hc_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

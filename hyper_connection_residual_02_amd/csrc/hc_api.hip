@@ -491,6 +491,17 @@ int hc_noalloc_status(int clear) {
     return r < 0 ? HC_ERR_DEVICE : (r ? HC_ERR_TIMEOUT : HC_OK);
 }
 
+int hc_probe_stream(const void* src, void* dst, size_t bytes, int32_t wg_per_cu, void* stream) {
+    if (bytes % 16 != 0) return HC_ERR_SHAPE;
+    if (wg_per_cu < 0 || wg_per_cu > 32) return HC_ERR_VALUE;
+    if (bytes == 0) return HC_OK;
+    if (!src) return HC_ERR_NULL;
+    if (!al16(src) || (dst && !al16(dst))) return HC_ERR_ALIGN;
+    if (dst && overlap(span(src, bytes), span(dst, bytes))) return HC_ERR_ALIAS;
+    return hc::launch_probe(src, dst, bytes, wg_per_cu ? wg_per_cu : 2, (hipStream_t)stream) ? HC_ERR_LAUNCH
+                                                                                              : HC_OK;
+}
+
 int hc_debug_force_timeout(int calls) {
     if (calls < 0) return HC_ERR_VALUE;
     hc::set_force_timeout(calls);

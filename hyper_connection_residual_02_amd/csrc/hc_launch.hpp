@@ -24,6 +24,10 @@ int norm_waves(int d);
 int launch_pre_norm(const void* R, const float* pre, const float* gamma, void* h, void* y, int64_t n, int hc,
                     int d, float norm_eps, hipStream_t s);
 
+// Bandwidth probe (hc_probe.hip): copy src -> dst, or read src when dst is
+// null, on wg_per_cu workgroups per compute unit.
+int launch_probe(const void* src, void* dst, uint64_t bytes, int wg_per_cu, hipStream_t s);
+
 // Standalone split + Sinkhorn (hc_sinkhorn.hip); pre may be NULL (not written).
 int launch_split(const float* mixes, const float* scale, const float* base, float* pre, float* post,
                  float* comb, int64_t n, int iters, float eps, hipStream_t s);

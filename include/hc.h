@@ -444,6 +444,20 @@ int hc_fused_mix_pre_noalloc(const void *R, const float *hc_fn,
                              int32_t sinkhorn_iters, float hc_eps,
                              float norm_eps, void *stream);
 
+/*
+ * hc_probe_stream -- a measurement probe, not a step of the method: a plain
+ * HBM stream with the access pattern of the library's streaming kernels
+ * (16-byte non-temporal accesses, two in flight per lane) on wg_per_cu
+ * workgroups of 256 lanes per compute unit (0: two, as the streaming
+ * kernels use on long runs; at most 32, else HC_ERR_VALUE).  dst non-NULL:
+ * copies `bytes` from src to dst; dst NULL: reads src only.  It gives the
+ * copy and read rates the kernels' roofline fractions are compared with.
+ * bytes % 16 == 0 (else HC_ERR_SHAPE); src, dst 16-byte aligned; dst must
+ * not overlap src.  Asynchronous on `stream`.
+ */
+int hc_probe_stream(const void *src, void *dst, size_t bytes,
+                    int32_t wg_per_cu, void *stream);
+
 /* HC_SCRATCH_BYTES, the static scratch of hc_fused_mix_pre_noalloc (host only). */
 size_t hc_scratch_bytes(void);
 

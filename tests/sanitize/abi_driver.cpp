@@ -147,6 +147,13 @@ int main() {
     expect("mix_pre_backward iters", mix_b(W, 1u << 24, 4, 256, 65), HC_ERR_UNSUPPORTED);
     expect("mix_pre_backward hc", mix_b(W, 1u << 24, 2, 256, 20), HC_ERR_UNSUPPORTED);
 
+    // the bandwidth probe
+    expect("probe n=0", hc_probe_stream(P(A), P(B), 0, 0, nullptr), HC_OK);
+    expect("probe shape", hc_probe_stream(P(A), P(B), 24, 0, nullptr), HC_ERR_SHAPE);
+    expect("probe null", hc_probe_stream(nullptr, P(B), 4096, 0, nullptr), HC_ERR_NULL);
+    expect("probe alias", hc_probe_stream(P(A), P(A + 1024), 4096, 0, nullptr), HC_ERR_ALIAS);
+    expect("probe wg", hc_probe_stream(P(A), P(B), 4096, 33, nullptr), HC_ERR_VALUE);
+
     // workspace status and diagnostics
     expect("status null", hc_workspace_status(nullptr, 256, 0), HC_ERR_NULL);
     expect("status align", hc_workspace_status(P(W + 16), 256, 0), HC_ERR_ALIGN);

@@ -128,6 +128,19 @@ def test_norm_checks(lib):
     assert g(y=B + 16) == ALIAS             # y overlaps pre
 
 
+def test_probe_checks(lib):
+    f = lambda s=A, d=B, nb=4096, wg=0: lib.hc_probe_stream(P(s), P(d), nb, wg, None)
+    assert f(nb=0) == OK
+    assert f(nb=24) == SHAPE
+    assert f(s=0) == NULL
+    assert f(s=A + 8) == ALIGN
+    assert f(d=B + 4) == ALIGN
+    assert f(d=A + 1024) == ALIAS
+    assert lib.hc_probe_stream(P(A), P(0), 24, 0, None) == SHAPE
+    assert f(wg=33) == VALUE
+    assert f(wg=-1) == VALUE
+
+
 def test_split_checks(lib):
     f = lambda m=A, s=B, b=B + 64, pre=C, post=D_, comb=E, n=4, hc=4, it=20, eps=1e-6: \
         lib.hc_split_sinkhorn(P(m), P(s), P(b), P(pre), P(post), P(comb), n, hc, it, eps, None)
