@@ -39,10 +39,25 @@ def algorithmic_bytes(n: int, d: int, hc: int = 4):
     return fused, post
 
 
-def kernel_source_hash() -> str:
+# the sources each measured kernel (and its launch configuration) is built
+# from: a counter record stays valid while these are unchanged
+KERNEL_SOURCES = {
+    "k_spec": ("hc_coop.hip", "hc_device.hpp"),
+    "k_spec_post": ("hc_coop.hip", "hc_device.hpp"),
+    "k_coop": ("hc_coop.hip", "hc_device.hpp"),
+    "k_post": ("hc_stream.hip", "hc_device.hpp"),
+    "k_pre_norm": ("hc_norm.hip", "hc_device.hpp"),
+    "k_rmsnorm": ("hc_norm.hip", "hc_device.hpp"),
+}
+
+
+def kernel_source_hash(kernel: str | None = None) -> str:
+    """sha256 (first 16 hex) of the kernel's sources, or of every file in
+    csrc/ when no kernel is named."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "hyper_connection_residual_02_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    files = KERNEL_SOURCES.get(kernel) if kernel else None
+    for f in sorted(files or os.listdir(csrc)):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -57,7 +72,7 @@ def measured_traffic(kernel: str, n: int, d: int):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != kernel_source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -131,7 +146,8 @@ def summarize_counters(d: str, n: int, dd: int, command: str, tag: str = ""):
         total = fm * f_scale * 1024 + wm * w_scale * 1024
         rec = {"kernel": k, "entry_point": api, "n": n, "d": dd, "fetch_kib": fm, "write_kib": wm,
                "fetch_scale": f_scale, "write_scale": w_scale, "bytes_per_launch": round(total),
-               "algorithmic_bytes": alg[k], "source_hash": src, "command": command}
+               "algorithmic_bytes": alg[k], "source_hash": kernel_source_hash(k),
+               "sources": list(KERNEL_SOURCES.get(k, ())), "command": command}
         with open(os.path.join(PROFILE_DIR, "hbm_traffic_%s_n%d_d%d.json" % (k, n, dd)), "w") as fh:
             json.dump(rec, fh, indent=1)
             fh.write("\n")
