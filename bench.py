@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E peak, GB/s
+LLC_BYTES = 256 << 20            # MI355X last-level (Infinity) cache
 
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -917,10 +918,17 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    if p_mean >= f_mean:
-        dom = dict(name="hc_post", kernel="k_post", us=p_mean, bytes=pb, gbs=p_gbs)
+    # A residual that fits the last-level cache may be found there by the
+    # step's next launch, so for such workloads (prefill, decode) the
+    # roofline reports the cold launch (every input evicted first); the large
+    # workload's residual is ten times the cache, and its in-step launches
+    # are the measure.
+    cold = n * w.hc * d * 2 <= LLC_BYTES
+    p_us, f_us = (pc_mean, fc_mean) if cold else (p_mean, f_mean)
+    if p_us >= f_us:
+        dom = dict(name="hc_post", kernel="k_post", us=p_us, bytes=pb, gbs=pb / (p_us * 1e-6) / 1e9)
     else:
-        dom = dict(name="hc_fused_mix_pre", kernel="k_spec", us=f_mean, bytes=fb, gbs=f_gbs)
+        dom = dict(name="hc_fused_mix_pre", kernel="k_spec", us=f_us, bytes=fb, gbs=fb / (f_us * 1e-6) / 1e9)
     if w.hc != 4:
         dom["kernel"] = "k_gpost" if dom["name"] == "hc_post" else "k_gmm + k_gsplit + k_gpre"
     traffic = measured_traffic(dom["kernel"], n, d) if w.hc == 4 else None
@@ -971,7 +979,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom["name"], "achieved": round(dom["gbs"], 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": dom["bytes"],
-                     "avg_launch_us": round(dom["us"], 2)},
+                     "avg_launch_us": round(dom["us"], 2),
+                     "timing": "cold: every input evicted before each launch (the residual fits the "
+                               "last-level cache)" if cold else "in the step"},
         "kernels": {
             "hc_fused_mix_pre": {"avg_us": round(f_mean, 2), "median_us": round(f_med, 2),
                                  "min_us": round(f_min, 2), "GB/s": round(f_gbs, 1),
