@@ -207,7 +207,7 @@ int hc_split_sinkhorn(const float* mixes, const float* hc_scale, const float* hc
 
 size_t hc_fused_workspace_bytes(int64_t n, int32_t hc_, int32_t d) {
     if (check_nd(n, hc_, d) != HC_OK || n == 0) return 0;
-    if (hc_ != 4) return hc::gen_ws_bytes(n, hc_);
+    if (hc_ != 4) return hc::gen_ws_bytes(n, hc_, d);
     hc::CoopPlan p;
     if (!hc::coop_plan(n, d, p)) return 0;
     return p.ws_bytes;
@@ -277,7 +277,7 @@ static int gen_fused(const hc::PostIn* prev, const void* R, const float* hc_fn, 
     if (!R || !hc_fn || !hc_scale || !hc_base || !h || !post || !comb) return HC_ERR_NULL;
     if (prev && (!prev->x || !prev->post || !prev->comb || !prev->Rout)) return HC_ERR_NULL;
     if (!workspace) return HC_ERR_WORKSPACE;
-    const size_t wsb = hc::gen_ws_bytes(n, hc_);
+    const size_t wsb = hc::gen_ws_bytes(n, hc_, d);
     if (workspace_bytes < wsb) return HC_ERR_WORKSPACE;
     if (!al16(R) || !al16(hc_fn) || ((uintptr_t)workspace & 255u) || !al4(hc_scale) || !al4(hc_base) || !al16(h) ||
         !al16(post) || !al16(comb) || (pre && !al16(pre)) || (mixes && !al16(mixes)))

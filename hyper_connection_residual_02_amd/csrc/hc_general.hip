@@ -38,11 +38,21 @@ bool gen_hc(int hc_) { return hc_ >= 1 && hc_ <= kGenMaxHC && hc_ != kHC; }
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// Bytes of the weights split into k_gmm's B fragments: per 64-element
+// chunk of the reduction axis, 2 k-steps x 3 pieces x ceil(M / 16) column
+// tiles x 64 lanes of 16 bytes.
+static size_t packed_gen_bytes(int hc_, int d) {
+    const size_t M = (size_t)(2 + hc_) * hc_, K = (size_t)hc_ * d;
+    return (K + 63) / 64 * 2 * 3 * ((M + 15) / 16) * 64 * 16;
+}
+
 // The fused call's workspace: k_gmm's partial sums (kSeg segments of
-// (2 + hc) * hc + 2 floats per token), then the mixes and pre.
-size_t gen_ws_bytes(int64_t n, int hc_) {
+// (2 + hc) * hc + 2 floats per token), then the mixes and pre, then the
+// weights split once per call.
+size_t gen_ws_bytes(int64_t n, int hc_, int d) {
     const size_t M = (size_t)(2 + hc_) * hc_;
-    return align256((size_t)n * 8 * (M + 2) * 4) + align256((size_t)n * M * 4) + align256((size_t)n * hc_ * 4);
+    return align256((size_t)n * 8 * (M + 2) * 4) + align256((size_t)n * M * 4) + align256((size_t)n * hc_ * 4) +
+           align256(packed_gen_bytes(hc_, d));
 }
 
 namespace {
@@ -54,6 +64,7 @@ constexpr int kGThreads = 256;
 // stream (x = R[t] read as K contiguous values).
 constexpr int kSeg = 8;      // segments of the reduction axis, added in order
 constexpr int kKC = 64;      // reduction elements per staged chunk (two MFMA k-steps)
+constexpr int64_t kPackMinN = 1024;   // fused calls from this many tokens split the weights once
 
 template <int HC>
 struct Gmm {
@@ -76,21 +87,27 @@ struct GmmLds {
 // Chunk ch of the reduction axis for this workgroup's tokens t0..t0+T-1,
 // loaded into registers (zeros past n and past K): residual pieces of 8
 // elements (token, 16-byte piece) and weight pieces of 4 (row j, 4 floats).
-template <int HC, int T>
+// PK: the weights come split already (k_gpack), as the chunk's B fragments
+// (kP 16-byte words per thread).
+template <int HC, int T, bool PK = false>
 struct GmmRegs {
     static constexpr int kA = (T * (kKC / 8) + 2 * T - 1) / (2 * T);      // residual pieces per thread
-    static constexpr int kW = (Gmm<HC>::M * (kKC / 4) + 2 * T - 1) / (2 * T);   // weight pieces per thread
+    static constexpr int kW = PK ? 1 : (Gmm<HC>::M * (kKC / 4) + 2 * T - 1) / (2 * T);   // weight pieces per thread
+    static constexpr int kFr = 2 * 3 * Gmm<HC>::CT * 64;                  // B fragments of a chunk
+    static constexpr int kP = PK ? (kFr + 2 * T - 1) / (2 * T) : 1;
     uint4 a[kA];
     float4 w[kW];
+    u32x4 p[kP];
 };
 
-template <int HC, int T>
-__device__ __forceinline__ void gmm_load(GmmRegs<HC, T>& g, const uint16_t* __restrict__ R,
-                                         const float* __restrict__ W, int64_t t0, int64_t n, int64_t K, int64_t ch) {
+template <int HC, int T, bool PK = false>
+__device__ __forceinline__ void gmm_load(GmmRegs<HC, T, PK>& g, const uint16_t* __restrict__ R,
+                                         const float* __restrict__ W, const u32x4* __restrict__ Wp, int64_t t0,
+                                         int64_t n, int64_t K, int64_t ch) {
     constexpr int M = Gmm<HC>::M;
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < GmmRegs<HC, T>::kA; ++i) {
+    for (int i = 0; i < GmmRegs<HC, T, PK>::kA; ++i) {
         const int p = i * 2 * T + tid;                  // piece p: token p / 8, elements 8 (p % 8) of the chunk
         const int tk = p >> 3;
         const int64_t k = ch * kKC + 8 * (p & 7);
@@ -98,8 +115,18 @@ __device__ __forceinline__ void gmm_load(GmmRegs<HC, T>& g, const uint16_t* __re
         if (p < T * 8 && t0 + tk < n && k < K) v = *reinterpret_cast<const uint4*>(R + (t0 + tk) * K + k);
         g.a[i] = v;
     }
+    if constexpr (PK) {
+        constexpr int kFr = GmmRegs<HC, T, PK>::kFr;
+        const u32x4* src = Wp + ch * kFr;
 #pragma unroll
-    for (int i = 0; i < GmmRegs<HC, T>::kW; ++i) {
+        for (int i = 0; i < GmmRegs<HC, T, PK>::kP; ++i) {
+            const int f = i * 2 * T + tid;
+            g.p[i] = f < kFr ? src[f] : u32x4{0u, 0u, 0u, 0u};
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < GmmRegs<HC, T, PK>::kW; ++i) {
         const int p = i * 2 * T + tid;                  // piece p: row p / 16, elements 4 (p % 16) of the chunk
         const int j = p >> 4;
         const int64_t k = ch * kKC + 4 * (p & 15);
@@ -111,17 +138,28 @@ __device__ __forceinline__ void gmm_load(GmmRegs<HC, T>& g, const uint16_t* __re
 
 // The loaded chunk into LDS buffer q: residual rows as they are, weights
 // split into their three exact bf16 pieces in B-fragment order.
-template <int HC, int T>
-__device__ __forceinline__ void gmm_store(const GmmRegs<HC, T>& g, GmmLds<HC, T>& L, int q) {
+template <int HC, int T, bool PK = false>
+__device__ __forceinline__ void gmm_store(const GmmRegs<HC, T, PK>& g, GmmLds<HC, T>& L, int q) {
     constexpr int M = Gmm<HC>::M;
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < GmmRegs<HC, T>::kA; ++i) {
+    for (int i = 0; i < GmmRegs<HC, T, PK>::kA; ++i) {
         const int p = i * 2 * T + tid;
         if (p < T * 8) *reinterpret_cast<uint4*>(&L.a[q][p >> 3][8 * (p & 7)]) = g.a[i];
     }
+    if constexpr (PK) {
+        // the fragments as they are: L.b[q] has the same [k-step][piece][column tile][lane] order
+        constexpr int kFr = GmmRegs<HC, T, PK>::kFr;
+        u32x4* dst = reinterpret_cast<u32x4*>(&L.b[q][0][0][0][0]);
 #pragma unroll
-    for (int i = 0; i < GmmRegs<HC, T>::kW; ++i) {
+        for (int i = 0; i < GmmRegs<HC, T, PK>::kP; ++i) {
+            const int f = i * 2 * T + tid;
+            if (f < kFr) dst[f] = g.p[i];
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < GmmRegs<HC, T, PK>::kW; ++i) {
         const int p = i * 2 * T + tid;
         const int j = p >> 4;
         if (j >= M) continue;
@@ -150,6 +188,60 @@ __device__ __forceinline__ void gmm_store(const GmmRegs<HC, T>& g, GmmLds<HC, T>
 #pragma unroll
         for (int pc_ = 0; pc_ < 3; ++pc_)
             *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(&L.b[q][st][pc_][ct][lane]) + e0) =
+                u32x2{pc[pc_][0], pc[pc_][1]};
+    }
+}
+
+// The weights split once per call (k_gpack): chunk ch of the reduction
+// axis as the B fragments gmm_store forms in LDS, [ch][k-step][piece]
+// [column tile][lane] of 8 bf16, columns past M zero.  Thread = (chunk,
+// row j of the column tiles, 4 elements), with gmm_store's arithmetic, so
+// a packed call's fragments are bitwise an unpacked call's.
+template <int HC>
+__global__ __launch_bounds__(kGThreads) void k_gpack(const float* __restrict__ W, bf16x8* __restrict__ out,
+                                                     int64_t K) {
+    constexpr int M = Gmm<HC>::M, CT = Gmm<HC>::CT;
+    const int64_t C = (K + kKC - 1) / kKC;
+    const int64_t items = C * (16 * CT) * 16;
+    for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items;
+         it += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t ch = it / (16 * CT * 16);
+        const int rem = (int)(it - ch * (16 * CT * 16));
+        const int j = rem >> 4;                         // row of the column tiles (j >= M: padding)
+        const int kc = 4 * (rem & 15);                  // element of the chunk
+        const int st = kc >> 5, kk = kc & 31, grp = kk >> 3, e0 = kk & 7;
+        const int ct = j >> 4, lane = (j & 15) + 16 * grp;
+        const int64_t k = ch * kKC + kc;
+        float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (j < M && k < K) {
+            const float4 v = *reinterpret_cast<const float4*>(W + (int64_t)j * K + k);
+            x[0] = v.x;
+            x[1] = v.y;
+            x[2] = v.z;
+            x[3] = v.w;
+        }
+        uint32_t pc[3][2];
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+            uint32_t hw[3][2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const float v = x[e + u];
+                const __bf16 hi = (__bf16)v;
+                const float r1 = v - (float)hi;
+                const __bf16 mid = (__bf16)r1;
+                const __bf16 lo = (__bf16)(r1 - (float)mid);
+                hw[0][u] = (uint32_t)__builtin_bit_cast(uint16_t, hi);
+                hw[1][u] = (uint32_t)__builtin_bit_cast(uint16_t, mid);
+                hw[2][u] = (uint32_t)__builtin_bit_cast(uint16_t, lo);
+            }
+#pragma unroll
+            for (int pc_ = 0; pc_ < 3; ++pc_) pc[pc_][e >> 1] = pack2(hw[pc_][0], hw[pc_][1]);
+        }
+        bf16x8* base = out + ch * (2 * 3 * CT * 64);
+#pragma unroll
+        for (int pc_ = 0; pc_ < 3; ++pc_)
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(&base[((st * 3 + pc_) * CT + ct) * 64 + lane]) + e0) =
                 u32x2{pc[pc_][0], pc[pc_][1]};
     }
 }
@@ -215,10 +307,10 @@ __device__ __forceinline__ void gmm_mma(GmmAcc<HC>& A, const GmmLds<HC, T>& L, i
 // order.  G = 1: the totals give the mixes here.  G = kSeg: each segment's
 // sums go to part[t][s][F] (the dots, then the two sums of squares), and
 // k_gred adds them in the same order.
-template <int HC, int T>
+template <int HC, int T, bool PK = false>
 __global__ __launch_bounds__(2 * T) void k_gmm(const uint16_t* __restrict__ R, const float* __restrict__ W,
-                                               float* __restrict__ mixes, float* __restrict__ part, int64_t n, int d,
-                                               int G, float norm_eps) {
+                                               const u32x4* __restrict__ Wp, float* __restrict__ mixes,
+                                               float* __restrict__ part, int64_t n, int d, int G, float norm_eps) {
     constexpr int M = Gmm<HC>::M, CT = Gmm<HC>::CT, F = Gmm<HC>::F;
     __shared__ __attribute__((aligned(16))) GmmLds<HC, T> L;
     const int64_t K = (int64_t)HC * d;
@@ -241,13 +333,13 @@ __global__ __launch_bounds__(2 * T) void k_gmm(const uint16_t* __restrict__ R, c
     // chunks in flight: kPD register sets, chunk c in set (c - c0) % kPD,
     // each loaded kPD - 1 chunks ahead of its turn in LDS
     constexpr int kPD = Gmm<HC>::M > 48 ? 2 : 3;
-    GmmRegs<HC, T> g[kPD];
+    GmmRegs<HC, T, PK> g[kPD];
     int s = s0;
     int64_t send = (int64_t)(s + 1) * C / kSeg;        // first chunk past segment s
 #pragma unroll
     for (int i = 0; i < kPD; ++i)
-        if (c0 + i < c1) gmm_load<HC, T>(g[i], R, W, t0, n, K, c0 + i);
-    if (c0 < c1) gmm_store<HC, T>(g[0], L, 0);
+        if (c0 + i < c1) gmm_load<HC, T, PK>(g[i], R, W, Wp, t0, n, K, c0 + i);
+    if (c0 < c1) gmm_store<HC, T, PK>(g[0], L, 0);
     __syncthreads();
     auto close = [&]() {
         // segment s complete: into the total (or the partial sums)
@@ -298,8 +390,8 @@ __global__ __launch_bounds__(2 * T) void k_gmm(const uint16_t* __restrict__ R, c
             ++s;
             send = (int64_t)(s + 1) * C / kSeg;
         }
-        if (ch + 1 < c1) gmm_store<HC, T>(g[(i + 1) % kPD], L, q ^ 1);
-        if (ch + kPD < c1) gmm_load<HC, T>(g[i], R, W, t0, n, K, ch + kPD);
+        if (ch + 1 < c1) gmm_store<HC, T, PK>(g[(i + 1) % kPD], L, q ^ 1);
+        if (ch + kPD < c1) gmm_load<HC, T, PK>(g[i], R, W, Wp, t0, n, K, ch + kPD);
         __syncthreads();
     };
     for (int64_t ch = c0; ch < c1; ch += kPD) {
@@ -551,11 +643,15 @@ template <int HC>
 size_t gmm_part_bytes(int64_t n) { return align256((size_t)n * kSeg * Gmm<HC>::F * 4); }
 
 template <int HC, int T>
-int gmm_launch(const void* R, const float* W, float* mixes, float* part, int64_t n, int d, int G, float norm_eps,
-               hipStream_t s) {
+int gmm_launch(const void* R, const float* W, const u32x4* Wp, float* mixes, float* part, int64_t n, int d, int G,
+               float norm_eps, hipStream_t s) {
     const int64_t tiles = (n + T - 1) / T;
-    hipLaunchKernelGGL((k_gmm<HC, T>), dim3((unsigned)(tiles * G)), dim3(2 * T), 0, s,
-                       static_cast<const uint16_t*>(R), W, mixes, part, n, d, G, norm_eps);
+    if (Wp)
+        hipLaunchKernelGGL((k_gmm<HC, T, true>), dim3((unsigned)(tiles * G)), dim3(2 * T), 0, s,
+                           static_cast<const uint16_t*>(R), W, Wp, mixes, part, n, d, G, norm_eps);
+    else
+        hipLaunchKernelGGL((k_gmm<HC, T, false>), dim3((unsigned)(tiles * G)), dim3(2 * T), 0, s,
+                           static_cast<const uint16_t*>(R), W, Wp, mixes, part, n, d, G, norm_eps);
     if (hipGetLastError() != hipSuccess) return -1;
     if (G != 1) {
         hipLaunchKernelGGL(k_gred<HC>, dim3(grid_for(n)), dim3(kGThreads), 0, s, part, mixes, n,
@@ -571,20 +667,33 @@ int gmm_launch(const void* R, const float* W, float* mixes, float* part, int64_t
 // gives the same bits.
 template <int HC>
 struct MixOp {
-    static int run(const void* R, const float* W, float* mixes, float* part, int64_t n, int d, float norm_eps,
-                   hipStream_t s) {
+    static int run(const void* R, const float* W, const u32x4* Wp, float* mixes, float* part, int64_t n, int d,
+                   float norm_eps, hipStream_t s) {
         const int64_t cus = num_cus();
         const int G = (part && (n + 255) / 256 < cus) ? kSeg : 1;
         const int64_t want = G == 1 ? cus : (cus + kSeg - 1) / kSeg;      // tiles that fill the chip
         // smallest tile: the weight chunk (M x 64 floats) spread over its
         // threads stays within 8 loads each
         constexpr int M = Gmm<HC>::M;
-        if ((n + 255) / 256 >= want) return gmm_launch<HC, 256>(R, W, mixes, part, n, d, G, norm_eps, s);
-        if constexpr (M > 48) return gmm_launch<HC, 128>(R, W, mixes, part, n, d, G, norm_eps, s);
-        if ((n + 127) / 128 >= want) return gmm_launch<HC, 128>(R, W, mixes, part, n, d, G, norm_eps, s);
-        if constexpr (M > 16) return gmm_launch<HC, 64>(R, W, mixes, part, n, d, G, norm_eps, s);
-        if ((n + 63) / 64 >= want) return gmm_launch<HC, 64>(R, W, mixes, part, n, d, G, norm_eps, s);
-        return gmm_launch<HC, 32>(R, W, mixes, part, n, d, G, norm_eps, s);
+        if ((n + 255) / 256 >= want) return gmm_launch<HC, 256>(R, W, Wp, mixes, part, n, d, G, norm_eps, s);
+        if constexpr (M > 48) return gmm_launch<HC, 128>(R, W, Wp, mixes, part, n, d, G, norm_eps, s);
+        if ((n + 127) / 128 >= want) return gmm_launch<HC, 128>(R, W, Wp, mixes, part, n, d, G, norm_eps, s);
+        if constexpr (M > 16) return gmm_launch<HC, 64>(R, W, Wp, mixes, part, n, d, G, norm_eps, s);
+        if ((n + 63) / 64 >= want) return gmm_launch<HC, 64>(R, W, Wp, mixes, part, n, d, G, norm_eps, s);
+        return gmm_launch<HC, 32>(R, W, Wp, mixes, part, n, d, G, norm_eps, s);
+    }
+};
+
+template <int HC>
+struct PackOp {
+    static int run(const float* W, void* out, int d, hipStream_t s) {
+        const int64_t K = (int64_t)HC * d;
+        const int64_t items = (K + kKC - 1) / kKC * (16 * Gmm<HC>::CT) * 16;
+        int64_t blocks = (items + kGThreads - 1) / kGThreads;
+        if (blocks > (int64_t)num_cus() * 8) blocks = (int64_t)num_cus() * 8;
+        hipLaunchKernelGGL(k_gpack<HC>, dim3((unsigned)blocks), dim3(kGThreads), 0, s, W,
+                           static_cast<bf16x8*>(out), K);
+        return hipGetLastError() == hipSuccess ? 0 : -1;
     }
 };
 
@@ -630,7 +739,7 @@ struct PostOp {
 
 int launch_gen_mixes(const void* R, const float* W, float* mixes, int64_t n, int hc_, int d, float norm_eps,
                      hipStream_t s) {
-    return dispatch_hc<MixOp>(hc_, R, W, mixes, (float*)nullptr, n, d, norm_eps, s);
+    return dispatch_hc<MixOp>(hc_, R, W, (const u32x4*)nullptr, mixes, (float*)nullptr, n, d, norm_eps, s);
 }
 
 int launch_gen_split(const float* mixes, const float* scale, const float* base, float* pre, float* post,
@@ -655,7 +764,7 @@ int launch_gen_fused(const void* R, const float* W, const float* scale, const fl
     // that a four-stream call's header (its first 256 bytes) is always
     // overwritten and a later four-stream call on the same workspace takes
     // it as fresh (clearing its record area) rather than trusting stale
-    // contents
+    // contents; the weights, split once for this call, at the end
     const size_t M = (size_t)(2 + hc_) * hc_;
     char* w = static_cast<char*>(ws);
     size_t pb = 0;
@@ -665,7 +774,17 @@ int launch_gen_fused(const void* R, const float* W, const float* scale, const fl
     float* mx = mixes ? mixes : reinterpret_cast<float*>(w + off);
     if (!mixes) off += align256((size_t)n * M * 4);
     float* pr = pre ? pre : reinterpret_cast<float*>(w + off);
-    if (dispatch_hc<MixOp>(hc_, R, W, mx, part, n, d, norm_eps, s)) return -1;
+    // calls of many tiles split the weights once (every 256-token tile
+    // would otherwise split all of them again); short calls split them as
+    // they are staged, which saves the extra launch.  Both give the same
+    // fragments, so the same bits.
+    const void* wp = nullptr;
+    if (n >= kPackMinN) {
+        void* dst = w + gen_ws_bytes(n, hc_, d) - align256(packed_gen_bytes(hc_, d));
+        if (dispatch_hc<PackOp>(hc_, W, dst, d, s)) return -1;
+        wp = dst;
+    }
+    if (dispatch_hc<MixOp>(hc_, R, W, (const u32x4*)wp, mx, part, n, d, norm_eps, s)) return -1;
     if (launch_gen_split(mx, scale, base, pr, post, comb, n, hc_, iters, eps, s)) return -1;
     return launch_gen_pre(R, pr, h, n, hc_, d, s);
 }

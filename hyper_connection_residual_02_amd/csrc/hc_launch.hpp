@@ -35,8 +35,9 @@ int launch_split(const float* mixes, const float* scale, const float* base, floa
 // Stream counts other than four (hc_general.hip): 1 <= hc <= kGenMaxHC.
 constexpr int kGenMaxHC = 8;
 bool gen_hc(int hc);
-// Workspace of the fused call: the mixes, then pre (each 256-byte aligned).
-size_t gen_ws_bytes(int64_t n, int hc);
+// Workspace of the fused call: the projection's partial sums, the mixes,
+// pre, then the weights split once (each 256-byte aligned).
+size_t gen_ws_bytes(int64_t n, int hc, int d);
 int launch_gen_mixes(const void* R, const float* W, float* mixes, int64_t n, int hc, int d, float norm_eps,
                      hipStream_t s);
 int launch_gen_split(const float* mixes, const float* scale, const float* base, float* pre, float* post,
