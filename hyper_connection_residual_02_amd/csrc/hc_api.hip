@@ -277,8 +277,11 @@ static int gen_fused(const hc::PostIn* prev, const void* R, const float* hc_fn, 
     if (!R || !hc_fn || !hc_scale || !hc_base || !h || !post || !comb) return HC_ERR_NULL;
     if (prev && (!prev->x || !prev->post || !prev->comb || !prev->Rout)) return HC_ERR_NULL;
     if (!workspace) return HC_ERR_WORKSPACE;
-    const size_t wsb = hc::gen_ws_bytes(n, hc_, d);
-    if (workspace_bytes < wsb) return HC_ERR_WORKSPACE;
+    // the call needs gen_ws_min_bytes; with gen_ws_bytes it also splits the
+    // weights once (long calls), and uses that much
+    const size_t full = hc::gen_ws_bytes(n, hc_, d);
+    if (workspace_bytes < hc::gen_ws_min_bytes(n, hc_, d)) return HC_ERR_WORKSPACE;
+    const size_t wsb = workspace_bytes >= full ? full : hc::gen_ws_min_bytes(n, hc_, d);
     if (!al16(R) || !al16(hc_fn) || ((uintptr_t)workspace & 255u) || !al4(hc_scale) || !al4(hc_base) || !al16(h) ||
         !al16(post) || !al16(comb) || (pre && !al16(pre)) || (mixes && !al16(mixes)))
         return HC_ERR_ALIGN;
@@ -317,7 +320,7 @@ static int gen_fused(const hc::PostIn* prev, const void* R, const float* hc_fn, 
     hipStream_t s = (hipStream_t)stream;
     if (prev && hc::launch_gen_post(prev->x, R, prev->post, prev->comb, prev->Rout, n, hc_, d, s))
         return HC_ERR_LAUNCH;
-    return hc::launch_gen_fused(Rin, hc_fn, hc_scale, hc_base, h, pre, post, comb, mixes, workspace, n, hc_, d,
+    return hc::launch_gen_fused(Rin, hc_fn, hc_scale, hc_base, h, pre, post, comb, mixes, workspace, wsb, n, hc_, d,
                                 sinkhorn_iters, hc_eps, norm_eps, s)
                ? HC_ERR_LAUNCH
                : HC_OK;
@@ -467,7 +470,11 @@ int hc_fused_mix_pre_noalloc(const void* R, const float* hc_fn, const float* hc_
     if (n == 0) return HC_OK;
     // the workspace this call needs must fit the static array; unsupported
     // shapes (size 0) are reported by the call itself
-    if (hc_fused_workspace_bytes(n, hc_, d) > HC_SCRATCH_BYTES) return HC_ERR_SCRATCH;
+    // other stream counts need only the minimum (the weights are then split
+    // as they are staged)
+    if (check_nd(n, hc_, d) == HC_OK && n > 0 &&
+        (hc_ == 4 ? hc_fused_workspace_bytes(n, hc_, d) : hc::gen_ws_min_bytes(n, hc_, d)) > HC_SCRATCH_BYTES)
+        return HC_ERR_SCRATCH;
     void* ws = hc::scratch_ptr();
     if (!ws) return HC_ERR_DEVICE;
     // no launch ordering across streams here: that would create an event

@@ -46,13 +46,20 @@ static size_t packed_gen_bytes(int hc_, int d) {
     return (K + 63) / 64 * 2 * 3 * ((M + 15) / 16) * 64 * 16;
 }
 
+constexpr int64_t kPackMinN = 1024;   // fused calls from this many tokens split the weights once
+
 // The fused call's workspace: k_gmm's partial sums (kSeg segments of
-// (2 + hc) * hc + 2 floats per token), then the mixes and pre, then the
-// weights split once per call.
-size_t gen_ws_bytes(int64_t n, int hc_, int d) {
+// (2 + hc) * hc + 2 floats per token), then the mixes and pre (the minimum,
+// gen_ws_min_bytes), then, for calls that split the weights once, the
+// split weights (gen_ws_bytes, the size the query reports).
+size_t gen_ws_min_bytes(int64_t n, int hc_, int d) {
+    (void)d;
     const size_t M = (size_t)(2 + hc_) * hc_;
-    return align256((size_t)n * 8 * (M + 2) * 4) + align256((size_t)n * M * 4) + align256((size_t)n * hc_ * 4) +
-           align256(packed_gen_bytes(hc_, d));
+    return align256((size_t)n * 8 * (M + 2) * 4) + align256((size_t)n * M * 4) + align256((size_t)n * hc_ * 4);
+}
+
+size_t gen_ws_bytes(int64_t n, int hc_, int d) {
+    return gen_ws_min_bytes(n, hc_, d) + (n >= kPackMinN ? align256(packed_gen_bytes(hc_, d)) : 0);
 }
 
 namespace {
@@ -64,7 +71,6 @@ constexpr int kGThreads = 256;
 // stream (x = R[t] read as K contiguous values).
 constexpr int kSeg = 8;      // segments of the reduction axis, added in order
 constexpr int kKC = 64;      // reduction elements per staged chunk (two MFMA k-steps)
-constexpr int64_t kPackMinN = 1024;   // fused calls from this many tokens split the weights once
 
 template <int HC>
 struct Gmm {
@@ -757,8 +763,8 @@ int launch_gen_post(const void* x, const void* R, const float* post, const float
 }
 
 int launch_gen_fused(const void* R, const float* W, const float* scale, const float* base, void* h, float* pre,
-                     float* post, float* comb, float* mixes, void* ws, int64_t n, int hc_, int d, int iters,
-                     float eps, float norm_eps, hipStream_t s) {
+                     float* post, float* comb, float* mixes, void* ws, size_t ws_bytes, int64_t n, int hc_, int d,
+                     int iters, float eps, float norm_eps, hipStream_t s) {
     // the workspace holds the projection's partial sums, then the mixes and
     // pre when the caller does not keep them, each from offset 0 on, so
     // that a four-stream call's header (its first 256 bytes) is always
@@ -775,12 +781,12 @@ int launch_gen_fused(const void* R, const float* W, const float* scale, const fl
     if (!mixes) off += align256((size_t)n * M * 4);
     float* pr = pre ? pre : reinterpret_cast<float*>(w + off);
     // calls of many tiles split the weights once (every 256-token tile
-    // would otherwise split all of them again); short calls split them as
-    // they are staged, which saves the extra launch.  Both give the same
-    // fragments, so the same bits.
+    // would otherwise split all of them again), when the workspace holds
+    // them; short calls split them as they are staged, which saves the extra
+    // launch.  Both give the same fragments, so the same bits.
     const void* wp = nullptr;
-    if (n >= kPackMinN) {
-        void* dst = w + gen_ws_bytes(n, hc_, d) - align256(packed_gen_bytes(hc_, d));
+    if (n >= kPackMinN && ws_bytes >= gen_ws_bytes(n, hc_, d)) {
+        void* dst = w + gen_ws_min_bytes(n, hc_, d);
         if (dispatch_hc<PackOp>(hc_, W, dst, d, s)) return -1;
         wp = dst;
     }

@@ -36,7 +36,9 @@ int launch_split(const float* mixes, const float* scale, const float* base, floa
 constexpr int kGenMaxHC = 8;
 bool gen_hc(int hc);
 // Workspace of the fused call: the projection's partial sums, the mixes,
-// pre, then the weights split once (each 256-byte aligned).
+// pre (gen_ws_min_bytes, what a call needs), then the weights split once
+// (gen_ws_bytes: with them, for calls long enough to use them).
+size_t gen_ws_min_bytes(int64_t n, int hc, int d);
 size_t gen_ws_bytes(int64_t n, int hc, int d);
 int launch_gen_mixes(const void* R, const float* W, float* mixes, int64_t n, int hc, int d, float norm_eps,
                      hipStream_t s);
@@ -48,8 +50,8 @@ int launch_gen_post(const void* x, const void* R, const float* post, const float
 // mixes, split + Sinkhorn and hc_pre in sequence; mixes and pre may be NULL
 // (kept in ws, of gen_ws_bytes).
 int launch_gen_fused(const void* R, const float* W, const float* scale, const float* base, void* h, float* pre,
-                     float* post, float* comb, float* mixes, void* ws, int64_t n, int hc, int d, int iters,
-                     float eps, float norm_eps, hipStream_t s);
+                     float* post, float* comb, float* mixes, void* ws, size_t ws_bytes, int64_t n, int hc, int d,
+                     int iters, float eps, float norm_eps, hipStream_t s);
 
 // Work split of the projection kernels (hc_coop.hip): each group of G
 // workgroups shares every token; member q owns a 32*KS-feature slice of

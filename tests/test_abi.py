@@ -297,8 +297,10 @@ def test_workspace_query(lib):
     assert lib.hc_fused_workspace_bytes(16, 9, 5120) == 0
     # the projection's partial sums (8 segments of 15 + 2 floats per token),
     # then the mixes, then pre, each 256-byte aligned
-    # partial sums, mixes, pre, then the weights split once (240 chunks x 6 KB at hc = 3)
-    assert lib.hc_fused_workspace_bytes(16, 3, 5120) == 8704 + 1024 + 256 + 240 * 6144
+    # partial sums, mixes, pre; calls of 1,024 tokens or more also hold the
+    # weights split once (240 chunks x 6 KB at hc = 3, d = 5120)
+    assert lib.hc_fused_workspace_bytes(16, 3, 5120) == 8704 + 1024 + 256
+    assert lib.hc_fused_workspace_bytes(1024, 3, 5120) == 1024 * 8 * 17 * 4 + 1024 * 15 * 4 + 1024 * 3 * 4 + 240 * 6144
     assert lib.hc_fused_workspace_bytes(16, 4, 48) == 0
     assert lib.hc_fused_workspace_bytes(16, 4, 64) > 0
     assert lib.hc_fused_workspace_bytes(65536, 4, 5120) > 0
