@@ -462,11 +462,16 @@ __global__ __launch_bounds__(kGThreads) void k_gred(const float* __restrict__ pa
 // plus eps, a column normalisation, then (iters - 1) row and column
 // normalisations, each dividing by (sum + eps).
 template <int HC>
+// scrub (the fused call): the workspace's first 256 bytes, zeroed here so
+// that a four-stream call on the same workspace later finds no valid header
+// and clears its record area (they belong to the partial sums, which k_gmm
+// and k_gred are done with by now).
 __global__ __launch_bounds__(kGThreads) void k_gsplit(const float* __restrict__ mixes, const float* __restrict__ scale,
                                                       const float* __restrict__ base, float* __restrict__ pre,
                                                       float* __restrict__ post, float* __restrict__ comb, int64_t n,
-                                                      int iters, float eps) {
+                                                      int iters, float eps, uint32_t* __restrict__ scrub) {
     constexpr int M = (2 + HC) * HC;
+    if (scrub && blockIdx.x == 0 && threadIdx.x < 64) scrub[threadIdx.x] = 0u;
     const float s0 = scale[0], s1 = scale[1], s2 = scale[2];
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += stride) {
@@ -714,9 +719,9 @@ struct PartOp {
 template <int HC>
 struct SplitOp {
     static int run(const float* mixes, const float* scale, const float* base, float* pre, float* post, float* comb,
-                   int64_t n, int iters, float eps, hipStream_t s) {
+                   int64_t n, int iters, float eps, uint32_t* scrub, hipStream_t s) {
         hipLaunchKernelGGL(k_gsplit<HC>, dim3(grid_for(n)), dim3(kGThreads), 0, s, mixes, scale, base, pre, post,
-                           comb, n, iters, eps);
+                           comb, n, iters, eps, scrub);
         return hipGetLastError() == hipSuccess ? 0 : -1;
     }
 };
@@ -750,7 +755,7 @@ int launch_gen_mixes(const void* R, const float* W, float* mixes, int64_t n, int
 
 int launch_gen_split(const float* mixes, const float* scale, const float* base, float* pre, float* post,
                      float* comb, int64_t n, int hc_, int iters, float eps, hipStream_t s) {
-    return dispatch_hc<SplitOp>(hc_, mixes, scale, base, pre, post, comb, n, iters, eps, s);
+    return dispatch_hc<SplitOp>(hc_, mixes, scale, base, pre, post, comb, n, iters, eps, (uint32_t*)nullptr, s);
 }
 
 int launch_gen_pre(const void* R, const float* pre, void* h, int64_t n, int hc_, int d, hipStream_t s) {
@@ -766,11 +771,11 @@ int launch_gen_fused(const void* R, const float* W, const float* scale, const fl
                      float* post, float* comb, float* mixes, void* ws, size_t ws_bytes, int64_t n, int hc_, int d,
                      int iters, float eps, float norm_eps, hipStream_t s) {
     // the workspace holds the projection's partial sums, then the mixes and
-    // pre when the caller does not keep them, each from offset 0 on, so
-    // that a four-stream call's header (its first 256 bytes) is always
-    // overwritten and a later four-stream call on the same workspace takes
-    // it as fresh (clearing its record area) rather than trusting stale
-    // contents; the weights, split once for this call, at the end
+    // pre when the caller does not keep them, then the weights split once
+    // for this call; its first 256 bytes (a four-stream call's header) are
+    // zeroed by the split kernel, so that a later four-stream call on the
+    // same workspace takes it as fresh (clearing its record area) rather
+    // than trusting stale contents
     const size_t M = (size_t)(2 + hc_) * hc_;
     char* w = static_cast<char*>(ws);
     size_t pb = 0;
@@ -791,7 +796,8 @@ int launch_gen_fused(const void* R, const float* W, const float* scale, const fl
         wp = dst;
     }
     if (dispatch_hc<MixOp>(hc_, R, W, (const u32x4*)wp, mx, part, n, d, norm_eps, s)) return -1;
-    if (launch_gen_split(mx, scale, base, pr, post, comb, n, hc_, iters, eps, s)) return -1;
+    if (dispatch_hc<SplitOp>(hc_, mx, scale, base, pr, post, comb, n, iters, eps, reinterpret_cast<uint32_t*>(w), s))
+        return -1;
     return launch_gen_pre(R, pr, h, n, hc_, d, s);
 }
 

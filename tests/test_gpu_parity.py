@@ -576,3 +576,26 @@ def test_other_stream_counts_batch_invariant_and_deterministic(hc, d, n, span):
         iv = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
         assert torch.equal(a.view(iv), b.view(iv))
         assert torch.equal(a[:, lo:hi].contiguous().view(iv), c.view(iv))
+
+
+def test_other_stream_count_call_invalidates_four_stream_header():
+    # a workspace shared across stream counts: a call at hc != 4 zeroes the
+    # first 256 bytes (a four-stream call's header), even when it takes one
+    # workgroup per tile (no partial sums written) with the mixes kept by the
+    # caller, so a later four-stream call clears its record area instead of
+    # trusting stale contents, and gives the fresh-workspace bits
+    ws = hcl.Workspace()
+    w4 = _hc_workload(4, 256)
+    t4 = hin.make_inputs(w4, DEV, seed=21, n_tokens=3000)
+    first = hcl.hc_fused_mix_pre(t4["R"], t4["W"], t4["scale"], t4["base"], workspace=ws, want_mixes=True)
+    w3 = _hc_workload(3, 64)
+    t3 = hin.make_inputs(w3, DEV, seed=22, n_tokens=70000)
+    hcl.hc_fused_mix_pre(t3["R"], t3["W"], t3["scale"], t3["base"], workspace=ws, want_pre=False, want_mixes=True)
+    torch.cuda.synchronize()
+    head = ws._buf[ws._off:ws._off + 256]
+    assert int(head.count_nonzero()) == 0, "the four-stream header survived a three-stream call"
+    again = hcl.hc_fused_mix_pre(t4["R"], t4["W"], t4["scale"], t4["base"], workspace=ws, want_mixes=True)
+    torch.cuda.synchronize()
+    for a, b in zip(first, again):
+        iv = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(a.view(iv), b.view(iv))
