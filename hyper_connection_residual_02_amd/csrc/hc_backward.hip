@@ -21,9 +21,10 @@
 //  * k_mix_bwd: dL/dR = sum_k comb[j][k] dL/dR'_k + pre_j dL/dh
 //    + sum_m dL/ddot_m W[m][i] + 2 x_i dL/dss, in float, rounded once to
 //    bf16; and per token group the partial sums of dL/dW[m][i] =
-//    sum_t dL/ddot_tm x_ti.  A workgroup owns 128 features of every stream
-//    (wave j: stream j) and walks a contiguous range of tokens; each thread
-//    keeps its 2 x 24 weights and 2 x 24 partial sums in registers.
+//    sum_t dL/ddot_tm x_ti.  Both sums over the mixes run on the matrix
+//    cores from exact bf16 pieces of the fp32 operands; a workgroup owns 128
+//    features of every stream and walks a contiguous range of tokens in
+//    rounds of 32.
 //  * k_gw_reduce, k_sb_partial + k_sb_final: the partial sums over token groups, and the
 //    per-token scale and base contributions over tokens, each added in one
 //    fixed order (double), so the results are deterministic.
@@ -39,8 +40,10 @@ constexpr int kCPre = 0, kCComb = 4, kCDot = 20, kCSs = 44;
 constexpr int kSB = 28;                     // floats per token: dL/dscale (3), dL/dbase (24), pad
 constexpr int kBwdMaxIters = 64;
 constexpr int kBwdSteps = 2 * kBwdMaxIters - 1;
-constexpr int kMixFeat = 128;               // features per stream owned by a k_mix_bwd workgroup
+constexpr int kMixFeat = 128;               // the backward takes widths d that are multiples of this
 constexpr int kMaxTokenGroups = 32;
+constexpr int kBufDword3 = 0x00020000;      // raw buffer resource, dword 3
+constexpr int kBufOOB = 0x7FFFFFF0;         // buffer offset past every resource: loads read 0
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -266,74 +269,344 @@ __global__ __launch_bounds__(256) void k_pre_bwd(PreBwdArgs a) {
 
 // --------------------------------------------------- projection bwd (dL/dR)
 struct MixBwdArgs {
-    const uint32_t* R;      // bf16 pairs
-    const uint32_t* gh;
-    const uint32_t* gRo;
+    const uint16_t* R;
+    const uint16_t* gh;
+    const uint16_t* gRo;
     const float* W;
     const float* coef;
-    uint32_t* gR;
+    uint16_t* gR;
     float* part;            // [NTG][24][K] partial dL/dW
     int64_t n;
     int d;
     int ntg;                // token groups
 };
 
-// Workgroup (feature block fb, token group tg): wave j owns features
-// fb * 128 + 2 lane, +1 of stream j.
-__global__ __launch_bounds__(256) void k_mix_bwd(MixBwdArgs a) {
-    const int nfb = a.d / kMixFeat;
+// The two contractions over the 24 mixes run on the matrix cores
+// (v_mfma_f32_16x16x32_bf16, mixes padded to 32 with zeros): fp32 operands
+// are split exactly into three bf16 pieces (a float's 24-bit significand is
+// three 8-bit ones), so every product below is an exact product of pieces.
+//  * sum_m dL/ddot[t][m] W[m][i]: rows = 16 tokens, columns = 16 features,
+//    reduction = the mixes.  Both operands are split; the six products of
+//    pieces whose weight is at least 2^-16 of the leading one are summed,
+//    the three dropped ones are below 2^-23 of it.
+//  * dL/dW[m][i] += sum_t dL/ddot[t][m] x[t][i]: rows = 16 mixes, columns =
+//    16 features, reduction = the round's 32 tokens; x is bf16 already, so
+//    the three pieces of dL/ddot give the products exactly.
+// A workgroup owns F features of every stream (F = 128: 256-byte row
+// segments) and walks its token group in rounds of kMbT tokens.  Per round: every thread has loaded (two
+// rounds ahead) one 8-feature chunk of one token from each stream of R and
+// dL/dR' and from dL/dh; the round's residual goes to LDS transposed
+// (feature-major, the MFMA operand order for a reduction over tokens) with
+// its coefficient records; each thread puts its chunk's four-term comb sum,
+// pre_j dL/dh and 2 x dL/dss in LDS (after which its registers take the
+// loads of the round two ahead); each wave adds the products of one
+// stream's 64 features to those sums on the matrix cores; then each thread
+// stores its chunk's dL/dR, rounded once to bf16.
+constexpr int kMbT = 32;                         // tokens per round
+constexpr int kXtRow = 80;                       // bytes per feature row of the transposed residual (32 tokens + pad)
+
+// H = 1 or 2: a workgroup of 256 H threads owns F = 64 H features of every
+// stream; wave w runs the products of stream w % 4, features 64 (w / 4) ..
+template <int H>
+struct MbGeo {
+    static constexpr int F = 64 * H;                        // features per stream of a workgroup
+    static constexpr int kThreads = 256 * H;
+    static constexpr int kXtStream = F * kXtRow + 16 * (F / 8);   // one stream, with a 16-byte skew per 8 features
+    static constexpr int kDrTok = kHC * F + 4;              // floats per token row of the matrix-core sums (+ pad)
+    static constexpr int kCfLoads = (kMbT * kCoef / 4 + kThreads - 1) / kThreads;   // record float4s per thread
+};
+
+template <int H>
+struct MbLds {
+    uint8_t xt[kHC * MbGeo<H>::kXtStream];       // x transposed: [stream][feature][token] bf16
+    float cf[2][kMbT][kCoef];                    // the round's coefficient records (by round parity)
+    float dr[kMbT][MbGeo<H>::kDrTok];            // the round's sum_m dL/ddot_m W[m][i], fp32
+};
+
+// Byte offset of (stream j, feature f, token t) in MbLds::xt.  The pad and
+// the skew keep both the transposing 2-byte stores (8 chunks x 8 tokens of
+// a wave) and the 16-byte operand reads (16 features) on distinct banks.
+template <int H>
+__device__ __forceinline__ int xt_off(int j, int f, int t) {
+    return j * MbGeo<H>::kXtStream + f * kXtRow + (f >> 3) * 16 + 2 * t;
+}
+
+// v = hi + mid + lo exactly, each piece bf16.
+__device__ __forceinline__ void split3(const float (&v)[8], bf16x8& hi, bf16x8& mid, bf16x8& lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const __bf16 h = (__bf16)v[e];
+        const float r1 = v[e] - (float)h;
+        const __bf16 m = (__bf16)r1;
+        hi[e] = h;
+        mid[e] = m;
+        lo[e] = (__bf16)(r1 - (float)m);
+    }
+}
+
+// A barrier for LDS only: this wave's LDS accesses complete, then the
+// workgroup barrier; global loads issued before it stay in flight.  In
+// assembly with a memory clobber, so the compiler moves no memory access
+// across it (an LDS-scoped fence pair around the barrier builtin let the
+// stores of MFMA results sink below the barrier).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One round's global inputs for one thread: chunk ic of token it.
+template <int H>
+struct MbIo {
+    u32x4 x[kHC], g[kHC], h;
+    f32x4 c[MbGeo<H>::kCfLoads];                 // the round's coefficient float4s tid, tid + threads, ..
+};
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Workgroup (feature block fb, token group tg).
+template <int H>
+__global__ __launch_bounds__(256 * H, H == 1 ? 2 : 1) void k_mix_bwd(MixBwdArgs a) {
+    using G = MbGeo<H>;
+    constexpr int kMbF = G::F, kDrTok = G::kDrTok;
+    __shared__ __attribute__((aligned(16))) MbLds<H> L;
+    const int nfb = a.d / kMbF;
     const int fb = blockIdx.x % nfb, tg = blockIdx.x / nfb;
-    const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int c0 = fb * kMixFeat + 2 * lane;
-    const int64_t K = (int64_t)kHC * a.d;
-    const int64_t i0 = (int64_t)j * a.d + c0;
+    const int tid = threadIdx.x, l = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = wv & 3, mc = 64 * (wv >> 2);   // matrix-core work: stream j, features mc .. mc + 63
+    const int row = l & 15, grp = l >> 4;
+    const int col0 = fb * kMbF;
+    const int d = a.d;
+    const int64_t K = (int64_t)kHC * d;
     const int64_t per = (a.n + a.ntg - 1) / a.ntg;
     const int64_t t0 = per * tg, t1 = t0 + per < a.n ? t0 + per : a.n;
-    float w[kMix][2], acc[kMix][2];
+    const int nr = t1 > t0 ? (int)((t1 - t0 + kMbT - 1) / kMbT) : 0;
+
+    // stream j's weights for features col0 + mc .. + 63 as B fragments:
+    // column tile ct, lane (row, grp) = feature 16 ct + row, mixes 8 grp ..
+    bf16x8 wh[4], wm[4], wl[4];
 #pragma unroll
-    for (int mm = 0; mm < kMix; ++mm) {
-        const float2 wv = *reinterpret_cast<const float2*>(a.W + mm * K + i0);
-        w[mm][0] = wv.x;
-        w[mm][1] = wv.y;
-        acc[mm][0] = acc[mm][1] = 0.0f;
-    }
-    const int d2 = a.d / 2;          // bf16 pairs per row
-    for (int64_t t = t0; t < t1; ++t) {
-        const float* cf = a.coef + t * kCoef;
-        const uint32_t xw = a.R[(t * kHC + j) * d2 + c0 / 2];
-        const uint32_t hw = a.gh[t * d2 + c0 / 2];
-        uint32_t gw[kHC];
+    for (int ct = 0; ct < 4; ++ct) {
+        const int64_t i = (int64_t)j * d + col0 + mc + 16 * ct + row;
+        float v[8];
 #pragma unroll
-        for (int k = 0; k < kHC; ++k) gw[k] = a.gRo[(t * kHC + k) * d2 + c0 / 2];
-        const float pj = cf[kCPre + j], gss2 = 2.0f * cf[kCSs];
-        float cb[kHC];
-#pragma unroll
-        for (int k = 0; k < kHC; ++k) cb[k] = cf[kCComb + j * kHC + k];
-        float gd[kMix];
-#pragma unroll
-        for (int mm = 0; mm < kMix; ++mm) gd[mm] = cf[kCDot + mm];
-        uint32_t o[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            auto v = [&](uint32_t word) { return e ? bf_hi(word) : bf_lo(word); };
-            const float xe = v(xw);
-            float y = cb[0] * v(gw[0]);
-#pragma unroll
-            for (int k = 1; k < kHC; ++k) y = __builtin_fmaf(cb[k], v(gw[k]), y);
-            y = __builtin_fmaf(pj, v(hw), y);
-#pragma unroll
-            for (int mm = 0; mm < kMix; ++mm) y = __builtin_fmaf(gd[mm], w[mm][e], y);
-            y = __builtin_fmaf(gss2, xe, y);
-            o[e] = bf16_rn(y);
-#pragma unroll
-            for (int mm = 0; mm < kMix; ++mm) acc[mm][e] = __builtin_fmaf(gd[mm], xe, acc[mm][e]);
+        for (int e = 0; e < 8; ++e) {
+            const int m = 8 * grp + e;
+            v[e] = m < kMix ? a.W[m * K + i] : 0.0f;
         }
-        a.gR[(t * kHC + j) * d2 + c0 / 2] = pack2(o[0], o[1]);
+        split3(v, wh[ct], wm[ct], wl[ct]);
     }
+    f32x4 gw[2][4];                              // dL/dW sums: mix tile, column tile
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) gw[mt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int it = tid / (8 * H), ic = tid % (8 * H);   // streaming item: token it of the round, features 8 ic ..
+    // the round's rows as buffer resources: tokens r0 .. r0 + 31 of the
+    // group; rows past the group's end lie outside the resource, so their
+    // loads return zeros and their stores are dropped
+    auto rows = [&](const void* base, int64_t tok_bytes, int64_t r0) {
+        int64_t valid = t1 - r0;
+        valid = valid < 0 ? 0 : (valid > kMbT ? kMbT : valid);
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(base)) + r0 * tok_bytes,
+                                                 0, (int)(valid * tok_bytes), kBufDword3);
+    };
+    const int ox = (it * kHC * d + col0 + 8 * ic) * 2;          // stream 0 of the item in a round of R, dL/dR'
+    const int oh = (it * d + col0 + 8 * ic) * 2;                // the item in a round of dL/dh
+    auto load = [&](MbIo<H>& io, int64_t r0) {
+        const __amdgpu_buffer_rsrc_t rx = rows(a.R, (int64_t)kHC * d * 2, r0);
+        const __amdgpu_buffer_rsrc_t rg = rows(a.gRo, (int64_t)kHC * d * 2, r0);
+        const __amdgpu_buffer_rsrc_t rh = rows(a.gh, (int64_t)d * 2, r0);
+        const __amdgpu_buffer_rsrc_t rc = rows(a.coef, kCoef * 4, r0);
+        // the streams non-temporal (aux 2): each is read once; the records
+        // are read by every feature block and stay cached
+#pragma unroll
+        for (int k = 0; k < kHC; ++k) {
+            io.x[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, ox, k * d * 2, 2));
+            io.g[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, ox, k * d * 2, 2));
+        }
+        io.h = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, oh, 0, 2));
+#pragma unroll
+        for (int u = 0; u < G::kCfLoads; ++u) {
+            const int q = tid + G::kThreads * u;                 // float4 q of the round's records
+            io.c[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rc, q < kMbT * kCoef / 4 ? 16 * q : kBufOOB, 0, 0));
+        }
+    };
+    // stage A: the round's residual transposed into xt, its records into cf
+    auto stage_a = [&](const MbIo<H>& io, int pb) {
+#pragma unroll
+        for (int k = 0; k < kHC; ++k)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t word = io.x[k][w];
+                *reinterpret_cast<uint16_t*>(&L.xt[xt_off<H>(k, 8 * ic + 2 * w, it)]) = (uint16_t)word;
+                *reinterpret_cast<uint16_t*>(&L.xt[xt_off<H>(k, 8 * ic + 2 * w + 1, it)]) = (uint16_t)(word >> 16);
+            }
+#pragma unroll
+        for (int u = 0; u < G::kCfLoads; ++u) {
+            const int q = tid + G::kThreads * u;
+            if (q < kMbT * kCoef / 4) *reinterpret_cast<f32x4*>(&L.cf[pb][q / 12][4 * (q % 12)]) = io.c[u];
+        }
+    };
+    // stage B: the item's terms outside the matrix cores, for every stream
+    // j: sum_k comb[j][k] dL/dR'_k + pre_j dL/dh + 2 dL/dss x_j, into dr
+    auto stage_b = [&](const MbIo<H>& io, int pb) {
+        const float* c = &L.cf[pb][it][0];
+        const float gss2 = 2.0f * c[kCSs];
+#pragma unroll
+        for (int jj = 0; jj < kHC; ++jj) {
+            const float pj = c[kCPre + jj];
+            float cb[kHC];
+#pragma unroll
+            for (int k = 0; k < kHC; ++k) cb[k] = c[kCComb + jj * kHC + k];
+            float y[8];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    auto v = [&](uint32_t word) { return e ? bf_hi(word) : bf_lo(word); };
+                    float acc = cb[0] * v(io.g[0][w]);
+#pragma unroll
+                    for (int k = 1; k < kHC; ++k) acc = __builtin_fmaf(cb[k], v(io.g[k][w]), acc);
+                    acc = __builtin_fmaf(pj, v(io.h[w]), acc);
+                    y[2 * w + e] = __builtin_fmaf(gss2, v(io.x[jj][w]), acc);
+                }
+            *reinterpret_cast<f32x4*>(&L.dr[it][jj * kMbF + 8 * ic]) = f32x4{y[0], y[1], y[2], y[3]};
+            *reinterpret_cast<f32x4*>(&L.dr[it][jj * kMbF + 8 * ic + 4]) = f32x4{y[4], y[5], y[6], y[7]};
+        }
+    };
+    auto mma = [&](int pb) {
+        // dr += sum_m dL/ddot[t][m] W[m][i]: A = 16 tokens x mixes 8 grp .. 8 grp + 7
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            float v[8];
+            if (grp < 3) {
+                const float* src = &L.cf[pb][16 * tt + row][kCDot + 8 * grp];
+                const f32x4 lo4 = *reinterpret_cast<const f32x4*>(src), hi4 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = lo4[e];
+                    v[4 + e] = hi4[e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+            }
+            bf16x8 ah, am, al;
+            split3(v, ah, am, al);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                float* dst = &L.dr[16 * tt + 4 * grp][j * kMbF + mc + 16 * ct + row];
+                f32x4 c;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) c[i] = dst[i * kDrTok];
+                c = mfma16(am, wm[ct], c);
+                c = mfma16(al, wh[ct], c);
+                c = mfma16(ah, wl[ct], c);
+                c = mfma16(am, wh[ct], c);
+                c = mfma16(ah, wm[ct], c);
+                c = mfma16(ah, wh[ct], c);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[i * kDrTok] = c[i];
+            }
+        }
+        // dL/dW[m][i] += sum_t dL/ddot[t][m] x[t][i]: A = mixes 16 mt + row x
+        // tokens 8 grp .. 8 grp + 7, B = the transposed residual
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int mix = 16 * mt + row;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = mix < kMix ? L.cf[pb][8 * grp + e][kCDot + mix] : 0.0f;
+            bf16x8 gh_, gm_, gl_;
+            split3(v, gh_, gm_, gl_);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const bf16x8 xb = *reinterpret_cast<const bf16x8*>(&L.xt[xt_off<H>(j, mc + 16 * ct + row, 8 * grp)]);
+                gw[mt][ct] = mfma16(gl_, xb, gw[mt][ct]);
+                gw[mt][ct] = mfma16(gm_, xb, gw[mt][ct]);
+                gw[mt][ct] = mfma16(gh_, xb, gw[mt][ct]);
+            }
+        }
+    };
+    // dL/dR of the item, rounded once to bf16
+    auto emit = [&](int64_t r0) {
+        const __amdgpu_buffer_rsrc_t ro = rows(a.gR, (int64_t)kHC * d * 2, r0);
+#pragma unroll
+        for (int jj = 0; jj < kHC; ++jj) {
+            const f32x4 d0 = *reinterpret_cast<const f32x4*>(&L.dr[it][jj * kMbF + 8 * ic]);
+            const f32x4 d1 = *reinterpret_cast<const f32x4*>(&L.dr[it][jj * kMbF + 8 * ic + 4]);
+            const u32x2 o0 = u32x2{bf16x2_rn(d0[0], d0[1]), bf16x2_rn(d0[2], d0[3])};
+            const u32x2 o1 = u32x2{bf16x2_rn(d1[0], d1[1]), bf16x2_rn(d1[2], d1[3])};
+            // two 8-byte stores, not one of 16: with the wider store, a
+            // 64-bit move into its data registers a few instructions later
+            // (the compiler's loop code) was seen to reach the data of lanes
+            // 12..15 of every 16 before the store had read it.  The data
+            // registers are also held, unwritten, through a few wait states.
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((__vector_size__(8))) int, o0), ro,
+                                                  ox, jj * d * 2, 2);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((__vector_size__(8))) int, o1), ro,
+                                                  ox + 8, jj * d * 2, 2);
+            asm volatile("s_nop 7" ::"v"(o0), "v"(o1) : "memory");     // (stores non-temporal: written once)
+        }
+    };
+    // round r: its inputs (loaded two rounds ahead) go to LDS and are
+    // consumed there, so their registers take round r + 2's loads at once;
+    // then the products, then the outputs.  LDS: xt and cf (by parity) are
+    // rewritten only after the barrier that follows the products reading
+    // them; dr after the first barrier of the next round, which follows the
+    // outputs reading it.  Every round issues the same memory instructions
+    // (rounds past the group's end lie outside their resources: zeros in,
+    // stores dropped), so the loop body is straight-line and the compiler's
+    // memory-counter waits let the next round's loads stay in flight.
+    auto round = [&](MbIo<H>& io, int r, int pb) {
+        stage_a(io, pb);
+        lds_barrier();
+        stage_b(io, pb);
+        load(io, t0 + (int64_t)(r + 2) * kMbT);
+        lds_barrier();
+        mma(pb);
+        lds_barrier();
+        emit(t0 + (int64_t)r * kMbT);
+    };
+    // stores outside every resource, in the order of a round's outputs:
+    // the prologue issues what a round issues, so the loop entry and its
+    // back edge present the same sequence of outstanding memory operations
+    auto no_emit = [&]() {
+        const __amdgpu_buffer_rsrc_t ro = rows(a.gR, (int64_t)kHC * d * 2, t1);
+        const u32x2 z = u32x2{0u, 0u};
+#pragma unroll
+        for (int jj = 0; jj < kHC; ++jj) {
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((__vector_size__(8))) int, z), ro,
+                                                  ox, jj * d * 2, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((__vector_size__(8))) int, z), ro,
+                                                  ox + 8, jj * d * 2, 0);
+        }
+    };
+    MbIo<H> io0, io1;
+    load(io0, t0);
+    no_emit();
+    load(io1, t0 + kMbT);
+    no_emit();
+    for (int r = 0; r < nr; r += 2) {
+        round(io0, r, 0);
+        round(io1, r + 1, 1);
+    }
+    // the token group's dL/dW partial sums: lane (row, grp) holds mixes
+    // 16 mt + 4 grp + i of feature 16 ct + row
     float* P = a.part + (int64_t)tg * kMix * K;
 #pragma unroll
-    for (int mm = 0; mm < kMix; ++mm)
-        *reinterpret_cast<float2*>(P + mm * K + i0) = make_float2(acc[mm][0], acc[mm][1]);
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 16 * mt + 4 * grp + i;
+                if (m < kMix) P[m * K + (int64_t)j * d + col0 + mc + 16 * ct + row] = gw[mt][ct][i];
+            }
 }
 
 // dL/dW[m][i] = sum over token groups of the partials, in group order.
@@ -430,9 +703,10 @@ int launch_mix_pre_bwd(const void* R, const float* W, const float* scale, const 
     k_pre_bwd<<<(unsigned)((n + 3) / 4), 256, 0, s>>>(pa);
     if (hipGetLastError() != hipSuccess) return -1;
     const int ntg = token_groups(n);
-    MixBwdArgs ma{(const uint32_t*)R, (const uint32_t*)gh, (const uint32_t*)gRo, W, coef, (uint32_t*)gR, part, n, d,
+    MixBwdArgs ma{(const uint16_t*)R, (const uint16_t*)gh, (const uint16_t*)gRo, W, coef, (uint16_t*)gR, part, n, d,
                   ntg};
-    k_mix_bwd<<<(unsigned)((d / kMixFeat) * ntg), 256, 0, s>>>(ma);
+    constexpr int kH = 2;                        // d % 128 == 0 (bwd_supported)
+    k_mix_bwd<kH><<<(unsigned)((d / MbGeo<kH>::F) * ntg), MbGeo<kH>::kThreads, 0, s>>>(ma);
     if (hipGetLastError() != hipSuccess) return -1;
     const int64_t total = kMix * K;
     int64_t blocks = (total + 255) / 256;
