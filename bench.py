@@ -685,6 +685,92 @@ def bench_probe(args, hcl, torch, np, w, dev):
     print(json.dumps(line), flush=True)
 
 
+PHASE_NAMES = {
+    "mfma": ["barrier", "publish", "dma_issue", "products", "dma_wait", "hc_post"],
+    "exchange": ["barrier", "exchange", "h", "residual_copy", "record_issue", "rprime_stores"],
+}
+
+
+def bench_phases(args, hcl, hin, torch, np, w, t, ws, outs, Rout, dev):
+    """--phases: where the persistent projection kernel (the wave-specialised
+    kernel of calls above 2,048 tokens) spends a tick, from the library built
+    with phase tracing (libhc_trace.so): per wave role, the average time per
+    tick of each phase (include/hc.h, hc_phase_trace, defines them), over every
+    workgroup and wave of the role in the last call.  With --boundary the call
+    is hc_post_mix_pre (the one-pass boundary kernel), else hc_fused_mix_pre.
+    Tracing adds a few instructions per phase, so the traced tick is a little
+    longer than the untraced one.  Prints one JSON line; --phases-md writes the
+    table as markdown."""
+    R, x, W, s, b = t["R"], t["x"], t["W"], t["scale"], t["base"]
+    if args.boundary:
+        nxt = hin.make_inputs(w, dev, seed=1)
+        hcl.hc_fused_mix_pre(R, W, s, b, workspace=ws, out=outs)
+        o2 = dict(h=torch.empty_like(outs["h"]), pre=torch.empty_like(outs["pre"]),
+                  post=torch.empty_like(outs["post"]), comb=torch.empty_like(outs["comb"]))
+
+        def call():
+            hcl.hc_post_mix_pre(x, R, outs["post"], outs["comb"], nxt["W"], nxt["scale"], nxt["base"],
+                                sinkhorn_iters=w.iters, hc_eps=w.hc_eps, norm_eps=w.norm_eps, workspace=ws,
+                                out_R=Rout, out=o2)
+    else:
+        def call():
+            hcl.hc_fused_mix_pre(R, W, s, b, sinkhorn_iters=w.iters, hc_eps=w.hc_eps, norm_eps=w.norm_eps,
+                                 workspace=ws, out=outs)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    v = []
+    for _ in range(args.steps):
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        z.record(stream)
+        torch.cuda.synchronize()
+        v.append(a.elapsed_time(z) * 1e3)
+    tr = hcl.phase_trace(1024 * 8 * 7).reshape(-1, 8, 7).astype(np.float64)
+    tr = tr[tr[:, 0, 6] > 0]
+    if len(tr) == 0:
+        print("--phases: the call did not run the wave-specialised kernel (calls of at most 2,048 tokens "
+              "take the two-pass path)", file=sys.stderr)
+        sys.exit(2)
+    ticks = tr[:, :, 6:7]
+    per_tick = tr[:, :, :6] * 0.01 / ticks                    # us per tick, [workgroup][wave][phase]
+    roles = {"mfma": per_tick[:, :4].reshape(-1, 6).mean(0), "exchange": per_tick[:, 4:].reshape(-1, 6).mean(0)}
+    phases = {r: {nm: round(float(roles[r][i]), 3) for i, nm in enumerate(PHASE_NAMES[r])
+                  if args.boundary or nm not in ("hc_post", "rprime_stores")} for r in roles}
+    call_us = float(np.mean(v))
+    nt = float(ticks.mean())
+    name = "hc_post_mix_pre" if args.boundary else "hc_fused_mix_pre"
+    line = {"metric": "time per tick of the persistent projection kernel, by wave role and phase "
+                      "(phase-tracing build)",
+            "value": round(float(roles["exchange"].sum()), 3), "unit": "us/tick", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "higher_is_better": False, "vs_baseline": None,
+            "data": "synthetic", "config": {"workload": "%s: %d tokens, d=%d, %s" % (w.name, w.n, w.d, name)},
+            "call_avg_us": round(call_us, 1), "workgroups": int(len(tr)), "ticks_per_workgroup": round(nt, 1),
+            "tick_us_from_call": round(call_us / nt, 3), "phases_us_per_tick": phases}
+    print(json.dumps(line), flush=True)
+    if args.phases_md:
+        rows = []
+        for r in ("mfma", "exchange"):
+            for nm, val in phases[r].items():
+                rows.append("| %s | %s | %.3f |" % ("MFMA waves (0-3)" if r == "mfma" else "exchange waves (4-7)",
+                                                   nm, val))
+        cmd = "python bench.py --phases%s --workload %s --steps %d --warmup %d --phases-md <file>" % (
+            " --boundary" if args.boundary else "", args.workload, args.steps, args.warmup)
+        md = ["# Phases of the persistent projection kernel, %s, %d tokens, d=%d" % (name, w.n, w.d), "",
+              "Command (after `python -m hyper_connection_residual_02_amd.build --phase-trace`):", "",
+              "    " + cmd, "",
+              "Library: libhc_trace.so (phase tracing compiled in). Call average %.1f us over %d calls; "
+              "%d workgroups, %.1f ticks each; %.3f us per tick from the call time." % (
+                  call_us, args.steps, len(tr), nt, call_us / nt), "",
+              "| wave role | phase | us per tick |", "|---|---|---|", *rows, "",
+              "Each wave's phase totals (s_memrealtime, 100 MHz) over the round loop, divided by its tick count "
+              "and averaged over the role's waves in every workgroup of the last call.", ""]
+        with open(args.phases_md, "w") as f:
+            f.write("\n".join(md))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -721,6 +807,10 @@ def main():
     ap.add_argument("--probe", action="store_true",
                     help="measure the streaming ceilings instead: the library's bandwidth probe (copy, read, "
                          "re-read) and torch's copy on residual-sized and 1 GiB buffers")
+    ap.add_argument("--phases", action="store_true",
+                    help="phase times per tick of the persistent projection kernel, from libhc_trace.so "
+                         "(build it with `python -m hyper_connection_residual_02_amd.build --phase-trace`)")
+    ap.add_argument("--phases-md", default="", help="with --phases: write the table as markdown to this path")
     ap.add_argument("--norm", action="store_true",
                     help="time the pre-sublayer RMSNorm instead: one hc_fused_mix_pre_norm call, with "
                          "hc_pre_norm and hc_rmsnorm timed beside it")
@@ -754,6 +844,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.phases:
+        if not os.path.exists(hcl.trace_library_path()):
+            print("--phases needs libhc_trace.so: python -m hyper_connection_residual_02_amd.build --phase-trace",
+                  file=sys.stderr)
+            sys.exit(2)
+        hcl.use_library(hcl.trace_library_path())
     hcl.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -783,6 +879,12 @@ def main():
                 comb=torch.empty(w.B, w.T, w.hc, w.hc, device=dev))
     Rout = torch.empty_like(R)
     packed = hcl.hc_pack_weights(W) if args.packed else None
+    if args.phases:
+        if w.hc != 4:
+            print("--phases runs four streams only", file=sys.stderr)
+            sys.exit(2)
+        bench_phases(args, hcl, hin, torch, np, w, t, ws, outs, Rout, dev)
+        return
     if args.boundary:
         bench_boundary(args, hcl, hin, torch, np, w, t, ws, outs, Rout, dev)
         return

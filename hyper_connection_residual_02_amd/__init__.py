@@ -47,6 +47,20 @@ def lib_path() -> str:
     return _LIB_PATH
 
 
+def use_library(path: str) -> None:
+    """Load the library from `path` instead of libhc.so: the phase-tracing
+    build (libhc_trace.so, ``python -m hyper_connection_residual_02_amd.build
+    --phase-trace``).  Call it before the first library call."""
+    global _LIB_PATH
+    if _lib is not None and os.path.abspath(path) != os.path.abspath(_LIB_PATH):
+        raise RuntimeError("the library is loaded already (%s)" % _LIB_PATH)
+    _LIB_PATH = path
+
+
+def trace_library_path() -> str:
+    return os.path.join(_HERE, "libhc_trace.so")
+
+
 def load():
     """Load libhc.so (built in-tree by ``hyper_connection_residual_02_amd.build``)."""
     global _lib
@@ -90,6 +104,8 @@ def load():
     lib.hc_noalloc_status.restype = ctypes.c_int
     lib.hc_debug_force_timeout.argtypes = [ctypes.c_int]
     lib.hc_debug_force_timeout.restype = ctypes.c_int
+    lib.hc_phase_trace.argtypes = [P, SZ]
+    lib.hc_phase_trace.restype = ctypes.c_int
     lib.hc_backward_workspace_bytes.argtypes = [I64, I32, I32]
     lib.hc_backward_workspace_bytes.restype = SZ
     lib.hc_scratch_bytes.argtypes = []
@@ -144,6 +160,21 @@ def probe_stream(src: torch.Tensor, dst: torch.Tensor | None = None, wg_per_cu: 
         raise ValueError("dst must be a contiguous GPU tensor of src's size, on its device")
     with torch.cuda.device(dev):
         _call("hc_probe_stream", _ptr(src), _ptr(dst), nbytes, int(wg_per_cu), _stream(dev))
+
+
+def phase_trace(words: int):
+    """The phase tables of the persistent projection kernel's last launch
+    (phase-tracing build only, see use_library): a uint64 numpy array of up
+    to `words` words, [workgroup][wave][7]: the s_memrealtime ticks (100 MHz)
+    of phases 0..5, then the round loop's tick count (include/hc.h,
+    hc_phase_trace, names the phases).  Synchronises."""
+    import numpy as np
+    out = np.zeros(int(words), dtype=np.uint64)
+    torch.cuda.synchronize()
+    r = load().hc_phase_trace(out.ctypes.data, out.size)
+    if r < 0:
+        raise HCError("hc_phase_trace", r)
+    return out[:r]
 
 
 def hc_fused_workspace_bytes(n: int, hc: int, d: int) -> int:

@@ -498,6 +498,12 @@ int hc_noalloc_status(int clear) {
     return r < 0 ? HC_ERR_DEVICE : (r ? HC_ERR_TIMEOUT : HC_OK);
 }
 
+int hc_phase_trace(uint64_t* out, size_t count) {
+    if (!out && count) return HC_ERR_NULL;
+    const int r = hc::phase_trace_copy(out, count);
+    return r < 0 ? HC_ERR_UNSUPPORTED : r;
+}
+
 int hc_probe_stream(const void* src, void* dst, size_t bytes, int32_t wg_per_cu, void* stream) {
     if (bytes % 16 != 0) return HC_ERR_SHAPE;
     if (wg_per_cu < 0 || wg_per_cu > 32) return HC_ERR_VALUE;

@@ -749,6 +749,53 @@ __global__ __launch_bounds__(kThreads, 1) void k_coop(CoopArgs a) {
 // fixed sequence of memory instructions of a tick.
 namespace spec {
 
+// Phase tracing of the wave-specialised kernel, compiled in only with
+// HC_PHASE_TRACE (the library built by `hyper_connection_residual_02_amd.build
+// --phase-trace`; hc_phase_trace copies the tables out).  Lane 0 of each
+// wave adds the s_memrealtime ticks (100 MHz) since its previous mark to the
+// phase just ended, in LDS; at the end every workgroup writes its waves'
+// totals and its tick count to kTrace.  Phases of the MFMA waves: 0 waiting
+// at the tick's barrier, 1 publication, 2 DMA issue, 3 products, 4 waiting
+// for the next round's DMA (with PO: and for the four waves' arrival), 5
+// (PO) hc_post of the next round.  Exchange waves: 0 barrier, 1 exchange
+// (tag check, member sums, pre, the owned token's mixes), 2 h, 3 residual
+// copy, 4 record-load issue, 5 (PO) R' stores.
+#ifdef HC_PHASE_TRACE
+constexpr int kTrPhases = 6;
+constexpr int kTrMaxBlocks = 1024;
+constexpr int kTrWords = kWaves * (kTrPhases + 1);       // per workgroup: per wave the phases, then ticks
+__device__ uint64_t kTrace[kTrMaxBlocks * kTrWords];
+__shared__ uint32_t tr_tot[kWaves][kTrPhases];
+__shared__ uint32_t tr_last[kWaves];
+__device__ __forceinline__ void tr_start() {
+    if ((threadIdx.x & 63) == 0) {
+        const int w = threadIdx.x >> 6;
+        for (int i = 0; i < kTrPhases; ++i) tr_tot[w][i] = 0u;
+        tr_last[w] = (uint32_t)__builtin_amdgcn_s_memrealtime();
+    }
+}
+__device__ __forceinline__ void tr_mark(int ph) {
+    if ((threadIdx.x & 63) == 0) {
+        const int w = threadIdx.x >> 6;
+        const uint32_t now = (uint32_t)__builtin_amdgcn_s_memrealtime();
+        tr_tot[w][ph] += now - tr_last[w];
+        tr_last[w] = now;
+    }
+}
+__device__ __forceinline__ void tr_finish(int ticks) {
+    if ((threadIdx.x & 63) == 0 && blockIdx.x < (unsigned)kTrMaxBlocks) {
+        const int w = threadIdx.x >> 6;
+        uint64_t* o = &kTrace[(size_t)blockIdx.x * kTrWords + w * (kTrPhases + 1)];
+        for (int i = 0; i < kTrPhases; ++i) o[i] = tr_tot[w][i];
+        o[kTrPhases] = (uint64_t)ticks;
+    }
+}
+#else
+__device__ __forceinline__ void tr_start() {}
+__device__ __forceinline__ void tr_mark(int) {}
+__device__ __forceinline__ void tr_finish(int) {}
+#endif
+
 constexpr int kMW = 4;                  // MFMA waves
 constexpr int kTokX = kT / 4;           // tokens per exchange wave
 constexpr int kXL = 8;                  // exchange loads per lane and pass: 32 members / 4 lane groups
@@ -1554,14 +1601,19 @@ __device__ __forceinline__ bool x_tick(XState<KS>& X, const CoopArgs& a, const R
     bool bad = false;
     const bool xr = t >= 2 && t - 2 < c.nr;
     if (xr) bad = x_exchange<KS, FUSED, LOCAL, PO>(X, a, c, L, xw, t - 2);
+    tr_mark(1);
     if (FUSED && xr && !bad) x_h<KS, PO>(X.rb[P], a, c, L, xw, t - 2);
+    tr_mark(2);
     if (FUSED) x_copy<KS, PO>(X.rb[P], c, L, xw, t);
+    tr_mark(3);
     if constexpr (PO) {
         if (t < c.nr) x_store<KS>(X.rb[P], a, c, xw, t);
+        tr_mark(5);
     }
     // records of round t-1 (published at the start of this tick) for the
     // next tick's exchange: their latency overlaps the barrier
     if (t >= 1 && t - 1 < c.nr) x_issue<KS, FUSED, LOCAL>(X, a, c, xw, t - 1);
+    tr_mark(4);
     return bad;
 }
 
@@ -1594,14 +1646,17 @@ __device__ __forceinline__ void spec_body(const CoopArgs& a, const RoundCtx& c, 
             else L.stop = 1;
         }
         __syncthreads();
+        tr_start();
         for (int t = 0;; ++t) {
             // records first (peers are waiting for them), then the residual
             // loads, then the products of round t
             m_publish<KS, LOCAL, PO>(a, c, L, M, t - 1);
+            tr_mark(1);
             if constexpr (PO) {
                 // round t+2 into the slots round t-1 left; round t (R' since
                 // last tick) is multiplied; round t+1 is turned into R'
                 m_dma<KS, PO>(S, a, c, L, t + 2);
+                tr_mark(2);
                 // round t+1 landed (issued last tick): younger than its loads
                 // are at most last tick's R' stores, this tick's two record
                 // stores and its loads, and the R' stores are older than the
@@ -1612,18 +1667,25 @@ __device__ __forceinline__ void spec_body(const CoopArgs& a, const RoundCtx& c, 
                 // every MFMA wave's publication has read the (single) partials
                 const bool bad = m_wait(a, &L.acnt, 4u * (t + 2));
                 if (bad) L.stop = 1;
+                tr_mark(4);
                 m_mfma<KS, PO>(S, c, L, t);
+                tr_mark(3);
                 if (t + 1 < c.nr && !bad) m_post<KS>(a, c, L, t + 1);
+                tr_mark(5);
             } else {
                 m_dma<KS>(S, a, c, L, t + 2);
+                tr_mark(2);
                 m_mfma<KS>(S, c, L, t);
+                tr_mark(3);
                 // round t+1 (issued last tick, its loads the youngest memory
                 // instructions of that tick) must be in LDS before the barrier:
                 // younger than them are only this tick's two record stores and
                 // its loads
                 asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW + 2) : "memory");
+                tr_mark(4);
             }
             __syncthreads();
+            tr_mark(0);
             if (L.stop || t + 1 > last) break;
         }
         // no load may still be writing this workgroup's LDS when it ends
@@ -1632,12 +1694,15 @@ __device__ __forceinline__ void spec_body(const CoopArgs& a, const RoundCtx& c, 
         XState<KS> X;
         x_offsets<KS>(X, a, c, c.w - kMW);
         __syncthreads();
+        tr_start();
         for (int t = 0;; t += 2) {
             if (x_tick<KS, FUSED, LOCAL, 0, PO>(X, a, c, L, t)) L.stop = 1;
             __syncthreads();
+            tr_mark(0);
             if (L.stop || t + 1 > last) break;
             if (x_tick<KS, FUSED, LOCAL, 1, PO>(X, a, c, L, t + 1)) L.stop = 1;
             __syncthreads();
+            tr_mark(0);
             if (L.stop || t + 2 > last) break;
         }
     }
@@ -1741,8 +1806,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
     if (mode < 0 || c.g >= a.ntiles) return;
     if (mode) spec_body<KS, FUSED, true, PO>(a, c, L);
     else spec_body<KS, FUSED, false, PO>(a, c, L);
+    tr_finish(c.nr + 2);
 }
 
+
+}  // namespace spec
+
+// The phase tables of the last wave-specialised launches (HC_PHASE_TRACE
+// builds): count words of [workgroup][wave][phase 0..5, ticks]; returns the
+// words copied, or -1 without tracing or on a copy failure.
+int phase_trace_copy(uint64_t* out, size_t count) {
+#ifdef HC_PHASE_TRACE
+    const size_t n = count < (size_t)spec::kTrMaxBlocks * spec::kTrWords ? count
+                                                                          : (size_t)spec::kTrMaxBlocks * spec::kTrWords;
+    if (hipMemcpyFromSymbol(out, HIP_SYMBOL(spec::kTrace), n * sizeof(uint64_t), 0, hipMemcpyDeviceToHost) !=
+        hipSuccess)
+        return -1;
+    return (int)n;
+#else
+    (void)out;
+    (void)count;
+    return -1;
+#endif
+}
+
+namespace spec {
 
 // ============================================== two-pass path (short runs)
 // For a call of few tokens the persistent kernel's fixed costs (the start-up

@@ -27,6 +27,9 @@ int launch_pre_norm(const void* R, const float* pre, const float* gamma, void* h
 // Bandwidth probe (hc_probe.hip): copy src -> dst, or read src when dst is
 // null, on wg_per_cu workgroups per compute unit.
 int launch_probe(const void* src, void* dst, uint64_t bytes, int wg_per_cu, hipStream_t s);
+// Phase tables of the wave-specialised kernel (phase-tracing builds only):
+// words copied, or -1.
+int phase_trace_copy(uint64_t* out, size_t count);
 
 // Standalone split + Sinkhorn (hc_sinkhorn.hip); pre may be NULL (not written).
 int launch_split(const float* mixes, const float* scale, const float* base, float* pre, float* post,

@@ -407,6 +407,29 @@ int hc_workspace_status(const void *workspace, size_t workspace_bytes,
 int hc_noalloc_status(int clear);
 
 /*
+ * hc_phase_trace -- diagnostics: where the persistent projection kernel of
+ * hc_fused_mix_pre / hc_mixes / hc_post_mix_pre (the wave-specialised
+ * kernel, calls of more than 2,048 tokens at d = 5120) spends its time.
+ * Only a library built with phase tracing (`python -m
+ * hyper_connection_residual_02_amd.build --phase-trace`, libhc_trace.so)
+ * records it; every other build returns HC_ERR_UNSUPPORTED.  Copies, after
+ * the caller's synchronisation, up to `count` words of the last launch's
+ * tables to the host array `out`: per workgroup (block index b, up to
+ * 1,024) and per wave (8), 7 words -- the s_memrealtime ticks (100 MHz)
+ * spent in phases 0..5, then the number of ticks of the round loop.
+ * Phases, MFMA waves 0..3: 0 the tick's barrier, 1 publishing partial
+ * sums, 2 issuing the residual loads, 3 products, 4 waiting for the next
+ * round's loads, 5 (hc_post_mix_pre) hc_post of the next round; exchange
+ * waves 4..7: 0 barrier, 1 exchange (record waits, member sums, pre, the
+ * owned token's mixes), 2 h, 3 residual copy, 4 issuing the next record
+ * loads, 5 (hc_post_mix_pre) R' stores.  A workgroup's words are those of
+ * the last launch that ran it.  Returns the number of words copied, or
+ * HC_ERR_NULL (out NULL, count > 0) / HC_ERR_UNSUPPORTED.  Synchronous
+ * (hipMemcpyFromSymbol).
+ */
+int hc_phase_trace(uint64_t *out, size_t count);
+
+/*
  * hc_debug_force_timeout -- diagnostics for tests of the failure path:
  * the next `calls` launches of the waiting kernels (see hc_mixes) made by
  * the calling host thread take every exchanged partial sum for stale and

@@ -160,6 +160,9 @@ int main() {
     expect("status small", hc_workspace_status(P(W), 16, 0), HC_ERR_WORKSPACE);
     (void)hc_noalloc_status(0);
     expect("force_timeout negative", hc_debug_force_timeout(-1), HC_ERR_VALUE);
+    uint64_t trace_words[16] = {0};
+    expect("phase_trace null", hc_phase_trace(nullptr, 16), HC_ERR_NULL);
+    expect("phase_trace untraced build", hc_phase_trace(trace_words, 16), HC_ERR_UNSUPPORTED);
 
     std::printf(g_bad ? "FAIL\n" : "ok\n");
     return g_bad;

@@ -128,6 +128,15 @@ def test_norm_checks(lib):
     assert g(y=B + 16) == ALIAS             # y overlaps pre
 
 
+def test_phase_trace_unsupported_in_the_library(lib):
+    # libhc.so has no phase tracing compiled in: no device access, only the status
+    buf = (ctypes.c_uint64 * 16)()
+    lib.hc_phase_trace.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    assert lib.hc_phase_trace(ctypes.cast(buf, ctypes.c_void_p), 16) == UNSUP
+    assert lib.hc_phase_trace(None, 16) == NULL
+    assert lib.hc_phase_trace(None, 0) == UNSUP
+
+
 def test_probe_checks(lib):
     f = lambda s=A, d=B, nb=4096, wg=0: lib.hc_probe_stream(P(s), P(d), nb, wg, None)
     assert f(nb=0) == OK
