@@ -1413,9 +1413,16 @@ __device__ __forceinline__ void x_issue(XState<KS>& X, const CoopArgs& a, const 
 #pragma unroll
     for (int s = 0; s < kXL; ++s)
         X.P[s] = ld_rec<LOCAL>(c, pre_live<FUSED>(a, c, s) ? slot + X.pb + s * kLoadStride : kOOB);
+    // the owned token's records: only the waves that own a token load them
+    // (the others' would all fall outside the resource)
+    if (xw < c.nown) {
 #pragma unroll
-    for (int s = 0; s < kXL; ++s)
-        X.O[s] = ld_rec<LOCAL>(c, own_live(a, c, xw, s) ? slot + X.ob + s * kLoadStride : kOOB);
+        for (int s = 0; s < kXL; ++s)
+            X.O[s] = ld_rec<LOCAL>(c, own_live(a, c, xw, s) ? slot + X.ob + s * kLoadStride : kOOB);
+    } else {
+#pragma unroll
+        for (int s = 0; s < kXL; ++s) X.O[s] = u32x4{0u, 0u, 0u, 0u};
+    }
 }
 
 // Exchange of round r for exchange wave xw, from the loads issued by
@@ -1469,25 +1476,22 @@ __device__ __forceinline__ bool x_exchange(XState<KS>& X, const CoopArgs& a, con
         pre_mine = pre_gate(mix_value(mk, mix_scale(n1, n2, a.K, a.norm_eps)), c.s0, c.bpre, a.eps);
         if ((e & 1) == 0) L.xpre[xw][j][k] = pre_mine;
     }
-    // owned token: entry e = chunk e
-    {
+    // owned token q + G xw (waves that own one): entry e = chunk e, then
+    // its mixes from lanes 0..23
+    if (xw < c.nown) {
         const float v0 = member_sum(X.O, 0), v1 = member_sum(X.O, 1), v2 = member_sum(X.O, 2);
         if (l < kChunks) {
             L.xown[xw][l][0] = v0;
             L.xown[xw][l][1] = v1;
             L.xown[xw][l][2] = v2;
         }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");     // the wave reads back its own LDS writes
-    {
-        // mixes of the owned token: lanes 0..23
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");     // the wave reads back its own LDS writes
         const int f = l < kMix ? l : 0;
         int ch, sl;
         field_pos(f, ch, sl);
         const float v = mix_value(L.xown[xw][ch][sl], mix_scale(L.xown[xw][1][1], L.xown[xw][1][2], a.K, a.norm_eps));
         const __amdgpu_buffer_rsrc_t rm = tile_rsrc(a.mixes, kMix * 4, tok0, a.n, kT);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rm,
-                                              xw < c.nown && l < kMix ? (otk * kMix + l) * 4 : kOOB, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rm, l < kMix ? (otk * kMix + l) * 4 : kOOB, 0, 0);
     }
     if (FUSED) {
         // pre output of the tokens this member owns
