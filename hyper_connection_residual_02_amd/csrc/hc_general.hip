@@ -21,6 +21,9 @@
 //               calls, to fill the chip).  The two give the same bits, and
 //               the tile size does not matter to a token's sums, so a
 //               token's mixes never depend on the rest of its call.
+//  * k_gmm_tall -- the same sums for long fused calls at 7 or 8 streams:
+//               512-token tiles with the residual loaded straight into the
+//               MFMA registers, one segment per workgroup (the same bits).
 //  * k_gsplit -- split + epsilon-Sinkhorn, one token per thread, with the
 //               gate, softmax and normalisation arithmetic of the four-stream
 //               kernel (same functions, same order).
@@ -65,6 +68,8 @@ size_t gen_ws_bytes(int64_t n, int hc_, int d) {
 namespace {
 
 constexpr int kGThreads = 256;
+constexpr int kBufDword3 = 0x00020000;      // raw buffer resource, dword 3
+constexpr int kBufOOB = 0x7FFFFFF0;         // buffer offset past every resource: loads read 0
 
 // Mix formula of the "Mix projection" page: m_j = r * sum_i x_i W[j, i] with
 // r = 1 / sqrt(sum_i x_i^2 / K + norm_eps), K = hc * d, over the flattened
@@ -435,6 +440,163 @@ __global__ __launch_bounds__(2 * T) void k_gmm(const uint16_t* __restrict__ R, c
         }
 }
 
+// Tall tiles for long fused calls (weights split once, a workspace for the
+// partial sums): a workgroup takes 512 tokens (8 waves of 64) and one of
+// the kSeg segments, loads the residual straight from HBM into the MFMA A
+// registers (two chunks ahead, no LDS), and stages only the split weights
+// through LDS.  A segment's weight pieces are then read once per 512 tokens
+// (k_gmm: per tile of at most 256, with the tile's residual rows in LDS
+// beside them), and each weight fragment read from LDS serves four 16-token
+// MFMA tiles.  Every accumulator sees k_gmm's sequence of MFMAs (per k-step
+// the hi, mid and lo pieces; the sums of squares from A A^T), the segment's
+// sums go to the workspace as in k_gmm's segment mode and k_gred adds them
+// in order: the bits are k_gmm's.  Every chunk step issues the same memory
+// instructions (chunks past the segment lie outside their buffer
+// resources: zeros in), so the loop body is straight-line and the loads of
+// the next chunks stay in flight across its waits.
+constexpr int kTallT = 512;                 // tokens per workgroup
+constexpr int64_t kTallMinN = 16384;        // from here the tall tiles fill the chip on their own
+// Stream counts whose weights the tall tiles pay for: more than 48 mixes
+// (hc = 7, 8).  At hc = 8 the fused call took 2,598 against 2,960 us at
+// 65,536 tokens, d = 5120, at hc = 7 2,175 against 2,339 us; at hc = 5 and 6
+// (35 and 48 mixes, the residual's bytes dominating) k_gmm was 1-2 % faster.
+constexpr int kTallMinM = 48;
+
+template <int HC>
+struct TallLds {
+    bf16x8 b[2][2][3][Gmm<HC>::CT][64];     // the chunk's B fragments, by chunk parity
+};
+
+template <int HC>
+__global__ __launch_bounds__(512, 1) void k_gmm_tall(const uint16_t* __restrict__ R, const u32x4* __restrict__ Wp,
+                                                     float* __restrict__ part, int64_t n, int d) {
+    constexpr int M = Gmm<HC>::M, CT = Gmm<HC>::CT, F = Gmm<HC>::F;
+    constexpr int kFr = 2 * 3 * CT * 64;                   // 16-byte B fragments per chunk
+    constexpr int kP = (kFr + 511) / 512;                  // per thread
+    __shared__ __attribute__((aligned(16))) TallLds<HC> L;
+    const int64_t K = (int64_t)HC * d;
+    const int64_t C = (K + kKC - 1) / kKC;
+    const int64_t tile = blockIdx.x / kSeg;
+    const int sg = (int)(blockIdx.x % kSeg);
+    const int tid = threadIdx.x, l = tid & 63, wv = tid >> 6;
+    const int row = l & 15, grp = l >> 4;
+    const int64_t c0 = sg * C / kSeg, c1 = (sg + 1) * C / kSeg;
+    // the wave's 64 token rows as a buffer resource (rows past n outside it)
+    const int64_t tw = tile * kTallT + 64 * wv;
+    int64_t rows = n - tw;
+    rows = rows < 0 ? 0 : (rows > 64 ? 64 : rows);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(R) + (rows > 0 ? tw : 0) * K, 0, (int)(rows * K * 2), kBufDword3);
+    // the segment's split weights: chunks c0 .. c1 - 1
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u32x4*>(Wp) + c0 * kFr, 0, (int)((c1 - c0) * kFr * 16), kBufDword3);
+    // A pieces of chunk ch: [16-token tile][k-step]; k past K reads zeros
+    auto load_a = [&](u32x4 (&a)[4][2], int64_t ch) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const int64_t k = ch * kKC + 32 * st + 8 * grp;
+                const int off = ch < c1 && k < K ? (int)(((int64_t)(16 * tt + row) * K + k) * 2) : kBufOOB;
+                a[tt][st] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+            }
+    };
+    auto load_b = [&](u32x4 (&p)[kP], int64_t ch) {
+#pragma unroll
+        for (int i = 0; i < kP; ++i) {
+            const int f = i * 512 + tid;
+            const int off = ch < c1 && f < kFr ? (int)(((ch - c0) * kFr + f) * 16) : kBufOOB;
+            p[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+        }
+    };
+    auto store_b = [&](const u32x4 (&p)[kP], int q) {
+        u32x4* dst = reinterpret_cast<u32x4*>(&L.b[q][0][0][0][0]);
+#pragma unroll
+        for (int i = 0; i < kP; ++i) {
+            const int f = i * 512 + tid;
+            if (f < kFr) dst[f] = p[i];
+        }
+    };
+    f32x4 dot[4][CT], sq[4], sb[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) dot[tt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        sq[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        sb[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    // products of one chunk from A registers a and LDS buffer q (k_gmm's
+    // order for every accumulator)
+    auto mma = [&](const u32x4 (&a)[4][2], int q) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            bf16x8 ab[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const u32x4 av = a[tt][st];
+                ab[tt] = __builtin_bit_cast(bf16x8, av);
+                sq[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab[tt], ab[tt], sq[tt], 0, 0, 0);
+                const u32x4 as = u32x4{scaled_x2(av[0]), scaled_x2(av[1]), scaled_x2(av[2]), scaled_x2(av[3])};
+                const bf16x8 sbf = __builtin_bit_cast(bf16x8, as);
+                sb[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sbf, sbf, sb[tt], 0, 0, 0);
+            }
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int pc = 0; pc < 3; ++pc) {
+                    const bf16x8 b = L.b[q][st][pc][ct][l];
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt)
+                        dot[tt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab[tt], b, dot[tt][ct], 0, 0, 0);
+                }
+            asm volatile("" ::: "memory");
+        }
+    };
+    if (c0 < c1) {
+        u32x4 a0[4][2], a1[4][2], pb[kP];
+        load_b(pb, c0);
+        store_b(pb, 0);
+        load_b(pb, c0 + 1);
+        load_a(a0, c0);
+        load_a(a1, c0 + 1);
+        __syncthreads();
+        // chunk ch from a0 / buffer 0, chunk ch + 1 from a1 / buffer 1; the
+        // weights of the next chunk go to the other buffer before the
+        // barrier, and each register set is refilled two chunks ahead
+        int64_t ch = c0;
+        for (; ch + 1 < c1; ch += 2) {
+            mma(a0, 0);
+            store_b(pb, 1);                 // chunk ch + 1
+            load_b(pb, ch + 2);
+            load_a(a0, ch + 2);
+            __syncthreads();
+            mma(a1, 1);
+            store_b(pb, 0);                 // chunk ch + 2
+            load_b(pb, ch + 3);
+            load_a(a1, ch + 3);
+            __syncthreads();
+        }
+        if (ch < c1) mma(a0, 0);            // an odd last chunk
+    }
+    // the segment's sums: lane (row, grp) holds tokens 4 grp + r of each
+    // 16-token tile for column row; the sums of squares are the diagonal
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t t = tw + 16 * tt + 4 * grp + r;
+            if (t >= n) continue;
+            float* pt = part + (t * kSeg + sg) * F;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                if (16 * ct + row < M) pt[16 * ct + row] = dot[tt][ct][r];
+            if (row == 4 * grp + r) {
+                pt[M] = sq[tt][r];
+                pt[M + 1] = sb[tt][r];
+            }
+        }
+}
+
 // The partial sums of k_gmm's segments, added in segment order (the order
 // of a workgroup that takes them all), then the mixes.  One thread per token.
 template <int HC>
@@ -672,14 +834,25 @@ int gmm_launch(const void* R, const float* W, const u32x4* Wp, float* mixes, flo
     return 0;
 }
 
-// The projection.  Tiles of 256 tokens while they fill the compute units
-// on their own; shorter calls take smaller tiles, and with a workspace for
-// the partial sums (part) one workgroup per segment as well.  Every choice
-// gives the same bits.
+// The projection.  With the weights split once and a workspace for the
+// partial sums, long calls at 7 or 8 streams take k_gmm_tall.  Otherwise tiles of 256 tokens
+// while they fill the compute units on their own; shorter calls take
+// smaller tiles, and with a workspace for the partial sums (part) one
+// workgroup per segment as well.  Every choice gives the same bits.
 template <int HC>
 struct MixOp {
     static int run(const void* R, const float* W, const u32x4* Wp, float* mixes, float* part, int64_t n, int d,
                    float norm_eps, hipStream_t s) {
+        if (Gmm<HC>::M > kTallMinM && Wp && part && n >= kTallMinN &&
+            (int64_t)HC * d * 2 * kTallT < ((int64_t)1 << 31)) {
+            const int64_t tiles = (n + kTallT - 1) / kTallT;
+            hipLaunchKernelGGL(k_gmm_tall<HC>, dim3((unsigned)(tiles * kSeg)), dim3(512), 0, s,
+                               static_cast<const uint16_t*>(R), Wp, part, n, d);
+            if (hipGetLastError() != hipSuccess) return -1;
+            hipLaunchKernelGGL(k_gred<HC>, dim3(grid_for(n)), dim3(kGThreads), 0, s, part, mixes, n,
+                               (float)((int64_t)HC * d), norm_eps);
+            return hipGetLastError() == hipSuccess ? 0 : -1;
+        }
         const int64_t cus = num_cus();
         const int G = (part && (n + 255) / 256 < cus) ? kSeg : 1;
         const int64_t want = G == 1 ? cus : (cus + kSeg - 1) / kSeg;      // tiles that fill the chip
