@@ -728,8 +728,11 @@ def bench_phases(args, hcl, hin, torch, np, w, t, ws, outs, Rout, dev):
         z.record(stream)
         torch.cuda.synchronize()
         v.append(a.elapsed_time(z) * 1e3)
-    tr = hcl.phase_trace(1024 * 8 * 7).reshape(-1, 8, 7).astype(np.float64)
-    tr = tr[tr[:, 0, 6] > 0]
+    raw = hcl.phase_trace(1024 * 60)
+    tr = raw[:1024 * 56].reshape(-1, 8, 7).astype(np.float64)
+    ran = tr[:, 0, 6] > 0
+    ts = raw[1024 * 56:].reshape(-1, 4).astype(np.int64)[ran]
+    tr = tr[ran]
     if len(tr) == 0:
         print("--phases: the call did not run the wave-specialised kernel (calls of at most 2,048 tokens "
               "take the two-pass path)", file=sys.stderr)
@@ -748,7 +751,15 @@ def bench_phases(args, hcl, hin, torch, np, w, t, ws, outs, Rout, dev):
             "steps": args.steps, "warmup": args.warmup, "higher_is_better": False, "vs_baseline": None,
             "data": "synthetic", "config": {"workload": "%s: %d tokens, d=%d, %s" % (w.name, w.n, w.d, name)},
             "call_avg_us": round(call_us, 1), "workgroups": int(len(tr)), "ticks_per_workgroup": round(nt, 1),
-            "tick_us_from_call": round(call_us / nt, 3), "phases_us_per_tick": phases}
+            "tick_us_from_call": round(call_us / nt, 3), "phases_us_per_tick": phases,
+            # the last call's workgroups on the common clock (100 MHz): start-up
+            # protocol, weights and first residual loads, round loop; and the
+            # span from the first entry to the last end
+            "workgroup_us_median": {"startup": round(float(np.median(ts[:, 1] - ts[:, 0])) * 0.01, 2),
+                                    "prologue": round(float(np.median(ts[:, 2] - ts[:, 1])) * 0.01, 2),
+                                    "loop": round(float(np.median(ts[:, 3] - ts[:, 2])) * 0.01, 2)},
+            "entry_spread_us": round(float(ts[:, 0].max() - ts[:, 0].min()) * 0.01, 2),
+            "device_span_us": round(float(ts[:, 3].max() - ts[:, 0].min()) * 0.01, 2)}
     print(json.dumps(line), flush=True)
     if args.phases_md:
         rows = []
@@ -764,6 +775,12 @@ def bench_phases(args, hcl, hin, torch, np, w, t, ws, outs, Rout, dev):
               "Library: libhc_trace.so (phase tracing compiled in). Call average %.1f us over %d calls; "
               "%d workgroups, %.1f ticks each; %.3f us per tick from the call time." % (
                   call_us, args.steps, len(tr), nt, call_us / nt), "",
+              "Last call, on the common clock: first workgroup entry to last end %.1f us (entries spread over "
+              "%.1f us); per workgroup (median) start-up protocol %.1f us, weights and first residual loads "
+              "%.1f us, round loop %.1f us." % (line["device_span_us"], line["entry_spread_us"],
+                                               line["workgroup_us_median"]["startup"],
+                                               line["workgroup_us_median"]["prologue"],
+                                               line["workgroup_us_median"]["loop"]), "",
               "| wave role | phase | us per tick |", "|---|---|---|", *rows, "",
               "Each wave's phase totals (s_memrealtime, 100 MHz) over the round loop, divided by its tick count "
               "and averaged over the role's waves in every workgroup of the last call.", ""]

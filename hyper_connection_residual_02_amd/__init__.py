@@ -165,9 +165,10 @@ def probe_stream(src: torch.Tensor, dst: torch.Tensor | None = None, wg_per_cu: 
 def phase_trace(words: int):
     """The phase tables of the persistent projection kernel's last launch
     (phase-tracing build only, see use_library): a uint64 numpy array of up
-    to `words` words, [workgroup][wave][7]: the s_memrealtime ticks (100 MHz)
-    of phases 0..5, then the round loop's tick count (include/hc.h,
-    hc_phase_trace, names the phases).  Synchronises."""
+    to `words` words, [1024 workgroups][8 waves][7]: the s_memrealtime ticks
+    (100 MHz) of phases 0..5, then the round loop's tick count; then
+    [1024 workgroups][4] clock stamps: entry, end of start-up, start of the
+    round loop, end (include/hc.h, hc_phase_trace).  Synchronises."""
     import numpy as np
     out = np.zeros(int(words), dtype=np.uint64)
     torch.cuda.synchronize()

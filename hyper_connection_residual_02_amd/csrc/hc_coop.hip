@@ -759,14 +759,22 @@ namespace spec {
 // for the next round's DMA (with PO: and for the four waves' arrival), 5
 // (PO) hc_post of the next round.  Exchange waves: 0 barrier, 1 exchange
 // (tag check, member sums, pre, the owned token's mixes), 2 h, 3 residual
-// copy, 4 record-load issue, 5 (PO) R' stores.
+// copy, 4 record-load issue, 5 (PO) R' stores.  Thread 0 of each workgroup
+// also stamps the clock at four points (kTraceTs): entry, the end of the
+// start-up protocol, the start of the round loop (after the weights and the
+// first residual loads) and the end.
 #ifdef HC_PHASE_TRACE
 constexpr int kTrPhases = 6;
 constexpr int kTrMaxBlocks = 1024;
 constexpr int kTrWords = kWaves * (kTrPhases + 1);       // per workgroup: per wave the phases, then ticks
 __device__ uint64_t kTrace[kTrMaxBlocks * kTrWords];
+__device__ uint64_t kTraceTs[kTrMaxBlocks * 4];
 __shared__ uint32_t tr_tot[kWaves][kTrPhases];
 __shared__ uint32_t tr_last[kWaves];
+__shared__ uint64_t tr_ts[4];
+__device__ __forceinline__ void tr_stamp(int i) {
+    if (threadIdx.x == 0) tr_ts[i] = __builtin_amdgcn_s_memrealtime();
+}
 __device__ __forceinline__ void tr_start() {
     if ((threadIdx.x & 63) == 0) {
         const int w = threadIdx.x >> 6;
@@ -788,9 +796,14 @@ __device__ __forceinline__ void tr_finish(int ticks) {
         uint64_t* o = &kTrace[(size_t)blockIdx.x * kTrWords + w * (kTrPhases + 1)];
         for (int i = 0; i < kTrPhases; ++i) o[i] = tr_tot[w][i];
         o[kTrPhases] = (uint64_t)ticks;
+        if (w == 0) {
+            tr_ts[3] = __builtin_amdgcn_s_memrealtime();
+            for (int i = 0; i < 4; ++i) kTraceTs[(size_t)blockIdx.x * 4 + i] = tr_ts[i];
+        }
     }
 }
 #else
+__device__ __forceinline__ void tr_stamp(int) {}
 __device__ __forceinline__ void tr_start() {}
 __device__ __forceinline__ void tr_mark(int) {}
 __device__ __forceinline__ void tr_finish(int) {}
@@ -1651,6 +1664,7 @@ __device__ __forceinline__ void spec_body(const CoopArgs& a, const RoundCtx& c, 
         }
         __syncthreads();
         tr_start();
+        tr_stamp(2);
         for (int t = 0;; ++t) {
             // records first (peers are waiting for them), then the residual
             // loads, then the products of round t
@@ -1716,6 +1730,7 @@ template <int KS, bool FUSED, bool PO = false>
 __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
     __shared__ __attribute__((aligned(16))) Lds<KS, PO> L;
     __shared__ int local_mode;
+    tr_stamp(0);
     RoundCtx c;
     c.g = blockIdx.x % a.NG;
     c.q = blockIdx.x / a.NG;
@@ -1807,6 +1822,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
     }
     __syncthreads();
     const int mode = local_mode;
+    tr_stamp(1);
     if (mode < 0 || c.g >= a.ntiles) return;
     if (mode) spec_body<KS, FUSED, true, PO>(a, c, L);
     else spec_body<KS, FUSED, false, PO>(a, c, L);
@@ -1817,16 +1833,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
 }  // namespace spec
 
 // The phase tables of the last wave-specialised launches (HC_PHASE_TRACE
-// builds): count words of [workgroup][wave][phase 0..5, ticks]; returns the
-// words copied, or -1 without tracing or on a copy failure.
+// builds): up to count words of [workgroup][wave][phase 0..5, ticks] (1,024
+// workgroups), then [workgroup][4 timestamps]; returns the words copied, or
+// -1 without tracing or on a copy failure.
 int phase_trace_copy(uint64_t* out, size_t count) {
 #ifdef HC_PHASE_TRACE
-    const size_t n = count < (size_t)spec::kTrMaxBlocks * spec::kTrWords ? count
-                                                                          : (size_t)spec::kTrMaxBlocks * spec::kTrWords;
-    if (hipMemcpyFromSymbol(out, HIP_SYMBOL(spec::kTrace), n * sizeof(uint64_t), 0, hipMemcpyDeviceToHost) !=
+    const size_t nt = (size_t)spec::kTrMaxBlocks * spec::kTrWords, ns = (size_t)spec::kTrMaxBlocks * 4;
+    const size_t n1 = count < nt ? count : nt;
+    const size_t n2 = count > nt ? (count - nt < ns ? count - nt : ns) : 0;
+    if (hipMemcpyFromSymbol(out, HIP_SYMBOL(spec::kTrace), n1 * sizeof(uint64_t), 0, hipMemcpyDeviceToHost) !=
         hipSuccess)
         return -1;
-    return (int)n;
+    if (n2 && hipMemcpyFromSymbol(out + nt, HIP_SYMBOL(spec::kTraceTs), n2 * sizeof(uint64_t), 0,
+                                  hipMemcpyDeviceToHost) != hipSuccess)
+        return -1;
+    return (int)(n1 + n2);
 #else
     (void)out;
     (void)count;

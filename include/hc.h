@@ -416,7 +416,11 @@ int hc_noalloc_status(int clear);
  * the caller's synchronisation, up to `count` words of the last launch's
  * tables to the host array `out`: per workgroup (block index b, up to
  * 1,024) and per wave (8), 7 words -- the s_memrealtime ticks (100 MHz)
- * spent in phases 0..5, then the number of ticks of the round loop.
+ * spent in phases 0..5, then the number of ticks of the round loop; then,
+ * after those 1,024 x 8 x 7 words, 4 words per workgroup -- the clock
+ * (s_memrealtime, common to all compute units) at the workgroup's entry, at
+ * the end of its start-up protocol, at the start of its round loop (after
+ * its weights and first residual loads) and at its end.
  * Phases, MFMA waves 0..3: 0 the tick's barrier, 1 publishing partial
  * sums, 2 issuing the residual loads, 3 products, 4 waiting for the next
  * round's loads, 5 (hc_post_mix_pre) hc_post of the next round; exchange

@@ -6,7 +6,7 @@ process of its own, since the binding loads one library per process) and
 every output is compared bitwise.  Its tables must describe the launch: one
 entry per workgroup of the persistent kernel, each with the round loop's
 tick count (rounds of the workgroup's token group + 2) and phase totals that
-add up to no more than the loop's duration.
+add up to no more than the loop's duration, and clock stamps in order.
 """
 import os
 import subprocess
@@ -34,7 +34,7 @@ h, pre, post, comb, mixes = hcl.hc_fused_mix_pre(t["R"], t["W"], t["scale"], t["
 res = dict(h=hin.bits(h), pre=pre.cpu().numpy(), post=post.cpu().numpy(), comb=comb.cpu().numpy(),
            mixes=mixes.cpu().numpy())
 if %(trace)r:
-    res["trace_fused"] = hcl.phase_trace(1024 * 8 * 7)
+    res["trace_fused"] = hcl.phase_trace(1024 * 60)
 nxt = hin.make_inputs(w, "cuda", seed=12)
 R2, h2, pre2, post2, comb2, mixes2 = hcl.hc_post_mix_pre(t["x"], t["R"], post, comb, nxt["W"], nxt["scale"],
                                                          nxt["base"], want_pre=True, want_mixes=True)
@@ -42,7 +42,7 @@ torch.cuda.synchronize()
 res.update(h2=hin.bits(h2), pre2=pre2.cpu().numpy(), post2=post2.cpu().numpy(), comb2=comb2.cpu().numpy(),
            mixes2=mixes2.cpu().numpy(), R2=hin.bits(R2))
 if %(trace)r:
-    res["trace_boundary"] = hcl.phase_trace(1024 * 8 * 7)
+    res["trace_boundary"] = hcl.phase_trace(1024 * 60)
 np.savez(%(out)r, **res)
 """
 
@@ -64,7 +64,12 @@ def test_traced_build_is_bitwise_the_library_and_its_tables_describe_the_launch(
         assert np.array_equal(a[k], b[k]), k
     rounds = (n + 31) // 32
     for key in ("trace_fused", "trace_boundary"):
-        tr = b[key].reshape(-1, 8, 7)
+        assert b[key].size == 1024 * 60, (key, b[key].size)
+        tr = b[key][:1024 * 56].reshape(-1, 8, 7)
+        ts = b[key][1024 * 56:].reshape(-1, 4)[:256].astype(np.int64)
+        # every workgroup's stamps in order: entry <= start-up done <= loop start <= end
+        assert np.all(np.diff(ts, axis=1) >= 0), key
+        assert np.all(ts[:, 3] - ts[:, 0] < 100_000_000), key
         ran = tr[:, 0, 6] > 0
         assert ran.sum() == 256, (key, int(ran.sum()))       # 8 token groups x 32 members at d = 5120
         assert np.all(ran[:256]) and not ran[256:].any(), key
