@@ -82,7 +82,6 @@ struct WsHeader {
     uint32_t epoch;
     uint32_t err;       // this call: a bounded wait gave up (the call's workgroups stop)
     int64_t clean;
-    uint64_t ready;     // number of the call whose header update is complete
     uint32_t clear;     // this call clears its record area before use
     uint32_t failed;    // sticky: a call on this workspace gave up; cleared by the host status query
     uint32_t garr[kMaxGroups];   // group g, this call: members arrived (low 16 bits) and
@@ -142,7 +141,6 @@ struct CoopArgs {
     int part_bytes;
     uint64_t call;      // process-wide number of this call (sets the record epoch)
     const u32x4* Wp;    // weights already split into MFMA pieces (hc_pack_weights), or null
-    int ext_init;       // k_spec: the header was updated by a launch just before (k_hdr)
     uint64_t spin;      // bound of an exchange wait, in s_memrealtime ticks (100 MHz)
     uint32_t force_tag; // 0; nonzero (diagnostics only) makes every exchange record look stale
     // hc_post_mix_pre in one pass (k_spec, PO): R' = hc_post(x, R, post, comb)
@@ -1747,41 +1745,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
     c.s0 = FUSED ? a.scale[0] : 0.0f;
     c.bpre = FUSED ? base_of_lane(a.base, (threadIdx.x & 63) >> 4) : 0.0f;
 
-    // Start of the call.  Workgroup 0 updates the workspace header and
-    // publishes this call's number; every workgroup waits for it.  Then the
+    // Start of the call.  The workspace header was updated by k_hdr, launched
+    // just before this kernel on the same stream, so it already holds this
+    // call's epoch and says whether the record area is to be cleared.  The
     // members of each group clear the group's share of the record area (if
-    // the header says so) and count themselves in on the group's arrival
-    // word, and a group starts once all G of its members have arrived: no
-    // record is written before the group's area is clean, and no workgroup
-    // waits for one outside its own group (there is no grid-wide count, so
-    // one group's members being held back by other work does not stall the
-    // others).  Placement: with NG a multiple of 8, the members of group g
-    // are the workgroups b = g (mod 8), which the dispatcher places on XCD
-    // b % 8 (checked against the XCC id register); a group whose members all
-    // sit on that XCD keeps its records in the XCD's L2.  Every wait is
-    // bounded (about two seconds): a member that is not resident in time
-    // makes the call give up (error flag, reported by hc_workspace_status).
+    // so) and count themselves in on the group's arrival word, and a group
+    // starts once all G of its members have arrived: no record is written
+    // before the group's area is clean, and no workgroup waits for one
+    // outside its own group (there is no grid-wide count, so one group's
+    // members being held back by other work does not stall the others).
+    // Placement: with NG a multiple of 8, the members of group g are the
+    // workgroups b = g (mod 8), which the dispatcher places on XCD b % 8
+    // (checked against the XCC id register); a group whose members all sit on
+    // that XCD keeps its records in the XCD's L2.  Every wait is bounded
+    // (about two seconds): a member that is not resident in time makes the
+    // call give up (error flag, reported by hc_workspace_status).
     const int64_t nchunks = a.part_bytes / 16;
-    if (threadIdx.x == 0 && a.ext_init) {
-        // the header was updated by k_hdr, launched just before this kernel
+    if (threadIdx.x == 0)
         local_mode = (int)__hip_atomic_load(&a.hdr->clear, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else if (threadIdx.x == 0) {
-        bool ok = true;
-        if (blockIdx.x == 0) {
-            header_update(a.hdr, a.call, nchunks, a.NG);
-            __hip_atomic_store(&a.hdr->ready, a.call, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-            while (__hip_atomic_load(&a.hdr->ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != a.call) {
-                if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull) {
-                    ok = false;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-        }
-        local_mode = ok ? (int)__hip_atomic_load(&a.hdr->clear, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -1;
-    }
     __syncthreads();
     if (local_mode < 0) {
         if (threadIdx.x == 0) give_up(a);
@@ -2103,13 +2084,12 @@ __global__ __launch_bounds__(256) void k_fin(CoopArgs a, int splits) {
 
 }  // namespace spec
 
-// Header update alone, before a call of the wave-specialised kernel that is
-// being captured into a graph.  k_spec's own start-up waits for the host's
-// number of this call to appear in the header; a replayed graph repeats the
-// number, so that wait would let workgroups run ahead of workgroup 0's
-// update.  With the update in a launch of its own, kernel order does it on
-// every replay (and since a replay repeats the epoch, the update orders the
-// record area cleared, which k_spec's workgroups then do in parallel).
+// Header update alone, launched before every call of the wave-specialised
+// kernel.  Kernel order on the stream makes the update visible to all of
+// k_spec's workgroups before any starts, with no grid-wide handshake inside
+// k_spec (a wait on workgroup 0 costs every workgroup the slowest start).
+// A replayed graph repeats the call number and so the epoch; the update then
+// orders the record area cleared, which k_spec's workgroups do in parallel.
 __global__ void k_hdr(WsHeader* hdr, int64_t nchunks, uint64_t call, int ngroups) {
     if (threadIdx.x == 0) header_update(hdr, call, nchunks, ngroups);
 }
@@ -2376,13 +2356,11 @@ int launch_coop(const CoopPlan& p, const void* R, const float* W, const float* s
         k_init<<<1, 1024, 0, s>>>(a.hdr, a.part, (int64_t)(a.part_bytes / 16), a.call);
         if (hipGetLastError() != hipSuccess) return -1;
     }
-    a.ext_init = 0;
     if (use_spec(p)) {
-        if (capturing) {
-            a.ext_init = 1;
-            k_hdr<<<1, 64, 0, s>>>(a.hdr, (int64_t)(a.part_bytes / 16), a.call, a.NG);
-            if (hipGetLastError() != hipSuccess) return -1;
-        }
+        // the header update is a launch of its own: k_spec's workgroups read
+        // it without a grid-wide handshake, and a replayed graph repeats it
+        k_hdr<<<1, 64, 0, s>>>(a.hdr, (int64_t)(a.part_bytes / 16), a.call, a.NG);
+        if (hipGetLastError() != hipSuccess) return -1;
         switch (p.KS) {
             case 1: rc = launch_spec<1>(p, a, fused, one_pass, s); break;
             case 2: rc = launch_spec<2>(p, a, fused, one_pass, s); break;
