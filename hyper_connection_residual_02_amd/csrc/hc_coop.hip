@@ -1780,14 +1780,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
     }
     __syncthreads();
     if (threadIdx.x == 0) {
+        // The count carries data only when the members cleared records: then
+        // the zeros are released before it and acquired after it.  Otherwise
+        // it is relaxed, which spares every member an L2 write-back and each
+        // poll an L2 invalidation (32 members per XCD at once).
+        const bool cleared = local_mode != 0;
         const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11)) & 0xFu;
         const uint32_t add = 1u + (xcc != (blockIdx.x & 7u) ? 0x10000u : 0u);
         uint32_t* gw = &a.hdr->garr[c.g];
-        __hip_atomic_fetch_add(gw, add, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        if (cleared) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(gw, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
         bool ok = true;
         uint32_t v;
-        while (((v = __hip_atomic_load(gw, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)) & 0xFFFFu) < (uint32_t)a.G) {
+        while (((v = __hip_atomic_load(gw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) & 0xFFFFu) < (uint32_t)a.G) {
             if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull ||
                 __hip_atomic_load(&a.hdr->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
                 give_up(a);
@@ -1796,6 +1802,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
             }
             __builtin_amdgcn_s_sleep(1);
         }
+        if (cleared) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         const bool local = a.NG % 8 == 0 && (v >> 16) == 0u;
         local_mode = ok ? (local ? 1 : 0) : -1;
         L.stop = 0;
