@@ -757,10 +757,10 @@ namespace spec {
 // for the next round's DMA (with PO: and for the four waves' arrival), 5
 // (PO) hc_post of the next round.  Exchange waves: 0 barrier, 1 exchange
 // (tag check, member sums, pre, the owned token's mixes), 2 h, 3 residual
-// copy, 4 record-load issue, 5 (PO) R' stores.  Thread 0 of each workgroup
-// also stamps the clock at four points (kTraceTs): entry, the end of the
-// start-up protocol, the start of the round loop (after the weights and the
-// first residual loads) and the end.
+// copy, 4 record-load issue, 5 (PO) R' stores.  Each workgroup also stamps
+// the clock at four points (kTraceTs): entry, the end of the start-up
+// protocol (run by the first exchange wave), the start of the round loop
+// (after the weights and the first residual loads) and the end.
 #ifdef HC_PHASE_TRACE
 constexpr int kTrPhases = 6;
 constexpr int kTrMaxBlocks = 1024;
@@ -770,8 +770,8 @@ __device__ uint64_t kTraceTs[kTrMaxBlocks * 4];
 __shared__ uint32_t tr_tot[kWaves][kTrPhases];
 __shared__ uint32_t tr_last[kWaves];
 __shared__ uint64_t tr_ts[4];
-__device__ __forceinline__ void tr_stamp(int i) {
-    if (threadIdx.x == 0) tr_ts[i] = __builtin_amdgcn_s_memrealtime();
+__device__ __forceinline__ void tr_stamp(int i, unsigned tid = 0) {
+    if (threadIdx.x == tid) tr_ts[i] = __builtin_amdgcn_s_memrealtime();
 }
 __device__ __forceinline__ void tr_start() {
     if ((threadIdx.x & 63) == 0) {
@@ -801,7 +801,7 @@ __device__ __forceinline__ void tr_finish(int ticks) {
     }
 }
 #else
-__device__ __forceinline__ void tr_stamp(int) {}
+__device__ __forceinline__ void tr_stamp(int, unsigned = 0) {}
 __device__ __forceinline__ void tr_start() {}
 __device__ __forceinline__ void tr_mark(int) {}
 __device__ __forceinline__ void tr_finish(int) {}
@@ -1050,11 +1050,18 @@ struct DmaRun {
     }
 };
 
+// The member's weight slice (packed, or split here) and the lane offsets of
+// the residual loads (m_dma).  m_dma_offsets alone is enough to start
+// loading rounds; the persistent kernel issues its first two rounds before
+// fetching the weights, so that both round trips overlap.
 template <int KS, bool PO = false>
-__device__ __forceinline__ void m_setup(MState<KS, PO>& S, const CoopArgs& a, const RoundCtx& c) {
-    using GG = Geo<KS, PO>;
+__device__ __forceinline__ void m_weights(MState<KS, PO>& S, const CoopArgs& a, const RoundCtx& c) {
     if (a.Wp) m_load_packed<KS, PO>(S, a, c);
     else m_split_weights<KS, PO>(S, a, c);
+}
+template <int KS, bool PO = false>
+__device__ __forceinline__ void m_dma_offsets(MState<KS, PO>& S, const CoopArgs& a, const RoundCtx& c) {
+    using GG = Geo<KS, PO>;
 #pragma unroll
     for (int i = 0; i < GG::kDmaW; ++i) {
         const int I = dma_real<KS, PO>(c.w * GG::kDmaW + i);
@@ -1079,6 +1086,11 @@ __device__ __forceinline__ void m_setup(MState<KS, PO>& S, const CoopArgs& a, co
         }
         S.dvoff[i] = v;
     }
+}
+template <int KS, bool PO = false>
+__device__ __forceinline__ void m_setup(MState<KS, PO>& S, const CoopArgs& a, const RoundCtx& c) {
+    m_weights<KS, PO>(S, a, c);
+    m_dma_offsets<KS, PO>(S, a, c);
 }
 
 // Round r of this group (rounds past the end: zeros) into slot r % 3; with
@@ -1635,7 +1647,9 @@ __device__ __forceinline__ bool x_tick(XState<KS>& X, const CoopArgs& a, const R
 // The two roles run separate loops with the same barrier sequence: a
 // prologue barrier, then one barrier per tick t = 0 .. nr+1 (the exchange of
 // the last round happens in tick nr+1); after each barrier both read the
-// stop flag, so both leave after the same tick.
+// stop flag, so both leave after the same tick.  The store scope of the
+// records (LOCAL) is known only at the prologue barrier, so each role's
+// loop is instantiated for both and chosen there.
 //
 // PO (hc_post_mix_pre): in tick t the MFMA waves publish round t-1, issue
 // round t+2 (residual, x, post, comb) into the slots round t-1 left, count
@@ -1643,85 +1657,123 @@ __device__ __forceinline__ bool x_tick(XState<KS>& X, const CoopArgs& a, const R
 // (turned into R' last tick), and then turn round t+1 into R' in place
 // (m_post), which the tick's closing barrier orders before round t+1's
 // products and the exchange waves' copy of it.
-template <int KS, bool FUSED, bool LOCAL, bool PO = false>
-__device__ __forceinline__ void spec_body(const CoopArgs& a, const RoundCtx& c, Lds<KS, PO>& L) {
+template <int KS, bool FUSED, bool LOCAL, bool PO>
+__device__ __forceinline__ void m_loop(MState<KS, PO>& S, const PubMap& M, const CoopArgs& a, const RoundCtx& c,
+                                       Lds<KS, PO>& L) {
     const int last = c.nr + 1;
-    if (c.w < kMW) {
-        MState<KS, PO> S;
-        m_setup<KS, PO>(S, a, c);
-        const PubMap M = pub_map(srec_of);
-        m_dma<KS, PO>(S, a, c, L, 0);
-        m_dma<KS, PO>(S, a, c, L, 1);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS, PO>::kDmaW) : "memory");   // round 0 landed
+    for (int t = 0;; ++t) {
+        // records first (peers are waiting for them), then the residual
+        // loads, then the products of round t
+        m_publish<KS, LOCAL, PO>(a, c, L, M, t - 1);
+        tr_mark(1);
         if constexpr (PO) {
-            // round 0 into R' before the first tick
+            // round t+2 into the slots round t-1 left; round t (R' since
+            // last tick) is multiplied; round t+1 is turned into R'
+            m_dma<KS, PO>(S, a, c, L, t + 2);
+            tr_mark(2);
+            // round t+1 landed (issued last tick): younger than its loads
+            // are at most last tick's R' stores, this tick's two record
+            // stores and its loads, and the R' stores are older than the
+            // last kDmaW + 2, so waiting down to kDmaW + 2 covers round
+            // t+1 (and those stores)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS, PO>::kDmaW + 2) : "memory");
             m_arrive(&L.acnt);
-            const bool bad = m_wait(a, &L.acnt, 4u);
-            if (!bad) m_post<KS>(a, c, L, 0);
-            else L.stop = 1;
+            // every MFMA wave's publication has read the (single) partials
+            const bool bad = m_wait(a, &L.acnt, 4u * (t + 2));
+            if (bad) L.stop = 1;
+            tr_mark(4);
+            m_mfma<KS, PO>(S, c, L, t);
+            tr_mark(3);
+            if (t + 1 < c.nr && !bad) m_post<KS>(a, c, L, t + 1);
+            tr_mark(5);
+        } else {
+            m_dma<KS>(S, a, c, L, t + 2);
+            tr_mark(2);
+            m_mfma<KS>(S, c, L, t);
+            tr_mark(3);
+            // round t+1 (issued last tick, its loads the youngest memory
+            // instructions of that tick) must be in LDS before the barrier:
+            // younger than them are only this tick's two record stores and
+            // its loads
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW + 2) : "memory");
+            tr_mark(4);
         }
         __syncthreads();
-        tr_start();
-        tr_stamp(2);
-        for (int t = 0;; ++t) {
-            // records first (peers are waiting for them), then the residual
-            // loads, then the products of round t
-            m_publish<KS, LOCAL, PO>(a, c, L, M, t - 1);
-            tr_mark(1);
-            if constexpr (PO) {
-                // round t+2 into the slots round t-1 left; round t (R' since
-                // last tick) is multiplied; round t+1 is turned into R'
-                m_dma<KS, PO>(S, a, c, L, t + 2);
-                tr_mark(2);
-                // round t+1 landed (issued last tick): younger than its loads
-                // are at most last tick's R' stores, this tick's two record
-                // stores and its loads, and the R' stores are older than the
-                // last kDmaW + 2, so waiting down to kDmaW + 2 covers round
-                // t+1 (and those stores)
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS, PO>::kDmaW + 2) : "memory");
-                m_arrive(&L.acnt);
-                // every MFMA wave's publication has read the (single) partials
-                const bool bad = m_wait(a, &L.acnt, 4u * (t + 2));
-                if (bad) L.stop = 1;
-                tr_mark(4);
-                m_mfma<KS, PO>(S, c, L, t);
-                tr_mark(3);
-                if (t + 1 < c.nr && !bad) m_post<KS>(a, c, L, t + 1);
-                tr_mark(5);
-            } else {
-                m_dma<KS>(S, a, c, L, t + 2);
-                tr_mark(2);
-                m_mfma<KS>(S, c, L, t);
-                tr_mark(3);
-                // round t+1 (issued last tick, its loads the youngest memory
-                // instructions of that tick) must be in LDS before the barrier:
-                // younger than them are only this tick's two record stores and
-                // its loads
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW + 2) : "memory");
-                tr_mark(4);
-            }
-            __syncthreads();
-            tr_mark(0);
-            if (L.stop || t + 1 > last) break;
-        }
-        // no load may still be writing this workgroup's LDS when it ends
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    } else {
-        XState<KS> X;
-        x_offsets<KS>(X, a, c, c.w - kMW);
-        __syncthreads();
-        tr_start();
-        for (int t = 0;; t += 2) {
-            if (x_tick<KS, FUSED, LOCAL, 0, PO>(X, a, c, L, t)) L.stop = 1;
-            __syncthreads();
-            tr_mark(0);
-            if (L.stop || t + 1 > last) break;
-            if (x_tick<KS, FUSED, LOCAL, 1, PO>(X, a, c, L, t + 1)) L.stop = 1;
-            __syncthreads();
-            tr_mark(0);
-            if (L.stop || t + 2 > last) break;
-        }
+        tr_mark(0);
+        if (L.stop || t + 1 > last) break;
     }
+}
+
+template <int KS, bool FUSED, bool LOCAL, bool PO>
+__device__ __forceinline__ void x_loop(XState<KS>& X, const CoopArgs& a, const RoundCtx& c, Lds<KS, PO>& L) {
+    const int last = c.nr + 1;
+    for (int t = 0;; t += 2) {
+        if (x_tick<KS, FUSED, LOCAL, 0, PO>(X, a, c, L, t)) L.stop = 1;
+        __syncthreads();
+        tr_mark(0);
+        if (L.stop || t + 1 > last) break;
+        if (x_tick<KS, FUSED, LOCAL, 1, PO>(X, a, c, L, t + 1)) L.stop = 1;
+        __syncthreads();
+        tr_mark(0);
+        if (L.stop || t + 2 > last) break;
+    }
+}
+
+// Start of the call, run by the first exchange wave while the MFMA waves
+// load their weights and the first two rounds.  The workspace header was
+// updated by k_hdr, launched just before this kernel on the same stream, so
+// it already holds this call's epoch and says whether the record area is to
+// be cleared.  The member clears its share of its group's record area (if
+// so) and counts itself in on the group's arrival word, and the group
+// starts once all G of its members have arrived: no record is written
+// before the group's area is clean, and no workgroup waits for one outside
+// its own group (there is no grid-wide count, so one group's members being
+// held back by other work does not stall the others).  Placement: with NG a
+// multiple of 8, the members of group g are the workgroups b = g (mod 8),
+// which the dispatcher places on XCD b % 8 (checked against the XCC id
+// register); a group whose members all sit on that XCD keeps its records in
+// the XCD's L2.  The wait is bounded (about two seconds): a member that is
+// not resident in time makes the call give up (error flag, reported by
+// hc_workspace_status).  The count carries data only when the members
+// cleared records: then the zeros are released before it and acquired after
+// it.  Otherwise it is relaxed, which spares every member an L2 write-back
+// and each poll an L2 invalidation.  Result in *mode: 1 local, 0 not, -1
+// gave up.
+__device__ __forceinline__ void start_protocol(const CoopArgs& a, const RoundCtx& c, int* mode) {
+    const bool cleared = __hip_atomic_load(&a.hdr->clear, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+    if (cleared) {
+        // this member's part of group g's records (a group's records are
+        // contiguous: [g][slot][member][record])
+        const int64_t nchunks = a.part_bytes / 16;
+        const int64_t gchunks = nchunks / a.NG;
+        const int64_t per = (gchunks + a.G - 1) / a.G;
+        const int64_t gend = (int64_t)(c.g + 1) * gchunks;
+        const int64_t lo = (int64_t)c.g * gchunks + per * c.q, hi = lo + per < gend ? lo + per : gend;
+        for (int64_t i = lo + c.l; i < hi; i += 64) a.part[i] = u32x4{0u, 0u, 0u, 0u};
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    }
+    if (c.l == 0) {
+        const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11)) & 0xFu;
+        const uint32_t add = 1u + (xcc != (blockIdx.x & 7u) ? 0x10000u : 0u);
+        uint32_t* gw = &a.hdr->garr[c.g];
+        __hip_atomic_fetch_add(gw, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        bool ok = true;
+        uint32_t v;
+        while (((v = __hip_atomic_load(gw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) & 0xFFFFu) < (uint32_t)a.G) {
+            if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull ||
+                __hip_atomic_load(&a.hdr->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+                give_up(a);
+                ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (cleared) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const bool local = a.NG % 8 == 0 && (v >> 16) == 0u;
+        *mode = ok ? (local ? 1 : 0) : -1;
+    }
+    tr_stamp(1, 64 * kMW);
 }
 
 template <int KS, bool FUSED, bool PO = false>
@@ -1744,76 +1796,53 @@ __global__ __launch_bounds__(kThreads, 1) void k_spec(CoopArgs a) {
     c.nr = (int)((a.ntiles - c.g + a.NG - 1) / a.NG);
     c.s0 = FUSED ? a.scale[0] : 0.0f;
     c.bpre = FUSED ? base_of_lane(a.base, (threadIdx.x & 63) >> 4) : 0.0f;
-
-    // Start of the call.  The workspace header was updated by k_hdr, launched
-    // just before this kernel on the same stream, so it already holds this
-    // call's epoch and says whether the record area is to be cleared.  The
-    // members of each group clear the group's share of the record area (if
-    // so) and count themselves in on the group's arrival word, and a group
-    // starts once all G of its members have arrived: no record is written
-    // before the group's area is clean, and no workgroup waits for one
-    // outside its own group (there is no grid-wide count, so one group's
-    // members being held back by other work does not stall the others).
-    // Placement: with NG a multiple of 8, the members of group g are the
-    // workgroups b = g (mod 8), which the dispatcher places on XCD b % 8
-    // (checked against the XCC id register); a group whose members all sit on
-    // that XCD keeps its records in the XCD's L2.  Every wait is bounded
-    // (about two seconds): a member that is not resident in time makes the
-    // call give up (error flag, reported by hc_workspace_status).
-    const int64_t nchunks = a.part_bytes / 16;
-    if (threadIdx.x == 0)
-        local_mode = (int)__hip_atomic_load(&a.hdr->clear, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (local_mode < 0) {
-        if (threadIdx.x == 0) give_up(a);
-        return;
-    }
-    if (local_mode) {
-        // this member's part of group g's records (a group's records are
-        // contiguous: [g][slot][member][record])
-        const int64_t gchunks = nchunks / a.NG;
-        const int64_t per = (gchunks + a.G - 1) / a.G;
-        const int64_t gend = (int64_t)(c.g + 1) * gchunks;
-        const int64_t lo = (int64_t)c.g * gchunks + per * c.q, hi = lo + per < gend ? lo + per : gend;
-        for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x) a.part[i] = u32x4{0u, 0u, 0u, 0u};
-        __threadfence();
-    }
-    __syncthreads();
+    // a group with no token tile: all its members leave (none waits on them)
+    if (c.g >= a.ntiles) return;
     if (threadIdx.x == 0) {
-        // The count carries data only when the members cleared records: then
-        // the zeros are released before it and acquired after it.  Otherwise
-        // it is relaxed, which spares every member an L2 write-back and each
-        // poll an L2 invalidation (32 members per XCD at once).
-        const bool cleared = local_mode != 0;
-        const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11)) & 0xFu;
-        const uint32_t add = 1u + (xcc != (blockIdx.x & 7u) ? 0x10000u : 0u);
-        uint32_t* gw = &a.hdr->garr[c.g];
-        if (cleared) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __hip_atomic_fetch_add(gw, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        bool ok = true;
-        uint32_t v;
-        while (((v = __hip_atomic_load(gw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) & 0xFFFFu) < (uint32_t)a.G) {
-            if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull ||
-                __hip_atomic_load(&a.hdr->err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-                give_up(a);
-                ok = false;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        if (cleared) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        const bool local = a.NG % 8 == 0 && (v >> 16) == 0u;
-        local_mode = ok ? (local ? 1 : 0) : -1;
         L.stop = 0;
         L.acnt = 0u;
     }
     __syncthreads();
-    const int mode = local_mode;
-    tr_stamp(1);
-    if (mode < 0 || c.g >= a.ntiles) return;
-    if (mode) spec_body<KS, FUSED, true, PO>(a, c, L);
-    else spec_body<KS, FUSED, false, PO>(a, c, L);
+    if (c.w < kMW) {
+        MState<KS, PO> S;
+        m_dma_offsets<KS, PO>(S, a, c);
+        const PubMap M = pub_map(srec_of);
+        m_dma<KS, PO>(S, a, c, L, 0);
+        m_dma<KS, PO>(S, a, c, L, 1);
+        m_weights<KS, PO>(S, a, c);
+        // round 0 landed (older than round 1 and the weight loads, which
+        // have landed too by now)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS, PO>::kDmaW) : "memory");
+        if constexpr (PO) {
+            // round 0 into R' before the first tick
+            m_arrive(&L.acnt);
+            const bool bad = m_wait(a, &L.acnt, 4u);
+            if (!bad) m_post<KS>(a, c, L, 0);
+            else L.stop = 1;
+        }
+        __syncthreads();
+        const int mode = local_mode;
+        if (mode < 0) {
+            // no load may still be writing this workgroup's LDS when it ends
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            return;
+        }
+        tr_start();
+        tr_stamp(2);
+        if (mode) m_loop<KS, FUSED, true, PO>(S, M, a, c, L);
+        else m_loop<KS, FUSED, false, PO>(S, M, a, c, L);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+        if (c.w == kMW) start_protocol(a, c, &local_mode);
+        XState<KS> X;
+        x_offsets<KS>(X, a, c, c.w - kMW);
+        __syncthreads();
+        const int mode = local_mode;
+        if (mode < 0) return;
+        tr_start();
+        if (mode) x_loop<KS, FUSED, true, PO>(X, a, c, L);
+        else x_loop<KS, FUSED, false, PO>(X, a, c, L);
+    }
     tr_finish(c.nr + 2);
 }
 
