@@ -1052,7 +1052,7 @@ struct DmaRun {
 
 // The member's weight slice (packed, or split here) and the lane offsets of
 // the residual loads (m_dma).  m_dma_offsets alone is enough to start
-// loading rounds; the persistent kernel issues its first two rounds before
+// loading rounds: k_spec and k_part issue their first rounds before
 // fetching the weights, so that both round trips overlap.
 template <int KS, bool PO = false>
 __device__ __forceinline__ void m_weights(MState<KS, PO>& S, const CoopArgs& a, const RoundCtx& c) {
@@ -1086,11 +1086,6 @@ __device__ __forceinline__ void m_dma_offsets(MState<KS, PO>& S, const CoopArgs&
         }
         S.dvoff[i] = v;
     }
-}
-template <int KS, bool PO = false>
-__device__ __forceinline__ void m_setup(MState<KS, PO>& S, const CoopArgs& a, const RoundCtx& c) {
-    m_weights<KS, PO>(S, a, c);
-    m_dma_offsets<KS, PO>(S, a, c);
 }
 
 // Round r of this group (rounds past the end: zeros) into slot r % 3; with
@@ -1954,18 +1949,17 @@ __global__ __launch_bounds__(kMW * 64, 1) void k_part(CoopArgs a) {
     c.s0 = 0.0f;
     c.bpre = 0.0f;
     MState<KS> S;
-    m_setup<KS>(S, a, c);
+    m_dma_offsets<KS>(S, a, c);
     const PubMap M = pub_map(prec_of);
     // rounds past the group's last are neither loaded nor multiplied (a
-    // call of a few tokens has one round per group); each wait below still
-    // covers the loads of every round that is used
+    // call of a few tokens has one round per group); the first rounds'
+    // loads go out before the weights are fetched, so that both round trips
+    // overlap; each wait below still covers the loads of every round used
     m_dma<KS>(S, a, c, L, 0);
-    if (1 < c.nr) {
-        m_dma<KS>(S, a, c, L, 1);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Geo<KS>::kDmaW) : "memory");   // round 0 landed
-    } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    if (1 < c.nr) m_dma<KS>(S, a, c, L, 1);
+    m_weights<KS>(S, a, c);
+    // the rounds' loads are older than the weight loads, which have landed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     for (int t = 0;; ++t) {
         p_publish<KS>(a, c, L, M, t - 1);
