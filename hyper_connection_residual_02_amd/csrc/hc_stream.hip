@@ -105,6 +105,45 @@ __global__ __launch_bounds__(256) void k_post(const u32x4* __restrict__ x, const
     }
 }
 
+// hc_post for short calls: items of 4 features (half a chunk; map.d8 holds
+// the token row's 8-byte pieces), so that a call of a few tokens spreads
+// over twice as many threads and each thread's chain of double sums is half
+// as long.  post_words_lean<2> forms the same double sums and rounding, so
+// the results are k_post's bit for bit.
+template <bool UNIFORM>
+__global__ __launch_bounds__(256) void k_post4(const u32x2* __restrict__ x, const u32x2* R,
+                                               const float* __restrict__ post, const float* __restrict__ comb,
+                                               u32x2* Rout, ItemMap map) {
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t it = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; it < map.items; it += stride) {
+        uint64_t t;
+        uint32_t c4;
+        item_of(it, map.d8, t, c4);
+        if (UNIFORM)
+            t = __builtin_amdgcn_readfirstlane((uint32_t)t) |
+                ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(t >> 32)) << 32);
+        const uint64_t row = t * kHC * (uint64_t)map.d8 + c4;
+        const u32x2 xp = __builtin_nontemporal_load(x + t * map.d8 + c4);
+        uint32_t xw[2] = {xp[0], xp[1]};
+        uint32_t rw[kHC][2];
+#pragma unroll
+        for (int j = 0; j < kHC; ++j) {
+            const u32x2 v = __builtin_nontemporal_load(R + row + j * (uint64_t)map.d8);
+            rw[j][0] = v[0];
+            rw[j][1] = v[1];
+        }
+        const f32x4 q = *reinterpret_cast<const f32x4*>(post + t * kHC);
+        f32x4 cb[kHC];
+#pragma unroll
+        for (int j = 0; j < kHC; ++j) cb[j] = *reinterpret_cast<const f32x4*>(comb + (t * kHC + j) * kHC);
+        uint32_t out[kHC][2];
+        post_words_lean<2>(q, cb, xw, rw, out);
+#pragma unroll
+        for (int k = 0; k < kHC; ++k)
+            __builtin_nontemporal_store(u32x2{out[k][0], out[k][1]}, Rout + row + k * (uint64_t)map.d8);
+    }
+}
+
 // ----------------------------------------------------------- diag_scale
 // x_c = bf16(h_c * D_c): the product of two bf16 values is exact in float.
 __global__ __launch_bounds__(256) void k_diag(const u32x4* __restrict__ h, const u32x4* __restrict__ D,
@@ -145,6 +184,17 @@ int launch_pre(const void* R, const float* pre, void* h, int64_t n, int d, hipSt
 int launch_post(const void* x, const void* R, const float* post, const float* comb, void* Rout,
                 int64_t n, int d, hipStream_t s) {
     ItemMap m{(uint32_t)(d / 8), (uint64_t)n * (uint64_t)(d / 8)};
+    if (m.items < 256ull * (uint64_t)num_cus()) {
+        // fewer 16-byte items than one 256-thread workgroup per CU: half
+        // items, one per thread
+        ItemMap h{(uint32_t)(d / 4), (uint64_t)n * (uint64_t)(d / 4)};
+        const int g = grid_for(h.items, 16);
+        if (h.d8 % 64 == 0)
+            k_post4<true><<<g, 256, 0, s>>>((const u32x2*)x, (const u32x2*)R, post, comb, (u32x2*)Rout, h);
+        else
+            k_post4<false><<<g, 256, 0, s>>>((const u32x2*)x, (const u32x2*)R, post, comb, (u32x2*)Rout, h);
+        return hipGetLastError() == hipSuccess ? 0 : -1;
+    }
     // Long runs: two workgroups per CU, whose waves each stream many items
     // and so keep fewer DRAM pages open at once (2.7 % faster than 16 per CU
     // at 65,536 tokens); short runs need the wider grid to fill the chip.
