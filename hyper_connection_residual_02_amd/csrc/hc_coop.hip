@@ -2125,8 +2125,9 @@ __global__ void k_hdr(WsHeader* hdr, int64_t nchunks, uint64_t call, int ngroups
 }
 
 // Header update and record-area clearing before a call of the cooperative
-// kernel of narrow or wide streams (the wave-specialised kernel does this
-// at its own start).
+// kernel of narrow or wide streams (before the wave-specialised kernel,
+// k_hdr updates the header and the kernel's workgroups clear the record
+// area themselves).
 __global__ __launch_bounds__(1024) void k_init(WsHeader* hdr, u32x4* part, int64_t nchunks, uint64_t call) {
     __shared__ int clear;
     if (threadIdx.x == 0) clear = header_update(hdr, call, nchunks, 0);
