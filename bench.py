@@ -192,7 +192,7 @@ def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, step
                 if sel:
                     timed[name] = sum(sel) / len(sel) / 1e3
     fb, pb = algorithmic_bytes(n, dd, hc)
-    alg = {"k_spec": fb, "k_coop": fb, "k_post": pb, "k_gpost": pb}
+    alg = {"k_spec": fb, "k_coop": fb, "k_post": pb, "k_post4": pb, "k_gpost": pb}
     if hc == 4:
         alg["k_spec_post"] = boundary_bytes(n, dd)
     if hc == 4:
