@@ -117,15 +117,21 @@ def summarize_counters(d: str, n: int, dd: int, command: str, tag: str = ""):
     csv, one pass per counter, each run with --copy-calib) under ``d`` into HBM
     bytes per launch of each hc kernel.  Each counter is scaled by what it
     reads for the plain 1 GiB device copy of the same run (the copy dispatch
-    with the largest WRITE_SIZE), so the figures are in bytes moved."""
+    whose WRITE_SIZE is nearest 1 GiB), so the figures are in bytes moved."""
     fetch, write = _counter_rows(d, "FETCH_SIZE"), _counter_rows(d, "WRITE_SIZE")
 
-    def copy_value(rows):
-        # the calibration copy is the largest device copy of the run
-        return max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
-
-    f_copy, w_copy = copy_value(fetch), copy_value(write)
+    # the calibration copy: the device copy whose WRITE_SIZE is nearest the
+    # 1 GiB it writes (the run may copy other buffers too)
     kib = COPY_CALIB_BYTES / 1024.0
+    def copies(rows):
+        c = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        return sorted(c, key=lambda r: int(r.get("Dispatch_Id", 0) or 0))
+    wc, fc = copies(write), copies(fetch)
+    if not wc or len(fc) != len(wc):
+        raise SystemExit("the two passes under %s do not hold the same device copies" % d)
+    i_cal = min(range(len(wc)), key=lambda i: abs(float(wc[i]["Counter_Value"]) - kib))
+    # the same dispatch in the FETCH_SIZE pass (same program, same copies)
+    w_copy, f_copy = float(wc[i_cal]["Counter_Value"]), float(fc[i_cal]["Counter_Value"])
     f_scale, w_scale = kib / f_copy, kib / w_copy
     fb, pb = algorithmic_bytes(n, dd)
     _, bn_pre, bn_rms = norm_bytes(n, dd)

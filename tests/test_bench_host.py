@@ -99,3 +99,38 @@ def test_summarize_trace_general_stream_count(tmp_path, monkeypatch):
     pcells = [c.strip() for c in prow.strip("|").split("|")]
     assert float(pcells[7]) == pytest.approx(33.0)
     assert float(pcells[8]) == pytest.approx(post / 33e-6 / 1e9 / bench.HBM_PEAK_GBS, abs=1e-3)
+
+
+def _write_counters(d, counter, rows):
+    os.makedirs(os.path.join(d, counter), exist_ok=True)
+    with open(os.path.join(d, counter, "x_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.writer(fh, quoting=csv.QUOTE_ALL)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, (name, v) in enumerate(rows):
+            w.writerow([i + 1, name, counter, v])
+
+
+def test_summarize_counters_calibrates_on_the_one_gib_copy(tmp_path, monkeypatch):
+    # the run copies a larger buffer too (a clone of the residual): the
+    # calibration must take the 1 GiB copy, not the largest one
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    d = str(tmp_path / "pmc")
+    copy = "__amd_rocclr_copyBuffer"
+    spec = "void hc::spec::k_spec<5, true, false>(hc::CoopArgs)"
+    post = "void hc::k_post<true>(HIP_vector_type<unsigned int, 4u> const*)"
+    n, dd = 65536, 5120
+    fb, pb = bench.algorithmic_bytes(n, dd)
+    kib = 1 << 20                                   # KiB in 1 GiB
+    # counters read as the real ones do: FETCH_SIZE half the bytes a copy
+    # moves, WRITE_SIZE all of them
+    _write_counters(d, "FETCH_SIZE", [(copy, 2.5 * kib / 2), (spec, 1.1 * fb / 2048), (post, pb / 2 / 2048),
+                                      (copy, kib / 2)])
+    _write_counters(d, "WRITE_SIZE", [(copy, 2.5 * kib), (spec, 0.1 * fb / 1024), (post, pb / 2 / 1024),
+                                      (copy, kib)])
+    bench.summarize_counters(d, n, dd, "cmd")
+    text = (tmp_path / "hbm_traffic_n65536_d5120.md").read_text()
+    assert "FETCH_SIZE read 524288 KiB" in text and "(x2.0000)" in text and "(x1.0000)" in text
+    row = [l for l in text.splitlines() if l.startswith("| k_spec ")][0]
+    assert float(row.strip("|").split("|")[-1]) == pytest.approx(1.2, abs=1e-3)
+    prow = [l for l in text.splitlines() if l.startswith("| k_post ")][0]
+    assert float(prow.strip("|").split("|")[-1]) == pytest.approx(1.0, abs=1e-3)
