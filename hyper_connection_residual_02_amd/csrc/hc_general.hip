@@ -971,6 +971,9 @@ int launch_gen_fused(const void* R, const float* W, const float* scale, const fl
     if (dispatch_hc<MixOp>(hc_, R, W, (const u32x4*)wp, mx, part, n, d, norm_eps, s)) return -1;
     if (dispatch_hc<SplitOp>(hc_, mx, scale, base, pr, post, comb, n, iters, eps, reinterpret_cast<uint32_t*>(w), s))
         return -1;
+    // h with hc_pre's one-token-per-workgroup kernel where it applies (the
+    // same exact double sums and one rounding as k_gpre)
+    if (norm_waves(d)) return launch_pre_norm(R, pr, nullptr, h, nullptr, n, hc_, d, 0.0f, s);
     return launch_gen_pre(R, pr, h, n, hc_, d, s);
 }
 
