@@ -756,10 +756,81 @@ __global__ __launch_bounds__(kGThreads) void k_gpre(const uint16_t* __restrict__
 }
 
 // hc_post of the "Mix projection" page: output stream k is
-// bf16(post_k x_c + sum_j comb[j][k] R_{j,c}).  An item reads every stream
-// of its chunk before writing any, so R_out may be R.
+// bf16(post_k x_c + sum_j comb[j][k] R_{j,c}), the double sum rounded once.
+// An item reads every stream of its chunk before writing any, and the next
+// item's loads (issued early) touch only that item's chunk, so R_out may be
+// R.  Up to 6 streams (k_gpost_lean beyond).
 template <int HC>
 __global__ __launch_bounds__(kGThreads) void k_gpost(const uint16_t* __restrict__ x, const uint16_t* R,
+                                                     const float* __restrict__ post, const float* __restrict__ comb,
+                                                     uint16_t* Rout, int64_t n, int d) {
+    const int cpt = d / 8;
+    const int64_t items = n * cpt;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (it >= items) return;
+    struct Item {
+        int64_t t;
+        int c0;
+        u32x4 xv, r[HC];
+    };
+    // the next item's loads are in flight while this item is computed; past
+    // the end the last item is loaded again (no branch around the loads)
+    auto fetch = [&](int64_t i, Item& I) {
+        const int64_t ii = i < items ? i : items - 1;
+        I.t = ii / cpt;
+        I.c0 = (int)(ii - I.t * cpt) * 8;
+        I.xv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + I.t * d + I.c0));
+#pragma unroll
+        for (int j = 0; j < HC; ++j)
+            I.r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(R + (I.t * HC + j) * d + I.c0));
+    };
+    auto bf = [](const u32x4& v, int e) { return (double)((e & 1) ? bf_hi(v[e >> 1]) : bf_lo(v[e >> 1])); };
+    Item cur, nxt;
+    fetch(it, cur);
+    for (; it < items; it += stride) {
+        fetch(it + stride, nxt);
+        const int64_t t = cur.t;
+#pragma unroll
+        for (int k = 0; k < HC; ++k) {
+            const double pk = post[t * HC + k];
+            double cj[HC];
+#pragma unroll
+            for (int j = 0; j < HC; ++j) cj[j] = comb[(t * HC + j) * HC + k];
+            auto sum = [&](int e) {
+                double y = pk * bf(cur.xv, e);
+#pragma unroll
+                for (int j = 0; j < HC; ++j) y = __builtin_fma(cj[j], bf(cur.r[j], e), y);
+                return y;
+            };
+            // each output is bf16_rn_f64 of its double sum: through the float
+            // rounding unless a lane of the wave hit a float halfway point
+            float f[8];
+            bool mid = false;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = f32_mid(sum(e), mid);
+            uint32_t o[8];
+            if (__builtin_amdgcn_ballot_w64(mid)) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = bf16_rn_f64(sum(e));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = bf16_rn(f[e]);
+            }
+            const uint4 pk8 = pack8(o);
+            __builtin_nontemporal_store(u32x4{pk8.x, pk8.y, pk8.z, pk8.w},
+                                        reinterpret_cast<u32x4*>(Rout + (t * HC + k) * d + cur.c0));
+        }
+        cur = nxt;
+    }
+}
+
+// hc_post for 7 and 8 streams: k_gpost's arithmetic without its prefetch
+// and fast path, whose registers (a second item of up to 8 streams) cost
+// more in resident waves than they gain there.  Each output is the same
+// bf16_rn_f64 of the same double sum.
+template <int HC>
+__global__ __launch_bounds__(kGThreads) void k_gpost_lean(const uint16_t* __restrict__ x, const uint16_t* R,
                                                      const float* __restrict__ post, const float* __restrict__ comb,
                                                      uint16_t* Rout, int64_t n, int d) {
     const int cpt = d / 8;
@@ -912,9 +983,14 @@ template <int HC>
 struct PostOp {
     static int run(const void* x, const void* R, const float* post, const float* comb, void* Rout, int64_t n, int d,
                    hipStream_t s) {
-        hipLaunchKernelGGL(k_gpost<HC>, dim3(grid_for(n * (d / 8))), dim3(kGThreads), 0, s,
-                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(R), post, comb,
-                           static_cast<uint16_t*>(Rout), n, d);
+        if constexpr (HC <= 6)
+            hipLaunchKernelGGL(k_gpost<HC>, dim3(grid_for(n * (d / 8))), dim3(kGThreads), 0, s,
+                               static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(R), post, comb,
+                               static_cast<uint16_t*>(Rout), n, d);
+        else
+            hipLaunchKernelGGL(k_gpost_lean<HC>, dim3(grid_for(n * (d / 8))), dim3(kGThreads), 0, s,
+                               static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(R), post, comb,
+                               static_cast<uint16_t*>(Rout), n, d);
         return hipGetLastError() == hipSuccess ? 0 : -1;
     }
 };
