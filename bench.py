@@ -198,7 +198,7 @@ def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, step
                 if sel:
                     timed[name] = sum(sel) / len(sel) / 1e3
     fb, pb = algorithmic_bytes(n, dd, hc)
-    alg = {"k_spec": fb, "k_coop": fb, "k_post": pb, "k_post4": pb, "k_gpost": pb}
+    alg = {"k_spec": fb, "k_coop": fb, "k_post": pb, "k_post4": pb, "k_gpost": pb, "k_gpost_lean": pb}
     if hc == 4:
         alg["k_spec_post"] = boundary_bytes(n, dd)
     if hc == 4:
@@ -236,23 +236,29 @@ def summarize_trace(d: str, n: int, dd: int, command: str, warmup: int = 0, step
         lines.append("| k_part + k_fin (hc_fused_mix_pre, two-pass) | %s | %.2f | - | - | %.1f | %.3f | %s | %s |" % (
             part[0]["Calls"], avg, gbs, gbs / HBM_PEAK_GBS, "%.2f" % t if t else "-",
             "%.3f" % (tg / HBM_PEAK_GBS) if tg else "-"))
-    # other stream counts run the fused entry point as the projection (k_gmm,
-    # with k_gred when its reduction is split over workgroups), the split and
-    # hc_pre
-    gen = [[r for r in rows if "::k_gmm<" in r["Name"]], [r for r in rows if "::k_gsplit<" in r["Name"]],
-           [r for r in rows if "::k_gpre<" in r["Name"]]]
+    # other stream counts run the fused entry point as the weight split
+    # (k_gpack), the projection (k_gmm or k_gmm_tall, with k_gred when its
+    # reduction is split over workgroups), the split and h (k_pre_norm, or
+    # k_gpre above 32,768 features)
+    proj = [r for r in rows if "::k_gmm<" in r["Name"] or "::k_gmm_tall<" in r["Name"]]
+    hpass = [r for r in rows if "::k_gpre<" in r["Name"] or "::k_pre_norm<" in r["Name"]]
+    gen = [proj, [r for r in rows if "::k_gsplit<" in r["Name"]], hpass]
     red = [r for r in rows if "::k_gred<" in r["Name"]]
+    pack = [r for r in rows if "::k_gpack<" in r["Name"]]
     if red:
         gen.append(red)
-    if all(gen):
+    if pack:
+        gen.append(pack)
+    if hc != 4 and all(gen):
         avg = sum(float(g[0]["AverageNs"]) for g in gen) / 1e3
         gbs = fb / (avg * 1e-6) / 1e9
         ts = [timed.get(g[0]["Name"]) for g in gen]
         t = sum(ts) if all(ts) else None
         tg = fb / (t * 1e-6) / 1e9 if t else None
-        lines.append("| k_gmm%s + k_gsplit + k_gpre (hc_fused_mix_pre) | %s | %.2f | - | - | %.1f | %.3f | %s | %s |" % (
-            " + k_gred" if red else "", gen[0][0]["Calls"], avg, gbs, gbs / HBM_PEAK_GBS, "%.2f" % t if t else "-",
-            "%.3f" % (tg / HBM_PEAK_GBS) if tg else "-"))
+        lines.append("| %s%s%s + k_gsplit + %s (hc_fused_mix_pre) | %s | %.2f | - | - | %.1f | %.3f | %s | %s |" % (
+            "k_gpack + " if pack else "", kernel_key(proj[0]["Name"]), " + k_gred" if red else "",
+            kernel_key(hpass[0]["Name"]), gen[0][0]["Calls"], avg, gbs, gbs / HBM_PEAK_GBS,
+            "%.2f" % t if t else "-", "%.3f" % (tg / HBM_PEAK_GBS) if tg else "-"))
     lines.append("")
     if steps:
         lines.append("Timed region: dispatches %d .. %d of each kernel (after %d warmup steps)."
@@ -1101,7 +1107,8 @@ def main():
     else:
         dom = dict(name="hc_fused_mix_pre", kernel="k_spec", us=f_us, bytes=fb, gbs=fb / (f_us * 1e-6) / 1e9)
     if w.hc != 4:
-        dom["kernel"] = "k_gpost" if dom["name"] == "hc_post" else "k_gmm + k_gsplit + k_gpre"
+        dom["kernel"] = (("k_gpost" if w.hc <= 6 else "k_gpost_lean") if dom["name"] == "hc_post"
+                         else "k_gpack + k_gmm + k_gsplit + k_pre_norm")
     traffic = measured_traffic(dom["kernel"], n, d) if w.hc == 4 else None
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample of the same workload
