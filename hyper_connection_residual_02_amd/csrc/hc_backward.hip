@@ -70,28 +70,45 @@ __global__ __launch_bounds__(256) void k_post_bwd(const u32x4* __restrict__ x, c
 #pragma unroll
         for (int j = 0; j < kHC; ++j) ac[j][k] = 0.0;
     }
-    for (int c8 = lane; c8 < d8; c8 += 64) {
-        const u32x4 xv = x[t * d8 + c8];
-        u32x4 rv[kHC], gv[kHC];
+    // the next chunk's loads are in flight while this one is computed
+    // (non-temporal: every input is read once); past the row's end the last
+    // chunk is loaded again, with no branch around the loads
+    struct Chunk {
+        u32x4 xv, rv[kHC], gv[kHC];
+    };
+    auto fetch = [&](int c8, Chunk& C) {
+        const int c = c8 < d8 ? c8 : d8 - 1;
+        C.xv = __builtin_nontemporal_load(x + t * d8 + c);
 #pragma unroll
         for (int k = 0; k < kHC; ++k) {
-            rv[k] = R[(t * kHC + k) * d8 + c8];
-            gv[k] = gRo[(t * kHC + k) * d8 + c8];
+            C.rv[k] = __builtin_nontemporal_load(R + (t * kHC + k) * d8 + c);
+            C.gv[k] = __builtin_nontemporal_load(gRo + (t * kHC + k) * d8 + c);
         }
-        u32x4 out;
+    };
+    Chunk cur, nxt;
+    if (lane < d8) fetch(lane, cur);
+    for (int c8 = lane; c8 < d8; c8 += 64) {
+        fetch(c8 + 64, nxt);
+        const u32x4 xv = cur.xv;
+        const u32x4(&rv)[kHC] = cur.rv;
+        const u32x4(&gv)[kHC] = cur.gv;
+        // dL/dx: exact products in double, one rounding (through the float
+        // rounding unless a lane of the wave hit a halfway point)
+        double ys[4][2];
+        float fs[4][2];
+        bool mid = false;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            uint32_t o2[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 auto v = [&](uint32_t word) { return (double)(e ? bf_hi(word) : bf_lo(word)); };
                 const double g0 = v(gv[0][w]), g1 = v(gv[1][w]), g2 = v(gv[2][w]), g3 = v(gv[3][w]);
-                // dL/dx: exact products in double, one rounding
                 double y = q0 * g0;
                 y = __builtin_fma(q1, g1, y);
                 y = __builtin_fma(q2, g2, y);
                 y = __builtin_fma(q3, g3, y);
-                o2[e] = bf16_rn_f64(y);
+                ys[w][e] = y;
+                fs[w][e] = f32_mid(y, mid);
                 const double xe = v(xv[w]);
                 const double g[kHC] = {g0, g1, g2, g3};
 #pragma unroll
@@ -103,9 +120,17 @@ __global__ __launch_bounds__(256) void k_post_bwd(const u32x4* __restrict__ x, c
                     for (int k = 0; k < kHC; ++k) ac[j][k] = __builtin_fma(rj, g[k], ac[j][k]);
                 }
             }
-            out[w] = pack2(o2[0], o2[1]);
         }
-        gx[t * d8 + c8] = out;
+        u32x4 out;
+        if (__builtin_amdgcn_ballot_w64(mid)) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) out[w] = pack2(bf16_rn_f64(ys[w][0]), bf16_rn_f64(ys[w][1]));
+        } else {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) out[w] = pack2(bf16_rn(fs[w][0]), bf16_rn(fs[w][1]));
+        }
+        __builtin_nontemporal_store(out, gx + t * d8 + c8);
+        cur = nxt;
     }
 #pragma unroll
     for (int k = 0; k < kHC; ++k) ap[k] = wave_sum_f64(ap[k]);
