@@ -183,11 +183,26 @@ __global__ __launch_bounds__(256) void k_pre_bwd(PreBwdArgs a) {
     if (t >= a.n) return;
     const int d8 = a.d / 8;
     double gp[kHC] = {0.0, 0.0, 0.0, 0.0}, ss = 0.0;
+    // the next chunk's loads are in flight while this one is summed (few
+    // waves fit beside the step table in LDS, so latency would show);
+    // non-temporal, and past the row's end the last chunk is loaded again
+    struct Chunk {
+        u32x4 hv, rv[kHC];
+    };
+    auto fetch = [&](int c8, Chunk& C) {
+        const int c = c8 < d8 ? c8 : d8 - 1;
+        C.hv = __builtin_nontemporal_load(a.gh + t * d8 + c);
+#pragma unroll
+        for (int k = 0; k < kHC; ++k) C.rv[k] = __builtin_nontemporal_load(a.R + (t * kHC + k) * d8 + c);
+    };
+    Chunk cur, nxt;
+    if (lane < d8) fetch(lane, cur);
     for (int c8 = lane; c8 < d8; c8 += 64) {
-        const u32x4 hv = a.gh[t * d8 + c8];
+        fetch(c8 + 64, nxt);
+        const u32x4 hv = cur.hv;
 #pragma unroll
         for (int k = 0; k < kHC; ++k) {
-            const u32x4 rv = a.R[(t * kHC + k) * d8 + c8];
+            const u32x4 rv = cur.rv[k];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const double r0 = bf_lo(rv[w]), r1 = bf_hi(rv[w]);
@@ -197,6 +212,7 @@ __global__ __launch_bounds__(256) void k_pre_bwd(PreBwdArgs a) {
                 ss = __builtin_fma(r1, r1, ss);
             }
         }
+        cur = nxt;
     }
 #pragma unroll
     for (int k = 0; k < kHC; ++k) gp[k] = wave_sum_f64(gp[k]);
