@@ -599,3 +599,27 @@ def test_other_stream_count_call_invalidates_four_stream_header():
     for a, b in zip(first, again):
         iv = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
         assert torch.equal(a.view(iv), b.view(iv))
+
+
+@pytest.mark.parametrize("d", [5120, 2048, 64])
+def test_post_short_and_long_calls_agree_bitwise(d):
+    # hc_post takes half-chunk items (k_post4) for calls with fewer 16-byte
+    # items than one workgroup per CU and full chunks (k_post) beyond: a
+    # token's R' is the same bits whichever kernel its call runs, in place
+    # or not
+    g = torch.Generator(device="cpu").manual_seed(61)
+    n = 2 * 256 * torch.cuda.get_device_properties(0).multi_processor_count * 8 // d + 40
+    R = torch.randn(n, 4, d, generator=g).to(torch.bfloat16).to(DEV)
+    x = torch.randn(n, d, generator=g).to(torch.bfloat16).to(DEV)
+    post = (2 * torch.rand(n, 4, generator=g)).to(DEV)
+    comb = torch.rand(n, 4, 4, generator=g).to(DEV)
+    full = hcl.hc_post(x, R, post, comb)
+    for lo, hi in [(0, 1), (3, 67), (0, n // 3), (n // 3, n)]:
+        part = hcl.hc_post(x[lo:hi].contiguous(), R[lo:hi].contiguous(), post[lo:hi].contiguous(),
+                           comb[lo:hi].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(full[lo:hi], part), (d, lo, hi)
+    Rin = R[:5].clone()
+    hcl.hc_post(x[:5].contiguous(), Rin, post[:5].contiguous(), comb[:5].contiguous(), out=Rin)
+    torch.cuda.synchronize()
+    assert torch.equal(full[:5], Rin), (d, "in place")
